@@ -1,0 +1,246 @@
+"""ctypes wrapper of the fp64 C oracle of the QSA layer.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the package's smoke check
+and the CPU-baseline leg of the benchmark, never by the product path.  It
+shares no code with the HIP library; inputs come from the ``synth`` module.
+Parity unpinned by the pages for end-to-end values: the pages print no worked
+example, so the oracle is pinned by closed forms, brute force and invariants
+(see tests/test_oracle_*.py).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libqsa_oracle.so")
+# A test that plants a mistake in the oracle builds a mutated copy and points
+# this variable at it (tests/test_oracle_mutations.py).
+_LIB_OVERRIDE = os.environ.get("QSA_ORACLE_LIB")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``libqsa_oracle.so`` (gcc, -O2, OpenMP over query rows)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB_PATH):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB_PATH)
+        vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        lib.qsa_oracle_rope.argtypes = [vp, vp, i64, i32, i32, i32, dbl, i64, vp]
+        lib.qsa_oracle_rope.restype = None
+        lib.qsa_oracle_compress.argtypes = [vp, i64, i32, i32, i32, vp]
+        lib.qsa_oracle_compress.restype = None
+        lib.qsa_oracle_num_complete.argtypes = [i64, i32]
+        lib.qsa_oracle_num_complete.restype = i64
+        lib.qsa_oracle_scores_row.argtypes = [vp, vp, i64, i64, i32, i32, i32, i32, vp]
+        lib.qsa_oracle_scores_row.restype = i64
+        lib.qsa_oracle_topk_row.argtypes = [vp, i64, i32, vp, vp, vp]
+        lib.qsa_oracle_topk_row.restype = i32
+        lib.qsa_oracle_token_set.argtypes = [vp, i32, i64, i32, vp]
+        lib.qsa_oracle_token_set.restype = i64
+        lib.qsa_oracle_attend_row.argtypes = [vp, vp, vp, i32, i32, i32, vp, i64, vp, vp, vp]
+        lib.qsa_oracle_attend_row.restype = None
+        lib.qsa_oracle_qsa_rows.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32,
+                                            i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp,
+                                            vp, vp]
+        lib.qsa_oracle_qsa_rows.restype = None
+        lib.qsa_oracle_sparse_attn_rows.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32,
+                                                    vp, i64, vp, vp, vp, vp]
+        lib.qsa_oracle_sparse_attn_rows.restype = None
+        lib.qsa_oracle_select_rows.argtypes = [vp, vp, i64, i64, i32, i32, i32, i32, i32, vp,
+                                               i64, vp, i64, vp, vp, vp, vp]
+        lib.qsa_oracle_select_rows.restype = None
+        lib.qsa_oracle_dense_rows.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, i64, vp, vp]
+        lib.qsa_oracle_dense_rows.restype = None
+        lib.qsa_oracle_f64_to_bf16.argtypes = [dbl]
+        lib.qsa_oracle_f64_to_bf16.restype = ctypes.c_uint16
+        lib.qsa_oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.qsa_oracle_bf16_to_f64.restype = dbl
+        _lib = lib
+    return _lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+MODE_MAXHEAD, MODE_RELUSUM = 0, 1
+KBAR_MEAN, KBAR_RMSNORM = 0, 1
+
+
+def f64_to_bf16(x: float) -> int:
+    return int(_load().qsa_oracle_f64_to_bf16(float(x)))
+
+
+def bf16_to_f64(h: int) -> float:
+    return float(_load().qsa_oracle_bf16_to_f64(int(h)))
+
+
+def rope(x: np.ndarray, rope_dim: int = 64, theta: float = 1e7, pos0: int = 0,
+         pos: np.ndarray | None = None) -> np.ndarray:
+    """x [T, nheads, head_dim] bf16 bits -> rotated copy (bf16 bits)."""
+    x = _c(x, np.uint16)
+    T, nh, hd = x.shape
+    y = np.empty_like(x)
+    pa = None if pos is None else _c(pos, np.int64)
+    _load().qsa_oracle_rope(_p(x), _p(y), T, nh, hd, rope_dim, theta, pos0, _p(pa))
+    return y
+
+
+def compress(k: np.ndarray, r: int = 4, mode: int = KBAR_MEAN) -> np.ndarray:
+    """k [Tk, Di] bf16 bits -> kbar [Tk // r, Di] bf16 bits."""
+    k = _c(k, np.uint16)
+    Tk, Di = k.shape
+    out = np.empty((Tk // r, Di), dtype=np.uint16)
+    _load().qsa_oracle_compress(_p(k), Tk, Di, r, mode, _p(out))
+    return out
+
+
+def num_complete(p: int, r: int = 4) -> int:
+    return int(_load().qsa_oracle_num_complete(p, r))
+
+
+def scores_row(qi_row: np.ndarray, kbar: np.ndarray, p: int, r: int = 4,
+               mode: int = MODE_MAXHEAD) -> np.ndarray:
+    """qi_row [Hi, Di], kbar [nb, Di] -> s [nc] (fp64)."""
+    qi_row = _c(qi_row, np.uint16)
+    kbar = _c(kbar, np.uint16)
+    Hi, Di = qi_row.shape
+    nc_full = max(num_complete(p, r), 1)
+    s = np.empty(nc_full, dtype=np.float64)
+    nc = _load().qsa_oracle_scores_row(_p(qi_row), _p(kbar), kbar.shape[0], p, Hi, Di, r, mode,
+                                       _p(s))
+    return s[:nc].copy()
+
+
+def topk_row(s: np.ndarray, K: int):
+    """-> (ascending selected blocks, rank-K score, rank-K+1 score)."""
+    s = _c(s, np.float64)
+    blk = np.full(max(K, 1), -1, dtype=np.int32)
+    sK = np.zeros(1)
+    sK1 = np.zeros(1)
+    n = _load().qsa_oracle_topk_row(_p(s), s.size, K, _p(blk), _p(sK), _p(sK1))
+    return blk[:n].copy(), float(sK[0]), float(sK1[0])
+
+
+def token_set(blk: np.ndarray, p: int, r: int = 4) -> np.ndarray:
+    blk = _c(blk, np.int32)
+    tok = np.empty(blk.size * r + r, dtype=np.int64)
+    n = _load().qsa_oracle_token_set(_p(blk), blk.size, p, r, _p(tok))
+    return tok[:n].copy()
+
+
+def attend_row(q_row: np.ndarray, K: np.ndarray, V: np.ndarray, tokens: np.ndarray):
+    """q_row [H, D], K/V [Tk, Hkv, D] bf16 bits -> (O [H, D], lse [H], wsum_err)."""
+    q_row = _c(q_row, np.uint16)
+    K = _c(K, np.uint16)
+    V = _c(V, np.uint16)
+    H, D = q_row.shape
+    Hkv = K.shape[1]
+    tokens = _c(tokens, np.int64)
+    O = np.empty((H, D))
+    lse = np.empty(H)
+    err = np.zeros(1)
+    _load().qsa_oracle_attend_row(_p(q_row), _p(K), _p(V), H, Hkv, D, _p(tokens), tokens.size,
+                                  _p(O), _p(lse), _p(err))
+    return O, lse, float(err[0])
+
+
+def qsa_rows(Q, K, V, qi, kbar, rows, pos0: int = 0, Kbudget: int = 512, r: int = 4,
+             mode: int = MODE_MAXHEAD):
+    """End-to-end QSA of selected query rows (inputs post-RoPE / post-compress).
+
+    Returns dict with O [n,H,D], lse [n,H], sel [n,K], nsel [n], sK, sK1,
+    wsum_err.
+    """
+    Q, K, V, qi, kbar = (_c(a, np.uint16) for a in (Q, K, V, qi, kbar))
+    rows = _c(rows, np.int64)
+    n = rows.size
+    _, H, D = Q.shape
+    Hkv = K.shape[1]
+    Hi, Di = qi.shape[1], qi.shape[2]
+    O = np.empty((n, H, D))
+    lse = np.empty((n, H))
+    sel = np.empty((n, Kbudget), dtype=np.int32)
+    nsel = np.empty(n, dtype=np.int32)
+    sK = np.empty(n)
+    sK1 = np.empty(n)
+    err = np.empty(n)
+    _load().qsa_oracle_qsa_rows(_p(Q), _p(K), _p(V), _p(qi), _p(kbar), kbar.shape[0], pos0, H,
+                                Hkv, D, Hi, Di, r, Kbudget, mode, _p(rows), n, _p(O), _p(lse),
+                                _p(sel), _p(nsel), _p(sK), _p(sK1), _p(err))
+    return dict(O=O, lse=lse, sel=sel, nsel=nsel, sK=sK, sK1=sK1, wsum_err=err)
+
+
+def sparse_attn_rows(Q, K, V, rows, sel, nsel, pos0: int = 0, r: int = 4):
+    """Attention of rows over a given selection sel [n, Kbudget] / nsel [n]."""
+    Q, K, V = (_c(a, np.uint16) for a in (Q, K, V))
+    rows = _c(rows, np.int64)
+    sel = _c(sel, np.int32)
+    nsel = _c(nsel, np.int32)
+    n = rows.size
+    _, H, D = Q.shape
+    Hkv = K.shape[1]
+    O = np.empty((n, H, D))
+    lse = np.empty((n, H))
+    _load().qsa_oracle_sparse_attn_rows(_p(Q), _p(K), _p(V), pos0, H, Hkv, D, r, sel.shape[1],
+                                        _p(rows), n, _p(sel), _p(nsel), _p(O), _p(lse))
+    return O, lse
+
+
+def select_rows(qi, kbar, rows, pos0: int = 0, Kbudget: int = 512, r: int = 4,
+                mode: int = MODE_MAXHEAD, want_scores: bool = False):
+    """Scores + top-K of rows.  Returns dict(sel, nsel, sK, sK1[, s])."""
+    qi, kbar = (_c(a, np.uint16) for a in (qi, kbar))
+    rows = _c(rows, np.int64)
+    n = rows.size
+    Hi, Di = qi.shape[1], qi.shape[2]
+    nb = kbar.shape[0]
+    s = np.empty((n, nb)) if want_scores else None
+    sel = np.empty((n, Kbudget), dtype=np.int32)
+    nsel = np.empty(n, dtype=np.int32)
+    sK = np.empty(n)
+    sK1 = np.empty(n)
+    _load().qsa_oracle_select_rows(_p(qi), _p(kbar), nb, pos0, Hi, Di, r, Kbudget, mode,
+                                   _p(rows), n, _p(s), nb, _p(sel), _p(nsel), _p(sK), _p(sK1))
+    out = dict(sel=sel, nsel=nsel, sK=sK, sK1=sK1)
+    if want_scores:
+        out["s"] = s
+    return out
+
+
+def dense_rows(Q, K, V, rows, pos0: int = 0):
+    """Dense causal attention of rows: O [n,H,D], lse [n,H]."""
+    Q, K, V = (_c(a, np.uint16) for a in (Q, K, V))
+    rows = _c(rows, np.int64)
+    n = rows.size
+    _, H, D = Q.shape
+    Hkv = K.shape[1]
+    O = np.empty((n, H, D))
+    lse = np.empty((n, H))
+    _load().qsa_oracle_dense_rows(_p(Q), _p(K), _p(V), pos0, H, Hkv, D, _p(rows), n, _p(O),
+                                  _p(lse))
+    return O, lse

@@ -1,0 +1,343 @@
+/*
+ * QSA layer oracle: a plain, slow CPU implementation in fp64.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file: only the tests, the package's smoke check and the CPU
+ * baseline leg of the benchmark do.  It shares no code with the HIP library.
+ *
+ * What it follows (page = "On the Design of Qwen3.8 Next Architecture", the
+ * papers.chlience.com reading notes, section 6 "GDN continuous compression and
+ * QSA exact retrieval", unless stated otherwise):
+ *   - keys are pooled over micro-blocks of r tokens (equation for k-bar_b;
+ *     also the ai.info summary, "Methodology in Plain English");
+ *   - the indexer scores each query against every fully formed micro-block
+ *     (equation for I_ib);
+ *   - at most K/r = 512 complete blocks are selected per query and the
+ *     trailing, not yet complete causal block is always kept; the selected
+ *     blocks expand to token indices for the core attention (same section);
+ *   - head shapes: 24 query heads, 2 KV heads, head dim 256, RoPE on 64 dims;
+ *     indexer 4 query heads, 1 shared key head, dim 128, ratio 4 (Model
+ *     Summary table of the same page).
+ * Readings where the pages are silent (each listed with its reason in the
+ * design notes): NeoX rotate-half pairs (j, j+32) with angle p*theta^(-2j/64);
+ * RoPE output and the pooled key rounded to bf16 (nearest even) as part of the
+ * definition; MAXHEAD score max_h(q_h.kbar)/sqrt(128) as default and the
+ * page's sum of ReLUs as a second mode; RMSNorm mode with unit gain and eps
+ * 1e-6; ties broken by (score descending, block index ascending); query head h
+ * reads KV head h / (H/Hkv); softmax scale 1/sqrt(D).
+ *
+ * bf16 values are passed as uint16 bit patterns.  Everything is computed in
+ * double precision; bf16 inputs convert exactly.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------- bf16 helpers (exact widening, direct nearest-even narrowing) -- */
+
+static double bf16_to_f64(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Round a finite double to bf16 (8 significant bits), ties to even, by
+ * scaling the value to an integer significand and using rint(). */
+static uint16_t f64_to_bf16(double x) {
+    if (x == 0.0) return signbit(x) ? 0x8000 : 0x0000;
+    int e;
+    frexp(x, &e);                    /* |x| = m * 2^e, m in [0.5, 1) */
+    if (e < -125) e = -125;          /* bf16 subnormal range: fixed quantum */
+    double q = ldexp(1.0, e - 8);    /* quantum of an 8-bit significand */
+    double y = rint(x / q) * q;      /* exact scaling; rint = nearest even */
+    float f = (float)y;              /* exact: y has <= 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+uint16_t qsa_oracle_f64_to_bf16(double x) { return f64_to_bf16(x); }
+double qsa_oracle_bf16_to_f64(uint16_t h) { return bf16_to_f64(h); }
+
+/* ---------- O1: partial RoPE on attention Q/K ---------------------------- */
+/* y[t][h][:] = x[t][h][:] with pairs (j, j+rope_dim/2), j < rope_dim/2,
+ * rotated by the angle pos(t) * theta^(-2j/rope_dim); other dims copied.
+ * pos(t) = pos ? pos[t] : pos0 + t.  Output rounded to bf16.  y may equal x. */
+void qsa_oracle_rope(const uint16_t *x, uint16_t *y, int64_t T, int nheads, int head_dim,
+                     int rope_dim, double theta, int64_t pos0, const int64_t *pos) {
+    int half = rope_dim / 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        double p = (double)(pos ? pos[t] : pos0 + t);
+        for (int h = 0; h < nheads; ++h) {
+            const uint16_t *xr = x + (t * nheads + h) * (int64_t)head_dim;
+            uint16_t *yr = y + (t * nheads + h) * (int64_t)head_dim;
+            double a[128], b[128];
+            for (int j = 0; j < half; ++j) {
+                a[j] = bf16_to_f64(xr[j]);
+                b[j] = bf16_to_f64(xr[j + half]);
+            }
+            for (int j = 0; j < half; ++j) {
+                double inv_freq = pow(theta, -2.0 * (double)j / (double)rope_dim);
+                double ang = p * inv_freq;
+                double c = cos(ang), s = sin(ang);
+                yr[j] = f64_to_bf16(a[j] * c - b[j] * s);
+                yr[j + half] = f64_to_bf16(b[j] * c + a[j] * s);
+            }
+            if (yr != xr)
+                for (int d = rope_dim; d < head_dim; ++d) yr[d] = xr[d];
+        }
+    }
+}
+
+/* ---------- O2: key compression ------------------------------------------ */
+/* kbar[b][:] for b < Tk/r: mode 0 = mean of the r keys of block b;
+ * mode 1 = that mean divided by sqrt(mean of its squares + 1e-6) (RMSNorm
+ * with unit gain).  Rounded to bf16. */
+void qsa_oracle_compress(const uint16_t *k, int64_t Tk, int Di, int r, int mode,
+                         uint16_t *kbar) {
+    int64_t nb = Tk / r;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nb; ++b) {
+        double m[1024];
+        for (int d = 0; d < Di; ++d) {
+            double s = 0.0;
+            for (int t = 0; t < r; ++t) s += bf16_to_f64(k[(b * r + t) * Di + d]);
+            m[d] = s / (double)r;
+        }
+        if (mode == 1) {
+            double ss = 0.0;
+            for (int d = 0; d < Di; ++d) ss += m[d] * m[d];
+            double inv = 1.0 / sqrt(ss / (double)Di + 1e-6);
+            for (int d = 0; d < Di; ++d) m[d] *= inv;
+        }
+        for (int d = 0; d < Di; ++d) kbar[b * Di + d] = f64_to_bf16(m[d]);
+    }
+}
+
+/* ---------- O3: indexer scores of one query ------------------------------ */
+/* Number of complete micro-blocks visible to the query at position p. */
+int64_t qsa_oracle_num_complete(int64_t p, int r) { return p < 0 ? 0 : (p + 1) / r; }
+
+/* s[b], b < nc = min(num_complete(p), nb_avail).  mode 0: max over heads of
+ * (q_h . kbar_b) / sqrt(Di); mode 1: sum over heads of max(0, q_h . kbar_b).
+ * Returns nc. */
+int64_t qsa_oracle_scores_row(const uint16_t *qi_row, const uint16_t *kbar, int64_t nb_avail,
+                              int64_t p, int Hi, int Di, int r, int mode, double *s) {
+    int64_t nc = qsa_oracle_num_complete(p, r);
+    if (nc > nb_avail) nc = nb_avail;
+    double q[8][256];
+    for (int h = 0; h < Hi; ++h)
+        for (int d = 0; d < Di; ++d) q[h][d] = bf16_to_f64(qi_row[h * Di + d]);
+    double scale = 1.0 / sqrt((double)Di);
+    for (int64_t b = 0; b < nc; ++b) {
+        const uint16_t *kr = kbar + b * Di;
+        double acc = mode == 0 ? -INFINITY : 0.0;
+        for (int h = 0; h < Hi; ++h) {
+            double dot = 0.0;
+            for (int d = 0; d < Di; ++d) dot += q[h][d] * bf16_to_f64(kr[d]);
+            if (mode == 0) {
+                if (dot > acc) acc = dot;
+            } else {
+                acc += dot > 0.0 ? dot : 0.0;
+            }
+        }
+        s[b] = mode == 0 ? acc * scale : acc;
+    }
+    return nc;
+}
+
+/* ---------- O4: top-K selection of one query ------------------------------ */
+typedef struct { double s; int64_t b; } cand_t;
+
+static int cand_cmp(const void *x, const void *y) {
+    const cand_t *a = (const cand_t *)x, *c = (const cand_t *)y;
+    if (a->s > c->s) return -1;
+    if (a->s < c->s) return 1;
+    return a->b < c->b ? -1 : (a->b > c->b ? 1 : 0);
+}
+
+static int i32_cmp(const void *x, const void *y) {
+    int32_t a = *(const int32_t *)x, b = *(const int32_t *)y;
+    return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+/* Selects min(K, nc) blocks: all of them if nc <= K, else the first K in the
+ * order (score descending, index ascending).  blk gets them ascending.
+ * *sK, *sK1 = scores at ranks K and K+1 of that order (NAN when absent).
+ * Returns the count. */
+int qsa_oracle_topk_row(const double *s, int64_t nc, int K, int32_t *blk, double *sK,
+                        double *sK1) {
+    *sK = NAN;
+    *sK1 = NAN;
+    if (nc <= K) {
+        for (int64_t b = 0; b < nc; ++b) blk[b] = (int32_t)b;
+        if (nc > 0 && nc == K) {
+            /* rank-K score still reported for the tie-band rule */
+            double mn = INFINITY;
+            for (int64_t b = 0; b < nc; ++b) if (s[b] < mn) mn = s[b];
+            *sK = mn;
+        }
+        return (int)nc;
+    }
+    cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)nc);
+    for (int64_t b = 0; b < nc; ++b) { c[b].s = s[b]; c[b].b = b; }
+    qsort(c, (size_t)nc, sizeof(cand_t), cand_cmp);
+    for (int i = 0; i < K; ++i) blk[i] = (int32_t)c[i].b;
+    *sK = c[K - 1].s;
+    *sK1 = c[K].s;
+    free(c);
+    qsort(blk, (size_t)K, sizeof(int32_t), i32_cmp);
+    return K;
+}
+
+/* ---------- O5: token set ----------------------------------------------- */
+/* Tokens of the selected blocks (ascending blocks -> ascending tokens),
+ * followed by the query's incomplete trailing block r*nc .. p (kept always,
+ * later tokens excluded).  Returns the count. */
+int64_t qsa_oracle_token_set(const int32_t *blk, int nsel, int64_t p, int r, int64_t *tok) {
+    int64_t n = 0;
+    for (int i = 0; i < nsel; ++i)
+        for (int t = 0; t < r; ++t) tok[n++] = (int64_t)blk[i] * r + t;
+    int64_t nc = qsa_oracle_num_complete(p, r);
+    for (int64_t j = nc * r; j <= p; ++j) tok[n++] = j;
+    return n;
+}
+
+/* ---------- O6: softmax attention of one query over a token set --------- */
+/* q_row [H][D] (post-RoPE), K/V [*][Hkv][D]; for head h, KV head
+ * g = h / (H/Hkv): logits l_j = q_h.k_{g,j} / sqrt(D); O_h = sum_j w_j v_{g,j}
+ * / sum_j w_j with w_j = exp(l_j - max l); lse_h = max l + ln sum_j w_j.
+ * *max_wsum_err = max over heads of |sum_j w_j/sum w - 1|. */
+void qsa_oracle_attend_row(const uint16_t *q_row, const uint16_t *K, const uint16_t *V, int H,
+                           int Hkv, int D, const int64_t *tok, int64_t ntok, double *O,
+                           double *lse, double *max_wsum_err) {
+    int group = H / Hkv;
+    double scale = 1.0 / sqrt((double)D);
+    double *l = (double *)malloc(sizeof(double) * (size_t)(ntok > 0 ? ntok : 1));
+    double err = 0.0;
+    for (int h = 0; h < H; ++h) {
+        int g = h / group;
+        double q[512];
+        for (int d = 0; d < D; ++d) q[d] = bf16_to_f64(q_row[h * D + d]);
+        double m = -INFINITY;
+        for (int64_t j = 0; j < ntok; ++j) {
+            const uint16_t *kr = K + (tok[j] * Hkv + g) * (int64_t)D;
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d) dot += q[d] * bf16_to_f64(kr[d]);
+            l[j] = dot * scale;
+            if (l[j] > m) m = l[j];
+        }
+        double sw = 0.0;
+        for (int64_t j = 0; j < ntok; ++j) { l[j] = exp(l[j] - m); sw += l[j]; }
+        double *o = O + (int64_t)h * D;
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        double check = 0.0;
+        for (int64_t j = 0; j < ntok; ++j) {
+            double w = l[j] / sw;
+            check += w;
+            const uint16_t *vr = V + (tok[j] * Hkv + g) * (int64_t)D;
+            for (int d = 0; d < D; ++d) o[d] += w * bf16_to_f64(vr[d]);
+        }
+        if (fabs(check - 1.0) > err) err = fabs(check - 1.0);
+        lse[h] = m + log(sw);
+    }
+    if (max_wsum_err) *max_wsum_err = err;
+    free(l);
+}
+
+/* ---------- QSA rows: O3 + O4 + O5 + O6 for a list of query rows -------- */
+/* Inputs of one sequence, all already past RoPE / compression:
+ *   Q [Tq][H][D] rows for positions pos0 + t; K, V [Tk][Hkv][D];
+ *   qi [Tq][Hi][Di]; kbar [nb][Di].
+ * For each rows[i] = t: O [n][H][D], lse [n][H], sel [n][K] (ascending, -1
+ * padded), nsel [n], sK/sK1 [n] (rank-K, rank-K+1 scores), wsum_err [n]. */
+void qsa_oracle_qsa_rows(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                         const uint16_t *qi, const uint16_t *kbar, int64_t nb, int64_t pos0,
+                         int H, int Hkv, int D, int Hi, int Di, int r, int Kbudget, int mode,
+                         const int64_t *rows, int64_t n, double *O, double *lse, int32_t *sel,
+                         int32_t *nsel, double *sK, double *sK1, double *wsum_err) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t t = rows[i];
+        int64_t p = pos0 + t;
+        int64_t nc_full = qsa_oracle_num_complete(p, r);
+        double *s = (double *)malloc(sizeof(double) * (size_t)(nc_full > 0 ? nc_full : 1));
+        int64_t nc = qsa_oracle_scores_row(qi + t * Hi * (int64_t)Di, kbar, nb, p, Hi, Di, r,
+                                           mode, s);
+        int32_t *blk = sel + i * Kbudget;
+        for (int k = 0; k < Kbudget; ++k) blk[k] = -1;
+        int ns = qsa_oracle_topk_row(s, nc, Kbudget, blk, &sK[i], &sK1[i]);
+        nsel[i] = ns;
+        int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)(ns * r + r));
+        int64_t ntok = qsa_oracle_token_set(blk, ns, p, r, tok);
+        qsa_oracle_attend_row(Q + t * H * (int64_t)D, K, V, H, Hkv, D, tok, ntok,
+                              O + i * H * (int64_t)D, lse + i * H, &wsum_err[i]);
+        free(tok);
+        free(s);
+    }
+}
+
+/* Attention rows over a GIVEN selection (e.g. one produced elsewhere and
+ * validated against the tie band): sel [n][Kbudget] ascending, nsel [n]. */
+void qsa_oracle_sparse_attn_rows(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                                 int64_t pos0, int H, int Hkv, int D, int r, int Kbudget,
+                                 const int64_t *rows, int64_t n, const int32_t *sel,
+                                 const int32_t *nsel, double *O, double *lse) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t t = rows[i];
+        int64_t p = pos0 + t;
+        int ns = nsel[i];
+        int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)(ns * r + r));
+        int64_t ntok = qsa_oracle_token_set(sel + i * Kbudget, ns, p, r, tok);
+        double e;
+        qsa_oracle_attend_row(Q + t * H * (int64_t)D, K, V, H, Hkv, D, tok, ntok,
+                              O + i * H * (int64_t)D, lse + i * H, &e);
+        free(tok);
+    }
+}
+
+/* Scores + selection only, for a list of rows: s_out [n][nb_out] (NAN past
+ * nc), sel/nsel/sK/sK1 as in qsa_oracle_qsa_rows.  s_out may be NULL. */
+void qsa_oracle_select_rows(const uint16_t *qi, const uint16_t *kbar, int64_t nb, int64_t pos0,
+                            int Hi, int Di, int r, int Kbudget, int mode, const int64_t *rows,
+                            int64_t n, double *s_out, int64_t nb_out, int32_t *sel,
+                            int32_t *nsel, double *sK, double *sK1) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t t = rows[i];
+        int64_t p = pos0 + t;
+        int64_t nc_full = qsa_oracle_num_complete(p, r);
+        double *s = (double *)malloc(sizeof(double) * (size_t)(nc_full > 0 ? nc_full : 1));
+        int64_t nc = qsa_oracle_scores_row(qi + t * Hi * (int64_t)Di, kbar, nb, p, Hi, Di, r,
+                                           mode, s);
+        if (s_out) {
+            for (int64_t b = 0; b < nb_out; ++b) s_out[i * nb_out + b] = b < nc ? s[b] : NAN;
+        }
+        int32_t *blk = sel + i * Kbudget;
+        for (int k = 0; k < Kbudget; ++k) blk[k] = -1;
+        nsel[i] = qsa_oracle_topk_row(s, nc, Kbudget, blk, &sK[i], &sK1[i]);
+        free(s);
+    }
+}
+
+/* ---------- O7: dense causal attention rows ------------------------------ */
+/* Same as O6 with the token set 0..p, p = pos0 + t. */
+void qsa_oracle_dense_rows(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                           int64_t pos0, int H, int Hkv, int D, const int64_t *rows, int64_t n,
+                           double *O, double *lse) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t t = rows[i];
+        int64_t p = pos0 + t;
+        int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)(p + 1));
+        for (int64_t j = 0; j <= p; ++j) tok[j] = j;
+        double e;
+        qsa_oracle_attend_row(Q + t * H * (int64_t)D, K, V, H, Hkv, D, tok, p + 1,
+                              O + i * H * (int64_t)D, lse + i * H, &e);
+        free(tok);
+    }
+}

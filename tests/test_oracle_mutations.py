@@ -1,0 +1,60 @@
+"""Plant one mistake at a time in a copy of the oracle (on the CPU) and check
+that the pins catch it.  Each mutation is a plausible slip: a sign, a pairing,
+a dropped term or scale, an off-by-one in the block rule, a reversed tie
+break, a wrong head mapping, a swapped operand."""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "qsa_oracle.c")
+
+MUTATIONS = {
+    "rope_sign": ("yr[j] = f64_to_bf16(a[j] * c - b[j] * s);",
+                  "yr[j] = f64_to_bf16(a[j] * c + b[j] * s);"),
+    "rope_pairing": ("b[j] = bf16_to_f64(xr[j + half]);", "b[j] = bf16_to_f64(xr[j + 1]);"),
+    "rope_frequency": ("pow(theta, -2.0 * (double)j / (double)rope_dim)",
+                       "pow(theta, -1.0 * (double)j / (double)rope_dim)"),
+    "compress_drops_token": ("for (int t = 0; t < r; ++t) s += bf16_to_f64",
+                             "for (int t = 1; t < r; ++t) s += bf16_to_f64"),
+    "compress_rms_eps": ("sqrt(ss / (double)Di + 1e-6)", "sqrt(ss + 1e-6)"),
+    "score_scale_dropped": ("s[b] = mode == 0 ? acc * scale : acc;", "s[b] = acc;"),
+    "score_relu_dropped": ("acc += dot > 0.0 ? dot : 0.0;", "acc += dot;"),
+    "complete_block_off_by_one": ("return p < 0 ? 0 : (p + 1) / r;",
+                                  "return p < 0 ? 0 : p / r;"),
+    "tie_break_reversed": ("return a->b < c->b ? -1 : (a->b > c->b ? 1 : 0);",
+                           "return a->b > c->b ? -1 : (a->b < c->b ? 1 : 0);"),
+    "partial_block_dropped": ("for (int64_t j = nc * r; j <= p; ++j) tok[n++] = j;",
+                              "for (int64_t j = nc * r; j < p; ++j) tok[n++] = j;"),
+    "gqa_mapping": ("int g = h / group;", "int g = h % Hkv;"),
+    "softmax_scale": ("double scale = 1.0 / sqrt((double)D);", "double scale = 1.0 / (double)D;"),
+    "value_operand_swapped": ("const uint16_t *vr = V + ", "const uint16_t *vr = K + "),
+    "lse_drops_max": ("lse[h] = m + log(sw);", "lse[h] = log(sw);"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_dir():
+    with tempfile.TemporaryDirectory() as d:
+        yield d
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name, mutant_dir):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    c_path = os.path.join(mutant_dir, f"{name}.c")
+    so_path = os.path.join(mutant_dir, f"{name}.so")
+    with open(c_path, "w") as f:
+        f.write(src.replace(old, new))
+    subprocess.check_call(["gcc", "-O1", "-fPIC", "-shared", "-fopenmp", "-std=c11", "-o",
+                           so_path, c_path, "-lm"])
+    env = dict(os.environ, QSA_ORACLE_LIB=so_path, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutation {name} survived the pins:\n{r.stdout[-2000:]}"
