@@ -1,0 +1,183 @@
+"""Python binding of libqsa, the MI355X (gfx950) QSA layer.
+
+Argument marshalling only: every function here has the name of the C entry
+point it calls (include/qsa.h), takes torch tensors as device memory, passes
+their data pointers and the current HIP stream, and raises QSAError on a
+non-zero status.  All arithmetic runs in the HIP kernels of libqsa.so; there
+is no CPU or PyTorch fallback, and importing fails loudly when the library is
+missing.
+
+bf16 tensors may be torch.bfloat16 or 16-bit integer views of the same bits.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqsa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        "(hipcc --offload-arch=gfx950); the QSA path has no fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i64, _i32, _dbl, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double,
+                              ctypes.c_size_t)
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_lib_status_string = _sig("qsa_status_string", ctypes.c_char_p, _i32)
+_sig("qsa_version", _i32)
+_sig("qsa_check_device", _i32)
+_sig("qsa_rope_bf16", _i32, _vp, _vp, _i64, _i32, _i32, _i32, _dbl, _i64, _vp, _vp)
+_sig("qsa_compress_keys", _i32, _vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _i64, _vp)
+_sig("qsa_index_scores", _i32, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _i32, _i32, _i32, _i32,
+     _vp, _i64, _vp)
+_sig("qsa_topk_workspace_bytes", _sz, _i32, _i64, _i64, _i32)
+_sig("qsa_topk_blocks", _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _vp,
+     _sz, _vp)
+_sig("qsa_select_workspace_bytes", _sz, _i32, _i64, _i64, _i32)
+_sig("qsa_select_blocks", _i32, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _i32, _i32, _i32, _i32,
+     _i32, _vp, _vp, _vp, _sz, _vp)
+_sig("qsa_sparse_attn_prefill", _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
+     _i32, _i32, _vp, _vp, _vp)
+_sig("qsa_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32)
+_sig("qsa_sparse_attn_decode", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
+     _i32, _i32, _vp, _vp, _vp, _sz, _vp)
+_sig("dense_attn_workspace_bytes", _sz, _i32, _i64, _i64, _i32, _i32, _i32)
+_sig("dense_attn", _i32, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _i32, _i32, _vp, _vp,
+     _vp, _sz, _vp)
+
+EXPORTED = ["qsa_status_string", "qsa_version", "qsa_check_device", "qsa_rope_bf16",
+            "qsa_compress_keys", "qsa_index_scores", "qsa_topk_workspace_bytes",
+            "qsa_topk_blocks", "qsa_select_workspace_bytes", "qsa_select_blocks",
+            "qsa_sparse_attn_prefill", "qsa_decode_workspace_bytes", "qsa_sparse_attn_decode",
+            "dense_attn_workspace_bytes", "dense_attn"]
+
+SCORE_MAXHEAD, SCORE_RELUSUM = 0, 1
+KBAR_MEAN, KBAR_RMSNORM = 0, 1
+H, HKV, D, HI, DI, R = 24, 2, 256, 4, 128, 4
+
+
+class QSAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {qsa_status_string(status)}")
+        self.status = status
+
+
+def qsa_status_string(status: int) -> str:
+    return _lib_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _call(name, *args):
+    st = getattr(_lib, name)(*args)
+    if st != 0:
+        raise QSAError(name, st)
+
+
+def qsa_version() -> int:
+    return int(_lib.qsa_version())
+
+
+def qsa_check_device() -> None:
+    st = _lib.qsa_check_device()
+    if st != 0:
+        raise QSAError("qsa_check_device", st)
+
+
+def qsa_rope_bf16(x, y, T: int, nheads: int, head_dim: int, rope_dim: int = 64,
+                  theta: float = 1e7, pos0: int = 0, seq_len=None, stream=None) -> None:
+    _call("qsa_rope_bf16", _ptr(x), _ptr(y), T, nheads, head_dim, rope_dim, theta, pos0,
+          _ptr(seq_len), _stream(stream))
+
+
+def qsa_compress_keys(k, B: int, Tk: int, k_seq_stride: int, Di: int, r: int, kbar_mode: int,
+                      kbar, kbar_seq_stride: int, stream=None) -> None:
+    _call("qsa_compress_keys", _ptr(k), B, Tk, k_seq_stride, Di, r, kbar_mode, _ptr(kbar),
+          kbar_seq_stride, _stream(stream))
+
+
+def qsa_index_scores(q_idx, kbar, B: int, Tq: int, pos0: int, seq_len, nb_max: int, Hi: int,
+                     Di: int, r: int, score_mode: int, scores, ld: int, stream=None) -> None:
+    _call("qsa_index_scores", _ptr(q_idx), _ptr(kbar), B, Tq, pos0, _ptr(seq_len), nb_max, Hi, Di,
+          r, score_mode, _ptr(scores), ld, _stream(stream))
+
+
+def qsa_topk_workspace_bytes(B: int, Tq: int, nb_max: int, K: int) -> int:
+    return int(_lib.qsa_topk_workspace_bytes(B, Tq, nb_max, K))
+
+
+def qsa_topk_blocks(scores, B: int, Tq: int, ld: int, pos0: int, seq_len, nb_max: int, r: int,
+                    K: int, blk_idx, n_sel, ws=None, ws_bytes: int = 0, stream=None) -> None:
+    _call("qsa_topk_blocks", _ptr(scores), B, Tq, ld, pos0, _ptr(seq_len), nb_max, r, K,
+          _ptr(blk_idx), _ptr(n_sel), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def qsa_select_workspace_bytes(B: int, Tq: int, nb_max: int, K: int) -> int:
+    return int(_lib.qsa_select_workspace_bytes(B, Tq, nb_max, K))
+
+
+def qsa_select_blocks(q_idx, kbar, B: int, Tq: int, pos0: int, seq_len, nb_max: int, Hi: int,
+                      Di: int, r: int, score_mode: int, K: int, blk_idx, n_sel, ws,
+                      ws_bytes: int, stream=None) -> None:
+    _call("qsa_select_blocks", _ptr(q_idx), _ptr(kbar), B, Tq, pos0, _ptr(seq_len), nb_max, Hi,
+          Di, r, score_mode, K, _ptr(blk_idx), _ptr(n_sel), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def qsa_sparse_attn_prefill(Q, K, V, blk_idx, n_sel, Tq: int, Tk: int, pos0: int, H: int,
+                            Hkv: int, D: int, r: int, Kbudget: int, O, lse=None,
+                            stream=None) -> None:
+    _call("qsa_sparse_attn_prefill", _ptr(Q), _ptr(K), _ptr(V), _ptr(blk_idx), _ptr(n_sel), Tq,
+          Tk, pos0, H, Hkv, D, r, Kbudget, _ptr(O), _ptr(lse), _stream(stream))
+
+
+def qsa_decode_workspace_bytes(B: int, H: int, Hkv: int, D: int, Kbudget: int) -> int:
+    return int(_lib.qsa_decode_workspace_bytes(B, H, Hkv, D, Kbudget))
+
+
+def qsa_sparse_attn_decode(q, Kc, Vc, seq_len, blk_idx, n_sel, B: int, Lmax: int, H: int,
+                           Hkv: int, D: int, r: int, Kbudget: int, O, lse, ws, ws_bytes: int,
+                           stream=None) -> None:
+    _call("qsa_sparse_attn_decode", _ptr(q), _ptr(Kc), _ptr(Vc), _ptr(seq_len), _ptr(blk_idx),
+          _ptr(n_sel), B, Lmax, H, Hkv, D, r, Kbudget, _ptr(O), _ptr(lse), _ptr(ws), ws_bytes,
+          _stream(stream))
+
+
+def dense_attn_workspace_bytes(B: int, Tq: int, Lmax: int, H: int, Hkv: int, D: int) -> int:
+    return int(_lib.dense_attn_workspace_bytes(B, Tq, Lmax, H, Hkv, D))
+
+
+def dense_attn(Q, K, V, B: int, Tq: int, Lmax: int, pos0: int, seq_len, H: int, Hkv: int, D: int,
+               O, lse=None, ws=None, ws_bytes: int = 0, stream=None) -> None:
+    _call("dense_attn", _ptr(Q), _ptr(K), _ptr(V), B, Tq, Lmax, pos0, _ptr(seq_len), H, Hkv, D,
+          _ptr(O), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream))
+
+
+from .layer import QSAPrefill, QSADecode  # noqa: E402  (chains of the calls above)

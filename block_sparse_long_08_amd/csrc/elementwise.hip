@@ -1,0 +1,161 @@
+// A1 (partial RoPE) and A2 (micro-block key pooling).  Both are HBM-bound
+// streaming kernels; their arithmetic runs in fp64 so that the single bf16
+// rounding at the end sees the exact (MEAN) or correctly rounded value.
+#include "qsa_internal.h"
+
+namespace qsa {
+
+// Round a finite double to bf16 (nearest, ties to even) by integer
+// manipulation of its bits.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+    uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+    uint32_t sign = static_cast<uint32_t>(u >> 63) << 15;
+    int e = static_cast<int>((u >> 52) & 0x7FF) - 1023;
+    if (x == 0.0) return static_cast<uint16_t>(sign);
+    if (e < -126) {
+        // bf16 subnormal range: quantum 2^-133
+        double n = rint(fabs(x) * 0x1p133);
+        return static_cast<uint16_t>(sign | static_cast<uint32_t>(n));
+    }
+    uint64_t mant = u & ((1ull << 52) - 1);
+    uint32_t top = (static_cast<uint32_t>(e + 127) << 7) | static_cast<uint32_t>(mant >> 45);
+    uint64_t rem = mant & ((1ull << 45) - 1);
+    const uint64_t half = 1ull << 44;
+    if (rem > half || (rem == half && (top & 1u))) top += 1;
+    return static_cast<uint16_t>(sign | top);
+}
+
+struct InvFreq {
+    double v[64];
+};
+
+// One workgroup per row t: angles for the row's position are formed once in
+// LDS, then every head's pairs are rotated.
+__global__ void __launch_bounds__(256) rope_kernel(const uint16_t *__restrict__ x,
+                                                   uint16_t *__restrict__ y, int64_t T,
+                                                   int nheads, int head_dim, int rope_dim,
+                                                   InvFreq inv_freq, int64_t pos0,
+                                                   const int64_t *__restrict__ seq_len) {
+#pragma clang fp contract(off)
+    __shared__ double cs[64], sn[64];
+    const int64_t t = blockIdx.x;
+    const int half = rope_dim / 2;
+    int64_t p = seq_len ? seq_len[t] - 1 : pos0 + t;
+    if (p < 0) p = 0;
+    for (int j = threadIdx.x; j < half; j += blockDim.x) {
+        double ang = static_cast<double>(p) * inv_freq.v[j];
+        double s, c;
+        sincos(ang, &s, &c);
+        cs[j] = c;
+        sn[j] = s;
+    }
+    __syncthreads();
+    const uint16_t *xr = x + t * nheads * static_cast<int64_t>(head_dim);
+    uint16_t *yr = y + t * nheads * static_cast<int64_t>(head_dim);
+    for (int idx = threadIdx.x; idx < nheads * half; idx += blockDim.x) {
+        int h = idx / half, j = idx - h * half;
+        const uint16_t *xh = xr + h * head_dim;
+        double a = static_cast<double>(bf16_bits_to_f32(xh[j]));
+        double b = static_cast<double>(bf16_bits_to_f32(xh[j + half]));
+        double c = cs[j], s = sn[j];
+        double ac = a * c, bs = b * s, bc = b * c, as = a * s;
+        uint16_t o0 = f64_to_bf16_rne(ac - bs);
+        uint16_t o1 = f64_to_bf16_rne(bc + as);
+        yr[h * head_dim + j] = o0;
+        yr[h * head_dim + j + half] = o1;
+    }
+    if (y != x) {
+        // copy the untouched dims, 16 bytes at a time (rope_dim % 8 == 0 and
+        // head_dim % 8 == 0 are checked by the caller)
+        const int per_head = (head_dim - rope_dim) / 8;
+        for (int idx = threadIdx.x; idx < nheads * per_head; idx += blockDim.x) {
+            int h = idx / per_head, c = idx - h * per_head;
+            const uint4 *src =
+                reinterpret_cast<const uint4 *>(xr + h * head_dim + rope_dim) + c;
+            uint4 *dst = reinterpret_cast<uint4 *>(yr + h * head_dim + rope_dim) + c;
+            *dst = *src;
+        }
+    }
+}
+
+hipError_t launch_rope(const uint16_t *x, uint16_t *y, int64_t T, int nheads, int head_dim,
+                       int rope_dim, const double *inv_freq, int64_t pos0,
+                       const int64_t *seq_len, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    InvFreq f;
+    for (int j = 0; j < 64; ++j) f.v[j] = j < rope_dim / 2 ? inv_freq[j] : 0.0;
+    hipLaunchKernelGGL(rope_kernel, dim3(static_cast<uint32_t>(T)), dim3(256), 0, s, x, y, T,
+                       nheads, head_dim, rope_dim, f, pos0, seq_len);
+    return hipGetLastError();
+}
+
+// One thread per (sequence, block, 8-dim chunk); the Di/8 threads of a block
+// are consecutive lanes, so the RMSNorm reduction stays inside a wave.
+template <int DI>
+__global__ void __launch_bounds__(256) compress_kernel(const uint16_t *__restrict__ k, int B,
+                                                       int64_t nb, int64_t k_seq_stride, int r,
+                                                       int mode, uint16_t *__restrict__ kbar,
+                                                       int64_t kbar_seq_stride) {
+    constexpr int CH = DI / 8;  // chunks per block row (8, 16 or 32 lanes)
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = static_cast<int64_t>(B) * nb * CH;
+    const bool live = gid < total;
+    const int64_t g = live ? gid : total - 1;
+    const int c = static_cast<int>(g % CH);
+    const int64_t jb = (g / CH) % nb;
+    const int64_t b = g / (CH * nb);
+    const uint16_t *src = k + b * k_seq_stride + (jb * r) * DI + c * 8;
+    double acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+    for (int t = 0; t < r; ++t) {
+        uint4 v = *reinterpret_cast<const uint4 *>(src + t * DI);
+        const uint16_t *h = reinterpret_cast<const uint16_t *>(&v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += static_cast<double>(bf16_bits_to_f32(h[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = acc[i] / static_cast<double>(r);
+    if (mode == 1) {
+        double ss = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += acc[i] * acc[i];
+#pragma unroll
+        for (int off = CH / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, CH);
+        double inv = 1.0 / sqrt(ss / static_cast<double>(DI) + 1e-6);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] *= inv;
+    }
+    if (!live) return;
+    uint16_t out[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = f64_to_bf16_rne(acc[i]);
+    *reinterpret_cast<uint4 *>(kbar + b * kbar_seq_stride + jb * DI + c * 8) =
+        *reinterpret_cast<const uint4 *>(out);
+}
+
+hipError_t launch_compress(const uint16_t *k, int B, int64_t Tk, int64_t k_seq_stride, int Di,
+                           int r, int mode, uint16_t *kbar, int64_t kbar_seq_stride,
+                           hipStream_t s) {
+    const int64_t nb = Tk / r;
+    if (nb == 0 || B == 0) return hipSuccess;
+    const int64_t threads = static_cast<int64_t>(B) * nb * (Di / 8);
+    const dim3 grid(static_cast<uint32_t>((threads + 255) / 256));
+    switch (Di) {
+    case 64:
+        hipLaunchKernelGGL(compress_kernel<64>, grid, dim3(256), 0, s, k, B, nb, k_seq_stride,
+                           r, mode, kbar, kbar_seq_stride);
+        break;
+    case 128:
+        hipLaunchKernelGGL(compress_kernel<128>, grid, dim3(256), 0, s, k, B, nb, k_seq_stride,
+                           r, mode, kbar, kbar_seq_stride);
+        break;
+    default:
+        hipLaunchKernelGGL(compress_kernel<256>, grid, dim3(256), 0, s, k, B, nb, k_seq_stride,
+                           r, mode, kbar, kbar_seq_stride);
+        break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace qsa

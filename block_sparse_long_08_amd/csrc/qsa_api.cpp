@@ -1,0 +1,293 @@
+// C ABI of libqsa: host-side argument checks, workspace sizing and dispatch
+// to the HIP launchers.  Every check runs before the first HIP call, so a
+// rejected call enqueues nothing (and can be tested without a GPU).
+#include <math.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/qsa.h"
+#include "qsa_internal.h"
+
+using namespace qsa;
+
+namespace {
+
+constexpr int64_t kI32Max = 2147483647;
+constexpr int kMaxBudget = 2048;
+constexpr int64_t kSelectChunkBytes = int64_t(1) << 30;  // score workspace per chunk
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int launch_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH; }
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Rows of a prefill score chunk for the fused selection.
+int64_t select_chunk_rows(int64_t Tq, int64_t ld) {
+    int64_t rows = kSelectChunkBytes / (ld * 4);
+    rows = rows / 64 * 64;
+    if (rows < 64) rows = 64;
+    return rows < Tq ? rows : Tq;
+}
+
+int check_attn_shape(int H, int Hkv, int D, int r) {
+    if (H <= 0 || Hkv <= 0 || D <= 0 || r <= 0) return QSA_ERR_SHAPE;
+    if (H % Hkv != 0) return QSA_ERR_SHAPE;
+    if (D != kHeadDim || r != kBlock) return QSA_ERR_UNSUPPORTED;
+    if (H / Hkv > 16 || (Hkv != 1 && Hkv != 2 && Hkv != 4)) return QSA_ERR_UNSUPPORTED;
+    return QSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qsa_status_string(int status) {
+    switch (status) {
+    case QSA_OK: return "QSA_OK";
+    case QSA_ERR_NULL: return "QSA_ERR_NULL: a required pointer is NULL";
+    case QSA_ERR_SHAPE: return "QSA_ERR_SHAPE: a size is out of range or sizes disagree";
+    case QSA_ERR_UNSUPPORTED: return "QSA_ERR_UNSUPPORTED: shape not covered by the tuned kernels";
+    case QSA_ERR_ALIGN: return "QSA_ERR_ALIGN: tensor pointer not 16-byte aligned";
+    case QSA_ERR_OVERFLOW: return "QSA_ERR_OVERFLOW: index range exceeds int32";
+    case QSA_ERR_WORKSPACE: return "QSA_ERR_WORKSPACE: workspace missing or too small";
+    case QSA_ERR_LAUNCH: return "QSA_ERR_LAUNCH: the HIP runtime rejected a launch";
+    case QSA_ERR_DEVICE: return "QSA_ERR_DEVICE: current device is not a gfx950 GPU";
+    default: return "unknown qsa_status";
+    }
+}
+
+int qsa_version(void) { return 100; }
+
+int qsa_check_device(void) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QSA_ERR_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QSA_ERR_DEVICE;
+    return strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? QSA_OK : QSA_ERR_DEVICE;
+}
+
+int qsa_rope_bf16(const qsa_bf16 *x, qsa_bf16 *y, int64_t T, int nheads, int head_dim,
+                  int rope_dim, double theta, int64_t pos0, const int64_t *seq_len,
+                  void *stream) {
+    if (!x || !y) return QSA_ERR_NULL;
+    if (T < 0 || nheads <= 0 || head_dim <= 0 || rope_dim <= 0 || !(theta > 0.0) || pos0 < 0)
+        return QSA_ERR_SHAPE;
+    if (rope_dim > head_dim || (rope_dim & 1)) return QSA_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
+        return QSA_ERR_UNSUPPORTED;
+    if (rope_dim > 128 || (rope_dim % 8) != 0) return QSA_ERR_UNSUPPORTED;
+    if (T > kI32Max) return QSA_ERR_OVERFLOW;
+    if (!aligned16(x) || !aligned16(y)) return QSA_ERR_ALIGN;
+    double inv_freq[64];
+    for (int j = 0; j < rope_dim / 2; ++j)
+        inv_freq[j] = pow(theta, -2.0 * static_cast<double>(j) / static_cast<double>(rope_dim));
+    return launch_status(launch_rope(x, y, T, nheads, head_dim, rope_dim, inv_freq, pos0,
+                                     seq_len, as_stream(stream)));
+}
+
+int qsa_compress_keys(const qsa_bf16 *k, int B, int64_t Tk, int64_t k_seq_stride, int Di, int r,
+                      int kbar_mode, qsa_bf16 *kbar, int64_t kbar_seq_stride, void *stream) {
+    if (!k || !kbar) return QSA_ERR_NULL;
+    if (B <= 0 || Tk < 0 || Di <= 0 || r <= 0) return QSA_ERR_SHAPE;
+    if (kbar_mode != QSA_KBAR_MEAN && kbar_mode != QSA_KBAR_RMSNORM) return QSA_ERR_SHAPE;
+    if (Di != 64 && Di != 128 && Di != 256) return QSA_ERR_UNSUPPORTED;
+    if (r > 16) return QSA_ERR_UNSUPPORTED;
+    const int64_t nb = Tk / r;
+    if (B > 1 && (k_seq_stride < Tk * Di || kbar_seq_stride < nb * Di)) return QSA_ERR_SHAPE;
+    if (k_seq_stride % 8 || kbar_seq_stride % 8) return QSA_ERR_ALIGN;
+    if (static_cast<int64_t>(B) * nb * (Di / 8) / 256 > kI32Max) return QSA_ERR_OVERFLOW;
+    if (!aligned16(k) || !aligned16(kbar)) return QSA_ERR_ALIGN;
+    return launch_status(launch_compress(k, B, Tk, k_seq_stride, Di, r, kbar_mode, kbar,
+                                         kbar_seq_stride, as_stream(stream)));
+}
+
+static int check_index_args(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t Tq,
+                            int64_t pos0, const int64_t *seq_len, int64_t nb_max, int Hi, int Di,
+                            int r, int score_mode) {
+    if (!q_idx || !kbar) return QSA_ERR_NULL;
+    if (B <= 0 || Tq < 0 || nb_max < 0 || pos0 < 0 || Hi <= 0 || Di <= 0 || r <= 0)
+        return QSA_ERR_SHAPE;
+    if (score_mode != QSA_SCORE_MAXHEAD && score_mode != QSA_SCORE_RELUSUM) return QSA_ERR_SHAPE;
+    if (seq_len && Tq != 1) return QSA_ERR_SHAPE;
+    if (Hi != kIdxHeads || Di != kIdxDim || r != kBlock) return QSA_ERR_UNSUPPORTED;
+    if (nb_max > kI32Max || B > 65535) return QSA_ERR_OVERFLOW;
+    if ((Tq + 63) / 64 > kI32Max) return QSA_ERR_OVERFLOW;
+    if (!aligned16(q_idx) || !aligned16(kbar)) return QSA_ERR_ALIGN;
+    return QSA_OK;
+}
+
+int qsa_index_scores(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t Tq,
+                     int64_t pos0, const int64_t *seq_len, int64_t nb_max, int Hi, int Di, int r,
+                     int score_mode, float *scores, int64_t ld, void *stream) {
+    int st = check_index_args(q_idx, kbar, B, Tq, pos0, seq_len, nb_max, Hi, Di, r, score_mode);
+    if (st != QSA_OK) return st;
+    if (!scores) return QSA_ERR_NULL;
+    if (ld < nb_max || ld % 4 != 0) return QSA_ERR_SHAPE;
+    if (!aligned16(scores)) return QSA_ERR_ALIGN;
+    return launch_status(launch_index_scores(q_idx, kbar, B, Tq, pos0, seq_len, nb_max,
+                                             score_mode, scores, ld, as_stream(stream)));
+}
+
+size_t qsa_topk_workspace_bytes(int B, int64_t Tq, int64_t nb_max, int K) {
+    (void)B; (void)Tq; (void)nb_max; (void)K;
+    return 0;
+}
+
+int qsa_topk_blocks(const float *scores, int B, int64_t Tq, int64_t ld, int64_t pos0,
+                    const int64_t *seq_len, int64_t nb_max, int r, int K, int32_t *blk_idx,
+                    int32_t *n_sel, void *ws, size_t ws_bytes, void *stream) {
+    (void)ws; (void)ws_bytes;
+    if (!scores || !blk_idx || !n_sel) return QSA_ERR_NULL;
+    if (B <= 0 || Tq < 0 || nb_max < 0 || pos0 < 0 || r <= 0 || K <= 0) return QSA_ERR_SHAPE;
+    if (seq_len && Tq != 1) return QSA_ERR_SHAPE;
+    if (ld < nb_max) return QSA_ERR_SHAPE;
+    if (K > kMaxBudget) return QSA_ERR_UNSUPPORTED;
+    if (nb_max > kI32Max || static_cast<int64_t>(B) * Tq > kI32Max) return QSA_ERR_OVERFLOW;
+    if (!aligned16(scores)) return QSA_ERR_ALIGN;
+    return launch_status(launch_topk(scores, B, Tq, ld, pos0, seq_len, nb_max, r, K, blk_idx,
+                                     n_sel, as_stream(stream)));
+}
+
+size_t qsa_select_workspace_bytes(int B, int64_t Tq, int64_t nb_max, int K) {
+    (void)K;
+    if (B <= 0 || Tq <= 0 || nb_max <= 0) return 0;
+    const int64_t ld = round_up(nb_max, 4);
+    if (Tq == 1) return static_cast<size_t>(B) * ld * 4;  // decode form: all rows at once
+    return static_cast<size_t>(select_chunk_rows(Tq, ld) * ld * 4);
+}
+
+int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t Tq,
+                      int64_t pos0, const int64_t *seq_len, int64_t nb_max, int Hi, int Di,
+                      int r, int score_mode, int K, int32_t *blk_idx, int32_t *n_sel, void *ws,
+                      size_t ws_bytes, void *stream) {
+    int st = check_index_args(q_idx, kbar, B, Tq, pos0, seq_len, nb_max, Hi, Di, r, score_mode);
+    if (st != QSA_OK) return st;
+    if (!blk_idx || !n_sel) return QSA_ERR_NULL;
+    if (K <= 0) return QSA_ERR_SHAPE;
+    if (K > kMaxBudget) return QSA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(B) * Tq > kI32Max) return QSA_ERR_OVERFLOW;
+    if (Tq == 0 || nb_max == 0) {
+        // no candidates: every row selects nothing
+        if (Tq == 0) return QSA_OK;
+    }
+    const size_t need = qsa_select_workspace_bytes(B, Tq, nb_max, K);
+    if (need > 0 && (!ws || ws_bytes < need)) return QSA_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(ws)) return QSA_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    float *sc = static_cast<float *>(ws);
+    const int64_t ld = round_up(nb_max > 0 ? nb_max : 1, 4);
+    if (seq_len || Tq == 1) {
+        hipError_t e = launch_index_scores(q_idx, kbar, B, Tq, pos0, seq_len, nb_max, score_mode,
+                                           sc, ld, s);
+        if (e != hipSuccess) return QSA_ERR_LAUNCH;
+        return launch_status(launch_topk(sc, B, Tq, ld, pos0, seq_len, nb_max, r, K, blk_idx,
+                                         n_sel, s));
+    }
+    const int64_t chunk = select_chunk_rows(Tq, ld);
+    for (int b = 0; b < B; ++b) {
+        for (int64_t q0 = 0; q0 < Tq; q0 += chunk) {
+            const int64_t len = Tq - q0 < chunk ? Tq - q0 : chunk;
+            const qsa_bf16 *qb = q_idx + (static_cast<int64_t>(b) * Tq + q0) * (kIdxHeads * kIdxDim);
+            const qsa_bf16 *kb = kbar + static_cast<int64_t>(b) * nb_max * kIdxDim;
+            hipError_t e = launch_index_scores(qb, kb, 1, len, pos0 + q0, nullptr, nb_max,
+                                               score_mode, sc, ld, s);
+            if (e != hipSuccess) return QSA_ERR_LAUNCH;
+            const int64_t row0 = static_cast<int64_t>(b) * Tq + q0;
+            e = launch_topk(sc, 1, len, ld, pos0 + q0, nullptr, nb_max, r, K, blk_idx + row0 * K,
+                            n_sel + row0, s);
+            if (e != hipSuccess) return QSA_ERR_LAUNCH;
+        }
+    }
+    return QSA_OK;
+}
+
+int qsa_sparse_attn_prefill(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
+                            const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq, int64_t Tk,
+                            int64_t pos0, int H, int Hkv, int D, int r, int Kbudget, float *O,
+                            float *lse, void *stream) {
+    if (!Q || !K || !V || !blk_idx || !n_sel || !O) return QSA_ERR_NULL;
+    if (Tq < 0 || Tk < 0 || pos0 < 0 || Kbudget <= 0) return QSA_ERR_SHAPE;
+    int st = check_attn_shape(H, Hkv, D, r);
+    if (st != QSA_OK) return st;
+    if (Tk < pos0 + Tq) return QSA_ERR_SHAPE;
+    if (Kbudget > kMaxBudget) return QSA_ERR_UNSUPPORTED;
+    if (Tq > kI32Max || Tk / kBlock > kI32Max) return QSA_ERR_OVERFLOW;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return QSA_ERR_ALIGN;
+    AttnArgs a{};
+    a.Q = Q; a.K = K; a.V = V; a.blk_idx = blk_idx; a.n_sel = n_sel; a.seq_len = nullptr;
+    a.O = O; a.lse = lse; a.part = nullptr;
+    a.Tq = Tq; a.Lmax = Tk; a.pos0 = pos0; a.B = 1; a.H = H; a.Hkv = Hkv; a.Kbudget = Kbudget;
+    return launch_status(launch_sparse_prefill(a, as_stream(stream)));
+}
+
+static size_t decode_ws(int B, int Hkv, int64_t max_entries) {
+    const int nsplit = decode_num_splits(B, Hkv, max_entries);
+    return decode_partial_floats(B, Hkv, nsplit) * sizeof(float);
+}
+
+size_t qsa_decode_workspace_bytes(int B, int H, int Hkv, int D, int Kbudget) {
+    (void)H; (void)D;
+    if (B <= 0 || Hkv <= 0 || Kbudget <= 0) return 0;
+    return decode_ws(B, Hkv, static_cast<int64_t>(Kbudget) + 1);
+}
+
+int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16 *Vc,
+                           const int64_t *seq_len, const int32_t *blk_idx, const int32_t *n_sel,
+                           int B, int64_t Lmax, int H, int Hkv, int D, int r, int Kbudget,
+                           float *O, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    if (!q || !Kc || !Vc || !seq_len || !blk_idx || !n_sel || !O) return QSA_ERR_NULL;
+    if (B <= 0 || Lmax < 0 || Kbudget <= 0) return QSA_ERR_SHAPE;
+    int st = check_attn_shape(H, Hkv, D, r);
+    if (st != QSA_OK) return st;
+    if (Kbudget > kMaxBudget) return QSA_ERR_UNSUPPORTED;
+    if (B > 65535 || Lmax / kBlock > kI32Max) return QSA_ERR_OVERFLOW;
+    if (!aligned16(q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(O)) return QSA_ERR_ALIGN;
+    const size_t need = qsa_decode_workspace_bytes(B, H, Hkv, D, Kbudget);
+    if (!ws || ws_bytes < need) return QSA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QSA_ERR_ALIGN;
+    AttnArgs a{};
+    a.Q = q; a.K = Kc; a.V = Vc; a.blk_idx = blk_idx; a.n_sel = n_sel; a.seq_len = seq_len;
+    a.O = O; a.lse = lse; a.part = static_cast<float *>(ws);
+    a.Tq = 1; a.Lmax = Lmax; a.pos0 = 0; a.B = B; a.H = H; a.Hkv = Hkv; a.Kbudget = Kbudget;
+    const int nsplit = decode_num_splits(B, Hkv, static_cast<int64_t>(Kbudget) + 1);
+    return launch_status(launch_attn_decode(a, nsplit, as_stream(stream)));
+}
+
+size_t dense_attn_workspace_bytes(int B, int64_t Tq, int64_t Lmax, int H, int Hkv, int D) {
+    (void)H; (void)D;
+    if (B <= 0 || Hkv <= 0 || Lmax <= 0) return 0;
+    if (Tq != 1) return 0;  // prefill form needs none
+    return decode_ws(B, Hkv, Lmax / kBlock + 1);
+}
+
+int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, int64_t Tq,
+               int64_t Lmax, int64_t pos0, const int64_t *seq_len, int H, int Hkv, int D,
+               float *O, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    if (!Q || !K || !V || !O) return QSA_ERR_NULL;
+    if (B <= 0 || Tq < 0 || Lmax < 0 || pos0 < 0) return QSA_ERR_SHAPE;
+    int st = check_attn_shape(H, Hkv, D, kBlock);
+    if (st != QSA_OK) return st;
+    if (seq_len && Tq != 1) return QSA_ERR_SHAPE;
+    if (!seq_len && pos0 + Tq > Lmax) return QSA_ERR_SHAPE;
+    if (B > 65535 || Tq > kI32Max || Lmax / kBlock > kI32Max) return QSA_ERR_OVERFLOW;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return QSA_ERR_ALIGN;
+    AttnArgs a{};
+    a.Q = Q; a.K = K; a.V = V; a.blk_idx = nullptr; a.n_sel = nullptr; a.seq_len = seq_len;
+    a.O = O; a.lse = lse; a.part = static_cast<float *>(ws);
+    a.Tq = Tq; a.Lmax = Lmax; a.pos0 = pos0; a.B = B; a.H = H; a.Hkv = Hkv; a.Kbudget = 0;
+    hipStream_t s = as_stream(stream);
+    if (seq_len) {
+        const size_t need = dense_attn_workspace_bytes(B, Tq, Lmax, H, Hkv, D);
+        if (!ws || ws_bytes < need) return QSA_ERR_WORKSPACE;
+        if (!aligned16(ws)) return QSA_ERR_ALIGN;
+        const int nsplit = decode_num_splits(B, Hkv, Lmax / kBlock + 1);
+        return launch_status(launch_attn_decode(a, nsplit, s));
+    }
+    return launch_status(launch_dense_prefill(a, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Internal declarations shared by the HIP translation units of libqsa.
+// Launchers are called by qsa_api.cpp after host-side argument checks; they
+// only enqueue kernels and return the HIP launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+// ---------------------------------------------------------------- types --
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// Tuned shapes.
+constexpr int kHeadDim = 256;   // attention head dim
+constexpr int kIdxHeads = 4;    // indexer query heads
+constexpr int kIdxDim = 128;    // indexer head dim
+constexpr int kBlock = 4;       // micro-block size r
+
+// ------------------------------------------------------- device helpers --
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Complete blocks visible to a query at position p: floor((p+1)/r).
+__host__ __device__ __forceinline__ int64_t num_complete_blocks(int64_t p, int r) {
+    return p < 0 ? 0 : (p + 1) / r;
+}
+
+// Order-preserving map of a finite fp32 to uint32 (larger float -> larger
+// key); -0.0 maps to the key of +0.0 so that equal values compare equal.
+__device__ __forceinline__ uint32_t score_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ------------------------------------------------------------ launchers --
+hipError_t launch_rope(const uint16_t *x, uint16_t *y, int64_t T, int nheads, int head_dim,
+                       int rope_dim, const double *inv_freq, int64_t pos0,
+                       const int64_t *seq_len, hipStream_t s);
+
+hipError_t launch_compress(const uint16_t *k, int B, int64_t Tk, int64_t k_seq_stride, int Di,
+                           int r, int mode, uint16_t *kbar, int64_t kbar_seq_stride,
+                           hipStream_t s);
+
+hipError_t launch_index_scores(const uint16_t *q_idx, const uint16_t *kbar, int B, int64_t Tq,
+                               int64_t pos0, const int64_t *seq_len, int64_t nb_max, int mode,
+                               float *scores, int64_t ld, hipStream_t s);
+
+hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64_t pos0,
+                       const int64_t *seq_len, int64_t nb_max, int r, int K, int32_t *blk_idx,
+                       int32_t *n_sel, hipStream_t s);
+
+// Sparse / dense attention over 4-token blocks (see attention.hip).
+struct AttnArgs {
+    const uint16_t *Q;       // [B][Tq][H][D]
+    const uint16_t *K;       // [B][Lmax][Hkv][D]
+    const uint16_t *V;
+    const int32_t *blk_idx;  // [B][Tq][Kbudget] or nullptr (dense: every complete block)
+    const int32_t *n_sel;    // [B][Tq] or nullptr
+    const int64_t *seq_len;  // decode form: [B]; prefill form: nullptr
+    float *O;                // [B][Tq][H][D]
+    float *lse;              // [B][Tq][H] or nullptr
+    float *part;             // split partials (decode), or nullptr
+    int64_t Tq, Lmax, pos0;
+    int B, H, Hkv, Kbudget;
+};
+
+hipError_t launch_sparse_prefill(const AttnArgs &a, hipStream_t s);
+size_t decode_partial_floats(int B, int Hkv, int nsplit);
+int decode_num_splits(int B, int Hkv, int64_t max_entries);
+hipError_t launch_attn_decode(const AttnArgs &a, int nsplit, hipStream_t s);
+hipError_t launch_dense_prefill(const AttnArgs &a, hipStream_t s);
+
+}  // namespace qsa

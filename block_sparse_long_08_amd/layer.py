@@ -1,0 +1,113 @@
+"""The QSA layer's two hot paths as chains of C-ABI calls.
+
+Each class owns its outputs and workspaces (torch device memory, allocated
+once) and enqueues the steps of the method on the current stream:
+
+prefill (chlience section 6): A1 RoPE on Q (and on K for a fresh context),
+A2 pooling of the indexer keys, A3+A4 block scores and top-K selection,
+A5+A6 sparse attention over the selected blocks plus the trailing block;
+decode: A1 on the new query, optional A2 of a block the new token completes,
+A3+A4 over the pooled-key cache, A7 split-K sparse attention.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (DI, HI, R, SCORE_MAXHEAD, KBAR_MEAN, qsa_compress_keys, qsa_decode_workspace_bytes,
+               qsa_rope_bf16, qsa_select_blocks, qsa_select_workspace_bytes,
+               qsa_sparse_attn_decode, qsa_sparse_attn_prefill)
+
+
+class QSAPrefill:
+    """Prefill of Tq queries at positions pos0 .. pos0+Tq-1 of one sequence.
+
+    fresh=True: K is raw and rotated here, and the whole indexer-key input
+    is pooled.  fresh=False: K is a post-RoPE cache and only the chunk's own
+    indexer keys (positions pos0 ..) are pooled into the caller's kbar cache
+    (pos0 must then be a multiple of r).
+    """
+
+    def __init__(self, Tq: int, pos0: int = 0, H: int = 24, Hkv: int = 2, D: int = 256,
+                 budget: int = 512, score_mode: int = SCORE_MAXHEAD, kbar_mode: int = KBAR_MEAN,
+                 theta: float = 1e7, rope_dim: int = 64, fresh: bool = True, device="cuda"):
+        self.Tq, self.pos0, self.H, self.Hkv, self.D = Tq, pos0, H, Hkv, D
+        self.Tk = pos0 + Tq
+        self.budget, self.score_mode, self.kbar_mode = budget, score_mode, kbar_mode
+        self.theta, self.rope_dim, self.fresh = theta, rope_dim, fresh
+        self.nb = self.Tk // R
+        dev = torch.device(device)
+        self.Qr = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=dev)
+        self.Kr = torch.empty((self.Tk, Hkv, D), dtype=torch.bfloat16, device=dev) if fresh else None
+        self.kbar = torch.empty((max(self.nb, 1), DI), dtype=torch.bfloat16, device=dev) if fresh else None
+        self.blk_idx = torch.empty((Tq, budget), dtype=torch.int32, device=dev)
+        self.n_sel = torch.empty((Tq,), dtype=torch.int32, device=dev)
+        self.O = torch.empty((Tq, H, D), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
+        self.ws_bytes = qsa_select_workspace_bytes(1, Tq, self.nb, budget)
+        self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=dev)
+
+    def rope_and_pool(self, Q, K, ki, kbar=None):
+        qsa_rope_bf16(Q, self.Qr, self.Tq, self.H, self.D, self.rope_dim, self.theta, self.pos0)
+        if self.fresh:
+            qsa_rope_bf16(K, self.Kr, self.Tk, self.Hkv, self.D, self.rope_dim, self.theta, 0)
+            qsa_compress_keys(ki, 1, self.Tk, self.Tk * DI, DI, R, self.kbar_mode, self.kbar,
+                              self.nb * DI)
+            return self.Kr, self.kbar
+        # pool the chunk's own keys into the cache (blocks pos0/r ..)
+        b0 = self.pos0 // R
+        qsa_compress_keys(ki[self.pos0:], 1, self.Tq, self.Tq * DI, DI, R, self.kbar_mode,
+                          kbar[b0:], self.Tq // R * DI)
+        return K, kbar
+
+    def select(self, qi, kbar):
+        qsa_select_blocks(qi, kbar, 1, self.Tq, self.pos0, None, self.nb, HI, DI, R,
+                          self.score_mode, self.budget, self.blk_idx, self.n_sel, self.ws,
+                          self.ws_bytes)
+
+    def attend(self, Kr, V):
+        qsa_sparse_attn_prefill(self.Qr, Kr, V, self.blk_idx, self.n_sel, self.Tq, self.Tk,
+                                self.pos0, self.H, self.Hkv, self.D, R, self.budget, self.O,
+                                self.lse)
+
+    def __call__(self, Q, K, V, qi, ki, kbar=None):
+        Kr, kb = self.rope_and_pool(Q, K, ki, kbar)
+        self.select(qi, kb)
+        self.attend(Kr, V)
+        return self.O, self.lse
+
+
+class QSADecode:
+    """One decode step for B sequences (query at seq_len[b]-1) over caches
+    Kc/Vc [B, Lmax, Hkv, D] (post-RoPE) and kbar [B, Lmax/r, DI]."""
+
+    def __init__(self, B: int, Lmax: int, H: int = 24, Hkv: int = 2, D: int = 256,
+                 budget: int = 512, score_mode: int = SCORE_MAXHEAD, kbar_mode: int = KBAR_MEAN,
+                 theta: float = 1e7, rope_dim: int = 64, device="cuda"):
+        self.B, self.Lmax, self.H, self.Hkv, self.D = B, Lmax, H, Hkv, D
+        self.budget, self.score_mode, self.kbar_mode = budget, score_mode, kbar_mode
+        self.theta, self.rope_dim = theta, rope_dim
+        self.nb_max = Lmax // R
+        dev = torch.device(device)
+        self.qr = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+        self.blk_idx = torch.empty((B, budget), dtype=torch.int32, device=dev)
+        self.n_sel = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.O = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        self.sel_ws_bytes = qsa_select_workspace_bytes(B, 1, self.nb_max, budget)
+        self.sel_ws = torch.empty((max(self.sel_ws_bytes, 16),), dtype=torch.uint8, device=dev)
+        self.dec_ws_bytes = qsa_decode_workspace_bytes(B, H, Hkv, D, budget)
+        self.dec_ws = torch.empty((max(self.dec_ws_bytes, 16),), dtype=torch.uint8, device=dev)
+
+    def append_block(self, ki_tail, kbar, block: int):
+        """Pool the r indexer keys ki_tail [B, r, DI] into kbar[:, block]."""
+        qsa_compress_keys(ki_tail, self.B, R, R * DI, DI, R, self.kbar_mode, kbar[:, block],
+                          self.nb_max * DI)
+
+    def __call__(self, q, qi, Kc, Vc, kbar, seq_len):
+        qsa_rope_bf16(q, self.qr, self.B, self.H, self.D, self.rope_dim, self.theta, 0, seq_len)
+        qsa_select_blocks(qi, kbar, self.B, 1, 0, seq_len, self.nb_max, HI, DI, R, self.score_mode,
+                          self.budget, self.blk_idx, self.n_sel, self.sel_ws, self.sel_ws_bytes)
+        qsa_sparse_attn_decode(self.qr, Kc, Vc, seq_len, self.blk_idx, self.n_sel, self.B,
+                               self.Lmax, self.H, self.Hkv, self.D, R, self.budget, self.O,
+                               self.lse, self.dec_ws, self.dec_ws_bytes)
+        return self.O, self.lse

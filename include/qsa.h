@@ -1,0 +1,182 @@
+/*
+ * qsa.h — C ABI of the MI355X (gfx950) Qwen Sparse Attention (QSA) layer.
+ *
+ * The layer is the one described on the papers.chlience.com reading notes of
+ * "On the Design of Qwen3.8 Next Architecture" (section 6, "GDN continuous
+ * compression and QSA exact retrieval"; Model Summary table) and summarised on
+ * the ai.info page ("Methodology in Plain English", Key Contribution 3):
+ *   keys are pooled over micro-blocks of r = 4 tokens; a multi-query indexer
+ *   (4 query heads, one shared key head, dim 128) scores every fully formed
+ *   block for each query; at most 512 blocks (2048 tokens) are kept per query
+ *   together with the query's incomplete trailing block; softmax attention
+ *   (24 query heads, 2 KV heads, dim 256, RoPE on 64 dims) runs over the
+ *   kept tokens only.
+ *
+ * Conventions for every entry point:
+ *   - bf16 tensors are raw bit patterns (qsa_bf16), row-major, contiguous in
+ *     the layouts given below, 16-byte aligned.  All tensor pointers are
+ *     DEVICE pointers owned by the caller; the library never allocates,
+ *     frees, synchronises or prints.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work; outputs are valid once the stream reaches that point.
+ *     Inputs must not be modified before then.
+ *   - Positions: in prefill form (`seq_len == NULL`) query t of every
+ *     sequence sits at absolute position pos0 + t.  In decode form
+ *     (`seq_len` = device int64 [B], Tq == 1) the query of sequence b sits at
+ *     seq_len[b] - 1 and its cache holds seq_len[b] tokens.  Device-side
+ *     lengths are not visible to the host: the kernels clamp them to the
+ *     allocated sizes (a length above Lmax acts as Lmax, a length < 1 gives an
+ *     empty context), so no access leaves the buffers.
+ *   - A query at position p sees nc(p) = floor((p+1)/r) complete blocks; its
+ *     incomplete block holds tokens r*nc(p) .. p ((p+1) mod r tokens).
+ *   - Arguments are checked on the host before any HIP call; the first failed
+ *     check's status is returned and nothing is enqueued.  QSA_ERR_LAUNCH is
+ *     returned when a launch is rejected; faults inside kernels surface at the
+ *     caller's next synchronisation.  Inputs are assumed finite.
+ *   - Supported shapes: head_dim 256 with at most 16 query heads per KV head
+ *     for attention; indexer 4 heads x 128; r = 4 wherever blocks are read by
+ *     attention or the indexer.  Other shapes return QSA_ERR_UNSUPPORTED:
+ *     there is no slow fallback.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t qsa_bf16;
+
+typedef enum {
+    QSA_OK = 0,
+    QSA_ERR_NULL = 1,        /* a required pointer is NULL */
+    QSA_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree */
+    QSA_ERR_UNSUPPORTED = 3, /* a shape the tuned kernels do not cover */
+    QSA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
+    QSA_ERR_OVERFLOW = 5,    /* a block index would not fit in int32 */
+    QSA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
+    QSA_ERR_LAUNCH = 7,      /* the HIP runtime rejected a launch */
+    QSA_ERR_DEVICE = 8       /* the current device is not a gfx950 GPU */
+} qsa_status;
+
+/* Indexer head combination.
+ * MAXHEAD: s = max over heads of <q_h, kbar_b> / sqrt(Di) (default).
+ * RELUSUM: s = sum over heads of max(0, <q_h, kbar_b>) (the indexer equation
+ *          I_ib of section 6 of the chlience notes). */
+typedef enum { QSA_SCORE_MAXHEAD = 0, QSA_SCORE_RELUSUM = 1 } qsa_score_mode;
+
+/* Pooled key.
+ * MEAN:    kbar_b = mean of the r keys of block b (average pooling, ai.info
+ *          "Methodology in Plain English"; default).
+ * RMSNORM: kbar_b = RMSNorm(mean) with unit gain and eps 1e-6 (the k-bar
+ *          equation of section 6 of the chlience notes).
+ * Either result is rounded to bf16, nearest even. */
+typedef enum { QSA_KBAR_MEAN = 0, QSA_KBAR_RMSNORM = 1 } qsa_kbar_mode;
+
+/* Human-readable name of a status code (static string). */
+const char *qsa_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int qsa_version(void);
+
+/* QSA_OK if the current HIP device is a gfx950 (MI355X-class) GPU. */
+int qsa_check_device(void);
+
+/* ---- A1: partial rotary embedding (Model Summary table: RoPE dimension 64).
+ * y[t][h][:] = x[t][h][:] with each pair (j, j + rope_dim/2), j < rope_dim/2,
+ * rotated counter-clockwise by the angle pos(t) * theta^(-2j/rope_dim)
+ * (angles and products in fp64), the result rounded to bf16 (nearest even);
+ * dims >= rope_dim are copied.  x, y: [T][nheads][head_dim]; y may equal x.
+ * pos(t) = pos0 + t, or seq_len[t] - 1 when seq_len (device int64 [T]) is
+ * given (one decode query per sequence).
+ * Supported: head_dim in {64,128,256,512}, even rope_dim <= min(head_dim, 128). */
+int qsa_rope_bf16(const qsa_bf16 *x, qsa_bf16 *y, int64_t T, int nheads, int head_dim,
+                  int rope_dim, double theta, int64_t pos0, const int64_t *seq_len,
+                  void *stream);
+
+/* ---- A2: key compression (chlience section 6, k-bar equation).
+ * For each sequence b < B and block j < Tk / r:
+ *   kbar[b*kbar_seq_stride + j*Di + :] = pool(k[b*k_seq_stride + (j*r + t)*Di + :], t < r)
+ * Sums are formed in fp64 in token order, so MEAN mode is exact before the
+ * single bf16 rounding.  Strides are in elements; Tk % r tokens at the end
+ * are ignored.  Supported: Di in {64,128,256}, 1 <= r <= 16. */
+int qsa_compress_keys(const qsa_bf16 *k, int B, int64_t Tk, int64_t k_seq_stride, int Di, int r,
+                      int kbar_mode, qsa_bf16 *kbar, int64_t kbar_seq_stride, void *stream);
+
+/* ---- A3: indexer block scores (chlience section 6, I_ib; ai.info
+ * contribution 3: MQA indexer, 4 query heads and one shared key head).
+ * q_idx: [B][Tq][Hi][Di]; kbar: [B][nb_max][Di]; scores: fp32 [B][Tq][ld].
+ * scores[b][t][j] for j < nc = min(nc(p), nb_max) holds the block score of
+ * query t against pooled block j.  Entries j >= nc may be left untouched or
+ * set to -inf (callers read only j < nc).
+ * Prefill form: positions pos0 + t; decode form: see conventions.
+ * Supported: Hi = 4, Di = 128, r = 4, ld >= nb_max, ld % 4 == 0. */
+int qsa_index_scores(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t Tq,
+                     int64_t pos0, const int64_t *seq_len, int64_t nb_max, int Hi, int Di, int r,
+                     int score_mode, float *scores, int64_t ld, void *stream);
+
+/* ---- A4: per-query top-K block selection (chlience section 6: at most 512
+ * complete blocks per query; djimit pillar 2: up to 512 full blocks).
+ * If nc <= K all nc blocks are taken, else the K largest scores, ties broken
+ * by lower block index.  blk_idx: int32 [B][Tq][K], ascending, padded with -1;
+ * n_sel: int32 [B][Tq] = min(K, nc).  scores as produced by qsa_index_scores.
+ * Workspace: qsa_topk_workspace_bytes (may be 0; ws may then be NULL).
+ * Supported: 1 <= K <= 2048. */
+size_t qsa_topk_workspace_bytes(int B, int64_t Tq, int64_t nb_max, int K);
+int qsa_topk_blocks(const float *scores, int B, int64_t Tq, int64_t ld, int64_t pos0,
+                    const int64_t *seq_len, int64_t nb_max, int r, int K, int32_t *blk_idx,
+                    int32_t *n_sel, void *ws, size_t ws_bytes, void *stream);
+
+/* ---- A3 + A4 without a caller-visible score matrix: same result as
+ * qsa_index_scores followed by qsa_topk_blocks.  Scores live in the
+ * caller's workspace (qsa_select_workspace_bytes), one query chunk at a
+ * time, so the workspace stays bounded at any Tq. */
+size_t qsa_select_workspace_bytes(int B, int64_t Tq, int64_t nb_max, int K);
+int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t Tq,
+                      int64_t pos0, const int64_t *seq_len, int64_t nb_max, int Hi, int Di,
+                      int r, int score_mode, int K, int32_t *blk_idx, int32_t *n_sel, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* ---- A5 + A6: sparse attention, prefill (chlience section 6: the selected
+ * blocks expand to token indices for the core attention; the incomplete
+ * trailing block is always kept).  One sequence.
+ * Q: [Tq][H][D] post-RoPE, queries at pos0 .. pos0+Tq-1;
+ * K, V: [Tk][Hkv][D] post-RoPE keys, Tk >= pos0 + Tq;
+ * blk_idx/n_sel as from qsa_topk_blocks (entries must be < nc of the row);
+ * O: fp32 [Tq][H][D];  lse: fp32 [Tq][H] natural-log sum of exp of the
+ * scaled logits, or NULL.  Query head h reads KV head h / (H / Hkv); logits
+ * are q.k / sqrt(D).  Supported: D = 256, H % Hkv == 0, H / Hkv <= 16, r = 4. */
+int qsa_sparse_attn_prefill(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
+                            const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq, int64_t Tk,
+                            int64_t pos0, int H, int Hkv, int D, int r, int Kbudget, float *O,
+                            float *lse, void *stream);
+
+/* ---- A7: sparse attention, decode (one query per sequence at seq_len-1).
+ * q: [B][H][D] post-RoPE; Kc, Vc: [B][Lmax][Hkv][D]; seq_len: device int64 [B];
+ * blk_idx: [B][Kbudget]; n_sel: [B]; O: fp32 [B][H][D]; lse: fp32 [B][H] or NULL.
+ * Workspace: qsa_decode_workspace_bytes (split partial results). */
+size_t qsa_decode_workspace_bytes(int B, int H, int Hkv, int D, int Kbudget);
+int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16 *Vc,
+                           const int64_t *seq_len, const int32_t *blk_idx, const int32_t *n_sel,
+                           int B, int64_t Lmax, int H, int Hkv, int D, int r, int Kbudget,
+                           float *O, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* ---- A8: dense causal attention (the pages' baseline in the chlience
+ * Result 2 kernel measurement), same precision contract as the sparse path.
+ * Q: [B][Tq][H][D]; K, V: [B][Lmax][Hkv][D]; O: fp32 [B][Tq][H][D];
+ * lse: fp32 [B][Tq][H] or NULL.  Prefill form: query t attends keys
+ * 0 .. pos0 + t (pos0 + Tq <= Lmax); decode form: Tq == 1, keys
+ * 0 .. seq_len[b] - 1.  Workspace: dense_attn_workspace_bytes. */
+size_t dense_attn_workspace_bytes(int B, int64_t Tq, int64_t Lmax, int H, int Hkv, int D);
+int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, int64_t Tq,
+               int64_t Lmax, int64_t pos0, const int64_t *seq_len, int H, int Hkv, int D,
+               float *O, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

@@ -1,0 +1,264 @@
+"""Stage-wise parity of the HIP path against the fp64 oracle (small sizes that
+span several tiles and a ragged tail)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import assert_close, check_selection, dev, host_u16, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qsa():
+    import torch
+    import block_sparse_long_08_amd as q
+    assert torch.cuda.is_available()
+    q.qsa_check_device()
+    return q
+
+
+def _torch():
+    import torch
+    return torch
+
+
+# ------------------------------------------------------------------ A1 RoPE
+@pytest.mark.parametrize("T,pos0", [(1029, 0), (257, 1040384)])
+def test_rope_parity(qsa, T, pos0):
+    torch = _torch()
+    log(f"rope T={T} pos0={pos0}")
+    x = synth.normal_bf16(1, (T, 24, 256), seed=3)
+    y = torch.empty((T, 24, 256), dtype=torch.int16, device="cuda")
+    qsa.qsa_rope_bf16(dev(x), y, T, 24, 256, 64, 1e7, pos0)
+    torch.cuda.synchronize()
+    got = host_u16(y)
+    ref = oracle.rope(x, pos0=pos0)
+    mism = int((got != ref).sum())
+    log(f"  bf16 mismatches {mism} of {got.size}")
+    # both sides round the fp64 rotation to bf16 once: allow a 1-ulp flip
+    diff = np.abs(got.astype(np.int32) - ref.astype(np.int32))
+    assert diff.max() <= 1 and mism <= got.size * 1e-6
+
+
+def test_rope_in_place_and_decode_form(qsa):
+    torch = _torch()
+    B = 5
+    x = synth.normal_bf16(1, (B, 24, 256), seed=4)
+    lens = np.array([1, 2, 4099, 262144, 1048576], dtype=np.int64)
+    t = dev(x)
+    qsa.qsa_rope_bf16(t, t, B, 24, 256, 64, 1e7, 0, dev(lens))
+    torch.cuda.synchronize()
+    got = host_u16(t)
+    ref = oracle.rope(x, pos=lens - 1)
+    assert np.abs(got.astype(np.int32) - ref.astype(np.int32)).max() <= 1
+
+
+# -------------------------------------------------------------- A2 compress
+@pytest.mark.parametrize("mode", [0, 1])
+def test_compress_parity(qsa, mode):
+    torch = _torch()
+    B, Tk = 3, 4 * 1000 + 3
+    k = synth.normal_bf16(5, (B, Tk, 128), seed=6)
+    nb = Tk // 4
+    out = torch.zeros((B, nb + 5, 128), dtype=torch.int16, device="cuda")
+    qsa.qsa_compress_keys(dev(k), B, Tk, Tk * 128, 128, 4, mode, out, (nb + 5) * 128)
+    torch.cuda.synchronize()
+    got = host_u16(out)[:, :nb]
+    for b in range(B):
+        ref = oracle.compress(k[b], mode=mode)
+        if mode == 0:
+            assert np.array_equal(got[b], ref), "MEAN pooling must be bit-exact"
+        else:
+            assert np.abs(got[b].astype(np.int32) - ref.astype(np.int32)).max() <= 1
+    assert np.all(host_u16(out)[:, nb:] == 0), "wrote past the complete blocks"
+
+
+# ---------------------------------------------------------- A3 index scores
+def _score_tol(qi_rows, kb, mode):
+    """|fp32 - fp64| bound: 1e-5 * sum of |terms| (per row, max over blocks)."""
+    q = synth.bf16_to_f32(qi_rows).astype(np.float64)   # [n, 4, 128]
+    k = synth.bf16_to_f32(kb).astype(np.float64)        # [nb, 128]
+    mag = np.abs(q) @ np.abs(k).T                        # [n, 4, nb]
+    if mode == 0:
+        return 1e-5 * mag.max(axis=1) / np.sqrt(128) + 1e-30
+    return 1e-5 * mag.sum(axis=1) + 1e-30
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("Tq,pos0", [(2048, 0), (333, 4101)])
+def test_index_scores_parity(qsa, mode, Tq, pos0):
+    torch = _torch()
+    log(f"index scores Tq={Tq} pos0={pos0} mode={mode}")
+    Tk = pos0 + Tq
+    qi = synth.normal_bf16(4, (Tq, 4, 128), seed=7)
+    ki = synth.normal_bf16(5, (Tk, 128), seed=7)
+    kb = oracle.compress(ki)
+    nb = kb.shape[0]
+    ld = (nb + 3) // 4 * 4
+    sc = torch.full((Tq, ld), float("nan"), dtype=torch.float32, device="cuda")
+    qsa.qsa_index_scores(dev(qi), dev(kb), 1, Tq, pos0, None, nb, 4, 128, 4, mode, sc, ld)
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy()
+    rows = np.unique(np.concatenate([np.arange(0, Tq, 7), [Tq - 1]]))
+    ref = oracle.select_rows(qi, kb, rows, pos0=pos0, Kbudget=64, mode=mode, want_scores=True)
+    tol = _score_tol(qi[rows], kb, mode)
+    worst = 0.0
+    for i, t in enumerate(rows):
+        nc = min((pos0 + t + 1) // 4, nb)
+        d = np.abs(got[t, :nc] - ref["s"][i, :nc])
+        assert np.all(d <= tol[i, :nc]), (t, float(d.max()))
+        worst = max(worst, float((d / tol[i, :nc]).max()) if nc else 0.0)
+    log(f"  worst |err|/bound = {worst:.3f}")
+
+
+# ------------------------------------------------------------------ A4 top-K
+@pytest.mark.parametrize("K", [1, 3, 64, 512])
+def test_topk_exact_on_shared_scores(qsa, K):
+    """Given the same fp32 scores, the GPU selection equals the oracle's
+    (score desc, index asc) top-K exactly, ties included."""
+    torch = _torch()
+    Tq, pos0 = 300, 3000
+    nb = (pos0 + Tq) // 4
+    rng = np.random.default_rng(K)
+    s = rng.standard_normal((Tq, nb)).astype(np.float32)
+    s[::3] = np.round(s[::3] * 4) / 4           # heavy ties on every third row
+    s[5] = 0.0                                   # an all-tie row
+    s[7, ::2] = -0.0                             # signed zeros compare equal
+    s[7, 1::2] = 0.0
+    blk = torch.empty((Tq, K), dtype=torch.int32, device="cuda")
+    ns = torch.empty((Tq,), dtype=torch.int32, device="cuda")
+    qsa.qsa_topk_blocks(dev(s), 1, Tq, nb, pos0, None, nb, 4, K, blk, ns)
+    torch.cuda.synchronize()
+    g, n = blk.cpu().numpy(), ns.cpu().numpy()
+    for t in range(Tq):
+        nc = (pos0 + t + 1) // 4
+        row = s[t, :nc].astype(np.float64)
+        row[row == 0] = 0.0
+        want, _, _ = oracle.topk_row(row, K)
+        assert n[t] == want.size
+        assert np.array_equal(g[t, :n[t]], want), t
+        assert np.all(g[t, n[t]:] == -1)
+
+
+def test_topk_decode_form_and_small_contexts(qsa):
+    torch = _torch()
+    B, nb_max, K = 6, 5000, 512
+    lens = np.array([1, 3, 4, 2049, 2052, 20000], dtype=np.int64)
+    s = np.random.default_rng(9).standard_normal((B, nb_max)).astype(np.float32)
+    blk = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    ns = torch.empty((B,), dtype=torch.int32, device="cuda")
+    qsa.qsa_topk_blocks(dev(s), B, 1, nb_max, 0, dev(lens), nb_max, 4, K, blk, ns)
+    torch.cuda.synchronize()
+    g, n = blk.cpu().numpy(), ns.cpu().numpy()
+    for b in range(B):
+        nc = min(int(lens[b]) // 4, nb_max)
+        want, _, _ = oracle.topk_row(s[b, :nc].astype(np.float64), K)
+        assert n[b] == want.size and np.array_equal(g[b, :n[b]], want)
+
+
+# --------------------------------------------------- A3+A4 vs fp64 scores
+@pytest.mark.parametrize("mode", [0, 1])
+def test_selection_tie_band(qsa, mode):
+    torch = _torch()
+    Tq, pos0, K = 512, 8192, 512
+    Tk = pos0 + Tq
+    qi = synth.normal_bf16(4, (Tq, 4, 128), seed=8)
+    ki = synth.normal_bf16(5, (Tk, 128), seed=8)
+    kb = oracle.compress(ki)
+    nb = kb.shape[0]
+    ws_bytes = qsa.qsa_select_workspace_bytes(1, Tq, nb, K)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device="cuda")
+    blk = torch.empty((Tq, K), dtype=torch.int32, device="cuda")
+    ns = torch.empty((Tq,), dtype=torch.int32, device="cuda")
+    qsa.qsa_select_blocks(dev(qi), dev(kb), 1, Tq, pos0, None, nb, 4, 128, 4, mode, K, blk, ns,
+                          ws, ws_bytes)
+    torch.cuda.synchronize()
+    g, n = blk.cpu().numpy(), ns.cpu().numpy()
+    rows = np.arange(0, Tq, 3)
+    ref = oracle.select_rows(qi, kb, rows, pos0=pos0, Kbudget=K, mode=mode, want_scores=True)
+    exempt = 0
+    for i, t in enumerate(rows):
+        nc = (pos0 + t + 1) // 4
+        exempt += check_selection(ref["s"][i, :nc], K, ref["sK"][i], ref["sK1"][i], g[t], n[t])
+    log(f"  mode {mode}: {exempt} of {rows.size} rows differ inside the tie band")
+
+
+# ---------------------------------------------------------- A6 attention
+def test_sparse_prefill_attention_parity(qsa):
+    torch = _torch()
+    T, K = 1029, 64
+    x = synth.prefill_inputs(T, seed=10)
+    Qr, Kr = oracle.rope(x.Q), oracle.rope(x.K)
+    kb = oracle.compress(x.ki)
+    rows = np.arange(T)
+    sel = oracle.select_rows(x.qi, kb, rows, Kbudget=K)
+    O = torch.empty((T, 24, 256), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, 24), dtype=torch.float32, device="cuda")
+    qsa.qsa_sparse_attn_prefill(dev(Qr), dev(Kr), dev(x.V), dev(sel["sel"]), dev(sel["nsel"]), T,
+                                T, 0, 24, 2, 256, 4, K, O, lse)
+    torch.cuda.synchronize()
+    Oref, lref = oracle.sparse_attn_rows(Qr, Kr, x.V, rows, sel["sel"], sel["nsel"])
+    assert_close(O.cpu().numpy(), Oref, "sparse prefill O")
+    assert_close(lse.cpu().numpy(), lref, "sparse prefill lse")
+
+
+def test_decode_attention_parity(qsa):
+    torch = _torch()
+    B, Lmax, K = 5, 5000, 64
+    lens = np.array([1, 2, 7, 4096, 4999], dtype=np.int64)
+    Kc = synth.normal_bf16(2, (B, Lmax, 2, 256), seed=11)
+    Vc = synth.normal_bf16(3, (B, Lmax, 2, 256), seed=11)
+    q = synth.normal_bf16(1, (B, 24, 256), seed=11)
+    rng = np.random.default_rng(0)
+    sel = np.full((B, K), -1, dtype=np.int32)
+    nsel = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        nc = int(lens[b]) // 4
+        m = min(K, nc)
+        sel[b, :m] = np.sort(rng.choice(nc, size=m, replace=False)) if m else []
+        nsel[b] = m
+    wsb = qsa.qsa_decode_workspace_bytes(B, 24, 2, 256, K)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+    O = torch.empty((B, 24, 256), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, 24), dtype=torch.float32, device="cuda")
+    qsa.qsa_sparse_attn_decode(dev(q), dev(Kc), dev(Vc), dev(lens), dev(sel), dev(nsel), B, Lmax,
+                               24, 2, 256, 4, K, O, lse, ws, wsb)
+    torch.cuda.synchronize()
+    Og, lg = O.cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        L = int(lens[b])
+        Oref, lref = oracle.sparse_attn_rows(q[b:b + 1], Kc[b, :L], Vc[b, :L], np.array([0]),
+                                             sel[b:b + 1], nsel[b:b + 1], pos0=L - 1)
+        assert_close(Og[b], Oref[0], f"decode seq {b} (L={L}) O")
+        assert_close(lg[b], lref[0], f"decode seq {b} lse")
+
+
+# ------------------------------------------------------------- A8 dense
+def test_dense_prefill_and_decode_parity(qsa):
+    torch = _torch()
+    T = 300
+    x = synth.prefill_inputs(T, seed=12)
+    O = torch.empty((T, 24, 256), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, 24), dtype=torch.float32, device="cuda")
+    qsa.dense_attn(dev(x.Q), dev(x.K), dev(x.V), 1, T, T, 0, None, 24, 2, 256, O, lse)
+    torch.cuda.synchronize()
+    rows = np.arange(T)
+    Oref, lref = oracle.dense_rows(x.Q, x.K, x.V, rows)
+    assert_close(O.cpu().numpy(), Oref, "dense prefill O")
+    assert_close(lse.cpu().numpy(), lref, "dense prefill lse")
+    # decode form over the same keys, query at L-1
+    B, Lmax = 2, T
+    lens = np.array([T, 77], dtype=np.int64)
+    Kc = np.stack([x.K, x.K])
+    Vc = np.stack([x.V, x.V])
+    q = np.stack([x.Q[T - 1], x.Q[76]])
+    wsb = qsa.dense_attn_workspace_bytes(B, 1, Lmax, 24, 2, 256)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+    Od = torch.empty((B, 24, 256), dtype=torch.float32, device="cuda")
+    qsa.dense_attn(dev(q), dev(Kc), dev(Vc), B, 1, Lmax, 0, dev(lens), 24, 2, 256, Od, None, ws,
+                   wsb)
+    torch.cuda.synchronize()
+    assert_close(Od.cpu().numpy()[0], Oref[T - 1], "dense decode O (L=300)")
+    assert_close(Od.cpu().numpy()[1], Oref[76], "dense decode O (L=77)")
