@@ -62,6 +62,10 @@ def _load():
                                             i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp,
                                             vp, vp]
         lib.qsa_oracle_qsa_rows.restype = None
+        lib.qsa_oracle_qsa_rows_at.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, i32, i32, i32,
+                                               i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp,
+                                               vp]
+        lib.qsa_oracle_qsa_rows_at.restype = None
         lib.qsa_oracle_sparse_attn_rows.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32,
                                                     vp, i64, vp, vp, vp, vp]
         lib.qsa_oracle_sparse_attn_rows.restype = None
@@ -192,6 +196,29 @@ def qsa_rows(Q, K, V, qi, kbar, rows, pos0: int = 0, Kbudget: int = 512, r: int 
     _load().qsa_oracle_qsa_rows(_p(Q), _p(K), _p(V), _p(qi), _p(kbar), kbar.shape[0], pos0, H,
                                 Hkv, D, Hi, Di, r, Kbudget, mode, _p(rows), n, _p(O), _p(lse),
                                 _p(sel), _p(nsel), _p(sK), _p(sK1), _p(err))
+    return dict(O=O, lse=lse, sel=sel, nsel=nsel, sK=sK, sK1=sK1, wsum_err=err)
+
+
+def qsa_rows_at(Q_rows, K, V, qi_rows, kbar, positions, Kbudget: int = 512, r: int = 4,
+                mode: int = MODE_MAXHEAD):
+    """End-to-end QSA of compact query rows: Q_rows [n,H,D] (post-RoPE) and
+    qi_rows [n,Hi,Di] are the queries at absolute positions positions[i]."""
+    Q_rows, K, V, qi_rows, kbar = (_c(a, np.uint16) for a in (Q_rows, K, V, qi_rows, kbar))
+    positions = _c(positions, np.int64)
+    n = positions.size
+    _, H, D = Q_rows.shape
+    Hkv = K.shape[1]
+    Hi, Di = qi_rows.shape[1], qi_rows.shape[2]
+    O = np.empty((n, H, D))
+    lse = np.empty((n, H))
+    sel = np.empty((n, Kbudget), dtype=np.int32)
+    nsel = np.empty(n, dtype=np.int32)
+    sK = np.empty(n)
+    sK1 = np.empty(n)
+    err = np.empty(n)
+    _load().qsa_oracle_qsa_rows_at(_p(Q_rows), _p(K), _p(V), _p(qi_rows), _p(kbar), kbar.shape[0],
+                                   _p(positions), H, Hkv, D, Hi, Di, r, Kbudget, mode, n, _p(O),
+                                   _p(lse), _p(sel), _p(nsel), _p(sK), _p(sK1), _p(err))
     return dict(O=O, lse=lse, sel=sel, nsel=nsel, sK=sK, sK1=sK1, wsum_err=err)
 
 

@@ -280,6 +280,34 @@ void qsa_oracle_qsa_rows(const uint16_t *Q, const uint16_t *K, const uint16_t *V
     }
 }
 
+/* Same as qsa_oracle_qsa_rows for compact inputs: row i of Q [n][H][D] and
+ * of qi [n][Hi][Di] is the query at absolute position pos[i]. */
+void qsa_oracle_qsa_rows_at(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                            const uint16_t *qi, const uint16_t *kbar, int64_t nb,
+                            const int64_t *pos, int H, int Hkv, int D, int Hi, int Di, int r,
+                            int Kbudget, int mode, int64_t n, double *O, double *lse,
+                            int32_t *sel, int32_t *nsel, double *sK, double *sK1,
+                            double *wsum_err) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t p = pos[i];
+        int64_t nc_full = qsa_oracle_num_complete(p, r);
+        double *s = (double *)malloc(sizeof(double) * (size_t)(nc_full > 0 ? nc_full : 1));
+        int64_t nc = qsa_oracle_scores_row(qi + i * Hi * (int64_t)Di, kbar, nb, p, Hi, Di, r,
+                                           mode, s);
+        int32_t *blk = sel + i * Kbudget;
+        for (int k = 0; k < Kbudget; ++k) blk[k] = -1;
+        int ns = qsa_oracle_topk_row(s, nc, Kbudget, blk, &sK[i], &sK1[i]);
+        nsel[i] = ns;
+        int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)(ns * r + r));
+        int64_t ntok = qsa_oracle_token_set(blk, ns, p, r, tok);
+        qsa_oracle_attend_row(Q + i * H * (int64_t)D, K, V, H, Hkv, D, tok, ntok,
+                              O + i * H * (int64_t)D, lse + i * H, &wsum_err[i]);
+        free(tok);
+        free(s);
+    }
+}
+
 /* Attention rows over a GIVEN selection (e.g. one produced elsewhere and
  * validated against the tie band): sel [n][Kbudget] ascending, nsel [n]. */
 void qsa_oracle_sparse_attn_rows(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
