@@ -15,19 +15,6 @@ constexpr int kBT = 64;          // blocks per LDS tile
 constexpr int kSplitTiles = 64;  // block tiles per workgroup (grid.y splits longer rows)
 constexpr int kRowBytes = 272;   // LDS row stride of one pooled key (256 B + 16 B pad)
 
-template <int MODE>
-__device__ __forceinline__ float combine_heads(f32x4 acc) {
-    if (MODE == 0) {
-        float m = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
-        return m * 0.08838834764831845f;  // 1/sqrt(128)
-    } else {
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s += acc[i] > 0.f ? acc[i] : 0.f;
-        return s;
-    }
-}
-
 // Prefill form: queries pos0 + t, t < Tq, one sequence per blockIdx.z.
 template <int MODE>
 __global__ void __launch_bounds__(256)

@@ -15,7 +15,7 @@ namespace {
 
 constexpr int64_t kI32Max = 2147483647;
 constexpr int kMaxBudget = 2048;
-constexpr int64_t kSelectChunkBytes = int64_t(1) << 30;  // score workspace per chunk
+constexpr int kFusedMaxBudget = 512;
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -25,9 +25,10 @@ inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s);
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// Rows of a prefill score chunk for the fused selection.
+// Rows of a prefill score chunk when the budget is too large for the fused
+// selector (the scores of one chunk live in the workspace).
 int64_t select_chunk_rows(int64_t Tq, int64_t ld) {
-    int64_t rows = kSelectChunkBytes / (ld * 4);
+    int64_t rows = (int64_t(1) << 30) / (ld * 4);
     rows = rows / 64 * 64;
     if (rows < 64) rows = 64;
     return rows < Tq ? rows : Tq;
@@ -153,10 +154,12 @@ int qsa_topk_blocks(const float *scores, int B, int64_t Tq, int64_t ld, int64_t 
 }
 
 size_t qsa_select_workspace_bytes(int B, int64_t Tq, int64_t nb_max, int K) {
-    (void)K;
     if (B <= 0 || Tq <= 0 || nb_max <= 0) return 0;
     const int64_t ld = round_up(nb_max, 4);
-    if (Tq == 1) return static_cast<size_t>(B) * ld * 4;  // decode form: all rows at once
+    // decode form (one query per sequence): scores of all rows, then top-K
+    if (Tq == 1) return static_cast<size_t>(B) * ld * 4;
+    // prefill form: fused on chip for K <= 512, else chunked scores
+    if (K <= kFusedMaxBudget) return 0;
     return static_cast<size_t>(select_chunk_rows(Tq, ld) * ld * 4);
 }
 
@@ -170,6 +173,7 @@ int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_
     if (K <= 0) return QSA_ERR_SHAPE;
     if (K > kMaxBudget) return QSA_ERR_UNSUPPORTED;
     if (static_cast<int64_t>(B) * Tq > kI32Max) return QSA_ERR_OVERFLOW;
+    if (nb_max >= (int64_t(1) << 27)) return QSA_ERR_OVERFLOW;  // 32-bit block offsets
     if (Tq == 0 || nb_max == 0) {
         // no candidates: every row selects nothing
         if (Tq == 0) return QSA_OK;
@@ -189,16 +193,22 @@ int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_
     }
     const int64_t chunk = select_chunk_rows(Tq, ld);
     for (int b = 0; b < B; ++b) {
+        const qsa_bf16 *qb = q_idx + static_cast<int64_t>(b) * Tq * (kIdxHeads * kIdxDim);
+        const qsa_bf16 *kb = kbar + static_cast<int64_t>(b) * nb_max * kIdxDim;
+        const int64_t row0 = static_cast<int64_t>(b) * Tq;
+        if (K <= kFusedMaxBudget) {
+            hipError_t e = launch_select_fused(qb, kb, Tq, pos0, nb_max, score_mode, K,
+                                               blk_idx + row0 * K, n_sel + row0, s);
+            if (e != hipSuccess) return QSA_ERR_LAUNCH;
+            continue;
+        }
         for (int64_t q0 = 0; q0 < Tq; q0 += chunk) {
             const int64_t len = Tq - q0 < chunk ? Tq - q0 : chunk;
-            const qsa_bf16 *qb = q_idx + (static_cast<int64_t>(b) * Tq + q0) * (kIdxHeads * kIdxDim);
-            const qsa_bf16 *kb = kbar + static_cast<int64_t>(b) * nb_max * kIdxDim;
-            hipError_t e = launch_index_scores(qb, kb, 1, len, pos0 + q0, nullptr, nb_max,
-                                               score_mode, sc, ld, s);
+            hipError_t e = launch_index_scores(qb + q0 * (kIdxHeads * kIdxDim), kb, 1, len,
+                                               pos0 + q0, nullptr, nb_max, score_mode, sc, ld, s);
             if (e != hipSuccess) return QSA_ERR_LAUNCH;
-            const int64_t row0 = static_cast<int64_t>(b) * Tq + q0;
-            e = launch_topk(sc, 1, len, ld, pos0 + q0, nullptr, nb_max, r, K, blk_idx + row0 * K,
-                            n_sel + row0, s);
+            e = launch_topk(sc, 1, len, ld, pos0 + q0, nullptr, nb_max, r, K,
+                            blk_idx + (row0 + q0) * K, n_sel + row0 + q0, s);
             if (e != hipSuccess) return QSA_ERR_LAUNCH;
         }
     }

@@ -45,6 +45,22 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Indexer head combination of one query's four head dot products (held by one
+// lane as rows 4*g4 .. 4*g4+3 of a 16x16 MFMA tile).  MODE 0: max over heads
+// scaled by 1/sqrt(128); MODE 1: sum of ReLUs.  Shared by every kernel that
+// scores blocks, so their scores agree bit for bit.
+template <int MODE>
+__device__ __forceinline__ float combine_heads(f32x4 acc) {
+    if (MODE == 0) {
+        const float m = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+        return m * 0.08838834764831845f;
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += acc[i] > 0.f ? acc[i] : 0.f;
+    return s;
+}
+
 // ------------------------------------------------------------ launchers --
 hipError_t launch_rope(const uint16_t *x, uint16_t *y, int64_t T, int nheads, int head_dim,
                        int rope_dim, const double *inv_freq, int64_t pos0,
@@ -57,6 +73,10 @@ hipError_t launch_compress(const uint16_t *k, int B, int64_t Tk, int64_t k_seq_s
 hipError_t launch_index_scores(const uint16_t *q_idx, const uint16_t *kbar, int B, int64_t Tq,
                                int64_t pos0, const int64_t *seq_len, int64_t nb_max, int mode,
                                float *scores, int64_t ld, hipStream_t s);
+
+hipError_t launch_select_fused(const uint16_t *q_idx, const uint16_t *kbar, int64_t Tq,
+                               int64_t pos0, int64_t nb_max, int mode, int K, int32_t *blk_idx,
+                               int32_t *n_sel, hipStream_t s);
 
 hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64_t pos0,
                        const int64_t *seq_len, int64_t nb_max, int r, int K, int32_t *blk_idx,

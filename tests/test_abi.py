@@ -134,14 +134,22 @@ def test_topk_validation(lib):
 
 def test_select_validation(lib):
     lib.qsa_select_workspace_bytes.restype = ctypes.c_size_t
-    need = lib.qsa_select_workspace_bytes(1, I64(1000), I64(250), 64)
-    assert need >= 1000 * 252 * 4 // 16  # holds a chunk of scores
-    st = lib.qsa_select_blocks(vp(P), vp(P), 1, I64(1000), I64(0), None, I64(250), 4, 128, 4, 0,
-                               64, vp(P), vp(P), vp(P), ctypes.c_size_t(16), None)
+    # prefill form runs fused on chip: no workspace
+    assert lib.qsa_select_workspace_bytes(1, I64(131072), I64(32768), 512) == 0
+    # budgets above 512 fall back to chunked scores in the workspace
+    assert lib.qsa_select_workspace_bytes(1, I64(131072), I64(32768), 1024) > 0
+    # decode form keeps one score row per sequence
+    need = lib.qsa_select_workspace_bytes(32, I64(1), I64(65536), 512)
+    assert need >= 32 * 65536 * 4
+    st = lib.qsa_select_blocks(vp(P), vp(P), 32, I64(1), I64(0), vp(P), I64(65536), 4, 128, 4, 0,
+                               512, vp(P), vp(P), vp(P), ctypes.c_size_t(16), None)
     assert st == WORKSPACE
     st = lib.qsa_select_blocks(vp(P), vp(P), 1, I64(1000), I64(0), None, I64(250), 4, 128, 4, 0,
-                               64, vp(P), vp(0), vp(P), ctypes.c_size_t(need), None)
+                               64, vp(P), vp(0), None, ctypes.c_size_t(0), None)
     assert st == NULL
+    st = lib.qsa_select_blocks(vp(P), vp(P), 1, I64(1000), I64(0), None, I64(250), 4, 128, 4, 0,
+                               4096, vp(P), vp(P), None, ctypes.c_size_t(0), None)
+    assert st == UNSUP
 
 
 def sparse_prefill(lib, Q=P, Kt=P, V=P, blk=P, ns=P, Tq=8, Tk=8, pos0=0, H=24, Hkv=2, D=256, r=4,

@@ -158,6 +158,30 @@ def test_topk_decode_form_and_small_contexts(qsa):
         assert n[b] == want.size and np.array_equal(g[b, :n[b]], want)
 
 
+def test_topk_long_rows_and_heavy_ties(qsa):
+    """Rows past the register-resident size (streamed path) and threshold
+    bins too full for the LDS buffer (whole-row resolve), K = 512."""
+    torch = _torch()
+    K, nb_max = 512, 100000
+    lens = np.array([4 * 100000, 4 * 50000, 4 * 30000, 4 * 32768, 4 * 32769, 4 * 7000],
+                    dtype=np.int64)
+    B = lens.size
+    rng = np.random.default_rng(21)
+    s = rng.standard_normal((B, nb_max)).astype(np.float32)
+    s[1] = 0.75                                        # one value: every key ties
+    s[2] = rng.choice([0.0, 0.25, 0.5], size=nb_max)   # three values, bins of ~10,000
+    s[5, :3000] = 1.0                                  # 3000 ties above the rest
+    blk = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    ns = torch.empty((B,), dtype=torch.int32, device="cuda")
+    qsa.qsa_topk_blocks(dev(s), B, 1, nb_max, 0, dev(lens), nb_max, 4, K, blk, ns)
+    torch.cuda.synchronize()
+    g, n = blk.cpu().numpy(), ns.cpu().numpy()
+    for b in range(B):
+        nc = min(int(lens[b]) // 4, nb_max)
+        want, _, _ = oracle.topk_row(s[b, :nc].astype(np.float64), K)
+        assert n[b] == want.size and np.array_equal(g[b, :n[b]], want), b
+
+
 # --------------------------------------------------- A3+A4 vs fp64 scores
 @pytest.mark.parametrize("mode", [0, 1])
 def test_selection_tie_band(qsa, mode):
@@ -183,6 +207,38 @@ def test_selection_tie_band(qsa, mode):
         nc = (pos0 + t + 1) // 4
         exempt += check_selection(ref["s"][i, :nc], K, ref["sK"][i], ref["sK1"][i], g[t], n[t])
     log(f"  mode {mode}: {exempt} of {rows.size} rows differ inside the tie band")
+
+
+@pytest.mark.parametrize("mode,Tq,pos0,K", [(0, 1500, 0, 64), (1, 1500, 0, 64),
+                                            (0, 700, 140000, 512), (1, 300, 1900, 512),
+                                            (0, 37, 5, 3), (0, 300, 2000, 100),
+                                            (1, 400, 12000, 1024)])
+def test_fused_select_matches_scores_plus_topk(qsa, mode, Tq, pos0, K):
+    """The fused prefill selector returns exactly what qsa_index_scores followed
+    by qsa_topk_blocks returns (same scores bit for bit, same tie order);
+    RELUSUM rows near nc = K put the K-th score on a run of exact zeros."""
+    torch = _torch()
+    Tk = pos0 + Tq
+    qi = synth.normal_bf16(4, (Tq, 4, 128), seed=13)
+    ki = synth.normal_bf16(5, (Tk, 128), seed=13)
+    kb = oracle.compress(ki)
+    nb = kb.shape[0]
+    ld = (nb + 3) // 4 * 4
+    sc = torch.empty((Tq, ld), dtype=torch.float32, device="cuda")
+    b1 = torch.empty((Tq, K), dtype=torch.int32, device="cuda")
+    n1 = torch.empty((Tq,), dtype=torch.int32, device="cuda")
+    b2 = torch.full((Tq, K), 7, dtype=torch.int32, device="cuda")
+    n2 = torch.full((Tq,), 7, dtype=torch.int32, device="cuda")
+    qd, kd = dev(qi), dev(kb)
+    qsa.qsa_index_scores(qd, kd, 1, Tq, pos0, None, nb, 4, 128, 4, mode, sc, ld)
+    qsa.qsa_topk_blocks(sc, 1, Tq, ld, pos0, None, nb, 4, K, b1, n1)
+    wsb = qsa.qsa_select_workspace_bytes(1, Tq, nb, K)
+    assert (wsb == 0) == (K <= 512)   # budgets above 512 use chunked scores
+    ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device="cuda")
+    qsa.qsa_select_blocks(qd, kd, 1, Tq, pos0, None, nb, 4, 128, 4, mode, K, b2, n2, ws, wsb)
+    torch.cuda.synchronize()
+    assert np.array_equal(n1.cpu().numpy(), n2.cpu().numpy())
+    assert np.array_equal(b1.cpu().numpy(), b2.cpu().numpy())
 
 
 # ---------------------------------------------------------- A6 attention
