@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqsa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["qsa_api.cpp", "elementwise.hip", "index_scores.hip", "topk.hip", "select_fused.hip",
+SOURCES = ["qsa_api.cpp", "elementwise.hip", "index_scores.hip", "topk.hip",
            "attention.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

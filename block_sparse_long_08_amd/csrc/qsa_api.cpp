@@ -15,7 +15,6 @@ namespace {
 
 constexpr int64_t kI32Max = 2147483647;
 constexpr int kMaxBudget = 2048;
-constexpr int kFusedMaxBudget = 512;
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -25,8 +24,8 @@ inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s);
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// Rows of a prefill score chunk when the budget is too large for the fused
-// selector (the scores of one chunk live in the workspace).
+// Rows of one prefill score chunk (the scores of a chunk, at most 1 GiB, live
+// in the workspace; top-K reads them back before the next chunk is scored).
 int64_t select_chunk_rows(int64_t Tq, int64_t ld) {
     int64_t rows = (int64_t(1) << 30) / (ld * 4);
     rows = rows / 64 * 64;
@@ -134,33 +133,46 @@ int qsa_index_scores(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t
 }
 
 size_t qsa_topk_workspace_bytes(int B, int64_t Tq, int64_t nb_max, int K) {
-    (void)B; (void)Tq; (void)nb_max; (void)K;
-    return 0;
+    if (B <= 0 || Tq <= 0 || nb_max <= 0 || K <= 0) return 0;
+    return topk_plan(static_cast<int64_t>(B) * Tq, nb_max, K).ws_bytes;
 }
 
 int qsa_topk_blocks(const float *scores, int B, int64_t Tq, int64_t ld, int64_t pos0,
                     const int64_t *seq_len, int64_t nb_max, int r, int K, int32_t *blk_idx,
                     int32_t *n_sel, void *ws, size_t ws_bytes, void *stream) {
-    (void)ws; (void)ws_bytes;
     if (!scores || !blk_idx || !n_sel) return QSA_ERR_NULL;
     if (B <= 0 || Tq < 0 || nb_max < 0 || pos0 < 0 || r <= 0 || K <= 0) return QSA_ERR_SHAPE;
     if (seq_len && Tq != 1) return QSA_ERR_SHAPE;
-    if (ld < nb_max) return QSA_ERR_SHAPE;
+    if (ld < nb_max || ld % 4 != 0) return QSA_ERR_SHAPE;
     if (K > kMaxBudget) return QSA_ERR_UNSUPPORTED;
     if (nb_max > kI32Max || static_cast<int64_t>(B) * Tq > kI32Max) return QSA_ERR_OVERFLOW;
     if (!aligned16(scores)) return QSA_ERR_ALIGN;
+    if (Tq == 0) return QSA_OK;
+    const size_t need = qsa_topk_workspace_bytes(B, Tq, nb_max, K);
+    if (need > 0 && (!ws || ws_bytes < need)) return QSA_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(ws)) return QSA_ERR_ALIGN;
     return launch_status(launch_topk(scores, B, Tq, ld, pos0, seq_len, nb_max, r, K, blk_idx,
-                                     n_sel, as_stream(stream)));
+                                     n_sel, ws, as_stream(stream)));
+}
+
+// Workspace of qsa_select_blocks: the fp32 scores of one chunk of query rows
+// (all rows in the decode form), then the top-K candidate lists of that chunk.
+static void select_layout(int B, int64_t Tq, int64_t nb_max, int K, int64_t *ld,
+                          int64_t *chunk, size_t *score_bytes, size_t *topk_bytes) {
+    *ld = round_up(nb_max > 0 ? nb_max : 1, 4);
+    const bool decode = Tq == 1;
+    *chunk = decode ? 1 : select_chunk_rows(Tq, *ld);
+    const int64_t rows = decode ? B : *chunk;
+    *score_bytes = static_cast<size_t>(round_up(rows * *ld * 4, 256));
+    *topk_bytes = topk_plan(rows, nb_max, K).ws_bytes;
 }
 
 size_t qsa_select_workspace_bytes(int B, int64_t Tq, int64_t nb_max, int K) {
-    if (B <= 0 || Tq <= 0 || nb_max <= 0) return 0;
-    const int64_t ld = round_up(nb_max, 4);
-    // decode form (one query per sequence): scores of all rows, then top-K
-    if (Tq == 1) return static_cast<size_t>(B) * ld * 4;
-    // prefill form: fused on chip for K <= 512, else chunked scores
-    if (K <= kFusedMaxBudget) return 0;
-    return static_cast<size_t>(select_chunk_rows(Tq, ld) * ld * 4);
+    if (B <= 0 || Tq <= 0 || nb_max <= 0 || K <= 0) return 0;
+    int64_t ld, chunk;
+    size_t sb, tb;
+    select_layout(B, Tq, nb_max, K, &ld, &chunk, &sb, &tb);
+    return sb + tb;
 }
 
 int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t Tq,
@@ -173,42 +185,35 @@ int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_
     if (K <= 0) return QSA_ERR_SHAPE;
     if (K > kMaxBudget) return QSA_ERR_UNSUPPORTED;
     if (static_cast<int64_t>(B) * Tq > kI32Max) return QSA_ERR_OVERFLOW;
-    if (nb_max >= (int64_t(1) << 27)) return QSA_ERR_OVERFLOW;  // 32-bit block offsets
-    if (Tq == 0 || nb_max == 0) {
-        // no candidates: every row selects nothing
-        if (Tq == 0) return QSA_OK;
-    }
+    if (nb_max >= (int64_t(1) << 27)) return QSA_ERR_OVERFLOW;  // bounds the score chunk
+    if (Tq == 0) return QSA_OK;
     const size_t need = qsa_select_workspace_bytes(B, Tq, nb_max, K);
     if (need > 0 && (!ws || ws_bytes < need)) return QSA_ERR_WORKSPACE;
     if (need > 0 && !aligned16(ws)) return QSA_ERR_ALIGN;
     hipStream_t s = as_stream(stream);
+    int64_t ld, chunk;
+    size_t sb, tb;
+    select_layout(B, Tq, nb_max, K, &ld, &chunk, &sb, &tb);
     float *sc = static_cast<float *>(ws);
-    const int64_t ld = round_up(nb_max > 0 ? nb_max : 1, 4);
+    void *tws = need > 0 ? static_cast<char *>(ws) + sb : nullptr;
     if (seq_len || Tq == 1) {
         hipError_t e = launch_index_scores(q_idx, kbar, B, Tq, pos0, seq_len, nb_max, score_mode,
                                            sc, ld, s);
         if (e != hipSuccess) return QSA_ERR_LAUNCH;
         return launch_status(launch_topk(sc, B, Tq, ld, pos0, seq_len, nb_max, r, K, blk_idx,
-                                         n_sel, s));
+                                         n_sel, tws, s));
     }
-    const int64_t chunk = select_chunk_rows(Tq, ld);
     for (int b = 0; b < B; ++b) {
         const qsa_bf16 *qb = q_idx + static_cast<int64_t>(b) * Tq * (kIdxHeads * kIdxDim);
         const qsa_bf16 *kb = kbar + static_cast<int64_t>(b) * nb_max * kIdxDim;
         const int64_t row0 = static_cast<int64_t>(b) * Tq;
-        if (K <= kFusedMaxBudget) {
-            hipError_t e = launch_select_fused(qb, kb, Tq, pos0, nb_max, score_mode, K,
-                                               blk_idx + row0 * K, n_sel + row0, s);
-            if (e != hipSuccess) return QSA_ERR_LAUNCH;
-            continue;
-        }
         for (int64_t q0 = 0; q0 < Tq; q0 += chunk) {
             const int64_t len = Tq - q0 < chunk ? Tq - q0 : chunk;
             hipError_t e = launch_index_scores(qb + q0 * (kIdxHeads * kIdxDim), kb, 1, len,
                                                pos0 + q0, nullptr, nb_max, score_mode, sc, ld, s);
             if (e != hipSuccess) return QSA_ERR_LAUNCH;
             e = launch_topk(sc, 1, len, ld, pos0 + q0, nullptr, nb_max, r, K,
-                            blk_idx + (row0 + q0) * K, n_sel + row0 + q0, s);
+                            blk_idx + (row0 + q0) * K, n_sel + row0 + q0, tws, s);
             if (e != hipSuccess) return QSA_ERR_LAUNCH;
         }
     }

@@ -74,13 +74,22 @@ hipError_t launch_index_scores(const uint16_t *q_idx, const uint16_t *kbar, int 
                                int64_t pos0, const int64_t *seq_len, int64_t nb_max, int mode,
                                float *scores, int64_t ld, hipStream_t s);
 
-hipError_t launch_select_fused(const uint16_t *q_idx, const uint16_t *kbar, int64_t Tq,
-                               int64_t pos0, int64_t nb_max, int mode, int K, int32_t *blk_idx,
-                               int32_t *n_sel, hipStream_t s);
+// Top-K passes for rows of up to nmax candidates: npass reduction passes
+// (segment lengths seg[i], entries[i] candidates per row after pass i), then
+// one final pass.  ws_bytes of workspace hold the candidate lists.
+struct TopkPlan {
+    int npass;
+    int64_t seg[4];
+    int64_t entries[4];
+    int64_t final_entries;
+    int64_t ld[2];
+    size_t ws_bytes;
+};
+TopkPlan topk_plan(int64_t rows, int64_t nmax, int K);
 
 hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64_t pos0,
                        const int64_t *seq_len, int64_t nb_max, int r, int K, int32_t *blk_idx,
-                       int32_t *n_sel, hipStream_t s);
+                       int32_t *n_sel, void *ws, hipStream_t s);
 
 // Sparse / dense attention over 4-token blocks (see attention.hip).
 struct AttnArgs {

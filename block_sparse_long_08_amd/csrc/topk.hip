@@ -1,275 +1,554 @@
 // A4: per-query top-K block selection (chlience section 6: at most 512
-// complete blocks per query).
+// complete blocks per query, chosen by indexer score).
 //
-// One workgroup (1024 threads) per query row finds the K-th largest score
-// exactly and emits the selected blocks in ascending order, realising the
-// order (score desc, index asc):
-//   1. histogram of the top 12 bits of the order-preserving uint32 keys
-//      (LDS atomics) -> the bin B holding the K-th key and how many keys lie
-//      above it;
-//   2. the keys of bin B (few, for any spread-out row) are gathered into LDS
-//      and the low 20 bits resolved by two 10-bit radix passes -> the exact
-//      threshold key T and how many keys equal to T are taken (lowest
-//      indices first); a bin too full for the LDS buffer is resolved by the
-//      same passes over the whole row;
-//   3. ordered compaction: wave w owns a contiguous run of the row, lane l
-//      holds 4 consecutive keys per 256-key slice, so wave scans plus one
-//      cross-wave prefix give every selected block its output slot.
-// Rows of up to 32,768 candidates stay in registers (one global read); longer
-// rows are streamed in tiles of 16,384 keys (three reads).
+// Every pass runs one workgroup per (row, segment).  A segment of up to
+// NT*VPT keys is held in registers: wave w owns a contiguous run of 64*VPT
+// keys and lane l holds 4 consecutive keys of every 256-key slice, so one
+// float4 load per slice is coalesced and "earlier in the row" is (wave,
+// slice, lane, element) order.  Finding the K-th largest key T:
+//   1. histogram of key bits 31..20 in LDS -> the bin B holding rank K and
+//      the count above it;
+//   2. each wave appends the keys of bin B it holds to a private LDS list
+//      (ballot + mbcnt, no shared counter); one wave then resolves bits
+//      19..0 by two 10-bit histograms over those lists.  If a list overflows
+//      (a crowded bin), the same two passes run block-wide over the
+//      registers instead;
+//   3. selection: every key > T, and the first `quota` keys equal to T (the
+//      lowest indices win ties).  Output slots come from ballots of the
+//      selection predicate, giving ascending index order without sorting.
+// A row longer than one segment is reduced first: each segment emits its
+// own top-K (key and index, ascending), and the global top-K is the top-K of
+// those lists, because an element among the K best of the row is among the
+// K best of its segment.  The order (score desc, index asc) is kept exactly.
 #include "qsa_internal.h"
 
 namespace qsa {
 
-constexpr int kNT = 1024;                 // threads per row
-constexpr int kNW = kNT / kWave;          // waves
-constexpr int kBins = 4096;               // first digit: key bits 31..20
-constexpr int kCap = 6144;                // LDS candidates of the threshold bin
+constexpr int kBins = 4096;                // first digit: key bits 31..20
+constexpr int kWaveCap = 256;              // bin-B keys one wave may list
+constexpr uint32_t kMinKey = 0x00100000u;  // smaller keys: empty slots (0) and NaNs only
+constexpr int kSegBig = 32768;             // 1024 threads x 32 keys
+constexpr int kSegSmall = 4096;            // 256 threads x 16 keys
 
-struct TopkShared {
-    uint32_t hist[kBins];
-    uint32_t ckey[kCap];
-    uint32_t wsum[kNW];
-    uint32_t sel_bin, sel_above, cand_n;
+struct TopkArgs {
+    const float *scores;     // source 0: fp32 score rows
+    int64_t ld;              //   row stride (multiple of 4)
+    const uint32_t *ckey;    // source 1: candidate keys of the previous pass
+    const int32_t *cidx;     //   and their block indices
+    int64_t cin_ld;          //   row stride of the candidate lists
+    uint32_t *okey;          // destination 1: this pass's candidate lists
+    int32_t *oidx;
+    int64_t cout_ld;
+    int32_t *blk_idx;        // destination 0: [rows][K] ascending, -1 padded
+    int32_t *n_sel;          //   [rows]
+    int64_t Tq, pos0, nb_max;
+    const int64_t *seq_len;
+    int r, K;
+    int nprev;               // passes before this one (source 1)
+    int64_t prev_seg[4];     // their segment lengths
 };
 
-// Block-wide inclusive scan of one value per thread (uint32).
-__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, TopkShared &sh, int lane,
-                                                    int wave) {
-    uint32_t x = v;
+template <int NT>
+struct TopkSmem {
+    static constexpr int NW = NT / kWave;
+    uint32_t hist[kBins];
+    uint32_t cand[NW][kWaveCap];
+    uint32_t wcnt[NW];
+    uint32_t wtot[NW];
+    uint32_t fd_bin, fd_above, total;
+    uint32_t thr, quota, eqcnt;
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Set bits of m in the lanes below this one.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
         const uint32_t y = __shfl_up(x, off, kWave);
         if (lane >= off) x += y;
     }
-    if (lane == kWave - 1) sh.wsum[wave] = x;
-    __syncthreads();
-    uint32_t before = 0;
-    for (int w = 0; w < wave; ++w) before += sh.wsum[w];
-    __syncthreads();
-    return x + before;
+    return x;
 }
 
-// Digit search: counts[i] (descending digit order across threads) -> the
-// digit holding rank `krem` and the count above it.  Thread t owns `per`
-// consecutive digits starting at digit (ndig - 1 - per*t) going down.
-template <int PER>
-__device__ __forceinline__ void find_digit(const uint32_t *cnt, int ndig, uint32_t krem,
-                                           TopkShared &sh, int tid, int lane, int wave) {
+// Rank search over NBINS counts held in LDS (bin NBINS-1 is the largest
+// digit).  Thread t owns PER consecutive digits, descending from
+// NBINS-1-PER*t.  Finds the digit holding rank krem (1-based, counted from
+// the top) and the count above it; the total count goes to sh.total.
+// SKIP0: bin 0 holds empty slots and is not counted.
+template <int NT, int NBINS, bool SKIP0>
+__device__ __forceinline__ void block_find(const uint32_t *h, uint32_t krem, TopkSmem<NT> &sh,
+                                           int tid, int lane, int wave) {
+    constexpr int PER = NBINS / NT;
+    static_assert(PER >= 1 && NBINS % NT == 0, "bins per thread");
+    const int base = NBINS - PER * (tid + 1);
     uint32_t c[PER];
     uint32_t local = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int d = ndig - 1 - PER * tid - i;
-        c[i] = d >= 0 ? cnt[d] : 0u;
+        const int d = base + PER - 1 - i;
+        c[i] = (SKIP0 && d == 0) ? 0u : h[d];
         local += c[i];
     }
-    const uint32_t incl = block_incl_scan(local, sh, lane, wave);
-    const uint32_t before = incl - local;
-    if (before < krem && krem <= incl) {
-        uint32_t acc = before;
+    const uint32_t x = wave_incl_scan(local, lane);
+    if (lane == kWave - 1) sh.wtot[wave] = x;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < TopkSmem<NT>::NW; ++w) {
+        const uint32_t t = sh.wtot[w];
+        before += w < wave ? t : 0u;
+        total += t;
+    }
+    const uint32_t incl = x + before;
+    uint32_t acc = incl - local;
+    if (acc < krem && krem <= incl) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             if (acc < krem && krem <= acc + c[i]) {
-                sh.sel_bin = static_cast<uint32_t>(ndig - 1 - PER * tid - i);
-                sh.sel_above = acc;
+                sh.fd_bin = static_cast<uint32_t>(base + PER - 1 - i);
+                sh.fd_above = acc;
             }
             acc += c[i];
         }
     }
+    if (tid == 0) sh.total = total;
     __syncthreads();
 }
 
-// Keys of one tile: wave w holds elements base + w*64*VPT + 256*j + 4*lane + c.
-// Slots past the row get key 0, which lies below the key of every finite
-// score (the smallest, -inf, maps to 0x007FFFFF): such slots never land in a
-// searched bin and never compare >= a threshold, so no bounds test is needed.
-template <int VPT>
-__device__ __forceinline__ void load_keys(const float *__restrict__ s, int64_t n, int64_t base,
-                                          int lane, int wave, uint32_t (&k)[VPT]) {
+// The same search by one wave over 1024 bins; returns the digit, the count
+// above it and its own count (wave-uniform).
+__device__ __forceinline__ void wave_find1024(const uint32_t *h, uint32_t krem, int lane,
+                                              uint32_t &digit, uint32_t &above, uint32_t &cnt) {
+    const int base = 1024 - 16 * (lane + 1);
+    uint32_t c[16];
 #pragma unroll
-    for (int j = 0; j < VPT / 4; ++j) {
-        const int64_t i = base + static_cast<int64_t>(wave) * 64 * VPT + 256 * j + 4 * lane;
-        if (i + 3 < n) {
-            const float4 v = *reinterpret_cast<const float4 *>(s + i);
-            k[4 * j + 0] = score_key(v.x);
-            k[4 * j + 1] = score_key(v.y);
-            k[4 * j + 2] = score_key(v.z);
-            k[4 * j + 3] = score_key(v.w);
-        } else {
+    for (int v = 0; v < 4; ++v) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(h + base + 4 * v);
+        c[15 - 4 * v] = q.x;
+        c[14 - 4 * v] = q.y;
+        c[13 - 4 * v] = q.z;
+        c[12 - 4 * v] = q.w;
+    }
+    uint32_t local = 0;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) k[4 * j + c] = i + c < n ? score_key(s[i + c]) : 0u;
+    for (int i = 0; i < 16; ++i) local += c[i];
+    const uint32_t incl = wave_incl_scan(local, lane);
+    uint32_t acc = incl - local;
+    const bool mine = acc < krem && krem <= incl;
+    uint32_t d = 0, ab = 0, cn = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (acc < krem && krem <= acc + c[i]) {
+            d = static_cast<uint32_t>(base + 15 - i);
+            ab = acc;
+            cn = c[i];
         }
+        acc += c[i];
+    }
+    const uint64_t m = __ballot(mine);
+    const int src = static_cast<int>(__builtin_ctzll(m));
+    digit = __shfl(d, src, kWave);
+    above = __shfl(ab, src, kWave);
+    cnt = __shfl(cn, src, kWave);
+}
+
+// Writes one selected element: gpos is its position in this pass's input
+// row, pos its output slot.
+template <int SRC, int DST>
+__device__ __forceinline__ void emit_one(const TopkArgs &a, int64_t row, int64_t obase,
+                                         int64_t gpos, uint32_t pos, uint32_t key) {
+    const int32_t idx = SRC == 0 ? static_cast<int32_t>(gpos) : a.cidx[row * a.cin_ld + gpos];
+    if (DST == 0) {
+        a.blk_idx[obase + pos] = idx;
+    } else {
+        a.okey[obase + pos] = key;
+        a.oidx[obase + pos] = idx;
     }
 }
 
-template <int VPT>
-__device__ __forceinline__ int64_t elem_index(int64_t base, int wave, int lane, int q) {
-    return base + static_cast<int64_t>(wave) * 64 * VPT + 256 * (q >> 2) + 4 * lane + (q & 3);
-}
+// SRC 0: keys from fp32 score rows; SRC 1: candidate lists of a previous
+// pass.  DST 0: final ascending block indices; DST 1: this segment's top-K
+// as a candidate list (K entries, unused ones key 0 / index -1).
+template <int NT, int VPT, int SRC, int DST>
+__global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
+    constexpr int NW = NT / kWave;
+    constexpr int SEG = NT * VPT;
+    constexpr int NSL = VPT / 4;  // 256-key slices per wave
+    __shared__ TopkSmem<NT> sh;
 
-// RESIDENT: the whole row is one tile held in registers (n <= 1024*VPT).
-template <int VPT, bool RESIDENT>
-__global__ void __launch_bounds__(kNT)
-topk_kernel(const float *__restrict__ scores, int64_t Tq, int64_t ld, int64_t pos0,
-            const int64_t *__restrict__ seq_len, int64_t nb_max, int r, int K,
-            int32_t *__restrict__ blk_idx, int32_t *__restrict__ n_sel) {
-    __shared__ TopkShared sh;
-    constexpr int64_t TILE = static_cast<int64_t>(kNT) * VPT;
     const int64_t row = blockIdx.x;
-    const int64_t seq = row / Tq, t = row - seq * Tq;
-    const int64_t p = seq_len ? seq_len[seq] - 1 : pos0 + t;
-    const int64_t n = min(num_complete_blocks(p, r), nb_max);
-    const float *s = scores + row * ld;
-    int32_t *out = blk_idx + row * K;
+    const int seg = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t sq = row / a.Tq;
+    const int64_t p = a.seq_len ? a.seq_len[sq] - 1 : a.pos0 + (row - sq * a.Tq);
+    const int64_t n_row = min(num_complete_blocks(p, a.r), a.nb_max);
+    const uint32_t K = static_cast<uint32_t>(a.K);
 
-    if (n <= K) {
-        for (int i = tid; i < K; i += kNT) out[i] = i < n ? i : -1;
-        if (tid == 0) n_sel[row] = static_cast<int32_t>(n);
+    if (n_row <= a.K) {  // every complete block is selected
+        if (DST == 0) {
+            int32_t *out = a.blk_idx + row * a.K;
+            for (int i = tid; i < a.K; i += NT) out[i] = i < n_row ? i : -1;
+            if (tid == 0) a.n_sel[row] = static_cast<int32_t>(n_row);
+        }
         return;
     }
+    // entries of this row at this pass's input
+    int64_t n_in = n_row;
+    if (SRC == 1)
+        for (int i = 0; i < a.nprev; ++i) n_in = (n_in + a.prev_seg[i] - 1) / a.prev_seg[i] * a.K;
+    const int64_t seg_base = static_cast<int64_t>(seg) * SEG;
+    const int m = static_cast<int>(max(int64_t(0), min(n_in - seg_base, int64_t(SEG))));
+    const int w0 = wave * 64 * VPT;
 
+    // ---- load keys (slots past the segment get key 0)
     uint32_t k[VPT];
-    if (RESIDENT) load_keys<VPT>(s, n, 0, lane, wave, k);
-
-    // ---- 1. histogram of key bits 31..20
-    for (int i = tid; i < kBins; i += kNT) sh.hist[i] = 0;
-    if (tid == 0) sh.cand_n = 0;
-    __syncthreads();
-    for (int64_t base = 0; base < n; base += TILE) {
-        if (!RESIDENT) load_keys<VPT>(s, n, base, lane, wave, k);
+    if (w0 < m) {
+        if (SRC == 0) {
+            const float *s = a.scores + row * a.ld + seg_base;
 #pragma unroll
-        for (int q = 0; q < VPT; ++q)
-            if (k[q]) atomicAdd(&sh.hist[k[q] >> 20], 1u);
+            for (int j = 0; j < NSL; ++j) {
+                const int i = w0 + 256 * j + 4 * lane;
+                const float4 v = *reinterpret_cast<const float4 *>(s + (i < m ? i : 0));
+                k[4 * j + 0] = i + 0 < m ? score_key(v.x) : 0u;
+                k[4 * j + 1] = i + 1 < m ? score_key(v.y) : 0u;
+                k[4 * j + 2] = i + 2 < m ? score_key(v.z) : 0u;
+                k[4 * j + 3] = i + 3 < m ? score_key(v.w) : 0u;
+            }
+        } else {
+            const uint32_t *s = a.ckey + row * a.cin_ld + seg_base;
+#pragma unroll
+            for (int j = 0; j < NSL; ++j) {
+                const int i = w0 + 256 * j + 4 * lane;
+                const uint4 v = *reinterpret_cast<const uint4 *>(s + (i < m ? i : 0));
+                k[4 * j + 0] = i + 0 < m ? v.x : 0u;
+                k[4 * j + 1] = i + 1 < m ? v.y : 0u;
+                k[4 * j + 2] = i + 2 < m ? v.z : 0u;
+                k[4 * j + 3] = i + 3 < m ? v.w : 0u;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) k[q] = 0u;
     }
-    __syncthreads();
-    find_digit<kBins / kNT>(sh.hist, kBins, static_cast<uint32_t>(K), sh, tid, lane, wave);
-    const uint32_t bin = sh.sel_bin;
-    uint32_t krem = static_cast<uint32_t>(K) - sh.sel_above;
-    const uint32_t nbin = sh.hist[bin];
-    const bool in_lds = nbin <= kCap;
-    __syncthreads();  // every thread has read the histogram before it is reused
+    // slices of this wave that hold keys (wave-uniform)
+    const int nsl = w0 < m ? min(NSL, (m - w0 + 255) >> 8) : 0;
 
-    // ---- 2. gather the threshold bin, resolve the low 20 bits
-    if (in_lds) {
-        for (int64_t base = 0; base < n; base += TILE) {
-            if (!RESIDENT) load_keys<VPT>(s, n, base, lane, wave, k);
+    bool all = m <= a.K;  // the whole segment is selected
+    uint32_t thr = kMinKey, quota = 0, eqcnt = 0;
+    if (!all) {
+        // ---- 1. first digit
+        for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;
+        __syncthreads();
 #pragma unroll
-            for (int q = 0; q < VPT; ++q) {
-                if ((k[q] >> 20) == bin) {
-                    const uint32_t slot = atomicAdd(&sh.cand_n, 1u);
-                    sh.ckey[slot] = k[q];
+        for (int j = 0; j < NSL; ++j) {
+            if (j < nsl) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) atomicAdd(&sh.hist[k[4 * j + c] >> 20], 1u);
+            }
+        }
+        __syncthreads();
+        block_find<NT, kBins, true>(sh.hist, K, sh, tid, lane, wave);
+        if (sh.total <= K) {
+            all = true;  // the segment holds at most K keys
+        } else {
+            const uint32_t bin = sh.fd_bin;
+            uint32_t krem = K - sh.fd_above;
+            // ---- 2. list the keys of the threshold bin, per wave
+            uint32_t wc = 0;  // wave-uniform
+#pragma unroll
+            for (int j = 0; j < NSL; ++j) {
+                if (j < nsl) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint32_t key = k[4 * j + c];
+                        const bool hit = (key >> 20) == bin;
+                        const uint64_t bm = __ballot(hit);
+                        if (bm) {
+                            const uint32_t slot = wc + lanes_below(bm);
+                            if (hit && slot < kWaveCap) sh.cand[wave][slot] = key;
+                            wc += static_cast<uint32_t>(__popcll(bm));
+                        }
+                    }
+                }
+            }
+            if (lane == 0) sh.wcnt[wave] = wc;
+            __syncthreads();  // lists written; every thread is done with hist
+            bool overflow = false;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) overflow |= sh.wcnt[w] > kWaveCap;
+            uint32_t prefix = bin << 20, mask = 0xFFF00000u;
+            if (!overflow) {
+                if (wave == 0) {
+                    uint32_t *h = sh.hist;
+                    uint32_t cnt = 0;
+                    for (int pass = 0; pass < 2; ++pass) {
+                        const int shift = 10 - 10 * pass;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            *reinterpret_cast<uint4 *>(h + 16 * lane + 4 * v) =
+                                make_uint4(0u, 0u, 0u, 0u);
+                        wave_lds_sync();
+                        for (int w = 0; w < NW; ++w) {
+                            const int nw = static_cast<int>(sh.wcnt[w]);
+                            for (int i = lane; i < nw; i += kWave) {
+                                const uint32_t key = sh.cand[w][i];
+                                if ((key & mask) == prefix)
+                                    atomicAdd(&h[(key >> shift) & 1023u], 1u);
+                            }
+                        }
+                        wave_lds_sync();
+                        uint32_t d, ab;
+                        wave_find1024(h, krem, lane, d, ab, cnt);
+                        prefix |= d << shift;
+                        mask |= 1023u << shift;
+                        krem -= ab;
+                        wave_lds_sync();
+                    }
+                    if (lane == 0) {
+                        sh.thr = prefix;
+                        sh.quota = krem;
+                        sh.eqcnt = cnt;
+                    }
+                }
+                __syncthreads();
+            } else {
+                // crowded bin: resolve block-wide over the registers
+                uint32_t cnt = 0;
+                for (int pass = 0; pass < 2; ++pass) {
+                    const int shift = 10 - 10 * pass;
+                    for (int i = tid; i < 1024; i += NT) sh.hist[i] = 0u;
+                    __syncthreads();
+#pragma unroll
+                    for (int j = 0; j < NSL; ++j) {
+                        if (j < nsl) {
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                const uint32_t key = k[4 * j + c];
+                                if ((key & mask) == prefix)
+                                    atomicAdd(&sh.hist[(key >> shift) & 1023u], 1u);
+                            }
+                        }
+                    }
+                    __syncthreads();
+                    block_find<NT, 1024, false>(sh.hist, krem, sh, tid, lane, wave);
+                    const uint32_t d = sh.fd_bin;
+                    prefix |= d << shift;
+                    mask |= 1023u << shift;
+                    krem -= sh.fd_above;
+                    cnt = sh.hist[d];
+                    __syncthreads();
+                }
+                if (tid == 0) {
+                    sh.thr = prefix;
+                    sh.quota = krem;
+                    sh.eqcnt = cnt;
+                }
+                __syncthreads();
+            }
+            thr = sh.thr;
+            quota = sh.quota;
+            eqcnt = sh.eqcnt;
+        }
+    }
+    if (all) {
+        thr = kMinKey;
+        quota = 0;
+        eqcnt = 0;
+    }
+    const bool split = quota != eqcnt;  // only some of the keys equal to T are taken
+
+    // ---- 3. selection in index order.  First sweep: per-wave counts.
+    uint32_t gt_w = 0, eq_w = 0;
+#pragma unroll
+    for (int j = 0; j < NSL; ++j) {
+        if (j < nsl) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t key = k[4 * j + c];
+                if (!split) {
+                    gt_w += static_cast<uint32_t>(__popcll(__ballot(key >= thr)));
+                } else {
+                    gt_w += static_cast<uint32_t>(__popcll(__ballot(key > thr)));
+                    eq_w += static_cast<uint32_t>(__popcll(__ballot(key == thr)));
                 }
             }
         }
-        __syncthreads();
     }
-    uint32_t prefix = bin << 20, mask = 0xFFF00000u;
-    for (int pass = 0; pass < 2; ++pass) {
-        const int shift = 10 - 10 * pass;
-        uint32_t *h = sh.hist;  // reuse: 1024 bins
-        for (int i = tid; i < 1024; i += kNT) h[i] = 0;
-        __syncthreads();
-        if (in_lds) {
-            for (uint32_t j = tid; j < nbin; j += kNT) {
-                const uint32_t key = sh.ckey[j];
-                if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 1023u], 1u);
-            }
-        } else {
-            for (int64_t base = 0; base < n; base += TILE) {
-                if (!RESIDENT) load_keys<VPT>(s, n, base, lane, wave, k);
+    if (lane == 0) sh.wtot[wave] = (eq_w << 16) | gt_w;  // each <= 64*VPT <= 2048
+    __syncthreads();
+    uint32_t gt_off = 0, eq_off = 0, gt_all = 0;
 #pragma unroll
-                for (int q = 0; q < VPT; ++q)
-                    if ((k[q] & mask) == prefix) atomicAdd(&h[(k[q] >> shift) & 1023u], 1u);
-            }
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t t = sh.wtot[w];
+        if (w < wave) {
+            gt_off += t & 0xFFFFu;
+            eq_off += t >> 16;
         }
-        __syncthreads();
-        find_digit<1>(h, 1024, krem, sh, tid, lane, wave);
-        prefix |= sh.sel_bin << shift;
-        mask |= 1023u << shift;
-        krem -= sh.sel_above;
-        __syncthreads();
+        gt_all += t & 0xFFFFu;
     }
-    const uint32_t thr = prefix;   // key of the K-th largest
-    const uint32_t quota = krem;   // keys equal to thr that are taken
+    const uint32_t nsel = split ? K : gt_all;  // selected in this segment
 
-    // ---- 3. ordered compaction.  Per 256-key slice j the wave scans packed
-    // (eq << 16 | gt) counts (a tile holds at most 32,768 keys, so neither
-    // half overflows); a first sweep only totals them per wave, the second
-    // recomputes the scans and writes, so no per-slice state is kept.
-    uint32_t gt_all = 0, eq_all = 0;  // over earlier tiles
-    for (int64_t base = 0; base < n; base += TILE) {
-        if (!RESIDENT) load_keys<VPT>(s, n, base, lane, wave, k);
-        auto slice_counts = [&](int j) -> uint32_t {
-            uint32_t gt = 0, eq = 0;
+    // second sweep: emit
+    const int64_t obase = DST == 0 ? row * a.K : row * a.cout_ld + static_cast<int64_t>(seg) * a.K;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                gt += k[4 * j + c] > thr;
-                eq += k[4 * j + c] == thr;
-            }
-            return (eq << 16) | gt;
-        };
-        auto wave_incl = [&](uint32_t x) -> uint32_t {
+    for (int j = 0; j < NSL; ++j) {
+        if (j < nsl) {
+            const int64_t lbase = seg_base + w0 + 256 * j + 4 * lane;
+            if (!split) {
+                uint64_t bm[4];
+                uint32_t rk = gt_off;
 #pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const uint32_t y = __shfl_up(x, off, kWave);
-                if (lane >= off) x += y;
-            }
-            return x;
-        };
-        uint32_t wave_run = 0;
+                for (int c = 0; c < 4; ++c) {
+                    bm[c] = __ballot(k[4 * j + c] >= thr);
+                    rk += lanes_below(bm[c]);
+                }
 #pragma unroll
-        for (int j = 0; j < VPT / 4; ++j) wave_run += __shfl(wave_incl(slice_counts(j)), kWave - 1, kWave);
-        if (lane == 0) sh.wsum[wave] = wave_run;
-        __syncthreads();
-        uint32_t run = 0, tile_total = 0;
-        for (int w = 0; w < kNW; ++w) {
-            const uint32_t tw = sh.wsum[w];
-            if (w < wave) run += tw;
-            tile_total += tw;
-        }
-        __syncthreads();
+                for (int c = 0; c < 4; ++c) {
+                    if (k[4 * j + c] >= thr) {
+                        emit_one<SRC, DST>(a, row, obase, lbase + c, rk, k[4 * j + c]);
+                        ++rk;
+                    }
+                    gt_off += static_cast<uint32_t>(__popcll(bm[c]));
+                }
+            } else {
+                uint64_t bg[4], be[4];
+                uint32_t gr = gt_off, er = eq_off;
 #pragma unroll
-        for (int j = 0; j < VPT / 4; ++j) {
-            const uint32_t v = slice_counts(j);
-            const uint32_t x = wave_incl(v);
-            const uint32_t b0 = run + x - v;
-            run += __shfl(x, kWave - 1, kWave);
-            uint32_t gt_before = gt_all + (b0 & 0xFFFFu);
-            uint32_t eq_before = eq_all + (b0 >> 16);
+                for (int c = 0; c < 4; ++c) {
+                    bg[c] = __ballot(k[4 * j + c] > thr);
+                    be[c] = __ballot(k[4 * j + c] == thr);
+                    gr += lanes_below(bg[c]);
+                    er += lanes_below(be[c]);
+                }
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int q = 4 * j + c;
-                const bool gt = k[q] > thr, eq = k[q] == thr;
-                const uint32_t pos = gt_before + (eq_before < quota ? eq_before : quota);
-                if ((gt || (eq && eq_before < quota)) && pos < static_cast<uint32_t>(K))
-                    out[pos] = static_cast<int32_t>(elem_index<VPT>(base, wave, lane, q));
-                gt_before += gt;
-                eq_before += eq;
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t key = k[4 * j + c];
+                    const bool gt = key > thr, eq = key == thr;
+                    if (gt || (eq && er < quota))
+                        emit_one<SRC, DST>(a, row, obase, lbase + c, gr + min(er, quota), key);
+                    gr += gt;
+                    er += eq;
+                    gt_off += static_cast<uint32_t>(__popcll(bg[c]));
+                    eq_off += static_cast<uint32_t>(__popcll(be[c]));
+                }
             }
         }
-        gt_all += tile_total & 0xFFFFu;
-        eq_all += tile_total >> 16;
     }
-    if (tid == 0) n_sel[row] = K;
+    // pad the unused slots
+    if (DST == 0) {
+        for (uint32_t i = nsel + tid; i < K; i += NT) a.blk_idx[obase + i] = -1;
+        if (tid == 0) a.n_sel[row] = static_cast<int32_t>(nsel);
+    } else {
+        for (uint32_t i = nsel + tid; i < K; i += NT) {
+            a.okey[obase + i] = 0u;
+            a.oidx[obase + i] = -1;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ plan --
+TopkPlan topk_plan(int64_t rows, int64_t nmax, int K) {
+    TopkPlan pl{};
+    int64_t e = nmax;
+    while (pl.npass < 4) {
+        const bool fits = e <= kSegBig;
+        if (fits && (rows >= 128 || e <= 8192)) break;
+        const int64_t big_wgs = rows * ((e + kSegBig - 1) / kSegBig);
+        const int64_t seg = (big_wgs < 512 && 4 * K <= kSegSmall) ? kSegSmall : kSegBig;
+        const int64_t e2 = (e + seg - 1) / seg * K;
+        if (e2 >= e) break;
+        pl.seg[pl.npass] = seg;
+        pl.entries[pl.npass] = e2;
+        ++pl.npass;
+        e = e2;
+    }
+    pl.final_entries = e;
+    // ping-pong candidate buffers (keys, then indices); rows padded to 4 entries
+    int64_t ea = 0, eb = 0;
+    for (int i = 0; i < pl.npass; ++i) {
+        const int64_t ld = (pl.entries[i] + 3) / 4 * 4;
+        if (i % 2 == 0)
+            ea = ea > ld ? ea : ld;
+        else
+            eb = eb > ld ? eb : ld;
+    }
+    pl.ld[0] = ea;
+    pl.ld[1] = eb;
+    pl.ws_bytes = static_cast<size_t>(rows) * static_cast<size_t>(ea + eb) * 8u;
+    return pl;
 }
 
 hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64_t pos0,
                        const int64_t *seq_len, int64_t nb_max, int r, int K, int32_t *blk_idx,
-                       int32_t *n_sel, hipStream_t s) {
+                       int32_t *n_sel, void *ws, hipStream_t s) {
     const int64_t rows = static_cast<int64_t>(B) * Tq;
     if (rows == 0) return hipSuccess;
-    // the longest row any query of the call can have
-    const int64_t nmax = seq_len ? nb_max
-                                 : min(num_complete_blocks(pos0 + Tq - 1, r), nb_max);
-    const dim3 grid(static_cast<uint32_t>(rows));
-    if (nmax <= 32 * kNT)
-        hipLaunchKernelGGL((topk_kernel<32, true>), grid, dim3(kNT), 0, s, scores, Tq, ld, pos0,
-                           seq_len, nb_max, r, K, blk_idx, n_sel);
-    else
-        hipLaunchKernelGGL((topk_kernel<16, false>), grid, dim3(kNT), 0, s, scores, Tq, ld, pos0,
-                           seq_len, nb_max, r, K, blk_idx, n_sel);
+    const TopkPlan pl = topk_plan(rows, nb_max, K);
+    TopkArgs a{};
+    a.scores = scores;
+    a.ld = ld;
+    a.blk_idx = blk_idx;
+    a.n_sel = n_sel;
+    a.Tq = Tq;
+    a.pos0 = pos0;
+    a.nb_max = nb_max;
+    a.seq_len = seq_len;
+    a.r = r;
+    a.K = K;
+    uint32_t *buf_key[2];
+    int32_t *buf_idx[2];
+    char *w = static_cast<char *>(ws);
+    for (int b = 0; b < 2; ++b) {
+        buf_key[b] = reinterpret_cast<uint32_t *>(w);
+        if (w) w += rows * pl.ld[b] * 4;
+        buf_idx[b] = reinterpret_cast<int32_t *>(w);
+        if (w) w += rows * pl.ld[b] * 4;
+    }
+    const uint32_t gx = static_cast<uint32_t>(rows);
+    for (int i = 0; i < pl.npass; ++i) {
+        a.nprev = i;
+        a.okey = buf_key[i % 2];
+        a.oidx = buf_idx[i % 2];
+        a.cout_ld = pl.ld[i % 2];
+        if (i > 0) {
+            a.ckey = buf_key[(i - 1) % 2];
+            a.cidx = buf_idx[(i - 1) % 2];
+            a.cin_ld = pl.ld[(i - 1) % 2];
+        }
+        const int64_t e_in = i == 0 ? nb_max : pl.entries[i - 1];
+        const dim3 grid(gx, static_cast<uint32_t>((e_in + pl.seg[i] - 1) / pl.seg[i]));
+        if (pl.seg[i] == kSegSmall) {
+            if (i == 0)
+                hipLaunchKernelGGL((topk_pass<256, 16, 0, 1>), grid, dim3(256), 0, s, a);
+            else
+                hipLaunchKernelGGL((topk_pass<256, 16, 1, 1>), grid, dim3(256), 0, s, a);
+        } else {
+            if (i == 0)
+                hipLaunchKernelGGL((topk_pass<1024, 32, 0, 1>), grid, dim3(1024), 0, s, a);
+            else
+                hipLaunchKernelGGL((topk_pass<1024, 32, 1, 1>), grid, dim3(1024), 0, s, a);
+        }
+        a.prev_seg[i] = pl.seg[i];
+    }
+    a.nprev = pl.npass;
+    if (pl.npass > 0) {
+        a.ckey = buf_key[(pl.npass - 1) % 2];
+        a.cidx = buf_idx[(pl.npass - 1) % 2];
+        a.cin_ld = pl.ld[(pl.npass - 1) % 2];
+        hipLaunchKernelGGL((topk_pass<1024, 32, 1, 0>), dim3(gx), dim3(1024), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((topk_pass<1024, 32, 0, 0>), dim3(gx), dim3(1024), 0, s, a);
+    }
     return hipGetLastError();
 }
 

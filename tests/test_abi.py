@@ -130,14 +130,22 @@ def test_topk_validation(lib):
     assert topk(lib, ld=2) == SHAPE
     assert topk(lib, K=4096) == UNSUP
     assert topk(lib, s=MIS) == ALIGN
+    assert topk(lib, nb=5, ld=6) == SHAPE               # rows must be 16-byte strided
+    # rows longer than one segment need candidate lists in the workspace
+    lib.qsa_topk_workspace_bytes.restype = ctypes.c_size_t
+    assert lib.qsa_topk_workspace_bytes(1, I64(8192), I64(32768), 512) == 0
+    assert lib.qsa_topk_workspace_bytes(32, I64(1), I64(65536), 512) > 0
+    assert topk(lib, B=32, Tq=1, nb=65536, ld=65536) == WORKSPACE
 
 
 def test_select_validation(lib):
     lib.qsa_select_workspace_bytes.restype = ctypes.c_size_t
-    # prefill form runs fused on chip: no workspace
-    assert lib.qsa_select_workspace_bytes(1, I64(131072), I64(32768), 512) == 0
-    # budgets above 512 fall back to chunked scores in the workspace
-    assert lib.qsa_select_workspace_bytes(1, I64(131072), I64(32768), 1024) > 0
+    # prefill form: scores of one chunk of rows (at most 1 GiB) in the workspace
+    need = lib.qsa_select_workspace_bytes(1, I64(131072), I64(32768), 512)
+    assert (1 << 29) <= need <= (1 << 30) + (1 << 20)
+    st = lib.qsa_select_blocks(vp(P), vp(P), 1, I64(131072), I64(0), None, I64(32768), 4, 128, 4,
+                               0, 512, vp(P), vp(P), vp(P), ctypes.c_size_t(need - 1), None)
+    assert st == WORKSPACE
     # decode form keeps one score row per sequence
     need = lib.qsa_select_workspace_bytes(32, I64(1), I64(65536), 512)
     assert need >= 32 * 65536 * 4

@@ -114,6 +114,18 @@ def test_index_scores_parity(qsa, mode, Tq, pos0):
 
 
 # ------------------------------------------------------------------ A4 top-K
+def run_topk(qsa, scores, B, Tq, ld, pos0, lens, nb_max, K):
+    """qsa_topk_blocks with the workspace it asks for; returns (blk, n_sel)."""
+    torch = _torch()
+    blk = torch.empty((B * Tq, K), dtype=torch.int32, device="cuda")
+    ns = torch.empty((B * Tq,), dtype=torch.int32, device="cuda")
+    wsb = qsa.qsa_topk_workspace_bytes(B, Tq, nb_max, K)
+    ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device="cuda")
+    qsa.qsa_topk_blocks(scores, B, Tq, ld, pos0, lens, nb_max, 4, K, blk, ns, ws, wsb)
+    torch.cuda.synchronize()
+    return blk.cpu().numpy(), ns.cpu().numpy()
+
+
 @pytest.mark.parametrize("K", [1, 3, 64, 512])
 def test_topk_exact_on_shared_scores(qsa, K):
     """Given the same fp32 scores, the GPU selection equals the oracle's
@@ -127,11 +139,10 @@ def test_topk_exact_on_shared_scores(qsa, K):
     s[5] = 0.0                                   # an all-tie row
     s[7, ::2] = -0.0                             # signed zeros compare equal
     s[7, 1::2] = 0.0
-    blk = torch.empty((Tq, K), dtype=torch.int32, device="cuda")
-    ns = torch.empty((Tq,), dtype=torch.int32, device="cuda")
-    qsa.qsa_topk_blocks(dev(s), 1, Tq, nb, pos0, None, nb, 4, K, blk, ns)
-    torch.cuda.synchronize()
-    g, n = blk.cpu().numpy(), ns.cpu().numpy()
+    ld = (nb + 3) // 4 * 4
+    sp = np.zeros((Tq, ld), dtype=np.float32)
+    sp[:, :nb] = s
+    g, n = run_topk(qsa, dev(sp), 1, Tq, ld, pos0, None, nb, K)
     for t in range(Tq):
         nc = (pos0 + t + 1) // 4
         row = s[t, :nc].astype(np.float64)
@@ -147,11 +158,7 @@ def test_topk_decode_form_and_small_contexts(qsa):
     B, nb_max, K = 6, 5000, 512
     lens = np.array([1, 3, 4, 2049, 2052, 20000], dtype=np.int64)
     s = np.random.default_rng(9).standard_normal((B, nb_max)).astype(np.float32)
-    blk = torch.empty((B, K), dtype=torch.int32, device="cuda")
-    ns = torch.empty((B,), dtype=torch.int32, device="cuda")
-    qsa.qsa_topk_blocks(dev(s), B, 1, nb_max, 0, dev(lens), nb_max, 4, K, blk, ns)
-    torch.cuda.synchronize()
-    g, n = blk.cpu().numpy(), ns.cpu().numpy()
+    g, n = run_topk(qsa, dev(s), B, 1, nb_max, 0, dev(lens), nb_max, K)
     for b in range(B):
         nc = min(int(lens[b]) // 4, nb_max)
         want, _, _ = oracle.topk_row(s[b, :nc].astype(np.float64), K)
@@ -159,9 +166,9 @@ def test_topk_decode_form_and_small_contexts(qsa):
 
 
 def test_topk_long_rows_and_heavy_ties(qsa):
-    """Rows past the register-resident size (streamed path) and threshold
-    bins too full for the LDS buffer (whole-row resolve), K = 512."""
-    torch = _torch()
+    """Rows longer than one segment (reduced over per-segment top-K lists),
+    threshold bins too crowded for the per-wave lists (block-wide resolve),
+    and all-equal rows where the lowest indices must win, K = 512."""
     K, nb_max = 512, 100000
     lens = np.array([4 * 100000, 4 * 50000, 4 * 30000, 4 * 32768, 4 * 32769, 4 * 7000],
                     dtype=np.int64)
@@ -171,11 +178,41 @@ def test_topk_long_rows_and_heavy_ties(qsa):
     s[1] = 0.75                                        # one value: every key ties
     s[2] = rng.choice([0.0, 0.25, 0.5], size=nb_max)   # three values, bins of ~10,000
     s[5, :3000] = 1.0                                  # 3000 ties above the rest
-    blk = torch.empty((B, K), dtype=torch.int32, device="cuda")
-    ns = torch.empty((B,), dtype=torch.int32, device="cuda")
-    qsa.qsa_topk_blocks(dev(s), B, 1, nb_max, 0, dev(lens), nb_max, 4, K, blk, ns)
-    torch.cuda.synchronize()
-    g, n = blk.cpu().numpy(), ns.cpu().numpy()
+    g, n = run_topk(qsa, dev(s), B, 1, nb_max, 0, dev(lens), nb_max, K)
+    for b in range(B):
+        nc = min(int(lens[b]) // 4, nb_max)
+        want, _, _ = oracle.topk_row(s[b, :nc].astype(np.float64), K)
+        assert n[b] == want.size and np.array_equal(g[b, :n[b]], want), b
+
+
+@pytest.mark.parametrize("Tq,pos0,K", [(300, 4 * 40000, 512), (200, 4 * 70000, 2048),
+                                       (130, 4 * 40000, 1024)])
+def test_topk_prefill_rows_longer_than_a_segment(qsa, Tq, pos0, K):
+    """Prefill-form rows past 32,768 candidates: one reduction pass over
+    32,768-key segments (or 4,096-key ones when rows are few), then the final
+    pass; rows cut at every 4th query position."""
+    nb = (pos0 + Tq) // 4
+    ld = (nb + 3) // 4 * 4
+    rng = np.random.default_rng(K + Tq)
+    s = np.zeros((Tq, ld), dtype=np.float32)
+    s[:, :nb] = rng.standard_normal((Tq, nb)).astype(np.float32)
+    s[1::7, :nb] = np.round(s[1::7, :nb] * 2) / 2     # crowded rows
+    g, n = run_topk(qsa, dev(s), 1, Tq, ld, pos0, None, nb, K)
+    for t in range(0, Tq, 3):
+        nc = (pos0 + t + 1) // 4
+        want, _, _ = oracle.topk_row(s[t, :nc].astype(np.float64), K)
+        assert n[t] == want.size and np.array_equal(g[t, :n[t]], want), t
+
+
+def test_topk_million_token_decode_rows(qsa):
+    """Decode form at 1,048,576 tokens (262,144 blocks): two reduction passes
+    and the final pass; one row of random scores, one of coarse ties."""
+    K, nb_max, B = 512, 262144, 2
+    lens = np.array([4 * nb_max, 4 * nb_max - 5], dtype=np.int64)
+    rng = np.random.default_rng(5)
+    s = rng.standard_normal((B, nb_max)).astype(np.float32)
+    s[1] = np.round(s[1] * 8) / 8
+    g, n = run_topk(qsa, dev(s), B, 1, nb_max, 0, dev(lens), nb_max, K)
     for b in range(B):
         nc = min(int(lens[b]) // 4, nb_max)
         want, _, _ = oracle.topk_row(s[b, :nc].astype(np.float64), K)
@@ -213,9 +250,9 @@ def test_selection_tie_band(qsa, mode):
                                             (0, 700, 140000, 512), (1, 300, 1900, 512),
                                             (0, 37, 5, 3), (0, 300, 2000, 100),
                                             (1, 400, 12000, 1024)])
-def test_fused_select_matches_scores_plus_topk(qsa, mode, Tq, pos0, K):
-    """The fused prefill selector returns exactly what qsa_index_scores followed
-    by qsa_topk_blocks returns (same scores bit for bit, same tie order);
+def test_select_matches_scores_plus_topk(qsa, mode, Tq, pos0, K):
+    """qsa_select_blocks returns exactly what qsa_index_scores followed by
+    qsa_topk_blocks returns (same scores bit for bit, same tie order);
     RELUSUM rows near nc = K put the K-th score on a run of exact zeros."""
     torch = _torch()
     Tk = pos0 + Tq
@@ -225,20 +262,17 @@ def test_fused_select_matches_scores_plus_topk(qsa, mode, Tq, pos0, K):
     nb = kb.shape[0]
     ld = (nb + 3) // 4 * 4
     sc = torch.empty((Tq, ld), dtype=torch.float32, device="cuda")
-    b1 = torch.empty((Tq, K), dtype=torch.int32, device="cuda")
-    n1 = torch.empty((Tq,), dtype=torch.int32, device="cuda")
     b2 = torch.full((Tq, K), 7, dtype=torch.int32, device="cuda")
     n2 = torch.full((Tq,), 7, dtype=torch.int32, device="cuda")
     qd, kd = dev(qi), dev(kb)
     qsa.qsa_index_scores(qd, kd, 1, Tq, pos0, None, nb, 4, 128, 4, mode, sc, ld)
-    qsa.qsa_topk_blocks(sc, 1, Tq, ld, pos0, None, nb, 4, K, b1, n1)
+    b1, n1 = run_topk(qsa, sc, 1, Tq, ld, pos0, None, nb, K)
     wsb = qsa.qsa_select_workspace_bytes(1, Tq, nb, K)
-    assert (wsb == 0) == (K <= 512)   # budgets above 512 use chunked scores
     ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device="cuda")
     qsa.qsa_select_blocks(qd, kd, 1, Tq, pos0, None, nb, 4, 128, 4, mode, K, b2, n2, ws, wsb)
     torch.cuda.synchronize()
-    assert np.array_equal(n1.cpu().numpy(), n2.cpu().numpy())
-    assert np.array_equal(b1.cpu().numpy(), b2.cpu().numpy())
+    assert np.array_equal(n1, n2.cpu().numpy())
+    assert np.array_equal(b1, b2.cpu().numpy())
 
 
 # ---------------------------------------------------------- A6 attention
