@@ -267,6 +267,21 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a) {
                 group, lane);
 }
 
+// Split record in HBM: unnormalised O of head n (column n of O^T) at
+// [n * 256 + d], then the max of head n at [4096 + n] and its weight sum at
+// [4160 + n].  Lanes (n, g4) write float4 runs, 64 bytes per head.
+__device__ __forceinline__ void record_store(const WaveState &st, float *rec, int lane) {
+    const int n = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt)
+        *reinterpret_cast<float4 *>(rec + n * kHeadDim + 16 * dt + 4 * g4) =
+            make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
+    if (g4 == 0) {
+        rec[4096 + n] = st.m;
+        rec[4096 + 64 + n] = st.l;
+    }
+}
+
 // ------------------------------------------------------------------------
 // Decode: workgroup (4 waves) per (split, KV head, sequence); waves take the
 // split's stages round-robin, merge through LDS, and wave 0 writes the
@@ -326,11 +341,12 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit
         for (int w = 0; w < 3; ++w) state_merge(st, mbuf + w * kRecFloats, lane);
         st.l = head_total(st.l);
         float *rec = a.part + ((b * a.Hkv + g) * nsplit + split) * static_cast<int64_t>(kRecFloats);
-        state_store(st, rec, lane);
+        record_store(st, rec, lane);
     }
 }
 
-// Merge the split records: one thread per output element (b, head, d).
+// Merge the split records: one thread per output element (b, head, d), so
+// neighbouring threads read neighbouring record words.
 __global__ void __launch_bounds__(256) attn_decode_merge(AttnArgs a, int nsplit) {
     const int group = a.H / a.Hkv;
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -340,19 +356,17 @@ __global__ void __launch_bounds__(256) attn_decode_merge(AttnArgs a, int nsplit)
     const int hq = static_cast<int>((idx / kHeadDim) % a.H);
     const int64_t b = idx / (static_cast<int64_t>(kHeadDim) * a.H);
     const int g = hq / group, n = hq - g * group;
-    // record layout: O^T element (d, head n) at ((d/16)*4 + d%4)*64 + lane with
-    // lane = n + 16 * ((d % 16) / 4); m, l of head n at lane n
-    const int dt = d >> 4, g4 = (d & 15) >> 2, i = d & 3;
-    const int slot = (dt * 4 + i) * 64 + n + 16 * g4;
     const float *rec = a.part + (b * a.Hkv + g) * nsplit * static_cast<int64_t>(kRecFloats);
     float M = -INFINITY;
+#pragma unroll 8
     for (int s = 0; s < nsplit; ++s) M = fmaxf(M, rec[s * kRecFloats + 4096 + n]);
     const float Mu = M == -INFINITY ? 0.f : M;
     float acc = 0.f, lsum = 0.f;
+#pragma unroll 8
     for (int s = 0; s < nsplit; ++s) {
         const float *r = rec + s * static_cast<int64_t>(kRecFloats);
         const float w = exp2f(r[4096 + n] - Mu);
-        acc += r[slot] * w;
+        acc += r[n * kHeadDim + d] * w;
         lsum += r[4096 + 64 + n] * w;
     }
     a.O[(b * a.H + hq) * kHeadDim + d] = lsum > 0.f ? acc / lsum : 0.f;
@@ -378,8 +392,9 @@ hipError_t launch_dense_gather_prefill(const AttnArgs &a, hipStream_t s) {
 
 int decode_num_splits(int B, int Hkv, int64_t max_entries) {
     const int64_t nstages = (max_entries + kStageEntries - 1) / kStageEntries;
-    // about 1024 workgroups (4 per CU), at least one stage per wave
-    int64_t want = (1024 + static_cast<int64_t>(B) * Hkv - 1) / (static_cast<int64_t>(B) * Hkv);
+    // about 512 workgroups (the two per CU that fit at once), at least one
+    // stage per wave
+    int64_t want = (512 + static_cast<int64_t>(B) * Hkv - 1) / (static_cast<int64_t>(B) * Hkv);
     const int64_t cap = (nstages + 3) / 4;  // at least one stage per wave
     if (want > cap) want = cap;
     if (want < 1) want = 1;

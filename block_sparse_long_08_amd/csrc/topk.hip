@@ -29,6 +29,7 @@ constexpr int kWaveCap = 256;              // bin-B keys one wave may list
 constexpr uint32_t kMinKey = 0x00100000u;  // smaller keys: empty slots (0) and NaNs only
 constexpr int kSegBig = 32768;             // 1024 threads x 32 keys
 constexpr int kSegSmall = 4096;            // 256 threads x 16 keys
+constexpr int kSegMid = 8192;              // 256 threads x 32 keys
 
 struct TopkArgs {
     const float *scores;     // source 0: fp32 score rows
@@ -51,7 +52,11 @@ struct TopkArgs {
 template <int NT>
 struct TopkSmem {
     static constexpr int NW = NT / kWave;
-    uint32_t hist[kBins];
+    // Copies of the first-digit histogram (lane l counts into copy
+    // l % NREP).  More copies spread the atomics of a wave over more
+    // addresses but cost LDS and zeroing; one copy measured best overall.
+    static constexpr int NREP = 1;
+    uint32_t hist[kBins * NREP];
     uint32_t cand[NW][kWaveCap];
     uint32_t wcnt[NW];
     uint32_t wtot[NW];
@@ -81,22 +86,41 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
 }
 
 // Rank search over NBINS counts held in LDS (bin NBINS-1 is the largest
-// digit).  Thread t owns PER consecutive digits, descending from
-// NBINS-1-PER*t.  Finds the digit holding rank krem (1-based, counted from
-// the top) and the count above it; the total count goes to sh.total.
-// SKIP0: bin 0 holds empty slots and is not counted.
-template <int NT, int NBINS, bool SKIP0>
+// digit), each stored as NREP consecutive partial counts.  Thread t owns PER
+// consecutive digits, descending from NBINS-1-PER*t.  Finds the digit holding
+// rank krem (1-based, counted from the top) and the count above it; the
+// total count goes to sh.total.  SKIP0: bin 0 holds empty slots and is not
+// counted.
+template <int NT, int NBINS, int NREP, bool SKIP0>
 __device__ __forceinline__ void block_find(const uint32_t *h, uint32_t krem, TopkSmem<NT> &sh,
                                            int tid, int lane, int wave) {
     constexpr int PER = NBINS / NT;
     static_assert(PER >= 1 && NBINS % NT == 0, "bins per thread");
+    static_assert((PER * NREP) % 4 == 0 || PER * NREP < 4, "vector reads");
     const int base = NBINS - PER * (tid + 1);
+    uint32_t w[PER * NREP];
+    if constexpr ((PER * NREP) % 4 == 0) {
+#pragma unroll
+        for (int v = 0; v < PER * NREP / 4; ++v) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(h + base * NREP + 4 * v);
+            w[4 * v + 0] = q.x;
+            w[4 * v + 1] = q.y;
+            w[4 * v + 2] = q.z;
+            w[4 * v + 3] = q.w;
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < PER * NREP; ++v) w[v] = h[base * NREP + v];
+    }
     uint32_t c[PER];
     uint32_t local = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int d = base + PER - 1 - i;
-        c[i] = (SKIP0 && d == 0) ? 0u : h[d];
+        uint32_t x = 0;
+#pragma unroll
+        for (int r = 0; r < NREP; ++r) x += w[(PER - 1 - i) * NREP + r];
+        c[i] = (SKIP0 && d == 0) ? 0u : x;
         local += c[i];
     }
     const uint32_t x = wave_incl_scan(local, lane);
@@ -104,9 +128,9 @@ __device__ __forceinline__ void block_find(const uint32_t *h, uint32_t krem, Top
     __syncthreads();
     uint32_t before = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < TopkSmem<NT>::NW; ++w) {
-        const uint32_t t = sh.wtot[w];
-        before += w < wave ? t : 0u;
+    for (int wv = 0; wv < TopkSmem<NT>::NW; ++wv) {
+        const uint32_t t = sh.wtot[wv];
+        before += wv < wave ? t : 0u;
         total += t;
     }
     const uint32_t incl = x + before;
@@ -247,17 +271,21 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
     uint32_t thr = kMinKey, quota = 0, eqcnt = 0;
     if (!all) {
         // ---- 1. first digit
-        for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;
+        constexpr int NREP = TopkSmem<NT>::NREP;
+        for (int i = tid; i < kBins * NREP / 4; i += NT)
+            reinterpret_cast<uint4 *>(sh.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
         __syncthreads();
+        const int rep = lane % NREP;
 #pragma unroll
         for (int j = 0; j < NSL; ++j) {
             if (j < nsl) {
 #pragma unroll
-                for (int c = 0; c < 4; ++c) atomicAdd(&sh.hist[k[4 * j + c] >> 20], 1u);
+                for (int c = 0; c < 4; ++c)
+                    atomicAdd(&sh.hist[(k[4 * j + c] >> 20) * NREP + rep], 1u);
             }
         }
         __syncthreads();
-        block_find<NT, kBins, true>(sh.hist, K, sh, tid, lane, wave);
+        block_find<NT, kBins, NREP, true>(sh.hist, K, sh, tid, lane, wave);
         if (sh.total <= K) {
             all = true;  // the segment holds at most K keys
         } else {
@@ -298,12 +326,19 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
                             *reinterpret_cast<uint4 *>(h + 16 * lane + 4 * v) =
                                 make_uint4(0u, 0u, 0u, 0u);
                         wave_lds_sync();
-                        for (int w = 0; w < NW; ++w) {
-                            const int nw = static_cast<int>(sh.wcnt[w]);
-                            for (int i = lane; i < nw; i += kWave) {
-                                const uint32_t key = sh.cand[w][i];
-                                if ((key & mask) == prefix)
-                                    atomicAdd(&h[(key >> shift) & 1023u], 1u);
+                        // LPL lanes walk each list, all lists at once
+                        constexpr int LPL = kWave / NW;
+                        const int lw = lane / LPL, li0 = lane % LPL;
+                        const int nw = static_cast<int>(sh.wcnt[lw]);
+                        for (int i0 = li0; i0 < nw; i0 += 8 * LPL) {
+#pragma unroll
+                            for (int u = 0; u < 8; ++u) {
+                                const int i = i0 + u * LPL;
+                                if (i < nw) {
+                                    const uint32_t key = sh.cand[lw][i];
+                                    if ((key & mask) == prefix)
+                                        atomicAdd(&h[(key >> shift) & 1023u], 1u);
+                                }
                             }
                         }
                         wave_lds_sync();
@@ -340,7 +375,7 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
                         }
                     }
                     __syncthreads();
-                    block_find<NT, 1024, false>(sh.hist, krem, sh, tid, lane, wave);
+                    block_find<NT, 1024, 1, false>(sh.hist, krem, sh, tid, lane, wave);
                     const uint32_t d = sh.fd_bin;
                     prefix |= d << shift;
                     mask |= 1023u << shift;
@@ -541,13 +576,22 @@ hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64
         a.prev_seg[i] = pl.seg[i];
     }
     a.nprev = pl.npass;
+    // final pass: a 4-wave workgroup when the rows fit in 8,192 keys (a
+    // shorter chain of barriers), else 16 waves
+    const bool small = pl.final_entries <= kSegMid;
     if (pl.npass > 0) {
         a.ckey = buf_key[(pl.npass - 1) % 2];
         a.cidx = buf_idx[(pl.npass - 1) % 2];
         a.cin_ld = pl.ld[(pl.npass - 1) % 2];
-        hipLaunchKernelGGL((topk_pass<1024, 32, 1, 0>), dim3(gx), dim3(1024), 0, s, a);
+        if (small)
+            hipLaunchKernelGGL((topk_pass<256, 32, 1, 0>), dim3(gx), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((topk_pass<1024, 32, 1, 0>), dim3(gx), dim3(1024), 0, s, a);
     } else {
-        hipLaunchKernelGGL((topk_pass<1024, 32, 0, 0>), dim3(gx), dim3(1024), 0, s, a);
+        if (small)
+            hipLaunchKernelGGL((topk_pass<256, 32, 0, 0>), dim3(gx), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((topk_pass<1024, 32, 0, 0>), dim3(gx), dim3(1024), 0, s, a);
     }
     return hipGetLastError();
 }
