@@ -106,24 +106,39 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
     }
 }
 
-// Decode form: one query per sequence at seq_len[b] - 1.  Each wave scores 64
-// pooled keys read straight from HBM (MFMA rows 0..3 = the 4 heads, rows
-// 4..15 zero); the kernel is bound by streaming the key cache.
+// Decode form: one query per sequence at seq_len[b] - 1; the kernel streams
+// the pooled-key cache.  Each wave scores 64 pooled keys: 16 LDS-DMA
+// instructions copy them into a 16 KB tile, each instruction 1 KB of
+// contiguous HBM (4 keys), with the 16-byte chunks of row r stored at slot
+// chunk ^ (r % 16) so that the MFMA B-fragment reads (16 rows, one chunk
+// each) hit distinct banks.  MFMA rows 0..3 are the 4 heads, rows 4..15 zero.
 template <int MODE>
 __global__ void __launch_bounds__(256)
 index_scores_decode(const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ kbar,
                     const int64_t *__restrict__ seq_len, int64_t nb_max,
                     float *__restrict__ scores, int64_t ld) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[4 * 64 * kIdxDim * 2];
     const int64_t seq = blockIdx.y;
-    int64_t p = seq_len[seq] - 1;
+    const int64_t p = seq_len[seq] - 1;
     const int64_t nc = min(num_complete_blocks(p, kBlock), nb_max);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g4 = lane >> 4;
     const int64_t w0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * 64;  // first block
     if (w0 >= nc) return;
-    const uint16_t *q = q_idx + seq * (kIdxHeads * kIdxDim);
+    unsigned char *tile = lds + wave * (64 * kIdxDim * 2);
     const uint16_t *kb = kbar + seq * nb_max * kIdxDim;
-    float *out = scores + seq * ld;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int r = 4 * j + (lane >> 4);
+        int64_t blk = w0 + r;
+        blk = blk < nb_max ? blk : nb_max - 1;
+        const uint16_t *src = kb + blk * kIdxDim + 8 * ((lane & 15) ^ (r & 15));
+        // (C-style casts: the builtin takes explicit global / LDS address spaces)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                         (__attribute__((address_space(3))) void *)(tile + 1024 * j),
+                                         16, 0, 0);
+    }
+    const uint16_t *q = q_idx + seq * (kIdxHeads * kIdxDim);
     bf16x8 qf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -132,21 +147,20 @@ index_scores_decode(const uint16_t *__restrict__ q_idx, const uint16_t *__restri
                       : make_uint4(0, 0, 0, 0);
         qf[s] = as_bf16x8(v);
     }
-    uint4 kv[4][4];
+    float *out = scores + seq * ld;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile has landed
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        int64_t blk = w0 + 16 * j + n;
-        blk = blk < nb_max ? blk : nb_max - 1;
-        const uint16_t *src = kb + blk * kIdxDim + 8 * g4;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kv[j][s] = *reinterpret_cast<const uint4 *>(src + 32 * s);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int jt = 0; jt < 4; ++jt) {
+        const int row = 16 * jt + n;  // row % 16 == n
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma_bf16_16x16x32(qf[s], as_bf16x8(kv[j][s]), acc);
-        const int64_t blk = w0 + 16 * j + n;
+        for (int s = 0; s < 4; ++s) {
+            const uint4 kv =
+                *reinterpret_cast<const uint4 *>(tile + 256 * row + 16 * ((4 * s + g4) ^ n));
+            acc = mfma_bf16_16x16x32(qf[s], as_bf16x8(kv), acc);
+        }
+        const int64_t blk = w0 + row;
         if (g4 == 0 && blk < nc) out[blk] = combine_heads<MODE>(acc);
     }
 }

@@ -186,18 +186,20 @@ __device__ __forceinline__ void wave_find1024(const uint32_t *h, uint32_t krem, 
     cnt = __shfl(cn, src, kWave);
 }
 
-// Writes one selected element: gpos is its position in this pass's input
-// row, pos its output slot.
-template <int SRC, int DST>
-__device__ __forceinline__ void emit_one(const TopkArgs &a, int64_t row, int64_t obase,
-                                         int64_t gpos, uint32_t pos, uint32_t key) {
-    const int32_t idx = SRC == 0 ? static_cast<int32_t>(gpos) : a.cidx[row * a.cin_ld + gpos];
+// Writes one selected element (block index idx) to output slot pos.
+template <int DST>
+__device__ __forceinline__ void emit_one(const TopkArgs &a, int64_t obase, uint32_t pos,
+                                         int32_t idx, uint32_t key) {
     if (DST == 0) {
         a.blk_idx[obase + pos] = idx;
     } else {
         a.okey[obase + pos] = key;
         a.oidx[obase + pos] = idx;
     }
+}
+
+__device__ __forceinline__ int32_t pick(const int4 &v, int c) {
+    return c == 0 ? v.x : (c == 1 ? v.y : (c == 2 ? v.z : v.w));
 }
 
 // SRC 0: keys from fp32 score rows; SRC 1: candidate lists of a previous
@@ -433,12 +435,23 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
     }
     const uint32_t nsel = split ? K : gt_all;  // selected in this segment
 
-    // second sweep: emit
+    // second sweep: emit.  The block indices of candidate-list entries are
+    // fetched for all slices at once, before any store depends on them.
     const int64_t obase = DST == 0 ? row * a.K : row * a.cout_ld + static_cast<int64_t>(seg) * a.K;
+    int4 cidx[SRC == 1 ? NSL : 1];
+    if (SRC == 1) {
+        const int32_t *src = a.cidx + row * a.cin_ld + seg_base;
+#pragma unroll
+        for (int j = 0; j < NSL; ++j) {
+            const int i = w0 + 256 * j + 4 * lane;
+            cidx[j] = j < nsl ? *reinterpret_cast<const int4 *>(src + (i < m ? i : 0))
+                              : make_int4(0, 0, 0, 0);
+        }
+    }
 #pragma unroll
     for (int j = 0; j < NSL; ++j) {
         if (j < nsl) {
-            const int64_t lbase = seg_base + w0 + 256 * j + 4 * lane;
+            const int lbase = static_cast<int>(seg_base) + w0 + 256 * j + 4 * lane;
             if (!split) {
                 uint64_t bm[4];
                 uint32_t rk = gt_off;
@@ -450,7 +463,8 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     if (k[4 * j + c] >= thr) {
-                        emit_one<SRC, DST>(a, row, obase, lbase + c, rk, k[4 * j + c]);
+                        const int32_t idx = SRC == 0 ? lbase + c : pick(cidx[SRC == 1 ? j : 0], c);
+                        emit_one<DST>(a, obase, rk, idx, k[4 * j + c]);
                         ++rk;
                     }
                     gt_off += static_cast<uint32_t>(__popcll(bm[c]));
@@ -469,8 +483,10 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
                 for (int c = 0; c < 4; ++c) {
                     const uint32_t key = k[4 * j + c];
                     const bool gt = key > thr, eq = key == thr;
-                    if (gt || (eq && er < quota))
-                        emit_one<SRC, DST>(a, row, obase, lbase + c, gr + min(er, quota), key);
+                    if (gt || (eq && er < quota)) {
+                        const int32_t idx = SRC == 0 ? lbase + c : pick(cidx[SRC == 1 ? j : 0], c);
+                        emit_one<DST>(a, obase, gr + min(er, quota), idx, key);
+                    }
                     gr += gt;
                     er += eq;
                     gt_off += static_cast<uint32_t>(__popcll(bg[c]));

@@ -113,6 +113,31 @@ def test_index_scores_parity(qsa, mode, Tq, pos0):
     log(f"  worst |err|/bound = {worst:.3f}")
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_index_scores_decode_form(qsa, mode):
+    """Decode form: one query per sequence at seq_len - 1 over a per-sequence
+    pooled-key cache; ragged lengths (no block, a partial 64-block tile, a
+    cache longer than the sequence)."""
+    torch = _torch()
+    B, nb_max = 5, 17501
+    lens = np.array([1, 5, 259, 4 * 4097 + 2, 4 * nb_max], dtype=np.int64)
+    qi = synth.normal_bf16(4, (B, 4, 128), seed=17)
+    kb = np.stack([oracle.compress(synth.normal_bf16(5, (4 * nb_max, 128), seed=17 + b))
+                   for b in range(B)])
+    ld = (nb_max + 3) // 4 * 4
+    sc = torch.full((B, ld), float("nan"), dtype=torch.float32, device="cuda")
+    qsa.qsa_index_scores(dev(qi), dev(kb), B, 1, 0, dev(lens), nb_max, 4, 128, 4, mode, sc, ld)
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy()
+    for b in range(B):
+        p = int(lens[b]) - 1
+        ref = oracle.scores_row(qi[b], kb[b], p, mode=mode)
+        nc = ref.size
+        tol = _score_tol(qi[b:b + 1], kb[b], mode)[0, :nc]
+        d = np.abs(got[b, :nc] - ref)
+        assert np.all(d <= tol), (b, float(d.max()))
+
+
 # ------------------------------------------------------------------ A4 top-K
 def run_topk(qsa, scores, B, Tq, ld, pos0, lens, nb_max, K):
     """qsa_topk_blocks with the workspace it asks for; returns (blk, n_sel)."""
