@@ -1,0 +1,289 @@
+// A8 baseline: dense causal attention, prefill form (the reference point of
+// the QSA speedup; same softmax attention as chlience section 6 but over every
+// earlier token).  A flash-attention forward pass on MFMA:
+//
+// Workgroup: 128 queries of one head, 4 waves x 32 queries; KV tiles of 64
+// tokens stream through LDS, double-buffered, one barrier per tile.
+//   S^T[64 tok, 32 q] = K . Q^T   v_mfma_f32_32x32x16_bf16, K from LDS, Q^T
+//                                   fragments held in registers;
+//   online softmax per query column in fp32 (log2 domain) with lazy
+//   rescaling: the running reference max moves only when a tile's max
+//   exceeds it by more than 2^8, so P <= 256 and O, l are rarely rescaled;
+//   O^T[256, 32 q] += V^T . P^T   v_mfma_f32_32x32x16_f16: the S^T accumulator
+//                                   of a lane is exactly the P^T fragment it
+//                                   supplies (fp16, P <= 256), V^T read from a
+//                                   transposed fp16 LDS tile (bf16 -> fp16 is
+//                                   exact for |v| in the fp16 normal range).
+// MFMA 32x32x16 layouts (lane l, n = l%32, h = l/32):
+//   A[m][k]: row m = n, k-slots 8h .. 8h+7;  B[k][j]: column j = n, same slots;
+//   D[m][j]: column j = n, rows 8*(r/4) + 4h + r%4 for r = 0..15.
+// The S^T rows a lane holds for one 16-token step are tokens 4h..4h+3 and
+// 8+4h..8+4h+3; the V^T tile stores each 16-token group in that order
+// (slots 8h..8h+7), so every MFMA operand read is one 16-byte LDS read.
+#include "qsa_internal.h"
+
+namespace qsa {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kFaQ = 128;                // queries per workgroup
+constexpr int kFaN = 64;                 // tokens per KV tile
+constexpr int kFaKRow = 512;             // K tile row (256 bf16), 16-byte chunks swizzled
+constexpr int kFaKTile = kFaN * kFaKRow; // 32 KB
+constexpr int kFaVRow = 144;             // V^T tile row: 64 token slots + 16 B pad
+constexpr int kFaVTile = 256 * kFaVRow;  // 36 KB
+constexpr int kFaLds = 2 * kFaKTile + 2 * kFaVTile;
+constexpr float kFaScaleLog2 = 0.09016844005556021f;  // log2(e) / sqrt(256)
+constexpr float kFaLn2 = 0.6931471805599453f;
+constexpr float kFaSlack = 8.f;          // lazy-rescale threshold (log2 units)
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// fp16 pair (a in the low half) of two bf16 values; exact for magnitudes in
+// the fp16 normal range, where truncation and nearest rounding agree.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t lo_bits, uint32_t hi_bits) {
+    const auto v = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(lo_bits << 16),
+                                              __uint_as_float(hi_bits << 16));
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Slot of token t (0..63) in a V^T row: inside each 16-token group, tokens
+// 4h+i go to slot 8h+i and tokens 8+4h+i to slot 8h+4+i.
+__device__ __forceinline__ int vslot(int t) {
+    const int t16 = t & 15;
+    return (t & ~15) | (t16 & 3) | (((t16 >> 3) & 1) << 2) | (((t16 >> 2) & 1) << 3);
+}
+
+struct FaArgs {
+    const uint16_t *Q;  // [B][Tq][H][256]
+    const uint16_t *K;  // [B][Lmax][Hkv][256]
+    const uint16_t *V;
+    float *O;           // [B][Tq][H][256]
+    float *lse;         // [B][Tq][H] or nullptr
+    int64_t Tq, Lmax, pos0;
+    int H, Hkv;
+};
+
+// K tile: 64 rows of 512 B; wave w copies rows 16w .. 16w+15 by LDS DMA, lane
+// l of instruction j landing on row 16w + 2j + l/32, slot l%32, which holds
+// chunk slot ^ (row % 32) of that token.
+__device__ __forceinline__ void fa_load_k(const uint16_t *Kg, int64_t rs, int64_t tok0,
+                                          int64_t tok_max, unsigned char *kbuf, int wave,
+                                          int lane) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int r = 16 * wave + 2 * j + (lane >> 5);
+        int64_t tok = tok0 + r;
+        tok = tok < tok_max ? tok : tok_max - 1;
+        const int chunk = (lane & 31) ^ (r & 31);
+        const uint16_t *src = Kg + tok * rs + 8 * chunk;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                         (__attribute__((address_space(3))) void *)(
+                                             kbuf + (16 * wave + 2 * j) * kFaKRow),
+                                         16, 0, 0);
+    }
+}
+
+// V tile into registers: thread t takes tokens 4a .. 4a+3 (a = t % 16) and
+// dims 8c .. 8c+7 for c = t / 16 and t / 16 + 16.
+__device__ __forceinline__ void fa_load_v(const uint16_t *Vg, int64_t rs, int64_t tok0,
+                                          int64_t tok_max, int tid, uint4 (&v)[2][4]) {
+    const int a = tid & 15, c0 = tid >> 4;
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+        const int c = c0 + 16 * pr;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            int64_t tok = tok0 + 4 * a + u;
+            tok = tok < tok_max ? tok : tok_max - 1;
+            v[pr][u] = *reinterpret_cast<const uint4 *>(Vg + tok * rs + 8 * c);
+        }
+    }
+}
+
+// ... and transposed into the V^T tile as fp16: for each of the 8 dims, the
+// 4 tokens' values as one 8-byte write.
+__device__ __forceinline__ void fa_store_vt(const uint4 (&v)[2][4], unsigned char *vbuf, int tid) {
+    const int a = tid & 15, c0 = tid >> 4;
+    const int slot = vslot(4 * a);
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+        const int c = c0 + 16 * pr;
+        const uint32_t w[4][4] = {{v[pr][0].x, v[pr][0].y, v[pr][0].z, v[pr][0].w},
+                                  {v[pr][1].x, v[pr][1].y, v[pr][1].z, v[pr][1].w},
+                                  {v[pr][2].x, v[pr][2].y, v[pr][2].z, v[pr][2].w},
+                                  {v[pr][3].x, v[pr][3].y, v[pr][3].z, v[pr][3].w}};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            // dim 2k: low halves of word k; dim 2k+1: high halves
+            const uint32_t lo0 = bf16x2_to_f16x2(w[0][k] & 0xFFFFu, w[1][k] & 0xFFFFu);
+            const uint32_t lo1 = bf16x2_to_f16x2(w[2][k] & 0xFFFFu, w[3][k] & 0xFFFFu);
+            const uint32_t hi0 = bf16x2_to_f16x2(w[0][k] >> 16, w[1][k] >> 16);
+            const uint32_t hi1 = bf16x2_to_f16x2(w[2][k] >> 16, w[3][k] >> 16);
+            *reinterpret_cast<uint2 *>(vbuf + (8 * c + 2 * k) * kFaVRow + 2 * slot) =
+                make_uint2(lo0, lo1);
+            *reinterpret_cast<uint2 *>(vbuf + (8 * c + 2 * k + 1) * kFaVRow + 2 * slot) =
+                make_uint2(hi0, hi1);
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) fa_prefill_kernel(FaArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char fa_lds[kFaLds];
+    unsigned char *const kbase = fa_lds;                 // two K tiles
+    unsigned char *const vbase = fa_lds + 2 * kFaKTile;  // two V^T tiles
+
+    const int qblk = gridDim.x - 1 - blockIdx.x;  // longest rows first
+    const int hq = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, h = lane >> 5;
+    const int group = a.H / a.Hkv, g = hq / group;
+    const int64_t rs = static_cast<int64_t>(a.Hkv) * kHeadDim;
+    const uint16_t *Kg = a.K + b * a.Lmax * rs + g * kHeadDim;
+    const uint16_t *Vg = a.V + b * a.Lmax * rs + g * kHeadDim;
+
+    const int64_t q0 = static_cast<int64_t>(qblk) * kFaQ;
+    const int64_t q_last = min(q0 + kFaQ, a.Tq) - 1;
+    const int64_t tok_end = a.pos0 + q_last + 1;  // tokens the workgroup needs
+    const int ntiles = static_cast<int>((tok_end + kFaN - 1) / kFaN);
+    // this lane's query (column n of the wave's 32)
+    const int64_t tq = q0 + 32 * wave + n;
+    const int64_t qpos = a.pos0 + (tq < a.Tq ? tq : a.Tq - 1);
+    const int64_t wave_first = a.pos0 + min(q0 + 32 * wave, a.Tq - 1);
+    const int64_t wave_last = a.pos0 + min(q0 + 32 * wave + 31, a.Tq - 1);
+
+    // Q^T fragments: dims 16*ks + 8h .. +7 of query tq
+    bf16x8 qf[16];
+    {
+        const uint16_t *src =
+            a.Q + ((b * a.Tq + (tq < a.Tq ? tq : a.Tq - 1)) * a.H + hq) * kHeadDim + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(src + 16 * ks));
+    }
+
+    f32x16 o[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+    float m_ref = -INFINITY, l = 0.f;
+
+    uint4 vreg[2][4];
+    fa_load_k(Kg, rs, 0, a.Lmax, kbase, wave, lane);
+    fa_load_v(Vg, rs, 0, a.Lmax, tid, vreg);
+    fa_store_vt(vreg, vbase, tid);
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int cur = it & 1;
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's K DMA landed
+        __syncthreads();                     // every wave's K DMA and V^T writes visible
+        const int64_t tile0 = static_cast<int64_t>(it) * kFaN;
+        const bool more = it + 1 < ntiles;
+        if (more) {
+            fa_load_k(Kg, rs, tile0 + kFaN, a.Lmax, kbase + (cur ^ 1) * kFaKTile, wave, lane);
+            fa_load_v(Vg, rs, tile0 + kFaN, a.Lmax, tid, vreg);
+        }
+        // two 32-token halves, each: S^T, softmax, P^T . V accumulation
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int64_t sub0 = tile0 + 32 * tt;
+            if (sub0 > wave_last) break;  // no query of this wave sees these tokens
+            f32x16 s;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = 0.f;
+            const unsigned char *krow = kbase + cur * kFaKTile + (32 * tt + n) * kFaKRow;
+#pragma unroll
+            for (int ks = 0; ks < 16; ++ks) {
+                const int slot = (2 * ks + h) ^ n;  // row % 32 == n
+                const uint4 kv = *reinterpret_cast<const uint4 *>(krow + 16 * slot);
+                s = mfma32(as_bf16x8(kv), qf[ks], s);
+            }
+            // online softmax of this lane's query column
+            const bool diag = sub0 + 31 > wave_first;
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float x = s[r] * kFaScaleLog2;
+                if (diag) {
+                    const int64_t tok = sub0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    x = tok <= qpos ? x : -INFINITY;
+                }
+                s[r] = x;
+                tmax = fmaxf(tmax, x);
+            }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            if (__ballot(tmax > m_ref + kFaSlack)) {
+                const float m_new = fmaxf(m_ref, tmax);
+                const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_ref - m_new);
+                l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+                m_ref = m_new;
+            }
+            const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+            // P^T fragments (fp16, nearest) of the two 16-token steps
+            f16x8 pf[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const _Float16 ph = static_cast<_Float16>(exp2f(s[8 * kk + j] - m_use));
+                    l += static_cast<float>(ph);
+                    pf[kk][j] = ph;
+                }
+            }
+            const unsigned char *vt = vbase + cur * kFaVTile + n * kFaVRow + 64 * tt + 16 * h;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) {
+                    const uint4 vv =
+                        *reinterpret_cast<const uint4 *>(vt + 32 * dt * kFaVRow + 32 * kk);
+                    o[dt] = mfma32h(__builtin_bit_cast(f16x8, vv), pf[kk], o[dt]);
+                }
+            }
+        }
+        if (more) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // the V registers (and K DMA) landed
+            fa_store_vt(vreg, vbase + (cur ^ 1) * kFaVTile, tid);
+        }
+    }
+
+    // ---- normalise and store this lane's query column
+    l += __shfl_xor(l, 32);
+    if (tq < a.Tq) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        float *dst = a.O + ((b * a.Tq + tq) * a.H + hq) * kHeadDim;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq)
+                *reinterpret_cast<float4 *>(dst + 32 * dt + 8 * gq + 4 * h) =
+                    make_float4(o[dt][4 * gq] * inv, o[dt][4 * gq + 1] * inv,
+                                o[dt][4 * gq + 2] * inv, o[dt][4 * gq + 3] * inv);
+        if (a.lse && h == 0)
+            a.lse[(b * a.Tq + tq) * a.H + hq] =
+                l > 0.f ? (m_ref + log2f(l)) * kFaLn2 : -INFINITY;
+    }
+}
+
+hipError_t launch_dense_prefill(const AttnArgs &aa, hipStream_t s) {
+    if (aa.Tq == 0 || aa.B == 0) return hipSuccess;
+    FaArgs a{};
+    a.Q = aa.Q; a.K = aa.K; a.V = aa.V; a.O = aa.O; a.lse = aa.lse;
+    a.Tq = aa.Tq; a.Lmax = aa.Lmax; a.pos0 = aa.pos0; a.H = aa.H; a.Hkv = aa.Hkv;
+    const dim3 grid(static_cast<uint32_t>((aa.Tq + kFaQ - 1) / kFaQ),
+                    static_cast<uint32_t>(aa.H), static_cast<uint32_t>(aa.B));
+    hipLaunchKernelGGL(fa_prefill_kernel, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace qsa

@@ -302,7 +302,7 @@ int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, i
         const int nsplit = decode_num_splits(B, Hkv, Lmax / kBlock + 1);
         return launch_status(launch_attn_decode(a, nsplit, s));
     }
-    return launch_status(launch_dense_gather_prefill(a, s));
+    return launch_status(launch_dense_prefill(a, s));
 }
 
 }  // extern "C"

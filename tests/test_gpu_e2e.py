@@ -76,7 +76,8 @@ def test_prefill_T2048_budget64_all_rows(qsa, mode, kbar_mode):
 
 
 def test_prefill_within_budget_is_dense(qsa):
-    """Rows with nc <= K: QSA output equals the GPU dense kernel's."""
+    """Rows with nc <= K: QSA output equals the GPU dense kernel's (a
+    different kernel, fp16 P.V, so to the parity tolerance)."""
     torch = _torch()
     T, K = 600, 64
     x = synth.prefill_inputs(T, seed=1)
@@ -86,9 +87,7 @@ def test_prefill_within_budget_is_dense(qsa):
     qsa.dense_attn(layer.Qr, Kr, dev(x.V), 1, T, T, 0, None, 24, 2, 256, Od, None)
     torch.cuda.synchronize()
     n_dense = 4 * K + 3  # p < 259 -> nc(p) <= 64
-    d = np.abs(O[:n_dense] - Od.cpu().numpy()[:n_dense]).max()
-    log(f"  dense-equivalent rows max |QSA - dense| = {d:.2e}")
-    assert d < 1e-5
+    assert_close(O[:n_dense], Od.cpu().numpy()[:n_dense], "rows within budget: QSA vs dense")
 
 
 @pytest.mark.parametrize("T,K", [(1, 1), (2, 1), (3, 1), (4, 1), (5, 1), (9, 2), (17, 3),

@@ -351,6 +351,28 @@ def test_decode_attention_parity(qsa):
 
 
 # ------------------------------------------------------------- A8 dense
+@pytest.mark.parametrize("B,Tq,pos0", [(1, 517, 0), (1, 200, 777), (1, 1, 1000), (1, 129, 64),
+                                       (2, 100, 50)])
+def test_dense_prefill_flash_parity(qsa, B, Tq, pos0):
+    """Flash prefill over several 128-query blocks and 64-token tiles, ragged
+    tails, a chunk after pos0 cached tokens, one query, two sequences."""
+    torch = _torch()
+    Tk = pos0 + Tq
+    xs = [synth.prefill_inputs(Tq, pos0=pos0, seed=40 + 7 * b + Tq) for b in range(B)]
+    Q = np.stack([x.Q for x in xs])
+    K = np.stack([x.K for x in xs])
+    V = np.stack([x.V for x in xs])
+    O = torch.empty((B, Tq, 24, 256), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Tq, 24), dtype=torch.float32, device="cuda")
+    qsa.dense_attn(dev(Q), dev(K), dev(V), B, Tq, Tk, pos0, None, 24, 2, 256, O, lse)
+    torch.cuda.synchronize()
+    Og, lg = O.cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        Oref, lref = oracle.dense_rows(Q[b], K[b], V[b], np.arange(Tq), pos0=pos0)
+        assert_close(Og[b], Oref, f"flash prefill O (seq {b})")
+        assert_close(lg[b], lref, f"flash prefill lse (seq {b})")
+
+
 def test_dense_prefill_and_decode_parity(qsa):
     torch = _torch()
     T = 300
