@@ -2,10 +2,12 @@
 // the QSA speedup; same softmax attention as chlience section 6 but over every
 // earlier token).  A flash-attention forward pass on MFMA:
 //
-// Workgroup: 128 queries of one head, 4 waves x 32 queries; KV tiles of 64
-// tokens stream through LDS, double-buffered, one barrier per tile.
-//   S^T[64 tok, 32 q] = K . Q^T   v_mfma_f32_32x32x16_bf16, K from LDS, Q^T
-//                                   fragments held in registers;
+// Workgroup: 128 queries of one head, 4 waves x 32 queries; KV tiles of 32
+// tokens stream through LDS, double-buffered, one barrier per tile: the next
+// tile is loaded into registers while the current one is consumed, then
+// written to the other LDS buffer.
+//   S^T[32 tok, 32 q] = K . Q^T   v_mfma_f32_32x32x16_bf16, K and Q both from
+//                                   LDS (16-byte chunks XOR-swizzled by row);
 //   online softmax per query column in fp32 (log2 domain) with lazy
 //   rescaling: the running reference max moves only when a tile's max
 //   exceeds it by more than 2^8, so P <= 256 and O, l are rarely rescaled;
@@ -28,12 +30,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kFaQ = 128;                // queries per workgroup
-constexpr int kFaN = 64;                 // tokens per KV tile
+constexpr int kFaN = 32;                 // tokens per KV tile
 constexpr int kFaKRow = 512;             // K tile row (256 bf16), 16-byte chunks swizzled
-constexpr int kFaKTile = kFaN * kFaKRow; // 32 KB
-constexpr int kFaVRow = 144;             // V^T tile row: 64 token slots + 16 B pad
-constexpr int kFaVTile = 256 * kFaVRow;  // 36 KB
-constexpr int kFaLds = 2 * kFaKTile + 2 * kFaVTile;
+constexpr int kFaKTile = kFaN * kFaKRow; // 16 KB
+constexpr int kFaVRow = 80;              // V^T tile row: 32 token slots + 16 B pad
+constexpr int kFaVTile = 256 * kFaVRow;  // 20 KB
+constexpr int kFaQTile = kFaQ * 512;     // 64 KB: the workgroup's queries, chunks swizzled
+constexpr int kFaLds = kFaQTile + 2 * kFaKTile + 2 * kFaVTile;
 constexpr float kFaScaleLog2 = 0.09016844005556021f;  // log2(e) / sqrt(256)
 constexpr float kFaLn2 = 0.6931471805599453f;
 constexpr float kFaSlack = 8.f;          // lazy-rescale threshold (log2 units)
@@ -54,7 +57,7 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t lo_bits, uint32_t h
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Slot of token t (0..63) in a V^T row: inside each 16-token group, tokens
+// Slot of token t (0..31) in a V^T row: inside each 16-token group, tokens
 // 4h+i go to slot 8h+i and tokens 8+4h+i to slot 8h+4+i.
 __device__ __forceinline__ int vslot(int t) {
     const int t16 = t & 15;
@@ -71,74 +74,70 @@ struct FaArgs {
     int H, Hkv;
 };
 
-// K tile: 64 rows of 512 B; wave w copies rows 16w .. 16w+15 by LDS DMA, lane
-// l of instruction j landing on row 16w + 2j + l/32, slot l%32, which holds
-// chunk slot ^ (row % 32) of that token.
+// K tile into registers: thread t takes row t/8 (token) and the chunks
+// (16 B each) c = t%8 + 8u, u = 0..3, of that row.
 __device__ __forceinline__ void fa_load_k(const uint16_t *Kg, int64_t rs, int64_t tok0,
-                                          int64_t tok_max, unsigned char *kbuf, int wave,
-                                          int lane) {
+                                          int64_t tok_max, int tid, uint4 (&kr)[4]) {
+    const int r = tid >> 3;
+    int64_t tok = tok0 + r;
+    tok = tok < tok_max ? tok : tok_max - 1;
+    const uint16_t *src = Kg + tok * rs + 8 * (tid & 7);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = 16 * wave + 2 * j + (lane >> 5);
-        int64_t tok = tok0 + r;
-        tok = tok < tok_max ? tok : tok_max - 1;
-        const int chunk = (lane & 31) ^ (r & 31);
-        const uint16_t *src = Kg + tok * rs + 8 * chunk;
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                         (__attribute__((address_space(3))) void *)(
-                                             kbuf + (16 * wave + 2 * j) * kFaKRow),
-                                         16, 0, 0);
+    for (int u = 0; u < 4; ++u) kr[u] = *reinterpret_cast<const uint4 *>(src + 64 * u);
+}
+
+// ... and into the K tile: row r, chunk c at slot c ^ r.
+__device__ __forceinline__ void fa_store_k(const uint4 (&kr)[4], unsigned char *kbuf, int tid) {
+    const int r = tid >> 3;
+    unsigned char *row = kbuf + r * kFaKRow;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int c = (tid & 7) + 8 * u;
+        *reinterpret_cast<uint4 *>(row + 16 * (c ^ r)) = kr[u];
     }
 }
 
-// V tile into registers: thread t takes tokens 4a .. 4a+3 (a = t % 16) and
-// dims 8c .. 8c+7 for c = t / 16 and t / 16 + 16.
+// V tile into registers: thread t takes tokens 4a .. 4a+3 (a = t % 8) and
+// dims 8c .. 8c+7 (c = t / 8).
 __device__ __forceinline__ void fa_load_v(const uint16_t *Vg, int64_t rs, int64_t tok0,
-                                          int64_t tok_max, int tid, uint4 (&v)[2][4]) {
-    const int a = tid & 15, c0 = tid >> 4;
+                                          int64_t tok_max, int tid, uint4 (&v)[4]) {
+    const int a = tid & 7, c = tid >> 3;
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-        const int c = c0 + 16 * pr;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            int64_t tok = tok0 + 4 * a + u;
-            tok = tok < tok_max ? tok : tok_max - 1;
-            v[pr][u] = *reinterpret_cast<const uint4 *>(Vg + tok * rs + 8 * c);
-        }
+    for (int u = 0; u < 4; ++u) {
+        int64_t tok = tok0 + 4 * a + u;
+        tok = tok < tok_max ? tok : tok_max - 1;
+        v[u] = *reinterpret_cast<const uint4 *>(Vg + tok * rs + 8 * c);
     }
 }
 
 // ... and transposed into the V^T tile as fp16: for each of the 8 dims, the
 // 4 tokens' values as one 8-byte write.
-__device__ __forceinline__ void fa_store_vt(const uint4 (&v)[2][4], unsigned char *vbuf, int tid) {
-    const int a = tid & 15, c0 = tid >> 4;
+__device__ __forceinline__ void fa_store_vt(const uint4 (&v)[4], unsigned char *vbuf, int tid) {
+    const int a = tid & 7, c = tid >> 3;
     const int slot = vslot(4 * a);
+    const uint32_t w[4][4] = {{v[0].x, v[0].y, v[0].z, v[0].w},
+                              {v[1].x, v[1].y, v[1].z, v[1].w},
+                              {v[2].x, v[2].y, v[2].z, v[2].w},
+                              {v[3].x, v[3].y, v[3].z, v[3].w}};
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-        const int c = c0 + 16 * pr;
-        const uint32_t w[4][4] = {{v[pr][0].x, v[pr][0].y, v[pr][0].z, v[pr][0].w},
-                                  {v[pr][1].x, v[pr][1].y, v[pr][1].z, v[pr][1].w},
-                                  {v[pr][2].x, v[pr][2].y, v[pr][2].z, v[pr][2].w},
-                                  {v[pr][3].x, v[pr][3].y, v[pr][3].z, v[pr][3].w}};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            // dim 2k: low halves of word k; dim 2k+1: high halves
-            const uint32_t lo0 = bf16x2_to_f16x2(w[0][k] & 0xFFFFu, w[1][k] & 0xFFFFu);
-            const uint32_t lo1 = bf16x2_to_f16x2(w[2][k] & 0xFFFFu, w[3][k] & 0xFFFFu);
-            const uint32_t hi0 = bf16x2_to_f16x2(w[0][k] >> 16, w[1][k] >> 16);
-            const uint32_t hi1 = bf16x2_to_f16x2(w[2][k] >> 16, w[3][k] >> 16);
-            *reinterpret_cast<uint2 *>(vbuf + (8 * c + 2 * k) * kFaVRow + 2 * slot) =
-                make_uint2(lo0, lo1);
-            *reinterpret_cast<uint2 *>(vbuf + (8 * c + 2 * k + 1) * kFaVRow + 2 * slot) =
-                make_uint2(hi0, hi1);
-        }
+    for (int k = 0; k < 4; ++k) {
+        // dim 2k: low halves of word k; dim 2k+1: high halves
+        const uint32_t lo0 = bf16x2_to_f16x2(w[0][k] & 0xFFFFu, w[1][k] & 0xFFFFu);
+        const uint32_t lo1 = bf16x2_to_f16x2(w[2][k] & 0xFFFFu, w[3][k] & 0xFFFFu);
+        const uint32_t hi0 = bf16x2_to_f16x2(w[0][k] >> 16, w[1][k] >> 16);
+        const uint32_t hi1 = bf16x2_to_f16x2(w[2][k] >> 16, w[3][k] >> 16);
+        *reinterpret_cast<uint2 *>(vbuf + (8 * c + 2 * k) * kFaVRow + 2 * slot) =
+            make_uint2(lo0, lo1);
+        *reinterpret_cast<uint2 *>(vbuf + (8 * c + 2 * k + 1) * kFaVRow + 2 * slot) =
+            make_uint2(hi0, hi1);
     }
 }
 
 __global__ void __launch_bounds__(256) fa_prefill_kernel(FaArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char fa_lds[kFaLds];
-    unsigned char *const kbase = fa_lds;                 // two K tiles
-    unsigned char *const vbase = fa_lds + 2 * kFaKTile;  // two V^T tiles
+    unsigned char *const qbase = fa_lds;                            // Q tile
+    unsigned char *const kbase = fa_lds + kFaQTile;                 // two K tiles
+    unsigned char *const vbase = fa_lds + kFaQTile + 2 * kFaKTile;  // two V^T tiles
 
     const int qblk = gridDim.x - 1 - blockIdx.x;  // longest rows first
     const int hq = blockIdx.y;
@@ -160,14 +159,22 @@ __global__ void __launch_bounds__(256) fa_prefill_kernel(FaArgs a) {
     const int64_t wave_first = a.pos0 + min(q0 + 32 * wave, a.Tq - 1);
     const int64_t wave_last = a.pos0 + min(q0 + 32 * wave + 31, a.Tq - 1);
 
-    // Q^T fragments: dims 16*ks + 8h .. +7 of query tq
-    bf16x8 qf[16];
+    // Q tile: row q (query q0 + q), chunk c at slot c ^ (q % 32); thread t
+    // copies chunks (t & 1) + 2u of row t / 2
     {
-        const uint16_t *src =
-            a.Q + ((b * a.Tq + (tq < a.Tq ? tq : a.Tq - 1)) * a.H + hq) * kHeadDim + 8 * h;
+        const int qr = tid >> 1;
+        const int64_t tqr = q0 + qr < a.Tq ? q0 + qr : a.Tq - 1;
+        const uint16_t *src = a.Q + ((b * a.Tq + tqr) * a.H + hq) * kHeadDim + 8 * (tid & 1);
+        uint4 qv[16];
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(src + 16 * ks));
+        for (int u = 0; u < 16; ++u) qv[u] = *reinterpret_cast<const uint4 *>(src + 16 * u);
+        unsigned char *row = qbase + qr * 512;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            *reinterpret_cast<uint4 *>(row + 16 * (((tid & 1) + 2 * u) ^ (qr & 31))) = qv[u];
     }
+    // Q^T fragment reads of this lane: row 32*wave + n, chunk 2*ks + h
+    const unsigned char *qrow = qbase + (32 * wave + n) * 512;
 
     f32x16 o[8];
 #pragma unroll
@@ -176,35 +183,33 @@ __global__ void __launch_bounds__(256) fa_prefill_kernel(FaArgs a) {
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
     float m_ref = -INFINITY, l = 0.f;
 
-    uint4 vreg[2][4];
-    fa_load_k(Kg, rs, 0, a.Lmax, kbase, wave, lane);
+    uint4 kreg[4], vreg[4];
+    fa_load_k(Kg, rs, 0, a.Lmax, tid, kreg);
     fa_load_v(Vg, rs, 0, a.Lmax, tid, vreg);
+    fa_store_k(kreg, kbase, tid);
     fa_store_vt(vreg, vbase, tid);
 
     for (int it = 0; it < ntiles; ++it) {
         const int cur = it & 1;
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's K DMA landed
-        __syncthreads();                     // every wave's K DMA and V^T writes visible
+        __syncthreads();  // tile `it` is in LDS; tile it-1's buffers are free
         const int64_t tile0 = static_cast<int64_t>(it) * kFaN;
-        const bool more = it + 1 < ntiles;
-        if (more) {
-            fa_load_k(Kg, rs, tile0 + kFaN, a.Lmax, kbase + (cur ^ 1) * kFaKTile, wave, lane);
-            fa_load_v(Vg, rs, tile0 + kFaN, a.Lmax, tid, vreg);
-        }
-        // two 32-token halves, each: S^T, softmax, P^T . V accumulation
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int64_t sub0 = tile0 + 32 * tt;
-            if (sub0 > wave_last) break;  // no query of this wave sees these tokens
+        // next tile into registers while this one is consumed (after the last
+        // tile this fetches clamped rows into a buffer nothing reads)
+        fa_load_k(Kg, rs, tile0 + kFaN, a.Lmax, tid, kreg);
+        fa_load_v(Vg, rs, tile0 + kFaN, a.Lmax, tid, vreg);
+        // S^T, softmax, P^T . V accumulation
+        if (tile0 <= wave_last) {  // some query of this wave sees the tile
+            const int64_t sub0 = tile0;
             f32x16 s;
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[r] = 0.f;
-            const unsigned char *krow = kbase + cur * kFaKTile + (32 * tt + n) * kFaKRow;
+            const unsigned char *krow = kbase + cur * kFaKTile + n * kFaKRow;
 #pragma unroll
             for (int ks = 0; ks < 16; ++ks) {
                 const int slot = (2 * ks + h) ^ n;  // row % 32 == n
                 const uint4 kv = *reinterpret_cast<const uint4 *>(krow + 16 * slot);
-                s = mfma32(as_bf16x8(kv), qf[ks], s);
+                const uint4 qv = *reinterpret_cast<const uint4 *>(qrow + 16 * slot);
+                s = mfma32(as_bf16x8(kv), as_bf16x8(qv), s);
             }
             // online softmax of this lane's query column
             const bool diag = sub0 + 31 > wave_first;
@@ -240,7 +245,7 @@ __global__ void __launch_bounds__(256) fa_prefill_kernel(FaArgs a) {
                     pf[kk][j] = ph;
                 }
             }
-            const unsigned char *vt = vbase + cur * kFaVTile + n * kFaVRow + 64 * tt + 16 * h;
+            const unsigned char *vt = vbase + cur * kFaVTile + n * kFaVRow + 16 * h;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -251,10 +256,8 @@ __global__ void __launch_bounds__(256) fa_prefill_kernel(FaArgs a) {
                 }
             }
         }
-        if (more) {
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // the V registers (and K DMA) landed
-            fa_store_vt(vreg, vbase + (cur ^ 1) * kFaVTile, tid);
-        }
+        fa_store_k(kreg, kbase + (cur ^ 1) * kFaKTile, tid);
+        fa_store_vt(vreg, vbase + (cur ^ 1) * kFaVTile, tid);
     }
 
     // ---- normalise and store this lane's query column
