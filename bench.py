@@ -27,6 +27,12 @@ sys.path.insert(0, ROOT)
 METRIC = "QSA prefill & decode tokens/s at 128K/1M ctx, % roofline, speedup vs dense"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+COPY_BYTES = 1 << 30  # the plain copy that calibrates the HBM byte counters
+# HBM counters of the dominant kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE) with
+# the hash of the sources they were taken from
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_128k_hbm_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_long_08_amd", "csrc", f)
+                  for f in ("attention.hip", "qsa_internal.h")]
 
 WORKLOADS = {
     # name: (Tq, pos0, budget, needles per KV head)
@@ -223,6 +229,54 @@ def bench_decode(name, steps, warmup, with_dense=True):
     return res
 
 
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what
+    the same counter reads for a plain copy of COPY_BYTES.  None when the
+    summary is missing, was taken on another workload, or the kernel's
+    sources changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    try:
+        if kv.get("workload") != workload or kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        cb = float(kv["copy_bytes"])
+        f_scale = cb / (float(kv["copy_fetch_kib"]) * 1024.0)
+        w_scale = cb / (float(kv["copy_write_kib"]) * 1024.0)
+        return (float(kv["kernel_fetch_kib"]) * 1024.0 * f_scale +
+                float(kv["kernel_write_kib"]) * 1024.0 * w_scale)
+    except (KeyError, ValueError, ZeroDivisionError):
+        return None
+
+
+def calibration_copy():
+    """One plain device copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES);
+    run under the byte counters it gives their scale."""
+    import torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def cpu_baseline(name, x, budget, seconds=15.0):
     """The oracle (fp64, OpenMP over rows) on sampled query rows of the workload."""
     import oracle
@@ -241,7 +295,7 @@ def cpu_baseline(name, x, budget, seconds=15.0):
         oracle.qsa_rows_at(Qr, Kr, x.V, x.qi[rows], kb, pos, Kbudget=budget)
         t_rows += time.time() - t1
         rows_done += rows.size
-    return dict(value=rows_done / t_rows, unit="tokens/s", cores=os.cpu_count(), kind="oracle",
+    return dict(value=rows_done / t_rows, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
                 sample=f"{rows_done} query rows drawn from the second half of the {name} "
                        f"workload (full QSA per row: scores over every complete block, "
                        f"top-{budget}, attention over the selected tokens, 24 heads); "
@@ -259,6 +313,8 @@ def main():
                     help="which dense-attention baselines to time")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain 1 GiB device copy (scale of the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the QSA path here is single-GPU "
@@ -269,6 +325,8 @@ def main():
     qsa.qsa_check_device()
     torch.cuda.init()
 
+    if args.calibrate_copy:
+        calibration_copy()
     pre, x = bench_prefill(args.workload, args.steps, args.warmup, with_dense=args.dense == "all")
     log(f"prefill {args.workload}: {pre['ms_per_step']:.2f} ms/step, stages {pre['stages_ms']}")
     st = pre["stages_ms"]
@@ -276,7 +334,9 @@ def main():
     if dominant == "attend":
         achieved = pre["attn_bytes"] / (st["attend"] * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=achieved / HBM_PEAK_GBS, traffic=None, kernel="attn_prefill_kernel")
+                    frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic(args.workload),
+                    kernel="attn_prefill_kernel", launch_ms=st["attend"],
+                    algorithmic_bytes=pre["attn_bytes"])
     else:
         achieved = pre["idx_flop"] / (st["select"] * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=achieved, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",

@@ -121,19 +121,26 @@ int qsa_index_scores(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t
 /* ---- A4: per-query top-K block selection (chlience section 6: at most 512
  * complete blocks per query; djimit pillar 2: up to 512 full blocks).
  * If nc <= K all nc blocks are taken, else the K largest scores, ties broken
- * by lower block index.  blk_idx: int32 [B][Tq][K], ascending, padded with -1;
+ * by lower block index (scores compare as fp32 values; -0 equals +0).
+ * blk_idx: int32 [B][Tq][K], ascending, padded with -1;
  * n_sel: int32 [B][Tq] = min(K, nc).  scores as produced by qsa_index_scores.
- * Workspace: qsa_topk_workspace_bytes (may be 0; ws may then be NULL).
- * Supported: 1 <= K <= 2048. */
+ * Workspace: qsa_topk_workspace_bytes(B, Tq, nb_max, K) bytes, 16-byte
+ * aligned: the per-segment candidate lists of rows longer than 32,768 blocks
+ * (or of few long rows, as in decode).  It is 0 when every row fits one pass;
+ * ws may then be NULL.  Contents need no initialisation and are scratch.
+ * Supported: 1 <= K <= 2048, ld >= nb_max, ld % 4 == 0. */
 size_t qsa_topk_workspace_bytes(int B, int64_t Tq, int64_t nb_max, int K);
 int qsa_topk_blocks(const float *scores, int B, int64_t Tq, int64_t ld, int64_t pos0,
                     const int64_t *seq_len, int64_t nb_max, int r, int K, int32_t *blk_idx,
                     int32_t *n_sel, void *ws, size_t ws_bytes, void *stream);
 
-/* ---- A3 + A4 without a caller-visible score matrix: same result as
- * qsa_index_scores followed by qsa_topk_blocks.  Scores live in the
- * caller's workspace (qsa_select_workspace_bytes), one query chunk at a
- * time, so the workspace stays bounded at any Tq. */
+/* ---- A3 + A4 in one call: exactly the result of qsa_index_scores followed
+ * by qsa_topk_blocks (same scores bit for bit, same tie order).  The scores
+ * live in the caller's workspace (qsa_select_workspace_bytes, 16-byte
+ * aligned), one chunk of query rows at a time (at most 1 GiB of fp32 scores
+ * per chunk, plus the top-K candidate lists of the chunk), so the workspace
+ * stays bounded at any Tq; the decode form keeps one row per sequence.
+ * Supported: as the two calls, and nb_max < 2^27. */
 size_t qsa_select_workspace_bytes(int B, int64_t Tq, int64_t nb_max, int K);
 int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t Tq,
                       int64_t pos0, const int64_t *seq_len, int64_t nb_max, int Hi, int Di,
@@ -165,11 +172,15 @@ int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16
                            float *O, float *lse, void *ws, size_t ws_bytes, void *stream);
 
 /* ---- A8: dense causal attention (the pages' baseline in the chlience
- * Result 2 kernel measurement), same precision contract as the sparse path.
+ * Result 2 kernel measurement).
  * Q: [B][Tq][H][D]; K, V: [B][Lmax][Hkv][D]; O: fp32 [B][Tq][H][D];
  * lse: fp32 [B][Tq][H] or NULL.  Prefill form: query t attends keys
- * 0 .. pos0 + t (pos0 + Tq <= Lmax); decode form: Tq == 1, keys
- * 0 .. seq_len[b] - 1.  Workspace: dense_attn_workspace_bytes. */
+ * 0 .. pos0 + t (pos0 + Tq <= Lmax), a flash-attention pass whose P.V
+ * product runs in fp16 (P and V rounded to fp16: V must lie within the fp16
+ * range, |v| < 65504; values below 2^-14 lose relative precision), fp32
+ * logits, softmax and accumulation.  Decode form: Tq == 1, keys
+ * 0 .. seq_len[b] - 1, the split-K kernel of the sparse decode path.
+ * Workspace: dense_attn_workspace_bytes (0 for the prefill form). */
 size_t dense_attn_workspace_bytes(int B, int64_t Tq, int64_t Lmax, int H, int Hkv, int D);
 int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, int64_t Tq,
                int64_t Lmax, int64_t pos0, const int64_t *seq_len, int H, int Hkv, int D,

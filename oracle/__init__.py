@@ -49,6 +49,8 @@ def _load():
         lib.qsa_oracle_compress.argtypes = [vp, i64, i32, i32, i32, vp]
         lib.qsa_oracle_compress.restype = None
         lib.qsa_oracle_num_complete.argtypes = [i64, i32]
+        lib.qsa_oracle_num_threads.restype = i32
+        lib.qsa_oracle_num_threads.argtypes = []
         lib.qsa_oracle_num_complete.restype = i64
         lib.qsa_oracle_scores_row.argtypes = [vp, vp, i64, i64, i32, i32, i32, i32, vp]
         lib.qsa_oracle_scores_row.restype = i64
@@ -121,6 +123,11 @@ def compress(k: np.ndarray, r: int = 4, mode: int = KBAR_MEAN) -> np.ndarray:
     out = np.empty((Tk // r, Di), dtype=np.uint16)
     _load().qsa_oracle_compress(_p(k), Tk, Di, r, mode, _p(out))
     return out
+
+
+def num_threads() -> int:
+    """Threads of the oracle's OpenMP loops."""
+    return int(_load().qsa_oracle_num_threads())
 
 
 def num_complete(p: int, r: int = 4) -> int:

@@ -30,6 +30,9 @@
  * double precision; bf16 inputs convert exactly.
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -118,6 +121,15 @@ void qsa_oracle_compress(const uint16_t *k, int64_t Tk, int Di, int r, int mode,
 }
 
 /* ---------- O3: indexer scores of one query ------------------------------ */
+/* Threads the OpenMP loops of this library use (1 without OpenMP). */
+int qsa_oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 /* Number of complete micro-blocks visible to the query at position p. */
 int64_t qsa_oracle_num_complete(int64_t p, int r) { return p < 0 ? 0 : (p + 1) / r; }
 
