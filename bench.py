@@ -5,9 +5,11 @@ N(0,1) bf16 inputs with 64 planted needle blocks per KV head, budget 512
 blocks).  One step = the whole prefill hot path: RoPE on Q and K, key
 pooling, indexer scores + top-K selection, sparse attention.  The same JSON
 line also carries the decode step (32 sequences x 262,144 cached tokens),
-the dense-attention baseline on the same inputs (speedups), the roofline of
-the dominant kernel (HIP events around each launch, on the launch stream),
-and the fp64 oracle timed on a bounded sample on the host cores.
+the same metric at 1M context (an 8,192-query prefill chunk at the end of a
+1,048,576-token context, and decode of 4 such sequences), the dense-attention
+baselines on the same inputs (speedups), the roofline of the dominant kernel
+(HIP events around each launch, on the launch stream), and the fp64 oracle
+timed on a bounded sample on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ...]
 """
@@ -313,6 +315,9 @@ def main():
                     help="which dense-attention baselines to time")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--million", default="on", choices=["on", "off"],
+                    help="also time the 1M-context workloads (8,192-query prefill chunk, "
+                         "decode of 4 sequences) with their dense baselines")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (scale of the HBM byte counters)")
     args = ap.parse_args()
@@ -369,7 +374,28 @@ def main():
                            with_dense=args.dense != "none")
         out["decode"] = dict(workload=args.decode, **dec)
         log(f"decode {args.decode}: {dec['ms_per_step']:.3f} ms/step")
+    if args.million == "on":
+        # the same metric at 1M context: prefill chunk and decode (own inputs)
+        del x
+        m_pre, _ = bench_prefill("prefill_1m_chunk", min(args.steps, 3), 1,
+                                 with_dense=args.dense == "all")
+        m = dict(workload="prefill_1m_chunk", ms_per_step=m_pre["ms_per_step"],
+                 tokens_per_s=m_pre["Tq"] / (m_pre["ms_per_step"] * 1e-3),
+                 stages_ms=m_pre["stages_ms"],
+                 attend_gather_gbs=m_pre["attn_bytes"] / (m_pre["stages_ms"]["attend"] * 1e-3) / 1e9)
+        if "dense_ms" in m_pre:
+            m.update(dense_ms=m_pre["dense_ms"],
+                     speedup_vs_dense=m_pre["dense_ms"] / m_pre["ms_per_step"])
+        out["prefill_1m_chunk"] = m
+        log(f"prefill prefill_1m_chunk: {m_pre['ms_per_step']:.2f} ms/step")
+        m_dec = bench_decode("decode_1m_b4", max(args.steps, 10), args.warmup,
+                             with_dense=args.dense != "none")
+        out["decode_1m_b4"] = dict(workload="decode_1m_b4", **m_dec)
+        log(f"decode decode_1m_b4: {m_dec['ms_per_step']:.3f} ms/step")
+        x = None
     if not args.no_cpu:
+        if x is None:
+            x = gen_prefill(args.workload)
         out["cpu_baseline"] = cpu_baseline(args.workload, x, pre["budget"], args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
