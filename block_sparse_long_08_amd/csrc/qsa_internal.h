@@ -74,10 +74,12 @@ hipError_t launch_index_scores(const uint16_t *q_idx, const uint16_t *kbar, int 
                                int64_t pos0, const int64_t *seq_len, int64_t nb_max, int mode,
                                float *scores, int64_t ld, hipStream_t s);
 
-// Top-K passes for rows of up to nmax candidates: npass reduction passes
-// (segment lengths seg[i], entries[i] candidates per row after pass i), then
-// one final pass.  ws_bytes of workspace hold the candidate lists.
+// Top-K passes for rows of up to nmax candidates: either one streaming pass
+// per row, or npass reduction passes (segment lengths seg[i], entries[i]
+// candidates per row after pass i) then one final pass.  ws_bytes of
+// workspace hold the candidate lists.
 struct TopkPlan {
+    bool stream;  // one streaming pass per row, no workspace
     int npass;
     int64_t seg[4];
     int64_t entries[4];

@@ -20,6 +20,7 @@
 // own top-K (key and index, ascending), and the global top-K is the top-K of
 // those lists, because an element among the K best of the row is among the
 // K best of its segment.  The order (score desc, index asc) is kept exactly.
+// Many such rows at once take the streaming kernel below instead.
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -507,9 +508,332 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
     }
 }
 
+// ------------------------------------------------------------ streaming --
+// One workgroup of 1024 threads per row; the row is read twice from HBM/L2
+// and never held whole, so rows of any length take one launch and few
+// registers (several rows in flight per CU).  Wave w owns the contiguous
+// range [w*chunk, (w+1)*chunk) of the row (chunk a multiple of 256), lane l
+// the 4 consecutive keys 4l..4l+3 of every 256-key slice.
+//   pass 1: per-lane maxima of 4 key groups (slices j mod 4).  If at least K
+//           groups hold keys, the K-th largest maximum has K keys at or
+//           above it: its bin's lower edge is a floor under T;
+//   pass 2: keys at or above the floor (typically 1-3 K) are appended, in
+//           index order, to per-wave LDS lists with their positions;
+//   then the exact T and tie quota come from the lists (first digit block-
+//   wide, low 20 bits by one wave), and the lists are emitted in order.
+// If a list overflows (a crowded floor bin, e.g. heavy ties), the threshold
+// is found by three streaming radix passes instead and the row is emitted by
+// two more streaming passes; the result is the same.
+constexpr int kStNT = 1024;
+constexpr int kStNW = kStNT / kWave;
+
+struct StreamSmem {
+    TopkSmem<kStNT> t;  // histogram, key lists, counts, results
+    int32_t cidx[kStNW][kWaveCap];
+    uint32_t eqtot[kStNW];
+};
+
+__device__ __forceinline__ void stream_keys(const float *s, int i, int lim, uint32_t (&kk)[4]) {
+    const float4 v = *reinterpret_cast<const float4 *>(s + (i < lim ? i : 0));
+    kk[0] = i + 0 < lim ? score_key(v.x) : 0u;
+    kk[1] = i + 1 < lim ? score_key(v.y) : 0u;
+    kk[2] = i + 2 < lim ? score_key(v.z) : 0u;
+    kk[3] = i + 3 < lim ? score_key(v.w) : 0u;
+}
+
+__device__ __forceinline__ uint32_t max4(const uint32_t (&kk)[4]) {
+    return max(max(kk[0], kk[1]), max(kk[2], kk[3]));
+}
+
+// Ordered append of the keys of one slice that satisfy key >= floor.
+__device__ __forceinline__ void stream_append(const uint32_t (&kk)[4], uint32_t floor_key,
+                                              int pos0, uint32_t &wc, uint32_t *lk,
+                                              int32_t *li) {
+    uint64_t b[4];
+    uint32_t rk = wc;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        b[c] = __ballot(kk[c] >= floor_key);
+        rk += lanes_below(b[c]);
+    }
+    if ((b[0] | b[1] | b[2] | b[3]) == 0) return;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        if (kk[c] >= floor_key) {
+            if (rk < kWaveCap) {
+                lk[rk] = kk[c];
+                li[rk] = pos0 + c;
+            }
+            ++rk;
+        }
+        wc += static_cast<uint32_t>(__popcll(b[c]));
+    }
+}
+
+__global__ void __launch_bounds__(kStNT) topk_stream(TopkArgs a) {
+    __shared__ StreamSmem sm;
+    TopkSmem<kStNT> &sh = sm.t;
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t sq = row / a.Tq;
+    const int64_t p = a.seq_len ? a.seq_len[sq] - 1 : a.pos0 + (row - sq * a.Tq);
+    const int64_t n_row = min(num_complete_blocks(p, a.r), a.nb_max);
+    const uint32_t K = static_cast<uint32_t>(a.K);
+    int32_t *out = a.blk_idx + row * a.K;
+    if (n_row <= a.K) {  // every complete block is selected
+        for (int i = tid; i < a.K; i += kStNT) out[i] = i < n_row ? i : -1;
+        if (tid == 0) a.n_sel[row] = static_cast<int32_t>(n_row);
+        return;
+    }
+    const int n = static_cast<int>(n_row);
+    const float *s = a.scores + row * a.ld;
+    const int chunk = ((n + kStNW - 1) / kStNW + 255) / 256 * 256;
+    const int w0 = min(n, wave * chunk), w1 = min(n, w0 + chunk);
+    const int l4 = 4 * lane;
+
+    // ---- pass 1: group maxima -> floor
+    uint32_t lm[4] = {0u, 0u, 0u, 0u};
+    for (int base = w0; base < w1; base += 1024) {
+        uint32_t kk[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) stream_keys(s, base + 256 * u + l4, w1, kk[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lm[u] = max(lm[u], max4(kk[u]));
+    }
+    for (int i = tid; i < kBins; i += kStNT) sh.hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) atomicAdd(&sh.hist[lm[u] >> 20], 1u);
+    __syncthreads();
+    block_find<kStNT, kBins, 1, true>(sh.hist, K, sh, tid, lane, wave);
+    const uint32_t floor_key = sh.total >= K ? sh.fd_bin << 20 : kMinKey;
+
+    // ---- pass 2: candidate lists
+    uint32_t wc = 0;  // wave-uniform
+    for (int base = w0; base < w1; base += 1024) {
+        uint32_t kk[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) stream_keys(s, base + 256 * u + l4, w1, kk[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            stream_append(kk[u], floor_key, base + 256 * u + l4, wc, sh.cand[wave], sm.cidx[wave]);
+    }
+    if (lane == 0) sh.wcnt[wave] = wc;
+    __syncthreads();
+    bool overflow = false;
+    uint32_t total_c = 0;
+#pragma unroll
+    for (int w = 0; w < kStNW; ++w) {
+        overflow |= sh.wcnt[w] > kWaveCap;
+        total_c += sh.wcnt[w];
+    }
+
+    uint32_t thr, quota = 0, eqcnt = 0;
+    if (!overflow) {
+        if (total_c <= K) {
+            thr = floor_key;  // exactly K keys reach the floor: take them all
+        } else {
+            // first digit over the lists
+            __syncthreads();  // every thread has read wcnt / the floor histogram
+            for (int i = tid; i < kBins; i += kStNT) sh.hist[i] = 0u;
+            __syncthreads();
+            for (int i = lane; i < static_cast<int>(wc); i += kWave)
+                atomicAdd(&sh.hist[sh.cand[wave][i] >> 20], 1u);
+            __syncthreads();
+            block_find<kStNT, kBins, 1, true>(sh.hist, K, sh, tid, lane, wave);
+            const uint32_t bin = sh.fd_bin;
+            uint32_t krem = K - sh.fd_above;
+            __syncthreads();  // done with the histogram
+            if (wave == 0) {
+                uint32_t *h = sh.hist;
+                uint32_t prefix = bin << 20, mask = 0xFFF00000u, cnt = 0;
+                for (int pass = 0; pass < 2; ++pass) {
+                    const int shift = 10 - 10 * pass;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        *reinterpret_cast<uint4 *>(h + 16 * lane + 4 * v) = make_uint4(0u, 0u, 0u, 0u);
+                    wave_lds_sync();
+                    constexpr int LPL = kWave / kStNW;
+                    const int lw = lane / LPL, li0 = lane % LPL;
+                    const int nw = static_cast<int>(sh.wcnt[lw]);
+                    for (int i0 = li0; i0 < nw; i0 += 8 * LPL) {
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            const int i = i0 + u * LPL;
+                            if (i < nw) {
+                                const uint32_t key = sh.cand[lw][i];
+                                if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 1023u], 1u);
+                            }
+                        }
+                    }
+                    wave_lds_sync();
+                    uint32_t d, ab;
+                    wave_find1024(h, krem, lane, d, ab, cnt);
+                    prefix |= d << shift;
+                    mask |= 1023u << shift;
+                    krem -= ab;
+                    wave_lds_sync();
+                }
+                if (lane == 0) {
+                    sh.thr = prefix;
+                    sh.quota = krem;
+                    sh.eqcnt = cnt;
+                }
+            }
+            __syncthreads();
+            thr = sh.thr;
+            quota = sh.quota;
+            eqcnt = sh.eqcnt;
+        }
+        // ---- emission from the lists, in index order
+        const bool split = quota != eqcnt;
+        uint32_t gt_w = 0, eq_w = 0;
+        for (int i0 = 0; i0 < static_cast<int>(wc); i0 += kWave) {
+            const int i = i0 + lane;
+            const uint32_t key = i < static_cast<int>(wc) ? sh.cand[wave][i] : 0u;
+            if (!split) {
+                gt_w += static_cast<uint32_t>(__popcll(__ballot(key >= thr)));
+            } else {
+                gt_w += static_cast<uint32_t>(__popcll(__ballot(key > thr)));
+                eq_w += static_cast<uint32_t>(__popcll(__ballot(key == thr)));
+            }
+        }
+        if (lane == 0) {
+            sh.wtot[wave] = gt_w;
+            sm.eqtot[wave] = eq_w;
+        }
+        __syncthreads();
+        uint32_t gt_off = 0, eq_off = 0, gt_all = 0;
+#pragma unroll
+        for (int w = 0; w < kStNW; ++w) {
+            const uint32_t g = sh.wtot[w], e = sm.eqtot[w];
+            if (w < wave) {
+                gt_off += g;
+                eq_off += e;
+            }
+            gt_all += g;
+        }
+        for (int i0 = 0; i0 < static_cast<int>(wc); i0 += kWave) {
+            const int i = i0 + lane;
+            const bool ok = i < static_cast<int>(wc);
+            const uint32_t key = ok ? sh.cand[wave][i] : 0u;
+            const int32_t idx = ok ? sm.cidx[wave][i] : 0;
+            if (!split) {
+                const bool sel = key >= thr;
+                const uint64_t b = __ballot(sel);
+                if (sel) out[gt_off + lanes_below(b)] = idx;
+                gt_off += static_cast<uint32_t>(__popcll(b));
+            } else {
+                const bool gt = key > thr, eq = key == thr;
+                const uint64_t bg = __ballot(gt), be = __ballot(eq);
+                const uint32_t gr = gt_off + lanes_below(bg), er = eq_off + lanes_below(be);
+                if (gt || (eq && er < quota)) out[gr + min(er, quota)] = idx;
+                gt_off += static_cast<uint32_t>(__popcll(bg));
+                eq_off += static_cast<uint32_t>(__popcll(be));
+            }
+        }
+        const uint32_t nsel = split ? K : gt_all;
+        for (uint32_t i = nsel + tid; i < K; i += kStNT) out[i] = -1;
+        if (tid == 0) a.n_sel[row] = static_cast<int32_t>(nsel);
+        return;
+    }
+
+    // ---- crowded rows: streaming radix select, then streaming emission
+    uint32_t prefix = 0, mask = 0, krem = K;
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
+        const uint32_t dmask = pass == 0 ? 4095u : 1023u;
+        __syncthreads();
+        for (int i = tid; i < kBins; i += kStNT) sh.hist[i] = 0u;
+        __syncthreads();
+        for (int base = w0; base < w1; base += 256) {
+            uint32_t kk[4];
+            stream_keys(s, base + l4, w1, kk);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (kk[c] != 0u && (kk[c] & mask) == prefix)
+                    atomicAdd(&sh.hist[(kk[c] >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        if (pass == 0)
+            block_find<kStNT, kBins, 1, true>(sh.hist, krem, sh, tid, lane, wave);
+        else
+            block_find<kStNT, 1024, 1, false>(sh.hist, krem, sh, tid, lane, wave);
+        const uint32_t d = sh.fd_bin;
+        krem -= sh.fd_above;
+        prefix |= d << shift;
+        mask |= dmask << shift;
+        eqcnt = sh.hist[d];
+    }
+    thr = prefix;
+    quota = krem;
+    const bool split = quota != eqcnt;
+    uint32_t gt_w = 0, eq_w = 0;
+    for (int base = w0; base < w1; base += 256) {
+        uint32_t kk[4];
+        stream_keys(s, base + l4, w1, kk);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            gt_w += static_cast<uint32_t>(__popcll(__ballot(split ? kk[c] > thr : kk[c] >= thr)));
+            eq_w += static_cast<uint32_t>(__popcll(__ballot(split && kk[c] == thr)));
+        }
+    }
+    __syncthreads();
+    if (lane == 0) {
+        sh.wtot[wave] = gt_w;
+        sm.eqtot[wave] = eq_w;
+    }
+    __syncthreads();
+    uint32_t gt_off = 0, eq_off = 0, gt_all = 0;
+#pragma unroll
+    for (int w = 0; w < kStNW; ++w) {
+        const uint32_t g = sh.wtot[w], e = sm.eqtot[w];
+        if (w < wave) {
+            gt_off += g;
+            eq_off += e;
+        }
+        gt_all += g;
+    }
+    for (int base = w0; base < w1; base += 256) {
+        uint32_t kk[4];
+        stream_keys(s, base + l4, w1, kk);
+        uint64_t bg[4], be[4];
+        uint32_t gr = gt_off, er = eq_off;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            bg[c] = __ballot(split ? kk[c] > thr : kk[c] >= thr);
+            be[c] = __ballot(split && kk[c] == thr);
+            gr += lanes_below(bg[c]);
+            er += lanes_below(be[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const bool gt = split ? kk[c] > thr : kk[c] >= thr;
+            const bool eq = split && kk[c] == thr;
+            if (gt || (eq && er < quota)) out[gr + min(er, quota)] = base + l4 + c;
+            gr += gt;
+            er += eq;
+            gt_off += static_cast<uint32_t>(__popcll(bg[c]));
+            eq_off += static_cast<uint32_t>(__popcll(be[c]));
+        }
+    }
+    const uint32_t nsel = split ? K : gt_all;
+    for (uint32_t i = nsel + tid; i < K; i += kStNT) out[i] = -1;
+    if (tid == 0) a.n_sel[row] = static_cast<int32_t>(nsel);
+}
+
 // ------------------------------------------------------------------ plan --
 TopkPlan topk_plan(int64_t rows, int64_t nmax, int K) {
     TopkPlan pl{};
+    // many rows longer than one segment: one streaming pass per row (no
+    // workspace); measured faster there than the reduction passes, slower
+    // for few rows (one workgroup streams a row at a fraction of a CU's
+    // share of HBM) and for rows that fit one segment
+    if (nmax > kSegBig && rows >= 256) {
+        pl.stream = true;
+        pl.final_entries = nmax;
+        return pl;
+    }
     int64_t e = nmax;
     while (pl.npass < 4) {
         const bool fits = e <= kSegBig;
@@ -556,6 +880,10 @@ hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64
     a.seq_len = seq_len;
     a.r = r;
     a.K = K;
+    if (pl.stream) {
+        hipLaunchKernelGGL(topk_stream, dim3(static_cast<uint32_t>(rows)), dim3(kStNT), 0, s, a);
+        return hipGetLastError();
+    }
     uint32_t *buf_key[2];
     int32_t *buf_idx[2];
     char *w = static_cast<char *>(ws);

@@ -229,6 +229,26 @@ def test_topk_prefill_rows_longer_than_a_segment(qsa, Tq, pos0, K):
         assert n[t] == want.size and np.array_equal(g[t, :n[t]], want), t
 
 
+def test_topk_streaming_rows(qsa):
+    """Many prefill rows longer than one segment take the streaming kernel:
+    exact selections on random rows, coarse ties, an all-equal row (the
+    crowded-floor fallback) and a row whose top-K sits in one block range."""
+    Tq, pos0, K = 300, 4 * 50000, 512
+    nb = (pos0 + Tq) // 4
+    ld = (nb + 3) // 4 * 4
+    rng = np.random.default_rng(77)
+    s = np.zeros((Tq, ld), dtype=np.float32)
+    s[:, :nb] = rng.standard_normal((Tq, nb)).astype(np.float32)
+    s[1::5, :nb] = np.round(s[1::5, :nb] * 4) / 4
+    s[2, :nb] = 0.5                                  # every key ties
+    s[3, 1000:3000] = 9.0                            # 2000 equal top keys
+    g, n = run_topk(qsa, dev(s), 1, Tq, ld, pos0, None, nb, K)
+    for t in list(range(0, 12)) + list(range(12, Tq, 23)):
+        nc = (pos0 + t + 1) // 4
+        want, _, _ = oracle.topk_row(s[t, :nc].astype(np.float64), K)
+        assert n[t] == want.size and np.array_equal(g[t, :n[t]], want), t
+
+
 def test_topk_million_token_decode_rows(qsa):
     """Decode form at 1,048,576 tokens (262,144 blocks): two reduction passes
     and the final pass; one row of random scores, one of coarse ties."""
