@@ -79,7 +79,8 @@ hipError_t launch_index_scores(const uint16_t *q_idx, const uint16_t *kbar, int 
 // candidates per row after pass i) then one final pass.  ws_bytes of
 // workspace hold the candidate lists.
 struct TopkPlan {
-    bool stream;  // one streaming pass per row, no workspace
+    bool stream;    // one streaming pass per row, no workspace
+    int stream_nt;  // its workgroup size
     int npass;
     int64_t seg[4];
     int64_t entries[4];

@@ -20,7 +20,7 @@
 // own top-K (key and index, ascending), and the global top-K is the top-K of
 // those lists, because an element among the K best of the row is among the
 // K best of its segment.  The order (score desc, index asc) is kept exactly.
-// Many such rows at once take the streaming kernel below instead.
+// Many long rows at once take the streaming kernel below instead.
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -31,6 +31,7 @@ constexpr uint32_t kMinKey = 0x00100000u;  // smaller keys: empty slots (0) and 
 constexpr int kSegBig = 32768;             // 1024 threads x 32 keys
 constexpr int kSegSmall = 4096;            // 256 threads x 16 keys
 constexpr int kSegMid = 8192;              // 256 threads x 32 keys
+constexpr int kStreamMin = 12288;          // shorter rows stay register-resident
 
 struct TopkArgs {
     const float *scores;     // source 0: fp32 score rows
@@ -509,7 +510,7 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
 }
 
 // ------------------------------------------------------------ streaming --
-// One workgroup of 1024 threads per row; the row is read twice from HBM/L2
+// One workgroup (256 or 1024 threads) per row; the row is read twice from HBM/L2
 // and never held whole, so rows of any length take one launch and few
 // registers (several rows in flight per CU).  Wave w owns the contiguous
 // range [w*chunk, (w+1)*chunk) of the row (chunk a multiple of 256), lane l
@@ -524,13 +525,13 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
 // If a list overflows (a crowded floor bin, e.g. heavy ties), the threshold
 // is found by three streaming radix passes instead and the row is emitted by
 // two more streaming passes; the result is the same.
-constexpr int kStNT = 1024;
-constexpr int kStNW = kStNT / kWave;
-
+template <int NT>
 struct StreamSmem {
-    TopkSmem<kStNT> t;  // histogram, key lists, counts, results
-    int32_t cidx[kStNW][kWaveCap];
-    uint32_t eqtot[kStNW];
+    static constexpr int CAP = NT >= 1024 ? 256 : 512;  // list entries per wave
+    TopkSmem<NT> t;  // histogram, counts, results
+    uint32_t ckey[NT / kWave][CAP];
+    int32_t cidx[NT / kWave][CAP];
+    uint32_t eqtot[NT / kWave];
 };
 
 __device__ __forceinline__ void stream_keys(const float *s, int i, int lim, uint32_t (&kk)[4]) {
@@ -547,7 +548,7 @@ __device__ __forceinline__ uint32_t max4(const uint32_t (&kk)[4]) {
 
 // Ordered append of the keys of one slice that satisfy key >= floor.
 __device__ __forceinline__ void stream_append(const uint32_t (&kk)[4], uint32_t floor_key,
-                                              int pos0, uint32_t &wc, uint32_t *lk,
+                                              int pos0, uint32_t cap, uint32_t &wc, uint32_t *lk,
                                               int32_t *li) {
     uint64_t b[4];
     uint32_t rk = wc;
@@ -560,7 +561,7 @@ __device__ __forceinline__ void stream_append(const uint32_t (&kk)[4], uint32_t 
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         if (kk[c] >= floor_key) {
-            if (rk < kWaveCap) {
+            if (rk < cap) {
                 lk[rk] = kk[c];
                 li[rk] = pos0 + c;
             }
@@ -570,8 +571,11 @@ __device__ __forceinline__ void stream_append(const uint32_t (&kk)[4], uint32_t 
     }
 }
 
+template <int kStNT>
 __global__ void __launch_bounds__(kStNT) topk_stream(TopkArgs a) {
-    __shared__ StreamSmem sm;
+    constexpr int kStNW = kStNT / kWave;
+    constexpr uint32_t kCap = StreamSmem<kStNT>::CAP;
+    __shared__ StreamSmem<kStNT> sm;
     TopkSmem<kStNT> &sh = sm.t;
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -616,7 +620,8 @@ __global__ void __launch_bounds__(kStNT) topk_stream(TopkArgs a) {
         for (int u = 0; u < 4; ++u) stream_keys(s, base + 256 * u + l4, w1, kk[u]);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            stream_append(kk[u], floor_key, base + 256 * u + l4, wc, sh.cand[wave], sm.cidx[wave]);
+            stream_append(kk[u], floor_key, base + 256 * u + l4, kCap, wc, sm.ckey[wave],
+                          sm.cidx[wave]);
     }
     if (lane == 0) sh.wcnt[wave] = wc;
     __syncthreads();
@@ -624,7 +629,7 @@ __global__ void __launch_bounds__(kStNT) topk_stream(TopkArgs a) {
     uint32_t total_c = 0;
 #pragma unroll
     for (int w = 0; w < kStNW; ++w) {
-        overflow |= sh.wcnt[w] > kWaveCap;
+        overflow |= sh.wcnt[w] > kCap;
         total_c += sh.wcnt[w];
     }
 
@@ -638,7 +643,7 @@ __global__ void __launch_bounds__(kStNT) topk_stream(TopkArgs a) {
             for (int i = tid; i < kBins; i += kStNT) sh.hist[i] = 0u;
             __syncthreads();
             for (int i = lane; i < static_cast<int>(wc); i += kWave)
-                atomicAdd(&sh.hist[sh.cand[wave][i] >> 20], 1u);
+                atomicAdd(&sh.hist[sm.ckey[wave][i] >> 20], 1u);
             __syncthreads();
             block_find<kStNT, kBins, 1, true>(sh.hist, K, sh, tid, lane, wave);
             const uint32_t bin = sh.fd_bin;
@@ -661,7 +666,7 @@ __global__ void __launch_bounds__(kStNT) topk_stream(TopkArgs a) {
                         for (int u = 0; u < 8; ++u) {
                             const int i = i0 + u * LPL;
                             if (i < nw) {
-                                const uint32_t key = sh.cand[lw][i];
+                                const uint32_t key = sm.ckey[lw][i];
                                 if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 1023u], 1u);
                             }
                         }
@@ -690,7 +695,7 @@ __global__ void __launch_bounds__(kStNT) topk_stream(TopkArgs a) {
         uint32_t gt_w = 0, eq_w = 0;
         for (int i0 = 0; i0 < static_cast<int>(wc); i0 += kWave) {
             const int i = i0 + lane;
-            const uint32_t key = i < static_cast<int>(wc) ? sh.cand[wave][i] : 0u;
+            const uint32_t key = i < static_cast<int>(wc) ? sm.ckey[wave][i] : 0u;
             if (!split) {
                 gt_w += static_cast<uint32_t>(__popcll(__ballot(key >= thr)));
             } else {
@@ -716,7 +721,7 @@ __global__ void __launch_bounds__(kStNT) topk_stream(TopkArgs a) {
         for (int i0 = 0; i0 < static_cast<int>(wc); i0 += kWave) {
             const int i = i0 + lane;
             const bool ok = i < static_cast<int>(wc);
-            const uint32_t key = ok ? sh.cand[wave][i] : 0u;
+            const uint32_t key = ok ? sm.ckey[wave][i] : 0u;
             const int32_t idx = ok ? sm.cidx[wave][i] : 0;
             if (!split) {
                 const bool sel = key >= thr;
@@ -825,19 +830,24 @@ __global__ void __launch_bounds__(kStNT) topk_stream(TopkArgs a) {
 // ------------------------------------------------------------------ plan --
 TopkPlan topk_plan(int64_t rows, int64_t nmax, int K) {
     TopkPlan pl{};
-    // many rows longer than one segment: one streaming pass per row (no
-    // workspace); measured faster there than the reduction passes, slower
-    // for few rows (one workgroup streams a row at a fraction of a CU's
-    // share of HBM) and for rows that fit one segment
-    if (nmax > kSegBig && rows >= 256) {
+    // many long rows: one streaming pass per row, no workspace (1024
+    // threads past one segment, 256 threads for rows of 12K..32K blocks).
+    // Measured faster there than the register-resident and reduction
+    // passes; slower for few rows (one workgroup streams a row at a
+    // fraction of a CU's share of HBM) and for short rows.
+    if (rows >= 256 && nmax > kStreamMin) {
         pl.stream = true;
+        pl.stream_nt = nmax > kSegBig ? 1024 : 256;
         pl.final_entries = nmax;
         return pl;
     }
     int64_t e = nmax;
     while (pl.npass < 4) {
+        // stop once one final pass can take the rows: always after a
+        // reduction pass (a third launch costs more than a longer final
+        // pass), else when the rows are many or short
         const bool fits = e <= kSegBig;
-        if (fits && (rows >= 128 || e <= 8192)) break;
+        if (fits && (rows >= 128 || pl.npass > 0 || e <= 8192)) break;
         const int64_t big_wgs = rows * ((e + kSegBig - 1) / kSegBig);
         const int64_t seg = (big_wgs < 512 && 4 * K <= kSegSmall) ? kSegSmall : kSegBig;
         const int64_t e2 = (e + seg - 1) / seg * K;
@@ -881,7 +891,12 @@ hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64
     a.r = r;
     a.K = K;
     if (pl.stream) {
-        hipLaunchKernelGGL(topk_stream, dim3(static_cast<uint32_t>(rows)), dim3(kStNT), 0, s, a);
+        if (pl.stream_nt == 1024)
+            hipLaunchKernelGGL(topk_stream<1024>, dim3(static_cast<uint32_t>(rows)), dim3(1024), 0,
+                               s, a);
+        else
+            hipLaunchKernelGGL(topk_stream<256>, dim3(static_cast<uint32_t>(rows)), dim3(256), 0, s,
+                               a);
         return hipGetLastError();
     }
     uint32_t *buf_key[2];

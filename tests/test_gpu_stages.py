@@ -229,11 +229,13 @@ def test_topk_prefill_rows_longer_than_a_segment(qsa, Tq, pos0, K):
         assert n[t] == want.size and np.array_equal(g[t, :n[t]], want), t
 
 
-def test_topk_streaming_rows(qsa):
-    """Many prefill rows longer than one segment take the streaming kernel:
-    exact selections on random rows, coarse ties, an all-equal row (the
-    crowded-floor fallback) and a row whose top-K sits in one block range."""
-    Tq, pos0, K = 300, 4 * 50000, 512
+@pytest.mark.parametrize("pos0", [4 * 50000, 4 * 20000])
+def test_topk_streaming_rows(qsa, pos0):
+    """Many long prefill rows take the streaming kernel (1024 threads past
+    32,768 blocks, 256 threads below): exact selections on random rows,
+    coarse ties, an all-equal row (the crowded-floor fallback) and a row
+    whose top-K sits in one block range."""
+    Tq, K = 300, 512
     nb = (pos0 + Tq) // 4
     ld = (nb + 3) // 4 * 4
     rng = np.random.default_rng(77)
