@@ -14,14 +14,41 @@ constexpr int kQT = 64;          // queries per prefill workgroup (4 waves x 16)
 constexpr int kBT = 64;          // blocks per LDS tile
 constexpr int kSplitTiles = 64;  // block tiles per workgroup (grid.y splits longer rows)
 constexpr int kRowBytes = 272;   // LDS row stride of one pooled key (256 B + 16 B pad)
+constexpr int kTileBytes = kBT * kRowBytes;
+constexpr int kStageRow = 272;   // LDS row of one query's 64 staged scores (256 B + pad)
+
+__device__ __forceinline__ void load_tile(const uint16_t *kbar, int64_t nb_max, int64_t tile,
+                                          int bl, int part, uint4 &v0, uint4 &v1, uint4 &v2,
+                                          uint4 &v3) {
+    int64_t bb = tile * kBT + bl;
+    bb = bb < nb_max ? bb : nb_max - 1;  // rows past the cache: any valid row, masked later
+    const uint4 *src = reinterpret_cast<const uint4 *>(kbar + bb * kIdxDim) + part * 4;
+    v0 = src[0];
+    v1 = src[1];
+    v2 = src[2];
+    v3 = src[3];
+}
+
+__device__ __forceinline__ void store_tile(unsigned char *buf, int bl, int part, const uint4 &v0,
+                                           const uint4 &v1, const uint4 &v2, const uint4 &v3) {
+    uint4 *dst = reinterpret_cast<uint4 *>(buf + bl * kRowBytes + part * 64);
+    dst[0] = v0;
+    dst[1] = v1;
+    dst[2] = v2;
+    dst[3] = v3;
+}
 
 // Prefill form: queries pos0 + t, t < Tq, one sequence per blockIdx.z.
+// Pooled-key tiles are double-buffered: the next tile is loaded into
+// registers while the current one feeds the MFMAs, then written to the other
+// LDS buffer (one barrier per tile).  Each wave stages its 16 x 64 scores in
+// LDS and writes them back as whole 256-byte row segments.
 template <int MODE>
 __global__ void __launch_bounds__(256)
 index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ kbar,
                      int64_t Tq, int64_t pos0, int64_t nb_max, float *__restrict__ scores,
                      int64_t ld) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[kBT * kRowBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileBytes + 4 * 16 * kStageRow];
     const int qt = gridDim.x - 1 - blockIdx.x;  // longest rows first
     const int64_t seq = blockIdx.z;
     q_idx += seq * Tq * (kIdxHeads * kIdxDim);
@@ -39,6 +66,7 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g4 = lane >> 4;
+    unsigned char *stage = lds + 2 * kTileBytes + wave * 16 * kStageRow;
 
     // A fragments: row m = lane%16 of row tile rt is query 16*wave + 4*rt + m/4,
     // head m%4; k-slots of group g4 cover dims 32*s + 8*g4 .. +7.
@@ -60,49 +88,56 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
         const int64_t tout = t0 + 16 * wave + 4 * rt + g4;
         ncq[rt] = tout < Tq ? min(num_complete_blocks(pos0 + tout, kBlock), nb_max) : -1;
     }
+    // write-back mapping: lane -> staged query row 4*i + lane/16, 16-byte chunk lane%16
+    const int wr_q = lane >> 4, wr_c = lane & 15;
+
+    // cooperative tile load: thread -> block tid/4, bytes 64*(tid%4) .. +63
+    const int ld_bl = tid >> 2, ld_part = tid & 3;
+    uint4 kv0, kv1, kv2, kv3;
+    load_tile(kbar, nb_max, tile_begin, ld_bl, ld_part, kv0, kv1, kv2, kv3);
+    store_tile(lds, ld_bl, ld_part, kv0, kv1, kv2, kv3);
 
     for (int64_t tile = tile_begin; tile < tile_end; ++tile) {
+        const int cur = static_cast<int>((tile - tile_begin) & 1);
+        unsigned char *buf = lds + cur * kTileBytes;
+        __syncthreads();  // tile ready; the other buffer is free
+        // next tile into registers (past the last tile: a clamped re-read of
+        // rows nothing will use)
+        load_tile(kbar, nb_max, tile + 1, ld_bl, ld_part, kv0, kv1, kv2, kv3);
         const int64_t b0 = tile * kBT;
-        // cooperative load: thread -> block tid/4, bytes 64*(tid%4) .. +63
-        {
-            const int bl = tid >> 2, part = tid & 3;
-            const int64_t bb = b0 + bl;
-            uint4 v[4];
-            if (bb < nb_max) {
-                const uint4 *src =
-                    reinterpret_cast<const uint4 *>(kbar + bb * kIdxDim) + part * 4;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = src[i];
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = make_uint4(0, 0, 0, 0);
-            }
-            uint4 *dst = reinterpret_cast<uint4 *>(lds + bl * kRowBytes + part * 64);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = v[i];
-        }
-        __syncthreads();
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             bf16x8 kf[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 kf[s] = as_bf16x8(*reinterpret_cast<const uint4 *>(
-                    lds + (16 * j + n) * kRowBytes + 64 * s + 16 * g4));
+                    buf + (16 * j + n) * kRowBytes + 64 * s + 16 * g4));
             const int64_t blk = b0 + 16 * j + n;
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 4; ++s) acc = mfma_bf16_16x16x32(qf[rt][s], kf[s], acc);
-                if (ncq[rt] >= 0 && blk < ld) {
-                    const float v = blk < ncq[rt] ? combine_heads<MODE>(acc) : -INFINITY;
-                    const int64_t tout = t0 + 16 * wave + 4 * rt + g4;
-                    scores[tout * ld + blk] = v;
-                }
+                const float v = blk < ncq[rt] ? combine_heads<MODE>(acc) : -INFINITY;
+                *reinterpret_cast<float *>(stage + (4 * rt + g4) * kStageRow + 4 * (16 * j + n)) = v;
             }
         }
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // write back: 4 instructions, each 4 query rows x 256 contiguous bytes
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ql = 4 * i + wr_q;  // staged row = 4*rt + g4 of query 16*wave + ql
+            const int64_t tout = t0 + 16 * wave + ql;
+            const int64_t blk = b0 + 4 * wr_c;
+            const float4 v = *reinterpret_cast<const float4 *>(stage + ql * kStageRow + 16 * wr_c);
+            if (tout < Tq && blk < ld) *reinterpret_cast<float4 *>(scores + tout * ld + blk) = v;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        store_tile(lds + (cur ^ 1) * kTileBytes, ld_bl, ld_part, kv0, kv1, kv2, kv3);
     }
 }
 
