@@ -1,7 +1,8 @@
 // A5-A8: softmax attention over 4-token micro-blocks (chlience section 6:
 // selected blocks expand to token indices; the query's incomplete block is
 // always kept, later tokens masked).  One per-wave routine serves the sparse
-// prefill, the split-K decode and the dense decode (every complete block).
+// prefill, the split-K decode and the dense decode (every complete block);
+// the dense prefill is the flash kernel of flash_prefill.hip.
 //
 // Work unit: a stage of 4 entries (16 tokens) of one KV head.  An entry is a
 // selected block (4 tokens) or the trailing partial block ((p+1) mod 4
@@ -223,7 +224,6 @@ __device__ __forceinline__ void state_write(const WaveState &st, float ltot,
 // Prefill: one workgroup per query, one wave per KV head; each wave walks all
 // stages of its head.  Grid: (Tq, B); block: 64 * Hkv threads.
 // Dynamic LDS: Hkv V tiles of 8 KB, then the selected-block list.
-template <bool DENSE>
 __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
     int32_t *lst = reinterpret_cast<int32_t *>(dyn_lds + a.Hkv * kVStageBytes);
@@ -231,22 +231,17 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a) {
     const int64_t row = b * a.Tq + t;
     const int64_t p = a.pos0 + t;
     const int64_t nc = num_complete_blocks(p, kBlock);
-    int ns;
-    if (DENSE) {
-        ns = static_cast<int>(nc);
-    } else {
-        const int v = a.n_sel[row];
-        const int64_t cap = min(static_cast<int64_t>(a.Kbudget), nc);
-        ns = v < 0 ? 0 : (v > cap ? static_cast<int>(cap) : v);
-        const int32_t *src = a.blk_idx + row * a.Kbudget;
-        for (int i = threadIdx.x; i < ns; i += blockDim.x) {
-            int32_t bi = src[i];
-            bi = bi < 0 ? 0 : (bi >= nc ? static_cast<int32_t>(nc - 1) : bi);
-            lst[i] = bi;
-        }
-        __syncthreads();
+    const int v = a.n_sel[row];
+    const int64_t cap = min(static_cast<int64_t>(a.Kbudget), nc);
+    const int ns = v < 0 ? 0 : (v > cap ? static_cast<int>(cap) : v);
+    const int32_t *src = a.blk_idx + row * a.Kbudget;
+    for (int i = threadIdx.x; i < ns; i += blockDim.x) {
+        int32_t bi = src[i];
+        bi = bi < 0 ? 0 : (bi >= nc ? static_cast<int32_t>(nc - 1) : bi);
+        lst[i] = bi;
     }
-    EntryList L{DENSE ? nullptr : lst, 0, ns, static_cast<int>((p + 1) % kBlock), nc};
+    __syncthreads();
+    EntryList L{lst, 0, ns, static_cast<int>((p + 1) % kBlock), nc};
     const int E = ns + (L.pr > 0 ? 1 : 0);
     const int nstages = (E + kStageEntries - 1) / kStageEntries;
 
@@ -345,48 +340,50 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit
     }
 }
 
-// Merge the split records: one thread per output element (b, head, d), so
-// neighbouring threads read neighbouring record words.
+// Merge the split records: 4 neighbouring threads per output element
+// (b, head, d), each folding every 4th split with an online rescale, then
+// combined by shuffles; neighbouring elements read neighbouring words.
+__device__ __forceinline__ void merge_step(float &M, float &acc, float &l, float m2, float acc2,
+                                           float l2) {
+    const float mn = fmaxf(M, m2);
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    const float a1 = exp2f(M - mu), a2 = exp2f(m2 - mu);
+    acc = acc * a1 + acc2 * a2;
+    l = l * a1 + l2 * a2;
+    M = mn;
+}
+
 __global__ void __launch_bounds__(256) attn_decode_merge(AttnArgs a, int nsplit) {
     const int group = a.H / a.Hkv;
-    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int sub = threadIdx.x & 3;
     const int64_t total = static_cast<int64_t>(a.B) * a.H * kHeadDim;
-    if (idx >= total) return;
+    int64_t idx = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 2;
+    const bool valid = idx < total;
+    idx = valid ? idx : total - 1;
     const int d = static_cast<int>(idx % kHeadDim);
     const int hq = static_cast<int>((idx / kHeadDim) % a.H);
     const int64_t b = idx / (static_cast<int64_t>(kHeadDim) * a.H);
     const int g = hq / group, n = hq - g * group;
     const float *rec = a.part + (b * a.Hkv + g) * nsplit * static_cast<int64_t>(kRecFloats);
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, rec[s * kRecFloats + 4096 + n]);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float acc = 0.f, lsum = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < nsplit; ++s) {
+    float M = -INFINITY, acc = 0.f, l = 0.f;
+#pragma unroll 4
+    for (int s = sub; s < nsplit; s += 4) {
         const float *r = rec + s * static_cast<int64_t>(kRecFloats);
-        const float w = exp2f(r[4096 + n] - Mu);
-        acc += r[n * kHeadDim + d] * w;
-        lsum += r[4096 + 64 + n] * w;
+        merge_step(M, acc, l, r[4096 + n], r[n * kHeadDim + d], r[4096 + 64 + n]);
     }
-    a.O[(b * a.H + hq) * kHeadDim + d] = lsum > 0.f ? acc / lsum : 0.f;
-    if (a.lse && d == 0)
-        a.lse[b * a.H + hq] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
+#pragma unroll
+    for (int off = 1; off < 4; off <<= 1)
+        merge_step(M, acc, l, __shfl_xor(M, off), __shfl_xor(acc, off), __shfl_xor(l, off));
+    if (sub != 0 || !valid) return;
+    a.O[(b * a.H + hq) * kHeadDim + d] = l > 0.f ? acc / l : 0.f;
+    if (a.lse && d == 0) a.lse[b * a.H + hq] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
 }
 
 hipError_t launch_sparse_prefill(const AttnArgs &a, hipStream_t s) {
     if (a.Tq == 0 || a.B == 0) return hipSuccess;
     const dim3 grid(static_cast<uint32_t>(a.Tq), static_cast<uint32_t>(a.B));
     const size_t lds = static_cast<size_t>(a.Hkv) * kVStageBytes + 4 * static_cast<size_t>(a.Kbudget);
-    hipLaunchKernelGGL(attn_prefill_kernel<false>, grid, dim3(64 * a.Hkv), lds, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_dense_gather_prefill(const AttnArgs &a, hipStream_t s) {
-    if (a.Tq == 0 || a.B == 0) return hipSuccess;
-    const dim3 grid(static_cast<uint32_t>(a.Tq), static_cast<uint32_t>(a.B));
-    const size_t lds = static_cast<size_t>(a.Hkv) * kVStageBytes;
-    hipLaunchKernelGGL(attn_prefill_kernel<true>, grid, dim3(64 * a.Hkv), lds, s, a);
+    hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(64 * a.Hkv), lds, s, a);
     return hipGetLastError();
 }
 
@@ -418,8 +415,8 @@ hipError_t launch_attn_decode(const AttnArgs &a, int nsplit, hipStream_t s) {
         hipLaunchKernelGGL(attn_decode_kernel<true>, grid, dim3(256), 0, s, a, nsplit, sps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t total = static_cast<int64_t>(a.B) * a.H * kHeadDim;
-    hipLaunchKernelGGL(attn_decode_merge, dim3(static_cast<uint32_t>((total + 255) / 256)),
+    const int64_t threads = 4 * static_cast<int64_t>(a.B) * a.H * kHeadDim;
+    hipLaunchKernelGGL(attn_decode_merge, dim3(static_cast<uint32_t>((threads + 255) / 256)),
                        dim3(256), 0, s, a, nsplit);
     return hipGetLastError();
 }

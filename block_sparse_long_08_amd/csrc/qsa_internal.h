@@ -113,7 +113,6 @@ hipError_t launch_sparse_prefill(const AttnArgs &a, hipStream_t s);
 size_t decode_partial_floats(int B, int Hkv, int nsplit);
 int decode_num_splits(int B, int Hkv, int64_t max_entries);
 hipError_t launch_attn_decode(const AttnArgs &a, int nsplit, hipStream_t s);
-hipError_t launch_dense_gather_prefill(const AttnArgs &a, hipStream_t s);
 hipError_t launch_dense_prefill(const AttnArgs &a, hipStream_t s);
 
 }  // namespace qsa

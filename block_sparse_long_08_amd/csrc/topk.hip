@@ -878,7 +878,12 @@ hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64
                        int32_t *n_sel, void *ws, hipStream_t s) {
     const int64_t rows = static_cast<int64_t>(B) * Tq;
     if (rows == 0) return hipSuccess;
-    const TopkPlan pl = topk_plan(rows, nb_max, K);
+    // With many rows no plan needs workspace, so the kernel choice may follow
+    // the longest row of this call (prefill form: the last query's) rather
+    // than the cache size the workspace was sized for.
+    int64_t nmax = nb_max;
+    if (!seq_len && rows >= 256) nmax = min(num_complete_blocks(pos0 + Tq - 1, r), nb_max);
+    const TopkPlan pl = topk_plan(rows, nmax, K);
     TopkArgs a{};
     a.scores = scores;
     a.ld = ld;
