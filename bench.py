@@ -150,6 +150,7 @@ def bench_prefill(name, steps, warmup, with_dense=True):
     idx_flop = int(nc.sum()) * 4 * 128 * 2
     res.update(gather_bytes=gather_bytes, attn_bytes=attn_bytes, attn_flop=attn_flop,
                idx_flop=idx_flop, candidates=int(nc.sum()))
+    res["dense_flop"] = float(((pos + 1).astype(np.float64)).sum()) * 24 * 256 * 2 * 2
     if with_dense:
         Od = torch.empty((Tq, 24, 256), dtype=torch.float32, device="cuda")
         Kr = layer.Kr if fresh else K
@@ -164,9 +165,7 @@ def bench_prefill(name, steps, warmup, with_dense=True):
         e1.record()
         torch.cuda.synchronize()
         dms = e0.elapsed_time(e1) / dsteps
-        dflop = float(((pos + 1).astype(np.float64)).sum()) * 24 * 256 * 2 * 2
-        res.update(dense_ms=dms, dense_flop=dflop,
-                   qsa_attention_ms=stage["select"] + stage["attend"])
+        res.update(dense_ms=dms, qsa_attention_ms=stage["select"] + stage["attend"])
     del layer
     torch.cuda.empty_cache()
     return res, x
@@ -369,6 +368,10 @@ def main():
         out["dense_prefill_ms"] = pre["dense_ms"]
         out["prefill_speedup_vs_dense"] = pre["dense_ms"] / pre["ms_per_step"]
         out["dense_prefill_tflops"] = pre["dense_flop"] / (pre["dense_ms"] * 1e-3) / 1e12
+    # dense attention at the bf16 MFMA peak: the speedup no dense kernel could shrink
+    dense_roof_ms = pre["dense_flop"] / (BF16_PEAK_TFLOPS * 1e12) * 1e3
+    out["dense_prefill_at_mfma_peak_ms"] = dense_roof_ms
+    out["prefill_speedup_vs_dense_at_mfma_peak"] = dense_roof_ms / pre["ms_per_step"]
     if args.decode != "none":
         dec = bench_decode(args.decode, max(args.steps, 10), args.warmup,
                            with_dense=args.dense != "none")
@@ -386,6 +389,9 @@ def main():
         if "dense_ms" in m_pre:
             m.update(dense_ms=m_pre["dense_ms"],
                      speedup_vs_dense=m_pre["dense_ms"] / m_pre["ms_per_step"])
+        m_roof = m_pre["dense_flop"] / (BF16_PEAK_TFLOPS * 1e12) * 1e3
+        m.update(dense_at_mfma_peak_ms=m_roof,
+                 speedup_vs_dense_at_mfma_peak=m_roof / m_pre["ms_per_step"])
         out["prefill_1m_chunk"] = m
         log(f"prefill prefill_1m_chunk: {m_pre['ms_per_step']:.2f} ms/step")
         m_dec = bench_decode("decode_1m_b4", max(args.steps, 10), args.warmup,
