@@ -33,8 +33,11 @@ COPY_BYTES = 1 << 30  # the plain copy that calibrates the HBM byte counters
 # HBM counters of the dominant kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE) with
 # the hash of the sources they were taken from
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_128k_hbm_traffic.txt")
+# (the kernel's own file, and the types and device helpers of the internal
+# header: the text before its launcher declarations)
 KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_long_08_amd", "csrc", f)
                   for f in ("attention.hip", "qsa_internal.h")]
+HEADER_CUT = "launchers --"
 
 WORKLOADS = {
     # name: (Tq, pos0, budget, needles per KV head)
@@ -235,7 +238,10 @@ def kernel_source_hash():
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(f, "rb") as fh:
-            h.update(fh.read())
+            data = fh.read()
+        if f.endswith(".h"):
+            data = data.split(HEADER_CUT.encode())[0]
+        h.update(data)
     return h.hexdigest()
 
 

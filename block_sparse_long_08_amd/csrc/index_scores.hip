@@ -151,7 +151,8 @@ template <int MODE>
 __global__ void __launch_bounds__(256)
 index_scores_decode(const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ kbar,
                     const int64_t *__restrict__ seq_len, int64_t nb_max,
-                    float *__restrict__ scores, int64_t ld) {
+                    float *__restrict__ scores, int64_t ld, uint32_t *__restrict__ gmax,
+                    int64_t gld) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[4 * 64 * kIdxDim * 2];
     const int64_t seq = blockIdx.y;
     const int64_t p = seq_len[seq] - 1;
@@ -185,6 +186,7 @@ index_scores_decode(const uint16_t *__restrict__ q_idx, const uint16_t *__restri
     float *out = scores + seq * ld;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile has landed
     __builtin_amdgcn_wave_barrier();
+    uint32_t kmax = 0u;  // largest key of the wave's valid blocks (lanes 0..15)
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
         const int row = 16 * jt + n;  // row % 16 == n
@@ -196,22 +198,35 @@ index_scores_decode(const uint16_t *__restrict__ q_idx, const uint16_t *__restri
             acc = mfma_bf16_16x16x32(qf[s], as_bf16x8(kv), acc);
         }
         const int64_t blk = w0 + row;
-        if (g4 == 0 && blk < nc) out[blk] = combine_heads<MODE>(acc);
+        const float v = combine_heads<MODE>(acc);
+        if (g4 == 0 && blk < nc) {
+            out[blk] = v;
+            kmax = max(kmax, score_key(v));
+        }
+    }
+    // Group maximum of the 64 blocks (a floor source for the top-K): lanes
+    // 0..15 fold within their 16-lane group.
+    if (gmax) {
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1)
+            kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), off)));
+        if (lane == 0) gmax[seq * gld + (w0 >> 6)] = kmax;
     }
 }
 
 hipError_t launch_index_scores(const uint16_t *q_idx, const uint16_t *kbar, int B, int64_t Tq,
                                int64_t pos0, const int64_t *seq_len, int64_t nb_max, int mode,
-                               float *scores, int64_t ld, hipStream_t s) {
+                               float *scores, int64_t ld, hipStream_t s, uint32_t *gmax,
+                               int64_t gld) {
     if (B == 0 || Tq == 0 || nb_max == 0) return hipSuccess;
     if (seq_len) {
         const dim3 grid(static_cast<uint32_t>((nb_max + 255) / 256), static_cast<uint32_t>(B));
         if (mode == 0)
             hipLaunchKernelGGL(index_scores_decode<0>, grid, dim3(256), 0, s, q_idx, kbar,
-                               seq_len, nb_max, scores, ld);
+                               seq_len, nb_max, scores, ld, gmax, gld);
         else
             hipLaunchKernelGGL(index_scores_decode<1>, grid, dim3(256), 0, s, q_idx, kbar,
-                               seq_len, nb_max, scores, ld);
+                               seq_len, nb_max, scores, ld, gmax, gld);
         return hipGetLastError();
     }
     const int64_t n_qt = (Tq + kQT - 1) / kQT;

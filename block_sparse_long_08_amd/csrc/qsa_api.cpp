@@ -165,6 +165,10 @@ static void select_layout(int B, int64_t Tq, int64_t nb_max, int K, int64_t *ld,
     const int64_t rows = decode ? B : *chunk;
     *score_bytes = static_cast<size_t>(round_up(rows * *ld * 4, 256));
     *topk_bytes = topk_plan(rows, nb_max, K).ws_bytes;
+    if (decode) {  // or the decode-form candidate lists, whichever is larger
+        const size_t lb = dec_list_layout(rows, nb_max, K).ws_bytes;
+        *topk_bytes = lb > *topk_bytes ? lb : *topk_bytes;
+    }
 }
 
 size_t qsa_select_workspace_bytes(int B, int64_t Tq, int64_t nb_max, int K) {
@@ -196,6 +200,16 @@ int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_
     select_layout(B, Tq, nb_max, K, &ld, &chunk, &sb, &tb);
     float *sc = static_cast<float *>(ws);
     void *tws = need > 0 ? static_cast<char *>(ws) + sb : nullptr;
+    if (seq_len && dec_list_layout(B, nb_max, K).use) {
+        // decode form, long rows: the scan also writes the group maxima the
+        // top-K filter takes its floor from (start of the top-K workspace)
+        const DecListLayout l = dec_list_layout(B, nb_max, K);
+        hipError_t e = launch_index_scores(q_idx, kbar, B, Tq, pos0, seq_len, nb_max, score_mode,
+                                           sc, ld, s, static_cast<uint32_t *>(tws), l.gld);
+        if (e != hipSuccess) return QSA_ERR_LAUNCH;
+        return launch_status(launch_topk_dec_lists(sc, B, ld, seq_len, nb_max, r, K, blk_idx,
+                                                   n_sel, tws, s));
+    }
     if (seq_len || Tq == 1) {
         hipError_t e = launch_index_scores(q_idx, kbar, B, Tq, pos0, seq_len, nb_max, score_mode,
                                            sc, ld, s);

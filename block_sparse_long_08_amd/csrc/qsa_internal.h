@@ -70,9 +70,13 @@ hipError_t launch_compress(const uint16_t *k, int B, int64_t Tk, int64_t k_seq_s
                            int r, int mode, uint16_t *kbar, int64_t kbar_seq_stride,
                            hipStream_t s);
 
+// Decode form (seq_len given): when gmax is set, also writes the largest
+// score key of every group of 64 consecutive blocks, gmax[b * gld + g] for
+// the groups holding complete blocks.
 hipError_t launch_index_scores(const uint16_t *q_idx, const uint16_t *kbar, int B, int64_t Tq,
                                int64_t pos0, const int64_t *seq_len, int64_t nb_max, int mode,
-                               float *scores, int64_t ld, hipStream_t s);
+                               float *scores, int64_t ld, hipStream_t s,
+                               uint32_t *gmax = nullptr, int64_t gld = 0);
 
 // Top-K passes for rows of up to nmax candidates: either one streaming pass
 // per row, or npass reduction passes (segment lengths seg[i], entries[i]
@@ -93,6 +97,21 @@ TopkPlan topk_plan(int64_t rows, int64_t nmax, int K);
 hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64_t pos0,
                        const int64_t *seq_len, int64_t nb_max, int r, int K, int32_t *blk_idx,
                        int32_t *n_sel, void *ws, hipStream_t s);
+
+// Decode-form top-K for few long rows (one query per sequence): a filter
+// pass over 4,096-key segments against a floor from the scan's group maxima,
+// then one exact pass per row over the candidates.  Workspace: the group
+// maxima [rows][gld] (written by the scan), then the candidate keys and
+// indices [rows][lld] and the per-segment counts [rows][cld].
+struct DecListLayout {
+    bool use;  // false: the general plan applies
+    int64_t gld, lld, cld;
+    size_t ws_bytes;
+};
+DecListLayout dec_list_layout(int64_t rows, int64_t nb_max, int K);
+hipError_t launch_topk_dec_lists(const float *scores, int B, int64_t ld, const int64_t *seq_len,
+                                 int64_t nb_max, int r, int K, int32_t *blk_idx, int32_t *n_sel,
+                                 void *ws, hipStream_t s);
 
 // Sparse / dense attention over 4-token blocks (see attention.hip).
 struct AttnArgs {

@@ -572,12 +572,11 @@ __device__ __forceinline__ void stream_append(const uint32_t (&kk)[4], uint32_t 
 }
 
 template <int kStNT>
-__global__ void __launch_bounds__(kStNT) topk_stream(TopkArgs a) {
+__device__ __forceinline__ void stream_row(const TopkArgs &a, int64_t row,
+                                           StreamSmem<kStNT> &sm) {
     constexpr int kStNW = kStNT / kWave;
     constexpr uint32_t kCap = StreamSmem<kStNT>::CAP;
-    __shared__ StreamSmem<kStNT> sm;
     TopkSmem<kStNT> &sh = sm.t;
-    const int64_t row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t sq = row / a.Tq;
     const int64_t p = a.seq_len ? a.seq_len[sq] - 1 : a.pos0 + (row - sq * a.Tq);
@@ -827,6 +826,327 @@ __global__ void __launch_bounds__(kStNT) topk_stream(TopkArgs a) {
     if (tid == 0) a.n_sel[row] = static_cast<int32_t>(nsel);
 }
 
+template <int kStNT>
+__global__ void __launch_bounds__(kStNT) topk_stream(TopkArgs a) {
+    __shared__ StreamSmem<kStNT> sm;
+    stream_row<kStNT>(a, blockIdx.x, sm);
+}
+
+// ------------------------------------------------- decode form, few rows --
+// Few long rows (one query per sequence) with the group maxima the decode
+// scan writes (the largest key of every 64 consecutive blocks):
+//   filter (workgroup per 4,096-key segment of a row): the K-th largest group
+//     maximum has at least K keys at or above it, so the lower edge of its
+//     12-bit bin is a floor under the row's K-th largest key; the segment's
+//     keys at or above the floor go, in index order, to the segment's slots
+//     of a candidate list in the workspace (a row with fewer than K groups
+//     keeps every key);
+//   final (workgroup per row): the segments' lists are packed in LDS, the
+//     exact K-th key and tie quota come from three histogram digits, and
+//     the selection is emitted in index order.  A row whose lists exceed
+//     the LDS capacity (short rows, heavy ties) runs the streaming
+//     selection over its scores instead; the result is the same.
+// Many workgroups share each row, so the row's keys are read once and at
+// the full memory rate instead of by one workgroup per row.
+constexpr int kDecSeg = 4096;       // keys per filter workgroup (256 threads x 16)
+constexpr int kDecMaxSeg = 1024;    // segments per row (rows of up to 4M blocks)
+constexpr int kDecListCap = 8192;   // candidates per row packed in LDS
+
+struct DecTopkArgs {
+    TopkArgs t;              // scores, ld, Tq = 1, seq_len, nb_max, r, K, outputs
+    const uint32_t *gmax;    // [rows][gld] group maxima (keys)
+    int64_t gld;
+    uint32_t *lkey;          // [rows][lld] candidate keys, segment s at s * kDecSeg
+    int32_t *lidx;           //   and block indices
+    int64_t lld;
+    uint32_t *lcnt;          // [rows][cld] candidates per segment
+    int64_t cld;
+};
+
+__device__ __forceinline__ int64_t dec_row_blocks(const TopkArgs &a, int64_t row) {
+    const int64_t p = a.seq_len[row] - 1;
+    return min(num_complete_blocks(p, a.r), a.nb_max);
+}
+
+// Block-wide minimum and maximum (every thread gets both); uses wcnt/wtot.
+template <int NT>
+__device__ __forceinline__ void block_minmax(uint32_t &lo, uint32_t &hi, TopkSmem<NT> &sh,
+                                             int lane, int wave) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), off)));
+        hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), off)));
+    }
+    if (lane == 0) {
+        sh.wtot[wave] = lo;
+        sh.wcnt[wave] = hi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) {
+        lo = min(lo, sh.wtot[w]);
+        hi = max(hi, sh.wcnt[w]);
+    }
+}
+
+// Bit length of x (0 for 0).
+__device__ __forceinline__ int bit_len(uint32_t x) { return 32 - __clz(static_cast<int>(x)); }
+
+__global__ void __launch_bounds__(256) topk_dec_filter(DecTopkArgs d) {
+    constexpr int NT = 256;
+    __shared__ TopkSmem<NT> sh;
+    const TopkArgs &a = d.t;
+    const int64_t row = blockIdx.y;
+    const int seg = blockIdx.x;
+    const int64_t n_row = dec_row_blocks(a, row);
+    const uint32_t K = static_cast<uint32_t>(a.K);
+    if (n_row <= a.K || static_cast<int64_t>(seg) * kDecSeg >= n_row) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = static_cast<int>(n_row);
+    const float *srow = a.scores + row * a.ld;
+    const int base = seg * kDecSeg + wave * 1024 + 4 * lane;
+    uint32_t kk[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) stream_keys(srow, base + 256 * u, n, kk[u]);
+
+    // Floor from the group maxima (the first 4,096 loaded with the keys):
+    // 4,096 bins spanning [min, max] of the maxima; the K-th largest maximum
+    // lies in bin b, so at least K keys are >= min + (b << shift).
+    const int ngrp = (n + 63) >> 6;
+    uint32_t floor_key = kMinKey;
+    if (ngrp >= a.K) {
+        const uint32_t *g = d.gmax + row * d.gld;
+        uint32_t gv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int i = tid + NT * j;
+            gv[j] = g[i < ngrp ? i : 0];
+        }
+        uint32_t lo = gv[0], hi = gv[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) {
+            lo = min(lo, gv[j]);
+            hi = max(hi, gv[j]);
+        }
+        for (int i = tid + 16 * NT; i < ngrp; i += NT) {
+            lo = min(lo, g[i]);
+            hi = max(hi, g[i]);
+        }
+        for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;
+        block_minmax<NT>(lo, hi, sh, lane, wave);
+        const int L = bit_len(hi - lo);
+        const int shift = L > 12 ? L - 12 : 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (tid + NT * j < ngrp) atomicAdd(&sh.hist[(gv[j] - lo) >> shift], 1u);
+        for (int i = tid + 16 * NT; i < ngrp; i += NT)
+            atomicAdd(&sh.hist[(g[i] - lo) >> shift], 1u);
+        __syncthreads();
+        block_find<NT, kBins, 1, false>(sh.hist, K, sh, tid, lane, wave);
+        floor_key = max(lo + (sh.fd_bin << shift), kMinKey);
+    }
+
+    // ordered write of the keys at or above the floor
+    uint32_t wc = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            wc += static_cast<uint32_t>(__popcll(__ballot(kk[u][c] >= floor_key)));
+    if (lane == 0) sh.wcnt[wave] = wc;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) {
+        off += w < wave ? sh.wcnt[w] : 0u;
+        tot += sh.wcnt[w];
+    }
+    const int64_t obase = row * d.lld + static_cast<int64_t>(seg) * kDecSeg;
+    uint32_t run = off;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        stream_append(kk[u], floor_key, base + 256 * u, 0xFFFFFFFFu, run, d.lkey + obase,
+                      d.lidx + obase);
+    if (tid == 0) d.lcnt[row * d.cld + seg] = tot;
+}
+
+struct DecFinalSmem {
+    TopkSmem<1024> t;
+    uint32_t ck[kDecListCap];
+    int32_t ci[kDecListCap];
+    uint32_t segoff[kDecMaxSeg + 1];
+    uint32_t eqtot[16];
+};
+
+union DecFinalLds {
+    DecFinalSmem f;
+    StreamSmem<1024> st;
+};
+
+__global__ void __launch_bounds__(1024) topk_dec_final(DecTopkArgs d) {
+    constexpr int NT = 1024, NW = NT / kWave;
+    __shared__ DecFinalLds lds;
+    DecFinalSmem &f = lds.f;
+    TopkSmem<NT> &sh = f.t;
+    const TopkArgs &a = d.t;
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n_row = dec_row_blocks(a, row);
+    const uint32_t K = static_cast<uint32_t>(a.K);
+    int32_t *out = a.blk_idx + row * a.K;
+    if (n_row <= a.K) {  // every complete block is selected
+        for (int i = tid; i < a.K; i += NT) out[i] = i < n_row ? i : -1;
+        if (tid == 0) a.n_sel[row] = static_cast<int32_t>(n_row);
+        return;
+    }
+    const int nseg = static_cast<int>((n_row + kDecSeg - 1) / kDecSeg);
+    // The first 128 entries of segments wave + 16 q (q < 4) are loaded
+    // before the counts are known (typical lists are shorter), so the lists
+    // and their counts arrive in one round trip.
+    uint32_t pk[4][2];
+    int32_t pi[4][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int sidx = min(wave + NW * q, nseg - 1);
+        const int64_t src = row * d.lld + static_cast<int64_t>(sidx) * kDecSeg;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            pk[q][u] = d.lkey[src + lane + kWave * u];
+            pi[q][u] = d.lidx[src + lane + kWave * u];
+        }
+    }
+    // exclusive prefix of the segment counts (wave 0)
+    if (wave == 0) {
+        uint32_t carry = 0;
+        const uint32_t *cnt = d.lcnt + row * d.cld;
+        for (int s0 = 0; s0 < nseg; s0 += kWave) {
+            const int sidx = s0 + lane;
+            const uint32_t c = sidx < nseg ? cnt[sidx] : 0u;
+            const uint32_t incl = wave_incl_scan(c, lane);
+            if (sidx < nseg) f.segoff[sidx] = carry + incl - c;
+            carry += __shfl(incl, kWave - 1, kWave);
+        }
+        if (lane == 0) f.segoff[nseg] = carry;
+    }
+    __syncthreads();
+    const uint32_t total = f.segoff[nseg];
+    if (total > static_cast<uint32_t>(kDecListCap)) {
+        __syncthreads();  // segoff read by all before the union is reused
+        stream_row<NT>(a, row, lds.st);
+        return;
+    }
+    // pack the lists (index order) into LDS
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int sidx = wave + NW * q;
+        if (sidx < nseg) {
+            const uint32_t o = f.segoff[sidx], c = f.segoff[sidx + 1] - o;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const uint32_t j = lane + kWave * u;
+                if (j < c) {
+                    f.ck[o + j] = pk[q][u];
+                    f.ci[o + j] = pi[q][u];
+                }
+            }
+        }
+    }
+    for (int sidx = wave; sidx < nseg; sidx += NW) {
+        const uint32_t o = f.segoff[sidx], c = f.segoff[sidx + 1] - o;
+        const int64_t src = row * d.lld + static_cast<int64_t>(sidx) * kDecSeg;
+        const uint32_t j0 = sidx < 4 * NW ? 2 * kWave : 0u;  // the rest
+        for (uint32_t j = j0 + lane; j < c; j += kWave) {
+            f.ck[o + j] = d.lkey[src + j];
+            f.ci[o + j] = d.lidx[src + j];
+        }
+    }
+    for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;
+    __syncthreads();
+
+    uint32_t thr = 0, quota = 0, eqcnt = 0;
+    bool split = false;
+    if (total > K) {
+        // Radix select on v = key - min over the list: digits of up to 12
+        // bits from the top of the list's range down to bit 0 (two levels
+        // for a range under 2^24), so the bins follow the data.
+        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+        for (uint32_t i = tid; i < total; i += NT) {
+            lo = min(lo, f.ck[i]);
+            hi = max(hi, f.ck[i]);
+        }
+        block_minmax<NT>(lo, hi, sh, lane, wave);
+        const int L = bit_len(hi - lo);
+        int s = L > 12 ? L - 12 : 0, s_prev = 32;
+        uint32_t hp = 0, krem = K;  // hp: the resolved bits v >> s_prev
+        for (;;) {
+            const uint32_t dmask = (1u << (s_prev - s > 12 ? 12 : s_prev - s)) - 1u;
+            for (uint32_t i = tid; i < total; i += NT) {
+                const uint32_t v = f.ck[i] - lo;
+                if (s_prev == 32 || (v >> s_prev) == hp)
+                    atomicAdd(&sh.hist[(v >> s) & dmask], 1u);
+            }
+            __syncthreads();
+            block_find<NT, kBins, 1, false>(sh.hist, krem, sh, tid, lane, wave);
+            const uint32_t dg = sh.fd_bin;
+            krem -= sh.fd_above;
+            eqcnt = sh.hist[dg];
+            hp = s_prev == 32 ? dg : (hp << (s_prev - s)) | dg;
+            if (s == 0) break;
+            s_prev = s;
+            s = s > 12 ? s - 12 : 0;
+            __syncthreads();  // every thread has read the histogram
+            for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;
+            __syncthreads();
+        }
+        thr = lo + hp;
+        quota = krem;
+        split = quota != eqcnt;
+    }
+    // emission: wave w takes the contiguous run [c0, c1) of the packed list
+    const uint32_t chunk = (total + NW * kWave - 1) / (NW * kWave) * kWave;
+    const uint32_t c0 = min(total, wave * chunk), c1 = min(total, c0 + chunk);
+    uint32_t gt_w = 0, eq_w = 0;
+    for (uint32_t i0 = c0; i0 < c1; i0 += kWave) {
+        const uint32_t i = i0 + lane;
+        const uint32_t key = i < c1 ? f.ck[i] : 0u;
+        const bool gt = split ? key > thr : (i < c1 && key >= thr);
+        gt_w += static_cast<uint32_t>(__popcll(__ballot(gt)));
+        eq_w += static_cast<uint32_t>(__popcll(__ballot(split && key == thr)));
+    }
+    __syncthreads();  // every thread has read the histogram
+    if (lane == 0) {
+        sh.wtot[wave] = gt_w;
+        f.eqtot[wave] = eq_w;
+    }
+    __syncthreads();
+    uint32_t gt_off = 0, eq_off = 0, gt_all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t g = sh.wtot[w], e = f.eqtot[w];
+        if (w < wave) {
+            gt_off += g;
+            eq_off += e;
+        }
+        gt_all += g;
+    }
+    for (uint32_t i0 = c0; i0 < c1; i0 += kWave) {
+        const uint32_t i = i0 + lane;
+        const bool ok = i < c1;
+        const uint32_t key = ok ? f.ck[i] : 0u;
+        const int32_t idx = ok ? f.ci[i] : 0;
+        const bool gt = split ? key > thr : (ok && key >= thr);
+        const bool eq = split && key == thr;
+        const uint64_t bg = __ballot(gt), be = __ballot(eq);
+        const uint32_t gr = gt_off + lanes_below(bg), er = eq_off + lanes_below(be);
+        if (gt || (eq && er < quota)) out[gr + min(er, quota)] = idx;
+        gt_off += static_cast<uint32_t>(__popcll(bg));
+        eq_off += static_cast<uint32_t>(__popcll(be));
+    }
+    const uint32_t nsel = split ? K : gt_all;
+    for (uint32_t i = nsel + tid; i < K; i += NT) out[i] = -1;
+    if (tid == 0) a.n_sel[row] = static_cast<int32_t>(nsel);
+}
+
 // ------------------------------------------------------------------ plan --
 TopkPlan topk_plan(int64_t rows, int64_t nmax, int K) {
     TopkPlan pl{};
@@ -957,6 +1277,55 @@ hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64
         else
             hipLaunchKernelGGL((topk_pass<1024, 32, 0, 0>), dim3(gx), dim3(1024), 0, s, a);
     }
+    return hipGetLastError();
+}
+
+DecListLayout dec_list_layout(int64_t rows, int64_t nb_max, int K) {
+    DecListLayout l{};
+    const int64_t nseg = (nb_max + kDecSeg - 1) / kDecSeg;
+    // few rows of more blocks than one register-resident pass takes
+    l.use = rows > 0 && rows < 256 && nb_max > kStreamMin && nseg <= kDecMaxSeg &&
+            K <= kDecSeg;
+    if (!l.use) return l;
+    l.gld = ((nb_max + 63) / 64 + 3) / 4 * 4;
+    l.lld = nseg * kDecSeg;
+    l.cld = (nseg + 3) / 4 * 4;
+    l.ws_bytes = static_cast<size_t>(rows) * static_cast<size_t>(l.gld + 2 * l.lld + l.cld) * 4u;
+    return l;
+}
+
+hipError_t launch_topk_dec_lists(const float *scores, int B, int64_t ld, const int64_t *seq_len,
+                                 int64_t nb_max, int r, int K, int32_t *blk_idx, int32_t *n_sel,
+                                 void *ws, hipStream_t s) {
+    if (B == 0) return hipSuccess;
+    const DecListLayout l = dec_list_layout(B, nb_max, K);
+    DecTopkArgs d{};
+    d.t.scores = scores;
+    d.t.ld = ld;
+    d.t.blk_idx = blk_idx;
+    d.t.n_sel = n_sel;
+    d.t.Tq = 1;
+    d.t.pos0 = 0;
+    d.t.nb_max = nb_max;
+    d.t.seq_len = seq_len;
+    d.t.r = r;
+    d.t.K = K;
+    char *w = static_cast<char *>(ws);
+    d.gmax = reinterpret_cast<const uint32_t *>(w);
+    d.gld = l.gld;
+    w += static_cast<size_t>(B) * l.gld * 4;
+    d.lkey = reinterpret_cast<uint32_t *>(w);
+    w += static_cast<size_t>(B) * l.lld * 4;
+    d.lidx = reinterpret_cast<int32_t *>(w);
+    w += static_cast<size_t>(B) * l.lld * 4;
+    d.lcnt = reinterpret_cast<uint32_t *>(w);
+    d.lld = l.lld;
+    d.cld = l.cld;
+    const dim3 grid(static_cast<uint32_t>(l.lld / kDecSeg), static_cast<uint32_t>(B));
+    hipLaunchKernelGGL(topk_dec_filter, grid, dim3(256), 0, s, d);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_dec_final, dim3(static_cast<uint32_t>(B)), dim3(1024), 0, s, d);
     return hipGetLastError();
 }
 

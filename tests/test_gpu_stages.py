@@ -322,6 +322,77 @@ def test_select_matches_scores_plus_topk(qsa, mode, Tq, pos0, K):
     assert np.array_equal(b1, b2.cpu().numpy())
 
 
+def _decode_select(qsa, qi, kb, lens, K, mode=0):
+    """qsa_select_blocks in the decode form; also returns the GPU scores."""
+    torch = _torch()
+    B, nb_max = kb.shape[0], kb.shape[1]
+    ld = (nb_max + 3) // 4 * 4
+    qd, kd, ln = dev(qi), dev(kb), dev(lens)
+    sc = torch.empty((B, ld), dtype=torch.float32, device="cuda")
+    qsa.qsa_index_scores(qd, kd, B, 1, 0, ln, nb_max, 4, 128, 4, mode, sc, ld)
+    blk = torch.full((B, K), 7, dtype=torch.int32, device="cuda")
+    ns = torch.full((B,), 7, dtype=torch.int32, device="cuda")
+    wsb = qsa.qsa_select_workspace_bytes(B, 1, nb_max, K)
+    ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device="cuda")
+    qsa.qsa_select_blocks(qd, kd, B, 1, 0, ln, nb_max, 4, 128, 4, mode, K, blk, ns, ws, wsb)
+    torch.cuda.synchronize()
+    return sc.cpu().numpy(), blk.cpu().numpy(), ns.cpu().numpy()
+
+
+def _check_decode_rows(scores, blk, ns, lens, nb_max, K):
+    """Each row's selection is the exact (score desc, index asc) top-K of the
+    row's GPU scores."""
+    for b in range(lens.size):
+        nc = min(int(lens[b]) // 4, nb_max)
+        row = scores[b, :nc].astype(np.float64)
+        row[row == 0] = 0.0
+        want, _, _ = oracle.topk_row(row, K)
+        assert ns[b] == want.size, (b, int(ns[b]), want.size)
+        assert np.array_equal(blk[b, :ns[b]], want), b
+        assert np.all(blk[b, ns[b]:] == -1), b
+
+
+@pytest.mark.parametrize("K,mode", [(512, 0), (512, 1), (2048, 0), (64, 0)])
+def test_select_decode_form_long_rows(qsa, K, mode):
+    """Decode-form selection over long pooled-key caches (the filter pass on
+    a floor from the scan's group maxima, then one exact pass per row), with
+    ragged lengths: rows at or under K, rows too short for the floor (all
+    keys kept, packed or streamed), a ragged last segment, needle blocks,
+    rows of 16 and 300 distinct pooled keys (ties at the threshold) and an
+    all-equal row (lists beyond the LDS capacity: streamed)."""
+    nb_max = 65536 + 7
+    lens = np.array([4 * nb_max, 4 * nb_max - 1, 4 * 40000 + 3, 4 * 20000, 4 * 6000, 4 * K + 3,
+                     1, 4 * 33000, 4 * nb_max, 4 * nb_max, 4 * nb_max], dtype=np.int64)
+    B = lens.size
+    qi = synth.normal_bf16(4, (B, 4, 128), seed=21)
+    kb = synth.normal_bf16(5, (B, nb_max, 128), seed=21)
+    rng = np.random.default_rng(21)
+    # needles: 40 blocks of row 2 scaled by 4 (bf16 exponent + 2)
+    nd = rng.choice(40000, 40, replace=False)
+    kb[2, nd] = (kb[2, nd].astype(np.uint32) + (2 << 7)).astype(np.uint16)
+    kb[8] = kb[8, rng.integers(0, 16, nb_max)]          # 16 distinct keys
+    kb[9] = kb[9, rng.integers(0, 300, nb_max)]         # 300 distinct keys
+    kb[10] = kb[10, 0]                                  # all equal
+    scores, blk, ns = _decode_select(qsa, qi, kb, lens, K, mode)
+    _check_decode_rows(scores, blk, ns, lens, nb_max, K)
+
+
+def test_select_decode_form_million_tokens(qsa):
+    """Decode-form selection at 1,048,576 tokens (4,096 groups per row) with
+    needle blocks, and a row whose scores agree with the old path's."""
+    nb_max, K = 262144, 512
+    lens = np.array([4 * nb_max, 4 * nb_max - 2, 4 * 200000 + 1], dtype=np.int64)
+    B = lens.size
+    qi = synth.normal_bf16(4, (B, 4, 128), seed=22)
+    kb = synth.normal_bf16(5, (B, nb_max, 128), seed=22)
+    nd = np.random.default_rng(22).choice(nb_max, 64, replace=False)
+    kb[0, nd] = (kb[0, nd].astype(np.uint32) + (2 << 7)).astype(np.uint16)
+    scores, blk, ns = _decode_select(qsa, qi, kb, lens, K)
+    _check_decode_rows(scores, blk, ns, lens, nb_max, K)
+    g, n = run_topk(qsa, dev(scores), B, 1, nb_max, 0, dev(lens), nb_max, K)
+    assert np.array_equal(g, blk) and np.array_equal(n, ns)
+
+
 # ---------------------------------------------------------- A6 attention
 def test_sparse_prefill_attention_parity(qsa):
     torch = _torch()
