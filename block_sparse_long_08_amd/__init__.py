@@ -40,7 +40,7 @@ def _sig(name, res, *args):
 _lib_status_string = _sig("qsa_status_string", ctypes.c_char_p, _i32)
 _sig("qsa_version", _i32)
 _sig("qsa_check_device", _i32)
-_sig("qsa_rope_bf16", _i32, _vp, _vp, _i64, _i32, _i32, _i32, _dbl, _i64, _vp, _vp)
+_sig("qsa_rope_bf16", _i32, _vp, _vp, _i64, _i32, _i32, _i32, _dbl, _i64, _vp, _i32, _vp)
 _sig("qsa_compress_keys", _i32, _vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _i64, _vp)
 _sig("qsa_index_scores", _i32, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _i32, _i32, _i32, _i32,
      _vp, _i64, _vp)
@@ -52,9 +52,9 @@ _sig("qsa_select_blocks", _i32, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _i32, _i3
      _i32, _vp, _vp, _vp, _sz, _vp)
 _sig("qsa_sparse_attn_prefill", _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
      _i32, _i32, _vp, _vp, _vp)
-_sig("qsa_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32)
-_sig("qsa_sparse_attn_decode", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
-     _i32, _i32, _vp, _vp, _vp, _sz, _vp)
+_sig("qsa_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32, _i32)
+_sig("qsa_sparse_attn_decode", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32,
+     _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp)
 _sig("dense_attn_workspace_bytes", _sz, _i32, _i64, _i64, _i32, _i32, _i32)
 _sig("dense_attn", _i32, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _i32, _i32, _vp, _vp,
      _vp, _sz, _vp)
@@ -113,9 +113,10 @@ def qsa_check_device() -> None:
 
 
 def qsa_rope_bf16(x, y, T: int, nheads: int, head_dim: int, rope_dim: int = 64,
-                  theta: float = 1e7, pos0: int = 0, seq_len=None, stream=None) -> None:
+                  theta: float = 1e7, pos0: int = 0, seq_len=None, next_n: int = 1,
+                  stream=None) -> None:
     _call("qsa_rope_bf16", _ptr(x), _ptr(y), T, nheads, head_dim, rope_dim, theta, pos0,
-          _ptr(seq_len), _stream(stream))
+          _ptr(seq_len), next_n, _stream(stream))
 
 
 def qsa_compress_keys(k, B: int, Tk: int, k_seq_stride: int, Di: int, r: int, kbar_mode: int,
@@ -158,16 +159,16 @@ def qsa_sparse_attn_prefill(Q, K, V, blk_idx, n_sel, Tq: int, Tk: int, pos0: int
           Tk, pos0, H, Hkv, D, r, Kbudget, _ptr(O), _ptr(lse), _stream(stream))
 
 
-def qsa_decode_workspace_bytes(B: int, H: int, Hkv: int, D: int, Kbudget: int) -> int:
-    return int(_lib.qsa_decode_workspace_bytes(B, H, Hkv, D, Kbudget))
+def qsa_decode_workspace_bytes(B: int, Tq: int, H: int, Hkv: int, D: int, Kbudget: int) -> int:
+    return int(_lib.qsa_decode_workspace_bytes(B, Tq, H, Hkv, D, Kbudget))
 
 
-def qsa_sparse_attn_decode(q, Kc, Vc, seq_len, blk_idx, n_sel, B: int, Lmax: int, H: int,
-                           Hkv: int, D: int, r: int, Kbudget: int, O, lse, ws, ws_bytes: int,
-                           stream=None) -> None:
+def qsa_sparse_attn_decode(q, Kc, Vc, seq_len, blk_idx, n_sel, B: int, Tq: int, Lmax: int,
+                           H: int, Hkv: int, D: int, r: int, Kbudget: int, O, lse, ws,
+                           ws_bytes: int, stream=None) -> None:
     _call("qsa_sparse_attn_decode", _ptr(q), _ptr(Kc), _ptr(Vc), _ptr(seq_len), _ptr(blk_idx),
-          _ptr(n_sel), B, Lmax, H, Hkv, D, r, Kbudget, _ptr(O), _ptr(lse), _ptr(ws), ws_bytes,
-          _stream(stream))
+          _ptr(n_sel), B, Tq, Lmax, H, Hkv, D, r, Kbudget, _ptr(O), _ptr(lse), _ptr(ws),
+          ws_bytes, _stream(stream))
 
 
 def dense_attn_workspace_bytes(B: int, Tq: int, Lmax: int, H: int, Hkv: int, D: int) -> int:

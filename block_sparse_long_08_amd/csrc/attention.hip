@@ -45,17 +45,31 @@ __device__ __forceinline__ void lds_fence() {
     __builtin_amdgcn_wave_barrier();
 }
 
-// Entry e of a query's list: first token and number of valid tokens.
+// Entry e of a query's list: first token and number of tokens.  Entries
+// below ns are selected complete blocks; the rest cover the tail, tokens
+// 4*nc .. 4*nc + tail - 1 after the selection's visible blocks (the query's
+// incomplete block, and for later speculative queries sharing the selection
+// also the tokens up to their own positions).
 struct EntryList {
     const int32_t *lst;  // LDS copy of the selected blocks (sparse), or nullptr (dense)
     int lst_off;         // index of lst[0] in the query's list
     int ns;              // number of complete-block entries
-    int pr;              // tokens in the partial block (0..3)
-    int64_t nc;          // complete blocks visible to the query
-    __device__ __forceinline__ int count(int e) const { return e < ns ? 4 : (e == ns ? pr : 0); }
+    int tail;            // tail tokens after block nc - 1
+    int64_t nc;          // complete blocks visible to the selecting query
+    __device__ __forceinline__ int count(int e) const {
+        return e < ns ? 4 : max(0, min(4, tail - 4 * (e - ns)));
+    }
     __device__ __forceinline__ int64_t base(int e) const {
         if (e < ns) return 4 * static_cast<int64_t>(lst ? lst[e - lst_off] : e);
-        return 4 * nc;
+        return 4 * (nc + e - ns);
+    }
+    // tokens of entry e visible to a query at position pq (selected blocks
+    // precede every query sharing the selection)
+    __device__ __forceinline__ int visible(int e, int64_t pq) const {
+        const int c = count(e);
+        if (e < ns) return c;
+        const int64_t v = pq - 4 * (nc + e - ns) + 1;
+        return v < 0 ? 0 : (v < c ? static_cast<int>(v) : c);
     }
 };
 
@@ -75,9 +89,9 @@ __device__ __forceinline__ void state_init(WaveState &st) {
 __device__ __forceinline__ int row_swizzle(int tt) { return 2 * ((tt >> 2) & 3); }
 
 // Entries e0 .. e0+3 of one KV head.  Kg/Vg point at token 0 of the head (row
-// stride rs elements); p is a safe row for masked tokens; vlds is the wave's
-// 8 KB LDS tile.
-__device__ __forceinline__ void attn_stage(const EntryList &L, int e0, int64_t p,
+// stride rs elements); p is a safe row for masked tokens; pq is the position
+// of the query in this lane's column; vlds is the wave's 8 KB LDS tile.
+__device__ __forceinline__ void attn_stage(const EntryList &L, int e0, int64_t p, int64_t pq,
                                            const uint16_t *__restrict__ Kg,
                                            const uint16_t *__restrict__ Vg, int64_t rs,
                                            const bf16x8 (&qT)[8], WaveState &st,
@@ -113,8 +127,8 @@ __device__ __forceinline__ void attn_stage(const EntryList &L, int e0, int64_t p
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 8; ++s) sacc = mfma_bf16_16x16x32(as_bf16x8(kf[s]), qT[s], sacc);
-    // lane (head n, group g4) holds entry e0 + g4, tokens 0..3
-    const int cnt = L.count(e0 + g4);
+    // lane (column n, group g4) holds entry e0 + g4, tokens 0..3
+    const int cnt = L.visible(e0 + g4, pq);
     float sv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sv[i] = i < cnt ? sacc[i] * kScaleLog2 : -INFINITY;
@@ -157,12 +171,17 @@ __device__ __forceinline__ void attn_stage(const EntryList &L, int e0, int64_t p
     }
 }
 
-// Q^T fragments of the heads of KV head g (columns n >= group are zero).
+// Q^T fragments of column tile ct of KV head g: column n is the pair
+// 16*ct + n = (query qi, head h of the group), query rows H * kHeadDim apart;
+// columns past ncols pairs are zero.
 __device__ __forceinline__ void load_qT(const uint16_t *__restrict__ qrow, int g, int group,
-                                        int lane, bf16x8 (&qT)[8]) {
+                                        int H, int ct, int ncols, int lane, bf16x8 (&qT)[8]) {
     const int n = lane & 15, g4 = lane >> 4;
-    const bool ok = n < group;
-    const uint16_t *src = qrow + static_cast<int64_t>(g * group + (ok ? n : 0)) * kHeadDim;
+    const int pair = 16 * ct + n;
+    const bool ok = pair < ncols;
+    const int qi = ok ? pair / group : 0, h = ok ? pair - qi * group : 0;
+    const uint16_t *src =
+        qrow + (static_cast<int64_t>(qi) * H + g * group + h) * kHeadDim;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         uint4 v = ok ? *reinterpret_cast<const uint4 *>(src + 32 * s + 8 * g4)
@@ -242,20 +261,20 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a) {
     }
     __syncthreads();
     EntryList L{lst, 0, ns, static_cast<int>((p + 1) % kBlock), nc};
-    const int E = ns + (L.pr > 0 ? 1 : 0);
+    const int E = ns + (L.tail > 0 ? 1 : 0);
     const int nstages = (E + kStageEntries - 1) / kStageEntries;
 
     const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
     const int group = a.H / a.Hkv;
     bf16x8 qT[8];
-    load_qT(a.Q + row * a.H * kHeadDim, g, group, lane, qT);
+    load_qT(a.Q + row * a.H * kHeadDim, g, group, a.H, 0, group, lane, qT);
     const int64_t rs = static_cast<int64_t>(a.Hkv) * kHeadDim;
     const uint16_t *Kg = a.K + b * a.Lmax * rs + g * kHeadDim;
     const uint16_t *Vg = a.V + b * a.Lmax * rs + g * kHeadDim;
     WaveState st;
     state_init(st);
     for (int sidx = 0; sidx < nstages; ++sidx)
-        attn_stage(L, sidx * kStageEntries, p, Kg, Vg, rs, qT, st, dyn_lds + g * kVStageBytes,
+        attn_stage(L, sidx * kStageEntries, p, p, Kg, Vg, rs, qT, st, dyn_lds + g * kVStageBytes,
                    lane);
     const float ltot = head_total(st.l);
     state_write(st, ltot, a.O + row * a.H * kHeadDim, a.lse ? a.lse + row * a.H : nullptr, g,
@@ -278,19 +297,26 @@ __device__ __forceinline__ void record_store(const WaveState &st, float *rec, in
 }
 
 // ------------------------------------------------------------------------
-// Decode: workgroup (4 waves) per (split, KV head, sequence); waves take the
-// split's stages round-robin, merge through LDS, and wave 0 writes the
-// split's record (unnormalised O^T, max, weight sum) to the workspace.
+// Decode: workgroup (4 waves) per (split, KV head x column tile, sequence);
+// waves take the split's stages round-robin, merge through LDS, and wave 0
+// writes the split's record (unnormalised O^T, max, weight sum) to the
+// workspace.  The Tq newest queries of a sequence share its selection (made
+// for the first of them, at seq_len - Tq); the columns of a tile are 16
+// (query, head) pairs and each column masks the tail past its own query.
 template <bool DENSE>
-__global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit, int sps) {
+__global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit, int sps,
+                                                          int nct) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[3 * kRecFloats * 4];
     __shared__ int32_t lst[DENSE ? 1 : kMaxListLds];
-    const int split = blockIdx.x, g = blockIdx.y;
+    const int split = blockIdx.x;
+    const int g = blockIdx.y / nct, ct = blockIdx.y - g * nct;
     const int64_t b = blockIdx.z;
+    const int nq = static_cast<int>(a.Tq);
     int64_t Lb = a.seq_len[b];
     Lb = Lb < 0 ? 0 : (Lb > a.Lmax ? a.Lmax : Lb);
-    const int64_t p = Lb - 1;
-    const int64_t nc = num_complete_blocks(p, kBlock);
+    const int64_t p_last = Lb - 1;
+    const int64_t p0 = Lb - nq;  // the selecting query
+    const int64_t nc = num_complete_blocks(p0, kBlock);
     int ns;
     if (DENSE) {
         ns = static_cast<int>(nc);
@@ -299,11 +325,16 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit
         const int64_t cap = min(static_cast<int64_t>(a.Kbudget), nc);
         ns = v < 0 ? 0 : (v > cap ? static_cast<int>(cap) : v);
     }
-    const int pr = p >= 0 ? static_cast<int>((p + 1) % kBlock) : 0;
-    const int E = ns + (pr > 0 ? 1 : 0);
+    const int tail = p_last >= 4 * nc ? static_cast<int>(p_last - 4 * nc + 1) : 0;
+    const int E = ns + (tail + 3) / 4;
     const int nstages = (E + kStageEntries - 1) / kStageEntries;
     const int s0 = split * sps, s1 = min(s0 + sps, nstages);
     const int e_lo = s0 * kStageEntries;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int group = a.H / a.Hkv;
+    // the query rows are read while the block list arrives
+    bf16x8 qT[8];
+    load_qT(a.Q + b * nq * a.H * kHeadDim, g, group, a.H, ct, nq * group, lane, qT);
     if (!DENSE) {
         const int e_hi = min(s1 * kStageEntries, ns);
         const int32_t *src = a.blk_idx + b * a.Kbudget;
@@ -313,13 +344,12 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit
             lst[i - e_lo] = bi;
         }
     }
-    EntryList L{DENSE ? nullptr : lst, e_lo, ns, pr, nc};
+    EntryList L{DENSE ? nullptr : lst, e_lo, ns, tail, nc};
     __syncthreads();
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int group = a.H / a.Hkv;
-    bf16x8 qT[8];
-    load_qT(a.Q + b * a.H * kHeadDim, g, group, lane, qT);
+    // position of this lane's column query (-1: no query, every token masked)
+    const int pair = 16 * ct + (lane & 15);
+    const int64_t pq = pair < nq * group ? p0 + pair / group : -1;
     const int64_t rs = static_cast<int64_t>(a.Hkv) * kHeadDim;
     const uint16_t *Kg = a.K + b * a.Lmax * rs + g * kHeadDim;
     const uint16_t *Vg = a.V + b * a.Lmax * rs + g * kHeadDim;
@@ -327,7 +357,8 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit
     WaveState st;
     state_init(st);
     for (int sidx = s0 + wave; sidx < s1; sidx += 4)
-        attn_stage(L, sidx * kStageEntries, p < 0 ? 0 : p, Kg, Vg, rs, qT, st, vlds, lane);
+        attn_stage(L, sidx * kStageEntries, p_last < 0 ? 0 : p_last, pq, Kg, Vg, rs, qT, st,
+                   vlds, lane);
     __syncthreads();
     float *mbuf = reinterpret_cast<float *>(lds);
     if (wave != 0) state_store(st, mbuf + (wave - 1) * kRecFloats, lane);
@@ -335,14 +366,14 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit
     if (wave == 0) {
         for (int w = 0; w < 3; ++w) state_merge(st, mbuf + w * kRecFloats, lane);
         st.l = head_total(st.l);
-        float *rec = a.part + ((b * a.Hkv + g) * nsplit + split) * static_cast<int64_t>(kRecFloats);
-        record_store(st, rec, lane);
+        const int64_t rec_id = ((b * a.Hkv + g) * nct + ct) * nsplit + split;
+        record_store(st, a.part + rec_id * static_cast<int64_t>(kRecFloats), lane);
     }
 }
 
 // Merge the split records: 4 neighbouring threads per output element
-// (b, head, d), each folding every 4th split with an online rescale, then
-// combined by shuffles; neighbouring elements read neighbouring words.
+// (b, query, head, d), each folding every 4th split with an online rescale,
+// then combined by shuffles; neighbouring elements read neighbouring words.
 __device__ __forceinline__ void merge_step(float &M, float &acc, float &l, float m2, float acc2,
                                            float l2) {
     const float mn = fmaxf(M, m2);
@@ -353,18 +384,22 @@ __device__ __forceinline__ void merge_step(float &M, float &acc, float &l, float
     M = mn;
 }
 
-__global__ void __launch_bounds__(256) attn_decode_merge(AttnArgs a, int nsplit) {
+__global__ void __launch_bounds__(256) attn_decode_merge(AttnArgs a, int nsplit, int nct) {
     const int group = a.H / a.Hkv;
     const int sub = threadIdx.x & 3;
-    const int64_t total = static_cast<int64_t>(a.B) * a.H * kHeadDim;
+    const int64_t total = static_cast<int64_t>(a.B) * a.Tq * a.H * kHeadDim;
     int64_t idx = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 2;
     const bool valid = idx < total;
     idx = valid ? idx : total - 1;
     const int d = static_cast<int>(idx % kHeadDim);
     const int hq = static_cast<int>((idx / kHeadDim) % a.H);
-    const int64_t b = idx / (static_cast<int64_t>(kHeadDim) * a.H);
-    const int g = hq / group, n = hq - g * group;
-    const float *rec = a.part + (b * a.Hkv + g) * nsplit * static_cast<int64_t>(kRecFloats);
+    const int64_t bq = idx / (static_cast<int64_t>(kHeadDim) * a.H);  // b * Tq + qi
+    const int64_t b = bq / a.Tq;
+    const int qi = static_cast<int>(bq - b * a.Tq);
+    const int g = hq / group, pair = qi * group + (hq - g * group);
+    const int ct = pair >> 4, n = pair & 15;
+    const float *rec =
+        a.part + ((b * a.Hkv + g) * nct + ct) * nsplit * static_cast<int64_t>(kRecFloats);
     float M = -INFINITY, acc = 0.f, l = 0.f;
 #pragma unroll 4
     for (int s = sub; s < nsplit; s += 4) {
@@ -375,8 +410,8 @@ __global__ void __launch_bounds__(256) attn_decode_merge(AttnArgs a, int nsplit)
     for (int off = 1; off < 4; off <<= 1)
         merge_step(M, acc, l, __shfl_xor(M, off), __shfl_xor(acc, off), __shfl_xor(l, off));
     if (sub != 0 || !valid) return;
-    a.O[(b * a.H + hq) * kHeadDim + d] = l > 0.f ? acc / l : 0.f;
-    if (a.lse && d == 0) a.lse[b * a.H + hq] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
+    a.O[(bq * a.H + hq) * kHeadDim + d] = l > 0.f ? acc / l : 0.f;
+    if (a.lse && d == 0) a.lse[bq * a.H + hq] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
 }
 
 hipError_t launch_sparse_prefill(const AttnArgs &a, hipStream_t s) {
@@ -386,6 +421,12 @@ hipError_t launch_sparse_prefill(const AttnArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(64 * a.Hkv), lds, s, a);
     return hipGetLastError();
 }
+
+int decode_col_tiles(int Tq, int group) { return (Tq * group + 15) / 16; }
+
+// Entries of the longest list: the selection (or every complete block) plus
+// the tail (at most 3 + Tq tokens).
+int64_t decode_max_entries(int Tq, int64_t sel_entries) { return sel_entries + (Tq + 6) / 4; }
 
 int decode_num_splits(int B, int Hkv, int64_t max_entries) {
     const int64_t nstages = (max_entries + kStageEntries - 1) / kStageEntries;
@@ -404,20 +445,23 @@ size_t decode_partial_floats(int B, int Hkv, int nsplit) {
 
 hipError_t launch_attn_decode(const AttnArgs &a, int nsplit, hipStream_t s) {
     if (a.B == 0) return hipSuccess;
-    const int64_t max_entries = a.blk_idx ? a.Kbudget + 1 : a.Lmax / kBlock + 1;
+    const int nq = static_cast<int>(a.Tq);
+    const int nct = decode_col_tiles(nq, a.H / a.Hkv);
+    const int64_t max_entries =
+        decode_max_entries(nq, a.blk_idx ? static_cast<int64_t>(a.Kbudget) : a.Lmax / kBlock);
     const int64_t nstages = (max_entries + kStageEntries - 1) / kStageEntries;
     const int sps = static_cast<int>((nstages + nsplit - 1) / nsplit);
-    const dim3 grid(static_cast<uint32_t>(nsplit), static_cast<uint32_t>(a.Hkv),
+    const dim3 grid(static_cast<uint32_t>(nsplit), static_cast<uint32_t>(a.Hkv * nct),
                     static_cast<uint32_t>(a.B));
     if (a.blk_idx)
-        hipLaunchKernelGGL(attn_decode_kernel<false>, grid, dim3(256), 0, s, a, nsplit, sps);
+        hipLaunchKernelGGL(attn_decode_kernel<false>, grid, dim3(256), 0, s, a, nsplit, sps, nct);
     else
-        hipLaunchKernelGGL(attn_decode_kernel<true>, grid, dim3(256), 0, s, a, nsplit, sps);
+        hipLaunchKernelGGL(attn_decode_kernel<true>, grid, dim3(256), 0, s, a, nsplit, sps, nct);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t threads = 4 * static_cast<int64_t>(a.B) * a.H * kHeadDim;
+    const int64_t threads = 4 * static_cast<int64_t>(a.B) * nq * a.H * kHeadDim;
     hipLaunchKernelGGL(attn_decode_merge, dim3(static_cast<uint32_t>((threads + 255) / 256)),
-                       dim3(256), 0, s, a, nsplit);
+                       dim3(256), 0, s, a, nsplit, nct);
     return hipGetLastError();
 }
 

@@ -35,12 +35,14 @@ __global__ void __launch_bounds__(256) rope_kernel(const uint16_t *__restrict__ 
                                                    uint16_t *__restrict__ y, int64_t T,
                                                    int nheads, int head_dim, int rope_dim,
                                                    InvFreq inv_freq, int64_t pos0,
-                                                   const int64_t *__restrict__ seq_len) {
+                                                   const int64_t *__restrict__ seq_len, int nq) {
 #pragma clang fp contract(off)
     __shared__ double cs[64], sn[64];
     const int64_t t = blockIdx.x;
     const int half = rope_dim / 2;
-    int64_t p = seq_len ? seq_len[t] - 1 : pos0 + t;
+    // decode form: row t is query t % nq of sequence t / nq, the nq newest
+    // positions of that sequence
+    int64_t p = seq_len ? seq_len[t / nq] - nq + t % nq : pos0 + t;
     if (p < 0) p = 0;
     for (int j = threadIdx.x; j < half; j += blockDim.x) {
         double ang = static_cast<double>(p) * inv_freq.v[j];
@@ -80,12 +82,12 @@ __global__ void __launch_bounds__(256) rope_kernel(const uint16_t *__restrict__ 
 
 hipError_t launch_rope(const uint16_t *x, uint16_t *y, int64_t T, int nheads, int head_dim,
                        int rope_dim, const double *inv_freq, int64_t pos0,
-                       const int64_t *seq_len, hipStream_t s) {
+                       const int64_t *seq_len, int nq, hipStream_t s) {
     if (T == 0) return hipSuccess;
     InvFreq f;
     for (int j = 0; j < 64; ++j) f.v[j] = j < rope_dim / 2 ? inv_freq[j] : 0.0;
     hipLaunchKernelGGL(rope_kernel, dim3(static_cast<uint32_t>(T)), dim3(256), 0, s, x, y, T,
-                       nheads, head_dim, rope_dim, f, pos0, seq_len);
+                       nheads, head_dim, rope_dim, f, pos0, seq_len, nq);
     return hipGetLastError();
 }
 

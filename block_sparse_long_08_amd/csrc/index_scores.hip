@@ -141,7 +141,9 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
     }
 }
 
-// Decode form: one query per sequence at seq_len[b] - 1; the kernel streams
+// Decode form: the selection of sequence b is made for the first of its nq
+// newest queries (position seq_len[b] - nq, indexer query q_idx[b][0]; nq > 1
+// when the speculative steps reuse one selection); the kernel streams
 // the pooled-key cache.  Each wave scores 64 pooled keys: 16 LDS-DMA
 // instructions copy them into a 16 KB tile, each instruction 1 KB of
 // contiguous HBM (4 keys), with the 16-byte chunks of row r stored at slot
@@ -152,10 +154,10 @@ __global__ void __launch_bounds__(256)
 index_scores_decode(const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ kbar,
                     const int64_t *__restrict__ seq_len, int64_t nb_max,
                     float *__restrict__ scores, int64_t ld, uint32_t *__restrict__ gmax,
-                    int64_t gld) {
+                    int64_t gld, int nq) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[4 * 64 * kIdxDim * 2];
     const int64_t seq = blockIdx.y;
-    const int64_t p = seq_len[seq] - 1;
+    const int64_t p = seq_len[seq] - nq;
     const int64_t nc = min(num_complete_blocks(p, kBlock), nb_max);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g4 = lane >> 4;
@@ -174,7 +176,7 @@ index_scores_decode(const uint16_t *__restrict__ q_idx, const uint16_t *__restri
                                          (__attribute__((address_space(3))) void *)(tile + 1024 * j),
                                          16, 0, 0);
     }
-    const uint16_t *q = q_idx + seq * (kIdxHeads * kIdxDim);
+    const uint16_t *q = q_idx + seq * nq * (kIdxHeads * kIdxDim);
     bf16x8 qf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -223,10 +225,10 @@ hipError_t launch_index_scores(const uint16_t *q_idx, const uint16_t *kbar, int 
         const dim3 grid(static_cast<uint32_t>((nb_max + 255) / 256), static_cast<uint32_t>(B));
         if (mode == 0)
             hipLaunchKernelGGL(index_scores_decode<0>, grid, dim3(256), 0, s, q_idx, kbar,
-                               seq_len, nb_max, scores, ld, gmax, gld);
+                               seq_len, nb_max, scores, ld, gmax, gld, static_cast<int>(Tq));
         else
             hipLaunchKernelGGL(index_scores_decode<1>, grid, dim3(256), 0, s, q_idx, kbar,
-                               seq_len, nb_max, scores, ld, gmax, gld);
+                               seq_len, nb_max, scores, ld, gmax, gld, static_cast<int>(Tq));
         return hipGetLastError();
     }
     const int64_t n_qt = (Tq + kQT - 1) / kQT;

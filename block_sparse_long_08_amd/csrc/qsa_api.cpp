@@ -15,6 +15,7 @@ namespace {
 
 constexpr int64_t kI32Max = 2147483647;
 constexpr int kMaxBudget = 2048;
+constexpr int kMaxNextN = 16;  // queries per sequence in the decode form
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -71,11 +72,13 @@ int qsa_check_device(void) {
 }
 
 int qsa_rope_bf16(const qsa_bf16 *x, qsa_bf16 *y, int64_t T, int nheads, int head_dim,
-                  int rope_dim, double theta, int64_t pos0, const int64_t *seq_len,
+                  int rope_dim, double theta, int64_t pos0, const int64_t *seq_len, int next_n,
                   void *stream) {
     if (!x || !y) return QSA_ERR_NULL;
     if (T < 0 || nheads <= 0 || head_dim <= 0 || rope_dim <= 0 || !(theta > 0.0) || pos0 < 0)
         return QSA_ERR_SHAPE;
+    if (next_n < 1 || next_n > kMaxNextN) return QSA_ERR_SHAPE;
+    if (seq_len && T % next_n != 0) return QSA_ERR_SHAPE;
     if (rope_dim > head_dim || (rope_dim & 1)) return QSA_ERR_SHAPE;
     if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
         return QSA_ERR_UNSUPPORTED;
@@ -86,7 +89,7 @@ int qsa_rope_bf16(const qsa_bf16 *x, qsa_bf16 *y, int64_t T, int nheads, int hea
     for (int j = 0; j < rope_dim / 2; ++j)
         inv_freq[j] = pow(theta, -2.0 * static_cast<double>(j) / static_cast<double>(rope_dim));
     return launch_status(launch_rope(x, y, T, nheads, head_dim, rope_dim, inv_freq, pos0,
-                                     seq_len, as_stream(stream)));
+                                     seq_len, next_n, as_stream(stream)));
 }
 
 int qsa_compress_keys(const qsa_bf16 *k, int B, int64_t Tk, int64_t k_seq_stride, int Di, int r,
@@ -112,7 +115,7 @@ static int check_index_args(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, 
     if (B <= 0 || Tq < 0 || nb_max < 0 || pos0 < 0 || Hi <= 0 || Di <= 0 || r <= 0)
         return QSA_ERR_SHAPE;
     if (score_mode != QSA_SCORE_MAXHEAD && score_mode != QSA_SCORE_RELUSUM) return QSA_ERR_SHAPE;
-    if (seq_len && Tq != 1) return QSA_ERR_SHAPE;
+    if (seq_len && (Tq < 1 || Tq > kMaxNextN)) return QSA_ERR_SHAPE;
     if (Hi != kIdxHeads || Di != kIdxDim || r != kBlock) return QSA_ERR_UNSUPPORTED;
     if (nb_max > kI32Max || B > 65535) return QSA_ERR_OVERFLOW;
     if ((Tq + 63) / 64 > kI32Max) return QSA_ERR_OVERFLOW;
@@ -134,7 +137,10 @@ int qsa_index_scores(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t
 
 size_t qsa_topk_workspace_bytes(int B, int64_t Tq, int64_t nb_max, int K) {
     if (B <= 0 || Tq <= 0 || nb_max <= 0 || K <= 0) return 0;
-    return topk_plan(static_cast<int64_t>(B) * Tq, nb_max, K).ws_bytes;
+    // prefill form: B * Tq rows; decode form (Tq <= 16): B rows
+    const size_t pre = topk_plan(static_cast<int64_t>(B) * Tq, nb_max, K).ws_bytes;
+    const size_t dec = Tq <= kMaxNextN ? topk_plan(B, nb_max, K).ws_bytes : 0;
+    return pre > dec ? pre : dec;
 }
 
 int qsa_topk_blocks(const float *scores, int B, int64_t Tq, int64_t ld, int64_t pos0,
@@ -142,7 +148,7 @@ int qsa_topk_blocks(const float *scores, int B, int64_t Tq, int64_t ld, int64_t 
                     int32_t *n_sel, void *ws, size_t ws_bytes, void *stream) {
     if (!scores || !blk_idx || !n_sel) return QSA_ERR_NULL;
     if (B <= 0 || Tq < 0 || nb_max < 0 || pos0 < 0 || r <= 0 || K <= 0) return QSA_ERR_SHAPE;
-    if (seq_len && Tq != 1) return QSA_ERR_SHAPE;
+    if (seq_len && (Tq < 1 || Tq > kMaxNextN)) return QSA_ERR_SHAPE;
     if (ld < nb_max || ld % 4 != 0) return QSA_ERR_SHAPE;
     if (K > kMaxBudget) return QSA_ERR_UNSUPPORTED;
     if (nb_max > kI32Max || static_cast<int64_t>(B) * Tq > kI32Max) return QSA_ERR_OVERFLOW;
@@ -157,10 +163,9 @@ int qsa_topk_blocks(const float *scores, int B, int64_t Tq, int64_t ld, int64_t 
 
 // Workspace of qsa_select_blocks: the fp32 scores of one chunk of query rows
 // (all rows in the decode form), then the top-K candidate lists of that chunk.
-static void select_layout(int B, int64_t Tq, int64_t nb_max, int K, int64_t *ld,
+static void select_layout(int B, int64_t Tq, int64_t nb_max, int K, bool decode, int64_t *ld,
                           int64_t *chunk, size_t *score_bytes, size_t *topk_bytes) {
     *ld = round_up(nb_max > 0 ? nb_max : 1, 4);
-    const bool decode = Tq == 1;
     *chunk = decode ? 1 : select_chunk_rows(Tq, *ld);
     const int64_t rows = decode ? B : *chunk;
     *score_bytes = static_cast<size_t>(round_up(rows * *ld * 4, 256));
@@ -175,8 +180,13 @@ size_t qsa_select_workspace_bytes(int B, int64_t Tq, int64_t nb_max, int K) {
     if (B <= 0 || Tq <= 0 || nb_max <= 0 || K <= 0) return 0;
     int64_t ld, chunk;
     size_t sb, tb;
-    select_layout(B, Tq, nb_max, K, &ld, &chunk, &sb, &tb);
-    return sb + tb;
+    select_layout(B, Tq, nb_max, K, false, &ld, &chunk, &sb, &tb);
+    size_t need = sb + tb;
+    if (Tq <= kMaxNextN) {  // the decode form may need more
+        select_layout(B, Tq, nb_max, K, true, &ld, &chunk, &sb, &tb);
+        need = sb + tb > need ? sb + tb : need;
+    }
+    return need;
 }
 
 int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t Tq,
@@ -197,7 +207,7 @@ int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_
     hipStream_t s = as_stream(stream);
     int64_t ld, chunk;
     size_t sb, tb;
-    select_layout(B, Tq, nb_max, K, &ld, &chunk, &sb, &tb);
+    select_layout(B, Tq, nb_max, K, seq_len != nullptr, &ld, &chunk, &sb, &tb);
     float *sc = static_cast<float *>(ws);
     void *tws = need > 0 ? static_cast<char *>(ws) + sb : nullptr;
     if (seq_len && dec_list_layout(B, nb_max, K).use) {
@@ -207,8 +217,8 @@ int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_
         hipError_t e = launch_index_scores(q_idx, kbar, B, Tq, pos0, seq_len, nb_max, score_mode,
                                            sc, ld, s, static_cast<uint32_t *>(tws), l.gld);
         if (e != hipSuccess) return QSA_ERR_LAUNCH;
-        return launch_status(launch_topk_dec_lists(sc, B, ld, seq_len, nb_max, r, K, blk_idx,
-                                                   n_sel, tws, s));
+        return launch_status(launch_topk_dec_lists(sc, B, static_cast<int>(Tq), ld, seq_len,
+                                                   nb_max, r, K, blk_idx, n_sel, tws, s));
     }
     if (seq_len || Tq == 1) {
         hipError_t e = launch_index_scores(q_idx, kbar, B, Tq, pos0, seq_len, nb_max, score_mode,
@@ -253,44 +263,51 @@ int qsa_sparse_attn_prefill(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16
     return launch_status(launch_sparse_prefill(a, as_stream(stream)));
 }
 
-static size_t decode_ws(int B, int Hkv, int64_t max_entries) {
-    const int nsplit = decode_num_splits(B, Hkv, max_entries);
-    return decode_partial_floats(B, Hkv, nsplit) * sizeof(float);
+// Split count and workspace bytes of the decode attention: one record per
+// (sequence, KV head, column tile of 16 query-head pairs, split).
+static size_t decode_ws(int B, int Tq, int H, int Hkv, int64_t sel_entries, int *nsplit) {
+    const int nct = decode_col_tiles(Tq, H / Hkv);
+    const int ns = decode_num_splits(B, Hkv * nct, decode_max_entries(Tq, sel_entries));
+    if (nsplit) *nsplit = ns;
+    return decode_partial_floats(B, Hkv * nct, ns) * sizeof(float);
 }
 
-size_t qsa_decode_workspace_bytes(int B, int H, int Hkv, int D, int Kbudget) {
-    (void)H; (void)D;
-    if (B <= 0 || Hkv <= 0 || Kbudget <= 0) return 0;
-    return decode_ws(B, Hkv, static_cast<int64_t>(Kbudget) + 1);
+size_t qsa_decode_workspace_bytes(int B, int Tq, int H, int Hkv, int D, int Kbudget) {
+    (void)D;
+    if (B <= 0 || Tq < 1 || Tq > kMaxNextN || H <= 0 || Hkv <= 0 || H % Hkv || Kbudget <= 0)
+        return 0;
+    return decode_ws(B, Tq, H, Hkv, Kbudget, nullptr);
 }
 
 int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16 *Vc,
                            const int64_t *seq_len, const int32_t *blk_idx, const int32_t *n_sel,
-                           int B, int64_t Lmax, int H, int Hkv, int D, int r, int Kbudget,
+                           int B, int Tq, int64_t Lmax, int H, int Hkv, int D, int r, int Kbudget,
                            float *O, float *lse, void *ws, size_t ws_bytes, void *stream) {
     if (!q || !Kc || !Vc || !seq_len || !blk_idx || !n_sel || !O) return QSA_ERR_NULL;
     if (B <= 0 || Lmax < 0 || Kbudget <= 0) return QSA_ERR_SHAPE;
+    if (Tq < 1 || Tq > kMaxNextN) return QSA_ERR_SHAPE;
     int st = check_attn_shape(H, Hkv, D, r);
     if (st != QSA_OK) return st;
     if (Kbudget > kMaxBudget) return QSA_ERR_UNSUPPORTED;
     if (B > 65535 || Lmax / kBlock > kI32Max) return QSA_ERR_OVERFLOW;
     if (!aligned16(q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(O)) return QSA_ERR_ALIGN;
-    const size_t need = qsa_decode_workspace_bytes(B, H, Hkv, D, Kbudget);
+    int nsplit = 0;
+    const size_t need = decode_ws(B, Tq, H, Hkv, Kbudget, &nsplit);
     if (!ws || ws_bytes < need) return QSA_ERR_WORKSPACE;
     if (!aligned16(ws)) return QSA_ERR_ALIGN;
     AttnArgs a{};
     a.Q = q; a.K = Kc; a.V = Vc; a.blk_idx = blk_idx; a.n_sel = n_sel; a.seq_len = seq_len;
     a.O = O; a.lse = lse; a.part = static_cast<float *>(ws);
-    a.Tq = 1; a.Lmax = Lmax; a.pos0 = 0; a.B = B; a.H = H; a.Hkv = Hkv; a.Kbudget = Kbudget;
-    const int nsplit = decode_num_splits(B, Hkv, static_cast<int64_t>(Kbudget) + 1);
+    a.Tq = Tq; a.Lmax = Lmax; a.pos0 = 0; a.B = B; a.H = H; a.Hkv = Hkv; a.Kbudget = Kbudget;
     return launch_status(launch_attn_decode(a, nsplit, as_stream(stream)));
 }
 
 size_t dense_attn_workspace_bytes(int B, int64_t Tq, int64_t Lmax, int H, int Hkv, int D) {
-    (void)H; (void)D;
-    if (B <= 0 || Hkv <= 0 || Lmax <= 0) return 0;
-    if (Tq != 1) return 0;  // prefill form needs none
-    return decode_ws(B, Hkv, Lmax / kBlock + 1);
+    (void)D;
+    if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv || Lmax <= 0) return 0;
+    // what the decode form needs (Tq <= 16); the prefill form needs none
+    if (Tq < 1 || Tq > kMaxNextN) return 0;
+    return decode_ws(B, static_cast<int>(Tq), H, Hkv, Lmax / kBlock, nullptr);
 }
 
 int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, int64_t Tq,
@@ -300,7 +317,7 @@ int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, i
     if (B <= 0 || Tq < 0 || Lmax < 0 || pos0 < 0) return QSA_ERR_SHAPE;
     int st = check_attn_shape(H, Hkv, D, kBlock);
     if (st != QSA_OK) return st;
-    if (seq_len && Tq != 1) return QSA_ERR_SHAPE;
+    if (seq_len && (Tq < 1 || Tq > kMaxNextN)) return QSA_ERR_SHAPE;
     if (!seq_len && pos0 + Tq > Lmax) return QSA_ERR_SHAPE;
     if (B > 65535 || Tq > kI32Max || Lmax / kBlock > kI32Max) return QSA_ERR_OVERFLOW;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return QSA_ERR_ALIGN;
@@ -310,10 +327,10 @@ int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, i
     a.Tq = Tq; a.Lmax = Lmax; a.pos0 = pos0; a.B = B; a.H = H; a.Hkv = Hkv; a.Kbudget = 0;
     hipStream_t s = as_stream(stream);
     if (seq_len) {
-        const size_t need = dense_attn_workspace_bytes(B, Tq, Lmax, H, Hkv, D);
+        int nsplit = 0;
+        const size_t need = decode_ws(B, static_cast<int>(Tq), H, Hkv, Lmax / kBlock, &nsplit);
         if (!ws || ws_bytes < need) return QSA_ERR_WORKSPACE;
         if (!aligned16(ws)) return QSA_ERR_ALIGN;
-        const int nsplit = decode_num_splits(B, Hkv, Lmax / kBlock + 1);
         return launch_status(launch_attn_decode(a, nsplit, s));
     }
     return launch_status(launch_dense_prefill(a, s));

@@ -62,9 +62,11 @@ __device__ __forceinline__ float combine_heads(f32x4 acc) {
 }
 
 // ------------------------------------------------------------ launchers --
+// Decode form (seq_len given): T = B * nq rows, row t at position
+// seq_len[t / nq] - nq + t % nq.
 hipError_t launch_rope(const uint16_t *x, uint16_t *y, int64_t T, int nheads, int head_dim,
                        int rope_dim, const double *inv_freq, int64_t pos0,
-                       const int64_t *seq_len, hipStream_t s);
+                       const int64_t *seq_len, int nq, hipStream_t s);
 
 hipError_t launch_compress(const uint16_t *k, int B, int64_t Tk, int64_t k_seq_stride, int Di,
                            int r, int mode, uint16_t *kbar, int64_t kbar_seq_stride,
@@ -94,6 +96,8 @@ struct TopkPlan {
 };
 TopkPlan topk_plan(int64_t rows, int64_t nmax, int K);
 
+// Decode form (seq_len given): B rows, row b made for position
+// seq_len[b] - Tq (the first of the sequence's Tq newest queries).
 hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64_t pos0,
                        const int64_t *seq_len, int64_t nb_max, int r, int K, int32_t *blk_idx,
                        int32_t *n_sel, void *ws, hipStream_t s);
@@ -109,18 +113,20 @@ struct DecListLayout {
     size_t ws_bytes;
 };
 DecListLayout dec_list_layout(int64_t rows, int64_t nb_max, int K);
-hipError_t launch_topk_dec_lists(const float *scores, int B, int64_t ld, const int64_t *seq_len,
-                                 int64_t nb_max, int r, int K, int32_t *blk_idx, int32_t *n_sel,
-                                 void *ws, hipStream_t s);
+hipError_t launch_topk_dec_lists(const float *scores, int B, int nq, int64_t ld,
+                                 const int64_t *seq_len, int64_t nb_max, int r, int K,
+                                 int32_t *blk_idx, int32_t *n_sel, void *ws, hipStream_t s);
 
 // Sparse / dense attention over 4-token blocks (see attention.hip).
 struct AttnArgs {
     const uint16_t *Q;       // [B][Tq][H][D]
     const uint16_t *K;       // [B][Lmax][Hkv][D]
     const uint16_t *V;
-    const int32_t *blk_idx;  // [B][Tq][Kbudget] or nullptr (dense: every complete block)
-    const int32_t *n_sel;    // [B][Tq] or nullptr
-    const int64_t *seq_len;  // decode form: [B]; prefill form: nullptr
+    const int32_t *blk_idx;  // prefill [Tq][Kbudget], decode [B][Kbudget] (one selection
+                             // per sequence), or nullptr (dense: every complete block)
+    const int32_t *n_sel;    // [Tq] / [B] or nullptr
+    const int64_t *seq_len;  // decode form: [B], the Tq queries of sequence b at
+                             // seq_len[b] - Tq .. seq_len[b] - 1; prefill form: nullptr
     float *O;                // [B][Tq][H][D]
     float *lse;              // [B][Tq][H] or nullptr
     float *part;             // split partials (decode), or nullptr
@@ -129,6 +135,10 @@ struct AttnArgs {
 };
 
 hipError_t launch_sparse_prefill(const AttnArgs &a, hipStream_t s);
+// Decode: split-K workgroups per (split, KV head, column tile, sequence); a
+// column tile holds 16 (query, head) pairs of one KV head.
+int decode_col_tiles(int Tq, int group);
+int64_t decode_max_entries(int Tq, int64_t Kbudget_or_blocks);
 size_t decode_partial_floats(int B, int Hkv, int nsplit);
 int decode_num_splits(int B, int Hkv, int64_t max_entries);
 hipError_t launch_attn_decode(const AttnArgs &a, int nsplit, hipStream_t s);

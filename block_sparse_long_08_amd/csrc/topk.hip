@@ -45,7 +45,8 @@ struct TopkArgs {
     int32_t *blk_idx;        // destination 0: [rows][K] ascending, -1 padded
     int32_t *n_sel;          //   [rows]
     int64_t Tq, pos0, nb_max;
-    const int64_t *seq_len;
+    const int64_t *seq_len;  // decode form: row b at position seq_len[b] - nq
+    int nq;
     int r, K;
     int nprev;               // passes before this one (source 1)
     int64_t prev_seg[4];     // their segment lengths
@@ -218,7 +219,7 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
     const int seg = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t sq = row / a.Tq;
-    const int64_t p = a.seq_len ? a.seq_len[sq] - 1 : a.pos0 + (row - sq * a.Tq);
+    const int64_t p = a.seq_len ? a.seq_len[sq] - a.nq : a.pos0 + (row - sq * a.Tq);
     const int64_t n_row = min(num_complete_blocks(p, a.r), a.nb_max);
     const uint32_t K = static_cast<uint32_t>(a.K);
 
@@ -579,7 +580,7 @@ __device__ __forceinline__ void stream_row(const TopkArgs &a, int64_t row,
     TopkSmem<kStNT> &sh = sm.t;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t sq = row / a.Tq;
-    const int64_t p = a.seq_len ? a.seq_len[sq] - 1 : a.pos0 + (row - sq * a.Tq);
+    const int64_t p = a.seq_len ? a.seq_len[sq] - a.nq : a.pos0 + (row - sq * a.Tq);
     const int64_t n_row = min(num_complete_blocks(p, a.r), a.nb_max);
     const uint32_t K = static_cast<uint32_t>(a.K);
     int32_t *out = a.blk_idx + row * a.K;
@@ -864,7 +865,7 @@ struct DecTopkArgs {
 };
 
 __device__ __forceinline__ int64_t dec_row_blocks(const TopkArgs &a, int64_t row) {
-    const int64_t p = a.seq_len[row] - 1;
+    const int64_t p = a.seq_len[row] - a.nq;
     return min(num_complete_blocks(p, a.r), a.nb_max);
 }
 
@@ -1196,7 +1197,8 @@ TopkPlan topk_plan(int64_t rows, int64_t nmax, int K) {
 hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64_t pos0,
                        const int64_t *seq_len, int64_t nb_max, int r, int K, int32_t *blk_idx,
                        int32_t *n_sel, void *ws, hipStream_t s) {
-    const int64_t rows = static_cast<int64_t>(B) * Tq;
+    // decode form: one row per sequence, made for the first of its Tq queries
+    const int64_t rows = seq_len ? static_cast<int64_t>(B) : static_cast<int64_t>(B) * Tq;
     if (rows == 0) return hipSuccess;
     // With many rows no plan needs workspace, so the kernel choice may follow
     // the longest row of this call (prefill form: the last query's) rather
@@ -1209,7 +1211,8 @@ hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64
     a.ld = ld;
     a.blk_idx = blk_idx;
     a.n_sel = n_sel;
-    a.Tq = Tq;
+    a.Tq = seq_len ? 1 : Tq;
+    a.nq = seq_len ? static_cast<int>(Tq) : 1;
     a.pos0 = pos0;
     a.nb_max = nb_max;
     a.seq_len = seq_len;
@@ -1294,9 +1297,9 @@ DecListLayout dec_list_layout(int64_t rows, int64_t nb_max, int K) {
     return l;
 }
 
-hipError_t launch_topk_dec_lists(const float *scores, int B, int64_t ld, const int64_t *seq_len,
-                                 int64_t nb_max, int r, int K, int32_t *blk_idx, int32_t *n_sel,
-                                 void *ws, hipStream_t s) {
+hipError_t launch_topk_dec_lists(const float *scores, int B, int nq, int64_t ld,
+                                 const int64_t *seq_len, int64_t nb_max, int r, int K,
+                                 int32_t *blk_idx, int32_t *n_sel, void *ws, hipStream_t s) {
     if (B == 0) return hipSuccess;
     const DecListLayout l = dec_list_layout(B, nb_max, K);
     DecTopkArgs d{};
@@ -1305,6 +1308,7 @@ hipError_t launch_topk_dec_lists(const float *scores, int B, int64_t ld, const i
     d.t.blk_idx = blk_idx;
     d.t.n_sel = n_sel;
     d.t.Tq = 1;
+    d.t.nq = nq;
     d.t.pos0 = 0;
     d.t.nb_max = nb_max;
     d.t.seq_len = seq_len;

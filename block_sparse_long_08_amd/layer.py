@@ -77,25 +77,29 @@ class QSAPrefill:
 
 
 class QSADecode:
-    """One decode step for B sequences (query at seq_len[b]-1) over caches
-    Kc/Vc [B, Lmax, Hkv, D] (post-RoPE) and kbar [B, Lmax/r, DI]."""
+    """One decode step for B sequences over caches Kc/Vc [B, Lmax, Hkv, D]
+    (post-RoPE) and kbar [B, Lmax/r, DI]: the next_n newest queries of
+    sequence b sit at seq_len[b] - next_n .. seq_len[b] - 1.  With next_n > 1
+    (speculative steps) the block selection is made once, for the first of
+    them, and reused by all (each adds its own causal tail)."""
 
     def __init__(self, B: int, Lmax: int, H: int = 24, Hkv: int = 2, D: int = 256,
                  budget: int = 512, score_mode: int = SCORE_MAXHEAD, kbar_mode: int = KBAR_MEAN,
-                 theta: float = 1e7, rope_dim: int = 64, device="cuda"):
+                 theta: float = 1e7, rope_dim: int = 64, next_n: int = 1, device="cuda"):
         self.B, self.Lmax, self.H, self.Hkv, self.D = B, Lmax, H, Hkv, D
         self.budget, self.score_mode, self.kbar_mode = budget, score_mode, kbar_mode
-        self.theta, self.rope_dim = theta, rope_dim
+        self.theta, self.rope_dim, self.next_n = theta, rope_dim, next_n
         self.nb_max = Lmax // R
         dev = torch.device(device)
-        self.qr = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+        n = next_n
+        self.qr = torch.empty((B, n, H, D), dtype=torch.bfloat16, device=dev)
         self.blk_idx = torch.empty((B, budget), dtype=torch.int32, device=dev)
         self.n_sel = torch.empty((B,), dtype=torch.int32, device=dev)
-        self.O = torch.empty((B, H, D), dtype=torch.float32, device=dev)
-        self.lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-        self.sel_ws_bytes = qsa_select_workspace_bytes(B, 1, self.nb_max, budget)
+        self.O = torch.empty((B, n, H, D), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, n, H), dtype=torch.float32, device=dev)
+        self.sel_ws_bytes = qsa_select_workspace_bytes(B, n, self.nb_max, budget)
         self.sel_ws = torch.empty((max(self.sel_ws_bytes, 16),), dtype=torch.uint8, device=dev)
-        self.dec_ws_bytes = qsa_decode_workspace_bytes(B, H, Hkv, D, budget)
+        self.dec_ws_bytes = qsa_decode_workspace_bytes(B, n, H, Hkv, D, budget)
         self.dec_ws = torch.empty((max(self.dec_ws_bytes, 16),), dtype=torch.uint8, device=dev)
 
     def append_block(self, ki_tail, kbar, block: int):
@@ -104,10 +108,18 @@ class QSADecode:
                           self.nb_max * DI)
 
     def __call__(self, q, qi, Kc, Vc, kbar, seq_len):
-        qsa_rope_bf16(q, self.qr, self.B, self.H, self.D, self.rope_dim, self.theta, 0, seq_len)
-        qsa_select_blocks(qi, kbar, self.B, 1, 0, seq_len, self.nb_max, HI, DI, R, self.score_mode,
-                          self.budget, self.blk_idx, self.n_sel, self.sel_ws, self.sel_ws_bytes)
-        qsa_sparse_attn_decode(self.qr, Kc, Vc, seq_len, self.blk_idx, self.n_sel, self.B,
+        """q [B, next_n, H, D] and qi [B, next_n, HI, DI] (or [B, H, D] and
+        [B, HI, DI] when next_n == 1); returns O [B, next_n, H, D] and lse
+        [B, next_n, H] (O [B, H, D] and lse [B, H] when next_n == 1)."""
+        n = self.next_n
+        qsa_rope_bf16(q, self.qr, self.B * n, self.H, self.D, self.rope_dim, self.theta, 0,
+                      seq_len, n)
+        qsa_select_blocks(qi, kbar, self.B, n, 0, seq_len, self.nb_max, HI, DI, R,
+                          self.score_mode, self.budget, self.blk_idx, self.n_sel, self.sel_ws,
+                          self.sel_ws_bytes)
+        qsa_sparse_attn_decode(self.qr, Kc, Vc, seq_len, self.blk_idx, self.n_sel, self.B, n,
                                self.Lmax, self.H, self.Hkv, self.D, R, self.budget, self.O,
                                self.lse, self.dec_ws, self.dec_ws_bytes)
+        if n == 1:
+            return self.O[:, 0], self.lse[:, 0]
         return self.O, self.lse

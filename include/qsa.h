@@ -22,8 +22,15 @@
  *     Inputs must not be modified before then.
  *   - Positions: in prefill form (`seq_len == NULL`) query t of every
  *     sequence sits at absolute position pos0 + t.  In decode form
- *     (`seq_len` = device int64 [B], Tq == 1) the query of sequence b sits at
- *     seq_len[b] - 1 and its cache holds seq_len[b] tokens.  Device-side
+ *     (`seq_len` = device int64 [B], 1 <= Tq <= 16 queries per sequence) the
+ *     cache of sequence b holds seq_len[b] tokens and its query i sits at
+ *     seq_len[b] - Tq + i.  Tq > 1 is speculative decoding with index reuse
+ *     (chlience "5. 贡献全景与方法总览", item 5: the MTP prediction steps reuse
+ *     the QSA top-k indices; "Result 2": decode with next_n = 4): the block
+ *     selection is made once per sequence, for its first query (position
+ *     p0 = seq_len[b] - Tq, indexer query q_idx[b][0]), and query i attends
+ *     the selected blocks plus every token from r*nc(p0) up to its own
+ *     position.  Tq = 1 is ordinary one-query decode.  Device-side
  *     lengths are not visible to the host: the kernels clamp them to the
  *     allocated sizes (a length above Lmax acts as Lmax, a length < 1 gives an
  *     empty context), so no access leaves the buffers.
@@ -90,11 +97,13 @@ int qsa_check_device(void);
  * rotated counter-clockwise by the angle pos(t) * theta^(-2j/rope_dim)
  * (angles and products in fp64), the result rounded to bf16 (nearest even);
  * dims >= rope_dim are copied.  x, y: [T][nheads][head_dim]; y may equal x.
- * pos(t) = pos0 + t, or seq_len[t] - 1 when seq_len (device int64 [T]) is
- * given (one decode query per sequence).
- * Supported: head_dim in {64,128,256,512}, even rope_dim <= min(head_dim, 128). */
+ * pos(t) = pos0 + t, or, when seq_len (device int64 [T / next_n]) is given,
+ * seq_len[t / next_n] - next_n + t % next_n (decode form: next_n queries per
+ * sequence, rows grouped by sequence); positions below 0 rotate as 0.
+ * Supported: head_dim in {64,128,256,512}, even rope_dim <= min(head_dim, 128),
+ * 1 <= next_n <= 16 (T % next_n == 0 in the decode form; ignored otherwise). */
 int qsa_rope_bf16(const qsa_bf16 *x, qsa_bf16 *y, int64_t T, int nheads, int head_dim,
-                  int rope_dim, double theta, int64_t pos0, const int64_t *seq_len,
+                  int rope_dim, double theta, int64_t pos0, const int64_t *seq_len, int next_n,
                   void *stream);
 
 /* ---- A2: key compression (chlience section 6, k-bar equation).
@@ -108,7 +117,8 @@ int qsa_compress_keys(const qsa_bf16 *k, int B, int64_t Tk, int64_t k_seq_stride
 
 /* ---- A3: indexer block scores (chlience section 6, I_ib; ai.info
  * contribution 3: MQA indexer, 4 query heads and one shared key head).
- * q_idx: [B][Tq][Hi][Di]; kbar: [B][nb_max][Di]; scores: fp32 [B][Tq][ld].
+ * q_idx: [B][Tq][Hi][Di]; kbar: [B][nb_max][Di]; scores: fp32 [B][Tq][ld]
+ * (decode form: [B][ld], one row per sequence, for its first query).
  * scores[b][t][j] for j < nc = min(nc(p), nb_max) holds the block score of
  * query t against pooled block j.  Entries j >= nc may be left untouched or
  * set to -inf (callers read only j < nc).
@@ -124,6 +134,8 @@ int qsa_index_scores(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t
  * by lower block index (scores compare as fp32 values; -0 equals +0).
  * blk_idx: int32 [B][Tq][K], ascending, padded with -1;
  * n_sel: int32 [B][Tq] = min(K, nc).  scores as produced by qsa_index_scores.
+ * Decode form: one selection per sequence (scores [B][ld], blk_idx [B][K],
+ * n_sel [B]), for the sequence's first query.
  * Workspace: qsa_topk_workspace_bytes(B, Tq, nb_max, K) bytes, 16-byte
  * aligned: the per-segment candidate lists of rows longer than 32,768 blocks
  * (or of few long rows, as in decode).  It is 0 when every row fits one pass;
@@ -163,15 +175,22 @@ int qsa_sparse_attn_prefill(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16
                             int64_t pos0, int H, int Hkv, int D, int r, int Kbudget, float *O,
                             float *lse, void *stream);
 
-/* ---- A7: sparse attention, decode (one query per sequence at seq_len-1).
- * q: [B][H][D] post-RoPE; Kc, Vc: [B][Lmax][Hkv][D]; seq_len: device int64 [B];
- * blk_idx: [B][Kbudget]; n_sel: [B]; O: fp32 [B][H][D]; lse: fp32 [B][H] or NULL.
- * Workspace: qsa_decode_workspace_bytes (split partial results). */
-size_t qsa_decode_workspace_bytes(int B, int H, int Hkv, int D, int Kbudget);
+/* ---- A7: sparse attention, decode: the Tq newest queries of each sequence
+ * (Tq = 1, or next_n speculative queries sharing one selection; see the
+ * position conventions).
+ * q: [B][Tq][H][D] post-RoPE; Kc, Vc: [B][Lmax][Hkv][D]; seq_len: device
+ * int64 [B]; blk_idx: [B][Kbudget] and n_sel: [B], the selection made for
+ * position seq_len[b] - Tq (entries must be < nc of that position);
+ * O: fp32 [B][Tq][H][D]; lse: fp32 [B][Tq][H] or NULL.  A query with no
+ * visible token (position < 0) gets O = 0 and lse = -inf.
+ * Workspace: qsa_decode_workspace_bytes (split partial results).
+ * Supported: 1 <= Tq <= 16, and as the prefill call. */
+size_t qsa_decode_workspace_bytes(int B, int Tq, int H, int Hkv, int D, int Kbudget);
 int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16 *Vc,
                            const int64_t *seq_len, const int32_t *blk_idx, const int32_t *n_sel,
-                           int B, int64_t Lmax, int H, int Hkv, int D, int r, int Kbudget,
-                           float *O, float *lse, void *ws, size_t ws_bytes, void *stream);
+                           int B, int Tq, int64_t Lmax, int H, int Hkv, int D, int r,
+                           int Kbudget, float *O, float *lse, void *ws, size_t ws_bytes,
+                           void *stream);
 
 /* ---- A8: dense causal attention (the pages' baseline in the chlience
  * Result 2 kernel measurement).
@@ -180,9 +199,11 @@ int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16
  * 0 .. pos0 + t (pos0 + Tq <= Lmax), a flash-attention pass whose P.V
  * product runs in fp16 (P and V rounded to fp16: V must lie within the fp16
  * range, |v| < 65504; values below 2^-14 lose relative precision), fp32
- * logits, softmax and accumulation.  Decode form: Tq == 1, keys
- * 0 .. seq_len[b] - 1, the split-K kernel of the sparse decode path.
- * Workspace: dense_attn_workspace_bytes (0 for the prefill form). */
+ * logits, softmax and accumulation.  Decode form: the Tq <= 16 newest
+ * queries of each sequence, query i attending keys 0 .. seq_len[b] - Tq + i,
+ * with the split-K kernel of the sparse decode path.
+ * Workspace: dense_attn_workspace_bytes: the decode form's need for Tq
+ * queries per sequence (the prefill form needs none; ws may be NULL). */
 size_t dense_attn_workspace_bytes(int B, int64_t Tq, int64_t Lmax, int H, int Hkv, int D);
 int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, int64_t Tq,
                int64_t Lmax, int64_t pos0, const int64_t *seq_len, int H, int Hkv, int D,

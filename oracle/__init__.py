@@ -58,6 +58,8 @@ def _load():
         lib.qsa_oracle_topk_row.restype = i32
         lib.qsa_oracle_token_set.argtypes = [vp, i32, i64, i32, vp]
         lib.qsa_oracle_token_set.restype = i64
+        lib.qsa_oracle_token_set_reuse.argtypes = [vp, i32, i64, i64, i32, vp]
+        lib.qsa_oracle_token_set_reuse.restype = i64
         lib.qsa_oracle_attend_row.argtypes = [vp, vp, vp, i32, i32, i32, vp, i64, vp, vp, vp]
         lib.qsa_oracle_attend_row.restype = None
         lib.qsa_oracle_qsa_rows.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32,
@@ -164,6 +166,17 @@ def token_set(blk: np.ndarray, p: int, r: int = 4) -> np.ndarray:
     return tok[:n].copy()
 
 
+def token_set_reuse(blk: np.ndarray, p_sel: int, p: int, r: int = 4) -> np.ndarray:
+    """Tokens of a query at position p >= p_sel that reuses the selection blk
+    made for position p_sel (speculative steps with index reuse): the blocks
+    expanded, then every token from r * nc(p_sel) through p."""
+    blk = _c(blk, np.int32)
+    tail = max(0, p - num_complete(p_sel, r) * r + 1)
+    tok = np.empty(blk.size * r + tail + 1, dtype=np.int64)
+    n = _load().qsa_oracle_token_set_reuse(_p(blk), blk.size, p_sel, p, r, _p(tok))
+    return tok[:n].copy()
+
+
 def attend_row(q_row: np.ndarray, K: np.ndarray, V: np.ndarray, tokens: np.ndarray):
     """q_row [H, D], K/V [Tk, Hkv, D] bf16 bits -> (O [H, D], lse [H], wsum_err)."""
     q_row = _c(q_row, np.uint16)
@@ -264,6 +277,32 @@ def select_rows(qi, kbar, rows, pos0: int = 0, Kbudget: int = 512, r: int = 4,
     if want_scores:
         out["s"] = s
     return out
+
+
+def decode_reuse_rows(Q_rows, K, V, qi_first, kbar, seq_len: int, Kbudget: int = 512,
+                      r: int = 4, mode: int = MODE_MAXHEAD):
+    """Decode of the n = Q_rows.shape[0] newest queries of one sequence of
+    seq_len tokens (query i at seq_len - n + i; Q_rows post-RoPE) that share
+    the selection made for the first of them from its indexer query qi_first
+    [Hi, Di] (speculative steps with index reuse).  A query at a position
+    below 0 sees no token: O = 0, lse = -inf.
+    Returns dict(O [n,H,D], lse [n,H], sel, nsel, s, sK, sK1, wsum_err [n])."""
+    Q_rows = _c(Q_rows, np.uint16)
+    n, H, D = Q_rows.shape
+    p0 = seq_len - n
+    sr = select_rows(qi_first[None], kbar, np.array([0]), pos0=p0, Kbudget=Kbudget, r=r,
+                     mode=mode, want_scores=True)
+    blk = sr["sel"][0, :sr["nsel"][0]]
+    O = np.zeros((n, H, D))
+    lse = np.full((n, H), -np.inf)
+    err = np.zeros(n)
+    for i in range(n):
+        p = p0 + i
+        if p < 0:
+            continue
+        O[i], lse[i], err[i] = attend_row(Q_rows[i], K, V, token_set_reuse(blk, p0, p, r))
+    return dict(O=O, lse=lse, sel=sr["sel"][0], nsel=int(sr["nsel"][0]), s=sr["s"][0],
+                sK=float(sr["sK"][0]), sK1=float(sr["sK1"][0]), wsum_err=err)
 
 
 def dense_rows(Q, K, V, rows, pos0: int = 0):

@@ -218,6 +218,24 @@ int64_t qsa_oracle_token_set(const int32_t *blk, int nsel, int64_t p, int r, int
     return n;
 }
 
+/* ---------- O5, index reuse: a later speculative query ------------------ */
+/* chlience "5. 贡献全景与方法总览" item 5 (the MTP prediction steps reuse the
+ * QSA top-k indices) and "Result 2" (decode with next_n = 4).  A query at
+ * position p >= p_sel reuses the selection made for position p_sel: its
+ * tokens are the selected blocks expanded, then every token from
+ * r * nc(p_sel) through p (the incomplete block of p_sel and whatever
+ * followed it).  For p = p_sel this is the token set above.  Returns the
+ * number of tokens written to tok. */
+int64_t qsa_oracle_token_set_reuse(const int32_t *blk, int nsel, int64_t p_sel, int64_t p, int r,
+                                   int64_t *tok) {
+    int64_t n = 0;
+    for (int i = 0; i < nsel; ++i)
+        for (int t = 0; t < r; ++t) tok[n++] = (int64_t)blk[i] * r + t;
+    int64_t from = qsa_oracle_num_complete(p_sel, r) * r;
+    for (int64_t j = from; j <= p; ++j) tok[n++] = j;
+    return n;
+}
+
 /* ---------- O6: softmax attention of one query over a token set --------- */
 /* q_row [H][D] (post-RoPE), K/V [*][Hkv][D]; for head h, KV head
  * g = h / (H/Hkv): logits l_j = q_h.k_{g,j} / sqrt(D); O_h = sum_j w_j v_{g,j}

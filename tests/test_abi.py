@@ -71,9 +71,9 @@ def vp(x):
     return ctypes.c_void_p(x)
 
 
-def rope(lib, x=P, y=P, T=4, nh=24, hd=256, rd=64, theta=1e7, pos0=0):
+def rope(lib, x=P, y=P, T=4, nh=24, hd=256, rd=64, theta=1e7, pos0=0, lens=None, next_n=1):
     return lib.qsa_rope_bf16(vp(x), vp(y), I64(T), nh, hd, rd, ctypes.c_double(theta), I64(pos0),
-                             None, None)
+                             lens, next_n, None)
 
 
 def test_rope_validation(lib):
@@ -84,6 +84,9 @@ def test_rope_validation(lib):
     assert rope(lib, hd=96) == UNSUP
     assert rope(lib, theta=-1.0) == SHAPE
     assert rope(lib, x=MIS) == ALIGN
+    assert rope(lib, next_n=0) == SHAPE
+    assert rope(lib, next_n=17) == SHAPE
+    assert rope(lib, T=6, lens=vp(P), next_n=4) == SHAPE   # rows not whole sequences
 
 
 def compress(lib, k=P, B=1, Tk=16, ks=16 * 128, Di=128, r=4, mode=0, kb=P, kbs=4 * 128):
@@ -114,7 +117,8 @@ def test_index_scores_validation(lib):
     assert scores(lib, ld=2) == SHAPE
     assert scores(lib, Hi=8) == UNSUP
     assert scores(lib, r=8) == UNSUP
-    assert scores(lib, sl=vp(P), Tq=2) == SHAPE
+    assert scores(lib, sl=vp(P), Tq=17) == SHAPE          # decode form: at most 16 queries
+    assert scores(lib, sl=vp(P), Tq=0) == SHAPE
     assert scores(lib, nb=1 << 33, ld=1 << 33) == OVERFLOW
     assert scores(lib, kb=MIS) == ALIGN
 
@@ -182,24 +186,34 @@ def test_sparse_prefill_validation(lib):
 
 def test_decode_validation(lib):
     lib.qsa_decode_workspace_bytes.restype = ctypes.c_size_t
-    need = lib.qsa_decode_workspace_bytes(32, 24, 2, 256, 512)
+    need = lib.qsa_decode_workspace_bytes(32, 1, 24, 2, 256, 512)
     assert need > 0
+    # speculative queries: three column tiles of 16 (query, head) pairs per KV head
+    assert lib.qsa_decode_workspace_bytes(4, 4, 24, 2, 256, 512) > 0
+    assert lib.qsa_decode_workspace_bytes(4, 17, 24, 2, 256, 512) == 0
     args = [vp(P)] * 6
-    st = lib.qsa_sparse_attn_decode(*args, 32, I64(1024), 24, 2, 256, 4, 512, vp(P), None, vp(P),
-                                    ctypes.c_size_t(need - 1), None)
+    st = lib.qsa_sparse_attn_decode(*args, 32, 1, I64(1024), 24, 2, 256, 4, 512, vp(P), None,
+                                    vp(P), ctypes.c_size_t(need - 1), None)
     assert st == WORKSPACE
-    st = lib.qsa_sparse_attn_decode(vp(P), vp(P), vp(P), None, vp(P), vp(P), 32, I64(1024), 24, 2,
-                                    256, 4, 512, vp(P), None, vp(P), ctypes.c_size_t(need), None)
+    st = lib.qsa_sparse_attn_decode(vp(P), vp(P), vp(P), None, vp(P), vp(P), 32, 1, I64(1024), 24,
+                                    2, 256, 4, 512, vp(P), None, vp(P), ctypes.c_size_t(need), None)
     assert st == NULL
+    for tq in (0, 17):
+        st = lib.qsa_sparse_attn_decode(*args, 32, tq, I64(1024), 24, 2, 256, 4, 512, vp(P), None,
+                                        vp(P), ctypes.c_size_t(1 << 30), None)
+        assert st == SHAPE
 
 
 def test_dense_validation(lib):
     st = lib.dense_attn(vp(P), vp(P), vp(P), 1, I64(16), I64(15), I64(0), None, 24, 2, 256,
                         vp(P), None, None, ctypes.c_size_t(0), None)
     assert st == SHAPE                                   # pos0 + Tq > Lmax
-    st = lib.dense_attn(vp(P), vp(P), vp(P), 1, I64(2), I64(16), I64(0), vp(P), 24, 2, 256,
+    st = lib.dense_attn(vp(P), vp(P), vp(P), 1, I64(17), I64(16), I64(0), vp(P), 24, 2, 256,
                         vp(P), None, None, ctypes.c_size_t(0), None)
-    assert st == SHAPE                                   # decode form has one query
+    assert st == SHAPE                                   # decode form: at most 16 queries
+    st = lib.dense_attn(vp(P), vp(P), vp(P), 1, I64(4), I64(16), I64(0), vp(P), 24, 2, 256,
+                        vp(P), None, None, ctypes.c_size_t(0), None)
+    assert st == WORKSPACE                               # 4 speculative queries need records
     lib.dense_attn_workspace_bytes.restype = ctypes.c_size_t
     need = lib.dense_attn_workspace_bytes(4, I64(1), I64(1 << 20), 24, 2, 256)
     st = lib.dense_attn(vp(P), vp(P), vp(P), 4, I64(1), I64(1 << 20), I64(0), vp(P), 24, 2, 256,

@@ -427,12 +427,12 @@ def test_decode_attention_parity(qsa):
         m = min(K, nc)
         sel[b, :m] = np.sort(rng.choice(nc, size=m, replace=False)) if m else []
         nsel[b] = m
-    wsb = qsa.qsa_decode_workspace_bytes(B, 24, 2, 256, K)
+    wsb = qsa.qsa_decode_workspace_bytes(B, 1, 24, 2, 256, K)
     ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
     O = torch.empty((B, 24, 256), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, 24), dtype=torch.float32, device="cuda")
-    qsa.qsa_sparse_attn_decode(dev(q), dev(Kc), dev(Vc), dev(lens), dev(sel), dev(nsel), B, Lmax,
-                               24, 2, 256, 4, K, O, lse, ws, wsb)
+    qsa.qsa_sparse_attn_decode(dev(q), dev(Kc), dev(Vc), dev(lens), dev(sel), dev(nsel), B, 1,
+                               Lmax, 24, 2, 256, 4, K, O, lse, ws, wsb)
     torch.cuda.synchronize()
     Og, lg = O.cpu().numpy(), lse.cpu().numpy()
     for b in range(B):

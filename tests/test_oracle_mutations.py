@@ -33,6 +33,10 @@ MUTATIONS = {
     "softmax_scale": ("double scale = 1.0 / sqrt((double)D);", "double scale = 1.0 / (double)D;"),
     "value_operand_swapped": ("const uint16_t *vr = V + ", "const uint16_t *vr = K + "),
     "lse_drops_max": ("lse[h] = m + log(sw);", "lse[h] = log(sw);"),
+    "reuse_tail_from_own_block": ("int64_t from = qsa_oracle_num_complete(p_sel, r) * r;",
+                                  "int64_t from = qsa_oracle_num_complete(p, r) * r;"),
+    "reuse_tail_stops_short": ("for (int64_t j = from; j <= p; ++j) tok[n++] = j;",
+                               "for (int64_t j = from; j < p; ++j) tok[n++] = j;"),
 }
 
 

@@ -281,6 +281,21 @@ def test_token_set(oracle_lib, p):
     assert list(tok) == want
 
 
+# Index reuse by later speculative queries: the selection made for p_sel
+# expanded, then every token from r*nc(p_sel) through the query's position.
+@pytest.mark.parametrize("p_sel", [0, 1, 2, 3, 4, 6, 30, 33, 34])
+def test_token_set_reuse(oracle_lib, p_sel):
+    nc = (p_sel + 1) // 4
+    blk = np.arange(0, nc, 3, dtype=np.int32)
+    assert np.array_equal(oracle_lib.token_set_reuse(blk, p_sel, p_sel),
+                          oracle_lib.token_set(blk, p_sel))
+    for p in range(p_sel, p_sel + 7):
+        tok = oracle_lib.token_set_reuse(blk, p_sel, p)
+        want = {4 * b + t for b in blk for t in range(4)} | set(range(4 * nc, p + 1))
+        assert tok.size == len(want) and set(tok.tolist()) == want
+        assert tok.size == 4 * blk.size + p - 4 * nc + 1 and tok.max() <= p
+
+
 # ----------------------------------------------------------------------------
 # Attention: closed forms.
 # ----------------------------------------------------------------------------
@@ -376,6 +391,69 @@ def test_qsa_equals_dense_within_budget(oracle_lib, synth_lib, mode):
     assert np.abs(res2["O"] - Od2).max() > 1e-3
     assert np.all(res2["nsel"] == Kb)
     assert np.all(res["wsum_err"] < 1e-12)
+
+
+@pytest.mark.parametrize("seq_len", [2, 5, 31, 34, 35, 36])
+def test_decode_reuse_equals_dense_within_budget(oracle_lib, synth_lib, seq_len):
+    """Four speculative queries sharing one selection: while the selecting
+    query sees at most K complete blocks, every query is dense causal
+    attention at its own position (queries before position 0 see nothing)."""
+    T, n = 40, 4
+    Q, K, V, qi, ki = _small_inputs(synth_lib, T)
+    kb = oracle_lib.compress(ki[:seq_len])
+    p0 = seq_len - n
+    res = oracle_lib.decode_reuse_rows(_window(Q, p0, n), K, V, qi[max(p0, 0)], kb, seq_len,
+                                       Kbudget=10)
+    for i in range(n):
+        p = p0 + i
+        if p < 0:
+            assert np.all(res["O"][i] == 0) and np.all(np.isneginf(res["lse"][i]))
+            continue
+        Od, lsed = oracle_lib.dense_rows(Q, K, V, np.array([p]))
+        assert np.allclose(res["O"][i], Od[0], atol=1e-12)
+        assert np.allclose(res["lse"][i], lsed[0], atol=1e-12)
+    assert np.all(res["wsum_err"] < 1e-12)
+
+
+def _window(Q, p0, n):
+    """Rows p0 .. p0+n-1 of Q; rows before position 0 are zero."""
+    out = np.zeros((n,) + Q.shape[1:], dtype=Q.dtype)
+    for i in range(n):
+        if p0 + i >= 0:
+            out[i] = Q[p0 + i]
+    return out
+
+
+def test_decode_reuse_token_sets_from_outputs(oracle_lib):
+    """Planted indexer scores and uniform attention (Q = 0) with one-hot V:
+    every speculative query attends the first query's K best blocks plus all
+    tokens from that query's incomplete block through its own position, also
+    when a block completes inside the window."""
+    T, Kb, n = 64, 3, 4
+    c = np.array([0.5, 3.0, -1.0, 2.0, 0.25, 4.0, 1.0, -2.0, 3.5, 0.125, 1.5, 2.5,
+                  -0.5, 0.75, 6.0, 1.25], dtype=np.float32)
+    kb = np.zeros((T // 4, 128), dtype=np.float32)
+    kb[:, 0] = c
+    qi = np.zeros((4, 128), dtype=np.float32)
+    qi[1, 0] = 1.0
+    Q = np.zeros((n, 24, 256), dtype=np.uint16)
+    Kc = np.zeros((T, 2, 256), dtype=np.uint16)
+    V = np.zeros((T, 2, 256), dtype=np.float32)
+    for j in range(T):
+        V[j, :, j] = 1.0
+    for seq_len in (31, 33, 34, 35, 36, 50, 64):
+        p0 = seq_len - n
+        nc0 = (p0 + 1) // 4
+        res = oracle_lib.decode_reuse_rows(Q, Kc, bf(V), bf(qi), bf(kb[:seq_len // 4]), seq_len,
+                                           Kbudget=Kb)
+        sel = sorted(sorted(range(nc0), key=lambda b: (-c[b], b))[:Kb])
+        assert list(res["sel"][:res["nsel"]]) == sel
+        for i in range(n):
+            p = p0 + i
+            S = sorted([4 * b + t for b in sel for t in range(4)] + list(range(4 * nc0, p + 1)))
+            O = res["O"][i, 5, :T]
+            assert np.allclose(O[S], 1.0 / len(S), atol=1e-14), (seq_len, i)
+            assert np.allclose(np.delete(O, S), 0.0, atol=1e-14), (seq_len, i)
 
 
 def test_qsa_selection_and_token_set_from_outputs(oracle_lib):
