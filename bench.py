@@ -50,6 +50,9 @@ DECODES = {
     "decode_256k_b32": (32, 262144, 512, 0),
     "decode_1m_b4": (4, 1048576, 512, 64),
 }
+# speculative decode with index reuse timed on the same caches (the pages'
+# decode condition: batch 4, next_n = 4)
+DECODE_NEXT_N = {"decode_1m_b4": 4}
 
 
 def log(msg):
@@ -174,6 +177,36 @@ def bench_prefill(name, steps, warmup, with_dense=True):
     return res, x
 
 
+def _time_steps(run, steps):
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def _decode_rates(B, L, budget, n, ms, dense_ms=None):
+    """Throughput and HBM fraction of a decode step of n queries per sequence:
+    the pooled keys, the gathered blocks (one selection per sequence) and the
+    tail tokens, q read and O written."""
+    nb = L // 4
+    tail = L - 4 * ((L - n + 1) // 4)  # tokens after the first query's complete blocks
+    bytes_step = B * (nb * 128 * 2 + (4 * budget + tail) * 2 * 256 * 2 * 2 + n * 24 * 256 * (2 + 4))
+    res = dict(ms_per_step=ms, B=B, L=L, next_n=n, tokens_per_s=B * n / (ms * 1e-3),
+               bytes_per_step=bytes_step, hbm_frac=bytes_step / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9))
+    # dense decode reads the whole cache once at best: its time at the HBM peak
+    dbytes = B * L * 2 * 256 * 2 * 2
+    dense_roof_ms = dbytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    res.update(dense_at_hbm_peak_ms=dense_roof_ms, speedup_vs_dense_at_hbm_peak=dense_roof_ms / ms)
+    if dense_ms is not None:
+        res.update(dense_ms=dense_ms, dense_hbm_frac=dbytes / (dense_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                   speedup_vs_dense=dense_ms / ms)
+    return res
+
+
 def bench_decode(name, steps, warmup, with_dense=True):
     import torch
     import block_sparse_long_08_amd as qsa
@@ -197,38 +230,35 @@ def bench_decode(name, steps, warmup, with_dense=True):
     torch.cuda.synchronize()
     log(f"generated {name} caches in {time.time() - t:.1f}s")
     seq_len = torch.full((B,), L, dtype=torch.int64, device="cuda")
-    dec = qsa.QSADecode(B, L, budget=budget)
-    for _ in range(warmup):
-        dec(q, qi, Kc, Vc, kbar, seq_len)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        dec(q, qi, Kc, Vc, kbar, seq_len)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    nb = L // 4
-    bytes_step = B * (nb * 128 * 2 + (4 * budget) * 2 * 256 * 2 * 2 + 24 * 256 * (2 + 4))
-    res = dict(ms_per_step=ms, B=B, L=L, tokens_per_s=B / (ms * 1e-3), bytes_per_step=bytes_step,
-               hbm_frac=bytes_step / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9))
-    if with_dense:
-        Od = torch.empty((B, 24, 256), dtype=torch.float32, device="cuda")
-        wsb = qsa.dense_attn_workspace_bytes(B, 1, L, 24, 2, 256)
-        ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
-        run = lambda: qsa.dense_attn(dec.qr, Kc, Vc, B, 1, L, 0, seq_len, 24, 2, 256, Od, None, ws, wsb)  # noqa
-        run()
+
+    def one(n, qq, qqi):
+        dec = qsa.QSADecode(B, L, budget=budget, next_n=n)
+        for _ in range(warmup):
+            dec(qq, qqi, Kc, Vc, kbar, seq_len)
         torch.cuda.synchronize()
-        e0.record()
-        for _ in range(steps):
+        ms = _time_steps(lambda: dec(qq, qqi, Kc, Vc, kbar, seq_len), steps)
+        dms = None
+        if with_dense:
+            Od = torch.empty((B, n, 24, 256), dtype=torch.float32, device="cuda")
+            wsb = qsa.dense_attn_workspace_bytes(B, n, L, 24, 2, 256)
+            ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+            run = lambda: qsa.dense_attn(dec.qr, Kc, Vc, B, n, L, 0, seq_len, 24, 2, 256, Od,  # noqa
+                                         None, ws, wsb)
             run()
-        e1.record()
-        torch.cuda.synchronize()
-        dms = e0.elapsed_time(e1) / steps
-        dbytes = B * L * 2 * 256 * 2 * 2
-        res.update(dense_ms=dms, dense_hbm_frac=dbytes / (dms * 1e-3) / (HBM_PEAK_GBS * 1e9),
-                   speedup_vs_dense=dms / ms)
-    del Kc, Vc, kbar, dec
+            torch.cuda.synchronize()
+            dms = _time_steps(run, steps)
+            del Od, ws
+        del dec
+        return _decode_rates(B, L, budget, n, ms, dms)
+
+    res = one(1, q, qi)
+    n = DECODE_NEXT_N.get(name)
+    if n:
+        # the n newest queries of every sequence (seeded N(0,1) rows)
+        qn = to_dev(synth.normal_bf16(1, (B, n, 24, 256), seed=7))
+        qin = to_dev(synth.normal_bf16(4, (B, n, 4, 128), seed=7))
+        res[f"next_n_{n}"] = one(n, qn, qin)
+    del Kc, Vc, kbar
     torch.cuda.empty_cache()
     return res
 
@@ -404,6 +434,8 @@ def main():
                              with_dense=args.dense != "none")
         out["decode_1m_b4"] = dict(workload="decode_1m_b4", **m_dec)
         log(f"decode decode_1m_b4: {m_dec['ms_per_step']:.3f} ms/step")
+        if "next_n_4" in m_dec:
+            log(f"decode decode_1m_b4 next_n=4: {m_dec['next_n_4']['ms_per_step']:.3f} ms/step")
         x = None
     if not args.no_cpu:
         if x is None:

@@ -50,6 +50,10 @@ __device__ __forceinline__ void lds_fence() {
 // 4*nc .. 4*nc + tail - 1 after the selection's visible blocks (the query's
 // incomplete block, and for later speculative queries sharing the selection
 // also the tokens up to their own positions).
+// MULTI: several queries share the list (the tail may span entries and each
+// column masks it at its own position); otherwise the tail is one entry of
+// (p+1) mod 4 tokens, all visible.
+template <bool MULTI>
 struct EntryList {
     const int32_t *lst;  // LDS copy of the selected blocks (sparse), or nullptr (dense)
     int lst_off;         // index of lst[0] in the query's list
@@ -57,17 +61,18 @@ struct EntryList {
     int tail;            // tail tokens after block nc - 1
     int64_t nc;          // complete blocks visible to the selecting query
     __device__ __forceinline__ int count(int e) const {
+        if (!MULTI) return e < ns ? 4 : (e == ns ? tail : 0);
         return e < ns ? 4 : max(0, min(4, tail - 4 * (e - ns)));
     }
     __device__ __forceinline__ int64_t base(int e) const {
         if (e < ns) return 4 * static_cast<int64_t>(lst ? lst[e - lst_off] : e);
-        return 4 * (nc + e - ns);
+        return MULTI ? 4 * (nc + e - ns) : 4 * nc;
     }
     // tokens of entry e visible to a query at position pq (selected blocks
     // precede every query sharing the selection)
     __device__ __forceinline__ int visible(int e, int64_t pq) const {
         const int c = count(e);
-        if (e < ns) return c;
+        if (!MULTI || e < ns) return c;
         const int64_t v = pq - 4 * (nc + e - ns) + 1;
         return v < 0 ? 0 : (v < c ? static_cast<int>(v) : c);
     }
@@ -91,7 +96,9 @@ __device__ __forceinline__ int row_swizzle(int tt) { return 2 * ((tt >> 2) & 3);
 // Entries e0 .. e0+3 of one KV head.  Kg/Vg point at token 0 of the head (row
 // stride rs elements); p is a safe row for masked tokens; pq is the position
 // of the query in this lane's column; vlds is the wave's 8 KB LDS tile.
-__device__ __forceinline__ void attn_stage(const EntryList &L, int e0, int64_t p, int64_t pq,
+template <bool MULTI>
+__device__ __forceinline__ void attn_stage(const EntryList<MULTI> &L, int e0, int64_t p,
+                                           int64_t pq,
                                            const uint16_t *__restrict__ Kg,
                                            const uint16_t *__restrict__ Vg, int64_t rs,
                                            const bf16x8 (&qT)[8], WaveState &st,
@@ -260,7 +267,7 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a) {
         lst[i] = bi;
     }
     __syncthreads();
-    EntryList L{lst, 0, ns, static_cast<int>((p + 1) % kBlock), nc};
+    EntryList<false> L{lst, 0, ns, static_cast<int>((p + 1) % kBlock), nc};
     const int E = ns + (L.tail > 0 ? 1 : 0);
     const int nstages = (E + kStageEntries - 1) / kStageEntries;
 
@@ -303,7 +310,7 @@ __device__ __forceinline__ void record_store(const WaveState &st, float *rec, in
 // workspace.  The Tq newest queries of a sequence share its selection (made
 // for the first of them, at seq_len - Tq); the columns of a tile are 16
 // (query, head) pairs and each column masks the tail past its own query.
-template <bool DENSE>
+template <bool DENSE, bool MULTI>
 __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit, int sps,
                                                           int nct) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[3 * kRecFloats * 4];
@@ -344,7 +351,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit
             lst[i - e_lo] = bi;
         }
     }
-    EntryList L{DENSE ? nullptr : lst, e_lo, ns, tail, nc};
+    EntryList<MULTI> L{DENSE ? nullptr : lst, e_lo, ns, tail, nc};
     __syncthreads();
 
     // position of this lane's column query (-1: no query, every token masked)
@@ -453,10 +460,21 @@ hipError_t launch_attn_decode(const AttnArgs &a, int nsplit, hipStream_t s) {
     const int sps = static_cast<int>((nstages + nsplit - 1) / nsplit);
     const dim3 grid(static_cast<uint32_t>(nsplit), static_cast<uint32_t>(a.Hkv * nct),
                     static_cast<uint32_t>(a.B));
-    if (a.blk_idx)
-        hipLaunchKernelGGL(attn_decode_kernel<false>, grid, dim3(256), 0, s, a, nsplit, sps, nct);
-    else
-        hipLaunchKernelGGL(attn_decode_kernel<true>, grid, dim3(256), 0, s, a, nsplit, sps, nct);
+    if (a.blk_idx) {
+        if (nq > 1)
+            hipLaunchKernelGGL((attn_decode_kernel<false, true>), grid, dim3(256), 0, s, a, nsplit,
+                               sps, nct);
+        else
+            hipLaunchKernelGGL((attn_decode_kernel<false, false>), grid, dim3(256), 0, s, a,
+                               nsplit, sps, nct);
+    } else {
+        if (nq > 1)
+            hipLaunchKernelGGL((attn_decode_kernel<true, true>), grid, dim3(256), 0, s, a, nsplit,
+                               sps, nct);
+        else
+            hipLaunchKernelGGL((attn_decode_kernel<true, false>), grid, dim3(256), 0, s, a, nsplit,
+                               sps, nct);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t threads = 4 * static_cast<int64_t>(a.B) * nq * a.H * kHeadDim;
