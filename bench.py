@@ -103,11 +103,11 @@ class StageTimer:
         return {n: float(np.mean(v)) for n, v in out.items()}
 
 
-def bench_prefill(name, steps, warmup, with_dense=True):
+def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None):
     import torch
     import block_sparse_long_08_amd as qsa
     Tq, pos0, budget, nd = WORKLOADS[name]
-    x = gen_prefill(name)
+    x = gen_prefill(name) if x is None else x
     fresh = pos0 == 0
     Q, K, V, qi, ki = map(to_dev, (x.Q, x.K, x.V, x.qi, x.ki))
     Tk = pos0 + Tq
@@ -115,8 +115,9 @@ def bench_prefill(name, steps, warmup, with_dense=True):
     if not fresh:
         # cache of pooled keys for the context before the chunk (setup, untimed)
         kbar = torch.empty((Tk // 4, 128), dtype=torch.bfloat16, device="cuda")
-        qsa.qsa_compress_keys(ki, 1, pos0, pos0 * 128, 128, 4, 0, kbar, (pos0 // 4) * 128)
-    layer = qsa.QSAPrefill(Tq, pos0=pos0, budget=budget, fresh=fresh)
+        qsa.qsa_compress_keys(ki, 1, pos0, pos0 * 128, 128, 4, 0, kbar, (pos0 // 4) * 128,
+                              rope_dim=idx_rope_dim)
+    layer = qsa.QSAPrefill(Tq, pos0=pos0, budget=budget, fresh=fresh, idx_rope_dim=idx_rope_dim)
     torch.cuda.synchronize()
     names = ["rope_pool", "select", "attend"]
     timer = StageTimer(names)
@@ -125,9 +126,10 @@ def bench_prefill(name, steps, warmup, with_dense=True):
         if t:
             t.start_step()
         Kr, kb = layer.rope_and_pool(Q, K, ki, kbar)
+        qs = layer.rope_indexer(qi)
         if t:
             t.mark()
-        layer.select(qi, kb)
+        layer.select(qs, kb)
         if t:
             t.mark()
         layer.attend(Kr, V)
@@ -353,6 +355,8 @@ def main():
     ap.add_argument("--million", default="on", choices=["on", "off"],
                     help="also time the 1M-context workloads (8,192-query prefill chunk, "
                          "decode of 4 sequences) with their dense baselines")
+    ap.add_argument("--indexer-rope", default="on", choices=["on", "off"],
+                    help="also time the 32K prefill with partial RoPE on the indexer")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (scale of the HBM byte counters)")
     args = ap.parse_args()
@@ -408,6 +412,21 @@ def main():
     dense_roof_ms = pre["dense_flop"] / (BF16_PEAK_TFLOPS * 1e12) * 1e3
     out["dense_prefill_at_mfma_peak_ms"] = dense_roof_ms
     out["prefill_speedup_vs_dense_at_mfma_peak"] = dense_roof_ms / pre["ms_per_step"]
+    if args.indexer_rope == "on":
+        # the indexer with partial RoPE (64 of its 128 dims) on the 32K workload,
+        # against the same workload without it
+        x32 = gen_prefill("prefill_32k")
+        plain, _ = bench_prefill("prefill_32k", args.steps, args.warmup, with_dense=False, x=x32)
+        rot, _ = bench_prefill("prefill_32k", args.steps, args.warmup, with_dense=False,
+                               idx_rope_dim=64, x=x32)
+        out["indexer_rope"] = dict(workload="prefill_32k", idx_rope_dim=64,
+                                   ms_per_step=rot["ms_per_step"], stages_ms=rot["stages_ms"],
+                                   tokens_per_s=rot["Tq"] / (rot["ms_per_step"] * 1e-3),
+                                   without_rope_ms_per_step=plain["ms_per_step"],
+                                   without_rope_stages_ms=plain["stages_ms"])
+        log(f"prefill_32k with indexer RoPE: {rot['ms_per_step']:.2f} ms/step "
+            f"(without: {plain['ms_per_step']:.2f})")
+        del x32
     if args.decode != "none":
         dec = bench_decode(args.decode, max(args.steps, 10), args.warmup,
                            with_dense=args.dense != "none")

@@ -41,7 +41,8 @@ _lib_status_string = _sig("qsa_status_string", ctypes.c_char_p, _i32)
 _sig("qsa_version", _i32)
 _sig("qsa_check_device", _i32)
 _sig("qsa_rope_bf16", _i32, _vp, _vp, _i64, _i32, _i32, _i32, _dbl, _i64, _vp, _i32, _vp)
-_sig("qsa_compress_keys", _i32, _vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _i64, _vp)
+_sig("qsa_compress_keys", _i32, _vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _i32, _dbl, _i64,
+     _vp, _i64, _vp)
 _sig("qsa_index_scores", _i32, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _i32, _i32, _i32, _i32,
      _vp, _i64, _vp)
 _sig("qsa_topk_workspace_bytes", _sz, _i32, _i64, _i64, _i32)
@@ -120,9 +121,10 @@ def qsa_rope_bf16(x, y, T: int, nheads: int, head_dim: int, rope_dim: int = 64,
 
 
 def qsa_compress_keys(k, B: int, Tk: int, k_seq_stride: int, Di: int, r: int, kbar_mode: int,
-                      kbar, kbar_seq_stride: int, stream=None) -> None:
-    _call("qsa_compress_keys", _ptr(k), B, Tk, k_seq_stride, Di, r, kbar_mode, _ptr(kbar),
-          kbar_seq_stride, _stream(stream))
+                      kbar, kbar_seq_stride: int, stream=None, gain=None, rope_dim: int = 0,
+                      theta: float = 1e7, block0: int = 0) -> None:
+    _call("qsa_compress_keys", _ptr(k), B, Tk, k_seq_stride, Di, r, kbar_mode, _ptr(gain),
+          rope_dim, theta, block0, _ptr(kbar), kbar_seq_stride, _stream(stream))
 
 
 def qsa_index_scores(q_idx, kbar, B: int, Tq: int, pos0: int, seq_len, nb_max: int, Hi: int,

@@ -93,11 +93,18 @@ hipError_t launch_rope(const uint16_t *x, uint16_t *y, int64_t T, int nheads, in
 
 // One thread per (sequence, block, 8-dim chunk); the Di/8 threads of a block
 // are consecutive lanes, so the RMSNorm reduction stays inside a wave.
+// Optional: RMSNorm gain (mode 1) and partial RoPE of the pooled key over its
+// first rope_dim dims at the block's first token, r * (block0 + block): the
+// pair partner of dim j < rope_dim/2 lives in chunk c ^ (rope_dim/16) of the
+// same block (rope_dim a power of two), one lane xor away.
 template <int DI>
 __global__ void __launch_bounds__(256) compress_kernel(const uint16_t *__restrict__ k, int B,
                                                        int64_t nb, int64_t k_seq_stride, int r,
-                                                       int mode, uint16_t *__restrict__ kbar,
+                                                       int mode, const uint16_t *__restrict__ gain,
+                                                       int rope_dim, InvFreq inv_freq,
+                                                       int64_t block0, uint16_t *__restrict__ kbar,
                                                        int64_t kbar_seq_stride) {
+#pragma clang fp contract(off)
     constexpr int CH = DI / 8;  // chunks per block row (8, 16 or 32 lanes)
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t total = static_cast<int64_t>(B) * nb * CH;
@@ -126,7 +133,27 @@ __global__ void __launch_bounds__(256) compress_kernel(const uint16_t *__restric
         for (int off = CH / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, CH);
         double inv = 1.0 / sqrt(ss / static_cast<double>(DI) + 1e-6);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] *= inv;
+        for (int i = 0; i < 8; ++i)
+            acc[i] *= inv * (gain ? static_cast<double>(bf16_bits_to_f32(gain[c * 8 + i])) : 1.0);
+    }
+    if (rope_dim > 0) {
+        const int hc = rope_dim / 16;  // chunks in half the rotated dims
+        double other[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) other[i] = __shfl_xor(acc[i], hc, CH);
+        if (c < 2 * hc) {
+            const bool lo = c < hc;  // holds a of the pairs (a, b)
+            const double p = static_cast<double>(r) * static_cast<double>(block0 + jb);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int j = (lo ? c : c - hc) * 8 + i;
+                double sn, cs;
+                sincos(p * inv_freq.v[j], &sn, &cs);
+                const double a = lo ? acc[i] : other[i], bb = lo ? other[i] : acc[i];
+                const double ac = a * cs, bs = bb * sn, bc = bb * cs, as = a * sn;
+                acc[i] = lo ? ac - bs : bc + as;
+            }
+        }
     }
     if (!live) return;
     uint16_t out[8];
@@ -137,24 +164,27 @@ __global__ void __launch_bounds__(256) compress_kernel(const uint16_t *__restric
 }
 
 hipError_t launch_compress(const uint16_t *k, int B, int64_t Tk, int64_t k_seq_stride, int Di,
-                           int r, int mode, uint16_t *kbar, int64_t kbar_seq_stride,
-                           hipStream_t s) {
+                           int r, int mode, const uint16_t *gain, int rope_dim,
+                           const double *inv_freq, int64_t block0, uint16_t *kbar,
+                           int64_t kbar_seq_stride, hipStream_t s) {
     const int64_t nb = Tk / r;
     if (nb == 0 || B == 0) return hipSuccess;
+    InvFreq f;
+    for (int j = 0; j < 64; ++j) f.v[j] = inv_freq && j < rope_dim / 2 ? inv_freq[j] : 0.0;
     const int64_t threads = static_cast<int64_t>(B) * nb * (Di / 8);
     const dim3 grid(static_cast<uint32_t>((threads + 255) / 256));
     switch (Di) {
     case 64:
         hipLaunchKernelGGL(compress_kernel<64>, grid, dim3(256), 0, s, k, B, nb, k_seq_stride,
-                           r, mode, kbar, kbar_seq_stride);
+                           r, mode, gain, rope_dim, f, block0, kbar, kbar_seq_stride);
         break;
     case 128:
         hipLaunchKernelGGL(compress_kernel<128>, grid, dim3(256), 0, s, k, B, nb, k_seq_stride,
-                           r, mode, kbar, kbar_seq_stride);
+                           r, mode, gain, rope_dim, f, block0, kbar, kbar_seq_stride);
         break;
     default:
         hipLaunchKernelGGL(compress_kernel<256>, grid, dim3(256), 0, s, k, B, nb, k_seq_stride,
-                           r, mode, kbar, kbar_seq_stride);
+                           r, mode, gain, rope_dim, f, block0, kbar, kbar_seq_stride);
         break;
     }
     return hipGetLastError();

@@ -93,18 +93,27 @@ int qsa_rope_bf16(const qsa_bf16 *x, qsa_bf16 *y, int64_t T, int nheads, int hea
 }
 
 int qsa_compress_keys(const qsa_bf16 *k, int B, int64_t Tk, int64_t k_seq_stride, int Di, int r,
-                      int kbar_mode, qsa_bf16 *kbar, int64_t kbar_seq_stride, void *stream) {
+                      int kbar_mode, const qsa_bf16 *gain, int rope_dim, double theta,
+                      int64_t block0, qsa_bf16 *kbar, int64_t kbar_seq_stride, void *stream) {
     if (!k || !kbar) return QSA_ERR_NULL;
-    if (B <= 0 || Tk < 0 || Di <= 0 || r <= 0) return QSA_ERR_SHAPE;
+    if (B <= 0 || Tk < 0 || Di <= 0 || r <= 0 || block0 < 0) return QSA_ERR_SHAPE;
     if (kbar_mode != QSA_KBAR_MEAN && kbar_mode != QSA_KBAR_RMSNORM) return QSA_ERR_SHAPE;
+    if (rope_dim < 0 || rope_dim > Di || (rope_dim > 0 && !(theta > 0.0))) return QSA_ERR_SHAPE;
     if (Di != 64 && Di != 128 && Di != 256) return QSA_ERR_UNSUPPORTED;
     if (r > 16) return QSA_ERR_UNSUPPORTED;
+    if (rope_dim != 0 && (rope_dim < 16 || rope_dim > 128 || (rope_dim & (rope_dim - 1))))
+        return QSA_ERR_UNSUPPORTED;
+    if (gain && !aligned16(gain)) return QSA_ERR_ALIGN;
     const int64_t nb = Tk / r;
     if (B > 1 && (k_seq_stride < Tk * Di || kbar_seq_stride < nb * Di)) return QSA_ERR_SHAPE;
     if (k_seq_stride % 8 || kbar_seq_stride % 8) return QSA_ERR_ALIGN;
     if (static_cast<int64_t>(B) * nb * (Di / 8) / 256 > kI32Max) return QSA_ERR_OVERFLOW;
     if (!aligned16(k) || !aligned16(kbar)) return QSA_ERR_ALIGN;
-    return launch_status(launch_compress(k, B, Tk, k_seq_stride, Di, r, kbar_mode, kbar,
+    double inv_freq[64];
+    for (int j = 0; j < rope_dim / 2; ++j)
+        inv_freq[j] = pow(theta, -2.0 * static_cast<double>(j) / static_cast<double>(rope_dim));
+    return launch_status(launch_compress(k, B, Tk, k_seq_stride, Di, r, kbar_mode, gain,
+                                         rope_dim, rope_dim ? inv_freq : nullptr, block0, kbar,
                                          kbar_seq_stride, as_stream(stream)));
 }
 

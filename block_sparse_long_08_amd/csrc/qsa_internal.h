@@ -68,9 +68,12 @@ hipError_t launch_rope(const uint16_t *x, uint16_t *y, int64_t T, int nheads, in
                        int rope_dim, const double *inv_freq, int64_t pos0,
                        const int64_t *seq_len, int nq, hipStream_t s);
 
+// gain: RMSNorm gain (mode 1) or nullptr; rope_dim > 0 (a power of two)
+// rotates the pooled keys at positions r * (block0 + block) with inv_freq.
 hipError_t launch_compress(const uint16_t *k, int B, int64_t Tk, int64_t k_seq_stride, int Di,
-                           int r, int mode, uint16_t *kbar, int64_t kbar_seq_stride,
-                           hipStream_t s);
+                           int r, int mode, const uint16_t *gain, int rope_dim,
+                           const double *inv_freq, int64_t block0, uint16_t *kbar,
+                           int64_t kbar_seq_stride, hipStream_t s);
 
 // Decode form (seq_len given): when gmax is set, also writes the largest
 // score key of every group of 64 consecutive blocks, gmax[b * gld + g] for

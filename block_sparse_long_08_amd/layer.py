@@ -25,15 +25,21 @@ class QSAPrefill:
     is pooled.  fresh=False: K is a post-RoPE cache and only the chunk's own
     indexer keys (positions pos0 ..) are pooled into the caller's kbar cache
     (pos0 must then be a multiple of r).
+
+    idx_rope_dim > 0: partial RoPE on the indexer (pooled keys rotated at their
+    block's first token, indexer queries at their own positions); kbar_gain:
+    the RMSNorm gain of the pooled keys (kbar_mode RMSNORM), bf16 [DI].
     """
 
     def __init__(self, Tq: int, pos0: int = 0, H: int = 24, Hkv: int = 2, D: int = 256,
                  budget: int = 512, score_mode: int = SCORE_MAXHEAD, kbar_mode: int = KBAR_MEAN,
-                 theta: float = 1e7, rope_dim: int = 64, fresh: bool = True, device="cuda"):
+                 theta: float = 1e7, rope_dim: int = 64, fresh: bool = True,
+                 idx_rope_dim: int = 0, kbar_gain=None, device="cuda"):
         self.Tq, self.pos0, self.H, self.Hkv, self.D = Tq, pos0, H, Hkv, D
         self.Tk = pos0 + Tq
         self.budget, self.score_mode, self.kbar_mode = budget, score_mode, kbar_mode
         self.theta, self.rope_dim, self.fresh = theta, rope_dim, fresh
+        self.idx_rope_dim, self.kbar_gain = idx_rope_dim, kbar_gain
         self.nb = self.Tk // R
         dev = torch.device(device)
         self.Qr = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=dev)
@@ -45,19 +51,30 @@ class QSAPrefill:
         self.lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
         self.ws_bytes = qsa_select_workspace_bytes(1, Tq, self.nb, budget)
         self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=dev)
+        self.qir = (torch.empty((Tq, HI, DI), dtype=torch.bfloat16, device=dev)
+                    if idx_rope_dim else None)
 
     def rope_and_pool(self, Q, K, ki, kbar=None):
         qsa_rope_bf16(Q, self.Qr, self.Tq, self.H, self.D, self.rope_dim, self.theta, self.pos0)
+        pool = dict(gain=self.kbar_gain, rope_dim=self.idx_rope_dim, theta=self.theta)
         if self.fresh:
             qsa_rope_bf16(K, self.Kr, self.Tk, self.Hkv, self.D, self.rope_dim, self.theta, 0)
             qsa_compress_keys(ki, 1, self.Tk, self.Tk * DI, DI, R, self.kbar_mode, self.kbar,
-                              self.nb * DI)
+                              self.nb * DI, **pool)
             return self.Kr, self.kbar
         # pool the chunk's own keys into the cache (blocks pos0/r ..)
         b0 = self.pos0 // R
         qsa_compress_keys(ki[self.pos0:], 1, self.Tq, self.Tq * DI, DI, R, self.kbar_mode,
-                          kbar[b0:], self.Tq // R * DI)
+                          kbar[b0:], self.Tq // R * DI, block0=b0, **pool)
         return K, kbar
+
+    def rope_indexer(self, qi):
+        """The indexer queries the scores use: qi, or qi rotated at positions
+        pos0 + t when the indexer has partial RoPE."""
+        if not self.idx_rope_dim:
+            return qi
+        qsa_rope_bf16(qi, self.qir, self.Tq, HI, DI, self.idx_rope_dim, self.theta, self.pos0)
+        return self.qir
 
     def select(self, qi, kbar):
         qsa_select_blocks(qi, kbar, 1, self.Tq, self.pos0, None, self.nb, HI, DI, R,
@@ -71,7 +88,7 @@ class QSAPrefill:
 
     def __call__(self, Q, K, V, qi, ki, kbar=None):
         Kr, kb = self.rope_and_pool(Q, K, ki, kbar)
-        self.select(qi, kb)
+        self.select(self.rope_indexer(qi), kb)
         self.attend(Kr, V)
         return self.O, self.lse
 
@@ -85,10 +102,12 @@ class QSADecode:
 
     def __init__(self, B: int, Lmax: int, H: int = 24, Hkv: int = 2, D: int = 256,
                  budget: int = 512, score_mode: int = SCORE_MAXHEAD, kbar_mode: int = KBAR_MEAN,
-                 theta: float = 1e7, rope_dim: int = 64, next_n: int = 1, device="cuda"):
+                 theta: float = 1e7, rope_dim: int = 64, next_n: int = 1,
+                 idx_rope_dim: int = 0, kbar_gain=None, device="cuda"):
         self.B, self.Lmax, self.H, self.Hkv, self.D = B, Lmax, H, Hkv, D
         self.budget, self.score_mode, self.kbar_mode = budget, score_mode, kbar_mode
         self.theta, self.rope_dim, self.next_n = theta, rope_dim, next_n
+        self.idx_rope_dim, self.kbar_gain = idx_rope_dim, kbar_gain
         self.nb_max = Lmax // R
         dev = torch.device(device)
         n = next_n
@@ -101,11 +120,19 @@ class QSADecode:
         self.sel_ws = torch.empty((max(self.sel_ws_bytes, 16),), dtype=torch.uint8, device=dev)
         self.dec_ws_bytes = qsa_decode_workspace_bytes(B, n, H, Hkv, D, budget)
         self.dec_ws = torch.empty((max(self.dec_ws_bytes, 16),), dtype=torch.uint8, device=dev)
+        self.qir = (torch.empty((B, n, HI, DI), dtype=torch.bfloat16, device=dev)
+                    if idx_rope_dim else None)
+
+    def pool_keys(self, ki, kbar, block0: int = 0):
+        """Pool indexer keys ki [B, T, DI] (T a multiple of r) into kbar[:, block0 ..]."""
+        T = ki.shape[1]
+        qsa_compress_keys(ki, self.B, T, T * DI, DI, R, self.kbar_mode, kbar[:, block0],
+                          self.nb_max * DI, gain=self.kbar_gain, rope_dim=self.idx_rope_dim,
+                          theta=self.theta, block0=block0)
 
     def append_block(self, ki_tail, kbar, block: int):
         """Pool the r indexer keys ki_tail [B, r, DI] into kbar[:, block]."""
-        qsa_compress_keys(ki_tail, self.B, R, R * DI, DI, R, self.kbar_mode, kbar[:, block],
-                          self.nb_max * DI)
+        self.pool_keys(ki_tail, kbar, block)
 
     def __call__(self, q, qi, Kc, Vc, kbar, seq_len):
         """q [B, next_n, H, D] and qi [B, next_n, HI, DI] (or [B, H, D] and
@@ -114,6 +141,10 @@ class QSADecode:
         n = self.next_n
         qsa_rope_bf16(q, self.qr, self.B * n, self.H, self.D, self.rope_dim, self.theta, 0,
                       seq_len, n)
+        if self.idx_rope_dim:  # indexer queries at their own positions
+            qsa_rope_bf16(qi, self.qir, self.B * n, HI, DI, self.idx_rope_dim, self.theta, 0,
+                          seq_len, n)
+            qi = self.qir
         qsa_select_blocks(qi, kbar, self.B, n, 0, seq_len, self.nb_max, HI, DI, R,
                           self.score_mode, self.budget, self.blk_idx, self.n_sel, self.sel_ws,
                           self.sel_ws_bytes)

@@ -110,10 +110,21 @@ int qsa_rope_bf16(const qsa_bf16 *x, qsa_bf16 *y, int64_t T, int nheads, int hea
  * For each sequence b < B and block j < Tk / r:
  *   kbar[b*kbar_seq_stride + j*Di + :] = pool(k[b*k_seq_stride + (j*r + t)*Di + :], t < r)
  * Sums are formed in fp64 in token order, so MEAN mode is exact before the
- * single bf16 rounding.  Strides are in elements; Tk % r tokens at the end
- * are ignored.  Supported: Di in {64,128,256}, 1 <= r <= 16. */
+ * single bf16 rounding.  In RMSNORM mode the normalised key is multiplied by
+ * the gain gain[0 .. Di-1] (bf16, NULL = unit gain).  With rope_dim > 0 the
+ * pooled key is then rotated like qsa_rope_bf16 over its first rope_dim dims
+ * (pairs (j, j + rope_dim/2), base theta) at the position of the block's first
+ * token, r * (block0 + j): the same section pools first and applies partial
+ * RoPE after, so tokens at different phases are never averaged (indexer
+ * queries are then rotated at their own positions with qsa_rope_bf16).
+ * Pooling, normalisation and rotation run in fp64 with one bf16 rounding.
+ * Strides are in elements; Tk % r tokens at the end are ignored; block0 is
+ * the index of the first pooled block (appending blocks to a cache).
+ * Supported: Di in {64,128,256}, 1 <= r <= 16, rope_dim 0 or a power of two
+ * in 16 .. min(Di, 128). */
 int qsa_compress_keys(const qsa_bf16 *k, int B, int64_t Tk, int64_t k_seq_stride, int Di, int r,
-                      int kbar_mode, qsa_bf16 *kbar, int64_t kbar_seq_stride, void *stream);
+                      int kbar_mode, const qsa_bf16 *gain, int rope_dim, double theta,
+                      int64_t block0, qsa_bf16 *kbar, int64_t kbar_seq_stride, void *stream);
 
 /* ---- A3: indexer block scores (chlience section 6, I_ib; ai.info
  * contribution 3: MQA indexer, 4 query heads and one shared key head).

@@ -47,6 +47,8 @@ def _load():
         lib.qsa_oracle_rope.argtypes = [vp, vp, i64, i32, i32, i32, dbl, i64, vp]
         lib.qsa_oracle_rope.restype = None
         lib.qsa_oracle_compress.argtypes = [vp, i64, i32, i32, i32, vp]
+        lib.qsa_oracle_compress_ext.argtypes = [vp, i64, i32, i32, i32, vp, i32, dbl, i64, vp]
+        lib.qsa_oracle_compress_ext.restype = None
         lib.qsa_oracle_compress.restype = None
         lib.qsa_oracle_num_complete.argtypes = [i64, i32]
         lib.qsa_oracle_num_threads.restype = i32
@@ -118,12 +120,20 @@ def rope(x: np.ndarray, rope_dim: int = 64, theta: float = 1e7, pos0: int = 0,
     return y
 
 
-def compress(k: np.ndarray, r: int = 4, mode: int = KBAR_MEAN) -> np.ndarray:
-    """k [Tk, Di] bf16 bits -> kbar [Tk // r, Di] bf16 bits."""
+def compress(k: np.ndarray, r: int = 4, mode: int = KBAR_MEAN, gain: np.ndarray | None = None,
+             rope_dim: int = 0, theta: float = 1e7, block0: int = 0) -> np.ndarray:
+    """k [Tk, Di] bf16 bits -> kbar [Tk // r, Di] bf16 bits.  gain: bf16 [Di]
+    RMSNorm gain (mode 1); rope_dim > 0 rotates the pooled keys at the block
+    start positions r * (block0 + b)."""
     k = _c(k, np.uint16)
     Tk, Di = k.shape
     out = np.empty((Tk // r, Di), dtype=np.uint16)
-    _load().qsa_oracle_compress(_p(k), Tk, Di, r, mode, _p(out))
+    if gain is None and rope_dim == 0:
+        _load().qsa_oracle_compress(_p(k), Tk, Di, r, mode, _p(out))
+    else:
+        g = None if gain is None else _c(gain, np.uint16)
+        _load().qsa_oracle_compress_ext(_p(k), Tk, Di, r, mode, _p(g), rope_dim, theta, block0,
+                                        _p(out))
     return out
 
 

@@ -96,15 +96,21 @@ void qsa_oracle_rope(const uint16_t *x, uint16_t *y, int64_t T, int nheads, int 
 }
 
 /* ---------- O2: key compression ------------------------------------------ */
-/* kbar[b][:] for b < Tk/r: mode 0 = mean of the r keys of block b;
- * mode 1 = that mean divided by sqrt(mean of its squares + 1e-6) (RMSNorm
- * with unit gain).  Rounded to bf16. */
-void qsa_oracle_compress(const uint16_t *k, int64_t Tk, int Di, int r, int mode,
-                         uint16_t *kbar) {
+/* kbar[b][:] for b < Tk/r (chlience section 6, the k-bar equation): m = the
+ * mean of the r keys of block b (mode 0, average pooling), or in mode 1
+ * RMSNorm(m) = m / sqrt(mean(m^2) + 1e-6), each dim times the gain gamma[d]
+ * (gain NULL: unit gain).  With rope_dim > 0 the pooled key is then rotated
+ * as in O1 over its first rope_dim dims, at the position of the block's first
+ * token, r * (block0 + b) (the same section: pooling first, then partial
+ * RoPE, so tokens at different phases are not averaged).  fp64 throughout,
+ * one bf16 rounding at the end. */
+void qsa_oracle_compress_ext(const uint16_t *k, int64_t Tk, int Di, int r, int mode,
+                             const uint16_t *gain, int rope_dim, double theta, int64_t block0,
+                             uint16_t *kbar) {
     int64_t nb = Tk / r;
 #pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < nb; ++b) {
-        double m[1024];
+        double m[1024], m2[1024];
         for (int d = 0; d < Di; ++d) {
             double s = 0.0;
             for (int t = 0; t < r; ++t) s += bf16_to_f64(k[(b * r + t) * Di + d]);
@@ -114,10 +120,32 @@ void qsa_oracle_compress(const uint16_t *k, int64_t Tk, int Di, int r, int mode,
             double ss = 0.0;
             for (int d = 0; d < Di; ++d) ss += m[d] * m[d];
             double inv = 1.0 / sqrt(ss / (double)Di + 1e-6);
-            for (int d = 0; d < Di; ++d) m[d] *= inv;
+            for (int d = 0; d < Di; ++d) {
+                double g = gain ? bf16_to_f64(gain[d]) : 1.0;
+                m[d] *= inv * g;
+            }
+        }
+        if (rope_dim > 0) {
+            int half = rope_dim / 2;
+            double p = (double)r * (double)(block0 + b);
+            for (int d = 0; d < Di; ++d) m2[d] = m[d];
+            for (int j = 0; j < half; ++j) {
+                double a = m[j], bb = m[j + half];
+                double ang = p * pow(theta, -(double)(2 * j) / (double)rope_dim);
+                double c = cos(ang), s = sin(ang);
+                m2[j] = a * c - bb * s;
+                m2[j + half] = bb * c + a * s;
+            }
+            for (int d = 0; d < Di; ++d) m[d] = m2[d];
         }
         for (int d = 0; d < Di; ++d) kbar[b * Di + d] = f64_to_bf16(m[d]);
     }
+}
+
+/* O2 without gain or rotation. */
+void qsa_oracle_compress(const uint16_t *k, int64_t Tk, int Di, int r, int mode,
+                         uint16_t *kbar) {
+    qsa_oracle_compress_ext(k, Tk, Di, r, mode, NULL, 0, 0.0, 0, kbar);
 }
 
 /* ---------- O3: indexer scores of one query ------------------------------ */

@@ -89,8 +89,10 @@ def test_rope_validation(lib):
     assert rope(lib, T=6, lens=vp(P), next_n=4) == SHAPE   # rows not whole sequences
 
 
-def compress(lib, k=P, B=1, Tk=16, ks=16 * 128, Di=128, r=4, mode=0, kb=P, kbs=4 * 128):
-    return lib.qsa_compress_keys(vp(k), B, I64(Tk), I64(ks), Di, r, mode, vp(kb), I64(kbs), None)
+def compress(lib, k=P, B=1, Tk=16, ks=16 * 128, Di=128, r=4, mode=0, kb=P, kbs=4 * 128,
+             gain=None, rope_dim=0, theta=1e7, block0=0):
+    return lib.qsa_compress_keys(vp(k), B, I64(Tk), I64(ks), Di, r, mode, gain, rope_dim,
+                                 ctypes.c_double(theta), I64(block0), vp(kb), I64(kbs), None)
 
 
 def test_compress_validation(lib):
@@ -101,6 +103,12 @@ def test_compress_validation(lib):
     assert compress(lib, r=32) == UNSUP
     assert compress(lib, B=2, ks=8) == SHAPE
     assert compress(lib, k=MIS) == ALIGN
+    assert compress(lib, rope_dim=48) == UNSUP        # partner chunk by xor: power of two
+    assert compress(lib, rope_dim=8) == UNSUP
+    assert compress(lib, rope_dim=256) == SHAPE       # more than Di
+    assert compress(lib, rope_dim=64, theta=0.0) == SHAPE
+    assert compress(lib, block0=-1) == SHAPE
+    assert compress(lib, mode=1, gain=vp(MIS)) == ALIGN
 
 
 def scores(lib, q=P, kb=P, B=1, Tq=8, pos0=0, sl=None, nb=4, Hi=4, Di=128, r=4, mode=0, out=P,

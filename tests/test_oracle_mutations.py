@@ -33,6 +33,12 @@ MUTATIONS = {
     "softmax_scale": ("double scale = 1.0 / sqrt((double)D);", "double scale = 1.0 / (double)D;"),
     "value_operand_swapped": ("const uint16_t *vr = V + ", "const uint16_t *vr = K + "),
     "lse_drops_max": ("lse[h] = m + log(sw);", "lse[h] = log(sw);"),
+    "kbar_rope_sign": ("m2[j] = a * c - bb * s;", "m2[j] = a * c + bb * s;"),
+    "kbar_rope_block_index": ("double p = (double)r * (double)(block0 + b);",
+                              "double p = (double)(block0 + b);"),
+    "kbar_gain_dropped": ("m[d] *= inv * g;", "m[d] *= inv;"),
+    "kbar_rope_frequency": ("pow(theta, -(double)(2 * j) / (double)rope_dim)",
+                            "pow(theta, -(double)j / (double)rope_dim)"),
     "reuse_tail_from_own_block": ("int64_t from = qsa_oracle_num_complete(p_sel, r) * r;",
                                   "int64_t from = qsa_oracle_num_complete(p, r) * r;"),
     "reuse_tail_stops_short": ("for (int64_t j = from; j <= p; ++j) tok[n++] = j;",

@@ -184,6 +184,50 @@ def test_compress_rmsnorm_mode(oracle_lib):
     assert np.all(np.sign(kb2) == np.sign(mean))
 
 
+def test_compress_gain_scales_rmsnorm(oracle_lib, synth_lib):
+    """A power-of-two gain scales the normalised key exactly, dim by dim."""
+    k = synth_lib.normal_bf16(5, (64, 128), seed=3)
+    g = np.ones(128, dtype=np.float32)
+    g[::3] = 2.0
+    g[1::3] = 0.25
+    plain = f32(oracle_lib.compress(k, mode=1))
+    gained = f32(oracle_lib.compress(k, mode=1, gain=bf(g)))
+    assert np.array_equal(gained, plain * g)
+    # MEAN mode ignores the gain
+    assert np.array_equal(oracle_lib.compress(k, gain=bf(g)), oracle_lib.compress(k))
+
+
+def test_compress_rope_is_o1_at_block_start(oracle_lib, synth_lib):
+    """Blocks of four equal keys pool exactly, so pooling-then-RoPE must equal
+    O1 applied to the key at the block's first token r*(block0 + b)."""
+    rows = synth_lib.normal_bf16(5, (40, 128), seed=4)
+    k = np.repeat(rows, 4, axis=0)
+    for rd, block0 in [(64, 0), (64, 1000), (32, 7), (128, 262143)]:
+        got = oracle_lib.compress(k, rope_dim=rd, block0=block0)
+        want = oracle_lib.rope(rows[:, None, :], rope_dim=rd,
+                               pos=4 * (block0 + np.arange(40)))[:, 0, :]
+        assert np.array_equal(got, want), (rd, block0)
+    assert np.array_equal(oracle_lib.compress(k, rope_dim=64, block0=0)[0], rows[0])
+
+
+def test_compress_rope_relative_scores(oracle_lib, synth_lib):
+    """Indexer scores with rotated queries and pooled keys depend on the
+    query-block distance only: shifting every position by 4m keeps them (up
+    to the bf16 roundings of the rotated vectors)."""
+    ki = synth_lib.normal_bf16(5, (256, 128), seed=5)
+    qi = synth_lib.normal_bf16(4, (1, 4, 128), seed=5)
+    p = 255
+    s = []
+    for m in (0, 5000):
+        kb = oracle_lib.compress(ki, rope_dim=64, block0=m)
+        q = oracle_lib.rope(qi, rope_dim=64, pos0=p + 4 * m)
+        s.append(oracle_lib.scores_row(q[0], kb, 255))
+    assert np.abs(s[0] - s[1]).max() < 0.02 * np.abs(s[0]).max()
+    kb0 = oracle_lib.compress(ki)
+    s_none = oracle_lib.scores_row(qi[0], kb0, 255)
+    assert np.abs(s[0] - s_none).max() > 0.05   # the rotation does act
+
+
 # ----------------------------------------------------------------------------
 # Indexer scores.
 # ----------------------------------------------------------------------------
