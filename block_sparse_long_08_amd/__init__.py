@@ -42,23 +42,23 @@ _sig("qsa_version", _i32)
 _sig("qsa_check_device", _i32)
 _sig("qsa_rope_bf16", _i32, _vp, _vp, _i64, _i32, _i32, _i32, _dbl, _i64, _vp, _i32, _vp)
 _sig("qsa_compress_keys", _i32, _vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _i32, _dbl, _i64,
-     _vp, _i64, _vp)
+     _vp, _i64, _vp, _vp)
 _sig("qsa_index_scores", _i32, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _i32, _i32, _i32, _i32,
-     _vp, _i64, _vp)
+     _vp, _i64, _vp, _vp)
 _sig("qsa_topk_workspace_bytes", _sz, _i32, _i64, _i64, _i32)
 _sig("qsa_topk_blocks", _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _vp,
      _sz, _vp)
 _sig("qsa_select_workspace_bytes", _sz, _i32, _i64, _i64, _i32)
 _sig("qsa_select_blocks", _i32, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _i32, _i32, _i32, _i32,
-     _i32, _vp, _vp, _vp, _sz, _vp)
+     _i32, _vp, _vp, _vp, _sz, _vp, _vp)
 _sig("qsa_sparse_attn_prefill", _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
-     _i32, _i32, _vp, _vp, _vp)
+     _i32, _i32, _vp, _vp, _vp, _vp)
 _sig("qsa_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32, _i32)
 _sig("qsa_sparse_attn_decode", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32,
-     _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp)
+     _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp, _vp)
 _sig("dense_attn_workspace_bytes", _sz, _i32, _i64, _i64, _i32, _i32, _i32)
 _sig("dense_attn", _i32, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _i32, _i32, _vp, _vp,
-     _vp, _sz, _vp)
+     _vp, _sz, _vp, _vp)
 
 EXPORTED = ["qsa_status_string", "qsa_version", "qsa_check_device", "qsa_rope_bf16",
             "qsa_compress_keys", "qsa_index_scores", "qsa_topk_workspace_bytes",
@@ -103,6 +103,21 @@ def _call(name, *args):
         raise QSAError(name, st)
 
 
+class Pages(ctypes.Structure):
+    """qsa_pages: a page table (device int32 tensor [B, table_stride]) and the
+    page size in tokens; the cache arguments of a call are then page pools."""
+    _fields_ = [("table", ctypes.c_void_p), ("table_stride", ctypes.c_int64),
+                ("page_tokens", ctypes.c_int)]
+
+    def __init__(self, table, page_tokens: int):
+        super().__init__(ctypes.c_void_p(table.data_ptr()), table.shape[-1], page_tokens)
+        self._table = table  # keeps the tensor alive
+
+
+def _pages(p):
+    return None if p is None else ctypes.byref(p)
+
+
 def qsa_version() -> int:
     return int(_lib.qsa_version())
 
@@ -122,15 +137,16 @@ def qsa_rope_bf16(x, y, T: int, nheads: int, head_dim: int, rope_dim: int = 64,
 
 def qsa_compress_keys(k, B: int, Tk: int, k_seq_stride: int, Di: int, r: int, kbar_mode: int,
                       kbar, kbar_seq_stride: int, stream=None, gain=None, rope_dim: int = 0,
-                      theta: float = 1e7, block0: int = 0) -> None:
+                      theta: float = 1e7, block0: int = 0, pages=None) -> None:
     _call("qsa_compress_keys", _ptr(k), B, Tk, k_seq_stride, Di, r, kbar_mode, _ptr(gain),
-          rope_dim, theta, block0, _ptr(kbar), kbar_seq_stride, _stream(stream))
+          rope_dim, theta, block0, _ptr(kbar), kbar_seq_stride, _pages(pages), _stream(stream))
 
 
 def qsa_index_scores(q_idx, kbar, B: int, Tq: int, pos0: int, seq_len, nb_max: int, Hi: int,
-                     Di: int, r: int, score_mode: int, scores, ld: int, stream=None) -> None:
+                     Di: int, r: int, score_mode: int, scores, ld: int, stream=None,
+                     pages=None) -> None:
     _call("qsa_index_scores", _ptr(q_idx), _ptr(kbar), B, Tq, pos0, _ptr(seq_len), nb_max, Hi, Di,
-          r, score_mode, _ptr(scores), ld, _stream(stream))
+          r, score_mode, _ptr(scores), ld, _pages(pages), _stream(stream))
 
 
 def qsa_topk_workspace_bytes(B: int, Tq: int, nb_max: int, K: int) -> int:
@@ -149,16 +165,17 @@ def qsa_select_workspace_bytes(B: int, Tq: int, nb_max: int, K: int) -> int:
 
 def qsa_select_blocks(q_idx, kbar, B: int, Tq: int, pos0: int, seq_len, nb_max: int, Hi: int,
                       Di: int, r: int, score_mode: int, K: int, blk_idx, n_sel, ws,
-                      ws_bytes: int, stream=None) -> None:
+                      ws_bytes: int, stream=None, pages=None) -> None:
     _call("qsa_select_blocks", _ptr(q_idx), _ptr(kbar), B, Tq, pos0, _ptr(seq_len), nb_max, Hi,
-          Di, r, score_mode, K, _ptr(blk_idx), _ptr(n_sel), _ptr(ws), ws_bytes, _stream(stream))
+          Di, r, score_mode, K, _ptr(blk_idx), _ptr(n_sel), _ptr(ws), ws_bytes, _pages(pages),
+          _stream(stream))
 
 
 def qsa_sparse_attn_prefill(Q, K, V, blk_idx, n_sel, Tq: int, Tk: int, pos0: int, H: int,
                             Hkv: int, D: int, r: int, Kbudget: int, O, lse=None,
-                            stream=None) -> None:
+                            stream=None, pages=None) -> None:
     _call("qsa_sparse_attn_prefill", _ptr(Q), _ptr(K), _ptr(V), _ptr(blk_idx), _ptr(n_sel), Tq,
-          Tk, pos0, H, Hkv, D, r, Kbudget, _ptr(O), _ptr(lse), _stream(stream))
+          Tk, pos0, H, Hkv, D, r, Kbudget, _ptr(O), _ptr(lse), _pages(pages), _stream(stream))
 
 
 def qsa_decode_workspace_bytes(B: int, Tq: int, H: int, Hkv: int, D: int, Kbudget: int) -> int:
@@ -167,10 +184,10 @@ def qsa_decode_workspace_bytes(B: int, Tq: int, H: int, Hkv: int, D: int, Kbudge
 
 def qsa_sparse_attn_decode(q, Kc, Vc, seq_len, blk_idx, n_sel, B: int, Tq: int, Lmax: int,
                            H: int, Hkv: int, D: int, r: int, Kbudget: int, O, lse, ws,
-                           ws_bytes: int, stream=None) -> None:
+                           ws_bytes: int, stream=None, pages=None) -> None:
     _call("qsa_sparse_attn_decode", _ptr(q), _ptr(Kc), _ptr(Vc), _ptr(seq_len), _ptr(blk_idx),
           _ptr(n_sel), B, Tq, Lmax, H, Hkv, D, r, Kbudget, _ptr(O), _ptr(lse), _ptr(ws),
-          ws_bytes, _stream(stream))
+          ws_bytes, _pages(pages), _stream(stream))
 
 
 def dense_attn_workspace_bytes(B: int, Tq: int, Lmax: int, H: int, Hkv: int, D: int) -> int:
@@ -178,9 +195,9 @@ def dense_attn_workspace_bytes(B: int, Tq: int, Lmax: int, H: int, Hkv: int, D: 
 
 
 def dense_attn(Q, K, V, B: int, Tq: int, Lmax: int, pos0: int, seq_len, H: int, Hkv: int, D: int,
-               O, lse=None, ws=None, ws_bytes: int = 0, stream=None) -> None:
+               O, lse=None, ws=None, ws_bytes: int = 0, stream=None, pages=None) -> None:
     _call("dense_attn", _ptr(Q), _ptr(K), _ptr(V), B, Tq, Lmax, pos0, _ptr(seq_len), H, Hkv, D,
-          _ptr(O), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream))
+          _ptr(O), _ptr(lse), _ptr(ws), ws_bytes, _pages(pages), _stream(stream))
 
 
 from .layer import QSAPrefill, QSADecode  # noqa: E402  (chains of the calls above)

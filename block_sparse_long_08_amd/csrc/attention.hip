@@ -36,7 +36,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kStageEntries = 4;             // 4 blocks = 16 tokens per stage
 constexpr int kVStageBytes = 16 * 512;       // 16 tokens x 256 bf16
 constexpr int kRecFloats = 4096 + 128;       // O^T (lane-major) + m + l of one wave
-constexpr int kMaxListLds = 2048;
+constexpr int kMaxListLds = 2048 + 16;  // budget entries plus the tail (paged lists)
 
 __device__ __forceinline__ void lds_fence() {
     // LDS ops of one wave complete in order; this keeps the compiler from
@@ -53,20 +53,30 @@ __device__ __forceinline__ void lds_fence() {
 // MULTI: several queries share the list (the tail may span entries and each
 // column masks it at its own position); otherwise the tail is one entry of
 // (p+1) mod 4 tokens, all visible.
-template <bool MULTI>
+// PMODE: 0 contiguous cache; 1 paged, lst holds the page-pool block of every
+// entry (selected blocks and tail); 2 paged without a list (dense), rows
+// looked up in the page table ptab (shift psh).
+template <bool MULTI, int PMODE = 0>
 struct EntryList {
     const int32_t *lst;  // LDS copy of the selected blocks (sparse), or nullptr (dense)
     int lst_off;         // index of lst[0] in the query's list
     int ns;              // number of complete-block entries
     int tail;            // tail tokens after block nc - 1
     int64_t nc;          // complete blocks visible to the selecting query
+    const int32_t *ptab = nullptr;
+    int psh = 0;
     __device__ __forceinline__ int count(int e) const {
         if (!MULTI) return e < ns ? 4 : (e == ns ? tail : 0);
         return e < ns ? 4 : max(0, min(4, tail - 4 * (e - ns)));
     }
     __device__ __forceinline__ int64_t base(int e) const {
-        if (e < ns) return 4 * static_cast<int64_t>(lst ? lst[e - lst_off] : e);
-        return MULTI ? 4 * (nc + e - ns) : 4 * nc;
+        if (PMODE == 1) return 4 * static_cast<int64_t>(lst[e - lst_off]);
+        int64_t t;
+        if (e < ns)
+            t = 4 * static_cast<int64_t>(lst ? lst[e - lst_off] : e);
+        else
+            t = MULTI ? 4 * (nc + e - ns) : 4 * nc;
+        return PMODE == 2 ? page_row(ptab, psh, t) : t;
     }
     // tokens of entry e visible to a query at position pq (selected blocks
     // precede every query sharing the selection)
@@ -96,8 +106,8 @@ __device__ __forceinline__ int row_swizzle(int tt) { return 2 * ((tt >> 2) & 3);
 // Entries e0 .. e0+3 of one KV head.  Kg/Vg point at token 0 of the head (row
 // stride rs elements); p is a safe row for masked tokens; pq is the position
 // of the query in this lane's column; vlds is the wave's 8 KB LDS tile.
-template <bool MULTI>
-__device__ __forceinline__ void attn_stage(const EntryList<MULTI> &L, int e0, int64_t p,
+template <bool MULTI, int PMODE>
+__device__ __forceinline__ void attn_stage(const EntryList<MULTI, PMODE> &L, int e0, int64_t p,
                                            int64_t pq,
                                            const uint16_t *__restrict__ Kg,
                                            const uint16_t *__restrict__ Vg, int64_t rs,
@@ -250,24 +260,32 @@ __device__ __forceinline__ void state_write(const WaveState &st, float ltot,
 // Prefill: one workgroup per query, one wave per KV head; each wave walks all
 // stages of its head.  Grid: (Tq, B); block: 64 * Hkv threads.
 // Dynamic LDS: Hkv V tiles of 8 KB, then the selected-block list.
+// PAGED: K and V are page pools; the list is translated to pool blocks once
+// (the tail block as entry ns).
+template <bool PAGED>
 __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
     int32_t *lst = reinterpret_cast<int32_t *>(dyn_lds + a.Hkv * kVStageBytes);
     const int64_t t = blockIdx.x, b = blockIdx.y;
     const int64_t row = b * a.Tq + t;
-    const int64_t p = a.pos0 + t;
+    int64_t p = a.pos0 + t;
     const int64_t nc = num_complete_blocks(p, kBlock);
     const int v = a.n_sel[row];
     const int64_t cap = min(static_cast<int64_t>(a.Kbudget), nc);
     const int ns = v < 0 ? 0 : (v > cap ? static_cast<int>(cap) : v);
     const int32_t *src = a.blk_idx + row * a.Kbudget;
+    const int32_t *ptab = PAGED ? a.ptable + b * a.pstride : nullptr;
     for (int i = threadIdx.x; i < ns; i += blockDim.x) {
         int32_t bi = src[i];
         bi = bi < 0 ? 0 : (bi >= nc ? static_cast<int32_t>(nc - 1) : bi);
-        lst[i] = bi;
+        lst[i] = PAGED ? static_cast<int32_t>(page_row(ptab, a.pshift, 4 * int64_t(bi)) >> 2) : bi;
     }
+    const int tail = static_cast<int>((p + 1) % kBlock);
+    if (PAGED && threadIdx.x == 0 && tail > 0)
+        lst[ns] = static_cast<int32_t>(page_row(ptab, a.pshift, 4 * nc) >> 2);
     __syncthreads();
-    EntryList<false> L{lst, 0, ns, static_cast<int>((p + 1) % kBlock), nc};
+    EntryList<false, PAGED ? 1 : 0> L{lst, 0, ns, tail, nc};
+    if (PAGED) p = page_row(ptab, a.pshift, p);  // the safe row for masked tokens
     const int E = ns + (L.tail > 0 ? 1 : 0);
     const int nstages = (E + kStageEntries - 1) / kStageEntries;
 
@@ -276,13 +294,15 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a) {
     bf16x8 qT[8];
     load_qT(a.Q + row * a.H * kHeadDim, g, group, a.H, 0, group, lane, qT);
     const int64_t rs = static_cast<int64_t>(a.Hkv) * kHeadDim;
-    const uint16_t *Kg = a.K + b * a.Lmax * rs + g * kHeadDim;
-    const uint16_t *Vg = a.V + b * a.Lmax * rs + g * kHeadDim;
+    const int64_t seq_off = PAGED ? 0 : b * a.Lmax * rs;
+    const uint16_t *Kg = a.K + seq_off + g * kHeadDim;
+    const uint16_t *Vg = a.V + seq_off + g * kHeadDim;
+    const int64_t pq = a.pos0 + t;  // every entry is visible (single query)
     WaveState st;
     state_init(st);
     for (int sidx = 0; sidx < nstages; ++sidx)
-        attn_stage(L, sidx * kStageEntries, p, p, Kg, Vg, rs, qT, st, dyn_lds + g * kVStageBytes,
-                   lane);
+        attn_stage(L, sidx * kStageEntries, p, pq, Kg, Vg, rs, qT, st,
+                   dyn_lds + g * kVStageBytes, lane);
     const float ltot = head_total(st.l);
     state_write(st, ltot, a.O + row * a.H * kHeadDim, a.lse ? a.lse + row * a.H : nullptr, g,
                 group, lane);
@@ -310,9 +330,10 @@ __device__ __forceinline__ void record_store(const WaveState &st, float *rec, in
 // workspace.  The Tq newest queries of a sequence share its selection (made
 // for the first of them, at seq_len - Tq); the columns of a tile are 16
 // (query, head) pairs and each column masks the tail past its own query.
-template <bool DENSE, bool MULTI>
+template <bool DENSE, bool MULTI, bool PAGED>
 __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit, int sps,
                                                           int nct) {
+    constexpr int PMODE = PAGED ? (DENSE ? 2 : 1) : 0;
     __shared__ __attribute__((aligned(16))) unsigned char lds[3 * kRecFloats * 4];
     __shared__ int32_t lst[DENSE ? 1 : kMaxListLds];
     const int split = blockIdx.x;
@@ -342,30 +363,36 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit
     // the query rows are read while the block list arrives
     bf16x8 qT[8];
     load_qT(a.Q + b * nq * a.H * kHeadDim, g, group, a.H, ct, nq * group, lane, qT);
+    const int32_t *ptab = PAGED ? a.ptable + b * a.pstride : nullptr;
     if (!DENSE) {
-        const int e_hi = min(s1 * kStageEntries, ns);
+        // paged: pool blocks of the split's entries, tail entries included
+        const int e_hi = min(s1 * kStageEntries, PAGED ? E : ns);
         const int32_t *src = a.blk_idx + b * a.Kbudget;
         for (int i = e_lo + static_cast<int>(threadIdx.x); i < e_hi; i += 256) {
-            int32_t bi = src[i];
-            bi = bi < 0 ? 0 : (bi >= nc ? static_cast<int32_t>(nc - 1) : bi);
-            lst[i - e_lo] = bi;
+            int64_t bi = i < ns ? src[i] : nc + (i - ns);
+            if (i < ns) bi = bi < 0 ? 0 : (bi >= nc ? nc - 1 : bi);
+            lst[i - e_lo] =
+                static_cast<int32_t>(PAGED ? page_row(ptab, a.pshift, 4 * bi) >> 2 : bi);
         }
     }
-    EntryList<MULTI> L{DENSE ? nullptr : lst, e_lo, ns, tail, nc};
+    EntryList<MULTI, PMODE> L{DENSE ? nullptr : lst, e_lo, ns, tail, nc, ptab, a.pshift};
     __syncthreads();
 
     // position of this lane's column query (-1: no query, every token masked)
     const int pair = 16 * ct + (lane & 15);
     const int64_t pq = pair < nq * group ? p0 + pair / group : -1;
     const int64_t rs = static_cast<int64_t>(a.Hkv) * kHeadDim;
-    const uint16_t *Kg = a.K + b * a.Lmax * rs + g * kHeadDim;
-    const uint16_t *Vg = a.V + b * a.Lmax * rs + g * kHeadDim;
+    const int64_t seq_off = PAGED ? 0 : b * a.Lmax * rs;
+    const uint16_t *Kg = a.K + seq_off + g * kHeadDim;
+    const uint16_t *Vg = a.V + seq_off + g * kHeadDim;
     unsigned char *vlds = lds + wave * kVStageBytes;
+    // a row that exists for masked tokens
+    int64_t psafe = p_last < 0 ? 0 : p_last;
+    if (PAGED && E > 0) psafe = page_row(ptab, a.pshift, psafe);
     WaveState st;
     state_init(st);
     for (int sidx = s0 + wave; sidx < s1; sidx += 4)
-        attn_stage(L, sidx * kStageEntries, p_last < 0 ? 0 : p_last, pq, Kg, Vg, rs, qT, st,
-                   vlds, lane);
+        attn_stage(L, sidx * kStageEntries, psafe, pq, Kg, Vg, rs, qT, st, vlds, lane);
     __syncthreads();
     float *mbuf = reinterpret_cast<float *>(lds);
     if (wave != 0) state_store(st, mbuf + (wave - 1) * kRecFloats, lane);
@@ -424,8 +451,12 @@ __global__ void __launch_bounds__(256) attn_decode_merge(AttnArgs a, int nsplit,
 hipError_t launch_sparse_prefill(const AttnArgs &a, hipStream_t s) {
     if (a.Tq == 0 || a.B == 0) return hipSuccess;
     const dim3 grid(static_cast<uint32_t>(a.Tq), static_cast<uint32_t>(a.B));
-    const size_t lds = static_cast<size_t>(a.Hkv) * kVStageBytes + 4 * static_cast<size_t>(a.Kbudget);
-    hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(64 * a.Hkv), lds, s, a);
+    const size_t lds =
+        static_cast<size_t>(a.Hkv) * kVStageBytes + 4 * (static_cast<size_t>(a.Kbudget) + 1);
+    if (a.ptable)
+        hipLaunchKernelGGL(attn_prefill_kernel<true>, grid, dim3(64 * a.Hkv), lds, s, a);
+    else
+        hipLaunchKernelGGL(attn_prefill_kernel<false>, grid, dim3(64 * a.Hkv), lds, s, a);
     return hipGetLastError();
 }
 
@@ -450,6 +481,32 @@ size_t decode_partial_floats(int B, int Hkv, int nsplit) {
     return static_cast<size_t>(B) * Hkv * nsplit * kRecFloats;
 }
 
+template <bool DENSE, bool MULTI>
+static void launch_decode_paging(const AttnArgs &a, dim3 grid, int nsplit, int sps, int nct,
+                                 bool paged, hipStream_t s) {
+    if (paged)
+        hipLaunchKernelGGL((attn_decode_kernel<DENSE, MULTI, true>), grid, dim3(256), 0, s, a,
+                           nsplit, sps, nct);
+    else
+        hipLaunchKernelGGL((attn_decode_kernel<DENSE, MULTI, false>), grid, dim3(256), 0, s, a,
+                           nsplit, sps, nct);
+}
+
+static void launch_decode_variant(const AttnArgs &a, dim3 grid, int nsplit, int sps, int nct,
+                                  bool dense, bool multi, bool paged, hipStream_t s) {
+    if (dense) {
+        if (multi)
+            launch_decode_paging<true, true>(a, grid, nsplit, sps, nct, paged, s);
+        else
+            launch_decode_paging<true, false>(a, grid, nsplit, sps, nct, paged, s);
+    } else {
+        if (multi)
+            launch_decode_paging<false, true>(a, grid, nsplit, sps, nct, paged, s);
+        else
+            launch_decode_paging<false, false>(a, grid, nsplit, sps, nct, paged, s);
+    }
+}
+
 hipError_t launch_attn_decode(const AttnArgs &a, int nsplit, hipStream_t s) {
     if (a.B == 0) return hipSuccess;
     const int nq = static_cast<int>(a.Tq);
@@ -460,21 +517,8 @@ hipError_t launch_attn_decode(const AttnArgs &a, int nsplit, hipStream_t s) {
     const int sps = static_cast<int>((nstages + nsplit - 1) / nsplit);
     const dim3 grid(static_cast<uint32_t>(nsplit), static_cast<uint32_t>(a.Hkv * nct),
                     static_cast<uint32_t>(a.B));
-    if (a.blk_idx) {
-        if (nq > 1)
-            hipLaunchKernelGGL((attn_decode_kernel<false, true>), grid, dim3(256), 0, s, a, nsplit,
-                               sps, nct);
-        else
-            hipLaunchKernelGGL((attn_decode_kernel<false, false>), grid, dim3(256), 0, s, a,
-                               nsplit, sps, nct);
-    } else {
-        if (nq > 1)
-            hipLaunchKernelGGL((attn_decode_kernel<true, true>), grid, dim3(256), 0, s, a, nsplit,
-                               sps, nct);
-        else
-            hipLaunchKernelGGL((attn_decode_kernel<true, false>), grid, dim3(256), 0, s, a, nsplit,
-                               sps, nct);
-    }
+    launch_decode_variant(a, grid, nsplit, sps, nct, a.blk_idx == nullptr, nq > 1,
+                          a.ptable != nullptr, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t threads = 4 * static_cast<int64_t>(a.B) * nq * a.H * kHeadDim;

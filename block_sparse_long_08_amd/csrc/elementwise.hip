@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(256) compress_kernel(const uint16_t *__restric
                                                        int mode, const uint16_t *__restrict__ gain,
                                                        int rope_dim, InvFreq inv_freq,
                                                        int64_t block0, uint16_t *__restrict__ kbar,
-                                                       int64_t kbar_seq_stride) {
+                                                       int64_t kbar_seq_stride, PageTable pg) {
 #pragma clang fp contract(off)
     constexpr int CH = DI / 8;  // chunks per block row (8, 16 or 32 lanes)
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -159,14 +159,15 @@ __global__ void __launch_bounds__(256) compress_kernel(const uint16_t *__restric
     uint16_t out[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) out[i] = f64_to_bf16_rne(acc[i]);
-    *reinterpret_cast<uint4 *>(kbar + b * kbar_seq_stride + jb * DI + c * 8) =
-        *reinterpret_cast<const uint4 *>(out);
+    uint16_t *dst = pg.table ? kbar + page_row(pg.table + b * pg.stride, pg.shift, block0 + jb) * DI
+                             : kbar + b * kbar_seq_stride + jb * DI;
+    *reinterpret_cast<uint4 *>(dst + c * 8) = *reinterpret_cast<const uint4 *>(out);
 }
 
 hipError_t launch_compress(const uint16_t *k, int B, int64_t Tk, int64_t k_seq_stride, int Di,
                            int r, int mode, const uint16_t *gain, int rope_dim,
                            const double *inv_freq, int64_t block0, uint16_t *kbar,
-                           int64_t kbar_seq_stride, hipStream_t s) {
+                           int64_t kbar_seq_stride, hipStream_t s, PageTable pg) {
     const int64_t nb = Tk / r;
     if (nb == 0 || B == 0) return hipSuccess;
     InvFreq f;
@@ -176,15 +177,15 @@ hipError_t launch_compress(const uint16_t *k, int B, int64_t Tk, int64_t k_seq_s
     switch (Di) {
     case 64:
         hipLaunchKernelGGL(compress_kernel<64>, grid, dim3(256), 0, s, k, B, nb, k_seq_stride,
-                           r, mode, gain, rope_dim, f, block0, kbar, kbar_seq_stride);
+                           r, mode, gain, rope_dim, f, block0, kbar, kbar_seq_stride, pg);
         break;
     case 128:
         hipLaunchKernelGGL(compress_kernel<128>, grid, dim3(256), 0, s, k, B, nb, k_seq_stride,
-                           r, mode, gain, rope_dim, f, block0, kbar, kbar_seq_stride);
+                           r, mode, gain, rope_dim, f, block0, kbar, kbar_seq_stride, pg);
         break;
     default:
         hipLaunchKernelGGL(compress_kernel<256>, grid, dim3(256), 0, s, k, B, nb, k_seq_stride,
-                           r, mode, gain, rope_dim, f, block0, kbar, kbar_seq_stride);
+                           r, mode, gain, rope_dim, f, block0, kbar, kbar_seq_stride, pg);
         break;
     }
     return hipGetLastError();

@@ -72,16 +72,27 @@ struct FaArgs {
     float *lse;         // [B][Tq][H] or nullptr
     int64_t Tq, Lmax, pos0;
     int H, Hkv;
+    const int32_t *ptable;  // paged K/V: page table [B][pstride], or nullptr
+    int64_t pstride;
+    int pshift;
 };
+
+// Row of token tok in K/V: the sequence's own rows, or a page-pool row.
+template <bool PAGED>
+__device__ __forceinline__ int64_t fa_row(const int32_t *ptab, int psh, int64_t tok) {
+    return PAGED ? page_row(ptab, psh, tok) : tok;
+}
 
 // K tile into registers: thread t takes row t/8 (token) and the chunks
 // (16 B each) c = t%8 + 8u, u = 0..3, of that row.
+template <bool PAGED>
 __device__ __forceinline__ void fa_load_k(const uint16_t *Kg, int64_t rs, int64_t tok0,
-                                          int64_t tok_max, int tid, uint4 (&kr)[4]) {
+                                          int64_t tok_max, int tid, uint4 (&kr)[4],
+                                          const int32_t *ptab, int psh) {
     const int r = tid >> 3;
     int64_t tok = tok0 + r;
     tok = tok < tok_max ? tok : tok_max - 1;
-    const uint16_t *src = Kg + tok * rs + 8 * (tid & 7);
+    const uint16_t *src = Kg + fa_row<PAGED>(ptab, psh, tok) * rs + 8 * (tid & 7);
 #pragma unroll
     for (int u = 0; u < 4; ++u) kr[u] = *reinterpret_cast<const uint4 *>(src + 64 * u);
 }
@@ -99,14 +110,16 @@ __device__ __forceinline__ void fa_store_k(const uint4 (&kr)[4], unsigned char *
 
 // V tile into registers: thread t takes tokens 4a .. 4a+3 (a = t % 8) and
 // dims 8c .. 8c+7 (c = t / 8).
+template <bool PAGED>
 __device__ __forceinline__ void fa_load_v(const uint16_t *Vg, int64_t rs, int64_t tok0,
-                                          int64_t tok_max, int tid, uint4 (&v)[4]) {
+                                          int64_t tok_max, int tid, uint4 (&v)[4],
+                                          const int32_t *ptab, int psh) {
     const int a = tid & 7, c = tid >> 3;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         int64_t tok = tok0 + 4 * a + u;
         tok = tok < tok_max ? tok : tok_max - 1;
-        v[u] = *reinterpret_cast<const uint4 *>(Vg + tok * rs + 8 * c);
+        v[u] = *reinterpret_cast<const uint4 *>(Vg + fa_row<PAGED>(ptab, psh, tok) * rs + 8 * c);
     }
 }
 
@@ -133,6 +146,7 @@ __device__ __forceinline__ void fa_store_vt(const uint4 (&v)[4], unsigned char *
     }
 }
 
+template <bool PAGED>
 __global__ void __launch_bounds__(256) fa_prefill_kernel(FaArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char fa_lds[kFaLds];
     unsigned char *const qbase = fa_lds;                            // Q tile
@@ -146,8 +160,11 @@ __global__ void __launch_bounds__(256) fa_prefill_kernel(FaArgs a) {
     const int n = lane & 31, h = lane >> 5;
     const int group = a.H / a.Hkv, g = hq / group;
     const int64_t rs = static_cast<int64_t>(a.Hkv) * kHeadDim;
-    const uint16_t *Kg = a.K + b * a.Lmax * rs + g * kHeadDim;
-    const uint16_t *Vg = a.V + b * a.Lmax * rs + g * kHeadDim;
+    const int64_t seq_off = PAGED ? 0 : b * a.Lmax * rs;
+    const uint16_t *Kg = a.K + seq_off + g * kHeadDim;
+    const uint16_t *Vg = a.V + seq_off + g * kHeadDim;
+    const int32_t *ptab = PAGED ? a.ptable + b * a.pstride : nullptr;
+    const int psh = a.pshift;
 
     const int64_t q0 = static_cast<int64_t>(qblk) * kFaQ;
     const int64_t q_last = min(q0 + kFaQ, a.Tq) - 1;
@@ -184,8 +201,8 @@ __global__ void __launch_bounds__(256) fa_prefill_kernel(FaArgs a) {
     float m_ref = -INFINITY, l = 0.f;
 
     uint4 kreg[4], vreg[4];
-    fa_load_k(Kg, rs, 0, a.Lmax, tid, kreg);
-    fa_load_v(Vg, rs, 0, a.Lmax, tid, vreg);
+    fa_load_k<PAGED>(Kg, rs, 0, a.Lmax, tid, kreg, ptab, psh);
+    fa_load_v<PAGED>(Vg, rs, 0, a.Lmax, tid, vreg, ptab, psh);
     fa_store_k(kreg, kbase, tid);
     fa_store_vt(vreg, vbase, tid);
 
@@ -195,8 +212,8 @@ __global__ void __launch_bounds__(256) fa_prefill_kernel(FaArgs a) {
         const int64_t tile0 = static_cast<int64_t>(it) * kFaN;
         // next tile into registers while this one is consumed (after the last
         // tile this fetches clamped rows into a buffer nothing reads)
-        fa_load_k(Kg, rs, tile0 + kFaN, a.Lmax, tid, kreg);
-        fa_load_v(Vg, rs, tile0 + kFaN, a.Lmax, tid, vreg);
+        fa_load_k<PAGED>(Kg, rs, tile0 + kFaN, a.Lmax, tid, kreg, ptab, psh);
+        fa_load_v<PAGED>(Vg, rs, tile0 + kFaN, a.Lmax, tid, vreg, ptab, psh);
         // S^T, softmax, P^T . V accumulation
         if (tile0 <= wave_last) {  // some query of this wave sees the tile
             const int64_t sub0 = tile0;
@@ -283,9 +300,13 @@ hipError_t launch_dense_prefill(const AttnArgs &aa, hipStream_t s) {
     FaArgs a{};
     a.Q = aa.Q; a.K = aa.K; a.V = aa.V; a.O = aa.O; a.lse = aa.lse;
     a.Tq = aa.Tq; a.Lmax = aa.Lmax; a.pos0 = aa.pos0; a.H = aa.H; a.Hkv = aa.Hkv;
+    a.ptable = aa.ptable; a.pstride = aa.pstride; a.pshift = aa.pshift;
     const dim3 grid(static_cast<uint32_t>((aa.Tq + kFaQ - 1) / kFaQ),
                     static_cast<uint32_t>(aa.H), static_cast<uint32_t>(aa.B));
-    hipLaunchKernelGGL(fa_prefill_kernel, grid, dim3(256), 0, s, a);
+    if (aa.ptable)
+        hipLaunchKernelGGL(fa_prefill_kernel<true>, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(fa_prefill_kernel<false>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -17,11 +17,13 @@ constexpr int kRowBytes = 272;   // LDS row stride of one pooled key (256 B + 16
 constexpr int kTileBytes = kBT * kRowBytes;
 constexpr int kStageRow = 272;   // LDS row of one query's 64 staged scores (256 B + pad)
 
+template <bool PAGED>
 __device__ __forceinline__ void load_tile(const uint16_t *kbar, int64_t nb_max, int64_t tile,
                                           int bl, int part, uint4 &v0, uint4 &v1, uint4 &v2,
-                                          uint4 &v3) {
+                                          uint4 &v3, const int32_t *ptab, int psh) {
     int64_t bb = tile * kBT + bl;
     bb = bb < nb_max ? bb : nb_max - 1;  // rows past the cache: any valid row, masked later
+    if (PAGED) bb = page_row(ptab, psh, bb);
     const uint4 *src = reinterpret_cast<const uint4 *>(kbar + bb * kIdxDim) + part * 4;
     v0 = src[0];
     v1 = src[1];
@@ -43,16 +45,17 @@ __device__ __forceinline__ void store_tile(unsigned char *buf, int bl, int part,
 // registers while the current one feeds the MFMAs, then written to the other
 // LDS buffer (one barrier per tile).  Each wave stages its 16 x 64 scores in
 // LDS and writes them back as whole 256-byte row segments.
-template <int MODE>
+template <int MODE, bool PAGED>
 __global__ void __launch_bounds__(256)
 index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ kbar,
                      int64_t Tq, int64_t pos0, int64_t nb_max, float *__restrict__ scores,
-                     int64_t ld) {
+                     int64_t ld, PageTable pg) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileBytes + 4 * 16 * kStageRow];
     const int qt = gridDim.x - 1 - blockIdx.x;  // longest rows first
     const int64_t seq = blockIdx.z;
     q_idx += seq * Tq * (kIdxHeads * kIdxDim);
-    kbar += seq * nb_max * kIdxDim;
+    if (!PAGED) kbar += seq * nb_max * kIdxDim;
+    const int32_t *ptab = PAGED ? pg.table + seq * pg.stride : nullptr;
     scores += seq * Tq * ld;
 
     const int64_t t0 = static_cast<int64_t>(qt) * kQT;
@@ -94,7 +97,11 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
     // cooperative tile load: thread -> block tid/4, bytes 64*(tid%4) .. +63
     const int ld_bl = tid >> 2, ld_part = tid & 3;
     uint4 kv0, kv1, kv2, kv3;
-    load_tile(kbar, nb_max, tile_begin, ld_bl, ld_part, kv0, kv1, kv2, kv3);
+    // rows past the valid blocks are clamped (paged: to the ones this tile
+    // of queries sees, whose pages exist)
+    const int64_t nb_rows = PAGED ? nc_hi : nb_max;
+    load_tile<PAGED>(kbar, nb_rows, tile_begin, ld_bl, ld_part, kv0, kv1, kv2, kv3, ptab,
+                     pg.shift);
     store_tile(lds, ld_bl, ld_part, kv0, kv1, kv2, kv3);
 
     for (int64_t tile = tile_begin; tile < tile_end; ++tile) {
@@ -103,7 +110,8 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
         __syncthreads();  // tile ready; the other buffer is free
         // next tile into registers (past the last tile: a clamped re-read of
         // rows nothing will use)
-        load_tile(kbar, nb_max, tile + 1, ld_bl, ld_part, kv0, kv1, kv2, kv3);
+        load_tile<PAGED>(kbar, nb_rows, tile + 1, ld_bl, ld_part, kv0, kv1, kv2, kv3, ptab,
+                         pg.shift);
         const int64_t b0 = tile * kBT;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -149,12 +157,12 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
 // contiguous HBM (4 keys), with the 16-byte chunks of row r stored at slot
 // chunk ^ (r % 16) so that the MFMA B-fragment reads (16 rows, one chunk
 // each) hit distinct banks.  MFMA rows 0..3 are the 4 heads, rows 4..15 zero.
-template <int MODE>
+template <int MODE, bool PAGED>
 __global__ void __launch_bounds__(256)
 index_scores_decode(const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ kbar,
                     const int64_t *__restrict__ seq_len, int64_t nb_max,
                     float *__restrict__ scores, int64_t ld, uint32_t *__restrict__ gmax,
-                    int64_t gld, int nq) {
+                    int64_t gld, int nq, PageTable pg) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[4 * 64 * kIdxDim * 2];
     const int64_t seq = blockIdx.y;
     const int64_t p = seq_len[seq] - nq;
@@ -164,12 +172,27 @@ index_scores_decode(const uint16_t *__restrict__ q_idx, const uint16_t *__restri
     const int64_t w0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * 64;  // first block
     if (w0 >= nc) return;
     unsigned char *tile = lds + wave * (64 * kIdxDim * 2);
-    const uint16_t *kb = kbar + seq * nb_max * kIdxDim;
+    const uint16_t *kb = PAGED ? kbar : kbar + seq * nb_max * kIdxDim;
+    // paged: lane l holds the page of the wave's l-th page of blocks (only
+    // pages of the sequence's complete blocks are read)
+    int32_t mypage = 0;
+    int64_t pg0 = 0;
+    if (PAGED) {
+        pg0 = w0 >> pg.shift;
+        const int64_t pg_last = min(w0 + 63, nc - 1) >> pg.shift;
+        mypage = lane <= pg_last - pg0 ? pg.table[seq * pg.stride + pg0 + lane] : 0;
+    }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const int r = 4 * j + (lane >> 4);
         int64_t blk = w0 + r;
-        blk = blk < nb_max ? blk : nb_max - 1;
+        if (PAGED) {
+            blk = blk < nc ? blk : nc - 1;
+            const int32_t page = __shfl(mypage, static_cast<int>((blk >> pg.shift) - pg0));
+            blk = (static_cast<int64_t>(page) << pg.shift) | (blk & ((int64_t(1) << pg.shift) - 1));
+        } else {
+            blk = blk < nb_max ? blk : nb_max - 1;
+        }
         const uint16_t *src = kb + blk * kIdxDim + 8 * ((lane & 15) ^ (r & 15));
         // (C-style casts: the builtin takes explicit global / LDS address spaces)
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
@@ -216,19 +239,45 @@ index_scores_decode(const uint16_t *__restrict__ q_idx, const uint16_t *__restri
     }
 }
 
+template <int MODE>
+static void launch_decode_scan(dim3 grid, hipStream_t s, const uint16_t *q_idx,
+                               const uint16_t *kbar, const int64_t *seq_len, int64_t nb_max,
+                               float *scores, int64_t ld, uint32_t *gmax, int64_t gld, int nq,
+                               const PageTable &pg) {
+    if (pg.table)
+        hipLaunchKernelGGL((index_scores_decode<MODE, true>), grid, dim3(256), 0, s, q_idx, kbar,
+                           seq_len, nb_max, scores, ld, gmax, gld, nq, pg);
+    else
+        hipLaunchKernelGGL((index_scores_decode<MODE, false>), grid, dim3(256), 0, s, q_idx,
+                           kbar, seq_len, nb_max, scores, ld, gmax, gld, nq, pg);
+}
+
+template <int MODE>
+static void launch_prefill_scores(dim3 grid, hipStream_t s, const uint16_t *q_idx,
+                                  const uint16_t *kbar, int64_t Tq, int64_t pos0, int64_t nb_max,
+                                  float *scores, int64_t ld, const PageTable &pg) {
+    if (pg.table)
+        hipLaunchKernelGGL((index_scores_prefill<MODE, true>), grid, dim3(256), 0, s, q_idx,
+                           kbar, Tq, pos0, nb_max, scores, ld, pg);
+    else
+        hipLaunchKernelGGL((index_scores_prefill<MODE, false>), grid, dim3(256), 0, s, q_idx,
+                           kbar, Tq, pos0, nb_max, scores, ld, pg);
+}
+
 hipError_t launch_index_scores(const uint16_t *q_idx, const uint16_t *kbar, int B, int64_t Tq,
                                int64_t pos0, const int64_t *seq_len, int64_t nb_max, int mode,
                                float *scores, int64_t ld, hipStream_t s, uint32_t *gmax,
-                               int64_t gld) {
+                               int64_t gld, PageTable pg) {
     if (B == 0 || Tq == 0 || nb_max == 0) return hipSuccess;
     if (seq_len) {
         const dim3 grid(static_cast<uint32_t>((nb_max + 255) / 256), static_cast<uint32_t>(B));
+        const int nq = static_cast<int>(Tq);
         if (mode == 0)
-            hipLaunchKernelGGL(index_scores_decode<0>, grid, dim3(256), 0, s, q_idx, kbar,
-                               seq_len, nb_max, scores, ld, gmax, gld, static_cast<int>(Tq));
+            launch_decode_scan<0>(grid, s, q_idx, kbar, seq_len, nb_max, scores, ld, gmax, gld,
+                                  nq, pg);
         else
-            hipLaunchKernelGGL(index_scores_decode<1>, grid, dim3(256), 0, s, q_idx, kbar,
-                               seq_len, nb_max, scores, ld, gmax, gld, static_cast<int>(Tq));
+            launch_decode_scan<1>(grid, s, q_idx, kbar, seq_len, nb_max, scores, ld, gmax, gld,
+                                  nq, pg);
         return hipGetLastError();
     }
     const int64_t n_qt = (Tq + kQT - 1) / kQT;
@@ -238,11 +287,9 @@ hipError_t launch_index_scores(const uint16_t *q_idx, const uint16_t *kbar, int 
     const dim3 grid(static_cast<uint32_t>(n_qt), static_cast<uint32_t>(n_split),
                     static_cast<uint32_t>(B));
     if (mode == 0)
-        hipLaunchKernelGGL(index_scores_prefill<0>, grid, dim3(256), 0, s, q_idx, kbar, Tq,
-                           pos0, nb_max, scores, ld);
+        launch_prefill_scores<0>(grid, s, q_idx, kbar, Tq, pos0, nb_max, scores, ld, pg);
     else
-        hipLaunchKernelGGL(index_scores_prefill<1>, grid, dim3(256), 0, s, q_idx, kbar, Tq,
-                           pos0, nb_max, scores, ld);
+        launch_prefill_scores<1>(grid, s, q_idx, kbar, Tq, pos0, nb_max, scores, ld, pg);
     return hipGetLastError();
 }
 

@@ -42,6 +42,34 @@ int check_attn_shape(int H, int Hkv, int D, int r) {
     return QSA_OK;
 }
 
+// A paged-cache argument: NULL, or a table covering `tokens` per sequence
+// with a supported page size.
+int check_pages(const qsa_pages *pg, int64_t tokens) {
+    if (!pg) return QSA_OK;
+    if (!pg->table) return QSA_ERR_NULL;
+    const int P = pg->page_tokens;
+    if (P < 16 || P > 4096 || (P & (P - 1))) return QSA_ERR_UNSUPPORTED;
+    if (pg->table_stride < (tokens + P - 1) / P) return QSA_ERR_SHAPE;
+    return QSA_OK;
+}
+
+int log2_int(int x) {
+    int s = 0;
+    while ((1 << s) < x) ++s;
+    return s;
+}
+
+// Page tables over token rows (K, V) and over pooled-block rows (kbar).
+PageTable token_pages(const qsa_pages *pg) {
+    return pg ? PageTable{pg->table, pg->table_stride, log2_int(pg->page_tokens)}
+              : PageTable{nullptr, 0, 0};
+}
+
+PageTable block_pages(const qsa_pages *pg) {
+    return pg ? PageTable{pg->table, pg->table_stride, log2_int(pg->page_tokens / kBlock)}
+              : PageTable{nullptr, 0, 0};
+}
+
 }  // namespace
 
 extern "C" {
@@ -94,7 +122,8 @@ int qsa_rope_bf16(const qsa_bf16 *x, qsa_bf16 *y, int64_t T, int nheads, int hea
 
 int qsa_compress_keys(const qsa_bf16 *k, int B, int64_t Tk, int64_t k_seq_stride, int Di, int r,
                       int kbar_mode, const qsa_bf16 *gain, int rope_dim, double theta,
-                      int64_t block0, qsa_bf16 *kbar, int64_t kbar_seq_stride, void *stream) {
+                      int64_t block0, qsa_bf16 *kbar, int64_t kbar_seq_stride,
+                      const qsa_pages *pages, void *stream) {
     if (!k || !kbar) return QSA_ERR_NULL;
     if (B <= 0 || Tk < 0 || Di <= 0 || r <= 0 || block0 < 0) return QSA_ERR_SHAPE;
     if (kbar_mode != QSA_KBAR_MEAN && kbar_mode != QSA_KBAR_RMSNORM) return QSA_ERR_SHAPE;
@@ -105,7 +134,11 @@ int qsa_compress_keys(const qsa_bf16 *k, int B, int64_t Tk, int64_t k_seq_stride
         return QSA_ERR_UNSUPPORTED;
     if (gain && !aligned16(gain)) return QSA_ERR_ALIGN;
     const int64_t nb = Tk / r;
-    if (B > 1 && (k_seq_stride < Tk * Di || kbar_seq_stride < nb * Di)) return QSA_ERR_SHAPE;
+    if (B > 1 && (k_seq_stride < Tk * Di || (!pages && kbar_seq_stride < nb * Di)))
+        return QSA_ERR_SHAPE;
+    if (pages && r != kBlock) return QSA_ERR_UNSUPPORTED;
+    int st = check_pages(pages, (block0 + nb) * r);
+    if (st != QSA_OK) return st;
     if (k_seq_stride % 8 || kbar_seq_stride % 8) return QSA_ERR_ALIGN;
     if (static_cast<int64_t>(B) * nb * (Di / 8) / 256 > kI32Max) return QSA_ERR_OVERFLOW;
     if (!aligned16(k) || !aligned16(kbar)) return QSA_ERR_ALIGN;
@@ -114,7 +147,8 @@ int qsa_compress_keys(const qsa_bf16 *k, int B, int64_t Tk, int64_t k_seq_stride
         inv_freq[j] = pow(theta, -2.0 * static_cast<double>(j) / static_cast<double>(rope_dim));
     return launch_status(launch_compress(k, B, Tk, k_seq_stride, Di, r, kbar_mode, gain,
                                          rope_dim, rope_dim ? inv_freq : nullptr, block0, kbar,
-                                         kbar_seq_stride, as_stream(stream)));
+                                         kbar_seq_stride, as_stream(stream),
+                                         block_pages(pages)));
 }
 
 static int check_index_args(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t Tq,
@@ -134,14 +168,18 @@ static int check_index_args(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, 
 
 int qsa_index_scores(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t Tq,
                      int64_t pos0, const int64_t *seq_len, int64_t nb_max, int Hi, int Di, int r,
-                     int score_mode, float *scores, int64_t ld, void *stream) {
+                     int score_mode, float *scores, int64_t ld, const qsa_pages *pages,
+                     void *stream) {
     int st = check_index_args(q_idx, kbar, B, Tq, pos0, seq_len, nb_max, Hi, Di, r, score_mode);
     if (st != QSA_OK) return st;
     if (!scores) return QSA_ERR_NULL;
     if (ld < nb_max || ld % 4 != 0) return QSA_ERR_SHAPE;
     if (!aligned16(scores)) return QSA_ERR_ALIGN;
+    st = check_pages(pages, nb_max * r);
+    if (st != QSA_OK) return st;
     return launch_status(launch_index_scores(q_idx, kbar, B, Tq, pos0, seq_len, nb_max,
-                                             score_mode, scores, ld, as_stream(stream)));
+                                             score_mode, scores, ld, as_stream(stream), nullptr,
+                                             0, block_pages(pages)));
 }
 
 size_t qsa_topk_workspace_bytes(int B, int64_t Tq, int64_t nb_max, int K) {
@@ -201,9 +239,12 @@ size_t qsa_select_workspace_bytes(int B, int64_t Tq, int64_t nb_max, int K) {
 int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t Tq,
                       int64_t pos0, const int64_t *seq_len, int64_t nb_max, int Hi, int Di,
                       int r, int score_mode, int K, int32_t *blk_idx, int32_t *n_sel, void *ws,
-                      size_t ws_bytes, void *stream) {
+                      size_t ws_bytes, const qsa_pages *pages, void *stream) {
     int st = check_index_args(q_idx, kbar, B, Tq, pos0, seq_len, nb_max, Hi, Di, r, score_mode);
     if (st != QSA_OK) return st;
+    st = check_pages(pages, nb_max * r);
+    if (st != QSA_OK) return st;
+    const PageTable pg = block_pages(pages);
     if (!blk_idx || !n_sel) return QSA_ERR_NULL;
     if (K <= 0) return QSA_ERR_SHAPE;
     if (K > kMaxBudget) return QSA_ERR_UNSUPPORTED;
@@ -224,26 +265,29 @@ int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_
         // top-K filter takes its floor from (start of the top-K workspace)
         const DecListLayout l = dec_list_layout(B, nb_max, K);
         hipError_t e = launch_index_scores(q_idx, kbar, B, Tq, pos0, seq_len, nb_max, score_mode,
-                                           sc, ld, s, static_cast<uint32_t *>(tws), l.gld);
+                                           sc, ld, s, static_cast<uint32_t *>(tws), l.gld, pg);
         if (e != hipSuccess) return QSA_ERR_LAUNCH;
         return launch_status(launch_topk_dec_lists(sc, B, static_cast<int>(Tq), ld, seq_len,
                                                    nb_max, r, K, blk_idx, n_sel, tws, s));
     }
     if (seq_len || Tq == 1) {
         hipError_t e = launch_index_scores(q_idx, kbar, B, Tq, pos0, seq_len, nb_max, score_mode,
-                                           sc, ld, s);
+                                           sc, ld, s, nullptr, 0, pg);
         if (e != hipSuccess) return QSA_ERR_LAUNCH;
         return launch_status(launch_topk(sc, B, Tq, ld, pos0, seq_len, nb_max, r, K, blk_idx,
                                          n_sel, tws, s));
     }
     for (int b = 0; b < B; ++b) {
         const qsa_bf16 *qb = q_idx + static_cast<int64_t>(b) * Tq * (kIdxHeads * kIdxDim);
-        const qsa_bf16 *kb = kbar + static_cast<int64_t>(b) * nb_max * kIdxDim;
+        // one sequence at a time: its own rows of the cache or of the page table
+        const qsa_bf16 *kb = pg.table ? kbar : kbar + static_cast<int64_t>(b) * nb_max * kIdxDim;
+        const PageTable pgb{pg.table ? pg.table + b * pg.stride : nullptr, pg.stride, pg.shift};
         const int64_t row0 = static_cast<int64_t>(b) * Tq;
         for (int64_t q0 = 0; q0 < Tq; q0 += chunk) {
             const int64_t len = Tq - q0 < chunk ? Tq - q0 : chunk;
             hipError_t e = launch_index_scores(qb + q0 * (kIdxHeads * kIdxDim), kb, 1, len,
-                                               pos0 + q0, nullptr, nb_max, score_mode, sc, ld, s);
+                                               pos0 + q0, nullptr, nb_max, score_mode, sc, ld, s,
+                                               nullptr, 0, pgb);
             if (e != hipSuccess) return QSA_ERR_LAUNCH;
             e = launch_topk(sc, 1, len, ld, pos0 + q0, nullptr, nb_max, r, K,
                             blk_idx + (row0 + q0) * K, n_sel + row0 + q0, tws, s);
@@ -256,7 +300,7 @@ int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_
 int qsa_sparse_attn_prefill(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
                             const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq, int64_t Tk,
                             int64_t pos0, int H, int Hkv, int D, int r, int Kbudget, float *O,
-                            float *lse, void *stream) {
+                            float *lse, const qsa_pages *pages, void *stream) {
     if (!Q || !K || !V || !blk_idx || !n_sel || !O) return QSA_ERR_NULL;
     if (Tq < 0 || Tk < 0 || pos0 < 0 || Kbudget <= 0) return QSA_ERR_SHAPE;
     int st = check_attn_shape(H, Hkv, D, r);
@@ -269,6 +313,10 @@ int qsa_sparse_attn_prefill(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16
     a.Q = Q; a.K = K; a.V = V; a.blk_idx = blk_idx; a.n_sel = n_sel; a.seq_len = nullptr;
     a.O = O; a.lse = lse; a.part = nullptr;
     a.Tq = Tq; a.Lmax = Tk; a.pos0 = pos0; a.B = 1; a.H = H; a.Hkv = Hkv; a.Kbudget = Kbudget;
+    st = check_pages(pages, Tk);
+    if (st != QSA_OK) return st;
+    const PageTable pt = token_pages(pages);
+    a.ptable = pt.table; a.pstride = pt.stride; a.pshift = pt.shift;
     return launch_status(launch_sparse_prefill(a, as_stream(stream)));
 }
 
@@ -291,7 +339,8 @@ size_t qsa_decode_workspace_bytes(int B, int Tq, int H, int Hkv, int D, int Kbud
 int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16 *Vc,
                            const int64_t *seq_len, const int32_t *blk_idx, const int32_t *n_sel,
                            int B, int Tq, int64_t Lmax, int H, int Hkv, int D, int r, int Kbudget,
-                           float *O, float *lse, void *ws, size_t ws_bytes, void *stream) {
+                           float *O, float *lse, void *ws, size_t ws_bytes,
+                           const qsa_pages *pages, void *stream) {
     if (!q || !Kc || !Vc || !seq_len || !blk_idx || !n_sel || !O) return QSA_ERR_NULL;
     if (B <= 0 || Lmax < 0 || Kbudget <= 0) return QSA_ERR_SHAPE;
     if (Tq < 1 || Tq > kMaxNextN) return QSA_ERR_SHAPE;
@@ -308,6 +357,10 @@ int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16
     a.Q = q; a.K = Kc; a.V = Vc; a.blk_idx = blk_idx; a.n_sel = n_sel; a.seq_len = seq_len;
     a.O = O; a.lse = lse; a.part = static_cast<float *>(ws);
     a.Tq = Tq; a.Lmax = Lmax; a.pos0 = 0; a.B = B; a.H = H; a.Hkv = Hkv; a.Kbudget = Kbudget;
+    st = check_pages(pages, Lmax);
+    if (st != QSA_OK) return st;
+    const PageTable pt = token_pages(pages);
+    a.ptable = pt.table; a.pstride = pt.stride; a.pshift = pt.shift;
     return launch_status(launch_attn_decode(a, nsplit, as_stream(stream)));
 }
 
@@ -321,7 +374,8 @@ size_t dense_attn_workspace_bytes(int B, int64_t Tq, int64_t Lmax, int H, int Hk
 
 int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, int64_t Tq,
                int64_t Lmax, int64_t pos0, const int64_t *seq_len, int H, int Hkv, int D,
-               float *O, float *lse, void *ws, size_t ws_bytes, void *stream) {
+               float *O, float *lse, void *ws, size_t ws_bytes, const qsa_pages *pages,
+               void *stream) {
     if (!Q || !K || !V || !O) return QSA_ERR_NULL;
     if (B <= 0 || Tq < 0 || Lmax < 0 || pos0 < 0) return QSA_ERR_SHAPE;
     int st = check_attn_shape(H, Hkv, D, kBlock);
@@ -334,6 +388,10 @@ int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, i
     a.Q = Q; a.K = K; a.V = V; a.blk_idx = nullptr; a.n_sel = nullptr; a.seq_len = seq_len;
     a.O = O; a.lse = lse; a.part = static_cast<float *>(ws);
     a.Tq = Tq; a.Lmax = Lmax; a.pos0 = pos0; a.B = B; a.H = H; a.Hkv = Hkv; a.Kbudget = 0;
+    st = check_pages(pages, Lmax);
+    if (st != QSA_OK) return st;
+    const PageTable pt = token_pages(pages);
+    a.ptable = pt.table; a.pstride = pt.stride; a.pshift = pt.shift;
     hipStream_t s = as_stream(stream);
     if (seq_len) {
         int nsplit = 0;

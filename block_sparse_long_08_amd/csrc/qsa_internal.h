@@ -61,6 +61,17 @@ __device__ __forceinline__ float combine_heads(f32x4 acc) {
     return s;
 }
 
+// Page table of paged caches: row i of sequence b lives at row
+// (table[b * stride + (i >> shift)] << shift) + i mod 2^shift of the pool.
+// Rows are tokens (K/V, shift = log2 of the page's tokens) or pooled blocks
+// (kbar, shift = log2 of the page's blocks).  table == nullptr: contiguous
+// per-sequence caches.
+struct PageTable {
+    const int32_t *table;
+    int64_t stride;
+    int shift;
+};
+
 // ------------------------------------------------------------ launchers --
 // Decode form (seq_len given): T = B * nq rows, row t at position
 // seq_len[t / nq] - nq + t % nq.
@@ -70,18 +81,24 @@ hipError_t launch_rope(const uint16_t *x, uint16_t *y, int64_t T, int nheads, in
 
 // gain: RMSNorm gain (mode 1) or nullptr; rope_dim > 0 (a power of two)
 // rotates the pooled keys at positions r * (block0 + block) with inv_freq.
+// pg.table set: kbar is a page pool of pooled blocks; block block0 + j of
+// sequence b goes to its page row.
 hipError_t launch_compress(const uint16_t *k, int B, int64_t Tk, int64_t k_seq_stride, int Di,
                            int r, int mode, const uint16_t *gain, int rope_dim,
                            const double *inv_freq, int64_t block0, uint16_t *kbar,
-                           int64_t kbar_seq_stride, hipStream_t s);
+                           int64_t kbar_seq_stride, hipStream_t s,
+                           PageTable pg = PageTable{nullptr, 0, 0});
 
 // Decode form (seq_len given): when gmax is set, also writes the largest
 // score key of every group of 64 consecutive blocks, gmax[b * gld + g] for
 // the groups holding complete blocks.
+// pg.table set: kbar is a page pool of pooled blocks (pg.shift = log2 of the
+// blocks per page); only blocks a query sees are read.
 hipError_t launch_index_scores(const uint16_t *q_idx, const uint16_t *kbar, int B, int64_t Tq,
                                int64_t pos0, const int64_t *seq_len, int64_t nb_max, int mode,
                                float *scores, int64_t ld, hipStream_t s,
-                               uint32_t *gmax = nullptr, int64_t gld = 0);
+                               uint32_t *gmax = nullptr, int64_t gld = 0,
+                               PageTable pg = PageTable{nullptr, 0, 0});
 
 // Top-K passes for rows of up to nmax candidates: either one streaming pass
 // per row, or npass reduction passes (segment lengths seg[i], entries[i]
@@ -135,7 +152,18 @@ struct AttnArgs {
     float *part;             // split partials (decode), or nullptr
     int64_t Tq, Lmax, pos0;
     int B, H, Hkv, Kbudget;
+    // Paged caches (ptable set): K, V are page pools [pages * 2^pshift][Hkv][D]
+    // and token t of sequence b is row (ptable[b * pstride + (t >> pshift)]
+    // << pshift) + t mod 2^pshift.
+    const int32_t *ptable;
+    int64_t pstride;
+    int pshift;
 };
+
+// Row of token t in a page pool (tab: the sequence's page-table row).
+__device__ __forceinline__ int64_t page_row(const int32_t *tab, int sh, int64_t t) {
+    return (static_cast<int64_t>(tab[t >> sh]) << sh) | (t & ((int64_t(1) << sh) - 1));
+}
 
 hipError_t launch_sparse_prefill(const AttnArgs &a, hipStream_t s);
 // Decode: split-K workgroups per (split, KV head, column tile, sequence); a

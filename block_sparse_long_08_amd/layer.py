@@ -34,8 +34,9 @@ class QSAPrefill:
     def __init__(self, Tq: int, pos0: int = 0, H: int = 24, Hkv: int = 2, D: int = 256,
                  budget: int = 512, score_mode: int = SCORE_MAXHEAD, kbar_mode: int = KBAR_MEAN,
                  theta: float = 1e7, rope_dim: int = 64, fresh: bool = True,
-                 idx_rope_dim: int = 0, kbar_gain=None, device="cuda"):
+                 idx_rope_dim: int = 0, kbar_gain=None, pages=None, device="cuda"):
         self.Tq, self.pos0, self.H, self.Hkv, self.D = Tq, pos0, H, Hkv, D
+        self.pages = pages  # paged caches (fresh=False): K, V and kbar are page pools
         self.Tk = pos0 + Tq
         self.budget, self.score_mode, self.kbar_mode = budget, score_mode, kbar_mode
         self.theta, self.rope_dim, self.fresh = theta, rope_dim, fresh
@@ -44,7 +45,9 @@ class QSAPrefill:
         dev = torch.device(device)
         self.Qr = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=dev)
         self.Kr = torch.empty((self.Tk, Hkv, D), dtype=torch.bfloat16, device=dev) if fresh else None
-        self.kbar = torch.empty((max(self.nb, 1), DI), dtype=torch.bfloat16, device=dev) if fresh else None
+        self.kbar = (torch.empty((max(self.nb, 1), DI), dtype=torch.bfloat16, device=dev)
+                     if fresh else None)
+        assert pages is None or not fresh, "paged caches hold earlier context: fresh=False"
         self.blk_idx = torch.empty((Tq, budget), dtype=torch.int32, device=dev)
         self.n_sel = torch.empty((Tq,), dtype=torch.int32, device=dev)
         self.O = torch.empty((Tq, H, D), dtype=torch.float32, device=dev)
@@ -64,8 +67,9 @@ class QSAPrefill:
             return self.Kr, self.kbar
         # pool the chunk's own keys into the cache (blocks pos0/r ..)
         b0 = self.pos0 // R
+        dst = kbar if self.pages is not None else kbar[b0:]
         qsa_compress_keys(ki[self.pos0:], 1, self.Tq, self.Tq * DI, DI, R, self.kbar_mode,
-                          kbar[b0:], self.Tq // R * DI, block0=b0, **pool)
+                          dst, self.Tq // R * DI, block0=b0, pages=self.pages, **pool)
         return K, kbar
 
     def rope_indexer(self, qi):
@@ -79,12 +83,12 @@ class QSAPrefill:
     def select(self, qi, kbar):
         qsa_select_blocks(qi, kbar, 1, self.Tq, self.pos0, None, self.nb, HI, DI, R,
                           self.score_mode, self.budget, self.blk_idx, self.n_sel, self.ws,
-                          self.ws_bytes)
+                          self.ws_bytes, pages=self.pages)
 
     def attend(self, Kr, V):
         qsa_sparse_attn_prefill(self.Qr, Kr, V, self.blk_idx, self.n_sel, self.Tq, self.Tk,
                                 self.pos0, self.H, self.Hkv, self.D, R, self.budget, self.O,
-                                self.lse)
+                                self.lse, pages=self.pages)
 
     def __call__(self, Q, K, V, qi, ki, kbar=None):
         Kr, kb = self.rope_and_pool(Q, K, ki, kbar)
@@ -103,8 +107,9 @@ class QSADecode:
     def __init__(self, B: int, Lmax: int, H: int = 24, Hkv: int = 2, D: int = 256,
                  budget: int = 512, score_mode: int = SCORE_MAXHEAD, kbar_mode: int = KBAR_MEAN,
                  theta: float = 1e7, rope_dim: int = 64, next_n: int = 1,
-                 idx_rope_dim: int = 0, kbar_gain=None, device="cuda"):
+                 idx_rope_dim: int = 0, kbar_gain=None, pages=None, device="cuda"):
         self.B, self.Lmax, self.H, self.Hkv, self.D = B, Lmax, H, Hkv, D
+        self.pages = pages  # paged caches: Kc, Vc and kbar are page pools
         self.budget, self.score_mode, self.kbar_mode = budget, score_mode, kbar_mode
         self.theta, self.rope_dim, self.next_n = theta, rope_dim, next_n
         self.idx_rope_dim, self.kbar_gain = idx_rope_dim, kbar_gain
@@ -126,9 +131,10 @@ class QSADecode:
     def pool_keys(self, ki, kbar, block0: int = 0):
         """Pool indexer keys ki [B, T, DI] (T a multiple of r) into kbar[:, block0 ..]."""
         T = ki.shape[1]
-        qsa_compress_keys(ki, self.B, T, T * DI, DI, R, self.kbar_mode, kbar[:, block0],
+        dst = kbar if self.pages is not None else kbar[:, block0]
+        qsa_compress_keys(ki, self.B, T, T * DI, DI, R, self.kbar_mode, dst,
                           self.nb_max * DI, gain=self.kbar_gain, rope_dim=self.idx_rope_dim,
-                          theta=self.theta, block0=block0)
+                          theta=self.theta, block0=block0, pages=self.pages)
 
     def append_block(self, ki_tail, kbar, block: int):
         """Pool the r indexer keys ki_tail [B, r, DI] into kbar[:, block]."""
@@ -147,10 +153,10 @@ class QSADecode:
             qi = self.qir
         qsa_select_blocks(qi, kbar, self.B, n, 0, seq_len, self.nb_max, HI, DI, R,
                           self.score_mode, self.budget, self.blk_idx, self.n_sel, self.sel_ws,
-                          self.sel_ws_bytes)
+                          self.sel_ws_bytes, pages=self.pages)
         qsa_sparse_attn_decode(self.qr, Kc, Vc, seq_len, self.blk_idx, self.n_sel, self.B, n,
                                self.Lmax, self.H, self.Hkv, self.D, R, self.budget, self.O,
-                               self.lse, self.dec_ws, self.dec_ws_bytes)
+                               self.lse, self.dec_ws, self.dec_ws_bytes, pages=self.pages)
         if n == 1:
             return self.O[:, 0], self.lse[:, 0]
         return self.O, self.lse

@@ -83,6 +83,26 @@ typedef enum { QSA_SCORE_MAXHEAD = 0, QSA_SCORE_RELUSUM = 1 } qsa_score_mode;
  * Either result is rounded to bf16, nearest even. */
 typedef enum { QSA_KBAR_MEAN = 0, QSA_KBAR_RMSNORM = 1 } qsa_kbar_mode;
 
+/* Paged caches (chlience "Result 2": the report's kernel measurement uses a
+ * paged GQA dense baseline).  The cache of sequence b is cut into pages of page_tokens
+ * tokens; table[b * table_stride + i] is the pool index of its i-th page.
+ * With a qsa_pages argument the cache tensors of a call are page pools:
+ *   K, V:  [n_pages * page_tokens][Hkv][D]     (token rows)
+ *   kbar:  [n_pages * page_tokens / r][Di]     (pooled-block rows)
+ * so token t of sequence b is row table[b*table_stride + t / page_tokens] *
+ * page_tokens + t mod page_tokens, and pooled block j is row
+ * table[b*table_stride + j*r / page_tokens] * (page_tokens / r) +
+ * j mod (page_tokens / r).  table is a DEVICE int32 array; page_tokens a
+ * power of two in 16 .. 4096; table_stride must cover the longest cache of
+ * the call.  The kernels read the pages of the tokens (blocks) their queries
+ * see, and only those: their table entries must be valid pool indices.
+ * A NULL qsa_pages pointer selects the contiguous layouts given per call. */
+typedef struct {
+    const int32_t *table;
+    int64_t table_stride;
+    int page_tokens;
+} qsa_pages;
+
 /* Human-readable name of a status code (static string). */
 const char *qsa_status_string(int status);
 
@@ -124,7 +144,8 @@ int qsa_rope_bf16(const qsa_bf16 *x, qsa_bf16 *y, int64_t T, int nheads, int hea
  * in 16 .. min(Di, 128). */
 int qsa_compress_keys(const qsa_bf16 *k, int B, int64_t Tk, int64_t k_seq_stride, int Di, int r,
                       int kbar_mode, const qsa_bf16 *gain, int rope_dim, double theta,
-                      int64_t block0, qsa_bf16 *kbar, int64_t kbar_seq_stride, void *stream);
+                      int64_t block0, qsa_bf16 *kbar, int64_t kbar_seq_stride,
+                      const qsa_pages *pages, void *stream);
 
 /* ---- A3: indexer block scores (chlience section 6, I_ib; ai.info
  * contribution 3: MQA indexer, 4 query heads and one shared key head).
@@ -137,7 +158,8 @@ int qsa_compress_keys(const qsa_bf16 *k, int B, int64_t Tk, int64_t k_seq_stride
  * Supported: Hi = 4, Di = 128, r = 4, ld >= nb_max, ld % 4 == 0. */
 int qsa_index_scores(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t Tq,
                      int64_t pos0, const int64_t *seq_len, int64_t nb_max, int Hi, int Di, int r,
-                     int score_mode, float *scores, int64_t ld, void *stream);
+                     int score_mode, float *scores, int64_t ld, const qsa_pages *pages,
+                     void *stream);
 
 /* ---- A4: per-query top-K block selection (chlience section 6: at most 512
  * complete blocks per query; djimit pillar 2: up to 512 full blocks).
@@ -170,7 +192,7 @@ size_t qsa_select_workspace_bytes(int B, int64_t Tq, int64_t nb_max, int K);
 int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_t Tq,
                       int64_t pos0, const int64_t *seq_len, int64_t nb_max, int Hi, int Di,
                       int r, int score_mode, int K, int32_t *blk_idx, int32_t *n_sel, void *ws,
-                      size_t ws_bytes, void *stream);
+                      size_t ws_bytes, const qsa_pages *pages, void *stream);
 
 /* ---- A5 + A6: sparse attention, prefill (chlience section 6: the selected
  * blocks expand to token indices for the core attention; the incomplete
@@ -184,7 +206,7 @@ int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_
 int qsa_sparse_attn_prefill(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
                             const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq, int64_t Tk,
                             int64_t pos0, int H, int Hkv, int D, int r, int Kbudget, float *O,
-                            float *lse, void *stream);
+                            float *lse, const qsa_pages *pages, void *stream);
 
 /* ---- A7: sparse attention, decode: the Tq newest queries of each sequence
  * (Tq = 1, or next_n speculative queries sharing one selection; see the
@@ -201,7 +223,7 @@ int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16
                            const int64_t *seq_len, const int32_t *blk_idx, const int32_t *n_sel,
                            int B, int Tq, int64_t Lmax, int H, int Hkv, int D, int r,
                            int Kbudget, float *O, float *lse, void *ws, size_t ws_bytes,
-                           void *stream);
+                           const qsa_pages *pages, void *stream);
 
 /* ---- A8: dense causal attention (the pages' baseline in the chlience
  * Result 2 kernel measurement).
@@ -218,7 +240,8 @@ int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16
 size_t dense_attn_workspace_bytes(int B, int64_t Tq, int64_t Lmax, int H, int Hkv, int D);
 int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, int64_t Tq,
                int64_t Lmax, int64_t pos0, const int64_t *seq_len, int H, int Hkv, int D,
-               float *O, float *lse, void *ws, size_t ws_bytes, void *stream);
+               float *O, float *lse, void *ws, size_t ws_bytes, const qsa_pages *pages,
+               void *stream);
 
 #ifdef __cplusplus
 }

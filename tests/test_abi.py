@@ -90,9 +90,10 @@ def test_rope_validation(lib):
 
 
 def compress(lib, k=P, B=1, Tk=16, ks=16 * 128, Di=128, r=4, mode=0, kb=P, kbs=4 * 128,
-             gain=None, rope_dim=0, theta=1e7, block0=0):
+             gain=None, rope_dim=0, theta=1e7, block0=0, pages=None):
     return lib.qsa_compress_keys(vp(k), B, I64(Tk), I64(ks), Di, r, mode, gain, rope_dim,
-                                 ctypes.c_double(theta), I64(block0), vp(kb), I64(kbs), None)
+                                 ctypes.c_double(theta), I64(block0), vp(kb), I64(kbs), pages,
+                                 None)
 
 
 def test_compress_validation(lib):
@@ -112,9 +113,9 @@ def test_compress_validation(lib):
 
 
 def scores(lib, q=P, kb=P, B=1, Tq=8, pos0=0, sl=None, nb=4, Hi=4, Di=128, r=4, mode=0, out=P,
-           ld=4):
+           ld=4, pages=None):
     return lib.qsa_index_scores(vp(q), vp(kb), B, I64(Tq), I64(pos0), sl, I64(nb), Hi, Di, r,
-                                mode, vp(out), I64(ld), None)
+                                mode, vp(out), I64(ld), pages, None)
 
 
 def test_index_scores_validation(lib):
@@ -156,26 +157,28 @@ def test_select_validation(lib):
     need = lib.qsa_select_workspace_bytes(1, I64(131072), I64(32768), 512)
     assert (1 << 29) <= need <= (1 << 30) + (1 << 20)
     st = lib.qsa_select_blocks(vp(P), vp(P), 1, I64(131072), I64(0), None, I64(32768), 4, 128, 4,
-                               0, 512, vp(P), vp(P), vp(P), ctypes.c_size_t(need - 1), None)
+                               0, 512, vp(P), vp(P), vp(P), ctypes.c_size_t(need - 1), None,
+                               None)
     assert st == WORKSPACE
     # decode form keeps one score row per sequence
     need = lib.qsa_select_workspace_bytes(32, I64(1), I64(65536), 512)
     assert need >= 32 * 65536 * 4
     st = lib.qsa_select_blocks(vp(P), vp(P), 32, I64(1), I64(0), vp(P), I64(65536), 4, 128, 4, 0,
-                               512, vp(P), vp(P), vp(P), ctypes.c_size_t(16), None)
+                               512, vp(P), vp(P), vp(P), ctypes.c_size_t(16), None, None)
     assert st == WORKSPACE
     st = lib.qsa_select_blocks(vp(P), vp(P), 1, I64(1000), I64(0), None, I64(250), 4, 128, 4, 0,
-                               64, vp(P), vp(0), None, ctypes.c_size_t(0), None)
+                               64, vp(P), vp(0), None, ctypes.c_size_t(0), None, None)
     assert st == NULL
     st = lib.qsa_select_blocks(vp(P), vp(P), 1, I64(1000), I64(0), None, I64(250), 4, 128, 4, 0,
-                               4096, vp(P), vp(P), None, ctypes.c_size_t(0), None)
+                               4096, vp(P), vp(P), None, ctypes.c_size_t(0), None, None)
     assert st == UNSUP
 
 
 def sparse_prefill(lib, Q=P, Kt=P, V=P, blk=P, ns=P, Tq=8, Tk=8, pos0=0, H=24, Hkv=2, D=256, r=4,
-                   Kb=4, O=P):
+                   Kb=4, O=P, pages=None):
     return lib.qsa_sparse_attn_prefill(vp(Q), vp(Kt), vp(V), vp(blk), vp(ns), I64(Tq), I64(Tk),
-                                       I64(pos0), H, Hkv, D, r, Kb, vp(O), None, None)
+                                       I64(pos0), H, Hkv, D, r, Kb, vp(O), None, pages,
+                                       None)
 
 
 def test_sparse_prefill_validation(lib):
@@ -201,29 +204,60 @@ def test_decode_validation(lib):
     assert lib.qsa_decode_workspace_bytes(4, 17, 24, 2, 256, 512) == 0
     args = [vp(P)] * 6
     st = lib.qsa_sparse_attn_decode(*args, 32, 1, I64(1024), 24, 2, 256, 4, 512, vp(P), None,
-                                    vp(P), ctypes.c_size_t(need - 1), None)
+                                    vp(P), ctypes.c_size_t(need - 1), None, None)
     assert st == WORKSPACE
     st = lib.qsa_sparse_attn_decode(vp(P), vp(P), vp(P), None, vp(P), vp(P), 32, 1, I64(1024), 24,
-                                    2, 256, 4, 512, vp(P), None, vp(P), ctypes.c_size_t(need), None)
+                                    2, 256, 4, 512, vp(P), None, vp(P), ctypes.c_size_t(need), None,
+                                    None)
     assert st == NULL
     for tq in (0, 17):
         st = lib.qsa_sparse_attn_decode(*args, 32, tq, I64(1024), 24, 2, 256, 4, 512, vp(P), None,
-                                        vp(P), ctypes.c_size_t(1 << 30), None)
+                                        vp(P), ctypes.c_size_t(1 << 30), None, None)
         assert st == SHAPE
 
 
 def test_dense_validation(lib):
     st = lib.dense_attn(vp(P), vp(P), vp(P), 1, I64(16), I64(15), I64(0), None, 24, 2, 256,
-                        vp(P), None, None, ctypes.c_size_t(0), None)
+                        vp(P), None, None, ctypes.c_size_t(0), None, None)
     assert st == SHAPE                                   # pos0 + Tq > Lmax
     st = lib.dense_attn(vp(P), vp(P), vp(P), 1, I64(17), I64(16), I64(0), vp(P), 24, 2, 256,
-                        vp(P), None, None, ctypes.c_size_t(0), None)
+                        vp(P), None, None, ctypes.c_size_t(0), None, None)
     assert st == SHAPE                                   # decode form: at most 16 queries
     st = lib.dense_attn(vp(P), vp(P), vp(P), 1, I64(4), I64(16), I64(0), vp(P), 24, 2, 256,
-                        vp(P), None, None, ctypes.c_size_t(0), None)
+                        vp(P), None, None, ctypes.c_size_t(0), None, None)
     assert st == WORKSPACE                               # 4 speculative queries need records
     lib.dense_attn_workspace_bytes.restype = ctypes.c_size_t
     need = lib.dense_attn_workspace_bytes(4, I64(1), I64(1 << 20), 24, 2, 256)
     st = lib.dense_attn(vp(P), vp(P), vp(P), 4, I64(1), I64(1 << 20), I64(0), vp(P), 24, 2, 256,
-                        vp(P), None, vp(P), ctypes.c_size_t(need - 16), None)
+                        vp(P), None, vp(P), ctypes.c_size_t(need - 16), None, None)
     assert st == WORKSPACE
+
+
+class Pages(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_void_p), ("table_stride", ctypes.c_int64),
+                ("page_tokens", ctypes.c_int)]
+
+
+def pages(table=P, stride=64, page_tokens=64):
+    return ctypes.byref(Pages(table, stride, page_tokens))
+
+
+def test_pages_validation(lib):
+    """Paged caches: a table, a power-of-two page of 16 .. 4096 tokens, and a
+    table row that covers the call's longest cache."""
+    assert sparse_prefill(lib, pages=pages(table=None)) == NULL
+    assert sparse_prefill(lib, pages=pages(page_tokens=48)) == UNSUP
+    assert sparse_prefill(lib, pages=pages(page_tokens=8)) == UNSUP
+    assert sparse_prefill(lib, pages=pages(page_tokens=8192)) == UNSUP
+    assert sparse_prefill(lib, Tk=8, Tq=8, pages=pages(stride=0)) == SHAPE
+    assert compress(lib, Tk=4096, ks=4096 * 128, pages=pages(stride=63, page_tokens=64)) == SHAPE
+    assert compress(lib, Tk=16, block0=100, pages=pages(stride=6, page_tokens=64)) == SHAPE
+    assert scores(lib, nb=1024, ld=1024, pages=pages(stride=63, page_tokens=64)) == SHAPE
+    args = [vp(P)] * 6
+    st = lib.qsa_sparse_attn_decode(*args, 32, 1, I64(1 << 20), 24, 2, 256, 4, 512, vp(P), None,
+                                    vp(P), ctypes.c_size_t(1 << 30), pages(stride=100), None)
+    assert st == SHAPE
+    st = lib.dense_attn(vp(P), vp(P), vp(P), 1, I64(8), I64(4096), I64(0), None, 24, 2, 256,
+                        vp(P), None, None, ctypes.c_size_t(0), pages(stride=1, page_tokens=64),
+                        None)
+    assert st == SHAPE
