@@ -45,6 +45,8 @@ WORKLOADS = {
     "prefill_32k": (32768, 0, 512, 0),
     "prefill_128k": (131072, 0, 512, 64),
     "prefill_1m_chunk": (8192, 1048576 - 8192, 512, 64),
+    # the report's prefill condition: 16K-token chunks over a paged cache
+    "prefill_1m_chunk16k": (16384, 1048576 - 16384, 512, 64),
 }
 DECODES = {
     "decode_256k_b32": (32, 262144, 512, 0),
@@ -53,6 +55,8 @@ DECODES = {
 # speculative decode with index reuse timed on the same caches (the pages'
 # decode condition: batch 4, next_n = 4)
 DECODE_NEXT_N = {"decode_1m_b4": 4}
+# paged-cache variant timed on the same caches (page size in tokens)
+DECODE_PAGED = {"decode_1m_b4": 64}
 
 
 def log(msg):
@@ -103,7 +107,27 @@ class StageTimer:
         return {n: float(np.mean(v)) for n, v in out.items()}
 
 
-def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None):
+def page_pool(cache, P, perm):
+    """Contiguous per-sequence rows [B, L, ...] -> a page pool whose page
+    perm[b * (L / P) + i] holds rows i*P .. of sequence b (device copy)."""
+    import torch
+    B, L = cache.shape[:2]
+    rows = cache.reshape(B * (L // P), -1)
+    pool = torch.empty_like(rows)
+    pool.index_copy_(0, perm, rows)
+    return pool.view((B * L,) + tuple(cache.shape[2:]))
+
+
+def page_table(B, L, P, seed):
+    """A random assignment of the B * L / P pages of B sequences to a pool:
+    (table [B, L/P] int32 on the device, the permutation as int64 indices)."""
+    import torch
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(B * (L // P), generator=g)
+    return perm.view(B, L // P).to(torch.int32).cuda(), perm.cuda()
+
+
+def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, page_tokens=0):
     import torch
     import block_sparse_long_08_amd as qsa
     Tq, pos0, budget, nd = WORKLOADS[name]
@@ -112,12 +136,24 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None):
     Q, K, V, qi, ki = map(to_dev, (x.Q, x.K, x.V, x.qi, x.ki))
     Tk = pos0 + Tq
     kbar = None
-    if not fresh:
+    pages = None
+    if page_tokens:
+        # the cache in randomly permuted pages (setup, untimed)
+        assert not fresh and Tk % page_tokens == 0
+        table, perm = page_table(1, Tk, page_tokens, seed=1)
+        pages = qsa.Pages(table, page_tokens)
+        K = page_pool(K.view(1, Tk, 2, 256), page_tokens, perm)
+        V = page_pool(V.view(1, Tk, 2, 256), page_tokens, perm)
+        kbar = torch.empty((Tk // 4, 128), dtype=torch.bfloat16, device="cuda")
+        qsa.qsa_compress_keys(ki, 1, pos0, pos0 * 128, 128, 4, 0, kbar, 0,
+                              rope_dim=idx_rope_dim, pages=pages)
+    elif not fresh:
         # cache of pooled keys for the context before the chunk (setup, untimed)
         kbar = torch.empty((Tk // 4, 128), dtype=torch.bfloat16, device="cuda")
         qsa.qsa_compress_keys(ki, 1, pos0, pos0 * 128, 128, 4, 0, kbar, (pos0 // 4) * 128,
                               rope_dim=idx_rope_dim)
-    layer = qsa.QSAPrefill(Tq, pos0=pos0, budget=budget, fresh=fresh, idx_rope_dim=idx_rope_dim)
+    layer = qsa.QSAPrefill(Tq, pos0=pos0, budget=budget, fresh=fresh, idx_rope_dim=idx_rope_dim,
+                           pages=pages)
     torch.cuda.synchronize()
     names = ["rope_pool", "select", "attend"]
     timer = StageTimer(names)
@@ -162,7 +198,8 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None):
     if with_dense:
         Od = torch.empty((Tq, 24, 256), dtype=torch.float32, device="cuda")
         Kr = layer.Kr if fresh else K
-        dense = lambda: qsa.dense_attn(layer.Qr, Kr, V, 1, Tq, Tk, pos0, None, 24, 2, 256, Od)  # noqa
+        dense = lambda: qsa.dense_attn(layer.Qr, Kr, V, 1, Tq, Tk, pos0, None, 24, 2, 256, Od,  # noqa
+                                       pages=pages)
         dense()
         torch.cuda.synchronize()
         dsteps = max(1, min(steps, 3))
@@ -233,19 +270,19 @@ def bench_decode(name, steps, warmup, with_dense=True):
     log(f"generated {name} caches in {time.time() - t:.1f}s")
     seq_len = torch.full((B,), L, dtype=torch.int64, device="cuda")
 
-    def one(n, qq, qqi):
-        dec = qsa.QSADecode(B, L, budget=budget, next_n=n)
+    def one(n, qq, qqi, kc=Kc, vc=Vc, kb=kbar, pages=None):
+        dec = qsa.QSADecode(B, L, budget=budget, next_n=n, pages=pages)
         for _ in range(warmup):
-            dec(qq, qqi, Kc, Vc, kbar, seq_len)
+            dec(qq, qqi, kc, vc, kb, seq_len)
         torch.cuda.synchronize()
-        ms = _time_steps(lambda: dec(qq, qqi, Kc, Vc, kbar, seq_len), steps)
+        ms = _time_steps(lambda: dec(qq, qqi, kc, vc, kb, seq_len), steps)
         dms = None
         if with_dense:
             Od = torch.empty((B, n, 24, 256), dtype=torch.float32, device="cuda")
             wsb = qsa.dense_attn_workspace_bytes(B, n, L, 24, 2, 256)
             ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
-            run = lambda: qsa.dense_attn(dec.qr, Kc, Vc, B, n, L, 0, seq_len, 24, 2, 256, Od,  # noqa
-                                         None, ws, wsb)
+            run = lambda: qsa.dense_attn(dec.qr, kc, vc, B, n, L, 0, seq_len, 24, 2, 256, Od,  # noqa
+                                         None, ws, wsb, pages=pages)
             run()
             torch.cuda.synchronize()
             dms = _time_steps(run, steps)
@@ -260,6 +297,18 @@ def bench_decode(name, steps, warmup, with_dense=True):
         qn = to_dev(synth.normal_bf16(1, (B, n, 24, 256), seed=7))
         qin = to_dev(synth.normal_bf16(4, (B, n, 4, 128), seed=7))
         res[f"next_n_{n}"] = one(n, qn, qin)
+    P = DECODE_PAGED.get(name)
+    if P:
+        # the same caches in randomly permuted pages of P tokens (setup, untimed)
+        table, perm = page_table(B, L, P, seed=2)
+        pages = qsa.Pages(table, P)
+        Kp, Vp = page_pool(Kc, P, perm), page_pool(Vc, P, perm)
+        kbp = page_pool(kbar, P // 4, perm)
+        paged = dict(page_tokens=P, **one(1, q, qi, Kp, Vp, kbp, pages))
+        if n:
+            paged[f"next_n_{n}"] = one(n, qn, qin, Kp, Vp, kbp, pages)
+        res["paged"] = paged
+        del Kp, Vp, kbp
     del Kc, Vc, kbar
     torch.cuda.empty_cache()
     return res
@@ -449,6 +498,20 @@ def main():
                  speedup_vs_dense_at_mfma_peak=m_roof / m_pre["ms_per_step"])
         out["prefill_1m_chunk"] = m
         log(f"prefill prefill_1m_chunk: {m_pre['ms_per_step']:.2f} ms/step")
+        # the report's prefill condition: a 16K-token chunk over a paged cache
+        c_pre, _ = bench_prefill("prefill_1m_chunk16k", min(args.steps, 3), 1,
+                                 with_dense=args.dense == "all", page_tokens=64)
+        c = dict(workload="prefill_1m_chunk16k", page_tokens=64, ms_per_step=c_pre["ms_per_step"],
+                 tokens_per_s=c_pre["Tq"] / (c_pre["ms_per_step"] * 1e-3),
+                 stages_ms=c_pre["stages_ms"])
+        if "dense_ms" in c_pre:
+            c.update(dense_ms=c_pre["dense_ms"],
+                     speedup_vs_dense=c_pre["dense_ms"] / c_pre["ms_per_step"])
+        c_roof = c_pre["dense_flop"] / (BF16_PEAK_TFLOPS * 1e12) * 1e3
+        c.update(dense_at_mfma_peak_ms=c_roof,
+                 speedup_vs_dense_at_mfma_peak=c_roof / c_pre["ms_per_step"])
+        out["prefill_1m_chunk16k_paged"] = c
+        log(f"prefill prefill_1m_chunk16k (paged): {c_pre['ms_per_step']:.2f} ms/step")
         m_dec = bench_decode("decode_1m_b4", max(args.steps, 10), args.warmup,
                              with_dense=args.dense != "none")
         out["decode_1m_b4"] = dict(workload="decode_1m_b4", **m_dec)
