@@ -80,6 +80,11 @@ def _load():
         lib.qsa_oracle_select_rows.restype = None
         lib.qsa_oracle_dense_rows.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, i64, vp, vp]
         lib.qsa_oracle_dense_rows.restype = None
+        lib.qsa_oracle_distill_row.argtypes = [vp, vp, i32, i32, i32, i64, i32, vp, vp, vp]
+        lib.qsa_oracle_distill_row.restype = dbl
+        lib.qsa_oracle_distill_rows.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32,
+                                                i32, i32, vp, i64, vp]
+        lib.qsa_oracle_distill_rows.restype = None
         lib.qsa_oracle_f64_to_bf16.argtypes = [dbl]
         lib.qsa_oracle_f64_to_bf16.restype = ctypes.c_uint16
         lib.qsa_oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
@@ -327,3 +332,32 @@ def dense_rows(Q, K, V, rows, pos0: int = 0):
     _load().qsa_oracle_dense_rows(_p(Q), _p(K), _p(V), pos0, H, Hkv, D, _p(rows), n, _p(O),
                                   _p(lse))
     return O, lse
+
+
+def distill_row(q_row, K, p: int, s: np.ndarray, r: int = 4):
+    """Stage-1 distillation of one query at position p: q_row [H, D] and K
+    post-RoPE, s the indexer scores of its nc(p) complete blocks.
+    Returns (KL, teacher T [nc], ln S [nc])."""
+    q_row = _c(q_row, np.uint16)
+    K = _c(K, np.uint16)
+    H, D = q_row.shape
+    nc = num_complete(p, r)
+    s = _c(s[:nc], np.float64)
+    T = np.zeros(max(nc, 1))
+    lS = np.zeros(max(nc, 1))
+    kl = _load().qsa_oracle_distill_row(_p(q_row), _p(K), H, K.shape[1], D, p, r, _p(s), _p(T),
+                                        _p(lS))
+    return float(kl), T[:nc], lS[:nc]
+
+
+def distill_rows(Q, K, qi, kbar, rows, pos0: int = 0, r: int = 4, mode: int = MODE_MAXHEAD):
+    """KL of stage-1 distillation for query rows (Q, K post-RoPE; qi, kbar the
+    indexer inputs) -> [n]."""
+    Q, K, qi, kbar = (_c(a, np.uint16) for a in (Q, K, qi, kbar))
+    rows = _c(rows, np.int64)
+    _, H, D = Q.shape
+    kl = np.empty(rows.size)
+    _load().qsa_oracle_distill_rows(_p(Q), _p(K), _p(qi), _p(kbar), kbar.shape[0], pos0, H,
+                                    K.shape[1], D, qi.shape[1], qi.shape[2], r, mode, _p(rows),
+                                    rows.size, _p(kl))
+    return kl

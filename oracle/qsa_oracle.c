@@ -427,3 +427,86 @@ void qsa_oracle_dense_rows(const uint16_t *Q, const uint16_t *K, const uint16_t 
         free(tok);
     }
 }
+
+/* ---------- O8: stage-1 indexer distillation, forward --------------------- */
+/* chlience section 6: the first stage trains the indexer alone against a
+ * teacher distribution made from full attention, max-pooled within each
+ * micro-block, by minimising a KL divergence.  For the query at position p
+ * (its Q row [H][D] and K [*][Hkv][D], both post-RoPE):
+ *   A_hj = softmax over j = 0..p of q_h . k_{g(h), j} / sqrt(D)   dense attention
+ *   M_hb = max over t < r of A_{h, r*b + t}, for b < nc(p)         block max-pool
+ *   T_b  = sum_h M_hb / sum_b' sum_h M_hb'                          heads summed,
+ *                                                                   L1-normalised
+ *   S_b  = softmax over b < nc(p) of the indexer scores s_b (O3)
+ *   KL   = sum_b T_b (ln T_b - ln S_b), with 0 ln 0 = 0.
+ * Returns KL (0 when nc(p) = 0); T_out / logS_out (length nc) if not NULL. */
+double qsa_oracle_distill_row(const uint16_t *q_row, const uint16_t *K, int H, int Hkv, int D,
+                              int64_t p, int r, const double *s, double *T_out,
+                              double *logS_out) {
+    int64_t nc = qsa_oracle_num_complete(p, r);
+    if (nc <= 0) return 0.0;
+    int group = H / Hkv;
+    double scale = 1.0 / sqrt((double)D);
+    double *l = (double *)malloc(sizeof(double) * (size_t)(p + 1));
+    double *T = (double *)calloc((size_t)nc, sizeof(double));
+    for (int h = 0; h < H; ++h) {
+        int g = h / group;
+        double q[512];
+        for (int d = 0; d < D; ++d) q[d] = bf16_to_f64(q_row[h * D + d]);
+        double m = -INFINITY;
+        for (int64_t j = 0; j <= p; ++j) {
+            const uint16_t *kr = K + (j * Hkv + g) * (int64_t)D;
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d) dot += q[d] * bf16_to_f64(kr[d]);
+            l[j] = dot * scale;
+            if (l[j] > m) m = l[j];
+        }
+        double z = 0.0;
+        for (int64_t j = 0; j <= p; ++j) z += exp(l[j] - m);
+        double lse = m + log(z);
+        for (int64_t b = 0; b < nc; ++b) {
+            double mb = 0.0;
+            for (int t = 0; t < r; ++t) {
+                double a = exp(l[b * r + t] - lse);
+                if (a > mb) mb = a;
+            }
+            T[b] += mb;
+        }
+    }
+    double zt = 0.0, ms = -INFINITY;
+    for (int64_t b = 0; b < nc; ++b) {
+        zt += T[b];
+        if (s[b] > ms) ms = s[b];
+    }
+    double zs = 0.0;
+    for (int64_t b = 0; b < nc; ++b) zs += exp(s[b] - ms);
+    double lse_s = ms + log(zs);
+    double kl = 0.0;
+    for (int64_t b = 0; b < nc; ++b) {
+        double t = T[b] / zt, ls = s[b] - lse_s;
+        if (t > 0.0) kl += t * (log(t) - ls);
+        if (T_out) T_out[b] = t;
+        if (logS_out) logS_out[b] = ls;
+    }
+    free(l);
+    free(T);
+    return kl;
+}
+
+/* O8 for rows of one sequence: the query at pos0 + rows[i] uses Q row
+ * rows[i], indexer row qi[rows[i]] and the pooled keys kbar[nb][Di]. */
+void qsa_oracle_distill_rows(const uint16_t *Q, const uint16_t *K, const uint16_t *qi,
+                             const uint16_t *kbar, int64_t nb, int64_t pos0, int H, int Hkv,
+                             int D, int Hi, int Di, int r, int mode, const int64_t *rows,
+                             int64_t n, double *kl) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t t = rows[i];
+        int64_t p = pos0 + t;
+        int64_t nc_full = qsa_oracle_num_complete(p, r);
+        double *s = (double *)malloc(sizeof(double) * (size_t)(nc_full > 0 ? nc_full : 1));
+        qsa_oracle_scores_row(qi + t * Hi * (int64_t)Di, kbar, nb, p, Hi, Di, r, mode, s);
+        kl[i] = qsa_oracle_distill_row(Q + t * H * (int64_t)D, K, H, Hkv, D, p, r, s, NULL, NULL);
+        free(s);
+    }
+}

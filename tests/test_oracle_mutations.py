@@ -39,6 +39,12 @@ MUTATIONS = {
     "kbar_gain_dropped": ("m[d] *= inv * g;", "m[d] *= inv;"),
     "kbar_rope_frequency": ("pow(theta, -(double)(2 * j) / (double)rope_dim)",
                             "pow(theta, -(double)j / (double)rope_dim)"),
+    "distill_mean_pool": ("if (a > mb) mb = a;", "mb += a / (double)r;"),
+    "distill_kl_reversed": ("if (t > 0.0) kl += t * (log(t) - ls);",
+                            "if (t > 0.0) kl += exp(ls) * (ls - log(t));"),
+    "distill_partial_block_dropped": ("for (int64_t j = 0; j <= p; ++j) z += exp(l[j] - m);",
+                                      "for (int64_t j = 0; j < nc * r; ++j) z += exp(l[j] - m);"),
+    "distill_scores_not_softmaxed": ("double lse_s = ms + log(zs);", "double lse_s = 0.0;"),
     "reuse_tail_from_own_block": ("int64_t from = qsa_oracle_num_complete(p_sel, r) * r;",
                                   "int64_t from = qsa_oracle_num_complete(p, r) * r;"),
     "reuse_tail_stops_short": ("for (int64_t j = from; j <= p; ++j) tok[n++] = j;",

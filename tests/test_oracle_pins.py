@@ -572,3 +572,69 @@ def test_indexer_pairs_count(oracle_lib):
     tot = sum(oracle_lib.num_complete(p) for p in range(n))
     assert tot == 2 * m * m - m          # sum_{q=1..4m} floor(q/4), closed form
     assert abs(tot / (n * n / 8) - 1) < 2e-3
+
+
+# ----------------------------------------------------------------------------
+# Stage-1 indexer distillation (forward): teacher = dense attention max-pooled
+# per block, heads summed, L1-normalised; KL against softmax of the scores.
+# ----------------------------------------------------------------------------
+
+def _distill_inputs(p, planted):
+    """q_row [24, 256] and K [p+1, 2, 256] with logits q_h.k_j / 16 equal to
+    planted[(group, j)] (0 elsewhere): dim g*2 carries group g's keys."""
+    q = np.zeros((24, 256), dtype=np.float32)
+    q[:12, 0] = 4.0
+    q[12:, 1] = 4.0
+    K = np.zeros((p + 1, 2, 256), dtype=np.float32)
+    for (g, j), c in planted.items():
+        K[j, g, g] = c * 16.0 / 4.0   # (4 * x) / 16 = c
+    return bf(q), bf(K)
+
+
+def test_distill_uniform_attention_closed_form(oracle_lib):
+    """K = 0: attention is uniform, so the teacher is uniform over the nc
+    complete blocks and KL = -ln nc - mean(s) + logsumexp(s)."""
+    p = 41
+    nc = (p + 1) // 4
+    q, K = _distill_inputs(p, {})
+    s0 = np.zeros(nc)
+    kl, T, _ = oracle_lib.distill_row(q, K, p, s0)
+    assert abs(kl) < 1e-14 and np.allclose(T, 1.0 / nc, atol=1e-15)
+    s = np.linspace(-1.0, 2.0, nc)
+    kl, T, lS = oracle_lib.distill_row(q, K, p, s)
+    lse = np.log(np.exp(s).sum())
+    assert abs(kl - (-np.log(nc) - s.mean() + lse)) < 1e-12
+    assert np.allclose(lS, s - lse, atol=1e-14)
+    assert oracle_lib.distill_row(q, K, 2, np.zeros(0))[0] == 0.0   # no complete block
+
+
+def test_distill_max_pool_and_head_sum(oracle_lib):
+    """Planted logits: group 1 heads see logit c1 on token 1 (block 0) and c2
+    on token 2 (same block); group 0 heads see c0 on token 9, inside the
+    query's incomplete block (p = 10: blocks 0, 1 complete).  The teacher is
+    the max inside each block, summed over all 24 heads, normalised; the
+    incomplete block counts in each head's softmax but not in the teacher."""
+    p, c0, c1, c2 = 10, 3.0, 2.0, 1.0
+    q, K = _distill_inputs(p, {(0, 9): c0, (1, 1): c1, (1, 2): c2})
+    kl, T, _ = oracle_lib.distill_row(q, K, p, np.zeros(2))
+    z0 = np.exp(c0) + 10.0                        # group 0 softmax denominator
+    z1 = np.exp(c1) + np.exp(c2) + 9.0            # group 1
+    m0 = 12 * (1.0 / z0) + 12 * (np.exp(c1) / z1)   # block 0: max = token 1
+    m1 = 12 * (1.0 / z0) + 12 * (1.0 / z1)          # block 1: all logits 0
+    want = np.array([m0, m1]) / (m0 + m1)
+    assert np.allclose(T, want, atol=1e-14)
+    assert abs(kl - np.sum(want * (np.log(want) - np.log(0.5)))) < 1e-13
+
+
+def test_distill_rows_nonnegative_and_zero_at_teacher(oracle_lib, synth_lib):
+    """KL >= 0 on random inputs, and KL = 0 when the indexer scores are the
+    log of the teacher (up to a constant)."""
+    T_len = 80
+    Q, K, V, qi, ki = _small_inputs(synth_lib, T_len)
+    kb = oracle_lib.compress(ki)
+    rows = np.arange(0, T_len, 7)
+    kl = oracle_lib.distill_rows(Q, K, qi, kb, rows)
+    assert np.all(kl >= -1e-12) and kl[rows >= 7].min() > 1e-6
+    kl_t, T, _ = oracle_lib.distill_row(Q[70], K, 70, np.zeros(17))
+    kl2, _, _ = oracle_lib.distill_row(Q[70], K, 70, np.log(T) + 3.0)
+    assert abs(kl2) < 1e-12 and kl_t > 0
