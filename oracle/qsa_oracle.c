@@ -450,7 +450,7 @@ double qsa_oracle_distill_row(const uint16_t *q_row, const uint16_t *K, int H, i
     double *l = (double *)malloc(sizeof(double) * (size_t)(p + 1));
     double *T = (double *)calloc((size_t)nc, sizeof(double));
     for (int h = 0; h < H; ++h) {
-        int g = h / group;
+        const int g = h / group;
         double q[512];
         for (int d = 0; d < D; ++d) q[d] = bf16_to_f64(q_row[h * D + d]);
         double m = -INFINITY;
