@@ -445,12 +445,11 @@ double qsa_oracle_distill_row(const uint16_t *q_row, const uint16_t *K, int H, i
                               double *logS_out) {
     int64_t nc = qsa_oracle_num_complete(p, r);
     if (nc <= 0) return 0.0;
-    int group = H / Hkv;
-    double scale = 1.0 / sqrt((double)D);
+    const double inv_sqrt_d = 1.0 / sqrt((double)D);
     double *l = (double *)malloc(sizeof(double) * (size_t)(p + 1));
     double *T = (double *)calloc((size_t)nc, sizeof(double));
     for (int h = 0; h < H; ++h) {
-        const int g = h / group;
+        const int g = h / (H / Hkv);
         double q[512];
         for (int d = 0; d < D; ++d) q[d] = bf16_to_f64(q_row[h * D + d]);
         double m = -INFINITY;
@@ -458,7 +457,7 @@ double qsa_oracle_distill_row(const uint16_t *q_row, const uint16_t *K, int H, i
             const uint16_t *kr = K + (j * Hkv + g) * (int64_t)D;
             double dot = 0.0;
             for (int d = 0; d < D; ++d) dot += q[d] * bf16_to_f64(kr[d]);
-            l[j] = dot * scale;
+            l[j] = dot * inv_sqrt_d;
             if (l[j] > m) m = l[j];
         }
         double z = 0.0;

@@ -39,7 +39,9 @@ MUTATIONS = {
     "kbar_gain_dropped": ("m[d] *= inv * g;", "m[d] *= inv;"),
     "kbar_rope_frequency": ("pow(theta, -(double)(2 * j) / (double)rope_dim)",
                             "pow(theta, -(double)j / (double)rope_dim)"),
-    "distill_gqa_mapping": ("const int g = h / group;", "const int g = h % Hkv;"),
+    "distill_gqa_mapping": ("const int g = h / (H / Hkv);", "const int g = h % Hkv;"),
+    "distill_softmax_scale": ("const double inv_sqrt_d = 1.0 / sqrt((double)D);",
+                              "const double inv_sqrt_d = 1.0 / (double)D;"),
     "distill_mean_pool": ("if (a > mb) mb = a;", "mb += a / (double)r;"),
     "distill_kl_reversed": ("if (t > 0.0) kl += t * (log(t) - ls);",
                             "if (t > 0.0) kl += exp(ls) * (ls - log(t));"),
