@@ -10,7 +10,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqsa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["qsa_api.cpp", "elementwise.hip", "index_scores.hip", "topk.hip",
-           "attention.hip", "flash_prefill.hip"]
+           "attention.hip", "flash_prefill.hip", "distill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          # packed fp32 instructions are kept out of every kernel

@@ -403,4 +403,52 @@ int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, i
     return launch_status(launch_dense_prefill(a, s));
 }
 
+// Distillation: the indexer scores of one chunk of query rows live in the
+// workspace (at most 1 GiB); the fused kernel reads them back.
+static void distill_layout(int64_t Tq, int64_t nb_max, int64_t *ld, int64_t *chunk) {
+    *ld = round_up(nb_max > 0 ? nb_max : 1, 4);
+    *chunk = select_chunk_rows(Tq, *ld);
+}
+
+size_t qsa_distill_workspace_bytes(int64_t Tq, int64_t Tk) {
+    if (Tq <= 0 || Tk < kBlock) return 0;
+    int64_t ld, chunk;
+    distill_layout(Tq, Tk / kBlock, &ld, &chunk);
+    return static_cast<size_t>(chunk * ld * 4);
+}
+
+int qsa_distill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const float *lse, const qsa_bf16 *q_idx,
+                   const qsa_bf16 *kbar, int64_t Tq, int64_t Tk, int64_t pos0, int H, int Hkv,
+                   int D, int Hi, int Di, int r, int score_mode, float *kl, void *ws,
+                   size_t ws_bytes, void *stream) {
+    if (!Q || !K || !lse || !kl) return QSA_ERR_NULL;
+    if (Tq < 0 || Tk < 0 || pos0 < 0 || pos0 + Tq > Tk) return QSA_ERR_SHAPE;
+    int st = check_attn_shape(H, Hkv, D, r);
+    if (st != QSA_OK) return st;
+    if (H != 24 || Hkv != 2) return QSA_ERR_UNSUPPORTED;  // one workgroup: 16 queries x 24 heads
+    const int64_t nb_max = Tk / kBlock;
+    st = check_index_args(q_idx, kbar, 1, Tq, pos0, nullptr, nb_max, Hi, Di, r, score_mode);
+    if (st != QSA_OK) return st;
+    if (nb_max >= (int64_t(1) << 27) || Tq > kI32Max) return QSA_ERR_OVERFLOW;
+    if (!aligned16(Q) || !aligned16(K)) return QSA_ERR_ALIGN;
+    if (Tq == 0) return QSA_OK;
+    const size_t need = qsa_distill_workspace_bytes(Tq, Tk);
+    if (need > 0 && (!ws || ws_bytes < need)) return QSA_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(ws)) return QSA_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    int64_t ld, chunk;
+    distill_layout(Tq, nb_max, &ld, &chunk);
+    float *sc = static_cast<float *>(ws);
+    for (int64_t q0 = 0; q0 < Tq; q0 += chunk) {
+        const int64_t len = Tq - q0 < chunk ? Tq - q0 : chunk;
+        hipError_t e = launch_index_scores(q_idx + q0 * (kIdxHeads * kIdxDim), kbar, 1, len,
+                                           pos0 + q0, nullptr, nb_max, score_mode, sc, ld, s);
+        if (e != hipSuccess) return QSA_ERR_LAUNCH;
+        e = launch_distill(Q + q0 * H * kHeadDim, lse + q0 * H, K, sc, len, pos0 + q0, Tk, ld,
+                           kl + q0, s);
+        if (e != hipSuccess) return QSA_ERR_LAUNCH;
+    }
+    return QSA_OK;
+}
+
 }  // extern "C"

@@ -175,4 +175,10 @@ int decode_num_splits(int B, int Hkv, int64_t max_entries);
 hipError_t launch_attn_decode(const AttnArgs &a, int nsplit, hipStream_t s);
 hipError_t launch_dense_prefill(const AttnArgs &a, hipStream_t s);
 
+// Stage-1 distillation KL of a chunk of rows (see distill.hip): Q [rows][24][256]
+// and lse [rows][24] of the chunk, K [Tk][2][256], scores [rows][ld]; kl: [rows].
+hipError_t launch_distill(const uint16_t *Q, const float *lse, const uint16_t *K,
+                          const float *scores, int64_t rows, int64_t pos0, int64_t Tk,
+                          int64_t ld, float *kl, hipStream_t s);
+
 }  // namespace qsa

@@ -243,6 +243,31 @@ int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, i
                float *O, float *lse, void *ws, size_t ws_bytes, const qsa_pages *pages,
                void *stream);
 
+/* ---- Stage-1 indexer distillation, forward (chlience section 6: the first
+ * QSA training stage trains the indexer alone, its teacher being the full
+ * attention distribution max-pooled inside each micro-block, with a KL
+ * objective; ai.info "Industry relevance": a fused kernel yields the KL loss
+ * without materialising intermediates).  One sequence, prefill form.  For the
+ * query at p = pos0 + t with nc = nc(p) complete blocks:
+ *   teacher T_b = sum over heads h of max over the r tokens j of block b of
+ *                 exp(q_h.k_j / sqrt(D) - lse_h), then divided by its sum
+ *                 over b (lse_h: log-sum-exp over all keys 0 .. p);
+ *   student S_b = softmax over b < nc of the indexer scores (qsa_index_scores);
+ *   kl[t]       = sum_b T_b (ln T_b - ln S_b)   (0 when nc = 0).
+ * Q: [Tq][H][D] post-RoPE; K: [Tk][Hkv][D] post-RoPE, Tk >= pos0 + Tq;
+ * lse: fp32 [Tq][H] from dense_attn over the same Q and K; q_idx:
+ * [Tq][Hi][Di]; kbar: [Tk / r][Di] (the indexer inputs as for
+ * qsa_index_scores); kl: fp32 [Tq].  The attention probabilities and the
+ * per-block teacher never leave the kernel; the indexer scores of one chunk
+ * of rows pass through the workspace (at most 1 GiB).
+ * Workspace: qsa_distill_workspace_bytes (0 when Tk < r: ws may be NULL).
+ * Supported: H = 24, Hkv = 2, D = 256, Hi = 4, Di = 128, r = 4. */
+size_t qsa_distill_workspace_bytes(int64_t Tq, int64_t Tk);
+int qsa_distill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const float *lse, const qsa_bf16 *q_idx,
+                   const qsa_bf16 *kbar, int64_t Tq, int64_t Tk, int64_t pos0, int H, int Hkv,
+                   int D, int Hi, int Di, int r, int score_mode, float *kl, void *ws,
+                   size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -261,3 +261,36 @@ def test_pages_validation(lib):
                         vp(P), None, None, ctypes.c_size_t(0), pages(stride=1, page_tokens=64),
                         None)
     assert st == SHAPE
+
+
+def distill(lib, Q=P, K=P, lse=P, qi=P, kb=P, Tq=8, Tk=64, pos0=0, H=24, Hkv=2, D=256, Hi=4,
+            Di=128, r=4, mode=0, kl=P, ws=P, wsb=1 << 30):
+    return lib.qsa_distill_kl(vp(Q), vp(K), vp(lse), vp(qi), vp(kb), I64(Tq), I64(Tk), I64(pos0),
+                              H, Hkv, D, Hi, Di, r, mode, vp(kl), vp(ws), ctypes.c_size_t(wsb),
+                              None)
+
+
+def test_distill_validation(lib):
+    lib.qsa_distill_workspace_bytes.restype = ctypes.c_size_t
+    need = lib.qsa_distill_workspace_bytes(I64(8), I64(64))
+    assert need >= 8 * 16 * 4                          # the chunk's indexer scores
+    assert lib.qsa_distill_workspace_bytes(I64(0), I64(64)) == 0
+    assert lib.qsa_distill_workspace_bytes(I64(8), I64(3)) == 0   # no complete block
+    # one chunk of rows stays within 1 GiB however long the context
+    assert lib.qsa_distill_workspace_bytes(I64(1 << 20), I64(1 << 20)) <= (1 << 30)
+    assert distill(lib, lse=0) == NULL
+    assert distill(lib, kb=0) == NULL
+    assert distill(lib, kl=0) == NULL
+    assert distill(lib, Tq=8, Tk=7) == SHAPE            # keys must cover every query
+    assert distill(lib, pos0=60) == SHAPE
+    assert distill(lib, H=16, Hkv=2) == UNSUP           # 24 query heads over 2 KV heads only
+    assert distill(lib, H=12, Hkv=1) == UNSUP
+    assert distill(lib, D=128) == UNSUP
+    assert distill(lib, Hi=8) == UNSUP
+    assert distill(lib, mode=3) == SHAPE
+    assert distill(lib, Q=MIS) == ALIGN
+    assert distill(lib, kb=MIS) == ALIGN
+    assert distill(lib, ws=0) == WORKSPACE
+    assert distill(lib, wsb=need - 1) == WORKSPACE
+    assert distill(lib, ws=MIS) == ALIGN
+    assert distill(lib, Tq=0, ws=0, wsb=0) == OK        # nothing to do, nothing enqueued
