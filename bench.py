@@ -127,7 +127,8 @@ def page_table(B, L, P, seed):
     return perm.view(B, L // P).to(torch.int32).cuda(), perm.cuda()
 
 
-def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, page_tokens=0):
+def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, page_tokens=0,
+                  with_distill=False):
     import torch
     import block_sparse_long_08_amd as qsa
     Tq, pos0, budget, nd = WORKLOADS[name]
@@ -197,9 +198,10 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
     res["dense_flop"] = float(((pos + 1).astype(np.float64)).sum()) * 24 * 256 * 2 * 2
     if with_dense:
         Od = torch.empty((Tq, 24, 256), dtype=torch.float32, device="cuda")
+        lse = torch.empty((Tq, 24), dtype=torch.float32, device="cuda")
         Kr = layer.Kr if fresh else K
         dense = lambda: qsa.dense_attn(layer.Qr, Kr, V, 1, Tq, Tk, pos0, None, 24, 2, 256, Od,  # noqa
-                                       pages=pages)
+                                       lse, pages=pages)
         dense()
         torch.cuda.synchronize()
         dsteps = max(1, min(steps, 3))
@@ -211,6 +213,33 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
         torch.cuda.synchronize()
         dms = e0.elapsed_time(e1) / dsteps
         res.update(dense_ms=dms, qsa_attention_ms=stage["select"] + stage["attend"])
+        if with_distill and pages is None:
+            # stage-1 distillation forward: KL of the indexer against the
+            # block-max-pooled dense attention (lse of the dense pass above)
+            del Od
+            Kr, kb = layer.rope_and_pool(Q, K, ki, kbar)
+            qs = layer.rope_indexer(qi)
+            wsb = qsa.qsa_distill_workspace_bytes(Tq, Tk)
+            ws = torch.empty((max(wsb, 1),), dtype=torch.uint8, device="cuda")
+            kl = torch.empty((Tq,), dtype=torch.float32, device="cuda")
+            distill = lambda: qsa.qsa_distill_kl(layer.Qr, Kr, lse, qs, kb, Tq, Tk, pos0, 24, 2,  # noqa
+                                                 256, 4, 128, 4, 0, kl, ws, wsb)
+            distill()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(dsteps):
+                distill()
+            e1.record()
+            torch.cuda.synchronize()
+            kms = e0.elapsed_time(e1) / dsteps
+            # algorithmic work: q.k over the complete blocks' tokens, 24 heads
+            teacher_flop = float((4 * nc).astype(np.float64).sum()) * 24 * 256 * 2
+            res["distill"] = dict(ms=kms, teacher_qk_flop=teacher_flop,
+                                  teacher_tflops=teacher_flop / (kms * 1e-3) / 1e12,
+                                  mfma_frac=teacher_flop / (kms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                                  dense_forward_ms=dms, forward_total_ms=dms + kms,
+                                  mean_kl=float(kl.mean().item()))
+            del ws, kl
     del layer
     torch.cuda.empty_cache()
     return res, x
@@ -406,6 +435,9 @@ def main():
                          "decode of 4 sequences) with their dense baselines")
     ap.add_argument("--indexer-rope", default="on", choices=["on", "off"],
                     help="also time the 32K prefill with partial RoPE on the indexer")
+    ap.add_argument("--distill", default="on", choices=["on", "off"],
+                    help="also time the stage-1 distillation KL on the prefill workload "
+                         "(needs the dense baseline's log-sum-exp)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (scale of the HBM byte counters)")
     args = ap.parse_args()
@@ -420,7 +452,8 @@ def main():
 
     if args.calibrate_copy:
         calibration_copy()
-    pre, x = bench_prefill(args.workload, args.steps, args.warmup, with_dense=args.dense == "all")
+    pre, x = bench_prefill(args.workload, args.steps, args.warmup, with_dense=args.dense == "all",
+                           with_distill=args.distill == "on")
     log(f"prefill {args.workload}: {pre['ms_per_step']:.2f} ms/step, stages {pre['stages_ms']}")
     st = pre["stages_ms"]
     dominant = max(st, key=st.get)
@@ -457,6 +490,10 @@ def main():
         out["dense_prefill_ms"] = pre["dense_ms"]
         out["prefill_speedup_vs_dense"] = pre["dense_ms"] / pre["ms_per_step"]
         out["dense_prefill_tflops"] = pre["dense_flop"] / (pre["dense_ms"] * 1e-3) / 1e12
+    if "distill" in pre:
+        out["distill"] = dict(workload=args.workload, **pre["distill"])
+        log(f"distill {args.workload}: {pre['distill']['ms']:.2f} ms "
+            f"({pre['distill']['teacher_tflops']:.0f} TFLOP/s on q.k)")
     # dense attention at the bf16 MFMA peak: the speedup no dense kernel could shrink
     dense_roof_ms = pre["dense_flop"] / (BF16_PEAK_TFLOPS * 1e12) * 1e3
     out["dense_prefill_at_mfma_peak_ms"] = dense_roof_ms

@@ -22,7 +22,11 @@
 // are added in a fixed order by one thread per (query, block), which keeps
 // Z, A, C and the running log-sum-exp of s for its row; the 16 threads of a
 // row combine them at the end and write KL.  Nothing per block leaves the
-// workgroup.
+// workgroup.  One barrier per tile: it publishes the tile's head sums and
+// the next tile's keys.  The two key buffers and the two head-sum buffers
+// are distinct LDS arrays picked at compile time (the tile loop runs in
+// pairs), so the compiler can tell that the reads of one buffer do not
+// alias the DMA into the other and does not wait for that DMA first.
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -42,8 +46,10 @@ __global__ void __launch_bounds__(512)
 distill_kl_kernel(const uint16_t *__restrict__ Q, const float *__restrict__ lse,
                   const uint16_t *__restrict__ K, const float *__restrict__ scores, int64_t rows,
                   int64_t pos0, int64_t Tk, int64_t ld, float *__restrict__ kl) {
-    __shared__ __attribute__((aligned(16))) unsigned char kt[2 * kDsBuf];
-    __shared__ float red[8][kDsQ][17];
+    __shared__ __attribute__((aligned(16))) unsigned char kt0[kDsBuf];
+    __shared__ __attribute__((aligned(16))) unsigned char kt1[kDsBuf];
+    __shared__ float red0[8][kDsQ][17];
+    __shared__ float red1[8][kDsQ][17];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g4 = lane >> 4;
     const int g = wave >> 2;  // this wave's KV head
@@ -69,12 +75,11 @@ distill_kl_kernel(const uint16_t *__restrict__ Q, const float *__restrict__ lse,
         lse2[k] = lse[qrow * H + h] * kDsLog2e;
     }
 
-    // Key tile `it` into buffer it % 2: DMA instruction j of wave w fills the
-    // 1 KB at 1024 * (8w + j) = KV head (8w + j) / 32, token rows
+    // Key tile `it` into dst: DMA instruction j of wave w fills the 1 KB at
+    // 1024 * (8w + j) = KV head (8w + j) / 32, token rows
     // 2 * ((8w + j) % 32) + lane / 32, slot lane % 32, where chunk c of row r
     // sits at slot c ^ (r % 32); the lane fetches the chunk of its slot.
-    auto dma_tile = [&](int it) {
-        unsigned char *dst = kt + (it & 1) * kDsBuf;
+    auto dma_tile = [&](int it, unsigned char *dst) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int piece = 8 * wave + j;
@@ -97,16 +102,15 @@ distill_kl_kernel(const uint16_t *__restrict__ Q, const float *__restrict__ lse,
     const int64_t nc = reducer ? num_complete_blocks(pos0 + row, kBlock) : 0;
     float z = 0.f, a = 0.f, c = 0.f, m = -INFINITY, zs = 0.f;
 
-    if (ntiles > 0) dma_tile(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 has landed
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-        if (it + 1 < ntiles) dma_tile(it + 1);
+    // tile `it` from cur while tile it + 1 streams into nxt; head sums in rd
+    auto step = [&](int it, const unsigned char *cur, unsigned char *nxt,
+                    float (*rd)[kDsQ][17]) {
+        if (it + 1 < ntiles) dma_tile(it + 1, nxt);
         const int64_t b = static_cast<int64_t>(it) * 16 + blk;
         const bool live = reducer && b < nc;
         const float s = live ? scores[row * ld + b] : 0.f;  // in flight during the MFMAs
-        const unsigned char *kb = kt + (it & 1) * kDsBuf + g * (kDsTok * kDsKRow);
-#pragma unroll
+        const unsigned char *kb = cur + g * (kDsTok * kDsKRow);
+#pragma unroll 2
         for (int ct = 0; ct < 4; ++ct) {
             const int r = 16 * ct + n;  // token row of this lane's A fragment
             bf16x8 kf[8];
@@ -125,15 +129,17 @@ distill_kl_kernel(const uint16_t *__restrict__ Q, const float *__restrict__ lse,
                 const float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
                 tsum += exp2f(mx * kDsScaleLog2 - lse2[k]);
             }
-            red[wave][n][4 * ct + g4] = tsum;
+            rd[wave][n][4 * ct + g4] = tsum;
         }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile it + 1 has landed
         __syncthreads();
+        // rd is written again two tiles on, after the next barrier
         if (live) {
             // the 24 heads in a fixed order: KV head 0's waves, then KV head 1's
-            const float t = (((red[0][q][blk] + red[1][q][blk]) + red[2][q][blk]) +
-                             red[3][q][blk]) +
-                            (((red[4][q][blk] + red[5][q][blk]) + red[6][q][blk]) +
-                             red[7][q][blk]);
+            const float t = (((rd[0][q][blk] + rd[1][q][blk]) + rd[2][q][blk]) +
+                             rd[3][q][blk]) +
+                            (((rd[4][q][blk] + rd[5][q][blk]) + rd[6][q][blk]) +
+                             rd[7][q][blk]);
             z += t;
             a += t > 0.f ? t * logf(t) : 0.f;
             c += t * s;
@@ -144,8 +150,13 @@ distill_kl_kernel(const uint16_t *__restrict__ Q, const float *__restrict__ lse,
                 zs += expf(s - m);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile it + 1 has landed
-        __syncthreads();
+    };
+    if (ntiles > 0) dma_tile(0, kt0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 has landed
+    __syncthreads();
+    for (int it = 0; it < ntiles; it += 2) {
+        step(it, kt0, kt1, red0);
+        if (it + 1 < ntiles) step(it + 1, kt1, kt0, red1);
     }
     if (tid >= 256) return;
     // the 16 threads of a row are 16 consecutive lanes
