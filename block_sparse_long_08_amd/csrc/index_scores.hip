@@ -44,12 +44,15 @@ __device__ __forceinline__ void store_tile(unsigned char *buf, int bl, int part,
 // Pooled-key tiles are double-buffered: the next tile is loaded into
 // registers while the current one feeds the MFMAs, then written to the other
 // LDS buffer (one barrier per tile).  Each wave stages its 16 x 64 scores in
-// LDS and writes them back as whole 256-byte row segments.
+// LDS and writes them back as whole 256-byte row segments.  With gmax set it
+// also writes the largest score key of every 16 consecutive blocks,
+// gmax[t * gld + g] (blocks a query does not see count as -inf), from which
+// the top-K takes its floor.
 template <int MODE, bool PAGED>
 __global__ void __launch_bounds__(256)
 index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ kbar,
                      int64_t Tq, int64_t pos0, int64_t nb_max, float *__restrict__ scores,
-                     int64_t ld, PageTable pg) {
+                     int64_t ld, uint32_t *__restrict__ gmax, int64_t gld, PageTable pg) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileBytes + 4 * 16 * kStageRow];
     const int qt = gridDim.x - 1 - blockIdx.x;  // longest rows first
     const int64_t seq = blockIdx.z;
@@ -57,6 +60,7 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
     if (!PAGED) kbar += seq * nb_max * kIdxDim;
     const int32_t *ptab = PAGED ? pg.table + seq * pg.stride : nullptr;
     scores += seq * Tq * ld;
+    if (gmax) gmax += seq * Tq * gld;
 
     const int64_t t0 = static_cast<int64_t>(qt) * kQT;
     const int64_t t_last = min(t0 + kQT, Tq) - 1;
@@ -141,6 +145,18 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
             const int64_t blk = b0 + 4 * wr_c;
             const float4 v = *reinterpret_cast<const float4 *>(stage + ql * kStageRow + 16 * wr_c);
             if (tout < Tq && blk < ld) *reinterpret_cast<float4 *>(scores + tout * ld + blk) = v;
+            if (gmax) {
+                // the 16-block group of the 4 lanes wr_c & ~3 .. | 3 (a quad):
+                // float max across the quad by DPP moves (lane ^ 1, lane ^ 2),
+                // then one key (the key order is the float order)
+                float m = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+                m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1,
+                                                                     0xF, 0xF, false)));
+                m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E,
+                                                                     0xF, 0xF, false)));
+                const int64_t gi = (b0 >> 4) + (wr_c >> 2);
+                if ((wr_c & 3) == 0 && tout < Tq && gi < gld) gmax[tout * gld + gi] = score_key(m);
+            }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -255,13 +271,14 @@ static void launch_decode_scan(dim3 grid, hipStream_t s, const uint16_t *q_idx,
 template <int MODE>
 static void launch_prefill_scores(dim3 grid, hipStream_t s, const uint16_t *q_idx,
                                   const uint16_t *kbar, int64_t Tq, int64_t pos0, int64_t nb_max,
-                                  float *scores, int64_t ld, const PageTable &pg) {
+                                  float *scores, int64_t ld, uint32_t *gmax, int64_t gld,
+                                  const PageTable &pg) {
     if (pg.table)
         hipLaunchKernelGGL((index_scores_prefill<MODE, true>), grid, dim3(256), 0, s, q_idx,
-                           kbar, Tq, pos0, nb_max, scores, ld, pg);
+                           kbar, Tq, pos0, nb_max, scores, ld, gmax, gld, pg);
     else
         hipLaunchKernelGGL((index_scores_prefill<MODE, false>), grid, dim3(256), 0, s, q_idx,
-                           kbar, Tq, pos0, nb_max, scores, ld, pg);
+                           kbar, Tq, pos0, nb_max, scores, ld, gmax, gld, pg);
 }
 
 hipError_t launch_index_scores(const uint16_t *q_idx, const uint16_t *kbar, int B, int64_t Tq,
@@ -287,9 +304,11 @@ hipError_t launch_index_scores(const uint16_t *q_idx, const uint16_t *kbar, int 
     const dim3 grid(static_cast<uint32_t>(n_qt), static_cast<uint32_t>(n_split),
                     static_cast<uint32_t>(B));
     if (mode == 0)
-        launch_prefill_scores<0>(grid, s, q_idx, kbar, Tq, pos0, nb_max, scores, ld, pg);
+        launch_prefill_scores<0>(grid, s, q_idx, kbar, Tq, pos0, nb_max, scores, ld, gmax, gld,
+                                 pg);
     else
-        launch_prefill_scores<1>(grid, s, q_idx, kbar, Tq, pos0, nb_max, scores, ld, pg);
+        launch_prefill_scores<1>(grid, s, q_idx, kbar, Tq, pos0, nb_max, scores, ld, gmax, gld,
+                                 pg);
     return hipGetLastError();
 }
 

@@ -210,12 +210,18 @@ int qsa_topk_blocks(const float *scores, int B, int64_t Tq, int64_t ld, int64_t 
 
 // Workspace of qsa_select_blocks: the fp32 scores of one chunk of query rows
 // (all rows in the decode form), then the top-K candidate lists of that chunk.
+// Prefill chunks: the scores [chunk][ld] and their 16-block group maxima
+// [chunk][gld] (gld = ld / 16 rounded up to whole 64-block tiles), then the
+// top-K workspace.
+static int64_t gmax_ld(int64_t ld) { return round_up(ld, 64) / 16; }
+
 static void select_layout(int B, int64_t Tq, int64_t nb_max, int K, bool decode, int64_t *ld,
                           int64_t *chunk, size_t *score_bytes, size_t *topk_bytes) {
     *ld = round_up(nb_max > 0 ? nb_max : 1, 4);
     *chunk = decode ? 1 : select_chunk_rows(Tq, *ld);
     const int64_t rows = decode ? B : *chunk;
     *score_bytes = static_cast<size_t>(round_up(rows * *ld * 4, 256));
+    if (!decode) *score_bytes += static_cast<size_t>(round_up(rows * gmax_ld(*ld) * 4, 256));
     *topk_bytes = topk_plan(rows, nb_max, K).ws_bytes;
     if (decode) {  // or the decode-form candidate lists, whichever is larger
         const size_t lb = dec_list_layout(rows, nb_max, K).ws_bytes;
@@ -277,6 +283,10 @@ int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_
         return launch_status(launch_topk(sc, B, Tq, ld, pos0, seq_len, nb_max, r, K, blk_idx,
                                          n_sel, tws, s));
     }
+    // the chunk's group maxima follow its scores
+    const int64_t gld = gmax_ld(ld);
+    uint32_t *gm = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) +
+                                                round_up(chunk * ld * 4, 256));
     for (int b = 0; b < B; ++b) {
         const qsa_bf16 *qb = q_idx + static_cast<int64_t>(b) * Tq * (kIdxHeads * kIdxDim);
         // one sequence at a time: its own rows of the cache or of the page table
@@ -287,10 +297,10 @@ int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_
             const int64_t len = Tq - q0 < chunk ? Tq - q0 : chunk;
             hipError_t e = launch_index_scores(qb + q0 * (kIdxHeads * kIdxDim), kb, 1, len,
                                                pos0 + q0, nullptr, nb_max, score_mode, sc, ld, s,
-                                               nullptr, 0, pgb);
+                                               gm, gld, pgb);
             if (e != hipSuccess) return QSA_ERR_LAUNCH;
             e = launch_topk(sc, 1, len, ld, pos0 + q0, nullptr, nb_max, r, K,
-                            blk_idx + (row0 + q0) * K, n_sel + row0 + q0, tws, s);
+                            blk_idx + (row0 + q0) * K, n_sel + row0 + q0, tws, s, gm, gld);
             if (e != hipSuccess) return QSA_ERR_LAUNCH;
         }
     }

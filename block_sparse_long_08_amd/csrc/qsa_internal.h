@@ -91,7 +91,9 @@ hipError_t launch_compress(const uint16_t *k, int B, int64_t Tk, int64_t k_seq_s
 
 // Decode form (seq_len given): when gmax is set, also writes the largest
 // score key of every group of 64 consecutive blocks, gmax[b * gld + g] for
-// the groups holding complete blocks.
+// the groups holding complete blocks.  Prefill form: groups of 16 blocks,
+// gmax[t * gld + g] for every 64-block tile a query's row covers (gld a
+// multiple of 4).
 // pg.table set: kbar is a page pool of pooled blocks (pg.shift = log2 of the
 // blocks per page); only blocks a query sees are read.
 hipError_t launch_index_scores(const uint16_t *q_idx, const uint16_t *kbar, int B, int64_t Tq,
@@ -118,9 +120,13 @@ TopkPlan topk_plan(int64_t rows, int64_t nmax, int K);
 
 // Decode form (seq_len given): B rows, row b made for position
 // seq_len[b] - Tq (the first of the sequence's Tq newest queries).
+// gmax (prefill form, optional): the 16-block group maxima of the score rows
+// (launch_index_scores); the streaming plan then takes its floor from them
+// and reads only the groups at or above it.
 hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64_t pos0,
                        const int64_t *seq_len, int64_t nb_max, int r, int K, int32_t *blk_idx,
-                       int32_t *n_sel, void *ws, hipStream_t s);
+                       int32_t *n_sel, void *ws, hipStream_t s,
+                       const uint32_t *gmax = nullptr, int64_t gld = 0);
 
 // Decode-form top-K for few long rows (one query per sequence): a filter
 // pass over 4,096-key segments against a floor from the scan's group maxima,

@@ -50,6 +50,8 @@ struct TopkArgs {
     int r, K;
     int nprev;               // passes before this one (source 1)
     int64_t prev_seg[4];     // their segment lengths
+    const uint32_t *gmax;    // streaming pass: largest key of each 16-block group, or null
+    int64_t gld;             //   its row stride
 };
 
 template <int NT>
@@ -526,6 +528,12 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
 // If a list overflows (a crowded floor bin, e.g. heavy ties), the threshold
 // is found by three streaming radix passes instead and the row is emitted by
 // two more streaming passes; the result is the same.
+// With the scores' 16-block group maxima at hand (gmax), pass 1 reads those
+// instead of the row, and pass 2 loads only the groups whose maximum reaches
+// the floor (the others hold no key at or above it): the wave takes its
+// groups 64 at a time, one per lane (the next batch's maxima load while this
+// one is processed), lists the surviving ones in order and loads their keys
+// 16 groups at a time, 4 lanes per group, so lane order stays block order.
 template <int NT>
 struct StreamSmem {
     static constexpr int CAP = NT >= 1024 ? 256 : 512;  // list entries per wave
@@ -533,6 +541,7 @@ struct StreamSmem {
     uint32_t ckey[NT / kWave][CAP];
     int32_t cidx[NT / kWave][CAP];
     uint32_t eqtot[NT / kWave];
+    int32_t glist[NT / kWave][kWave];  // surviving 16-block groups of one batch
 };
 
 __device__ __forceinline__ void stream_keys(const float *s, int i, int lim, uint32_t (&kk)[4]) {
@@ -596,32 +605,68 @@ __device__ __forceinline__ void stream_row(const TopkArgs &a, int64_t row,
     const int l4 = 4 * lane;
 
     // ---- pass 1: group maxima -> floor
-    uint32_t lm[4] = {0u, 0u, 0u, 0u};
-    for (int base = w0; base < w1; base += 1024) {
-        uint32_t kk[4][4];
+    const uint32_t *gm = a.gmax ? a.gmax + row * a.gld : nullptr;
+    if (gm) {
+        // the precomputed maxima of the ceil(n / 16) groups holding blocks
+        for (int i = tid; i < kBins; i += kStNT) sh.hist[i] = 0u;
+        __syncthreads();
+        const int ng = (n + 15) >> 4;
+        for (int i = tid; i < ng; i += kStNT) atomicAdd(&sh.hist[gm[i] >> 20], 1u);
+    } else {
+        uint32_t lm[4] = {0u, 0u, 0u, 0u};
+        for (int base = w0; base < w1; base += 1024) {
+            uint32_t kk[4][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) stream_keys(s, base + 256 * u + l4, w1, kk[u]);
+            for (int u = 0; u < 4; ++u) stream_keys(s, base + 256 * u + l4, w1, kk[u]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) lm[u] = max(lm[u], max4(kk[u]));
+            for (int u = 0; u < 4; ++u) lm[u] = max(lm[u], max4(kk[u]));
+        }
+        for (int i = tid; i < kBins; i += kStNT) sh.hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) atomicAdd(&sh.hist[lm[u] >> 20], 1u);
     }
-    for (int i = tid; i < kBins; i += kStNT) sh.hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 4; ++u) atomicAdd(&sh.hist[lm[u] >> 20], 1u);
     __syncthreads();
     block_find<kStNT, kBins, 1, true>(sh.hist, K, sh, tid, lane, wave);
     const uint32_t floor_key = sh.total >= K ? sh.fd_bin << 20 : kMinKey;
 
     // ---- pass 2: candidate lists
     uint32_t wc = 0;  // wave-uniform
-    for (int base = w0; base < w1; base += 1024) {
-        uint32_t kk[4][4];
+    if (gm) {
+        const int g_lo = w0 >> 4, g_hi = (w1 + 15) >> 4;
+        int32_t *gl = sm.glist[wave];
+        uint32_t gnext = g_lo + lane < g_hi ? gm[g_lo + lane] : 0u;
+        for (int g0 = g_lo; g0 < g_hi; g0 += kWave) {
+            const uint32_t gcur = gnext;
+            gnext = g0 + kWave + lane < g_hi ? gm[g0 + kWave + lane] : 0u;
+            const bool keep = g0 + lane < g_hi && gcur >= floor_key;
+            const uint64_t bal = __ballot(keep);
+            if (bal == 0) continue;
+            if (keep) gl[lanes_below(bal)] = g0 + lane;
+            wave_lds_sync();
+            const int nsurv = __popcll(bal);
+            for (int j = 0; j < nsurv; j += 16) {
+                const int sidx = j + (lane >> 2);
+                uint32_t kk[4] = {0u, 0u, 0u, 0u};
+                int i = 0;
+                if (sidx < nsurv) {
+                    i = 16 * gl[sidx] + 4 * (lane & 3);
+                    stream_keys(s, i, w1, kk);
+                }
+                stream_append(kk, floor_key, i, kCap, wc, sm.ckey[wave], sm.cidx[wave]);
+            }
+            wave_lds_sync();  // the list is rewritten by the next batch
+        }
+    } else {
+        for (int base = w0; base < w1; base += 1024) {
+            uint32_t kk[4][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) stream_keys(s, base + 256 * u + l4, w1, kk[u]);
+            for (int u = 0; u < 4; ++u) stream_keys(s, base + 256 * u + l4, w1, kk[u]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            stream_append(kk[u], floor_key, base + 256 * u + l4, kCap, wc, sm.ckey[wave],
-                          sm.cidx[wave]);
+            for (int u = 0; u < 4; ++u)
+                stream_append(kk[u], floor_key, base + 256 * u + l4, kCap, wc, sm.ckey[wave],
+                              sm.cidx[wave]);
+        }
     }
     if (lane == 0) sh.wcnt[wave] = wc;
     __syncthreads();
@@ -1196,7 +1241,8 @@ TopkPlan topk_plan(int64_t rows, int64_t nmax, int K) {
 
 hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64_t pos0,
                        const int64_t *seq_len, int64_t nb_max, int r, int K, int32_t *blk_idx,
-                       int32_t *n_sel, void *ws, hipStream_t s) {
+                       int32_t *n_sel, void *ws, hipStream_t s, const uint32_t *gmax,
+                       int64_t gld) {
     // decode form: one row per sequence, made for the first of its Tq queries
     const int64_t rows = seq_len ? static_cast<int64_t>(B) : static_cast<int64_t>(B) * Tq;
     if (rows == 0) return hipSuccess;
@@ -1219,6 +1265,8 @@ hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64
     a.r = r;
     a.K = K;
     if (pl.stream) {
+        a.gmax = seq_len ? nullptr : gmax;
+        a.gld = gld;
         if (pl.stream_nt == 1024)
             hipLaunchKernelGGL(topk_stream<1024>, dim3(static_cast<uint32_t>(rows)), dim3(1024), 0,
                                s, a);

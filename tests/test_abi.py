@@ -153,9 +153,10 @@ def test_topk_validation(lib):
 
 def test_select_validation(lib):
     lib.qsa_select_workspace_bytes.restype = ctypes.c_size_t
-    # prefill form: scores of one chunk of rows (at most 1 GiB) in the workspace
+    # prefill form: scores of one chunk of rows (at most 1 GiB) and their
+    # 16-block group maxima (1/16 of that) in the workspace
     need = lib.qsa_select_workspace_bytes(1, I64(131072), I64(32768), 512)
-    assert (1 << 29) <= need <= (1 << 30) + (1 << 20)
+    assert (1 << 29) <= need <= (1 << 30) * 17 // 16 + (1 << 20)
     st = lib.qsa_select_blocks(vp(P), vp(P), 1, I64(131072), I64(0), None, I64(32768), 4, 128, 4,
                                0, 512, vp(P), vp(P), vp(P), ctypes.c_size_t(need - 1), None,
                                None)
