@@ -605,7 +605,11 @@ __device__ __forceinline__ void stream_row(const TopkArgs &a, int64_t row,
     const int l4 = 4 * lane;
 
     // ---- pass 1: group maxima -> floor
-    const uint32_t *gm = a.gmax ? a.gmax + row * a.gld : nullptr;
+    // (the precomputed 16-block maxima when they are at least as many groups
+    // as the per-lane maxima below, 4 per thread: a looser floor could
+    // overflow the lists)
+    const uint32_t *gm =
+        a.gmax && ((n + 15) >> 4) >= 4 * kStNT ? a.gmax + row * a.gld : nullptr;
     if (gm) {
         // the precomputed maxima of the ceil(n / 16) groups holding blocks
         for (int i = tid; i < kBins; i += kStNT) sh.hist[i] = 0u;

@@ -298,15 +298,18 @@ def test_selection_tie_band(qsa, mode):
                                             (0, 37, 5, 3), (0, 300, 2000, 100),
                                             (1, 400, 12000, 1024), (0, 1300, 60000, 512),
                                             (1, 700, 140000, 512), (0, 300, 1048000, 512),
-                                            (1, 260, 1048000, 2048)])
+                                            (1, 260, 1048000, 2048), (0, 600, 100000, 512),
+                                            (0, 2000, 64000, 512)])
 def test_select_matches_scores_plus_topk(qsa, mode, Tq, pos0, K):
     """qsa_select_blocks returns exactly what qsa_index_scores followed by
     qsa_topk_blocks returns (same scores bit for bit, same tie order);
     RELUSUM rows near nc = K put the K-th score on a run of exact zeros.
-    Chunks of >= 256 rows longer than 12,288 blocks take the streaming top-K
-    with the indexer's 16-block group maxima (floor from the maxima, groups
-    below it never read); qsa_topk_blocks alone reads the scores only, so the
-    two paths must agree exactly, RELUSUM zero runs and 1M rows included."""
+    Chunks of >= 256 rows longer than 12,288 blocks take the streaming top-K;
+    rows with at least 4 groups of 16 blocks per thread take its floor from
+    the indexer's 16-block group maxima and never read the groups below it
+    (1M rows, 25K-block rows, and a chunk whose rows straddle that bound);
+    qsa_topk_blocks alone reads the scores only, so the paths must agree
+    exactly, RELUSUM zero runs included."""
     torch = _torch()
     Tk = pos0 + Tq
     qi = synth.normal_bf16(4, (Tq, 4, 128), seed=13)
