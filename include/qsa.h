@@ -183,8 +183,10 @@ int qsa_topk_blocks(const float *scores, int B, int64_t Tq, int64_t ld, int64_t 
  * by qsa_topk_blocks (same scores bit for bit, same tie order).  The scores
  * live in the caller's workspace (qsa_select_workspace_bytes, 16-byte
  * aligned), one chunk of query rows at a time (at most 1 GiB of fp32 scores
- * per chunk, plus the top-K candidate lists of the chunk), so the workspace
- * stays bounded at any Tq; the decode form keeps one row per sequence, and
+ * per chunk, the largest score of every 16 blocks of each row, from which
+ * the top-K of long rows takes its floor and skips the groups below it, and
+ * the top-K candidate lists of the chunk), so the workspace stays bounded at
+ * any Tq; the decode form keeps one row per sequence, and
  * for long rows also the maxima of every 64 blocks and the candidate lists
  * of a filter pass (about 12 bytes per block and sequence in all).
  * Supported: as the two calls, and nb_max < 2^27. */
