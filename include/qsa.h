@@ -182,7 +182,7 @@ int qsa_topk_blocks(const float *scores, int B, int64_t Tq, int64_t ld, int64_t 
 /* ---- A3 + A4 in one call: exactly the result of qsa_index_scores followed
  * by qsa_topk_blocks (same scores bit for bit, same tie order).  The scores
  * live in the caller's workspace (qsa_select_workspace_bytes, 16-byte
- * aligned), one chunk of query rows at a time (at most 1 GiB of fp32 scores
+ * aligned), one chunk of query rows at a time (at most 4 GiB of fp32 scores
  * per chunk, the largest score of every 16 blocks of each row, from which
  * the top-K of long rows takes its floor and skips the groups below it, and
  * the top-K candidate lists of the chunk), so the workspace stays bounded at
@@ -261,7 +261,7 @@ int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, i
  * [Tq][Hi][Di]; kbar: [Tk / r][Di] (the indexer inputs as for
  * qsa_index_scores); kl: fp32 [Tq].  The attention probabilities and the
  * per-block teacher never leave the kernel; the indexer scores of one chunk
- * of rows pass through the workspace (at most 1 GiB).
+ * of rows pass through the workspace (at most 4 GiB).
  * Workspace: qsa_distill_workspace_bytes (0 when Tk < r: ws may be NULL).
  * Supported: H = 24, Hkv = 2, D = 256, Hi = 4, Di = 128, r = 4. */
 size_t qsa_distill_workspace_bytes(int64_t Tq, int64_t Tk);

@@ -96,10 +96,10 @@ def test_distill_tiny_contexts(qsa):
 
 
 def test_distill_million_token_context_several_chunks(qsa):
-    """2,200 queries ending a 1,048,576-token context: the row chunks of the
-    workspace (1,024 rows at this length) split them 1024 + 1024 + 152; rows
+    """8,500 queries ending a 1,048,576-token context: the row chunks of the
+    workspace (4,096 rows at this length) split them 4096 + 4096 + 308; rows
     at and next to each chunk edge against the oracle."""
-    Tk, Tq = 1 << 20, 2200
+    Tk, Tq = 1 << 20, 8500
     pos0 = Tk - Tq
     K = synth.normal_bf16(synth.STREAM_K, (Tk, 2, 256), seed=86)
     ki = synth.normal_bf16(synth.STREAM_KIDX, (Tk, 128), seed=86)
@@ -108,7 +108,7 @@ def test_distill_million_token_context_several_chunks(qsa):
     Qr = oracle.rope(Q, pos0=pos0)
     kb = oracle.compress(ki)
     got = run_distill(qsa, Qr, K, qi, kb, Tq, pos0)
-    rows = np.array([0, 1023, 1024, 1025, 2047, 2048, 2199])
+    rows = np.array([0, 4095, 4096, 4097, 8191, 8192, 8499])
     ref = oracle.distill_rows(Qr, K, qi, kb, rows, pos0)
     check_kl(got[rows], ref, "1M context, chunk edges")
     assert np.all(np.isfinite(got)) and np.all(got >= -1e-6)
