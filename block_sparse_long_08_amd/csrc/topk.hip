@@ -530,10 +530,12 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
 // two more streaming passes; the result is the same.
 // With the scores' 16-block group maxima at hand (gmax), pass 1 reads those
 // instead of the row, and pass 2 loads only the groups whose maximum reaches
-// the floor (the others hold no key at or above it): the wave takes its
-// groups 64 at a time, one per lane (the next batch's maxima load while this
-// one is processed), lists the surviving ones in order and loads their keys
-// 16 groups at a time, 4 lanes per group, so lane order stays block order.
+// the floor (the others hold no key at or above it): each lane takes 8
+// consecutive groups of its wave's range at a time, a wave prefix sum over
+// the lanes' survivor counts places the surviving groups in order in an LDS
+// list, and their keys are loaded 64 groups at a time (4 steps of 16 groups,
+// 4 lanes per group, all loads issued before the ordered appends), so lane
+// order stays block order.
 template <int NT>
 struct StreamSmem {
     static constexpr int CAP = NT >= 1024 ? 256 : 512;  // list entries per wave
@@ -637,29 +639,52 @@ __device__ __forceinline__ void stream_row(const TopkArgs &a, int64_t row,
     // ---- pass 2: candidate lists
     uint32_t wc = 0;  // wave-uniform
     if (gm) {
+        constexpr int kQ = 8;  // consecutive groups per lane and round
         const int g_lo = w0 >> 4, g_hi = (w1 + 15) >> 4;
         int32_t *gl = sm.glist[wave];
-        uint32_t gnext = g_lo + lane < g_hi ? gm[g_lo + lane] : 0u;
-        for (int g0 = g_lo; g0 < g_hi; g0 += kWave) {
-            const uint32_t gcur = gnext;
-            gnext = g0 + kWave + lane < g_hi ? gm[g0 + kWave + lane] : 0u;
-            const bool keep = g0 + lane < g_hi && gcur >= floor_key;
-            const uint64_t bal = __ballot(keep);
-            if (bal == 0) continue;
-            if (keep) gl[lanes_below(bal)] = g0 + lane;
-            wave_lds_sync();
-            const int nsurv = __popcll(bal);
-            for (int j = 0; j < nsurv; j += 16) {
-                const int sidx = j + (lane >> 2);
-                uint32_t kk[4] = {0u, 0u, 0u, 0u};
-                int i = 0;
-                if (sidx < nsurv) {
-                    i = 16 * gl[sidx] + 4 * (lane & 3);
-                    stream_keys(s, i, w1, kk);
-                }
-                stream_append(kk, floor_key, i, kCap, wc, sm.ckey[wave], sm.cidx[wave]);
+        for (int r0 = g_lo; r0 < g_hi; r0 += kWave * kQ) {
+            const int gb = r0 + kQ * lane;
+            uint32_t gk[kQ];
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) {
+                gk[q] = gb + q < g_hi ? gm[gb + q] : 0u;
+                cnt += gk[q] >= floor_key ? 1u : 0u;
             }
-            wave_lds_sync();  // the list is rewritten by the next batch
+            const uint32_t incl = wave_incl_scan(cnt, lane);
+            const uint32_t total = static_cast<uint32_t>(__shfl(static_cast<int>(incl), kWave - 1));
+            for (uint32_t p0 = 0; p0 < total; p0 += kWave) {
+                // the survivors at list positions p0 .. p0+63
+                uint32_t pos = incl - cnt;
+#pragma unroll
+                for (int q = 0; q < kQ; ++q) {
+                    if (gk[q] >= floor_key) {
+                        if (pos >= p0 && pos < p0 + kWave) gl[pos - p0] = gb + q;
+                        ++pos;
+                    }
+                }
+                wave_lds_sync();
+                const int np = static_cast<int>(min(total - p0, static_cast<uint32_t>(kWave)));
+                uint32_t kk[4][4];
+                int ii[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int sidx = 16 * u + (lane >> 2);
+                    ii[u] = 0;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) kk[u][c] = 0u;
+                    if (sidx < np) {
+                        ii[u] = 16 * gl[sidx] + 4 * (lane & 3);
+                        stream_keys(s, ii[u], w1, kk[u]);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (16 * u < np)
+                        stream_append(kk[u], floor_key, ii[u], kCap, wc, sm.ckey[wave],
+                                      sm.cidx[wave]);
+                wave_lds_sync();  // the list is rewritten by the next piece
+            }
         }
     } else {
         for (int base = w0; base < w1; base += 1024) {
@@ -1271,7 +1296,9 @@ hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64
     if (pl.stream) {
         a.gmax = seq_len ? nullptr : gmax;
         a.gld = gld;
-        if (pl.stream_nt == 1024)
+        // with the group maxima a row's passes are short: 256 threads, so
+        // that more rows are in flight per CU
+        if (pl.stream_nt == 1024 && !a.gmax)
             hipLaunchKernelGGL(topk_stream<1024>, dim3(static_cast<uint32_t>(rows)), dim3(1024), 0,
                                s, a);
         else
