@@ -283,7 +283,7 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a) {
     const int tail = static_cast<int>((p + 1) % kBlock);
     if (PAGED && threadIdx.x == 0 && tail > 0)
         lst[ns] = static_cast<int32_t>(page_row(ptab, a.pshift, 4 * nc) >> 2);
-    __syncthreads();
+    block_sync();
     EntryList<false, PAGED ? 1 : 0> L{lst, 0, ns, tail, nc};
     if (PAGED) p = page_row(ptab, a.pshift, p);  // the safe row for masked tokens
     const int E = ns + (L.tail > 0 ? 1 : 0);
@@ -376,7 +376,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit
         }
     }
     EntryList<MULTI, PMODE> L{DENSE ? nullptr : lst, e_lo, ns, tail, nc, ptab, a.pshift};
-    __syncthreads();
+    block_sync();
 
     // position of this lane's column query (-1: no query, every token masked)
     const int pair = 16 * ct + (lane & 15);
@@ -393,10 +393,10 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit
     state_init(st);
     for (int sidx = s0 + wave; sidx < s1; sidx += 4)
         attn_stage(L, sidx * kStageEntries, psafe, pq, Kg, Vg, rs, qT, st, vlds, lane);
-    __syncthreads();
+    block_sync();
     float *mbuf = reinterpret_cast<float *>(lds);
     if (wave != 0) state_store(st, mbuf + (wave - 1) * kRecFloats, lane);
-    __syncthreads();
+    block_sync();
     if (wave == 0) {
         for (int w = 0; w < 3; ++w) state_merge(st, mbuf + w * kRecFloats, lane);
         st.l = head_total(st.l);

@@ -132,7 +132,7 @@ distill_kl_kernel(const uint16_t *__restrict__ Q, const float *__restrict__ lse,
             rd[wave][n][4 * ct + g4] = tsum;
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile it + 1 has landed
-        __syncthreads();
+        block_sync();
         // rd is written again two tiles on, after the next barrier
         if (live) {
             // the 24 heads in a fixed order: KV head 0's waves, then KV head 1's
@@ -153,7 +153,7 @@ distill_kl_kernel(const uint16_t *__restrict__ Q, const float *__restrict__ lse,
     };
     if (ntiles > 0) dma_tile(0, kt0);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 has landed
-    __syncthreads();
+    block_sync();
     for (int it = 0; it < ntiles; it += 2) {
         step(it, kt0, kt1, red0);
         if (it + 1 < ntiles) step(it + 1, kt1, kt0, red1);

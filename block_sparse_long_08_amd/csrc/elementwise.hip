@@ -51,7 +51,7 @@ __global__ void __launch_bounds__(256) rope_kernel(const uint16_t *__restrict__ 
         cs[j] = c;
         sn[j] = s;
     }
-    __syncthreads();
+    block_sync();
     const uint16_t *xr = x + t * nheads * static_cast<int64_t>(head_dim);
     uint16_t *yr = y + t * nheads * static_cast<int64_t>(head_dim);
     for (int idx = threadIdx.x; idx < nheads * half; idx += blockDim.x) {

@@ -208,7 +208,7 @@ __global__ void __launch_bounds__(256) fa_prefill_kernel(FaArgs a) {
 
     for (int it = 0; it < ntiles; ++it) {
         const int cur = it & 1;
-        __syncthreads();  // tile `it` is in LDS; tile it-1's buffers are free
+        block_sync();  // tile `it` is in LDS; tile it-1's buffers are free
         const int64_t tile0 = static_cast<int64_t>(it) * kFaN;
         // next tile into registers while this one is consumed (after the last
         // tile this fetches clamped rows into a buffer nothing reads)

@@ -111,7 +111,7 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
     for (int64_t tile = tile_begin; tile < tile_end; ++tile) {
         const int cur = static_cast<int>((tile - tile_begin) & 1);
         unsigned char *buf = lds + cur * kTileBytes;
-        __syncthreads();  // tile ready; the other buffer is free
+        block_sync();  // tile ready; the other buffer is free
         // next tile into registers (past the last tile: a clamped re-read of
         // rows nothing will use)
         load_tile<PAGED>(kbar, nb_rows, tile + 1, ld_bl, ld_part, kv0, kv1, kv2, kv3, ptab,

@@ -45,6 +45,17 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Workgroup barrier that publishes LDS data: the wave's own LDS operations
+// are waited for (lgkmcnt(0)) before s_barrier.  The compiler's barrier can
+// omit that wait, e.g. for LDS stores at the end of a loop body followed by
+// the barrier at the top of the next iteration; other waves could then read
+// rows still being written, which was observed when other kernels' LDS DMA
+// loaded the CU.
+__device__ __forceinline__ void block_sync() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __syncthreads();
+}
+
 // Indexer head combination of one query's four head dot products (held by one
 // lane as rows 4*g4 .. 4*g4+3 of a 16x16 MFMA tile).  MODE 0: max over heads
 // scaled by 1/sqrt(128); MODE 1: sum of ReLUs.  Shared by every kernel that

@@ -130,7 +130,7 @@ __device__ __forceinline__ void block_find(const uint32_t *h, uint32_t krem, Top
     }
     const uint32_t x = wave_incl_scan(local, lane);
     if (lane == kWave - 1) sh.wtot[wave] = x;
-    __syncthreads();
+    block_sync();
     uint32_t before = 0, total = 0;
 #pragma unroll
     for (int wv = 0; wv < TopkSmem<NT>::NW; ++wv) {
@@ -151,7 +151,7 @@ __device__ __forceinline__ void block_find(const uint32_t *h, uint32_t krem, Top
         }
     }
     if (tid == 0) sh.total = total;
-    __syncthreads();
+    block_sync();
 }
 
 // The same search by one wave over 1024 bins; returns the digit, the count
@@ -281,7 +281,7 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
         constexpr int NREP = TopkSmem<NT>::NREP;
         for (int i = tid; i < kBins * NREP / 4; i += NT)
             reinterpret_cast<uint4 *>(sh.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
-        __syncthreads();
+        block_sync();
         const int rep = lane % NREP;
 #pragma unroll
         for (int j = 0; j < NSL; ++j) {
@@ -291,7 +291,7 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
                     atomicAdd(&sh.hist[(k[4 * j + c] >> 20) * NREP + rep], 1u);
             }
         }
-        __syncthreads();
+        block_sync();
         block_find<NT, kBins, NREP, true>(sh.hist, K, sh, tid, lane, wave);
         if (sh.total <= K) {
             all = true;  // the segment holds at most K keys
@@ -317,7 +317,7 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
                 }
             }
             if (lane == 0) sh.wcnt[wave] = wc;
-            __syncthreads();  // lists written; every thread is done with hist
+            block_sync();  // lists written; every thread is done with hist
             bool overflow = false;
 #pragma unroll
             for (int w = 0; w < NW; ++w) overflow |= sh.wcnt[w] > kWaveCap;
@@ -362,14 +362,14 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
                         sh.eqcnt = cnt;
                     }
                 }
-                __syncthreads();
+                block_sync();
             } else {
                 // crowded bin: resolve block-wide over the registers
                 uint32_t cnt = 0;
                 for (int pass = 0; pass < 2; ++pass) {
                     const int shift = 10 - 10 * pass;
                     for (int i = tid; i < 1024; i += NT) sh.hist[i] = 0u;
-                    __syncthreads();
+                    block_sync();
 #pragma unroll
                     for (int j = 0; j < NSL; ++j) {
                         if (j < nsl) {
@@ -381,21 +381,21 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
                             }
                         }
                     }
-                    __syncthreads();
+                    block_sync();
                     block_find<NT, 1024, 1, false>(sh.hist, krem, sh, tid, lane, wave);
                     const uint32_t d = sh.fd_bin;
                     prefix |= d << shift;
                     mask |= 1023u << shift;
                     krem -= sh.fd_above;
                     cnt = sh.hist[d];
-                    __syncthreads();
+                    block_sync();
                 }
                 if (tid == 0) {
                     sh.thr = prefix;
                     sh.quota = krem;
                     sh.eqcnt = cnt;
                 }
-                __syncthreads();
+                block_sync();
             }
             thr = sh.thr;
             quota = sh.quota;
@@ -427,7 +427,7 @@ __global__ void __launch_bounds__(NT) topk_pass(TopkArgs a) {
         }
     }
     if (lane == 0) sh.wtot[wave] = (eq_w << 16) | gt_w;  // each <= 64*VPT <= 2048
-    __syncthreads();
+    block_sync();
     uint32_t gt_off = 0, eq_off = 0, gt_all = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -615,7 +615,7 @@ __device__ __forceinline__ void stream_row(const TopkArgs &a, int64_t row,
     if (gm) {
         // the precomputed maxima of the ceil(n / 16) groups holding blocks
         for (int i = tid; i < kBins; i += kStNT) sh.hist[i] = 0u;
-        __syncthreads();
+        block_sync();
         const int ng = (n + 15) >> 4;
         for (int i = tid; i < ng; i += kStNT) atomicAdd(&sh.hist[gm[i] >> 20], 1u);
     } else {
@@ -628,11 +628,11 @@ __device__ __forceinline__ void stream_row(const TopkArgs &a, int64_t row,
             for (int u = 0; u < 4; ++u) lm[u] = max(lm[u], max4(kk[u]));
         }
         for (int i = tid; i < kBins; i += kStNT) sh.hist[i] = 0u;
-        __syncthreads();
+        block_sync();
 #pragma unroll
         for (int u = 0; u < 4; ++u) atomicAdd(&sh.hist[lm[u] >> 20], 1u);
     }
-    __syncthreads();
+    block_sync();
     block_find<kStNT, kBins, 1, true>(sh.hist, K, sh, tid, lane, wave);
     const uint32_t floor_key = sh.total >= K ? sh.fd_bin << 20 : kMinKey;
 
@@ -698,7 +698,7 @@ __device__ __forceinline__ void stream_row(const TopkArgs &a, int64_t row,
         }
     }
     if (lane == 0) sh.wcnt[wave] = wc;
-    __syncthreads();
+    block_sync();
     bool overflow = false;
     uint32_t total_c = 0;
 #pragma unroll
@@ -713,16 +713,16 @@ __device__ __forceinline__ void stream_row(const TopkArgs &a, int64_t row,
             thr = floor_key;  // exactly K keys reach the floor: take them all
         } else {
             // first digit over the lists
-            __syncthreads();  // every thread has read wcnt / the floor histogram
+            block_sync();  // every thread has read wcnt / the floor histogram
             for (int i = tid; i < kBins; i += kStNT) sh.hist[i] = 0u;
-            __syncthreads();
+            block_sync();
             for (int i = lane; i < static_cast<int>(wc); i += kWave)
                 atomicAdd(&sh.hist[sm.ckey[wave][i] >> 20], 1u);
-            __syncthreads();
+            block_sync();
             block_find<kStNT, kBins, 1, true>(sh.hist, K, sh, tid, lane, wave);
             const uint32_t bin = sh.fd_bin;
             uint32_t krem = K - sh.fd_above;
-            __syncthreads();  // done with the histogram
+            block_sync();  // done with the histogram
             if (wave == 0) {
                 uint32_t *h = sh.hist;
                 uint32_t prefix = bin << 20, mask = 0xFFF00000u, cnt = 0;
@@ -759,7 +759,7 @@ __device__ __forceinline__ void stream_row(const TopkArgs &a, int64_t row,
                     sh.eqcnt = cnt;
                 }
             }
-            __syncthreads();
+            block_sync();
             thr = sh.thr;
             quota = sh.quota;
             eqcnt = sh.eqcnt;
@@ -781,7 +781,7 @@ __device__ __forceinline__ void stream_row(const TopkArgs &a, int64_t row,
             sh.wtot[wave] = gt_w;
             sm.eqtot[wave] = eq_w;
         }
-        __syncthreads();
+        block_sync();
         uint32_t gt_off = 0, eq_off = 0, gt_all = 0;
 #pragma unroll
         for (int w = 0; w < kStNW; ++w) {
@@ -822,9 +822,9 @@ __device__ __forceinline__ void stream_row(const TopkArgs &a, int64_t row,
     for (int pass = 0; pass < 3; ++pass) {
         const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
         const uint32_t dmask = pass == 0 ? 4095u : 1023u;
-        __syncthreads();
+        block_sync();
         for (int i = tid; i < kBins; i += kStNT) sh.hist[i] = 0u;
-        __syncthreads();
+        block_sync();
         for (int base = w0; base < w1; base += 256) {
             uint32_t kk[4];
             stream_keys(s, base + l4, w1, kk);
@@ -833,7 +833,7 @@ __device__ __forceinline__ void stream_row(const TopkArgs &a, int64_t row,
                 if (kk[c] != 0u && (kk[c] & mask) == prefix)
                     atomicAdd(&sh.hist[(kk[c] >> shift) & dmask], 1u);
         }
-        __syncthreads();
+        block_sync();
         if (pass == 0)
             block_find<kStNT, kBins, 1, true>(sh.hist, krem, sh, tid, lane, wave);
         else
@@ -857,12 +857,12 @@ __device__ __forceinline__ void stream_row(const TopkArgs &a, int64_t row,
             eq_w += static_cast<uint32_t>(__popcll(__ballot(split && kk[c] == thr)));
         }
     }
-    __syncthreads();
+    block_sync();
     if (lane == 0) {
         sh.wtot[wave] = gt_w;
         sm.eqtot[wave] = eq_w;
     }
-    __syncthreads();
+    block_sync();
     uint32_t gt_off = 0, eq_off = 0, gt_all = 0;
 #pragma unroll
     for (int w = 0; w < kStNW; ++w) {
@@ -956,7 +956,7 @@ __device__ __forceinline__ void block_minmax(uint32_t &lo, uint32_t &hi, TopkSme
         sh.wtot[wave] = lo;
         sh.wcnt[wave] = hi;
     }
-    __syncthreads();
+    block_sync();
 #pragma unroll
     for (int w = 0; w < NT / kWave; ++w) {
         lo = min(lo, sh.wtot[w]);
@@ -1016,7 +1016,7 @@ __global__ void __launch_bounds__(256) topk_dec_filter(DecTopkArgs d) {
             if (tid + NT * j < ngrp) atomicAdd(&sh.hist[(gv[j] - lo) >> shift], 1u);
         for (int i = tid + 16 * NT; i < ngrp; i += NT)
             atomicAdd(&sh.hist[(g[i] - lo) >> shift], 1u);
-        __syncthreads();
+        block_sync();
         block_find<NT, kBins, 1, false>(sh.hist, K, sh, tid, lane, wave);
         floor_key = max(lo + (sh.fd_bin << shift), kMinKey);
     }
@@ -1029,7 +1029,7 @@ __global__ void __launch_bounds__(256) topk_dec_filter(DecTopkArgs d) {
         for (int c = 0; c < 4; ++c)
             wc += static_cast<uint32_t>(__popcll(__ballot(kk[u][c] >= floor_key)));
     if (lane == 0) sh.wcnt[wave] = wc;
-    __syncthreads();
+    block_sync();
     uint32_t off = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < NT / kWave; ++w) {
@@ -1103,10 +1103,10 @@ __global__ void __launch_bounds__(1024) topk_dec_final(DecTopkArgs d) {
         }
         if (lane == 0) f.segoff[nseg] = carry;
     }
-    __syncthreads();
+    block_sync();
     const uint32_t total = f.segoff[nseg];
     if (total > static_cast<uint32_t>(kDecListCap)) {
-        __syncthreads();  // segoff read by all before the union is reused
+        block_sync();  // segoff read by all before the union is reused
         stream_row<NT>(a, row, lds.st);
         return;
     }
@@ -1136,7 +1136,7 @@ __global__ void __launch_bounds__(1024) topk_dec_final(DecTopkArgs d) {
         }
     }
     for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;
-    __syncthreads();
+    block_sync();
 
     uint32_t thr = 0, quota = 0, eqcnt = 0;
     bool split = false;
@@ -1160,7 +1160,7 @@ __global__ void __launch_bounds__(1024) topk_dec_final(DecTopkArgs d) {
                 if (s_prev == 32 || (v >> s_prev) == hp)
                     atomicAdd(&sh.hist[(v >> s) & dmask], 1u);
             }
-            __syncthreads();
+            block_sync();
             block_find<NT, kBins, 1, false>(sh.hist, krem, sh, tid, lane, wave);
             const uint32_t dg = sh.fd_bin;
             krem -= sh.fd_above;
@@ -1169,9 +1169,9 @@ __global__ void __launch_bounds__(1024) topk_dec_final(DecTopkArgs d) {
             if (s == 0) break;
             s_prev = s;
             s = s > 12 ? s - 12 : 0;
-            __syncthreads();  // every thread has read the histogram
+            block_sync();  // every thread has read the histogram
             for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;
-            __syncthreads();
+            block_sync();
         }
         thr = lo + hp;
         quota = krem;
@@ -1188,12 +1188,12 @@ __global__ void __launch_bounds__(1024) topk_dec_final(DecTopkArgs d) {
         gt_w += static_cast<uint32_t>(__popcll(__ballot(gt)));
         eq_w += static_cast<uint32_t>(__popcll(__ballot(split && key == thr)));
     }
-    __syncthreads();  // every thread has read the histogram
+    block_sync();  // every thread has read the histogram
     if (lane == 0) {
         sh.wtot[wave] = gt_w;
         f.eqtot[wave] = eq_w;
     }
-    __syncthreads();
+    block_sync();
     uint32_t gt_off = 0, eq_off = 0, gt_all = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {

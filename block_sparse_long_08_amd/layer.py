@@ -29,12 +29,19 @@ class QSAPrefill:
     idx_rope_dim > 0: partial RoPE on the indexer (pooled keys rotated at their
     block's first token, indexer queries at their own positions); kbar_gain:
     the RMSNorm gain of the pooled keys (kbar_mode RMSNORM), bf16 [DI].
+
+    pipeline_rows > 0 (and < Tq): the queries are selected in chunks of that
+    many rows, and each chunk's sparse attention runs on a second stream
+    while the next chunk is selected (selection is MFMA and ALU work, the
+    attention streams gathers from HBM, so the two overlap); the results are
+    those of the stages run one after the other.
     """
 
     def __init__(self, Tq: int, pos0: int = 0, H: int = 24, Hkv: int = 2, D: int = 256,
                  budget: int = 512, score_mode: int = SCORE_MAXHEAD, kbar_mode: int = KBAR_MEAN,
                  theta: float = 1e7, rope_dim: int = 64, fresh: bool = True,
-                 idx_rope_dim: int = 0, kbar_gain=None, pages=None, device="cuda"):
+                 idx_rope_dim: int = 0, kbar_gain=None, pages=None, pipeline_rows: int = 4096,
+                 device="cuda"):
         self.Tq, self.pos0, self.H, self.Hkv, self.D = Tq, pos0, H, Hkv, D
         self.pages = pages  # paged caches (fresh=False): K, V and kbar are page pools
         self.Tk = pos0 + Tq
@@ -52,8 +59,11 @@ class QSAPrefill:
         self.n_sel = torch.empty((Tq,), dtype=torch.int32, device=dev)
         self.O = torch.empty((Tq, H, D), dtype=torch.float32, device=dev)
         self.lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
-        self.ws_bytes = qsa_select_workspace_bytes(1, Tq, self.nb, budget)
+        self.pipeline_rows = pipeline_rows if 0 < pipeline_rows < Tq else 0
+        self.ws_bytes = qsa_select_workspace_bytes(1, self.pipeline_rows or Tq, self.nb, budget)
         self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=dev)
+        # the attention stream of the pipeline (default priority)
+        self.side = torch.cuda.Stream(device=dev) if self.pipeline_rows else None
         self.qir = (torch.empty((Tq, HI, DI), dtype=torch.bfloat16, device=dev)
                     if idx_rope_dim else None)
 
@@ -80,20 +90,64 @@ class QSAPrefill:
         qsa_rope_bf16(qi, self.qir, self.Tq, HI, DI, self.idx_rope_dim, self.theta, self.pos0)
         return self.qir
 
+    def _chunks(self):
+        c = self.pipeline_rows or self.Tq
+        return [(r0, min(c, self.Tq - r0)) for r0 in range(0, self.Tq, c)]
+
+    def _select_rows(self, qi, kbar, r0, n):
+        qsa_select_blocks(qi[r0:r0 + n], kbar, 1, n, self.pos0 + r0, None, self.nb, HI, DI, R,
+                          self.score_mode, self.budget, self.blk_idx[r0:r0 + n],
+                          self.n_sel[r0:r0 + n], self.ws, self.ws_bytes, pages=self.pages)
+
+    def _attend_rows(self, Kr, V, r0, n):
+        p0 = self.pos0 + r0
+        qsa_sparse_attn_prefill(self.Qr[r0:r0 + n], Kr, V, self.blk_idx[r0:r0 + n],
+                                self.n_sel[r0:r0 + n], n, p0 + n, p0, self.H, self.Hkv, self.D, R,
+                                self.budget, self.O[r0:r0 + n], self.lse[r0:r0 + n],
+                                pages=self.pages)
+
     def select(self, qi, kbar):
-        qsa_select_blocks(qi, kbar, 1, self.Tq, self.pos0, None, self.nb, HI, DI, R,
-                          self.score_mode, self.budget, self.blk_idx, self.n_sel, self.ws,
-                          self.ws_bytes, pages=self.pages)
+        for r0, n in self._chunks():
+            self._select_rows(qi, kbar, r0, n)
 
     def attend(self, Kr, V):
-        qsa_sparse_attn_prefill(self.Qr, Kr, V, self.blk_idx, self.n_sel, self.Tq, self.Tk,
-                                self.pos0, self.H, self.Hkv, self.D, R, self.budget, self.O,
-                                self.lse, pages=self.pages)
+        self._attend_rows(Kr, V, 0, self.Tq)
+
+    def select_and_attend(self, qi, kbar, Kr, V, attn_events=None, select_events=None):
+        """Selection and sparse attention of every row; with pipeline_rows,
+        the attention of each chunk on the second stream (after that chunk's
+        selection) overlaps the selection of the next.  attn_events /
+        select_events: lists that receive a timing event pair around each
+        attention launch / each chunk's selection."""
+        if not self.pipeline_rows:
+            self.select(qi, kbar)
+            self.attend(Kr, V)
+            return
+        main = torch.cuda.current_stream()
+        for r0, n in self._chunks():
+            if select_events is not None:
+                s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s0.record()
+            self._select_rows(qi, kbar, r0, n)
+            if select_events is not None:
+                s1.record()
+                select_events.append((s0, s1))
+            ready = torch.cuda.Event()
+            ready.record(main)
+            self.side.wait_event(ready)
+            with torch.cuda.stream(self.side):
+                if attn_events is not None:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                self._attend_rows(Kr, V, r0, n)
+                if attn_events is not None:
+                    e1.record()
+                    attn_events.append((e0, e1))
+        main.wait_stream(self.side)  # later work on the caller's stream sees O and lse
 
     def __call__(self, Q, K, V, qi, ki, kbar=None):
         Kr, kb = self.rope_and_pool(Q, K, ki, kbar)
-        self.select(self.rope_indexer(qi), kb)
-        self.attend(Kr, V)
+        self.select_and_attend(self.rope_indexer(qi), kb, Kr, V)
         return self.O, self.lse
 
 
