@@ -519,6 +519,12 @@ def main():
     dense_roof_ms = pre["dense_flop"] / (BF16_PEAK_TFLOPS * 1e12) * 1e3
     out["dense_prefill_at_mfma_peak_ms"] = dense_roof_ms
     out["prefill_speedup_vs_dense_at_mfma_peak"] = dense_roof_ms / pre["ms_per_step"]
+    # the step's MFMA work (indexer contraction and attention products) over
+    # its wall time: the composite share of the bf16 peak, low by design since
+    # the step is bound by the attention's gathers
+    comp = (pre["idx_flop"] + pre["attn_flop"]) / (pre["ms_per_step"] * 1e-3) / 1e12
+    out["composite_mfma"] = dict(tflops=comp, frac=comp / BF16_PEAK_TFLOPS,
+                                 flop=pre["idx_flop"] + pre["attn_flop"])
     if args.indexer_rope == "on":
         # the indexer with partial RoPE (64 of its 128 dims) on the 32K workload,
         # against the same workload without it
