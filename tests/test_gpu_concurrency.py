@@ -75,3 +75,38 @@ def test_pipelined_prefill_equals_sequential(qsa):
         del layer
     for name, a, b in zip(("blk_idx", "n_sel", "O", "lse"), *outs):
         assert np.array_equal(a, b), name
+
+
+@pytest.mark.parametrize("P", [0, 64])
+def test_pipelined_chunk_over_a_cache_equals_sequential(qsa, P):
+    """A prefill chunk against a post-RoPE cache (contiguous, or in 64-token
+    pages): the pipelined layer (256-row chunks) equals the stages run in
+    turn, bit for bit."""
+    import torch
+    from test_gpu_paged import page_layout, to_pool
+    pos0, Tq = 9000, 1800
+    Tk = pos0 + Tq
+    x = synth.prefill_inputs(Tq, pos0=pos0, seed=93, k_is_rotated=True)
+    pages = None
+    if P:
+        table, total = page_layout([Tk], Tk, P, seed=93)
+        pages = qsa.Pages(dev(table), P)
+        kc, vc = dev(to_pool(x.K[None], table, total, P)), dev(to_pool(x.V[None], table, total, P))
+    else:
+        kc, vc = dev(x.K), dev(x.V)
+    outs = []
+    for rows in (0, 256):
+        if P:
+            kbar = torch.full((total * P // 4, 128), -1, dtype=torch.int16, device="cuda")
+            qsa.qsa_compress_keys(dev(x.ki), 1, pos0, pos0 * 128, 128, 4, 0, kbar, 0, pages=pages)
+        else:
+            kbar = torch.full((Tk // 4, 128), -1, dtype=torch.int16, device="cuda")
+            qsa.qsa_compress_keys(dev(x.ki), 1, pos0, pos0 * 128, 128, 4, 0, kbar, (pos0 // 4) * 128)
+        layer = qsa.QSAPrefill(Tq, pos0=pos0, budget=512, fresh=False, pages=pages,
+                               pipeline_rows=rows)
+        O, lse = layer(dev(x.Q), kc, vc, dev(x.qi), dev(x.ki), kbar)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy().copy() for t in (layer.blk_idx, layer.n_sel, O, lse)])
+        del layer, kbar
+    for name, a, b in zip(("blk_idx", "n_sel", "O", "lse"), *outs):
+        assert np.array_equal(a, b), name
