@@ -85,6 +85,12 @@ def _load():
         lib.qsa_oracle_distill_rows.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32,
                                                 i32, i32, vp, i64, vp]
         lib.qsa_oracle_distill_rows.restype = None
+        lib.qsa_oracle_sparse_kl_row.argtypes = [vp, vp, i32, i32, i32, i64, i32, vp, i32, vp,
+                                                 vp, vp]
+        lib.qsa_oracle_sparse_kl_row.restype = dbl
+        lib.qsa_oracle_sparse_kl_rows.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32,
+                                                  i32, i32, i32, i32, vp, i64, vp, vp, vp]
+        lib.qsa_oracle_sparse_kl_rows.restype = None
         lib.qsa_oracle_f64_to_bf16.argtypes = [dbl]
         lib.qsa_oracle_f64_to_bf16.restype = ctypes.c_uint16
         lib.qsa_oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
@@ -360,4 +366,39 @@ def distill_rows(Q, K, qi, kbar, rows, pos0: int = 0, r: int = 4, mode: int = MO
     _load().qsa_oracle_distill_rows(_p(Q), _p(K), _p(qi), _p(kbar), kbar.shape[0], pos0, H,
                                     K.shape[1], D, qi.shape[1], qi.shape[2], r, mode, _p(rows),
                                     rows.size, _p(kl))
+    return kl
+
+
+def sparse_kl_row(q_row, K, p: int, blk, s_sel, r: int = 4):
+    """Distillation KL of one query at position p under the sparse pattern:
+    blk the selected blocks (ascending), s_sel their indexer scores.
+    Returns (KL, teacher T [nsel], ln S [nsel])."""
+    q_row = _c(q_row, np.uint16)
+    K = _c(K, np.uint16)
+    H, D = q_row.shape
+    blk = _c(blk, np.int32)
+    ns = blk.size
+    s_sel = _c(np.asarray(s_sel, dtype=np.float64).reshape(-1)[:ns], np.float64)
+    T = np.zeros(max(ns, 1))
+    lS = np.zeros(max(ns, 1))
+    kl = _load().qsa_oracle_sparse_kl_row(_p(q_row), _p(K), H, K.shape[1], D, p, r,
+                                          _p(blk if ns else np.zeros(1, np.int32)), ns,
+                                          _p(s_sel if ns else np.zeros(1)), _p(T), _p(lS))
+    return float(kl), T[:ns], lS[:ns]
+
+
+def sparse_kl_rows(Q, K, qi, kbar, rows, sel, nsel, pos0: int = 0, r: int = 4,
+                   mode: int = MODE_MAXHEAD):
+    """Distillation KL under the sparse pattern for query rows over a given
+    selection sel [n, Kbudget] / nsel [n] -> [n]."""
+    Q, K, qi, kbar = (_c(a, np.uint16) for a in (Q, K, qi, kbar))
+    rows = _c(rows, np.int64)
+    sel = _c(sel, np.int32)
+    nsel = _c(nsel, np.int32)
+    _, H, D = Q.shape
+    kl = np.empty(rows.size)
+    _load().qsa_oracle_sparse_kl_rows(_p(Q), _p(K), _p(qi), _p(kbar), kbar.shape[0], pos0, H,
+                                      K.shape[1], D, qi.shape[1], qi.shape[2], r, mode,
+                                      sel.shape[1], _p(rows), rows.size, _p(sel), _p(nsel),
+                                      _p(kl))
     return kl

@@ -509,3 +509,98 @@ void qsa_oracle_distill_rows(const uint16_t *Q, const uint16_t *K, const uint16_
         free(s);
     }
 }
+
+/* ---------- O9: distillation KL under the sparse pattern ------------------ */
+/* ai.info "Industry relevance": a fused QSA kernel yields the sparse
+ * attention outputs and the KL loss without storing intermediates; chlience
+ * section 6: in the second stage backbone and indexer train together under
+ * the sparse pattern.  Reading (the pages give no formula for this loss): the
+ * teacher is the sparse attention the layer actually computes, i.e. for each
+ * head the softmax over the query's token set (its nsel selected blocks and
+ * its incomplete block, O5), max-pooled within each selected block, summed
+ * over the heads and L1-normalised over the selected blocks; the student is
+ * the softmax of the indexer scores over the same selected blocks; the loss
+ * is KL(teacher || student) as in O8.  The incomplete block counts in each
+ * head's softmax but is not a block of either distribution.
+ *   blk[0..nsel) the selected blocks (ascending), s_sel[i] the score of blk[i].
+ * With every complete block selected this is O8.  Returns KL (0 when nsel is
+ * 0); T_out / logS_out (length nsel) if not NULL. */
+double qsa_oracle_sparse_kl_row(const uint16_t *q_row, const uint16_t *K, int H, int Hkv, int D,
+                                int64_t p, int r, const int32_t *blk, int nsel,
+                                const double *s_sel, double *T_out, double *logS_out) {
+    if (nsel <= 0) return 0.0;
+    int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nsel * r + r));
+    const int64_t ntok = qsa_oracle_token_set(blk, nsel, p, r, tok);
+    double *lg = (double *)malloc(sizeof(double) * (size_t)ntok);
+    double *Tb = (double *)calloc((size_t)nsel, sizeof(double));
+    const double qk_scale = 1.0 / sqrt((double)D);
+    for (int h = 0; h < H; ++h) {
+        const int kvh = h / (H / Hkv);
+        double mh = -INFINITY;
+        for (int64_t j = 0; j < ntok; ++j) {
+            const uint16_t *kr = K + (tok[j] * Hkv + kvh) * (int64_t)D;
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d) dot += bf16_to_f64(q_row[h * D + d]) * bf16_to_f64(kr[d]);
+            lg[j] = dot * qk_scale;
+            mh = lg[j] > mh ? lg[j] : mh;
+        }
+        double zh = 0.0;
+        for (int64_t j = 0; j < ntok; ++j) zh += exp(lg[j] - mh);
+        const double lse_h = mh + log(zh);
+        /* tokens i*r .. i*r + r - 1 of the set are selected block i */
+        for (int i = 0; i < nsel; ++i) {
+            double mb = 0.0;
+            for (int t = 0; t < r; ++t) {
+                const double a = exp(lg[(int64_t)i * r + t] - lse_h);
+                mb = a > mb ? a : mb;
+            }
+            Tb[i] += mb;
+        }
+    }
+    double tsum = 0.0, smax = -INFINITY;
+    for (int i = 0; i < nsel; ++i) {
+        tsum += Tb[i];
+        smax = s_sel[i] > smax ? s_sel[i] : smax;
+    }
+    double ssum = 0.0;
+    for (int i = 0; i < nsel; ++i) ssum += exp(s_sel[i] - smax);
+    const double s_lse = smax + log(ssum);
+    double acc = 0.0;
+    for (int i = 0; i < nsel; ++i) {
+        const double ti = Tb[i] / tsum, lsi = s_sel[i] - s_lse;
+        if (ti > 0.0) acc += ti * (log(ti) - lsi);
+        if (T_out) T_out[i] = ti;
+        if (logS_out) logS_out[i] = lsi;
+    }
+    free(tok);
+    free(lg);
+    free(Tb);
+    return acc;
+}
+
+/* O9 for rows of one sequence over a GIVEN selection sel [n][Kbudget] /
+ * nsel [n] (ascending blocks, as the attention rows above): the student's
+ * scores are O3's for the query at pos0 + rows[i] (indexer row qi[rows[i]],
+ * pooled keys kbar[nb][Di]), taken at the selected blocks. */
+void qsa_oracle_sparse_kl_rows(const uint16_t *Q, const uint16_t *K, const uint16_t *qi,
+                               const uint16_t *kbar, int64_t nb, int64_t pos0, int H, int Hkv,
+                               int D, int Hi, int Di, int r, int mode, int Kbudget,
+                               const int64_t *rows, int64_t n, const int32_t *sel,
+                               const int32_t *nsel, double *kl) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t t = rows[i];
+        int64_t p = pos0 + t;
+        int64_t nc_full = qsa_oracle_num_complete(p, r);
+        double *s = (double *)malloc(sizeof(double) * (size_t)(nc_full > 0 ? nc_full : 1));
+        qsa_oracle_scores_row(qi + t * Hi * (int64_t)Di, kbar, nb, p, Hi, Di, r, mode, s);
+        const int ns = nsel[i];
+        const int32_t *bi = sel + i * (int64_t)Kbudget;
+        double *s_sel = (double *)malloc(sizeof(double) * (size_t)(ns > 0 ? ns : 1));
+        for (int k = 0; k < ns; ++k) s_sel[k] = s[bi[k]];
+        kl[i] = qsa_oracle_sparse_kl_row(Q + t * H * (int64_t)D, K, H, Hkv, D, p, r, bi, ns,
+                                         s_sel, NULL, NULL);
+        free(s_sel);
+        free(s);
+    }
+}

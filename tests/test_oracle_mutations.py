@@ -48,6 +48,17 @@ MUTATIONS = {
     "distill_partial_block_dropped": ("for (int64_t j = 0; j <= p; ++j) z += exp(l[j] - m);",
                                       "for (int64_t j = 0; j < nc * r; ++j) z += exp(l[j] - m);"),
     "distill_scores_not_softmaxed": ("double lse_s = ms + log(zs);", "double lse_s = 0.0;"),
+    "sparse_kl_tail_out_of_softmax": ("for (int64_t j = 0; j < ntok; ++j) zh += exp(lg[j] - mh);",
+                                      "for (int64_t j = 0; j < (int64_t)nsel * r; ++j) zh += exp(lg[j] - mh);"),
+    "sparse_kl_mean_pool": ("mb = a > mb ? a : mb;", "mb += a / (double)r;"),
+    "sparse_kl_last_head_only": ("Tb[i] += mb;", "Tb[i] = mb;"),
+    "sparse_kl_gqa_mapping": ("const int kvh = h / (H / Hkv);", "const int kvh = h % Hkv;"),
+    "sparse_kl_reversed": ("if (ti > 0.0) acc += ti * (log(ti) - lsi);",
+                           "if (ti > 0.0) acc += exp(lsi) * (lsi - log(ti));"),
+    "sparse_kl_score_by_rank": ("for (int k = 0; k < ns; ++k) s_sel[k] = s[bi[k]];",
+                                "for (int k = 0; k < ns; ++k) s_sel[k] = s[k];"),
+    "sparse_kl_student_not_normalised": ("const double s_lse = smax + log(ssum);",
+                                         "const double s_lse = smax;"),
     "reuse_tail_from_own_block": ("int64_t from = qsa_oracle_num_complete(p_sel, r) * r;",
                                   "int64_t from = qsa_oracle_num_complete(p, r) * r;"),
     "reuse_tail_stops_short": ("for (int64_t j = from; j <= p; ++j) tok[n++] = j;",

@@ -638,3 +638,75 @@ def test_distill_rows_nonnegative_and_zero_at_teacher(oracle_lib, synth_lib):
     kl_t, T, _ = oracle_lib.distill_row(Q[70], K, 70, np.zeros(17))
     kl2, _, _ = oracle_lib.distill_row(Q[70], K, 70, np.log(T) + 3.0)
     assert abs(kl2) < 1e-12 and kl_t > 0
+
+
+# ----------------------------------------------------------------------------
+# Distillation KL under the sparse pattern: teacher = the sparse attention
+# (softmax over the selected blocks and the incomplete block) max-pooled per
+# selected block, heads summed, L1-normalised; student = softmax of the
+# selected blocks' scores.
+# ----------------------------------------------------------------------------
+
+def test_sparse_kl_planted_closed_form(oracle_lib):
+    """p = 30: complete blocks 0..6, incomplete block 28..30; blocks 1, 4, 6
+    selected.  Group 0 heads see c0 on token 17 (block 4) and c2 on token 29
+    (incomplete block); group 1 heads see c1 on token 5 (block 1) and c3 on
+    token 9 (block 2, not selected, so outside every softmax).  Each head's
+    softmax runs over the 15 tokens of the set."""
+    p, c0, c1, c2, c3 = 30, 2.5, 1.75, 3.0, 5.0
+    q, K = _distill_inputs(p, {(0, 17): c0, (0, 29): c2, (1, 5): c1, (1, 9): c3})
+    blk = np.array([1, 4, 6], dtype=np.int32)
+    s = np.array([0.3, -0.2, 1.1])
+    kl, T, lS = oracle_lib.sparse_kl_row(q, K, p, blk, s)
+    z0 = np.exp(c0) + np.exp(c2) + 13.0
+    z1 = np.exp(c1) + 14.0
+    m = 12 * np.array([1.0 / z0 + np.exp(c1) / z1,
+                       np.exp(c0) / z0 + 1.0 / z1,
+                       1.0 / z0 + 1.0 / z1])
+    want = m / m.sum()
+    ls = s - np.log(np.exp(s).sum())
+    assert np.allclose(T, want, atol=1e-14)
+    assert np.allclose(lS, ls, atol=1e-14)
+    assert abs(kl - np.sum(want * (np.log(want) - ls))) < 1e-13
+    # nothing selected: no distribution, KL 0
+    assert oracle_lib.sparse_kl_row(q, K, p, np.zeros(0, np.int32), np.zeros(0))[0] == 0.0
+
+
+def test_sparse_kl_with_every_block_selected_is_stage1(oracle_lib, synth_lib):
+    """A budget above nc(p) selects every complete block: the token set is
+    0..p, the sparse softmax is the dense one, and the KL equals the dense
+    distillation's (computed by its own code)."""
+    T_len = 90
+    Q, K, V, qi, ki = _small_inputs(synth_lib, T_len, seed=7)
+    kb = oracle_lib.compress(ki)
+    rows = np.arange(0, T_len, 5)
+    for mode in (oracle_lib.MODE_MAXHEAD, oracle_lib.MODE_RELUSUM):
+        sel = oracle_lib.select_rows(qi, kb, rows, Kbudget=32, mode=mode)
+        assert np.all(sel["nsel"] == np.array([oracle_lib.num_complete(t) for t in rows]))
+        got = oracle_lib.sparse_kl_rows(Q, K, qi, kb, rows, sel["sel"], sel["nsel"], mode=mode)
+        ref = oracle_lib.distill_rows(Q, K, qi, kb, rows, mode=mode)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-13), mode
+
+
+def test_sparse_kl_subset_rows_scores_and_bounds(oracle_lib, synth_lib):
+    """A budget of 5 below nc(p): the rows form takes each selected block's
+    own score (checked against the single-row form fed the selected entries of
+    the full score row); KL >= 0, = 0 when the scores are ln T + const, and the
+    subset KL differs from the dense one."""
+    T_len = 90
+    Q, K, V, qi, ki = _small_inputs(synth_lib, T_len, seed=8)
+    kb = oracle_lib.compress(ki)
+    rows = np.arange(30, T_len, 6)
+    sel = oracle_lib.select_rows(qi, kb, rows, Kbudget=5, want_scores=True)
+    got = oracle_lib.sparse_kl_rows(Q, K, qi, kb, rows, sel["sel"], sel["nsel"])
+    dense = oracle_lib.distill_rows(Q, K, qi, kb, rows)
+    for i, t in enumerate(rows):
+        ns = sel["nsel"][i]
+        assert ns == 5
+        blk = sel["sel"][i, :ns]
+        s = sel["s"][i, blk]
+        kl, T, _ = oracle_lib.sparse_kl_row(Q[t], K, int(t), blk, s)
+        assert abs(kl - got[i]) < 1e-13
+        assert kl >= -1e-12 and abs(kl - dense[i]) > 1e-6
+        kl0, _, _ = oracle_lib.sparse_kl_row(Q[t], K, int(t), blk, np.log(T) - 2.0)
+        assert abs(kl0) < 1e-12
