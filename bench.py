@@ -257,7 +257,24 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
                                   mfma_frac=teacher_flop / (kms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                                   dense_forward_ms=dms, forward_total_ms=dms + kms,
                                   mean_kl=float(kl.mean().item()))
-            del ws, kl
+            del ws
+            # second stage: the sparse attention fused with the KL under the
+            # sparse pattern, over the selection of the timed steps, in the
+            # attention's row chunks
+            fused = lambda: layer.attend_with_kl(Kr, V, qs, kb, kl)  # noqa: E731
+            fused()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(dsteps):
+                fused()
+            e1.record()
+            torch.cuda.synchronize()
+            fms = e0.elapsed_time(e1) / dsteps
+            res["sparse_kl"] = dict(ms=fms, launches=nlaunch, attend_ms=stage["attend"],
+                                    vs_attend=fms / stage["attend"],
+                                    hbm_gbps_algorithmic=attn_bytes / (fms * 1e-3) / 1e9,
+                                    mean_kl=float(kl.mean().item()))
+            del kl
     del layer
     torch.cuda.empty_cache()
     return res, x
@@ -511,6 +528,10 @@ def main():
         out["dense_prefill_ms"] = pre["dense_ms"]
         out["prefill_speedup_vs_dense"] = pre["dense_ms"] / pre["ms_per_step"]
         out["dense_prefill_tflops"] = pre["dense_flop"] / (pre["dense_ms"] * 1e-3) / 1e12
+    if "sparse_kl" in pre:
+        out["sparse_kl"] = dict(workload=args.workload, **pre["sparse_kl"])
+        log(f"sparse attention + KL {args.workload}: {pre['sparse_kl']['ms']:.2f} ms "
+            f"({pre['sparse_kl']['vs_attend']:.2f}x the attention alone)")
     if "distill" in pre:
         out["distill"] = dict(workload=args.workload, **pre["distill"])
         log(f"distill {args.workload}: {pre['distill']['ms']:.2f} ms "

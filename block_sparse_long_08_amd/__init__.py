@@ -62,13 +62,15 @@ _sig("dense_attn", _i32, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _i32,
 _sig("qsa_distill_workspace_bytes", _sz, _i64, _i64)
 _sig("qsa_distill_kl", _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
      _i32, _i32, _i32, _vp, _vp, _sz, _vp)
+_sig("qsa_sparse_attn_prefill_kl", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+     _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp)
 
 EXPORTED = ["qsa_status_string", "qsa_version", "qsa_check_device", "qsa_rope_bf16",
             "qsa_compress_keys", "qsa_index_scores", "qsa_topk_workspace_bytes",
             "qsa_topk_blocks", "qsa_select_workspace_bytes", "qsa_select_blocks",
             "qsa_sparse_attn_prefill", "qsa_decode_workspace_bytes", "qsa_sparse_attn_decode",
             "dense_attn_workspace_bytes", "dense_attn", "qsa_distill_workspace_bytes",
-            "qsa_distill_kl"]
+            "qsa_distill_kl", "qsa_sparse_attn_prefill_kl"]
 
 SCORE_MAXHEAD, SCORE_RELUSUM = 0, 1
 KBAR_MEAN, KBAR_RMSNORM = 0, 1
@@ -213,6 +215,14 @@ def qsa_distill_kl(Q, K, lse, q_idx, kbar, Tq: int, Tk: int, pos0: int, H: int, 
                    stream=None) -> None:
     _call("qsa_distill_kl", _ptr(Q), _ptr(K), _ptr(lse), _ptr(q_idx), _ptr(kbar), Tq, Tk, pos0,
           H, Hkv, D, Hi, Di, r, score_mode, _ptr(kl), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def qsa_sparse_attn_prefill_kl(Q, K, V, q_idx, kbar, blk_idx, n_sel, Tq: int, Tk: int,
+                               pos0: int, H: int, Hkv: int, D: int, Hi: int, Di: int, r: int,
+                               Kbudget: int, score_mode: int, O, lse, kl, stream=None) -> None:
+    _call("qsa_sparse_attn_prefill_kl", _ptr(Q), _ptr(K), _ptr(V), _ptr(q_idx), _ptr(kbar),
+          _ptr(blk_idx), _ptr(n_sel), Tq, Tk, pos0, H, Hkv, D, Hi, Di, r, Kbudget, score_mode,
+          _ptr(O), _ptr(lse), _ptr(kl), _stream(stream))
 
 
 from .layer import QSAPrefill, QSADecode  # noqa: E402  (chains of the calls above)

@@ -106,8 +106,10 @@ __device__ __forceinline__ int row_swizzle(int tt) { return 2 * ((tt >> 2) & 3);
 // Entries e0 .. e0+3 of one KV head.  Kg/Vg point at token 0 of the head (row
 // stride rs elements); p is a safe row for masked tokens; pq is the position
 // of the query in this lane's column; vlds is the wave's 8 KB LDS tile.
+// Returns the largest scaled logit (log2 units) among the lane's own tokens:
+// entry e0 + g4 for column n (-inf where none is visible).
 template <bool MULTI, int PMODE>
-__device__ __forceinline__ void attn_stage(const EntryList<MULTI, PMODE> &L, int e0, int64_t p,
+__device__ __forceinline__ float attn_stage(const EntryList<MULTI, PMODE> &L, int e0, int64_t p,
                                            int64_t pq,
                                            const uint16_t *__restrict__ Kg,
                                            const uint16_t *__restrict__ Vg, int64_t rs,
@@ -149,8 +151,8 @@ __device__ __forceinline__ void attn_stage(const EntryList<MULTI, PMODE> &L, int
     float sv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sv[i] = i < cnt ? sacc[i] * kScaleLog2 : -INFINITY;
-    float cm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    cm = fmaxf(cm, __shfl_xor(cm, 16));
+    const float lm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    float cm = fmaxf(lm, __shfl_xor(lm, 16));
     cm = fmaxf(cm, __shfl_xor(cm, 32));
     const float m_new = fmaxf(st.m, cm);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -186,6 +188,7 @@ __device__ __forceinline__ void attn_stage(const EntryList<MULTI, PMODE> &L, int
         st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, st.o[dt], 0, 0, 0);
         st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, st.o[dt], 0, 0, 0);
     }
+    return lm;
 }
 
 // Q^T fragments of column tile ct of KV head g: column n is the pair
@@ -256,16 +259,94 @@ __device__ __forceinline__ void state_write(const WaveState &st, float ltot,
         lse_row[hq] = ltot > 0.f ? (st.m + log2f(ltot)) * kLn2 : -INFINITY;
 }
 
+// Distillation KL under the sparse pattern, fused into the prefill (ai.info
+// "Industry relevance": one kernel yields the sparse outputs and the KL loss
+// without storing intermediates; chlience section 6, second stage: indexer and
+// backbone train under the sparse pattern).  Teacher: each head's attention
+// over the query's token set, max-pooled within each selected block, summed
+// over the 24 heads, normalised over the selected blocks; student: softmax of
+// the selected blocks' indexer scores; loss KL(teacher || student).
+// While the attention runs, a wave keeps the block-max logit of every
+// (selected block, head of its group) in LDS (the block max is one lane's
+// register-local max, and exp is monotone).  After the pass each head's final
+// log-sum-exp turns them into probabilities; the per-block head sums of the
+// two waves meet in LDS, and the indexer scores of the selected blocks are
+// recomputed from the query's indexer row and the pooled keys.
+constexpr int kKlGroup = 12;  // query heads per KV head (24 / 2)
+
+// Dynamic LDS of the prefill kernel, in bytes from the start: Hkv V tiles of
+// 8 KB, the block list (Kbudget + 1 entries); for the KL form then the block
+// maxima [Hkv][Kbudget][12], the per-wave head sums [Hkv][Kbudget], the
+// selected blocks' indexer scores [Kbudget] and 16 floats of reduction space.
+struct PrefillLds {
+    size_t list, mx, part, score, red, total;
+    __host__ __device__ PrefillLds(int Hkv, int Kbudget, bool kl) {
+        list = static_cast<size_t>(Hkv) * kVStageBytes;
+        mx = list + ((4 * (static_cast<size_t>(Kbudget) + 1) + 15) & ~size_t(15));
+        if (!kl) {
+            part = score = red = total = mx;
+            return;
+        }
+        part = mx + 4 * static_cast<size_t>(Hkv) * kKlGroup * Kbudget;
+        score = part + 4 * static_cast<size_t>(Hkv) * Kbudget;
+        red = score + 4 * static_cast<size_t>(Kbudget);
+        total = red + 4 * 16;
+    }
+};
+
+// Indexer scores of selected entries, 16 per tile: D[head][entry] =
+// q_idx[head] . kbar[block of entry] on 16x16x32 bf16 MFMA, A = the 4 indexer
+// heads (rows 4..15 zero), B = the pooled keys of the tile's entries.  Lanes
+// of group 0 then hold the 4 heads of entry 16 * tile + n.  Tiles
+// t0, t0 + dt, ... below ntile; each lane's 4 key loads of 4 tiles are issued
+// before their MFMAs.
+__device__ __forceinline__ void tile_scores(const uint16_t *__restrict__ qi_row,
+                                            const uint16_t *__restrict__ kbar,
+                                            const int32_t *lst, int ns, int t0, int dt, int mode,
+                                            float *sc, int lane) {
+    const int n = lane & 15, g4 = lane >> 4;
+    bf16x8 qa[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+        qa[st] = as_bf16x8(n < kIdxHeads ? *reinterpret_cast<const uint4 *>(
+                                               qi_row + n * kIdxDim + 32 * st + 8 * g4)
+                                         : make_uint4(0, 0, 0, 0));
+    const int ntile = (ns + 15) / 16;
+    for (int t = t0; t < ntile; t += 4 * dt) {
+        uint4 kb[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = min(16 * (t + u * dt) + n, ns - 1);
+            const uint16_t *src = kbar + static_cast<int64_t>(lst[e]) * kIdxDim + 8 * g4;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) kb[u][st] = *reinterpret_cast<const uint4 *>(src + 32 * st);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                acc = mfma_bf16_16x16x32(qa[st], as_bf16x8(kb[u][st]), acc);
+            const int e = 16 * (t + u * dt) + n;
+            if (g4 == 0 && e < ns) sc[e] = mode == 0 ? combine_heads<0>(acc) : combine_heads<1>(acc);
+        }
+    }
+}
+
 // ------------------------------------------------------------------------
 // Prefill: one workgroup per query, one wave per KV head; each wave walks all
 // stages of its head.  Grid: (Tq, B); block: 64 * Hkv threads.
-// Dynamic LDS: Hkv V tiles of 8 KB, then the selected-block list.
+// Dynamic LDS: PrefillLds.
 // PAGED: K and V are page pools; the list is translated to pool blocks once
 // (the tail block as entry ns).
-template <bool PAGED>
+// KL: also the distillation KL of each query (above); contiguous caches, one
+// sequence, 2 KV heads of 12 query heads.
+template <bool PAGED, bool KL>
 __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a) {
+    static_assert(!(PAGED && KL), "the fused KL runs on contiguous caches");
     extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
-    int32_t *lst = reinterpret_cast<int32_t *>(dyn_lds + a.Hkv * kVStageBytes);
+    const PrefillLds lay(a.Hkv, a.Kbudget, KL);
+    int32_t *lst = reinterpret_cast<int32_t *>(dyn_lds + lay.list);
     const int64_t t = blockIdx.x, b = blockIdx.y;
     const int64_t row = b * a.Tq + t;
     int64_t p = a.pos0 + t;
@@ -300,12 +381,83 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a) {
     const int64_t pq = a.pos0 + t;  // every entry is visible (single query)
     WaveState st;
     state_init(st);
-    for (int sidx = 0; sidx < nstages; ++sidx)
-        attn_stage(L, sidx * kStageEntries, p, pq, Kg, Vg, rs, qT, st,
-                   dyn_lds + g * kVStageBytes, lane);
+    const int n = lane & 15, g4 = lane >> 4;
+    float *mxw = reinterpret_cast<float *>(dyn_lds + lay.mx) +
+                 static_cast<int64_t>(g) * a.Kbudget * kKlGroup;
+    for (int sidx = 0; sidx < nstages; ++sidx) {
+        const float lm = attn_stage(L, sidx * kStageEntries, p, pq, Kg, Vg, rs, qT, st,
+                                    dyn_lds + g * kVStageBytes, lane);
+        const int e = sidx * kStageEntries + g4;
+        if (KL && n < kKlGroup && e < ns) mxw[e * kKlGroup + n] = lm;
+    }
     const float ltot = head_total(st.l);
     state_write(st, ltot, a.O + row * a.H * kHeadDim, a.lse ? a.lse + row * a.H : nullptr, g,
                 group, lane);
+    if (!KL) return;
+
+    // teacher mass of each selected block from this wave's 12 heads: the
+    // head's probability of the block's best token, exp2(max - lse2)
+    const float lse2 = ltot > 0.f ? st.m + log2f(ltot) : INFINITY;
+    float l2[kKlGroup];
+#pragma unroll
+    for (int h = 0; h < kKlGroup; ++h) l2[h] = __shfl(lse2, h);
+    float *part = reinterpret_cast<float *>(dyn_lds + lay.part);
+    lds_fence();  // the wave's block maxima are in LDS
+    for (int e = lane; e < ns; e += kWave) {
+        const float *mr = mxw + e * kKlGroup;
+        float tb = 0.f;
+#pragma unroll
+        for (int h = 0; h < kKlGroup; ++h) tb += exp2f(mr[h] - l2[h]);
+        part[g * a.Kbudget + e] = tb;
+    }
+    // student logits: wave g scores tiles g, g + 2, ...
+    float *sc = reinterpret_cast<float *>(dyn_lds + lay.score);
+    tile_scores(a.q_idx + row * (kIdxHeads * kIdxDim), a.kbar, lst, ns, g, a.Hkv, a.score_mode,
+                sc, lane);
+    block_sync();
+    // thread i takes blocks i, i + 128, ...: t = both waves' sums; the row's
+    // Z = sum t, A = sum t ln t, C = sum t s and the log-sum-exp of s
+    float z = 0.f, aa = 0.f, c = 0.f, m = -INFINITY, zs = 0.f;
+    for (int e = threadIdx.x; e < ns; e += blockDim.x) {
+        const float tb = part[e] + part[a.Kbudget + e];
+        const float se = sc[e];
+        z += tb;
+        aa += tb > 0.f ? tb * logf(tb) : 0.f;
+        c += tb * se;
+        if (se > m) {
+            zs = zs * expf(m - se) + 1.f;
+            m = se;
+        } else {
+            zs += expf(se - m);
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        z += __shfl_xor(z, off);
+        aa += __shfl_xor(aa, off);
+        c += __shfl_xor(c, off);
+        const float m2 = __shfl_xor(m, off), zs2 = __shfl_xor(zs, off);
+        const float mn = fmaxf(m, m2);
+        zs = (m == -INFINITY ? 0.f : zs * expf(m - mn)) +
+             (m2 == -INFINITY ? 0.f : zs2 * expf(m2 - mn));
+        m = mn;
+    }
+    float *red = reinterpret_cast<float *>(dyn_lds + lay.red);
+    if (lane == 0) {
+        red[5 * g + 0] = z;
+        red[5 * g + 1] = aa;
+        red[5 * g + 2] = c;
+        red[5 * g + 3] = m;
+        red[5 * g + 4] = zs;
+    }
+    block_sync();
+    if (threadIdx.x != 0) return;
+    // wave 1 after wave 0
+    const float m1 = red[8], mn = fmaxf(red[3], m1);
+    const float zsum = (red[3] == -INFINITY ? 0.f : red[4] * expf(red[3] - mn)) +
+                       (m1 == -INFINITY ? 0.f : red[9] * expf(m1 - mn));
+    const float zt = red[0] + red[5], at = red[1] + red[6], ct = red[2] + red[7];
+    a.kl[row] = ns > 0 ? at / zt - logf(zt) - ct / zt + (mn + logf(zsum)) : 0.f;
 }
 
 // Split record in HBM: unnormalised O of head n (column n of O^T) at
@@ -451,12 +603,26 @@ __global__ void __launch_bounds__(256) attn_decode_merge(AttnArgs a, int nsplit,
 hipError_t launch_sparse_prefill(const AttnArgs &a, hipStream_t s) {
     if (a.Tq == 0 || a.B == 0) return hipSuccess;
     const dim3 grid(static_cast<uint32_t>(a.Tq), static_cast<uint32_t>(a.B));
-    const size_t lds =
-        static_cast<size_t>(a.Hkv) * kVStageBytes + 4 * (static_cast<size_t>(a.Kbudget) + 1);
+    const size_t lds = PrefillLds(a.Hkv, a.Kbudget, false).total;
     if (a.ptable)
-        hipLaunchKernelGGL(attn_prefill_kernel<true>, grid, dim3(64 * a.Hkv), lds, s, a);
+        hipLaunchKernelGGL((attn_prefill_kernel<true, false>), grid, dim3(64 * a.Hkv), lds, s, a);
     else
-        hipLaunchKernelGGL(attn_prefill_kernel<false>, grid, dim3(64 * a.Hkv), lds, s, a);
+        hipLaunchKernelGGL((attn_prefill_kernel<false, false>), grid, dim3(64 * a.Hkv), lds, s,
+                           a);
+    return hipGetLastError();
+}
+
+size_t sparse_prefill_kl_lds(int Kbudget) { return PrefillLds(2, Kbudget, true).total; }
+
+hipError_t launch_sparse_prefill_kl(const AttnArgs &a, hipStream_t s) {
+    if (a.Tq == 0 || a.B == 0) return hipSuccess;
+    const dim3 grid(static_cast<uint32_t>(a.Tq), static_cast<uint32_t>(a.B));
+    const size_t lds = PrefillLds(a.Hkv, a.Kbudget, true).total;
+    const void *fn = reinterpret_cast<const void *>(&attn_prefill_kernel<false, true>);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_prefill_kernel<false, true>), grid, dim3(64 * a.Hkv), lds, s, a);
     return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@ namespace {
 
 constexpr int64_t kI32Max = 2147483647;
 constexpr int kMaxBudget = 2048;
+constexpr int kMaxKlBudget = 1024;  // block maxima of 24 heads in LDS
 constexpr int kMaxNextN = 16;  // queries per sequence in the decode form
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -463,6 +464,32 @@ int qsa_distill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const float *lse, const
         if (e != hipSuccess) return QSA_ERR_LAUNCH;
     }
     return QSA_OK;
+}
+
+int qsa_sparse_attn_prefill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
+                               const qsa_bf16 *q_idx, const qsa_bf16 *kbar,
+                               const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq,
+                               int64_t Tk, int64_t pos0, int H, int Hkv, int D, int Hi, int Di,
+                               int r, int Kbudget, int score_mode, float *O, float *lse,
+                               float *kl, void *stream) {
+    if (!Q || !K || !V || !blk_idx || !n_sel || !O || !kl) return QSA_ERR_NULL;
+    if (Tq < 0 || Tk < 0 || pos0 < 0 || Kbudget <= 0) return QSA_ERR_SHAPE;
+    int st = check_attn_shape(H, Hkv, D, r);
+    if (st != QSA_OK) return st;
+    if (Tk < pos0 + Tq) return QSA_ERR_SHAPE;
+    if (H != 24 || Hkv != 2 || Kbudget > kMaxKlBudget) return QSA_ERR_UNSUPPORTED;
+    const int64_t nb_max = Tk / kBlock;
+    st = check_index_args(q_idx, kbar, 1, Tq, pos0, nullptr, nb_max > 0 ? nb_max : 1, Hi, Di, r,
+                          score_mode);
+    if (st != QSA_OK) return st;
+    if (Tq > kI32Max || nb_max > kI32Max) return QSA_ERR_OVERFLOW;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return QSA_ERR_ALIGN;
+    AttnArgs a{};
+    a.Q = Q; a.K = K; a.V = V; a.blk_idx = blk_idx; a.n_sel = n_sel; a.seq_len = nullptr;
+    a.O = O; a.lse = lse; a.part = nullptr;
+    a.Tq = Tq; a.Lmax = Tk; a.pos0 = pos0; a.B = 1; a.H = H; a.Hkv = Hkv; a.Kbudget = Kbudget;
+    a.q_idx = q_idx; a.kbar = kbar; a.kl = kl; a.score_mode = score_mode;
+    return launch_status(launch_sparse_prefill_kl(a, as_stream(stream)));
 }
 
 }  // extern "C"

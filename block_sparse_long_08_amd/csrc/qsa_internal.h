@@ -175,6 +175,12 @@ struct AttnArgs {
     const int32_t *ptable;
     int64_t pstride;
     int pshift;
+    // Fused distillation KL (prefill, contiguous): the chunk's indexer queries
+    // [Tq][4][128], the pooled keys [nb][128], the score mode and kl [Tq].
+    const uint16_t *q_idx;
+    const uint16_t *kbar;
+    float *kl;
+    int score_mode;
 };
 
 // Row of token t in a page pool (tab: the sequence's page-table row).
@@ -183,6 +189,10 @@ __device__ __forceinline__ int64_t page_row(const int32_t *tab, int sh, int64_t 
 }
 
 hipError_t launch_sparse_prefill(const AttnArgs &a, hipStream_t s);
+// Sparse prefill plus the distillation KL of every query (H = 24, Hkv = 2);
+// dynamic LDS bytes it takes at a budget.
+hipError_t launch_sparse_prefill_kl(const AttnArgs &a, hipStream_t s);
+size_t sparse_prefill_kl_lds(int Kbudget);
 // Decode: split-K workgroups per (split, KV head, column tile, sequence); a
 // column tile holds 16 (query, head) pairs of one KV head.
 int decode_col_tiles(int Tq, int group);

@@ -15,7 +15,7 @@ import torch
 
 from . import (DI, HI, R, SCORE_MAXHEAD, KBAR_MEAN, qsa_compress_keys, qsa_decode_workspace_bytes,
                qsa_rope_bf16, qsa_select_blocks, qsa_select_workspace_bytes,
-               qsa_sparse_attn_decode, qsa_sparse_attn_prefill)
+               qsa_sparse_attn_decode, qsa_sparse_attn_prefill, qsa_sparse_attn_prefill_kl)
 
 
 class QSAPrefill:
@@ -105,6 +105,21 @@ class QSAPrefill:
                                 self.n_sel[r0:r0 + n], n, p0 + n, p0, self.H, self.Hkv, self.D, R,
                                 self.budget, self.O[r0:r0 + n], self.lse[r0:r0 + n],
                                 pages=self.pages)
+
+    def attend_with_kl(self, Kr, V, qi, kbar, kl):
+        """Training form of attend(), after select(): the sparse attention of
+        every row fused with the distillation KL under the sparse pattern
+        (kl: fp32 [Tq]); qi and kbar as given to the selection (qi after
+        rope_indexer).  Contiguous caches; the same row chunks as the
+        pipelined attention."""
+        assert self.pages is None, "the fused KL runs on contiguous caches"
+        for r0, n in self._chunks():
+            p0 = self.pos0 + r0
+            qsa_sparse_attn_prefill_kl(self.Qr[r0:r0 + n], Kr, V, qi[r0:r0 + n], kbar,
+                                       self.blk_idx[r0:r0 + n], self.n_sel[r0:r0 + n], n, p0 + n,
+                                       p0, self.H, self.Hkv, self.D, HI, DI, R, self.budget,
+                                       self.score_mode, self.O[r0:r0 + n], self.lse[r0:r0 + n],
+                                       kl[r0:r0 + n])
 
     def select(self, qi, kbar):
         for r0, n in self._chunks():

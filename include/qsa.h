@@ -270,6 +270,39 @@ int qsa_distill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const float *lse, const
                    int D, int Hi, int Di, int r, int score_mode, float *kl, void *ws,
                    size_t ws_bytes, void *stream);
 
+/* ---- Sparse attention prefill fused with the distillation KL under the
+ * sparse pattern (ai.info "Industry relevance": a fused QSA kernel yields the
+ * sparse attention outputs and the KL loss without materialising
+ * intermediates; chlience section 6: the second stage trains backbone and
+ * indexer together under the sparse pattern).  The pages give no formula for
+ * this loss; it is read as the stage-1 loss above with the dense attention
+ * replaced by the sparse attention the layer computes.  For the query at
+ * p = pos0 + t with its ns selected blocks (n_sel, clamped as in
+ * qsa_sparse_attn_prefill):
+ *   O, lse      exactly as qsa_sparse_attn_prefill;
+ *   teacher T_b = for each selected block b, sum over heads h of the largest
+ *                 probability A_hj over the r tokens j of the block, where
+ *                 A_h is the softmax over the query's token set (selected
+ *                 blocks and incomplete block: the lse above); divided by its
+ *                 sum over the selected blocks;
+ *   student S_b = softmax over the selected blocks of their indexer scores
+ *                 (qsa_index_scores' values, recomputed in the kernel);
+ *   kl[t]       = sum_b T_b (ln T_b - ln S_b)   (0 when ns = 0).
+ * Q, K, V, blk_idx, n_sel, O, lse as for qsa_sparse_attn_prefill (contiguous
+ * caches, one sequence, lse may be NULL); q_idx: [Tq][Hi][Di] the chunk's
+ * indexer queries as given to the selection; kbar: [Tk / r][Di];
+ * score_mode: the selection's; kl: fp32 [Tq].  Probabilities, block maxima
+ * and scores stay on chip (LDS, about 98 bytes per selected block).  No
+ * workspace.
+ * Supported: H = 24, Hkv = 2, D = 256, Hi = 4, Di = 128, r = 4,
+ * Kbudget <= 1024. */
+int qsa_sparse_attn_prefill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
+                               const qsa_bf16 *q_idx, const qsa_bf16 *kbar,
+                               const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq,
+                               int64_t Tk, int64_t pos0, int H, int Hkv, int D, int Hi, int Di,
+                               int r, int Kbudget, int score_mode, float *O, float *lse,
+                               float *kl, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

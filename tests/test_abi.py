@@ -297,3 +297,31 @@ def test_distill_validation(lib):
     assert distill(lib, wsb=need - 1) == WORKSPACE
     assert distill(lib, ws=MIS) == ALIGN
     assert distill(lib, Tq=0, ws=0, wsb=0) == OK        # nothing to do, nothing enqueued
+
+
+def attn_kl(lib, Q=P, K=P, V=P, qi=P, kb=P, blk=P, ns=P, Tq=8, Tk=64, pos0=0, H=24, Hkv=2, D=256,
+            Hi=4, Di=128, r=4, Kb=512, mode=0, O=P, lse=P, kl=P):
+    return lib.qsa_sparse_attn_prefill_kl(vp(Q), vp(K), vp(V), vp(qi), vp(kb), vp(blk), vp(ns),
+                                          I64(Tq), I64(Tk), I64(pos0), H, Hkv, D, Hi, Di, r, Kb,
+                                          mode, vp(O), vp(lse), vp(kl), None)
+
+
+def test_sparse_attn_prefill_kl_validation(lib):
+    assert attn_kl(lib, V=0) == NULL
+    assert attn_kl(lib, qi=0) == NULL
+    assert attn_kl(lib, kb=0) == NULL
+    assert attn_kl(lib, kl=0) == NULL
+    assert attn_kl(lib, blk=0) == NULL
+    assert attn_kl(lib, Tq=8, Tk=7) == SHAPE             # keys must cover every query
+    assert attn_kl(lib, Kb=0) == SHAPE
+    assert attn_kl(lib, Kb=1025) == UNSUP                 # block maxima of 24 heads in LDS
+    assert attn_kl(lib, H=16) == UNSUP
+    assert attn_kl(lib, H=12, Hkv=1) == UNSUP
+    assert attn_kl(lib, D=128) == UNSUP
+    assert attn_kl(lib, Hi=8) == UNSUP
+    assert attn_kl(lib, mode=2) == SHAPE
+    assert attn_kl(lib, Q=MIS) == ALIGN
+    assert attn_kl(lib, qi=MIS) == ALIGN
+    assert attn_kl(lib, O=MIS) == ALIGN
+    assert attn_kl(lib, Tq=0) == OK                      # nothing to do, nothing enqueued
+    assert attn_kl(lib, Tq=0, lse=0) == OK               # lse is optional
