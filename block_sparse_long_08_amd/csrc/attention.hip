@@ -78,6 +78,15 @@ struct EntryList {
             t = MULTI ? 4 * (nc + e - ns) : 4 * nc;
         return PMODE == 2 ? page_row(ptab, psh, t) : t;
     }
+    // token i of entry e, or the safe row p past the entry's count, with no
+    // control flow: the list is read at a clamped index (contiguous
+    // single-query lists with an LDS list)
+    __device__ __forceinline__ int64_t token_or(int e, int i, int64_t p) const {
+        static_assert(!MULTI && PMODE == 0, "contiguous single-query lists only");
+        const int64_t b = 4 * static_cast<int64_t>(lst[e < ns ? e : 0]);
+        const int64_t t = (e < ns ? b : 4 * nc) + i;
+        return i < count(e) ? t : p;
+    }
     // tokens of entry e visible to a query at position pq (selected blocks
     // precede every query sharing the selection)
     __device__ __forceinline__ int visible(int e, int64_t pq) const {
@@ -103,22 +112,18 @@ __device__ __forceinline__ void state_init(WaveState &st) {
 
 __device__ __forceinline__ int row_swizzle(int tt) { return 2 * ((tt >> 2) & 3); }
 
-// Entries e0 .. e0+3 of one KV head.  Kg/Vg point at token 0 of the head (row
-// stride rs elements); p is a safe row for masked tokens; pq is the position
-// of the query in this lane's column; vlds is the wave's 8 KB LDS tile.
-// Returns the largest scaled logit (log2 units) among the lane's own tokens:
-// entry e0 + g4 for column n (-inf where none is visible).
+// Stage helpers.  Entries e0 .. e0+3 of one KV head; Kg/Vg point at token 0
+// of the head (row stride rs elements); p is a safe row for masked tokens.
+// The V tile of a stage is 16 rows of 512 B whose 16-byte chunks sit at
+// position c ^ row_swizzle(row): LDS bytes 1024*j + 16*lane hold row
+// tt = 2j + lane/32, chunk (lane%32) ^ row_swizzle(tt).
+
+// V rows into the tile by LDS DMA (instruction j fills bytes 1024*j ...).
 template <bool MULTI, int PMODE>
-__device__ __forceinline__ float attn_stage(const EntryList<MULTI, PMODE> &L, int e0, int64_t p,
-                                           int64_t pq,
-                                           const uint16_t *__restrict__ Kg,
-                                           const uint16_t *__restrict__ Vg, int64_t rs,
-                                           const bf16x8 (&qT)[8], WaveState &st,
-                                           unsigned char *vlds, int lane) {
-    const int n = lane & 15, g4 = lane >> 4, h = lane >> 5;
-    // V: DMA instruction j writes LDS bytes 1024*j + 16*lane = row tt = 2j+h,
-    // position lane%32; the lane fetches the chunk that belongs there.
-    lds_fence();  // the previous stage's reads of this tile are done
+__device__ __forceinline__ void stage_v_dma(const EntryList<MULTI, PMODE> &L, int e0, int64_t p,
+                                            const uint16_t *__restrict__ Vg, int64_t rs,
+                                            unsigned char *vlds, int lane) {
+    const int h = lane >> 5;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int tt = 2 * j + h;
@@ -132,20 +137,69 @@ __device__ __forceinline__ float attn_stage(const EntryList<MULTI, PMODE> &L, in
                                          (__attribute__((address_space(3))) void *)(vlds + 1024 * j),
                                          16, 0, 0);
     }
-    // K: A fragment row m = n is entry e0 + n/4, token n%4; k-slots of group
-    // g4 at step s are dims 32*s + 8*g4 .. +7.
-    uint4 kf[8];
-    {
-        const int e = e0 + (n >> 2), i = n & 3;
-        const bool ok = i < L.count(e);
-        const int64_t tok = ok ? L.base(e) + i : p;
-        const uint16_t *src = Kg + tok * rs + 8 * g4;
+}
+
+// The same 8 chunks of V into registers (written to the tile later), and K
+// as stage_k below, both addressed without control flow (token_or), so that
+// the loads issue unconditionally and their registers need no merging.
+__device__ __forceinline__ void stage_v_regs(const EntryList<false, 0> &L, int e0, int64_t p,
+                                             const uint16_t *__restrict__ Vg, int64_t rs,
+                                             bf16x8 (&vr)[8], int lane) {
+    const int h = lane >> 5;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) kf[s] = *reinterpret_cast<const uint4 *>(src + 32 * s);
+    for (int j = 0; j < 8; ++j) {
+        const int tt = 2 * j + h;
+        const int64_t tok = L.token_or(e0 + (tt >> 2), tt & 3, p);
+        const int c = (lane & 31) ^ row_swizzle(tt);
+        vr[j] = *reinterpret_cast<const bf16x8 *>(Vg + tok * rs + 8 * c);
     }
+}
+
+__device__ __forceinline__ void stage_k_regs(const EntryList<false, 0> &L, int e0, int64_t p,
+                                             const uint16_t *__restrict__ Kg, int64_t rs,
+                                             bf16x8 (&kf)[8], int lane) {
+    const int n = lane & 15, g4 = lane >> 4;
+    const uint16_t *src = Kg + L.token_or(e0 + (n >> 2), n & 3, p) * rs + 8 * g4;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kf[s] = *reinterpret_cast<const bf16x8 *>(src + 32 * s);
+}
+
+__device__ __forceinline__ void stage_v_store(const bf16x8 (&vr)[8], unsigned char *vlds,
+                                              int lane) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<bf16x8 *>(vlds + 1024 * j + 16 * lane) = vr[j];
+}
+
+// K: A fragment row m = n is entry e0 + n/4, token n%4; k-slots of group g4
+// at step s are dims 32*s + 8*g4 .. +7.
+template <bool MULTI, int PMODE>
+__device__ __forceinline__ void stage_k(const EntryList<MULTI, PMODE> &L, int e0, int64_t p,
+                                        const uint16_t *__restrict__ Kg, int64_t rs,
+                                        uint4 (&kf)[8], int lane) {
+    const int n = lane & 15, g4 = lane >> 4;
+    const int e = e0 + (n >> 2), i = n & 3;
+    const bool ok = i < L.count(e);
+    const int64_t tok = ok ? L.base(e) + i : p;
+    const uint16_t *src = Kg + tok * rs + 8 * g4;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kf[s] = *reinterpret_cast<const uint4 *>(src + 32 * s);
+}
+
+// Logits, online softmax and the PV product of one stage whose K fragments
+// are in kf; pq is the position of the query in this lane's column.  DMA_V:
+// the V tile is still arriving by LDS DMA (wait for it before the PV reads);
+// otherwise the caller has written it and fenced.  Returns the largest scaled
+// logit (log2 units) among the lane's own tokens: entry e0 + g4 for column n
+// (-inf where none is visible).
+template <bool DMA_V, bool MULTI, int PMODE>
+__device__ __forceinline__ float stage_compute(const EntryList<MULTI, PMODE> &L, int e0,
+                                               int64_t pq, const bf16x8 (&kf)[8],
+                                               const bf16x8 (&qT)[8], WaveState &st,
+                                               const unsigned char *vlds, int lane) {
+    const int n = lane & 15, g4 = lane >> 4;
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) sacc = mfma_bf16_16x16x32(as_bf16x8(kf[s]), qT[s], sacc);
+    for (int s = 0; s < 8; ++s) sacc = mfma_bf16_16x16x32(kf[s], qT[s], sacc);
     // lane (column n, group g4) holds entry e0 + g4, tokens 0..3
     const int cnt = L.visible(e0 + g4, pq);
     float sv[4];
@@ -172,9 +226,11 @@ __device__ __forceinline__ float attn_stage(const EntryList<MULTI, PMODE> &L, in
     st.m = m_new;
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) st.o[dt] *= alpha;
-    // V tile has landed (the compiler waits on the DMA before LDS reads)
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __builtin_amdgcn_wave_barrier();
+    if (DMA_V) {
+        // V tile has landed (the compiler waits on the DMA before LDS reads)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+    }
     // O^T += V^T P^T: A = V^T rows d = 16*dt + n, k-slots = tokens 4*g4 .. +3
     const int swz = 2 * g4;  // row_swizzle(4*g4 + jj)
 #pragma unroll
@@ -189,6 +245,25 @@ __device__ __forceinline__ float attn_stage(const EntryList<MULTI, PMODE> &L, in
         st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, st.o[dt], 0, 0, 0);
     }
     return lm;
+}
+
+// One stage as a unit: V by LDS DMA into vlds (the wave's 8 KB tile), K into
+// registers, then the compute.  Returns stage_compute's block max.
+template <bool MULTI, int PMODE>
+__device__ __forceinline__ float attn_stage(const EntryList<MULTI, PMODE> &L, int e0, int64_t p,
+                                           int64_t pq,
+                                           const uint16_t *__restrict__ Kg,
+                                           const uint16_t *__restrict__ Vg, int64_t rs,
+                                           const bf16x8 (&qT)[8], WaveState &st,
+                                           unsigned char *vlds, int lane) {
+    lds_fence();  // the previous stage's reads of this tile are done
+    stage_v_dma(L, e0, p, Vg, rs, vlds, lane);
+    uint4 kf[8];
+    stage_k(L, e0, p, Kg, rs, kf, lane);
+    bf16x8 kb[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kb[s] = as_bf16x8(kf[s]);
+    return stage_compute<true>(L, e0, pq, kb, qT, st, vlds, lane);
 }
 
 // Q^T fragments of column tile ct of KV head g: column n is the pair
@@ -384,11 +459,34 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a) {
     const int n = lane & 15, g4 = lane >> 4;
     float *mxw = reinterpret_cast<float *>(dyn_lds + lay.mx) +
                  static_cast<int64_t>(g) * a.Kbudget * kKlGroup;
-    for (int sidx = 0; sidx < nstages; ++sidx) {
-        const float lm = attn_stage(L, sidx * kStageEntries, p, pq, Kg, Vg, rs, qT, st,
-                                    dyn_lds + g * kVStageBytes, lane);
-        const int e = sidx * kStageEntries + g4;
-        if (KL && n < kKlGroup && e < ns) mxw[e * kKlGroup + n] = lm;
+    unsigned char *vl = dyn_lds + g * kVStageBytes;
+    if constexpr (!KL) {
+        for (int sidx = 0; sidx < nstages; ++sidx)
+            attn_stage(L, sidx * kStageEntries, p, pq, Kg, Vg, rs, qT, st, vl, lane);
+    } else {
+        // Two stages per step: the first stage's V by LDS DMA as above, its
+        // K and the second stage's K and V into registers, all issued before
+        // the first wait.  The LDS of the block maxima leaves one wave per
+        // SIMD, so each wave keeps two stages' bytes in flight.  Loads past
+        // the last stage read the safe row p.
+        for (int sidx = 0; sidx < nstages; sidx += 2) {
+            const int e0 = sidx * kStageEntries, e1 = e0 + kStageEntries;
+            lds_fence();  // the previous stage's reads of the tile are done
+            stage_v_dma(L, e0, p, Vg, rs, vl, lane);
+            bf16x8 ka[8], kb[8], vb[8];
+            stage_k_regs(L, e0, p, Kg, rs, ka, lane);
+            stage_k_regs(L, e1, p, Kg, rs, kb, lane);
+            stage_v_regs(L, e1, p, Vg, rs, vb, lane);
+            float lm = stage_compute<true>(L, e0, pq, ka, qT, st, vl, lane);
+            if (n < kKlGroup && e0 + g4 < ns) mxw[(e0 + g4) * kKlGroup + n] = lm;
+            if (sidx + 1 < nstages) {
+                lds_fence();
+                stage_v_store(vb, vl, lane);
+                lds_fence();
+                lm = stage_compute<false>(L, e1, pq, kb, qT, st, vl, lane);
+                if (n < kKlGroup && e1 + g4 < ns) mxw[(e1 + g4) * kKlGroup + n] = lm;
+            }
+        }
     }
     const float ltot = head_total(st.l);
     state_write(st, ltot, a.O + row * a.H * kHeadDim, a.lse ? a.lse + row * a.H : nullptr, g,
