@@ -48,8 +48,11 @@ __device__ __forceinline__ void store_tile(unsigned char *buf, int bl, int part,
 // also writes the largest score key of every 16 consecutive blocks,
 // gmax[t * gld + g] (blocks a query does not see count as -inf), from which
 // the top-K takes its floor.
+// (at most the registers of 3 waves per SIMD: the LDS allows 3 workgroups
+// per CU, and the interleaved accumulators would otherwise take one more
+// register block than that)
 template <int MODE, bool PAGED>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 3)
 index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ kbar,
                      int64_t Tq, int64_t pos0, int64_t nb_max, float *__restrict__ scores,
                      int64_t ld, uint32_t *__restrict__ gmax, int64_t gld, PageTable pg) {
@@ -125,12 +128,19 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
                 kf[s] = as_bf16x8(*reinterpret_cast<const uint4 *>(
                     buf + (16 * j + n) * kRowBytes + 64 * s + 16 * g4));
             const int64_t blk = b0 + 16 * j + n;
+            // the 4 row tiles' accumulators interleaved: no MFMA waits on the
+            // one before it
+            f32x4 acc[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    acc[rt] = mfma_bf16_16x16x32(qf[rt][s], kf[s], acc[rt]);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 4; ++s) acc = mfma_bf16_16x16x32(qf[rt][s], kf[s], acc);
-                const float v = blk < ncq[rt] ? combine_heads<MODE>(acc) : -INFINITY;
+                const float v = blk < ncq[rt] ? combine_heads<MODE>(acc[rt]) : -INFINITY;
                 *reinterpret_cast<float *>(stage + (4 * rt + g4) * kStageRow + 4 * (16 * j + n)) = v;
             }
         }
