@@ -292,8 +292,8 @@ int qsa_distill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const float *lse, const
  * caches, one sequence, lse may be NULL); q_idx: [Tq][Hi][Di] the chunk's
  * indexer queries as given to the selection; kbar: [Tk / r][Di];
  * score_mode: the selection's; kl: fp32 [Tq].  Probabilities, block maxima
- * and scores stay on chip (LDS, about 98 bytes per selected block).  No
- * workspace.
+ * and scores stay on chip (LDS: 112 bytes per budget entry plus 16.5 KB per
+ * query's workgroup).  No workspace.
  * Supported: H = 24, Hkv = 2, D = 256, Hi = 4, Di = 128, r = 4,
  * Kbudget <= 1024. */
 int qsa_sparse_attn_prefill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
