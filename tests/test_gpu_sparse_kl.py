@@ -213,3 +213,31 @@ def test_layer_attend_with_kl_in_row_chunks(qsa):
     ref = oracle.sparse_kl_rows(Qh, Kh, x.qi, kbh, rows, layer.blk_idx.cpu().numpy()[rows],
                                 layer.n_sel.cpu().numpy()[rows])
     check_kl(kl.cpu().numpy().astype(np.float64)[rows], ref, "layer, chunks of 1024 rows")
+
+
+def test_layer_attend_with_kl_chunk_over_a_cache(qsa):
+    """A 1,800-query chunk at pos0 = 9000 against a post-RoPE cache (the
+    layer's fresh=False form, 512-row chunks): attend_with_kl after the
+    layer's forward gives the forward's O and lse bit for bit, and its KL
+    matches the oracle on sampled rows of the layer's own selection."""
+    import torch
+    pos0, Tq = 9000, 1800
+    Tk = pos0 + Tq
+    x = synth.prefill_inputs(Tq, pos0=pos0, seed=94, k_is_rotated=True)
+    kc, vc = dev(x.K), dev(x.V)
+    kbar = torch.full((Tk // 4, 128), -1, dtype=torch.int16, device="cuda")
+    qsa.qsa_compress_keys(dev(x.ki), 1, pos0, pos0 * 128, 128, 4, 0, kbar, (pos0 // 4) * 128)
+    layer = qsa.QSAPrefill(Tq, pos0=pos0, budget=512, fresh=False, pipeline_rows=512)
+    qi = dev(x.qi)
+    O, lse = layer(dev(x.Q), kc, vc, qi, dev(x.ki), kbar)
+    O0, lse0 = O.clone(), lse.clone()
+    kl = torch.empty((Tq,), dtype=torch.float32, device="cuda")
+    layer.attend_with_kl(kc, vc, layer.rope_indexer(qi), kbar, kl)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.O, O0) and torch.equal(layer.lse, lse0)
+    rows = np.unique(np.r_[0, 1, np.arange(7, Tq, 61), Tq - 1])
+    Qh = layer.Qr.view(torch.int16).cpu().numpy().view(np.uint16)
+    kbh = kbar.cpu().numpy().view(np.uint16)
+    ref = oracle.sparse_kl_rows(Qh, x.K, x.qi, kbh, rows, layer.blk_idx.cpu().numpy()[rows],
+                                layer.n_sel.cpu().numpy()[rows], pos0=pos0)
+    check_kl(kl.cpu().numpy().astype(np.float64)[rows], ref, "layer chunk over a cache")
