@@ -54,7 +54,8 @@ class QSAPrefill:
         self.Kr = torch.empty((self.Tk, Hkv, D), dtype=torch.bfloat16, device=dev) if fresh else None
         self.kbar = (torch.empty((max(self.nb, 1), DI), dtype=torch.bfloat16, device=dev)
                      if fresh else None)
-        assert pages is None or not fresh, "paged caches hold earlier context: fresh=False"
+        if pages is not None and fresh:
+            raise ValueError("paged caches hold earlier context: use fresh=False")
         self.blk_idx = torch.empty((Tq, budget), dtype=torch.int32, device=dev)
         self.n_sel = torch.empty((Tq,), dtype=torch.int32, device=dev)
         self.O = torch.empty((Tq, H, D), dtype=torch.float32, device=dev)
@@ -112,7 +113,8 @@ class QSAPrefill:
         (kl: fp32 [Tq]); qi and kbar as given to the selection (qi after
         rope_indexer).  Contiguous caches; the same row chunks as the
         pipelined attention."""
-        assert self.pages is None, "the fused KL runs on contiguous caches"
+        if self.pages is not None:
+            raise ValueError("attend_with_kl: the fused KL runs on contiguous caches only")
         for r0, n in self._chunks():
             p0 = self.pos0 + r0
             qsa_sparse_attn_prefill_kl(self.Qr[r0:r0 + n], Kr, V, qi[r0:r0 + n], kbar,
