@@ -273,7 +273,13 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
             res["sparse_kl"] = dict(ms=fms, launches=nlaunch, attend_ms=stage["attend"],
                                     vs_attend=fms / stage["attend"],
                                     hbm_gbps_algorithmic=attn_bytes / (fms * 1e-3) / 1e9,
+                                    hbm_frac_algorithmic=attn_bytes / (fms * 1e-3) / 1e9
+                                    / HBM_PEAK_GBS,
                                     mean_kl=float(kl.mean().item()))
+            # 64 consecutive rows' selection, for the oracle's timing on the host
+            r0 = min(Tq - 64, (3 * Tq) // 4)
+            res["_kl_sample"] = dict(r0=r0, sel=layer.blk_idx[r0:r0 + 64].cpu().numpy(),
+                                     nsel=layer.n_sel[r0:r0 + 64].cpu().numpy())
             del kl
     del layer
     torch.cuda.empty_cache()
@@ -429,7 +435,7 @@ def calibration_copy():
     torch.cuda.empty_cache()
 
 
-def cpu_baseline(name, x, budget, seconds=15.0):
+def cpu_baseline(name, x, budget, seconds=15.0, kl_sample=None):
     """The oracle (fp64, OpenMP over rows) on sampled query rows of the workload."""
     import oracle
     Tq, pos0, _, _ = WORKLOADS[name]
@@ -467,6 +473,27 @@ def cpu_baseline(name, x, budget, seconds=15.0):
     out["dense"] = dict(rows=64, seconds=td, rows_per_s=64 / td,
                         sample=f"rows {r0}..{r0 + 63} of {name} (dense causal attention, 24 heads)",
                         extrapolated_s=td * all_vis / vis)
+    if kl_sample is not None:
+        # the two distillation KLs: under the sparse pattern on the GPU's
+        # selection of 64 consecutive rows, and the stage-1 (dense) KL of 8
+        # rows, extrapolated per visible token (labelled as such)
+        k0 = kl_sample["r0"]
+        Qk = oracle.rope(x.Q[k0:k0 + 64], pos0=pos0 + k0)
+        qik = x.qi[k0:k0 + 64]
+        t1 = time.time()
+        oracle.sparse_kl_rows(Qk, Kr, qik, kb, np.arange(64), kl_sample["sel"], kl_sample["nsel"],
+                              pos0=pos0 + k0)
+        ts = time.time() - t1
+        out["sparse_kl"] = dict(rows=64, seconds=ts, rows_per_s=64 / ts,
+                                sample=f"rows {k0}..{k0 + 63} of {name} on the GPU's selection",
+                                extrapolated_s=ts * Tq / 64)
+        t1 = time.time()
+        oracle.distill_rows(Qk[:8], Kr, qik[:8], kb, np.arange(8), pos0=pos0 + k0)
+        tdd = time.time() - t1
+        v8 = float((pos0 + k0 + np.arange(8) + 1).sum())
+        out["distill"] = dict(rows=8, seconds=tdd, rows_per_s=8 / tdd,
+                              sample=f"rows {k0}..{k0 + 7} of {name} (stage-1 KL, dense teacher)",
+                              extrapolated_s=tdd * all_vis / v8)
     return out
 
 
@@ -630,7 +657,8 @@ def main():
     if not args.no_cpu:
         if x is None:
             x = gen_prefill(args.workload)
-        out["cpu_baseline"] = cpu_baseline(args.workload, x, pre["budget"], args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(args.workload, x, pre["budget"], args.cpu_seconds,
+                                           kl_sample=pre.get("_kl_sample"))
     print(json.dumps(out), flush=True)
 
 
