@@ -241,3 +241,26 @@ def test_layer_attend_with_kl_chunk_over_a_cache(qsa):
     ref = oracle.sparse_kl_rows(Qh, x.K, x.qi, kbh, rows, layer.blk_idx.cpu().numpy()[rows],
                                 layer.n_sel.cpu().numpy()[rows], pos0=pos0)
     check_kl(kl.cpu().numpy().astype(np.float64)[rows], ref, "layer chunk over a cache")
+
+
+def test_layer_attend_with_kl_with_indexer_rope(qsa):
+    """The layer with a 64-dim partial RoPE on the indexer (rotated queries
+    and pooled keys, as its selection uses them): the fused KL's student
+    scores come from the rotated inputs, against the oracle's KL on the
+    oracle's rotated indexer inputs and the GPU selection."""
+    import torch
+    T, K = 2048, 64
+    x = synth.prefill_inputs(T, seed=43)
+    layer = qsa.QSAPrefill(T, budget=K, idx_rope_dim=64, pipeline_rows=512)
+    Q, Kt, V, qi, ki = (dev(a) for a in (x.Q, x.K, x.V, x.qi, x.ki))
+    Kr, kb = layer.rope_and_pool(Q, Kt, ki, None)
+    qs = layer.rope_indexer(qi)
+    layer.select(qs, kb)
+    kl = torch.empty((T,), dtype=torch.float32, device="cuda")
+    layer.attend_with_kl(Kr, V, qs, kb, kl)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[0, 3, np.arange(11, T, 37), T - 1])
+    ref = oracle.sparse_kl_rows(oracle.rope(x.Q), oracle.rope(x.K), oracle.rope(x.qi, rope_dim=64),
+                                oracle.compress(x.ki, rope_dim=64), rows,
+                                layer.blk_idx.cpu().numpy()[rows], layer.n_sel.cpu().numpy()[rows])
+    check_kl(kl.cpu().numpy().astype(np.float64)[rows], ref, "indexer RoPE, budget 64")
