@@ -167,10 +167,11 @@ def test_fused_kl_empty_and_clamped_selections(qsa):
     check_kl(got[rows], ref, "rows next to emptied ones and clamped rows")
 
 
-def test_fused_kl_128k_context_chunk(qsa):
+@pytest.mark.parametrize("mode", [0, 1])
+def test_fused_kl_128k_context_chunk(qsa, mode):
     """The last 4,096 queries of a 131,072-token context with a budget of
-    512 blocks (every row selects a strict subset); rows at the chunk's edges
-    and a spread sample against the oracle."""
+    512 blocks (every row selects a strict subset), in both score modes; rows
+    at the chunk's edges and a spread sample against the oracle."""
     Tk, Tq = 1 << 17, 4096
     pos0 = Tk - Tq
     x = synth.PrefillInputs(
@@ -180,9 +181,9 @@ def test_fused_kl_128k_context_chunk(qsa):
         synth.normal_bf16(synth.STREAM_QIDX, (Tq, 4, 128), seed=98),
         synth.normal_bf16(synth.STREAM_KIDX, (Tk, 128), seed=98), pos0, None, True)
     rows = np.unique(np.r_[0, 1, np.arange(97, Tq, 331), Tq - 1])
-    got, ref, _, nsel = fused_case(qsa, x, Tq, pos0, 512, 0, rows)
+    got, ref, _, nsel = fused_case(qsa, x, Tq, pos0, 512, mode, rows)
     assert np.all(nsel == 512)
-    check_kl(got[rows], ref, "128K context, sampled rows")
+    check_kl(got[rows], ref, f"128K context, mode {mode}, sampled rows")
 
 
 def test_layer_attend_with_kl_in_row_chunks(qsa):
