@@ -89,7 +89,8 @@ def fused_case(qsa, x, Tq, pos0, K, mode, rows):
 
 
 @pytest.mark.parametrize("mode,T,K,needles", [(0, 2600, 512, 0), (1, 2600, 512, 0),
-                                              (0, 1500, 64, 8), (1, 4500, 1024, 0)])
+                                              (0, 1500, 64, 8), (1, 4500, 1024, 0),
+                                              (0, 900, 37, 0), (1, 700, 3, 4)])
 def test_fused_kl_rows(qsa, mode, T, K, needles):
     """From position 0: early rows select every block, later ones a subset;
     rows 0..2 see no complete block (KL 0); sampled rows against the oracle."""
