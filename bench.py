@@ -128,7 +128,7 @@ def page_table(B, L, P, seed):
 
 
 def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, page_tokens=0,
-                  with_distill=False):
+                  with_distill=False, pipeline_rows=4096):
     import torch
     import block_sparse_long_08_amd as qsa
     Tq, pos0, budget, nd = WORKLOADS[name]
@@ -154,7 +154,7 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
         qsa.qsa_compress_keys(ki, 1, pos0, pos0 * 128, 128, 4, 0, kbar, (pos0 // 4) * 128,
                               rope_dim=idx_rope_dim)
     layer = qsa.QSAPrefill(Tq, pos0=pos0, budget=budget, fresh=fresh, idx_rope_dim=idx_rope_dim,
-                           pages=pages)
+                           pages=pages, pipeline_rows=pipeline_rows)
     torch.cuda.synchronize()
     # the layer's product path: selection and attention overlapped on two
     # streams in row chunks (pipeline_rows), else one after the other
@@ -516,6 +516,10 @@ def main():
     ap.add_argument("--distill", default="on", choices=["on", "off"],
                     help="also time the stage-1 distillation KL on the prefill workload "
                          "(needs the dense baseline's log-sum-exp)")
+    ap.add_argument("--pipeline-rows", type=int, default=4096,
+                    help="rows per selection chunk whose attention overlaps the next chunk's "
+                         "selection; 0 runs the selection of all rows, then the attention "
+                         "(standalone stage times)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (scale of the HBM byte counters)")
     args = ap.parse_args()
@@ -531,7 +535,7 @@ def main():
     if args.calibrate_copy:
         calibration_copy()
     pre, x = bench_prefill(args.workload, args.steps, args.warmup, with_dense=args.dense == "all",
-                           with_distill=args.distill == "on")
+                           with_distill=args.distill == "on", pipeline_rows=args.pipeline_rows)
     log(f"prefill {args.workload}: {pre['ms_per_step']:.2f} ms/step, stages {pre['stages_ms']}")
     st = pre["stages_ms"]
     dominant = max(("rope_pool", "select", "attend"), key=st.get)
@@ -620,7 +624,7 @@ def main():
         # the same metric at 1M context: prefill chunk and decode (own inputs)
         del x
         m_pre, _ = bench_prefill("prefill_1m_chunk", min(args.steps, 3), 1,
-                                 with_dense=args.dense == "all")
+                                 with_dense=args.dense == "all", pipeline_rows=args.pipeline_rows)
         m = dict(workload="prefill_1m_chunk", ms_per_step=m_pre["ms_per_step"],
                  tokens_per_s=m_pre["Tq"] / (m_pre["ms_per_step"] * 1e-3),
                  stages_ms=m_pre["stages_ms"],
@@ -635,7 +639,8 @@ def main():
         log(f"prefill prefill_1m_chunk: {m_pre['ms_per_step']:.2f} ms/step")
         # the report's prefill condition: a 16K-token chunk over a paged cache
         c_pre, _ = bench_prefill("prefill_1m_chunk16k", min(args.steps, 3), 1,
-                                 with_dense=args.dense == "all", page_tokens=64)
+                                 with_dense=args.dense == "all", page_tokens=64,
+                                 pipeline_rows=args.pipeline_rows)
         c = dict(workload="prefill_1m_chunk16k", page_tokens=64, ms_per_step=c_pre["ms_per_step"],
                  tokens_per_s=c_pre["Tq"] / (c_pre["ms_per_step"] * 1e-3),
                  stages_ms=c_pre["stages_ms"])

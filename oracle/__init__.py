@@ -26,8 +26,10 @@ _lib = None
 
 def build(force: bool = True) -> str:
     """Compile ``libqsa_oracle.so`` (gcc, -O2, OpenMP over query rows)."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
+    stale = (not os.path.exists(_LIB_PATH)
+             or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC))
+    if force or stale:
+        tmp = f"{_LIB_PATH}.tmp{os.getpid()}"
         subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11",
                                "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB_PATH)
@@ -106,6 +108,27 @@ def _c(a: np.ndarray, dtype) -> np.ndarray:
 
 def _p(a):
     return None if a is None else a.ctypes.data
+
+
+def _check_rows(name, rows, n_rows, positions, Tk, sel=None, nsel=None, r=4):
+    """Reject inputs that would make the C loops read outside the arrays:
+    rows outside the query array, positions outside the key array, selected
+    blocks that are not complete blocks of their row's position."""
+    if rows is not None and rows.size and (rows.min() < 0 or rows.max() >= n_rows):
+        raise ValueError(f"{name}: a row lies outside the {n_rows} query rows")
+    if positions.size and (positions.min() < 0 or positions.max() >= Tk):
+        raise ValueError(f"{name}: a query position lies outside the {Tk} keys")
+    if sel is not None:
+        if nsel.size != positions.size or sel.shape[0] != positions.size:
+            raise ValueError(f"{name}: selection rows do not match the query rows")
+        if nsel.size and (nsel.min() < 0 or nsel.max() > sel.shape[1]):
+            raise ValueError(f"{name}: a selection count exceeds the budget")
+        nc = (positions + 1) // r
+        for i in range(positions.size):
+            b = sel[i, :nsel[i]]
+            if b.size and (b.min() < 0 or b.max() >= nc[i]):
+                raise ValueError(f"{name}: row {i} selects a block that is not complete at "
+                                 f"position {positions[i]}")
 
 
 MODE_MAXHEAD, MODE_RELUSUM = 0, 1
@@ -206,6 +229,8 @@ def attend_row(q_row: np.ndarray, K: np.ndarray, V: np.ndarray, tokens: np.ndarr
     H, D = q_row.shape
     Hkv = K.shape[1]
     tokens = _c(tokens, np.int64)
+    if tokens.size and (tokens.min() < 0 or tokens.max() >= min(K.shape[0], V.shape[0])):
+        raise ValueError("attend_row: a token lies outside the key array")
     O = np.empty((H, D))
     lse = np.empty(H)
     err = np.zeros(1)
@@ -227,6 +252,7 @@ def qsa_rows(Q, K, V, qi, kbar, rows, pos0: int = 0, Kbudget: int = 512, r: int 
     _, H, D = Q.shape
     Hkv = K.shape[1]
     Hi, Di = qi.shape[1], qi.shape[2]
+    _check_rows("qsa_rows", rows, min(Q.shape[0], qi.shape[0]), pos0 + rows, K.shape[0])
     O = np.empty((n, H, D))
     lse = np.empty((n, H))
     sel = np.empty((n, Kbudget), dtype=np.int32)
@@ -250,6 +276,9 @@ def qsa_rows_at(Q_rows, K, V, qi_rows, kbar, positions, Kbudget: int = 512, r: i
     _, H, D = Q_rows.shape
     Hkv = K.shape[1]
     Hi, Di = qi_rows.shape[1], qi_rows.shape[2]
+    if Q_rows.shape[0] < n or qi_rows.shape[0] < n:
+        raise ValueError("qsa_rows_at: fewer query rows than positions")
+    _check_rows("qsa_rows_at", None, n, positions, K.shape[0])
     O = np.empty((n, H, D))
     lse = np.empty((n, H))
     sel = np.empty((n, Kbudget), dtype=np.int32)
@@ -272,6 +301,7 @@ def sparse_attn_rows(Q, K, V, rows, sel, nsel, pos0: int = 0, r: int = 4):
     n = rows.size
     _, H, D = Q.shape
     Hkv = K.shape[1]
+    _check_rows("sparse_attn_rows", rows, Q.shape[0], pos0 + rows, K.shape[0], sel, nsel, r)
     O = np.empty((n, H, D))
     lse = np.empty((n, H))
     _load().qsa_oracle_sparse_attn_rows(_p(Q), _p(K), _p(V), pos0, H, Hkv, D, r, sel.shape[1],
@@ -287,6 +317,8 @@ def select_rows(qi, kbar, rows, pos0: int = 0, Kbudget: int = 512, r: int = 4,
     n = rows.size
     Hi, Di = qi.shape[1], qi.shape[2]
     nb = kbar.shape[0]
+    if rows.size and (rows.min() < 0 or rows.max() >= qi.shape[0]):
+        raise ValueError(f"select_rows: a row lies outside the {qi.shape[0]} indexer rows")
     s = np.empty((n, nb)) if want_scores else None
     sel = np.empty((n, Kbudget), dtype=np.int32)
     nsel = np.empty(n, dtype=np.int32)
@@ -333,6 +365,7 @@ def dense_rows(Q, K, V, rows, pos0: int = 0):
     n = rows.size
     _, H, D = Q.shape
     Hkv = K.shape[1]
+    _check_rows("dense_rows", rows, Q.shape[0], pos0 + rows, K.shape[0])
     O = np.empty((n, H, D))
     lse = np.empty((n, H))
     _load().qsa_oracle_dense_rows(_p(Q), _p(K), _p(V), pos0, H, Hkv, D, _p(rows), n, _p(O),
@@ -362,6 +395,7 @@ def distill_rows(Q, K, qi, kbar, rows, pos0: int = 0, r: int = 4, mode: int = MO
     Q, K, qi, kbar = (_c(a, np.uint16) for a in (Q, K, qi, kbar))
     rows = _c(rows, np.int64)
     _, H, D = Q.shape
+    _check_rows("distill_rows", rows, min(Q.shape[0], qi.shape[0]), pos0 + rows, K.shape[0])
     kl = np.empty(rows.size)
     _load().qsa_oracle_distill_rows(_p(Q), _p(K), _p(qi), _p(kbar), kbar.shape[0], pos0, H,
                                     K.shape[1], D, qi.shape[1], qi.shape[2], r, mode, _p(rows),
@@ -396,6 +430,10 @@ def sparse_kl_rows(Q, K, qi, kbar, rows, sel, nsel, pos0: int = 0, r: int = 4,
     sel = _c(sel, np.int32)
     nsel = _c(nsel, np.int32)
     _, H, D = Q.shape
+    _check_rows("sparse_kl_rows", rows, min(Q.shape[0], qi.shape[0]), pos0 + rows, K.shape[0],
+                sel, nsel, r)
+    if (pos0 + rows).size and ((pos0 + rows + 1) // r).max() > kbar.shape[0]:
+        raise ValueError("sparse_kl_rows: fewer pooled keys than complete blocks")
     kl = np.empty(rows.size)
     _load().qsa_oracle_sparse_kl_rows(_p(Q), _p(K), _p(qi), _p(kbar), kbar.shape[0], pos0, H,
                                       K.shape[1], D, qi.shape[1], qi.shape[2], r, mode,

@@ -77,7 +77,8 @@ void qsa_oracle_rope(const uint16_t *x, uint16_t *y, int64_t T, int nheads, int 
         for (int h = 0; h < nheads; ++h) {
             const uint16_t *xr = x + (t * nheads + h) * (int64_t)head_dim;
             uint16_t *yr = y + (t * nheads + h) * (int64_t)head_dim;
-            double a[128], b[128];
+            double *a = (double *)malloc(sizeof(double) * (size_t)(half > 0 ? 2 * half : 1));
+            double *b = a + half;
             for (int j = 0; j < half; ++j) {
                 a[j] = bf16_to_f64(xr[j]);
                 b[j] = bf16_to_f64(xr[j + half]);
@@ -91,6 +92,7 @@ void qsa_oracle_rope(const uint16_t *x, uint16_t *y, int64_t T, int nheads, int 
             }
             if (yr != xr)
                 for (int d = rope_dim; d < head_dim; ++d) yr[d] = xr[d];
+            free(a);
         }
     }
 }
@@ -110,7 +112,8 @@ void qsa_oracle_compress_ext(const uint16_t *k, int64_t Tk, int Di, int r, int m
     int64_t nb = Tk / r;
 #pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < nb; ++b) {
-        double m[1024], m2[1024];
+        double *m = (double *)malloc(sizeof(double) * 2 * (size_t)Di);
+        double *m2 = m + Di;
         for (int d = 0; d < Di; ++d) {
             double s = 0.0;
             for (int t = 0; t < r; ++t) s += bf16_to_f64(k[(b * r + t) * Di + d]);
@@ -139,6 +142,7 @@ void qsa_oracle_compress_ext(const uint16_t *k, int64_t Tk, int Di, int r, int m
             for (int d = 0; d < Di; ++d) m[d] = m2[d];
         }
         for (int d = 0; d < Di; ++d) kbar[b * Di + d] = f64_to_bf16(m[d]);
+        free(m);
     }
 }
 
@@ -168,16 +172,16 @@ int64_t qsa_oracle_scores_row(const uint16_t *qi_row, const uint16_t *kbar, int6
                               int64_t p, int Hi, int Di, int r, int mode, double *s) {
     int64_t nc = qsa_oracle_num_complete(p, r);
     if (nc > nb_avail) nc = nb_avail;
-    double q[8][256];
+    double *q = (double *)malloc(sizeof(double) * (size_t)Hi * (size_t)Di);
     for (int h = 0; h < Hi; ++h)
-        for (int d = 0; d < Di; ++d) q[h][d] = bf16_to_f64(qi_row[h * Di + d]);
+        for (int d = 0; d < Di; ++d) q[h * Di + d] = bf16_to_f64(qi_row[h * Di + d]);
     double scale = 1.0 / sqrt((double)Di);
     for (int64_t b = 0; b < nc; ++b) {
         const uint16_t *kr = kbar + b * Di;
         double acc = mode == 0 ? -INFINITY : 0.0;
         for (int h = 0; h < Hi; ++h) {
             double dot = 0.0;
-            for (int d = 0; d < Di; ++d) dot += q[h][d] * bf16_to_f64(kr[d]);
+            for (int d = 0; d < Di; ++d) dot += q[h * Di + d] * bf16_to_f64(kr[d]);
             if (mode == 0) {
                 if (dot > acc) acc = dot;
             } else {
@@ -186,6 +190,7 @@ int64_t qsa_oracle_scores_row(const uint16_t *qi_row, const uint16_t *kbar, int6
         }
         s[b] = mode == 0 ? acc * scale : acc;
     }
+    free(q);
     return nc;
 }
 
@@ -275,10 +280,10 @@ void qsa_oracle_attend_row(const uint16_t *q_row, const uint16_t *K, const uint1
     int group = H / Hkv;
     double scale = 1.0 / sqrt((double)D);
     double *l = (double *)malloc(sizeof(double) * (size_t)(ntok > 0 ? ntok : 1));
+    double *q = (double *)malloc(sizeof(double) * (size_t)D);
     double err = 0.0;
     for (int h = 0; h < H; ++h) {
         int g = h / group;
-        double q[512];
         for (int d = 0; d < D; ++d) q[d] = bf16_to_f64(q_row[h * D + d]);
         double m = -INFINITY;
         for (int64_t j = 0; j < ntok; ++j) {
@@ -303,6 +308,7 @@ void qsa_oracle_attend_row(const uint16_t *q_row, const uint16_t *K, const uint1
         lse[h] = m + log(sw);
     }
     if (max_wsum_err) *max_wsum_err = err;
+    free(q);
     free(l);
 }
 
@@ -448,9 +454,9 @@ double qsa_oracle_distill_row(const uint16_t *q_row, const uint16_t *K, int H, i
     const double inv_sqrt_d = 1.0 / sqrt((double)D);
     double *l = (double *)malloc(sizeof(double) * (size_t)(p + 1));
     double *T = (double *)calloc((size_t)nc, sizeof(double));
+    double *q = (double *)malloc(sizeof(double) * (size_t)D);
     for (int h = 0; h < H; ++h) {
         const int g = h / (H / Hkv);
-        double q[512];
         for (int d = 0; d < D; ++d) q[d] = bf16_to_f64(q_row[h * D + d]);
         double m = -INFINITY;
         for (int64_t j = 0; j <= p; ++j) {
@@ -487,6 +493,7 @@ double qsa_oracle_distill_row(const uint16_t *q_row, const uint16_t *K, int H, i
         if (T_out) T_out[b] = t;
         if (logS_out) logS_out[b] = ls;
     }
+    free(q);
     free(l);
     free(T);
     return kl;

@@ -19,6 +19,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
 _LIB_PATH = os.path.join(_HERE, "libqsa_synth.so")
+# A test that runs the generator under the sanitizers points this variable at
+# an instrumented build (tests/test_sanitizers.py).
+_LIB_OVERRIDE = os.environ.get("QSA_SYNTH_LIB")
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_QIDX, STREAM_KIDX, STREAM_NEEDLE = 1, 2, 3, 4, 5, 6
 
@@ -27,8 +30,10 @@ _lib = None
 
 def build(force: bool = True) -> str:
     """Compile ``libqsa_synth.so`` with gcc (OpenMP)."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
+    stale = (not os.path.exists(_LIB_PATH)
+             or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC))
+    if force or stale:
+        tmp = f"{_LIB_PATH}.tmp{os.getpid()}"
         subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11",
                                "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB_PATH)
@@ -38,9 +43,12 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build(force=True)
-        lib = ctypes.CDLL(_LIB_PATH)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB_PATH):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB_PATH)
         u64, i64, i32 = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int
         vp = ctypes.c_void_p
         lib.synth_fill_normal_bf16.argtypes = [u64, u64, u64, i64, vp]

@@ -63,6 +63,47 @@ MUTATIONS = {
                                   "int64_t from = qsa_oracle_num_complete(p, r) * r;"),
     "reuse_tail_stops_short": ("for (int64_t j = from; j <= p; ++j) tok[n++] = j;",
                                "for (int64_t j = from; j < p; ++j) tok[n++] = j;"),
+    # row drivers: a position or a row taken from the loop index instead of
+    # the row's own index
+    "sparse_attn_rows_position_by_index": ("int64_t p = pos0 + t;\n        int ns = nsel[i];",
+                                           "int64_t p = pos0 + i;\n        int ns = nsel[i];"),
+    "sparse_attn_rows_query_by_index": (
+        "qsa_oracle_attend_row(Q + t * H * (int64_t)D, K, V, H, Hkv, D, tok, ntok,\n"
+        "                              O + i * H * (int64_t)D, lse + i * H, &e);",
+        "qsa_oracle_attend_row(Q + i * H * (int64_t)D, K, V, H, Hkv, D, tok, ntok,\n"
+        "                              O + i * H * (int64_t)D, lse + i * H, &e);"),
+    "qsa_rows_at_query_row_zero": (
+        "qsa_oracle_attend_row(Q + i * H * (int64_t)D, K, V, H, Hkv, D, tok, ntok,\n"
+        "                              O + i * H * (int64_t)D, lse + i * H, &wsum_err[i]);",
+        "qsa_oracle_attend_row(Q, K, V, H, Hkv, D, tok, ntok,\n"
+        "                              O + i * H * (int64_t)D, lse + i * H, &wsum_err[i]);"),
+    "qsa_rows_at_indexer_row_zero": ("qsa_oracle_scores_row(qi + i * Hi * (int64_t)Di, kbar, nb, p,",
+                                     "qsa_oracle_scores_row(qi, kbar, nb, p,"),
+    "qsa_rows_at_position_of_row_zero": ("int64_t p = pos[i];", "int64_t p = pos[0];"),
+    "qsa_rows_position_by_index": (
+        "int64_t p = pos0 + t;\n        int64_t nc_full = qsa_oracle_num_complete(p, r);\n"
+        "        double *s = (double *)malloc(sizeof(double) * (size_t)(nc_full > 0 ? nc_full : 1));\n"
+        "        int64_t nc = qsa_oracle_scores_row(qi + t * Hi * (int64_t)Di, kbar, nb, p, Hi, Di, r,\n"
+        "                                           mode, s);\n        int32_t *blk",
+        "int64_t p = pos0 + i;\n        int64_t nc_full = qsa_oracle_num_complete(p, r);\n"
+        "        double *s = (double *)malloc(sizeof(double) * (size_t)(nc_full > 0 ? nc_full : 1));\n"
+        "        int64_t nc = qsa_oracle_scores_row(qi + t * Hi * (int64_t)Di, kbar, nb, p, Hi, Di, r,\n"
+        "                                           mode, s);\n        int32_t *blk"),
+    "select_rows_position_by_index": (
+        "int64_t p = pos0 + t;\n        int64_t nc_full = qsa_oracle_num_complete(p, r);\n"
+        "        double *s = (double *)malloc(sizeof(double) * (size_t)(nc_full > 0 ? nc_full : 1));\n"
+        "        int64_t nc = qsa_oracle_scores_row(qi + t * Hi * (int64_t)Di, kbar, nb, p, Hi, Di, r,\n"
+        "                                           mode, s);\n        if (s_out)",
+        "int64_t p = pos0 + i;\n        int64_t nc_full = qsa_oracle_num_complete(p, r);\n"
+        "        double *s = (double *)malloc(sizeof(double) * (size_t)(nc_full > 0 ? nc_full : 1));\n"
+        "        int64_t nc = qsa_oracle_scores_row(qi + t * Hi * (int64_t)Di, kbar, nb, p, Hi, Di, r,\n"
+        "                                           mode, s);\n        if (s_out)"),
+    "dense_rows_position_by_index": (
+        "int64_t p = pos0 + t;\n        int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)(p + 1));",
+        "int64_t p = pos0 + i;\n        int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)(p + 1));"),
+    # bf16 narrowing below the normal range
+    "bf16_subnormal_quantum": ("if (e < -125) e = -125;", "if (e < -126) e = -126;"),
+    "bf16_subnormal_unclamped": ("if (e < -125) e = -125;", "if (e < -1075) e = -1075;"),
 }
 
 

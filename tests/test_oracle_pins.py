@@ -710,3 +710,202 @@ def test_sparse_kl_subset_rows_scores_and_bounds(oracle_lib, synth_lib):
         assert kl >= -1e-12 and abs(kl - dense[i]) > 1e-6
         kl0, _, _ = oracle_lib.sparse_kl_row(Q[t], K, int(t), blk, np.log(T) - 2.0)
         assert abs(kl0) < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# Row drivers (the functions every full-size GPU comparison calls): rows that
+# are not 0..n-1, a chunk that does not start at position 0, a compact form.
+# Planted inputs make each row's selection, token set and query row visible
+# in its output, so a row or position taken from the wrong index fails.
+# ----------------------------------------------------------------------------
+
+_DRV_POS0, _DRV_TQ, _DRV_K = 100, 100, 3
+# (p + 1) mod 4 of the rows' positions p = 100 + t is 2, 1, 0, 3, 2: every
+# trailing-block length, and never the value of position 100 + i for row i
+_DRV_ROWS = np.array([5, 40, 63, 2, 97])
+
+
+def _driver_inputs(mode):
+    """Positions 0..199; queries t = 0..99 at positions 100 + t.  Indexer:
+    pooled key b carries c_b in dim 0 (distinct multiples of 1/8), every head
+    of query t carries +1 (t even) or -1 (t odd) there, so the score order is
+    c ascending or descending by row.  Returns inputs, scores per row, the
+    selection by brute force and the planted target token per row."""
+    Tk, nb = _DRV_POS0 + _DRV_TQ, (_DRV_POS0 + _DRV_TQ) // 4
+    c = (np.random.default_rng(17).permutation(nb) - 20.0) / 8.0
+    kb = np.zeros((nb, 128), dtype=np.float32)
+    kb[:, 0] = c
+    qi = np.zeros((_DRV_TQ, 4, 128), dtype=np.float32)
+    qi[:, :, 0] = np.where(np.arange(_DRV_TQ) % 2 == 0, 1.0, -1.0)[:, None]
+    sel, targets = {}, {}
+    for t in _DRV_ROWS:
+        p = _DRV_POS0 + int(t)
+        nc = (p + 1) // 4
+        sgn = 1.0 if t % 2 == 0 else -1.0
+        sc = [sgn * c[b] / math.sqrt(128) if mode == 0 else 4 * max(0.0, sgn * c[b])
+              for b in range(nc)]
+        blocks = sorted(sorted(range(nc), key=lambda b: (-sc[b], b))[:_DRV_K])
+        sel[int(t)] = blocks
+        targets[int(t)] = 4 * blocks[1] + int(t) % 4
+    assert len(set(targets.values())) == len(_DRV_ROWS)
+    # one-hot keys and values: K[j, g, j] = 64, V[j, g, j] = 1 (j < 200 < 256)
+    K = np.zeros((Tk, 2, 256), dtype=np.float32)
+    V = np.zeros((Tk, 2, 256), dtype=np.float32)
+    for j in range(Tk):
+        K[j, :, j] = 64.0
+        V[j, :, j] = 1.0
+    # Q row t points at its target token: logit 64 * 64 / 16 = 256 there, 0
+    # elsewhere, so the softmax is one-hot at the target to e^-256
+    Qt = np.zeros((_DRV_TQ, 24, 256), dtype=np.float32)
+    for t, j in targets.items():
+        Qt[t, :, j] = 64.0
+    return dict(kb=bf(kb), qi=bf(qi), K=bf(K), V=bf(V), Qt=bf(Qt),
+                Q0=np.zeros((_DRV_TQ, 24, 256), dtype=np.uint16), sel=sel, targets=targets)
+
+
+def _token_set_expected(blocks, p):
+    nc = (p + 1) // 4
+    return sorted([4 * b + u for b in blocks for u in range(4)] + list(range(4 * nc, p + 1)))
+
+
+def _check_uniform(O, lse, S, what):
+    """Q = 0: O of every head is 1/|S| on the tokens of S, 0 elsewhere."""
+    want = np.zeros(256)
+    want[S] = 1.0 / len(S)
+    assert np.allclose(O, want[None, :], atol=1e-14), what
+    assert np.allclose(lse, math.log(len(S)), atol=1e-12), what
+
+
+def _check_target(O, lse, target, what):
+    want = np.zeros(256)
+    want[target] = 1.0
+    assert np.allclose(O, want[None, :], atol=1e-12), what
+    assert np.allclose(lse, 256.0, atol=1e-12), what
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_row_drivers_select_planted(oracle_lib, mode):
+    x = _driver_inputs(mode)
+    res = oracle_lib.select_rows(x["qi"], x["kb"], _DRV_ROWS, pos0=_DRV_POS0, Kbudget=_DRV_K,
+                                 mode=mode)
+    for i, t in enumerate(_DRV_ROWS):
+        assert list(res["sel"][i, :res["nsel"][i]]) == x["sel"][int(t)], (mode, t)
+        assert np.all(res["sel"][i, res["nsel"][i]:] == -1)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_row_drivers_qsa_rows_planted(oracle_lib, mode):
+    """qsa_rows (full chunk arrays, row t = query at pos0 + t) and
+    qsa_rows_at (compact arrays, row i = query at positions[i]) give each row
+    its own selection, trailing block and query row."""
+    x = _driver_inputs(mode)
+    rows = _DRV_ROWS
+    pos = _DRV_POS0 + rows
+    for qkey in ("Q0", "Qt"):
+        Q = x[qkey]
+        full = oracle_lib.qsa_rows(Q, x["K"], x["V"], x["qi"], x["kb"], rows, pos0=_DRV_POS0,
+                                   Kbudget=_DRV_K, mode=mode)
+        at = oracle_lib.qsa_rows_at(Q[rows], x["K"], x["V"], x["qi"][rows], x["kb"], pos,
+                                    Kbudget=_DRV_K, mode=mode)
+        for res, name in ((full, "qsa_rows"), (at, "qsa_rows_at")):
+            for i, t in enumerate(rows):
+                t = int(t)
+                what = (name, qkey, mode, t)
+                assert list(res["sel"][i, :res["nsel"][i]]) == x["sel"][t], what
+                S = _token_set_expected(x["sel"][t], _DRV_POS0 + t)
+                if qkey == "Q0":
+                    _check_uniform(res["O"][i], res["lse"][i], S, what)
+                else:
+                    _check_target(res["O"][i], res["lse"][i], x["targets"][t], what)
+            assert np.all(res["wsum_err"] < 1e-12)
+
+
+def test_row_drivers_sparse_attn_rows_planted(oracle_lib):
+    """Attention over a given selection: row i uses Q row rows[i], the
+    selection row i and the trailing block of position pos0 + rows[i]."""
+    x = _driver_inputs(0)
+    rows = _DRV_ROWS
+    sel = np.full((rows.size, 8), -1, dtype=np.int32)   # a wider budget than used
+    nsel = np.zeros(rows.size, dtype=np.int32)
+    for i, t in enumerate(rows):
+        sel[i, :_DRV_K] = x["sel"][int(t)]
+        nsel[i] = _DRV_K
+    for qkey in ("Q0", "Qt"):
+        O, lse = oracle_lib.sparse_attn_rows(x[qkey], x["K"], x["V"], rows, sel, nsel,
+                                             pos0=_DRV_POS0)
+        for i, t in enumerate(rows):
+            t = int(t)
+            S = _token_set_expected(x["sel"][t], _DRV_POS0 + t)
+            if qkey == "Q0":
+                _check_uniform(O[i], lse[i], S, (qkey, t))
+            else:
+                _check_target(O[i], lse[i], x["targets"][t], (qkey, t))
+    # an empty selection leaves the trailing block alone
+    O, lse = oracle_lib.sparse_attn_rows(x["Q0"], x["K"], x["V"], rows, sel,
+                                         np.zeros(rows.size, dtype=np.int32), pos0=_DRV_POS0)
+    for i, t in enumerate(rows):
+        p = _DRV_POS0 + int(t)
+        tail = list(range(4 * ((p + 1) // 4), p + 1))
+        if tail:
+            _check_uniform(O[i], lse[i], tail, ("empty", int(t)))
+
+
+def test_row_drivers_dense_rows_planted(oracle_lib):
+    x = _driver_inputs(0)
+    rows = _DRV_ROWS
+    for qkey in ("Q0", "Qt"):
+        O, lse = oracle_lib.dense_rows(x[qkey], x["K"], x["V"], rows, pos0=_DRV_POS0)
+        for i, t in enumerate(rows):
+            t = int(t)
+            if qkey == "Q0":
+                _check_uniform(O[i], lse[i], list(range(_DRV_POS0 + t + 1)), (qkey, t))
+            else:
+                _check_target(O[i], lse[i], x["targets"][t], (qkey, t))
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_row_drivers_compact_within_budget_is_dense(oracle_lib, synth_lib, mode):
+    """Compact rows at positions whose context fits the budget: QSA is dense
+    causal attention there (N(0,1) inputs, rows out of order, positions
+    spread over every trailing-block length)."""
+    T, Kb = 60, 9
+    Q, K, V, qi, ki = _small_inputs(synth_lib, T, seed=21)
+    kb = oracle_lib.compress(ki)
+    pos = np.array([33, 2, 17, 36, 0, 24, 11])          # nc(p) <= 9
+    at = oracle_lib.qsa_rows_at(Q[pos], K, V, qi[pos], kb, pos, Kbudget=Kb, mode=mode)
+    Od, lsed = oracle_lib.dense_rows(Q, K, V, pos)
+    assert np.allclose(at["O"], Od, atol=1e-12) and np.allclose(at["lse"], lsed, atol=1e-12)
+    assert list(at["nsel"]) == [(p + 1) // 4 for p in pos]
+    # beyond the budget it is not dense, and it equals the full-array driver
+    pos2 = np.array([59, 41, 50])
+    at2 = oracle_lib.qsa_rows_at(Q[pos2], K, V, qi[pos2], kb, pos2, Kbudget=Kb, mode=mode)
+    full2 = oracle_lib.qsa_rows(Q, K, V, qi, kb, pos2, Kbudget=Kb, mode=mode)
+    Od2, _ = oracle_lib.dense_rows(Q, K, V, pos2)
+    assert np.abs(at2["O"] - Od2).max() > 1e-3
+    assert np.array_equal(at2["sel"], full2["sel"]) and np.array_equal(at2["O"], full2["O"])
+
+
+# ----------------------------------------------------------------------------
+# bf16 narrowing below the normal range: a fixed quantum of 2^-133, ties to
+# even, the sign kept.
+# ----------------------------------------------------------------------------
+
+def test_bf16_rounding_subnormals(oracle_lib):
+    o = oracle_lib
+    u = 2.0 ** -133                      # the smallest bf16 subnormal (bits 0x0001)
+    assert o.f64_to_bf16(u) == 0x0001
+    assert o.f64_to_bf16(0.5 * u) == 0x0000            # tie -> even (0)
+    assert o.f64_to_bf16(0.5 * u * (1 + 2 ** -20)) == 0x0001
+    assert o.f64_to_bf16(1.5 * u) == 0x0002            # tie -> even (2)
+    assert o.f64_to_bf16(2.5 * u) == 0x0002            # tie -> even (2)
+    assert o.f64_to_bf16(2.4 * u) == 0x0002
+    assert o.f64_to_bf16(-5 * u) == 0x8005
+    assert o.f64_to_bf16(-0.25 * u) == 0x8000          # rounds to -0
+    assert o.f64_to_bf16(0.25 * u) == 0x0000
+    assert o.f64_to_bf16(127 * u) == 0x007F            # largest subnormal
+    assert o.f64_to_bf16(127.5 * u) == 0x0080          # tie -> even: the smallest normal 2^-126
+    assert o.f64_to_bf16(2.0 ** -126) == 0x0080
+    # the normal quantum starts at 2^-126: 2^-126 + 2^-133 is exact
+    assert o.f64_to_bf16(2.0 ** -126 + u) == 0x0081
+    for k in (1, 2, 3, 64, 100, 127):
+        assert f32(o.f64_to_bf16(k * u)) == np.float32(k * u)
