@@ -127,8 +127,45 @@ def page_table(B, L, P, seed):
     return perm.view(B, L // P).to(torch.int32).cuda(), perm.cuda()
 
 
+def probe_lib():
+    """The gather-ceiling probe (libqsa_probe.so, a measurement kernel built
+    beside the layer's library), or None when it is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "block_sparse_long_08_amd", "libqsa_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.qsa_probe_gather.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, vp, vp]
+    lib.qsa_probe_gather.restype = i32
+    return lib
+
+
+def gather_ceiling(layer, Kr, V, reps):
+    """Time the probe over the layer's selection in the attention's row
+    chunks, each launch alone on one stream: the time the memory system needs
+    for exactly the attention's gathers."""
+    import torch
+    lib = probe_lib()
+    if lib is None or layer.pages is not None:
+        return None
+    out = torch.empty((layer.Tq, layer.Hkv), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        for r0, n in layer._chunks():
+            st = lib.qsa_probe_gather(Kr.data_ptr(), V.data_ptr(), layer.blk_idx[r0:].data_ptr(),
+                                      layer.n_sel[r0:].data_ptr(), n, layer.pos0 + r0,
+                                      layer.budget, layer.Hkv, out[r0:].data_ptr(), stream)
+            if st != 0:
+                raise RuntimeError("qsa_probe_gather rejected its arguments")
+    run()
+    torch.cuda.synchronize()
+    return _time_steps(run, reps)
+
+
 def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, page_tokens=0,
-                  with_distill=False, pipeline_rows=4096):
+                  with_distill=False, pipeline_rows=None, with_probe=False):
     import torch
     import block_sparse_long_08_amd as qsa
     Tq, pos0, budget, nd = WORKLOADS[name]
@@ -194,14 +231,27 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
     nlaunch = 1
     if pipe:
         # stage durations from events around each chunk's selection (launch
-        # stream) and each attention launch (its own stream); they overlap
+        # stream) and each attention launch (its own stream); the two overlap,
+        # so each is its time beside the other, not its cost alone
         nlaunch = len(att_ev) // steps
         sel_ms = sum(a.elapsed_time(b) for a, b in sel_ev) / steps
         att_ms = sum(a.elapsed_time(b) for a, b in att_ev) / steps
-        stage = dict(rope_pool=stage["rope_pool"], select=sel_ms, attend=att_ms,
-                     select_attend_overlapped=stage["select_attend"])
+        stage = dict(rope_pool=stage["rope_pool"], select_overlapped=sel_ms,
+                     attend_overlapped=att_ms, select_attend=stage["select_attend"])
+    # each stage alone on one stream (after the timed steps): every row
+    # chunk's selection, then every chunk's attention
+    Kr0, kb0 = layer.rope_and_pool(Q, K, ki, kbar)
+    qs0 = layer.rope_indexer(qi)
+    torch.cuda.synchronize()
+    reps = max(1, min(steps, 3))
+    stage["select_standalone"] = _time_steps(lambda: layer.select(qs0, kb0), reps)
+    stage["attend_standalone"] = _time_steps(lambda: layer.attend_chunks(Kr0, V), reps)
+    probe_ms = gather_ceiling(layer, Kr0, V, reps) if with_probe else None
     res = dict(ms_per_step=wall * 1e3, stages_ms=stage, Tq=Tq, Tk=Tk, budget=budget,
                attn_launches=nlaunch, pipeline_rows=layer.pipeline_rows)
+    res["attend_launch_ms"] = (att_ms if pipe else stage["attend"]) / nlaunch
+    if probe_ms is not None:
+        res["gather_probe_ms"] = probe_ms
     # algorithmic work of the step
     nsel = layer.n_sel.cpu().numpy().astype(np.int64)
     pos = pos0 + np.arange(Tq)
@@ -230,7 +280,7 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
         e1.record()
         torch.cuda.synchronize()
         dms = e0.elapsed_time(e1) / dsteps
-        res.update(dense_ms=dms, qsa_attention_ms=stage["select"] + stage["attend"])
+        res.update(dense_ms=dms)
         if with_distill and pages is None:
             # stage-1 distillation forward: KL of the indexer against the
             # block-max-pooled dense attention (lse of the dense pass above)
@@ -270,8 +320,9 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
             e1.record()
             torch.cuda.synchronize()
             fms = e0.elapsed_time(e1) / dsteps
-            res["sparse_kl"] = dict(ms=fms, launches=nlaunch, attend_ms=stage["attend"],
-                                    vs_attend=fms / stage["attend"],
+            res["sparse_kl"] = dict(ms=fms, launches=nlaunch,
+                                    attend_standalone_ms=stage["attend_standalone"],
+                                    vs_attend=fms / stage["attend_standalone"],
                                     hbm_gbps_algorithmic=attn_bytes / (fms * 1e-3) / 1e9,
                                     hbm_frac_algorithmic=attn_bytes / (fms * 1e-3) / 1e9
                                     / HBM_PEAK_GBS,
@@ -435,6 +486,18 @@ def calibration_copy():
     torch.cuda.empty_cache()
 
 
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(name, x, budget, seconds=15.0, kl_sample=None):
     """The oracle (fp64, OpenMP over rows) on sampled query rows of the workload."""
     import oracle
@@ -454,6 +517,7 @@ def cpu_baseline(name, x, budget, seconds=15.0, kl_sample=None):
         t_rows += time.time() - t1
         rows_done += rows.size
     out = dict(value=rows_done / t_rows, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+               cpu_model=cpu_model(), host_logical_cpus=os.cpu_count(),
                sample=f"{rows_done} query rows drawn from the second half of the {name} "
                       f"workload (full QSA per row: scores over every complete block, "
                       f"top-{budget}, attention over the selected tokens, 24 heads); "
@@ -516,10 +580,10 @@ def main():
     ap.add_argument("--distill", default="on", choices=["on", "off"],
                     help="also time the stage-1 distillation KL on the prefill workload "
                          "(needs the dense baseline's log-sum-exp)")
-    ap.add_argument("--pipeline-rows", type=int, default=4096,
+    ap.add_argument("--pipeline-rows", type=int, default=None,
                     help="rows per selection chunk whose attention overlaps the next chunk's "
-                         "selection; 0 runs the selection of all rows, then the attention "
-                         "(standalone stage times)")
+                         "selection; 0 runs the selection of all rows, then the attention; "
+                         "default: the layer's own choice")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (scale of the HBM byte counters)")
     args = ap.parse_args()
@@ -535,29 +599,42 @@ def main():
     if args.calibrate_copy:
         calibration_copy()
     pre, x = bench_prefill(args.workload, args.steps, args.warmup, with_dense=args.dense == "all",
-                           with_distill=args.distill == "on", pipeline_rows=args.pipeline_rows)
+                           with_distill=args.distill == "on", pipeline_rows=args.pipeline_rows,
+                           with_probe=True)
     log(f"prefill {args.workload}: {pre['ms_per_step']:.2f} ms/step, stages {pre['stages_ms']}")
     st = pre["stages_ms"]
-    dominant = max(("rope_pool", "select", "attend"), key=st.get)
-    if dominant == "attend":
-        # per launch: the attention runs as attn_launches row chunks per step
-        nl = pre["attn_launches"]
-        achieved = pre["attn_bytes"] / (st["attend"] * 1e-3) / 1e9
-        traffic = measured_traffic(args.workload)
-        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=achieved / HBM_PEAK_GBS, traffic=traffic,
-                    kernel="attn_prefill_kernel", launch_ms=st["attend"] / nl,
-                    algorithmic_bytes=pre["attn_bytes"] / nl, launches_per_step=nl)
-        if traffic:
-            # the measured bytes over the same duration: the rate the memory
-            # fabric actually served (the caches serve the rest of the gathers,
-            # which is how the algorithmic rate can pass the HBM peak)
-            roof["traffic_gbps"] = traffic / (st["attend"] / nl * 1e-3) / 1e9
-            roof["traffic_frac"] = roof["traffic_gbps"] / HBM_PEAK_GBS
+    # the dominant kernel of the step is the sparse attention (attn_launches
+    # row chunks per step); its launch duration from the timed region
+    nl = pre["attn_launches"]
+    launch_s = pre["attend_launch_ms"] * 1e-3
+    algo = pre["attn_bytes"] / nl            # gathers (no cache reuse), Q, O per launch
+    algo_gbps = algo / launch_s / 1e9
+    flop = pre["attn_flop"] / nl
+    traffic = measured_traffic(args.workload)
+    mfma = dict(flop_per_launch=flop, tflops=flop / launch_s / 1e12,
+                frac=flop / launch_s / 1e12 / BF16_PEAK_TFLOPS)
+    if traffic:
+        # the bound: bytes the memory fabric delivered (L2 misses and writes,
+        # counter-measured) over the launch duration; the gathers' algorithmic
+        # rate passes the HBM peak because the caches serve part of them
+        achieved = traffic / launch_s / 1e9
+        basis = "measured fabric bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     else:
-        achieved = pre["idx_flop"] / (st["select"] * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=achieved, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=achieved / BF16_PEAK_TFLOPS, traffic=None, kernel="select (scores+top-K)")
+        achieved = algo_gbps
+        basis = "algorithmic bytes, no cache reuse (no counter summary for these kernel sources)"
+    roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=achieved / HBM_PEAK_GBS, traffic=traffic, basis=basis,
+                kernel="attn_prefill_kernel", launch_ms=launch_s * 1e3, launches_per_step=nl,
+                algorithmic_bytes=algo, algorithmic_gbps_no_reuse=algo_gbps,
+                algorithmic_frac_no_reuse=algo_gbps / HBM_PEAK_GBS, mfma=mfma)
+    if "gather_probe_ms" in pre:
+        # the same gathers by the probe kernel (no compute), each launch alone,
+        # against the attention's launches alone over the same row chunks
+        att_alone = st["attend_standalone"]
+        roof["gather_ceiling"] = dict(
+            probe_ms_per_step=pre["gather_probe_ms"], attend_standalone_ms_per_step=att_alone,
+            probe_gather_gbps_no_reuse=pre["gather_bytes"] / (pre["gather_probe_ms"] * 1e-3) / 1e9,
+            attention_frac_of_ceiling=pre["gather_probe_ms"] / att_alone)
     out = {
         "metric": METRIC,
         "value": pre["Tq"] / (pre["ms_per_step"] * 1e-3),
@@ -628,7 +705,8 @@ def main():
         m = dict(workload="prefill_1m_chunk", ms_per_step=m_pre["ms_per_step"],
                  tokens_per_s=m_pre["Tq"] / (m_pre["ms_per_step"] * 1e-3),
                  stages_ms=m_pre["stages_ms"],
-                 attend_gather_gbs=m_pre["attn_bytes"] / (m_pre["stages_ms"]["attend"] * 1e-3) / 1e9)
+                 attend_gather_gbs_no_reuse=m_pre["attn_bytes"] /
+                 (m_pre["attend_launch_ms"] * m_pre["attn_launches"] * 1e-3) / 1e9)
         if "dense_ms" in m_pre:
             m.update(dense_ms=m_pre["dense_ms"],
                      speedup_vs_dense=m_pre["dense_ms"] / m_pre["ms_per_step"])
@@ -659,6 +737,27 @@ def main():
         if "next_n_4" in m_dec:
             log(f"decode decode_1m_b4 next_n=4: {m_dec['next_n_4']['ms_per_step']:.3f} ms/step")
         x = None
+    # QSA against dense attention on the same GPU: measured, and against a
+    # dense kernel at the roofline (MFMA peak for prefill, one read of the
+    # cache at the HBM peak for decode), which no faster dense kernel can
+    # shrink
+    sp = {}
+    if "prefill_speedup_vs_dense" in out:
+        sp[args.workload] = dict(measured=out["prefill_speedup_vs_dense"],
+                                 vs_dense_at_roofline=out["prefill_speedup_vs_dense_at_mfma_peak"])
+    for key in ("prefill_1m_chunk", "prefill_1m_chunk16k_paged"):
+        if key in out and "speedup_vs_dense" in out[key]:
+            sp[key] = dict(measured=out[key]["speedup_vs_dense"],
+                           vs_dense_at_roofline=out[key]["speedup_vs_dense_at_mfma_peak"])
+    for key in ("decode", "decode_1m_b4"):
+        d = out.get(key)
+        if not d:
+            continue
+        for name, rec in ((d["workload"], d), (d["workload"] + "_next_n_4", d.get("next_n_4"))):
+            if rec and "speedup_vs_dense" in rec:
+                sp[name] = dict(measured=rec["speedup_vs_dense"],
+                                vs_dense_at_roofline=rec["speedup_vs_dense_at_hbm_peak"])
+    out["speedup_vs_dense"] = sp
     if not args.no_cpu:
         if x is None:
             x = gen_prefill(args.workload)

@@ -18,6 +18,26 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          "-Wno-unused-command-line-argument"]
 
 
+# The benchmark's gather-ceiling probe (a measurement kernel, not part of the
+# layer) lives in a library of its own.
+PROBE_SRC = "probe_gather.hip"
+PROBE_LIB = os.path.join(HERE, "libqsa_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", "-x", "hip", os.path.join(CSRC, PROBE_SRC), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        errs = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{errs}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False, resource_usage: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = []
@@ -39,6 +59,7 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     tmp = LIB + ".tmp"
     subprocess.check_call([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    build_probe(verbose)
     return LIB
 
 

@@ -578,20 +578,27 @@ __device__ __forceinline__ void record_store(const WaveState &st, float *rec, in
 }
 
 // ------------------------------------------------------------------------
-// Decode: workgroup (4 waves) per (split, KV head x column tile, sequence);
+// Decode: workgroup (4 waves) per (split, column tile, KV head, sequence);
 // waves take the split's stages round-robin, merge through LDS, and wave 0
 // writes the split's record (unnormalised O^T, max, weight sum) to the
 // workspace.  The Tq newest queries of a sequence share its selection (made
 // for the first of them, at seq_len - Tq); the columns of a tile are 16
 // (query, head) pairs and each column masks the tail past its own query.
+// Grid x enumerates (split, column tile) so that the column tiles of one
+// split have workgroup ids 8 apart: workgroups go to the 8 XCDs in turn, so
+// those tiles run on one XCD back to back and its L2 serves their repeated
+// reads of the split's keys and values (one HBM read per split, not one
+// per column tile).
 template <bool DENSE, bool MULTI, bool PAGED>
 __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit, int sps,
                                                           int nct) {
     constexpr int PMODE = PAGED ? (DENSE ? 2 : 1) : 0;
     __shared__ __attribute__((aligned(16))) unsigned char lds[3 * kRecFloats * 4];
     __shared__ int32_t lst[DENSE ? 1 : kMaxListLds];
-    const int split = blockIdx.x;
-    const int g = blockIdx.y / nct, ct = blockIdx.y - g * nct;
+    const int bx = blockIdx.x, grp = bx / (8 * nct), rem = bx - grp * 8 * nct;
+    const int ct = rem >> 3, split = 8 * grp + (rem & 7);
+    if (split >= nsplit) return;  // the grid rounds the splits up to 8
+    const int g = blockIdx.y;
     const int64_t b = blockIdx.z;
     const int nq = static_cast<int>(a.Tq);
     int64_t Lb = a.seq_len[b];
@@ -783,8 +790,8 @@ hipError_t launch_attn_decode(const AttnArgs &a, int nsplit, hipStream_t s) {
         decode_max_entries(nq, a.blk_idx ? static_cast<int64_t>(a.Kbudget) : a.Lmax / kBlock);
     const int64_t nstages = (max_entries + kStageEntries - 1) / kStageEntries;
     const int sps = static_cast<int>((nstages + nsplit - 1) / nsplit);
-    const dim3 grid(static_cast<uint32_t>(nsplit), static_cast<uint32_t>(a.Hkv * nct),
-                    static_cast<uint32_t>(a.B));
+    const dim3 grid(static_cast<uint32_t>((nsplit + 7) / 8 * 8 * nct),
+                    static_cast<uint32_t>(a.Hkv), static_cast<uint32_t>(a.B));
     launch_decode_variant(a, grid, nsplit, sps, nct, a.blk_idx == nullptr, nq > 1,
                           a.ptable != nullptr, s);
     hipError_t e = hipGetLastError();

@@ -18,6 +18,11 @@ from . import (DI, HI, R, SCORE_MAXHEAD, KBAR_MEAN, qsa_compress_keys, qsa_decod
                qsa_sparse_attn_decode, qsa_sparse_attn_prefill, qsa_sparse_attn_prefill_kl)
 
 
+# rows per selection chunk of the prefill pipeline (measured fastest at 128K
+# and 1M against 1,024 to 6,144)
+PIPELINE_ROWS = 4096
+
+
 class QSAPrefill:
     """Prefill of Tq queries at positions pos0 .. pos0+Tq-1 of one sequence.
 
@@ -34,13 +39,20 @@ class QSAPrefill:
     many rows, and each chunk's sparse attention runs on a second stream
     while the next chunk is selected (selection is MFMA and ALU work, the
     attention streams gathers from HBM, so the two overlap); the results are
-    those of the stages run one after the other.
+    those of the stages run one after the other.  pipeline_rows = 0: one
+    stage after the other.  None (default): chunks of 4,096 rows when there
+    are at least 8 of them, else no pipeline.  With fewer chunks the first
+    selection and the last attention are exposed and the two stages contend
+    for the same CUs (measured: a 1M-context chunk of 8,192 rows takes
+    7.99 ms in turn against 8.40 ms overlapped in 4,096-row chunks; 16,384
+    rows 15.8 against 17.5 ms; 131,072 rows 60.6 ms overlapped against
+    69.7 ms in turn).
     """
 
     def __init__(self, Tq: int, pos0: int = 0, H: int = 24, Hkv: int = 2, D: int = 256,
                  budget: int = 512, score_mode: int = SCORE_MAXHEAD, kbar_mode: int = KBAR_MEAN,
                  theta: float = 1e7, rope_dim: int = 64, fresh: bool = True,
-                 idx_rope_dim: int = 0, kbar_gain=None, pages=None, pipeline_rows: int = 4096,
+                 idx_rope_dim: int = 0, kbar_gain=None, pages=None, pipeline_rows=None,
                  device="cuda"):
         self.Tq, self.pos0, self.H, self.Hkv, self.D = Tq, pos0, H, Hkv, D
         self.pages = pages  # paged caches (fresh=False): K, V and kbar are page pools
@@ -60,6 +72,8 @@ class QSAPrefill:
         self.n_sel = torch.empty((Tq,), dtype=torch.int32, device=dev)
         self.O = torch.empty((Tq, H, D), dtype=torch.float32, device=dev)
         self.lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
+        if pipeline_rows is None:
+            pipeline_rows = PIPELINE_ROWS if Tq >= 8 * PIPELINE_ROWS else 0
         self.pipeline_rows = pipeline_rows if 0 < pipeline_rows < Tq else 0
         self.ws_bytes = qsa_select_workspace_bytes(1, self.pipeline_rows or Tq, self.nb, budget)
         self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=dev)
@@ -126,6 +140,12 @@ class QSAPrefill:
     def select(self, qi, kbar):
         for r0, n in self._chunks():
             self._select_rows(qi, kbar, r0, n)
+
+    def attend_chunks(self, Kr, V):
+        """The sparse attention of every row chunk, one after the other on the
+        current stream (the launches of the pipelined form, not overlapped)."""
+        for r0, n in self._chunks():
+            self._attend_rows(Kr, V, r0, n)
 
     def attend(self, Kr, V):
         self._attend_rows(Kr, V, 0, self.Tq)

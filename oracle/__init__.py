@@ -77,6 +77,9 @@ def _load():
         lib.qsa_oracle_sparse_attn_rows.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32,
                                                     vp, i64, vp, vp, vp, vp]
         lib.qsa_oracle_sparse_attn_rows.restype = None
+        lib.qsa_oracle_sparse_attn_rows_at.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                       i64, vp, vp, vp, vp]
+        lib.qsa_oracle_sparse_attn_rows_at.restype = None
         lib.qsa_oracle_select_rows.argtypes = [vp, vp, i64, i64, i32, i32, i32, i32, i32, vp,
                                                i64, vp, i64, vp, vp, vp, vp]
         lib.qsa_oracle_select_rows.restype = None
@@ -306,6 +309,27 @@ def sparse_attn_rows(Q, K, V, rows, sel, nsel, pos0: int = 0, r: int = 4):
     lse = np.empty((n, H))
     _load().qsa_oracle_sparse_attn_rows(_p(Q), _p(K), _p(V), pos0, H, Hkv, D, r, sel.shape[1],
                                         _p(rows), n, _p(sel), _p(nsel), _p(O), _p(lse))
+    return O, lse
+
+
+def sparse_attn_rows_at(Q_rows, K, V, positions, sel, nsel, r: int = 4):
+    """Attention of compact query rows over a given selection: Q_rows [n,H,D]
+    (post-RoPE) are the queries at absolute positions positions[i], with
+    selection row sel[i] / nsel[i]."""
+    Q_rows, K, V = (_c(a, np.uint16) for a in (Q_rows, K, V))
+    positions = _c(positions, np.int64)
+    sel = _c(sel, np.int32)
+    nsel = _c(nsel, np.int32)
+    n = positions.size
+    _, H, D = Q_rows.shape
+    if Q_rows.shape[0] < n:
+        raise ValueError("sparse_attn_rows_at: fewer query rows than positions")
+    _check_rows("sparse_attn_rows_at", None, n, positions, K.shape[0], sel, nsel, r)
+    O = np.empty((n, H, D))
+    lse = np.empty((n, H))
+    _load().qsa_oracle_sparse_attn_rows_at(_p(Q_rows), _p(K), _p(V), _p(positions), H, K.shape[1],
+                                           D, r, sel.shape[1], n, _p(sel), _p(nsel), _p(O),
+                                           _p(lse))
     return O, lse
 
 

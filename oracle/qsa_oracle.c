@@ -392,6 +392,25 @@ void qsa_oracle_sparse_attn_rows(const uint16_t *Q, const uint16_t *K, const uin
     }
 }
 
+/* Same as qsa_oracle_sparse_attn_rows for compact inputs: row i of Q
+ * [n][H][D] is the query at absolute position pos[i], with selection row i. */
+void qsa_oracle_sparse_attn_rows_at(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                                    const int64_t *pos, int H, int Hkv, int D, int r,
+                                    int Kbudget, int64_t n, const int32_t *sel,
+                                    const int32_t *nsel, double *O, double *lse) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t p_i = pos[i];
+        const int ns_i = nsel[i];
+        int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)(ns_i * r + r));
+        const int64_t ntok = qsa_oracle_token_set(sel + i * Kbudget, ns_i, p_i, r, tok);
+        double e;
+        qsa_oracle_attend_row(Q + i * H * (int64_t)D, K, V, H, Hkv, D, tok, ntok,
+                              O + i * H * (int64_t)D, lse + i * H, &e);
+        free(tok);
+    }
+}
+
 /* Scores + selection only, for a list of rows: s_out [n][nb_out] (NAN past
  * nc), sel/nsel/sK/sK1 as in qsa_oracle_qsa_rows.  s_out may be NULL. */
 void qsa_oracle_select_rows(const uint16_t *qi, const uint16_t *kbar, int64_t nb, int64_t pos0,

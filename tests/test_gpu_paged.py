@@ -1,13 +1,16 @@
 """Paged KV and pooled-key caches: the same workload laid out in randomly
 permuted pages of a pool (page table per sequence) must give bit for bit the
-results of the contiguous layout, whose parity with the oracle the other
-tests establish.  Pages no sequence owns are filled with NaN, so a read of
-a page the table does not hand out would show in the outputs."""
+results of the contiguous layout, and the paged results are checked against
+the fp64 oracle on the contiguous arrays (selection by the tie-band rule,
+attention over the GPU's selection, dense attention).  Pages no sequence
+owns are filled with NaN, so a read of a page the table does not hand out
+would show in the outputs."""
 import numpy as np
 import pytest
 
+import oracle
 import synth
-from gpu_helpers import dev, host_u16
+from gpu_helpers import assert_close, check_prefill_rows, check_selection, dev, host_u16, log
 
 pytestmark = pytest.mark.gpu
 
@@ -106,6 +109,40 @@ def test_paged_decode_equals_contiguous(qsa, P, n, budget, idx_rope):
     for name, a, b in zip(("blk_idx", "n_sel", "O", "lse", "dense O"), *outs):
         assert np.array_equal(a, b, equal_nan=False), name
     assert np.all(np.isfinite(outs[1][2])) and np.all(np.isfinite(outs[1][4]))
+    # the paged results against the oracle: the selection made for the first
+    # of each sequence's n queries (indexer RoPE at its position when on), each
+    # query over the shared selection plus its own causal tail, dense attention
+    blk, nsel, O, lse, Od = outs[1]
+    O, lse = O.reshape(B, n, 24, 256), lse.reshape(B, n, 24)   # next_n = 1 returns [B, H, ...]
+    Og, lg, Or, lr, Odg, Odr = [], [], [], [], [], []
+    exempt = 0
+    for b in range(B):
+        L = int(lens[b])
+        p0 = L - n
+        kb = oracle.compress(ki[b, :L], rope_dim=idx_rope)
+        q0 = qi[b, :1]
+        if idx_rope:
+            q0 = oracle.rope(q0, rope_dim=idx_rope, pos=np.array([p0]))
+        ref = oracle.select_rows(q0, kb, np.array([0]), pos0=p0, Kbudget=budget,
+                                 want_scores=True)
+        exempt += int(check_selection(ref["s"][0], budget, ref["sK"][0], ref["sK1"][0], blk[b],
+                                      nsel[b], strict=ref["sel"][0, :ref["nsel"][0]]))
+        Qr = oracle.rope(q[b], pos=p0 + np.arange(n))
+        sel_b = blk[b, :nsel[b]]
+        for i in range(n):
+            o, l, _ = oracle.attend_row(Qr[i], Kc[b], Vc[b], oracle.token_set_reuse(sel_b, p0,
+                                                                                     p0 + i))
+            Og.append(O[b, i])
+            lg.append(lse[b, i])
+            Or.append(o)
+            lr.append(l)
+        od, _ = oracle.dense_rows(Qr, Kc[b], Vc[b], np.arange(n), pos0=p0)
+        Odg.append(Od[b])
+        Odr.append(od)
+    log(f"  paged decode P={P} next_n={n}: {exempt} of {B} selections differ inside the tie band")
+    assert_close(np.stack(Og), np.stack(Or), "paged decode O vs oracle on the GPU selection")
+    assert_close(np.stack(lg), np.stack(lr), "paged decode lse vs oracle")
+    assert_close(np.concatenate(Odg), np.concatenate(Odr), "paged dense decode O vs oracle")
 
 
 @pytest.mark.parametrize("P", [16, 128])
@@ -142,6 +179,15 @@ def test_paged_prefill_chunk_equals_contiguous(qsa, P):
         del layer, kc, vc, kbar
     for name, a, b in zip(("blk_idx", "n_sel", "O", "lse", "dense O"), *outs):
         assert np.array_equal(a, b), name
+    # every row of the paged chunk against the oracle on the contiguous arrays
+    blk, nsel, O, lse, Od = outs[1]
+    kb = oracle.compress(x.ki)
+    check_prefill_rows(O, lse, blk, nsel, x.Q, x.K, x.V, x.qi, kb, np.arange(Tq), pos0, K)
+    rows = np.array([0, 1, 2, 3, 517, Tq - 2, Tq - 1])
+    Qr = oracle.rope(x.Q[rows], pos=pos0 + rows)
+    Odr = np.stack([oracle.dense_rows(Qr[i:i + 1], x.K, x.V, np.array([0]),
+                                      pos0=pos0 + int(t))[0][0] for i, t in enumerate(rows)])
+    assert_close(Od[0, rows], Odr, f"paged dense prefill O vs oracle (P={P})")
 
 
 def test_paged_compress_and_scores(qsa):

@@ -101,6 +101,16 @@ MUTATIONS = {
     "dense_rows_position_by_index": (
         "int64_t p = pos0 + t;\n        int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)(p + 1));",
         "int64_t p = pos0 + i;\n        int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)(p + 1));"),
+    "sparse_attn_rows_at_position_of_row_zero": ("const int64_t p_i = pos[i];",
+                                                 "const int64_t p_i = pos[0];"),
+    "sparse_attn_rows_at_query_row_zero": (
+        "qsa_oracle_attend_row(Q + i * H * (int64_t)D, K, V, H, Hkv, D, tok, ntok,\n"
+        "                              O + i * H * (int64_t)D, lse + i * H, &e);",
+        "qsa_oracle_attend_row(Q, K, V, H, Hkv, D, tok, ntok,\n"
+        "                              O + i * H * (int64_t)D, lse + i * H, &e);"),
+    "sparse_attn_rows_at_selection_row_zero": (
+        "qsa_oracle_token_set(sel + i * Kbudget, ns_i, p_i, r, tok);",
+        "qsa_oracle_token_set(sel, ns_i, p_i, r, tok);"),
     # bf16 narrowing below the normal range
     "bf16_subnormal_quantum": ("if (e < -125) e = -125;", "if (e < -126) e = -126;"),
     "bf16_subnormal_unclamped": ("if (e < -125) e = -125;", "if (e < -1075) e = -1075;"),

@@ -840,6 +840,16 @@ def test_row_drivers_sparse_attn_rows_planted(oracle_lib):
                 _check_uniform(O[i], lse[i], S, (qkey, t))
             else:
                 _check_target(O[i], lse[i], x["targets"][t], (qkey, t))
+        # the compact form: row i is the query at position pos0 + rows[i]
+        Oc, lc = oracle_lib.sparse_attn_rows_at(x[qkey][rows], x["K"], x["V"], _DRV_POS0 + rows,
+                                                sel, nsel)
+        for i, t in enumerate(rows):
+            t = int(t)
+            S = _token_set_expected(x["sel"][t], _DRV_POS0 + t)
+            if qkey == "Q0":
+                _check_uniform(Oc[i], lc[i], S, ("at", qkey, t))
+            else:
+                _check_target(Oc[i], lc[i], x["targets"][t], ("at", qkey, t))
     # an empty selection leaves the trailing block alone
     O, lse = oracle_lib.sparse_attn_rows(x["Q0"], x["K"], x["V"], rows, sel,
                                          np.zeros(rows.size, dtype=np.int32), pos0=_DRV_POS0)
