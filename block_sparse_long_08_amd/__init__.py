@@ -56,6 +56,9 @@ _sig("qsa_sparse_attn_prefill", _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
 _sig("qsa_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32, _i32)
 _sig("qsa_sparse_attn_decode", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32,
      _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp, _vp)
+_sig("qsa_decode_noalloc_max_bytes", _sz)
+_sig("qsa_sparse_attn_decode_noalloc", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32,
+     _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp)
 _sig("dense_attn_workspace_bytes", _sz, _i32, _i64, _i64, _i32, _i32, _i32)
 _sig("dense_attn", _i32, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _i32, _i32, _vp, _vp,
      _vp, _sz, _vp, _vp)
@@ -69,6 +72,7 @@ EXPORTED = ["qsa_status_string", "qsa_version", "qsa_check_device", "qsa_rope_bf
             "qsa_compress_keys", "qsa_index_scores", "qsa_topk_workspace_bytes",
             "qsa_topk_blocks", "qsa_select_workspace_bytes", "qsa_select_blocks",
             "qsa_sparse_attn_prefill", "qsa_decode_workspace_bytes", "qsa_sparse_attn_decode",
+            "qsa_decode_noalloc_max_bytes", "qsa_sparse_attn_decode_noalloc",
             "dense_attn_workspace_bytes", "dense_attn", "qsa_distill_workspace_bytes",
             "qsa_distill_kl", "qsa_sparse_attn_prefill_kl"]
 
@@ -194,6 +198,18 @@ def qsa_sparse_attn_decode(q, Kc, Vc, seq_len, blk_idx, n_sel, B: int, Tq: int, 
     _call("qsa_sparse_attn_decode", _ptr(q), _ptr(Kc), _ptr(Vc), _ptr(seq_len), _ptr(blk_idx),
           _ptr(n_sel), B, Tq, Lmax, H, Hkv, D, r, Kbudget, _ptr(O), _ptr(lse), _ptr(ws),
           ws_bytes, _pages(pages), _stream(stream))
+
+
+def qsa_decode_noalloc_max_bytes() -> int:
+    return int(_lib.qsa_decode_noalloc_max_bytes())
+
+
+def qsa_sparse_attn_decode_noalloc(q, Kc, Vc, seq_len, blk_idx, n_sel, B: int, Tq: int,
+                                   Lmax: int, H: int, Hkv: int, D: int, r: int, Kbudget: int, O,
+                                   lse=None, stream=None, pages=None) -> None:
+    _call("qsa_sparse_attn_decode_noalloc", _ptr(q), _ptr(Kc), _ptr(Vc), _ptr(seq_len),
+          _ptr(blk_idx), _ptr(n_sel), B, Tq, Lmax, H, Hkv, D, r, Kbudget, _ptr(O), _ptr(lse),
+          _pages(pages), _stream(stream))
 
 
 def dense_attn_workspace_bytes(B: int, Tq: int, Lmax: int, H: int, Hkv: int, D: int) -> int:

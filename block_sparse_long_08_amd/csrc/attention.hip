@@ -25,6 +25,8 @@
 // S^T row 4*e + i is entry e (0..3) token i, so a lane's accumulator holds one
 // whole block for one head: exactly the k-slots (tokens 4*g4 .. 4*g4+3) it
 // supplies as the B operand P^T of the 16x16x16 PV product.
+#include <mutex>
+
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -780,6 +782,37 @@ static void launch_decode_variant(const AttnArgs &a, dim3 grid, int nsplit, int 
         else
             launch_decode_paging<false, false>(a, grid, nsplit, sps, nct, paged, s);
     }
+}
+
+// Scratch of the no-allocation decode entry point: the split records of one
+// call, in a file-scope device array (each GPU the library runs on holds its
+// own copy until the process ends).  Host code never passes the array's
+// name to a kernel: its device address comes from hipGetSymbolAddress, once
+// per device, with that device current.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t decode_scratch(size_t need, float **ptr) {
+    *ptr = nullptr;
+    if (need > kDecodeScratchBytes) return hipErrorInvalidValue;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        scratch_ptr[dev] = p;
+    }
+    *ptr = static_cast<float *>(scratch_ptr[dev]);
+    return hipSuccess;
 }
 
 hipError_t launch_attn_decode(const AttnArgs &a, int nsplit, hipStream_t s) {

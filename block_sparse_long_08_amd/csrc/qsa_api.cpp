@@ -90,6 +90,8 @@ const char *qsa_status_string(int status) {
     case QSA_ERR_WORKSPACE: return "QSA_ERR_WORKSPACE: workspace missing or too small";
     case QSA_ERR_LAUNCH: return "QSA_ERR_LAUNCH: the HIP runtime rejected a launch";
     case QSA_ERR_DEVICE: return "QSA_ERR_DEVICE: current device is not a gfx950 GPU";
+    case QSA_ERR_SCRATCH:
+        return "QSA_ERR_SCRATCH: the call needs more than the library's static scratch holds";
     default: return "unknown qsa_status";
     }
 }
@@ -374,6 +376,37 @@ int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16
     a.Tq = Tq; a.Lmax = Lmax; a.pos0 = 0; a.B = B; a.H = H; a.Hkv = Hkv; a.Kbudget = Kbudget;
     st = check_pages(pages, Lmax);
     if (st != QSA_OK) return st;
+    const PageTable pt = token_pages(pages);
+    a.ptable = pt.table; a.pstride = pt.stride; a.pshift = pt.shift;
+    return launch_status(launch_attn_decode(a, nsplit, as_stream(stream)));
+}
+
+size_t qsa_decode_noalloc_max_bytes(void) { return kDecodeScratchBytes; }
+
+int qsa_sparse_attn_decode_noalloc(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16 *Vc,
+                                   const int64_t *seq_len, const int32_t *blk_idx,
+                                   const int32_t *n_sel, int B, int Tq, int64_t Lmax, int H,
+                                   int Hkv, int D, int r, int Kbudget, float *O, float *lse,
+                                   const qsa_pages *pages, void *stream) {
+    if (!q || !Kc || !Vc || !seq_len || !blk_idx || !n_sel || !O) return QSA_ERR_NULL;
+    if (B <= 0 || Lmax < 0 || Kbudget <= 0) return QSA_ERR_SHAPE;
+    if (Tq < 1 || Tq > kMaxNextN) return QSA_ERR_SHAPE;
+    int st = check_attn_shape(H, Hkv, D, r);
+    if (st != QSA_OK) return st;
+    if (Kbudget > kMaxBudget) return QSA_ERR_UNSUPPORTED;
+    if (B > 65535 || Lmax / kBlock > kI32Max) return QSA_ERR_OVERFLOW;
+    if (!aligned16(q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(O)) return QSA_ERR_ALIGN;
+    st = check_pages(pages, Lmax);
+    if (st != QSA_OK) return st;
+    int nsplit = 0;
+    const size_t need = decode_ws(B, Tq, H, Hkv, Kbudget, &nsplit);
+    if (need > kDecodeScratchBytes) return QSA_ERR_SCRATCH;
+    float *part = nullptr;
+    if (decode_scratch(need, &part) != hipSuccess) return QSA_ERR_LAUNCH;
+    AttnArgs a{};
+    a.Q = q; a.K = Kc; a.V = Vc; a.blk_idx = blk_idx; a.n_sel = n_sel; a.seq_len = seq_len;
+    a.O = O; a.lse = lse; a.part = part;
+    a.Tq = Tq; a.Lmax = Lmax; a.pos0 = 0; a.B = B; a.H = H; a.Hkv = Hkv; a.Kbudget = Kbudget;
     const PageTable pt = token_pages(pages);
     a.ptable = pt.table; a.pstride = pt.stride; a.pshift = pt.shift;
     return launch_status(launch_attn_decode(a, nsplit, as_stream(stream)));

@@ -200,6 +200,12 @@ int64_t decode_max_entries(int Tq, int64_t Kbudget_or_blocks);
 size_t decode_partial_floats(int B, int Hkv, int nsplit);
 int decode_num_splits(int B, int Hkv, int64_t max_entries);
 hipError_t launch_attn_decode(const AttnArgs &a, int nsplit, hipStream_t s);
+// The no-allocation decode: its split records live in a static device array
+// of kDecodeScratchBytes per GPU.  decode_scratch gives the array's address
+// on the current device (looked up once per device), or an error when need
+// exceeds the array.
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+hipError_t decode_scratch(size_t need, float **ptr);
 hipError_t launch_dense_prefill(const AttnArgs &a, hipStream_t s);
 
 // Stage-1 distillation KL of a chunk of rows (see distill.hip): Q [rows][24][256]

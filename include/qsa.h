@@ -66,7 +66,8 @@ typedef enum {
     QSA_ERR_OVERFLOW = 5,    /* a block index would not fit in int32 */
     QSA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
     QSA_ERR_LAUNCH = 7,      /* the HIP runtime rejected a launch */
-    QSA_ERR_DEVICE = 8       /* the current device is not a gfx950 GPU */
+    QSA_ERR_DEVICE = 8,      /* the current device is not a gfx950 GPU */
+    QSA_ERR_SCRATCH = 9      /* the call needs more than the static scratch holds */
 } qsa_status;
 
 /* Indexer head combination.
@@ -226,6 +227,28 @@ int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16
                            int B, int Tq, int64_t Lmax, int H, int Hkv, int D, int r,
                            int Kbudget, float *O, float *lse, void *ws, size_t ws_bytes,
                            const qsa_pages *pages, void *stream);
+
+/* ---- A7 without allocation: qsa_sparse_attn_decode for callers that cannot
+ * allocate device memory or hand over a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * arguments and results are those of qsa_sparse_attn_decode without ws and
+ * ws_bytes; the same kernels run, and the split records live instead in a
+ * static device array of qsa_decode_noalloc_max_bytes() bytes (64 MiB) that
+ * each GPU the library runs on holds until the process ends.  The call
+ * allocates nothing.  A call whose records need more than that array
+ * (qsa_decode_workspace_bytes > 64 MiB, e.g. more than about 1,900 sequences
+ * at Tq = 1) returns QSA_ERR_SCRATCH and enqueues nothing.
+ * Every call on one GPU shares that GPU's array, whatever its stream: calls
+ * whose work overlaps on one GPU (on different streams, or from several host
+ * threads) race on it and give undefined results; order them on one stream
+ * or with events.  Each call writes every record it later reads, so no
+ * contents carry over from an earlier call. */
+size_t qsa_decode_noalloc_max_bytes(void);
+int qsa_sparse_attn_decode_noalloc(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16 *Vc,
+                                   const int64_t *seq_len, const int32_t *blk_idx,
+                                   const int32_t *n_sel, int B, int Tq, int64_t Lmax, int H,
+                                   int Hkv, int D, int r, int Kbudget, float *O, float *lse,
+                                   const qsa_pages *pages, void *stream);
 
 /* ---- A8: dense causal attention (the pages' baseline in the chlience
  * Result 2 kernel measurement).

@@ -55,7 +55,7 @@ def test_binding_names_match_header():
 
 def test_status_strings(lib):
     lib.qsa_status_string.restype = ctypes.c_char_p
-    for st in range(9):
+    for st in range(10):
         s = lib.qsa_status_string(st).decode()
         assert s.startswith("QSA_")
     assert lib.qsa_version() >= 100
@@ -330,3 +330,33 @@ def test_sparse_attn_prefill_kl_validation(lib):
     assert attn_kl(lib, O=MIS) == ALIGN
     assert attn_kl(lib, Tq=0) == OK                      # nothing to do, nothing enqueued
     assert attn_kl(lib, Tq=0, lse=0) == OK               # lse is optional
+
+
+def noalloc(lib, q=P, Kc=P, Vc=P, sl=P, blk=P, ns=P, B=2, Tq=1, Lmax=64, H=24, Hkv=2, D=256,
+            r=4, K=8, O=P, lse=P, pages=None):
+    return lib.qsa_sparse_attn_decode_noalloc(vp(q), vp(Kc), vp(Vc), vp(sl), vp(blk), vp(ns), B,
+                                              Tq, I64(Lmax), H, Hkv, D, r, K, vp(O), vp(lse),
+                                              pages, None)
+
+
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode checks its arguments like the workspace form,
+    and rejects a call whose split records exceed its static scratch
+    (QSA_ERR_SCRATCH) before any HIP call."""
+    lib.qsa_decode_noalloc_max_bytes.restype = ctypes.c_size_t
+    lib.qsa_decode_workspace_bytes.restype = ctypes.c_size_t
+    assert lib.qsa_decode_noalloc_max_bytes() == 64 << 20
+    assert noalloc(lib, q=0) == NULL
+    assert noalloc(lib, O=0) == NULL
+    assert noalloc(lib, sl=0) == NULL
+    assert noalloc(lib, B=0) == SHAPE
+    assert noalloc(lib, Tq=0) == SHAPE and noalloc(lib, Tq=17) == SHAPE
+    assert noalloc(lib, K=0) == SHAPE and noalloc(lib, K=4096) == UNSUP
+    assert noalloc(lib, H=25) == SHAPE and noalloc(lib, D=128) == UNSUP
+    assert noalloc(lib, q=MIS) == ALIGN
+    SCRATCH = 9
+    # 4,000 sequences: one split each, 8,000 records of 16.9 KB > 64 MiB
+    big = lib.qsa_decode_workspace_bytes(4000, 1, 24, 2, 256, 512)
+    assert big > lib.qsa_decode_noalloc_max_bytes()
+    assert noalloc(lib, B=4000, K=512) == SCRATCH
+    assert noalloc(lib, B=70000, K=512) == OVERFLOW
