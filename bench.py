@@ -165,7 +165,7 @@ def gather_ceiling(layer, Kr, V, reps):
 
 
 def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, page_tokens=0,
-                  with_distill=False, pipeline_rows=None, with_probe=False):
+                  with_distill=False, pipeline_rows=0, with_probe=False, attn_rows=None):
     import torch
     import block_sparse_long_08_amd as qsa
     Tq, pos0, budget, nd = WORKLOADS[name]
@@ -190,8 +190,9 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
         kbar = torch.empty((Tk // 4, 128), dtype=torch.bfloat16, device="cuda")
         qsa.qsa_compress_keys(ki, 1, pos0, pos0 * 128, 128, 4, 0, kbar, (pos0 // 4) * 128,
                               rope_dim=idx_rope_dim)
+    extra = {} if attn_rows is None else dict(attn_rows=attn_rows)
     layer = qsa.QSAPrefill(Tq, pos0=pos0, budget=budget, fresh=fresh, idx_rope_dim=idx_rope_dim,
-                           pages=pages, pipeline_rows=pipeline_rows)
+                           pages=pages, pipeline_rows=pipeline_rows, **extra)
     torch.cuda.synchronize()
     # the layer's product path: selection and attention overlapped on two
     # streams in row chunks (pipeline_rows), else one after the other
@@ -228,7 +229,7 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     stage = timer.per_stage_ms()
-    nlaunch = 1
+    nlaunch = len(layer.attn_chunks())
     if pipe:
         # stage durations from events around each chunk's selection (launch
         # stream) and each attention launch (its own stream); the two overlap,
@@ -248,7 +249,8 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
     stage["attend_standalone"] = _time_steps(lambda: layer.attend_chunks(Kr0, V), reps)
     probe_ms = gather_ceiling(layer, Kr0, V, reps) if with_probe else None
     res = dict(ms_per_step=wall * 1e3, stages_ms=stage, Tq=Tq, Tk=Tk, budget=budget,
-               attn_launches=nlaunch, pipeline_rows=layer.pipeline_rows)
+               attn_launches=nlaunch, pipeline_rows=layer.pipeline_rows,
+               attn_rows=layer.attn_rows)
     res["attend_launch_ms"] = (att_ms if pipe else stage["attend"]) / nlaunch
     if probe_ms is not None:
         res["gather_probe_ms"] = probe_ms
@@ -580,10 +582,12 @@ def main():
     ap.add_argument("--distill", default="on", choices=["on", "off"],
                     help="also time the stage-1 distillation KL on the prefill workload "
                          "(needs the dense baseline's log-sum-exp)")
-    ap.add_argument("--pipeline-rows", type=int, default=None,
+    ap.add_argument("--pipeline-rows", type=int, default=0,
                     help="rows per selection chunk whose attention overlaps the next chunk's "
-                         "selection; 0 runs the selection of all rows, then the attention; "
-                         "default: the layer's own choice")
+                         "selection on a second stream; 0 (default): the selection of all "
+                         "rows, then the attention")
+    ap.add_argument("--attn-rows", type=int, default=None,
+                    help="rows per sparse-attention launch (default: the layer's)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (scale of the HBM byte counters)")
     args = ap.parse_args()
@@ -600,7 +604,7 @@ def main():
         calibration_copy()
     pre, x = bench_prefill(args.workload, args.steps, args.warmup, with_dense=args.dense == "all",
                            with_distill=args.distill == "on", pipeline_rows=args.pipeline_rows,
-                           with_probe=True)
+                           with_probe=True, attn_rows=args.attn_rows)
     log(f"prefill {args.workload}: {pre['ms_per_step']:.2f} ms/step, stages {pre['stages_ms']}")
     st = pre["stages_ms"]
     # the dominant kernel of the step is the sparse attention (attn_launches
@@ -651,7 +655,7 @@ def main():
         "config": {"workload": args.workload, "Tq": pre["Tq"], "context": pre["Tk"],
                    "budget_blocks": pre["budget"], "block": 4, "heads": "24q/2kv x 256",
                    "indexer": "4q/1k x 128", "score_mode": "maxhead", "kbar_mode": "mean",
-                   "pipeline_rows": pre["pipeline_rows"]},
+                   "pipeline_rows": pre["pipeline_rows"], "attn_rows": pre["attn_rows"]},
         "stages_ms": pre["stages_ms"],
         "roofline": roof,
     }
@@ -701,7 +705,8 @@ def main():
         # the same metric at 1M context: prefill chunk and decode (own inputs)
         del x
         m_pre, _ = bench_prefill("prefill_1m_chunk", min(args.steps, 3), 1,
-                                 with_dense=args.dense == "all", pipeline_rows=args.pipeline_rows)
+                                 with_dense=args.dense == "all", pipeline_rows=args.pipeline_rows,
+                                 attn_rows=args.attn_rows)
         m = dict(workload="prefill_1m_chunk", ms_per_step=m_pre["ms_per_step"],
                  tokens_per_s=m_pre["Tq"] / (m_pre["ms_per_step"] * 1e-3),
                  stages_ms=m_pre["stages_ms"],
@@ -718,7 +723,7 @@ def main():
         # the report's prefill condition: a 16K-token chunk over a paged cache
         c_pre, _ = bench_prefill("prefill_1m_chunk16k", min(args.steps, 3), 1,
                                  with_dense=args.dense == "all", page_tokens=64,
-                                 pipeline_rows=args.pipeline_rows)
+                                 pipeline_rows=args.pipeline_rows, attn_rows=args.attn_rows)
         c = dict(workload="prefill_1m_chunk16k", page_tokens=64, ms_per_step=c_pre["ms_per_step"],
                  tokens_per_s=c_pre["Tq"] / (c_pre["ms_per_step"] * 1e-3),
                  stages_ms=c_pre["stages_ms"])

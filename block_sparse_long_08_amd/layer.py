@@ -18,9 +18,8 @@ from . import (DI, HI, R, SCORE_MAXHEAD, KBAR_MEAN, qsa_compress_keys, qsa_decod
                qsa_sparse_attn_decode, qsa_sparse_attn_prefill, qsa_sparse_attn_prefill_kl)
 
 
-# rows per selection chunk of the prefill pipeline (measured fastest at 128K
-# and 1M against 1,024 to 6,144)
-PIPELINE_ROWS = 4096
+# rows per sparse-attention launch of the prefill
+ATTN_ROWS = 4096
 
 
 class QSAPrefill:
@@ -35,25 +34,24 @@ class QSAPrefill:
     block's first token, indexer queries at their own positions); kbar_gain:
     the RMSNorm gain of the pooled keys (kbar_mode RMSNORM), bf16 [DI].
 
-    pipeline_rows > 0 (and < Tq): the queries are selected in chunks of that
-    many rows, and each chunk's sparse attention runs on a second stream
-    while the next chunk is selected (selection is MFMA and ALU work, the
-    attention streams gathers from HBM, so the two overlap); the results are
-    those of the stages run one after the other.  pipeline_rows = 0: one
-    stage after the other.  None (default): chunks of 4,096 rows when there
-    are at least 8 of them, else no pipeline.  With fewer chunks the first
-    selection and the last attention are exposed and the two stages contend
-    for the same CUs (measured: a 1M-context chunk of 8,192 rows takes
-    7.99 ms in turn against 8.40 ms overlapped in 4,096-row chunks; 16,384
-    rows 15.8 against 17.5 ms; 131,072 rows 60.6 ms overlapped against
-    69.7 ms in turn).
+    The selection of all rows runs first (one call; the library scores the
+    rows in chunks of at most 4 GiB of scores), then the sparse attention in
+    launches of attn_rows rows (default 4,096: the 128K prefill's launches
+    take 48.7 ms in all against 62.5 ms as one launch of 131,072 rows).
+    pipeline_rows > 0 (and < Tq) instead selects the queries in chunks of
+    that many rows and runs each chunk's attention on a second stream while
+    the next chunk is selected; the results are those of the stages run one
+    after the other.  It is off by default: the selection's score traffic
+    slows the attention more than the overlap saves (128K: 60.8 ms
+    overlapped in 4,096-row chunks against 0.7 + 6.5 + 48.7 ms in turn; a
+    1M-context chunk of 8,192 rows 8.40 against 7.9 ms).
     """
 
     def __init__(self, Tq: int, pos0: int = 0, H: int = 24, Hkv: int = 2, D: int = 256,
                  budget: int = 512, score_mode: int = SCORE_MAXHEAD, kbar_mode: int = KBAR_MEAN,
                  theta: float = 1e7, rope_dim: int = 64, fresh: bool = True,
-                 idx_rope_dim: int = 0, kbar_gain=None, pages=None, pipeline_rows=None,
-                 device="cuda"):
+                 idx_rope_dim: int = 0, kbar_gain=None, pages=None, pipeline_rows: int = 0,
+                 attn_rows: int = ATTN_ROWS, device="cuda"):
         self.Tq, self.pos0, self.H, self.Hkv, self.D = Tq, pos0, H, Hkv, D
         self.pages = pages  # paged caches (fresh=False): K, V and kbar are page pools
         self.Tk = pos0 + Tq
@@ -72,9 +70,8 @@ class QSAPrefill:
         self.n_sel = torch.empty((Tq,), dtype=torch.int32, device=dev)
         self.O = torch.empty((Tq, H, D), dtype=torch.float32, device=dev)
         self.lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
-        if pipeline_rows is None:
-            pipeline_rows = PIPELINE_ROWS if Tq >= 8 * PIPELINE_ROWS else 0
         self.pipeline_rows = pipeline_rows if 0 < pipeline_rows < Tq else 0
+        self.attn_rows = self.pipeline_rows or (attn_rows if attn_rows > 0 else Tq)
         self.ws_bytes = qsa_select_workspace_bytes(1, self.pipeline_rows or Tq, self.nb, budget)
         self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=dev)
         # the attention stream of the pipeline (default priority)
@@ -105,9 +102,13 @@ class QSAPrefill:
         qsa_rope_bf16(qi, self.qir, self.Tq, HI, DI, self.idx_rope_dim, self.theta, self.pos0)
         return self.qir
 
-    def _chunks(self):
-        c = self.pipeline_rows or self.Tq
+    def _chunks(self, rows=None):
+        c = rows or self.pipeline_rows or self.Tq
         return [(r0, min(c, self.Tq - r0)) for r0 in range(0, self.Tq, c)]
+
+    def attn_chunks(self):
+        """(first row, rows) of each sparse-attention launch."""
+        return self._chunks(self.attn_rows)
 
     def _select_rows(self, qi, kbar, r0, n):
         qsa_select_blocks(qi[r0:r0 + n], kbar, 1, n, self.pos0 + r0, None, self.nb, HI, DI, R,
@@ -129,7 +130,7 @@ class QSAPrefill:
         pipelined attention."""
         if self.pages is not None:
             raise ValueError("attend_with_kl: the fused KL runs on contiguous caches only")
-        for r0, n in self._chunks():
+        for r0, n in self.attn_chunks():
             p0 = self.pos0 + r0
             qsa_sparse_attn_prefill_kl(self.Qr[r0:r0 + n], Kr, V, qi[r0:r0 + n], kbar,
                                        self.blk_idx[r0:r0 + n], self.n_sel[r0:r0 + n], n, p0 + n,
@@ -142,13 +143,13 @@ class QSAPrefill:
             self._select_rows(qi, kbar, r0, n)
 
     def attend_chunks(self, Kr, V):
-        """The sparse attention of every row chunk, one after the other on the
-        current stream (the launches of the pipelined form, not overlapped)."""
-        for r0, n in self._chunks():
+        """The sparse attention of every row, in its launches one after the
+        other on the current stream."""
+        for r0, n in self.attn_chunks():
             self._attend_rows(Kr, V, r0, n)
 
     def attend(self, Kr, V):
-        self._attend_rows(Kr, V, 0, self.Tq)
+        self.attend_chunks(Kr, V)
 
     def select_and_attend(self, qi, kbar, Kr, V, attn_events=None, select_events=None):
         """Selection and sparse attention of every row; with pipeline_rows,
