@@ -603,6 +603,12 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit
     const int g = blockIdx.y;
     const int64_t b = blockIdx.z;
     const int nq = static_cast<int>(a.Tq);
+    // the split's first list entries do not depend on the lengths: they are
+    // requested together with the length and the selection count
+    const int e_lo = split * sps * kStageEntries;
+    int32_t pre = 0;
+    if (!DENSE && e_lo + static_cast<int>(threadIdx.x) < a.Kbudget)
+        pre = a.blk_idx[b * a.Kbudget + e_lo + threadIdx.x];
     int64_t Lb = a.seq_len[b];
     Lb = Lb < 0 ? 0 : (Lb > a.Lmax ? a.Lmax : Lb);
     const int64_t p_last = Lb - 1;
@@ -620,7 +626,6 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit
     const int E = ns + (tail + 3) / 4;
     const int nstages = (E + kStageEntries - 1) / kStageEntries;
     const int s0 = split * sps, s1 = min(s0 + sps, nstages);
-    const int e_lo = s0 * kStageEntries;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int group = a.H / a.Hkv;
     // the query rows are read while the block list arrives
@@ -632,7 +637,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit
         const int e_hi = min(s1 * kStageEntries, PAGED ? E : ns);
         const int32_t *src = a.blk_idx + b * a.Kbudget;
         for (int i = e_lo + static_cast<int>(threadIdx.x); i < e_hi; i += 256) {
-            int64_t bi = i < ns ? src[i] : nc + (i - ns);
+            int64_t bi = i < ns ? (i < e_lo + 256 ? pre : src[i]) : nc + (i - ns);
             if (i < ns) bi = bi < 0 ? 0 : (bi >= nc ? nc - 1 : bi);
             lst[i - e_lo] =
                 static_cast<int32_t>(PAGED ? page_row(ptab, a.pshift, 4 * bi) >> 2 : bi);

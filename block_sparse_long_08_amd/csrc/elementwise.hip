@@ -30,7 +30,11 @@ struct InvFreq {
 };
 
 // One workgroup per row t: angles for the row's position are formed once in
-// LDS, then every head's pairs are rotated.
+// LDS, then every head's pairs are rotated.  The row's values do not depend
+// on its position, so they are requested first (and the untouched dims
+// copied) while the position and the angles are formed.
+constexpr int kRopePairsPerThread = 4;  // pairs a thread keeps in registers
+
 __global__ void __launch_bounds__(256) rope_kernel(const uint16_t *__restrict__ x,
                                                    uint16_t *__restrict__ y, int64_t T,
                                                    int nheads, int head_dim, int rope_dim,
@@ -40,31 +44,19 @@ __global__ void __launch_bounds__(256) rope_kernel(const uint16_t *__restrict__ 
     __shared__ double cs[64], sn[64];
     const int64_t t = blockIdx.x;
     const int half = rope_dim / 2;
-    // decode form: row t is query t % nq of sequence t / nq, the nq newest
-    // positions of that sequence
-    int64_t p = seq_len ? seq_len[t / nq] - nq + t % nq : pos0 + t;
-    if (p < 0) p = 0;
-    for (int j = threadIdx.x; j < half; j += blockDim.x) {
-        double ang = static_cast<double>(p) * inv_freq.v[j];
-        double s, c;
-        sincos(ang, &s, &c);
-        cs[j] = c;
-        sn[j] = s;
-    }
-    block_sync();
     const uint16_t *xr = x + t * nheads * static_cast<int64_t>(head_dim);
     uint16_t *yr = y + t * nheads * static_cast<int64_t>(head_dim);
-    for (int idx = threadIdx.x; idx < nheads * half; idx += blockDim.x) {
-        int h = idx / half, j = idx - h * half;
+    const int npairs = nheads * half;
+    // the first pairs of this thread, loaded before the position is known
+    uint16_t pa[kRopePairsPerThread], pb[kRopePairsPerThread];
+#pragma unroll
+    for (int u = 0; u < kRopePairsPerThread; ++u) {
+        const int idx = threadIdx.x + u * blockDim.x;
+        const int ii = idx < npairs ? idx : 0;  // an existing pair for idle threads
+        const int h = ii / half, j = ii - h * half;
         const uint16_t *xh = xr + h * head_dim;
-        double a = static_cast<double>(bf16_bits_to_f32(xh[j]));
-        double b = static_cast<double>(bf16_bits_to_f32(xh[j + half]));
-        double c = cs[j], s = sn[j];
-        double ac = a * c, bs = b * s, bc = b * c, as = a * s;
-        uint16_t o0 = f64_to_bf16_rne(ac - bs);
-        uint16_t o1 = f64_to_bf16_rne(bc + as);
-        yr[h * head_dim + j] = o0;
-        yr[h * head_dim + j + half] = o1;
+        pa[u] = xh[j];
+        pb[u] = xh[j + half];
     }
     if (y != x) {
         // copy the untouched dims, 16 bytes at a time (rope_dim % 8 == 0 and
@@ -77,6 +69,33 @@ __global__ void __launch_bounds__(256) rope_kernel(const uint16_t *__restrict__ 
             uint4 *dst = reinterpret_cast<uint4 *>(yr + h * head_dim + rope_dim) + c;
             *dst = *src;
         }
+    }
+    // decode form: row t is query t % nq of sequence t / nq, the nq newest
+    // positions of that sequence
+    int64_t p = seq_len ? seq_len[t / nq] - nq + t % nq : pos0 + t;
+    if (p < 0) p = 0;
+    for (int j = threadIdx.x; j < half; j += blockDim.x) {
+        double ang = static_cast<double>(p) * inv_freq.v[j];
+        double s, c;
+        sincos(ang, &s, &c);
+        cs[j] = c;
+        sn[j] = s;
+    }
+    block_sync();
+    for (int idx = threadIdx.x, u = 0; idx < npairs; idx += blockDim.x, ++u) {
+        int h = idx / half, j = idx - h * half;
+        const uint16_t *xh = xr + h * head_dim;
+        const uint16_t ra = u < kRopePairsPerThread ? pa[u & (kRopePairsPerThread - 1)] : xh[j];
+        const uint16_t rb =
+            u < kRopePairsPerThread ? pb[u & (kRopePairsPerThread - 1)] : xh[j + half];
+        double a = static_cast<double>(bf16_bits_to_f32(ra));
+        double b = static_cast<double>(bf16_bits_to_f32(rb));
+        double c = cs[j], s = sn[j];
+        double ac = a * c, bs = b * s, bc = b * c, as = a * s;
+        uint16_t o0 = f64_to_bf16_rne(ac - bs);
+        uint16_t o1 = f64_to_bf16_rne(bc + as);
+        yr[h * head_dim + j] = o0;
+        yr[h * head_dim + j + half] = o1;
     }
 }
 
