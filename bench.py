@@ -153,7 +153,7 @@ def gather_ceiling(layer, Kr, V, reps):
     stream = torch.cuda.current_stream().cuda_stream
 
     def run():
-        for r0, n in layer._chunks():
+        for r0, n in layer.attn_chunks():
             st = lib.qsa_probe_gather(Kr.data_ptr(), V.data_ptr(), layer.blk_idx[r0:].data_ptr(),
                                       layer.n_sel[r0:].data_ptr(), n, layer.pos0 + r0,
                                       layer.budget, layer.Hkv, out[r0:].data_ptr(), stream)

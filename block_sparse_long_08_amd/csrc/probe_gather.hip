@@ -1,13 +1,15 @@
 // Gather ceiling probe: a measurement kernel, not part of the layer (it is
 // built into its own library, libqsa_probe.so, which only the benchmark
-// loads).  It reads exactly the key and value bytes the sparse prefill
-// attention reads for a selection -- per query and KV head the 512-byte head
-// rows of the tokens of each selected 4-token block and of the query's
-// incomplete block, in the attention's order of 16-token stages -- with the
-// same grid (one workgroup per query, one wave per KV head), and does nothing
-// with them but fold them into one word per (query, head).  Each wave keeps
-// two stages (32 KB) in flight, so the time of a launch is what the memory
-// system needs to deliver the attention's gathers: the ceiling the attention
+// loads).  It issues exactly the loads of the sparse prefill attention for a
+// selection -- per query and KV head, 16-token stages of the selected
+// 4-token blocks and the query's incomplete block; per stage the value rows
+// by LDS DMA into an 8 KB tile (16-byte chunks at the same XOR-swizzled
+// slots) and the key rows into registers with the same lane map -- with the
+// same grid (one workgroup per query, one wave per KV head) and one stage
+// in flight per wave, and does no arithmetic but folding the key words into
+// one word per (query, head).  It needs few registers, so more waves run per
+// CU than the attention's three per SIMD: its time per launch is what the
+// memory system needs for the attention's loads, the ceiling the attention
 // kernel is measured against.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -32,27 +34,36 @@ struct Entries {
     }
 };
 
-// Lane l reads 128 contiguous bytes (8 x 16) of token l/4 of a 16-token stage:
-// four lanes cover one 512-byte head row.
-__device__ __forceinline__ void stage_load(const Entries &L, int e0, int64_t p,
-                                           const uint16_t *__restrict__ Kg,
-                                           const uint16_t *__restrict__ Vg, int64_t rs, int lane,
-                                           uint4 (&k)[8], uint4 (&v)[8]) {
-    const int tt = lane >> 2, c0 = (lane & 3) * 8;
-    const int64_t tok = L.token(e0 + (tt >> 2), tt & 3, p);
-    const uint4 *ks = reinterpret_cast<const uint4 *>(Kg + tok * rs) + c0;
-    const uint4 *vs = reinterpret_cast<const uint4 *>(Vg + tok * rs) + c0;
+__device__ __forceinline__ int row_swizzle(int tt) { return 2 * ((tt >> 2) & 3); }
+
+// One stage: V rows by LDS DMA (instruction j fills bytes 1024*j .. of the
+// tile: row tt = 2j + lane/32, chunk (lane%32) ^ row_swizzle(tt)), K rows
+// into registers (lane l: token l%16 of the stage, dims 8*(l/16) + 32*s).
+__device__ __forceinline__ uint32_t stage(const Entries &L, int e0, int64_t p,
+                                          const uint16_t *__restrict__ Kg,
+                                          const uint16_t *__restrict__ Vg, int64_t rs,
+                                          unsigned char *tile, int lane) {
+    const int h = lane >> 5;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        k[j] = ks[j];
-        v[j] = vs[j];
+        const int tt = 2 * j + h;
+        const int64_t tok = L.token(e0 + (tt >> 2), tt & 3, p);
+        const int c = (lane & 31) ^ row_swizzle(tt);
+        const uint16_t *src = Vg + tok * rs + 8 * c;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                         (__attribute__((address_space(3))) void *)(tile + 1024 * j),
+                                         16, 0, 0);
     }
-}
-
-__device__ __forceinline__ uint32_t fold(const uint4 (&k)[8], const uint4 (&v)[8]) {
+    const int n = lane & 15, g4 = lane >> 4;
+    const uint16_t *ks = Kg + L.token(e0 + (n >> 2), n & 3, p) * rs + 8 * g4;
+    uint4 k[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) k[s] = *reinterpret_cast<const uint4 *>(ks + 32 * s);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): keys and the value tile have landed
+    __builtin_amdgcn_wave_barrier();
     uint32_t x = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x ^= k[j].x ^ k[j].y ^ k[j].z ^ k[j].w ^ v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    for (int s = 0; s < 8; ++s) x ^= k[s].x ^ k[s].y ^ k[s].z ^ k[s].w;
     return x;
 }
 
@@ -60,6 +71,7 @@ __global__ void __launch_bounds__(128) gather_probe_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const int32_t *__restrict__ blk_idx, const int32_t *__restrict__ n_sel, int64_t pos0,
     int Kbudget, int Hkv, uint32_t *__restrict__ out) {
+    __shared__ __attribute__((aligned(16))) unsigned char tiles[2 * 8192];
     const int64_t t = blockIdx.x;
     const int64_t p = pos0 + t;
     const int64_t nc = (p + 1) / kBlock;
@@ -73,16 +85,9 @@ __global__ void __launch_bounds__(128) gather_probe_kernel(
     const int64_t rs = static_cast<int64_t>(Hkv) * kHeadDim;
     const uint16_t *Kg = K + g * kHeadDim;
     const uint16_t *Vg = V + g * kHeadDim;
+    unsigned char *tile = tiles + 8192 * g;
     uint32_t acc = 0;
-    for (int s = 0; s < nstages; s += 2) {
-        uint4 k0[8], v0[8], k1[8], v1[8];
-        stage_load(L, 4 * s, p, Kg, Vg, rs, lane, k0, v0);
-        if (s + 1 < nstages) {
-            stage_load(L, 4 * (s + 1), p, Kg, Vg, rs, lane, k1, v1);
-            acc ^= fold(k1, v1);
-        }
-        acc ^= fold(k0, v0);
-    }
+    for (int s = 0; s < nstages; ++s) acc ^= stage(L, 4 * s, p, Kg, Vg, rs, tile, lane);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) acc ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(acc), off));
     if (lane == 0) out[t * Hkv + g] = acc;
