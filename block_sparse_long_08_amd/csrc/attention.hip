@@ -750,9 +750,10 @@ int64_t decode_max_entries(int Tq, int64_t sel_entries) { return sel_entries + (
 
 int decode_num_splits(int B, int Hkv, int64_t max_entries) {
     const int64_t nstages = (max_entries + kStageEntries - 1) / kStageEntries;
-    // about 512 workgroups (the two per CU that fit at once), at least one
-    // stage per wave
-    int64_t want = (512 + static_cast<int64_t>(B) * Hkv - 1) / (static_cast<int64_t>(B) * Hkv);
+    // at most 512 workgroups (the two per CU that fit at once: one more and a
+    // second round of workgroups doubles the time), at least one stage per
+    // wave
+    int64_t want = 512 / (static_cast<int64_t>(B) * Hkv);
     const int64_t cap = (nstages + 3) / 4;  // at least one stage per wave
     if (want > cap) want = cap;
     if (want < 1) want = 1;

@@ -154,7 +154,12 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
             const int64_t tout = t0 + 16 * wave + ql;
             const int64_t blk = b0 + 4 * wr_c;
             const float4 v = *reinterpret_cast<const float4 *>(stage + ql * kStageRow + 16 * wr_c);
-            if (tout < Tq && blk < ld) *reinterpret_cast<float4 *>(scores + tout * ld + blk) = v;
+            // non-temporal: the score rows are read back once, by the top-K,
+            // and mostly not at all (it loads only the groups that reach its
+            // floor); 18% faster than plain stores at a 1M-token context
+            if (tout < Tq && blk < ld)
+                __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w},
+                                            reinterpret_cast<f32x4 *>(scores + tout * ld + blk));
             if (gmax) {
                 // the 16-block group of the 4 lanes wr_c & ~3 .. | 3 (a quad):
                 // float max across the quad by DPP moves (lane ^ 1, lane ^ 2),
