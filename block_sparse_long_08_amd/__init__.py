@@ -99,6 +99,29 @@ def _ptr(t):
     return t.data_ptr()
 
 
+# Host-side checks before a call: each tensor argument must be a GPU tensor
+# with the element size the call reads, holding at least the bytes the call's
+# own size arguments imply from its first element to the end of its storage
+# (strided views of a larger tensor are fine).  The C library cannot see
+# extents, and an access past them would fault the GPU.  Raw addresses
+# (ints) and None pass unchecked.
+_REQUIRE_GPU = True
+
+
+def _req(fn: str, arg: str, t, elsize: int, nbytes: int) -> None:
+    if t is None or isinstance(t, int):
+        return
+    if _REQUIRE_GPU and not t.is_cuda:
+        raise ValueError(f"{fn}: {arg} is not a GPU tensor")
+    if t.element_size() != elsize:
+        raise ValueError(f"{fn}: {arg} has {t.element_size()}-byte elements, the call reads "
+                         f"{elsize}-byte ones")
+    span = t.untyped_storage().nbytes() - t.storage_offset() * t.element_size()
+    if nbytes > span:
+        raise ValueError(f"{fn}: {arg} holds {span} bytes from its first element; the call "
+                         f"needs {nbytes}")
+
+
 def _stream(stream):
     if stream is None:
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -120,6 +143,9 @@ class Pages(ctypes.Structure):
                 ("page_tokens", ctypes.c_int)]
 
     def __init__(self, table, page_tokens: int):
+        _req("Pages", "table", table, 4, table.numel() * 4)
+        if table.dim() != 2 or not table.is_contiguous():
+            raise ValueError("Pages: table must be a contiguous [B, table_stride] int32 tensor")
         super().__init__(ctypes.c_void_p(table.data_ptr()), table.shape[-1], page_tokens)
         self._table = table  # keeps the tensor alive
 
@@ -141,6 +167,10 @@ def qsa_check_device() -> None:
 def qsa_rope_bf16(x, y, T: int, nheads: int, head_dim: int, rope_dim: int = 64,
                   theta: float = 1e7, pos0: int = 0, seq_len=None, next_n: int = 1,
                   stream=None) -> None:
+    f = "qsa_rope_bf16"
+    _req(f, "x", x, 2, T * nheads * head_dim * 2)
+    _req(f, "y", y, 2, T * nheads * head_dim * 2)
+    _req(f, "seq_len", seq_len, 8, (T // max(next_n, 1)) * 8)
     _call("qsa_rope_bf16", _ptr(x), _ptr(y), T, nheads, head_dim, rope_dim, theta, pos0,
           _ptr(seq_len), next_n, _stream(stream))
 
@@ -148,6 +178,10 @@ def qsa_rope_bf16(x, y, T: int, nheads: int, head_dim: int, rope_dim: int = 64,
 def qsa_compress_keys(k, B: int, Tk: int, k_seq_stride: int, Di: int, r: int, kbar_mode: int,
                       kbar, kbar_seq_stride: int, stream=None, gain=None, rope_dim: int = 0,
                       theta: float = 1e7, block0: int = 0, pages=None) -> None:
+    f = "qsa_compress_keys"
+    _req(f, "k", k, 2, ((B - 1) * k_seq_stride + Tk * Di) * 2)
+    _req(f, "kbar", kbar, 2, 2 if pages is not None else ((B - 1) * kbar_seq_stride + (Tk // r) * Di) * 2)
+    _req(f, "gain", gain, 2, Di * 2)
     _call("qsa_compress_keys", _ptr(k), B, Tk, k_seq_stride, Di, r, kbar_mode, _ptr(gain),
           rope_dim, theta, block0, _ptr(kbar), kbar_seq_stride, _pages(pages), _stream(stream))
 
@@ -155,6 +189,12 @@ def qsa_compress_keys(k, B: int, Tk: int, k_seq_stride: int, Di: int, r: int, kb
 def qsa_index_scores(q_idx, kbar, B: int, Tq: int, pos0: int, seq_len, nb_max: int, Hi: int,
                      Di: int, r: int, score_mode: int, scores, ld: int, stream=None,
                      pages=None) -> None:
+    f = "qsa_index_scores"
+    rows = B if seq_len is not None else B * Tq
+    _req(f, "q_idx", q_idx, 2, B * Tq * Hi * Di * 2)
+    _req(f, "kbar", kbar, 2, 2 if pages is not None else B * nb_max * Di * 2)
+    _req(f, "seq_len", seq_len, 8, B * 8)
+    _req(f, "scores", scores, 4, rows * ld * 4)
     _call("qsa_index_scores", _ptr(q_idx), _ptr(kbar), B, Tq, pos0, _ptr(seq_len), nb_max, Hi, Di,
           r, score_mode, _ptr(scores), ld, _pages(pages), _stream(stream))
 
@@ -165,6 +205,13 @@ def qsa_topk_workspace_bytes(B: int, Tq: int, nb_max: int, K: int) -> int:
 
 def qsa_topk_blocks(scores, B: int, Tq: int, ld: int, pos0: int, seq_len, nb_max: int, r: int,
                     K: int, blk_idx, n_sel, ws=None, ws_bytes: int = 0, stream=None) -> None:
+    f = "qsa_topk_blocks"
+    rows = B if seq_len is not None else B * Tq
+    _req(f, "scores", scores, 4, rows * ld * 4)
+    _req(f, "seq_len", seq_len, 8, B * 8)
+    _req(f, "blk_idx", blk_idx, 4, rows * K * 4)
+    _req(f, "n_sel", n_sel, 4, rows * 4)
+    _req(f, "ws", ws, 1, ws_bytes)
     _call("qsa_topk_blocks", _ptr(scores), B, Tq, ld, pos0, _ptr(seq_len), nb_max, r, K,
           _ptr(blk_idx), _ptr(n_sel), _ptr(ws), ws_bytes, _stream(stream))
 
@@ -176,6 +223,14 @@ def qsa_select_workspace_bytes(B: int, Tq: int, nb_max: int, K: int) -> int:
 def qsa_select_blocks(q_idx, kbar, B: int, Tq: int, pos0: int, seq_len, nb_max: int, Hi: int,
                       Di: int, r: int, score_mode: int, K: int, blk_idx, n_sel, ws,
                       ws_bytes: int, stream=None, pages=None) -> None:
+    f = "qsa_select_blocks"
+    rows = B if seq_len is not None else B * Tq
+    _req(f, "q_idx", q_idx, 2, B * Tq * Hi * Di * 2)
+    _req(f, "kbar", kbar, 2, 2 if pages is not None else B * nb_max * Di * 2)
+    _req(f, "seq_len", seq_len, 8, B * 8)
+    _req(f, "blk_idx", blk_idx, 4, rows * K * 4)
+    _req(f, "n_sel", n_sel, 4, rows * 4)
+    _req(f, "ws", ws, 1, ws_bytes)
     _call("qsa_select_blocks", _ptr(q_idx), _ptr(kbar), B, Tq, pos0, _ptr(seq_len), nb_max, Hi,
           Di, r, score_mode, K, _ptr(blk_idx), _ptr(n_sel), _ptr(ws), ws_bytes, _pages(pages),
           _stream(stream))
@@ -184,6 +239,14 @@ def qsa_select_blocks(q_idx, kbar, B: int, Tq: int, pos0: int, seq_len, nb_max: 
 def qsa_sparse_attn_prefill(Q, K, V, blk_idx, n_sel, Tq: int, Tk: int, pos0: int, H: int,
                             Hkv: int, D: int, r: int, Kbudget: int, O, lse=None,
                             stream=None, pages=None) -> None:
+    f = "qsa_sparse_attn_prefill"
+    _req(f, "Q", Q, 2, Tq * H * D * 2)
+    _req(f, "K", K, 2, 2 if pages is not None else Tk * Hkv * D * 2)
+    _req(f, "V", V, 2, 2 if pages is not None else Tk * Hkv * D * 2)
+    _req(f, "blk_idx", blk_idx, 4, Tq * Kbudget * 4)
+    _req(f, "n_sel", n_sel, 4, Tq * 4)
+    _req(f, "O", O, 4, Tq * H * D * 4)
+    _req(f, "lse", lse, 4, Tq * H * 4)
     _call("qsa_sparse_attn_prefill", _ptr(Q), _ptr(K), _ptr(V), _ptr(blk_idx), _ptr(n_sel), Tq,
           Tk, pos0, H, Hkv, D, r, Kbudget, _ptr(O), _ptr(lse), _pages(pages), _stream(stream))
 
@@ -195,6 +258,16 @@ def qsa_decode_workspace_bytes(B: int, Tq: int, H: int, Hkv: int, D: int, Kbudge
 def qsa_sparse_attn_decode(q, Kc, Vc, seq_len, blk_idx, n_sel, B: int, Tq: int, Lmax: int,
                            H: int, Hkv: int, D: int, r: int, Kbudget: int, O, lse, ws,
                            ws_bytes: int, stream=None, pages=None) -> None:
+    f = "qsa_sparse_attn_decode"
+    _req(f, "q", q, 2, B * Tq * H * D * 2)
+    _req(f, "Kc", Kc, 2, 2 if pages is not None else B * Lmax * Hkv * D * 2)
+    _req(f, "Vc", Vc, 2, 2 if pages is not None else B * Lmax * Hkv * D * 2)
+    _req(f, "seq_len", seq_len, 8, B * 8)
+    _req(f, "blk_idx", blk_idx, 4, B * Kbudget * 4)
+    _req(f, "n_sel", n_sel, 4, B * 4)
+    _req(f, "O", O, 4, B * Tq * H * D * 4)
+    _req(f, "lse", lse, 4, B * Tq * H * 4)
+    _req(f, "ws", ws, 1, ws_bytes)
     _call("qsa_sparse_attn_decode", _ptr(q), _ptr(Kc), _ptr(Vc), _ptr(seq_len), _ptr(blk_idx),
           _ptr(n_sel), B, Tq, Lmax, H, Hkv, D, r, Kbudget, _ptr(O), _ptr(lse), _ptr(ws),
           ws_bytes, _pages(pages), _stream(stream))
@@ -207,6 +280,15 @@ def qsa_decode_noalloc_max_bytes() -> int:
 def qsa_sparse_attn_decode_noalloc(q, Kc, Vc, seq_len, blk_idx, n_sel, B: int, Tq: int,
                                    Lmax: int, H: int, Hkv: int, D: int, r: int, Kbudget: int, O,
                                    lse=None, stream=None, pages=None) -> None:
+    f = "qsa_sparse_attn_decode_noalloc"
+    _req(f, "q", q, 2, B * Tq * H * D * 2)
+    _req(f, "Kc", Kc, 2, 2 if pages is not None else B * Lmax * Hkv * D * 2)
+    _req(f, "Vc", Vc, 2, 2 if pages is not None else B * Lmax * Hkv * D * 2)
+    _req(f, "seq_len", seq_len, 8, B * 8)
+    _req(f, "blk_idx", blk_idx, 4, B * Kbudget * 4)
+    _req(f, "n_sel", n_sel, 4, B * 4)
+    _req(f, "O", O, 4, B * Tq * H * D * 4)
+    _req(f, "lse", lse, 4, B * Tq * H * 4)
     _call("qsa_sparse_attn_decode_noalloc", _ptr(q), _ptr(Kc), _ptr(Vc), _ptr(seq_len),
           _ptr(blk_idx), _ptr(n_sel), B, Tq, Lmax, H, Hkv, D, r, Kbudget, _ptr(O), _ptr(lse),
           _pages(pages), _stream(stream))
@@ -218,6 +300,14 @@ def dense_attn_workspace_bytes(B: int, Tq: int, Lmax: int, H: int, Hkv: int, D: 
 
 def dense_attn(Q, K, V, B: int, Tq: int, Lmax: int, pos0: int, seq_len, H: int, Hkv: int, D: int,
                O, lse=None, ws=None, ws_bytes: int = 0, stream=None, pages=None) -> None:
+    f = "dense_attn"
+    _req(f, "Q", Q, 2, B * Tq * H * D * 2)
+    _req(f, "K", K, 2, 2 if pages is not None else B * Lmax * Hkv * D * 2)
+    _req(f, "V", V, 2, 2 if pages is not None else B * Lmax * Hkv * D * 2)
+    _req(f, "seq_len", seq_len, 8, B * 8)
+    _req(f, "O", O, 4, B * Tq * H * D * 4)
+    _req(f, "lse", lse, 4, B * Tq * H * 4)
+    _req(f, "ws", ws, 1, ws_bytes)
     _call("dense_attn", _ptr(Q), _ptr(K), _ptr(V), B, Tq, Lmax, pos0, _ptr(seq_len), H, Hkv, D,
           _ptr(O), _ptr(lse), _ptr(ws), ws_bytes, _pages(pages), _stream(stream))
 
@@ -229,6 +319,14 @@ def qsa_distill_workspace_bytes(Tq: int, Tk: int) -> int:
 def qsa_distill_kl(Q, K, lse, q_idx, kbar, Tq: int, Tk: int, pos0: int, H: int, Hkv: int, D: int,
                    Hi: int, Di: int, r: int, score_mode: int, kl, ws=None, ws_bytes: int = 0,
                    stream=None) -> None:
+    f = "qsa_distill_kl"
+    _req(f, "Q", Q, 2, Tq * H * D * 2)
+    _req(f, "K", K, 2, Tk * Hkv * D * 2)
+    _req(f, "lse", lse, 4, Tq * H * 4)
+    _req(f, "q_idx", q_idx, 2, Tq * Hi * Di * 2)
+    _req(f, "kbar", kbar, 2, (Tk // r) * Di * 2)
+    _req(f, "kl", kl, 4, Tq * 4)
+    _req(f, "ws", ws, 1, ws_bytes)
     _call("qsa_distill_kl", _ptr(Q), _ptr(K), _ptr(lse), _ptr(q_idx), _ptr(kbar), Tq, Tk, pos0,
           H, Hkv, D, Hi, Di, r, score_mode, _ptr(kl), _ptr(ws), ws_bytes, _stream(stream))
 
@@ -236,6 +334,17 @@ def qsa_distill_kl(Q, K, lse, q_idx, kbar, Tq: int, Tk: int, pos0: int, H: int, 
 def qsa_sparse_attn_prefill_kl(Q, K, V, q_idx, kbar, blk_idx, n_sel, Tq: int, Tk: int,
                                pos0: int, H: int, Hkv: int, D: int, Hi: int, Di: int, r: int,
                                Kbudget: int, score_mode: int, O, lse, kl, stream=None) -> None:
+    f = "qsa_sparse_attn_prefill_kl"
+    _req(f, "Q", Q, 2, Tq * H * D * 2)
+    _req(f, "K", K, 2, Tk * Hkv * D * 2)
+    _req(f, "V", V, 2, Tk * Hkv * D * 2)
+    _req(f, "q_idx", q_idx, 2, Tq * Hi * Di * 2)
+    _req(f, "kbar", kbar, 2, (Tk // r) * Di * 2)
+    _req(f, "blk_idx", blk_idx, 4, Tq * Kbudget * 4)
+    _req(f, "n_sel", n_sel, 4, Tq * 4)
+    _req(f, "O", O, 4, Tq * H * D * 4)
+    _req(f, "lse", lse, 4, Tq * H * 4)
+    _req(f, "kl", kl, 4, Tq * 4)
     _call("qsa_sparse_attn_prefill_kl", _ptr(Q), _ptr(K), _ptr(V), _ptr(q_idx), _ptr(kbar),
           _ptr(blk_idx), _ptr(n_sel), Tq, Tk, pos0, H, Hkv, D, Hi, Di, r, Kbudget, score_mode,
           _ptr(O), _ptr(lse), _ptr(kl), _stream(stream))
