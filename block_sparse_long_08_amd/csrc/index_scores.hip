@@ -10,7 +10,9 @@
 
 namespace qsa {
 
-constexpr int kQT = 64;          // queries per prefill workgroup (4 waves x 16)
+constexpr int kRT = 8;           // MFMA row tiles (4 queries each) per prefill wave
+constexpr int kQW = 4 * kRT;     // queries per prefill wave
+constexpr int kQT = 4 * kQW;     // queries per prefill workgroup (4 waves)
 constexpr int kBT = 64;          // blocks per LDS tile
 constexpr int kSplitTiles = 64;  // block tiles per workgroup (grid.y splits longer rows)
 constexpr int kRowBytes = 272;   // LDS row stride of one pooled key (256 B + 16 B pad)
@@ -43,20 +45,21 @@ __device__ __forceinline__ void store_tile(unsigned char *buf, int bl, int part,
 // Prefill form: queries pos0 + t, t < Tq, one sequence per blockIdx.z.
 // Pooled-key tiles are double-buffered: the next tile is loaded into
 // registers while the current one feeds the MFMAs, then written to the other
-// LDS buffer (one barrier per tile).  Each wave stages its 16 x 64 scores in
+// LDS buffer (one barrier per tile).  Each wave stages its 32 x 64 scores in
 // LDS and writes them back as whole 256-byte row segments.  With gmax set it
 // also writes the largest score key of every 16 consecutive blocks,
 // gmax[t * gld + g] (blocks a query does not see count as -inf), from which
 // the top-K takes its floor.
-// (at most the registers of 3 waves per SIMD: the LDS allows 3 workgroups
-// per CU, and the interleaved accumulators would otherwise take one more
-// register block than that)
+// Each wave holds 32 queries' fragments (128 VGPRs), so every pooled-key
+// fragment read from LDS feeds 8 MFMAs; at 2 waves per SIMD (68 KB of LDS,
+// 2 workgroups per CU) that measured 1.30 against 1.50 ms per 4,096 rows at
+// a 1M-token context for 16 queries per wave at 3 waves per SIMD.
 template <int MODE, bool PAGED>
-__global__ void __launch_bounds__(256, 3)
+__global__ void __launch_bounds__(256, 2)
 index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ kbar,
                      int64_t Tq, int64_t pos0, int64_t nb_max, float *__restrict__ scores,
                      int64_t ld, uint32_t *__restrict__ gmax, int64_t gld, PageTable pg) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileBytes + 4 * 16 * kStageRow];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileBytes + 4 * kQW * kStageRow];
     const int qt = gridDim.x - 1 - blockIdx.x;  // longest rows first
     const int64_t seq = blockIdx.z;
     q_idx += seq * Tq * (kIdxHeads * kIdxDim);
@@ -76,15 +79,15 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g4 = lane >> 4;
-    unsigned char *stage = lds + 2 * kTileBytes + wave * 16 * kStageRow;
+    unsigned char *stage = lds + 2 * kTileBytes + wave * kQW * kStageRow;
 
-    // A fragments: row m = lane%16 of row tile rt is query 16*wave + 4*rt + m/4,
+    // A fragments: row m = lane%16 of row tile rt is query kQW*wave + 4*rt + m/4,
     // head m%4; k-slots of group g4 cover dims 32*s + 8*g4 .. +7.
-    bf16x8 qf[4][4];
-    int64_t ncq[4];
+    bf16x8 qf[kRT][4];
+    int ncq[kRT];  // complete blocks of the query whose scores this lane holds
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const int64_t tq = t0 + 16 * wave + 4 * rt + (n >> 2);
+    for (int rt = 0; rt < kRT; ++rt) {
+        const int64_t tq = t0 + kQW * wave + 4 * rt + (n >> 2);
         const int head = n & 3;
         const bool ok = tq < Tq;
         const uint16_t *src = q_idx + (ok ? tq : 0) * (kIdxHeads * kIdxDim) + head * kIdxDim;
@@ -94,9 +97,10 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
                          : make_uint4(0, 0, 0, 0);
             qf[rt][s] = as_bf16x8(v);
         }
-        // the query whose scores this lane will hold: 16*wave + 4*rt + g4
-        const int64_t tout = t0 + 16 * wave + 4 * rt + g4;
-        ncq[rt] = tout < Tq ? min(num_complete_blocks(pos0 + tout, kBlock), nb_max) : -1;
+        // the query whose scores this lane will hold: kQW*wave + 4*rt + g4
+        const int64_t tout = t0 + kQW * wave + 4 * rt + g4;
+        ncq[rt] = tout < Tq ? static_cast<int>(min(num_complete_blocks(pos0 + tout, kBlock), nb_max))
+                            : -1;
     }
     // write-back mapping: lane -> staged query row 4*i + lane/16, 16-byte chunk lane%16
     const int wr_q = lane >> 4, wr_c = lane & 15;
@@ -127,19 +131,19 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
             for (int s = 0; s < 4; ++s)
                 kf[s] = as_bf16x8(*reinterpret_cast<const uint4 *>(
                     buf + (16 * j + n) * kRowBytes + 64 * s + 16 * g4));
-            const int64_t blk = b0 + 16 * j + n;
-            // the 4 row tiles' accumulators interleaved: no MFMA waits on the
+            const int blk = static_cast<int>(b0) + 16 * j + n;  // blocks < 2^27
+            // the row tiles' accumulators interleaved: no MFMA waits on the
             // one before it
-            f32x4 acc[4];
+            f32x4 acc[kRT];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int rt = 0; rt < kRT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
+                for (int rt = 0; rt < kRT; ++rt)
                     acc[rt] = mfma_bf16_16x16x32(qf[rt][s], kf[s], acc[rt]);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
+            for (int rt = 0; rt < kRT; ++rt) {
                 const float v = blk < ncq[rt] ? combine_heads<MODE>(acc[rt]) : -INFINITY;
                 *reinterpret_cast<float *>(stage + (4 * rt + g4) * kStageRow + 4 * (16 * j + n)) = v;
             }
@@ -147,11 +151,12 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // write back: 4 instructions, each 4 query rows x 256 contiguous bytes
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ql = 4 * i + wr_q;  // staged row = 4*rt + g4 of query 16*wave + ql
-            const int64_t tout = t0 + 16 * wave + ql;
+        // write back: kRT instructions, each 4 query rows x 256 contiguous
+        // bytes (unrolled by 2: fully unrolled, the 8 rounds spill registers)
+#pragma unroll 2
+        for (int i = 0; i < kRT; ++i) {
+            const int ql = 4 * i + wr_q;  // staged row = 4*rt + g4 of query kQW*wave + ql
+            const int64_t tout = t0 + kQW * wave + ql;
             const int64_t blk = b0 + 4 * wr_c;
             const float4 v = *reinterpret_cast<const float4 *>(stage + ql * kStageRow + 16 * wr_c);
             // non-temporal: the score rows are read back once, by the top-K,

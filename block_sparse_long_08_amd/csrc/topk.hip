@@ -154,31 +154,34 @@ __device__ __forceinline__ void block_find(const uint32_t *h, uint32_t krem, Top
     block_sync();
 }
 
-// The same search by one wave over 1024 bins; returns the digit, the count
-// above it and its own count (wave-uniform).
-__device__ __forceinline__ void wave_find1024(const uint32_t *h, uint32_t krem, int lane,
-                                              uint32_t &digit, uint32_t &above, uint32_t &cnt) {
-    const int base = 1024 - 16 * (lane + 1);
-    uint32_t c[16];
+// The same search by one wave over 64 * PER bins (PER a multiple of 4);
+// returns the digit, the count above it and its own count (wave-uniform).
+template <int PER>
+__device__ __forceinline__ void wave_find(const uint32_t *h, uint32_t krem, int lane,
+                                          uint32_t &digit, uint32_t &above, uint32_t &cnt) {
+    static_assert(PER % 4 == 0, "vector reads");
+    constexpr int NB = 64 * PER;
+    const int base = NB - PER * (lane + 1);
+    uint32_t c[PER];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < PER / 4; ++v) {
         const uint4 q = *reinterpret_cast<const uint4 *>(h + base + 4 * v);
-        c[15 - 4 * v] = q.x;
-        c[14 - 4 * v] = q.y;
-        c[13 - 4 * v] = q.z;
-        c[12 - 4 * v] = q.w;
+        c[PER - 1 - 4 * v] = q.x;
+        c[PER - 2 - 4 * v] = q.y;
+        c[PER - 3 - 4 * v] = q.z;
+        c[PER - 4 - 4 * v] = q.w;
     }
     uint32_t local = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) local += c[i];
+    for (int i = 0; i < PER; ++i) local += c[i];
     const uint32_t incl = wave_incl_scan(local, lane);
     uint32_t acc = incl - local;
     const bool mine = acc < krem && krem <= incl;
     uint32_t d = 0, ab = 0, cn = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < PER; ++i) {
         if (acc < krem && krem <= acc + c[i]) {
-            d = static_cast<uint32_t>(base + 15 - i);
+            d = static_cast<uint32_t>(base + PER - 1 - i);
             ab = acc;
             cn = c[i];
         }
@@ -189,6 +192,11 @@ __device__ __forceinline__ void wave_find1024(const uint32_t *h, uint32_t krem, 
     digit = __shfl(d, src, kWave);
     above = __shfl(ab, src, kWave);
     cnt = __shfl(cn, src, kWave);
+}
+
+__device__ __forceinline__ void wave_find1024(const uint32_t *h, uint32_t krem, int lane,
+                                              uint32_t &digit, uint32_t &above, uint32_t &cnt) {
+    wave_find<16>(h, krem, lane, digit, above, cnt);
 }
 
 // Writes one selected element (block index idx) to output slot pos.
@@ -1222,6 +1230,391 @@ __global__ void __launch_bounds__(1024) topk_dec_final(DecTopkArgs d) {
     if (tid == 0) a.n_sel[row] = static_cast<int32_t>(nsel);
 }
 
+// ----------------------------------------- prefill chunks, one wave per row --
+// Rows of a prefill score chunk whose indexer also wrote the 16-block group
+// maxima, for budgets K <= 512: one wave per row and no workgroup barriers,
+// so four rows share a workgroup and 16 rows are in flight per CU.
+//   floor: a key at or below the row's K-th largest key, the lower edge of
+//     the digit holding rank K in a histogram of 256 bins spanning
+//     [smallest, largest] group maximum, refined by a second histogram
+//     inside that bin when it is crowded.  Rows of at least 3K/2 groups
+//     take the histogram of the group maxima (K groups whose maximum reaches
+//     the floor hold K keys at or above it); shorter rows take that of their
+//     keys (keys below the smallest group maximum cannot be among the K
+//     best once the row has K groups);
+//   candidates: the keys at or above the floor, in index order, in a list
+//     of up to 1,024 entries in LDS; the group form reads only the groups
+//     whose maximum reaches the floor, 128 of them per round;
+//   the exact K-th key and its tie quota by 8-bit digits over the list's
+//     range, then emission in index order.
+// A row with fewer than K groups, or whose list overflows, gets n_sel = -1
+// and is finished by the streaming kernel in a second launch (topk_redo).
+constexpr int kWvMaxK = 512;    // budgets this form takes
+constexpr int kWvCap = 1024;    // candidates per row in LDS
+constexpr int kWvBatch = 128;   // surviving groups loaded per round
+constexpr int kWvBins = 256;
+constexpr uint32_t kWvRefine = 64;  // a floor bin holding more is refined
+
+struct __attribute__((aligned(16))) WaveRowSmem {
+    uint32_t hist[kWvBins];
+    int32_t glist[kWvBatch];
+    uint32_t ckey[kWvCap];
+    int32_t cidx[kWvCap];
+};
+
+__device__ __forceinline__ void wave_minmax(uint32_t &lo, uint32_t &hi) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), off)));
+        hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), off)));
+    }
+}
+
+// Calls f(key) for the first cnt group-maximum keys g[0 .. cnt) (a row of
+// the group-maximum array, padded to a multiple of 4).
+template <class F>
+__device__ __forceinline__ void visit_gmax(const uint32_t *g, int cnt, int lane, F f) {
+    for (int base = 0; base < cnt; base += 1024) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = base + 256 * u + 4 * lane;
+            v[u] = i < cnt ? *reinterpret_cast<const uint4 *>(g + i) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = base + 256 * u + 4 * lane;
+            if (i + 0 < cnt) f(v[u].x);
+            if (i + 1 < cnt) f(v[u].y);
+            if (i + 2 < cnt) f(v[u].z);
+            if (i + 3 < cnt) f(v[u].w);
+        }
+    }
+}
+
+// Calls f(key) for the keys of score row s[0 .. n).
+template <class F>
+__device__ __forceinline__ void visit_keys(const float *s, int n, int lane, F f) {
+    for (int base = 0; base < n; base += 1024) {
+        uint32_t kk[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) stream_keys(s, base + 256 * u + 4 * lane, n, kk[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (base + 256 * u + 4 * lane + c < n) f(kk[u][c]);
+    }
+}
+
+// The floor: at least K of the keys the visitor yields (those >= lo; their
+// largest is hi) are >= the returned key, and it is at or below the K-th
+// largest of them.
+template <class V>
+__device__ __forceinline__ uint32_t wave_floor(V visit, uint32_t lo, uint32_t hi, uint32_t K,
+                                               uint32_t *hist, int lane) {
+    const int L = bit_len(hi - lo);
+    const int s1 = L > 8 ? L - 8 : 0;
+    *reinterpret_cast<uint4 *>(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_sync();
+    visit([&](uint32_t k) {
+        // (keys above hi only from NaN scores, which the group maxima skip)
+        if (k >= lo) atomicAdd(&hist[min((k - lo) >> s1, static_cast<uint32_t>(kWvBins - 1))], 1u);
+    });
+    wave_lds_sync();
+    uint32_t d, above, cnt;
+    wave_find<4>(hist, K, lane, d, above, cnt);
+    uint32_t floor_key = lo + (d << s1);
+    if (s1 > 0 && cnt > kWvRefine) {
+        // the keys of bin d, by the next 8 bits below its edge
+        const int s2 = s1 > 8 ? s1 - 8 : 0;
+        wave_lds_sync();  // every lane has read the histogram
+        *reinterpret_cast<uint4 *>(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+        wave_lds_sync();
+        visit([&](uint32_t k) {
+            if (k >= floor_key && ((k - lo) >> s1) == d) atomicAdd(&hist[(k - floor_key) >> s2], 1u);
+        });
+        wave_lds_sync();
+        uint32_t d2, a2, c2;
+        wave_find<4>(hist, K - above, lane, d2, a2, c2);
+        floor_key += d2 << s2;
+    }
+    wave_lds_sync();
+    return floor_key;
+}
+
+// The group maxima of one row: REG (rows of at most 2,048 groups) holds them
+// in registers, group 256 u + 4 lane + c in g[4 u + c], read once; otherwise
+// each pass reads them from memory.
+template <bool REG>
+struct GmaxRow {
+    const uint32_t *gm;
+    int ng;
+    uint32_t g[REG ? 32 : 1];
+
+    __device__ __forceinline__ void load(int lane) {
+        if constexpr (REG) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = 256 * u + 4 * lane;
+                const uint4 v =
+                    i < ng ? *reinterpret_cast<const uint4 *>(gm + i) : make_uint4(0u, 0u, 0u, 0u);
+                g[4 * u + 0] = i + 0 < ng ? v.x : 0u;
+                g[4 * u + 1] = i + 1 < ng ? v.y : 0u;
+                g[4 * u + 2] = i + 2 < ng ? v.z : 0u;
+                g[4 * u + 3] = i + 3 < ng ? v.w : 0u;
+            }
+        }
+    }
+    template <class F>
+    __device__ __forceinline__ void visit(int lane, F f) const {
+        if constexpr (REG) {
+#pragma unroll
+            for (int q = 0; q < 32; ++q)
+                if (256 * (q >> 2) + 4 * lane + (q & 3) < ng) f(g[q]);
+        } else {
+            visit_gmax(gm, ng, lane, f);
+        }
+    }
+    // piece p: groups 1024 p + 256 u + 4 lane + c into gk[4 u + c] (0 past ng)
+    __device__ __forceinline__ void piece(int p, int lane, uint32_t (&gk)[16]) const {
+        if constexpr (REG) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) gk[q] = p == 0 ? g[q] : g[16 + q];
+        } else {
+            const int base = 1024 * p;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = base + 256 * u + 4 * lane;
+                const uint4 v =
+                    i < ng ? *reinterpret_cast<const uint4 *>(gm + i) : make_uint4(0u, 0u, 0u, 0u);
+                gk[4 * u + 0] = i + 0 < ng ? v.x : 0u;
+                gk[4 * u + 1] = i + 1 < ng ? v.y : 0u;
+                gk[4 * u + 2] = i + 2 < ng ? v.z : 0u;
+                gk[4 * u + 3] = i + 3 < ng ? v.w : 0u;
+            }
+        }
+    }
+};
+
+// Candidates of one row: the keys >= the floor, in index order, appended to
+// the wave's list (wc counts past the capacity).  Returns the floor.
+template <bool REG>
+__device__ __forceinline__ uint32_t wave_candidates(const TopkArgs &a, const float *s, int n,
+                                                    GmaxRow<REG> &G, WaveRowSmem &sm, int lane,
+                                                    uint32_t &wc) {
+    const uint32_t K = static_cast<uint32_t>(a.K);
+    const int ng = G.ng;
+    G.load(lane);
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    G.visit(lane, [&](uint32_t k) {
+        lo = min(lo, k);
+        hi = max(hi, k);
+    });
+    wave_minmax(lo, hi);
+    wc = 0;
+    if (2 * ng < 3 * a.K) {
+        // ---- row form: floor from the keys themselves, then the keys that
+        // reach it
+        const uint32_t floor_key = wave_floor(
+            [&](auto f) { visit_keys(s, n, lane, f); }, lo, hi, K, sm.hist, lane);
+        for (int base = 0; base < n; base += 1024) {
+            uint32_t kk[4][4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) stream_keys(s, base + 256 * u + 4 * lane, n, kk[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                stream_append(kk[u], floor_key, base + 256 * u + 4 * lane, kWvCap, wc, sm.ckey,
+                              sm.cidx);
+        }
+        wave_lds_sync();
+        return floor_key;
+    }
+    // ---- group form: floor from the group maxima, then the groups that
+    // reach it
+    const uint32_t floor_key =
+        wave_floor([&](auto f) { G.visit(lane, f); }, lo, hi, K, sm.hist, lane);
+    uint32_t carry = 0;  // surviving groups listed, not yet loaded
+    const int npieces = (ng + 1023) >> 10;
+    for (int p = 0; p < npieces; ++p) {
+        uint32_t gk[16];
+        G.piece(p, lane, gk);
+        const int base = 1024 * p;
+        // survivors of this piece in (u, lane, c) order = index order
+        const bool last = p + 1 >= npieces;
+        uint32_t before[4];
+        uint32_t tot = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            uint32_t cu = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) cu += gk[4 * u + c] >= floor_key ? 1u : 0u;
+            const uint32_t incl = wave_incl_scan(cu, lane);
+            before[u] = tot + incl - cu;
+            tot += static_cast<uint32_t>(__shfl(static_cast<int>(incl), kWave - 1));
+        }
+        // combined positions: the carried survivors of the last piece first
+        // (already listed at 0 .. c0-1), then this piece's
+        const uint32_t c0 = carry;
+        const uint32_t all = c0 + tot;
+        carry = 0;
+        for (uint32_t w0 = 0; w0 < all; w0 += kWvBatch) {
+            const bool full = w0 + kWvBatch <= all;
+            // list the survivors at combined positions [w0, w0 + batch)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint32_t pos = c0 + before[u];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (gk[4 * u + c] >= floor_key) {
+                        if (pos >= w0 && pos < w0 + kWvBatch)
+                            sm.glist[pos - w0] = base + 256 * u + 4 * lane + c;
+                        ++pos;
+                    }
+                }
+            }
+            wave_lds_sync();
+            if (!full && !last) {  // a partial round waits for the next piece
+                carry = all - w0;
+                break;
+            }
+            const int np = static_cast<int>(min(all - w0, static_cast<uint32_t>(kWvBatch)));
+            uint32_t kk[8][4];
+            int ii[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int sidx = 16 * u + (lane >> 2);
+                ii[u] = 0;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) kk[u][c] = 0u;
+                if (sidx < np) {
+                    ii[u] = 16 * sm.glist[sidx] + 4 * (lane & 3);
+                    stream_keys(s, ii[u], n, kk[u]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (16 * u < np)
+                    stream_append(kk[u], floor_key, ii[u], kWvCap, wc, sm.ckey, sm.cidx);
+            wave_lds_sync();  // the list is rewritten by the next round
+        }
+    }
+    return floor_key;
+}
+
+__global__ void __launch_bounds__(256) topk_wave(TopkArgs a, int64_t rows) {
+    __shared__ WaveRowSmem smem[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    if (row >= rows) return;
+    WaveRowSmem &sm = smem[wave];
+    const int64_t sq = row / a.Tq;
+    const int64_t p = a.pos0 + (row - sq * a.Tq);
+    const int64_t n_row = min(num_complete_blocks(p, a.r), a.nb_max);
+    const uint32_t K = static_cast<uint32_t>(a.K);
+    int32_t *out = a.blk_idx + row * a.K;
+    if (n_row <= a.K) {  // every complete block is selected
+        for (int i = lane; i < a.K; i += kWave) out[i] = i < n_row ? i : -1;
+        if (lane == 0) a.n_sel[row] = static_cast<int32_t>(n_row);
+        return;
+    }
+    const int n = static_cast<int>(n_row);
+    const int ng = (n + 15) >> 4;
+    if (ng < a.K) {  // too few groups for the group-maximum bound
+        if (lane == 0) a.n_sel[row] = -1;
+        return;
+    }
+    const float *s = a.scores + row * a.ld;
+    const uint32_t *gm = a.gmax + row * a.gld;
+    uint32_t wc, lo;
+    if (ng <= 2048) {
+        GmaxRow<true> G{gm, ng, {}};
+        lo = wave_candidates<true>(a, s, n, G, sm, lane, wc);
+    } else {
+        GmaxRow<false> G{gm, ng, {}};
+        lo = wave_candidates<false>(a, s, n, G, sm, lane, wc);
+    }
+    if (wc > static_cast<uint32_t>(kWvCap)) {  // crowded: the streaming kernel takes it
+        if (lane == 0) a.n_sel[row] = -1;
+        return;
+    }
+
+    // ---- exact K-th key over the list (every entry >= lo), digits of up to
+    // 8 bits from the top of the list's range
+    uint32_t thr = lo, quota = 0, eqcnt = 0;
+    bool split = false;
+    if (wc > K) {
+        uint32_t cmax = 0u;
+        for (uint32_t i = lane; i < wc; i += kWave) cmax = max(cmax, sm.ckey[i]);
+        uint32_t dummy = 0u;
+        wave_minmax(dummy, cmax);
+        const int L = bit_len(cmax - lo);
+        int sh = L > 8 ? L - 8 : 0, sh_prev = 32;
+        uint32_t hp = 0, krem = K;
+        for (;;) {
+            const uint32_t dmask = (1u << (sh_prev - sh > 8 ? 8 : sh_prev - sh)) - 1u;
+            *reinterpret_cast<uint4 *>(sm.hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+            wave_lds_sync();
+            for (uint32_t i = lane; i < wc; i += kWave) {
+                const uint32_t v = sm.ckey[i] - lo;
+                if (sh_prev == 32 || (v >> sh_prev) == hp) atomicAdd(&sm.hist[(v >> sh) & dmask], 1u);
+            }
+            wave_lds_sync();
+            uint32_t dg, ab, cn;
+            wave_find<4>(sm.hist, krem, lane, dg, ab, cn);
+            krem -= ab;
+            eqcnt = cn;
+            hp = sh_prev == 32 ? dg : (hp << (sh_prev - sh)) | dg;
+            wave_lds_sync();  // every lane has read the histogram
+            if (sh == 0) break;
+            sh_prev = sh;
+            sh = sh > 8 ? sh - 8 : 0;
+        }
+        thr = lo + hp;
+        quota = krem;
+        split = quota != eqcnt;
+    }
+    // ---- emission in index order (the list is in index order)
+    uint32_t gt_off = 0, eq_off = 0;
+    for (uint32_t i0 = 0; i0 < wc; i0 += kWave) {
+        const uint32_t i = i0 + lane;
+        const bool ok = i < wc;
+        const uint32_t key = ok ? sm.ckey[i] : 0u;
+        const int32_t idx = ok ? sm.cidx[i] : 0;
+        const bool gt = ok && (split ? key > thr : key >= thr);
+        const bool eq = ok && split && key == thr;
+        const uint64_t bg = __ballot(gt), be = __ballot(eq);
+        const uint32_t gr = gt_off + lanes_below(bg), er = eq_off + lanes_below(be);
+        if (gt || (eq && er < quota)) out[gr + min(er, quota)] = idx;
+        gt_off += static_cast<uint32_t>(__popcll(bg));
+        eq_off += static_cast<uint32_t>(__popcll(be));
+    }
+    const uint32_t nsel = split ? K : gt_off;
+    for (uint32_t i = nsel + lane; i < K; i += kWave) out[i] = -1;
+    if (lane == 0) a.n_sel[row] = static_cast<int32_t>(nsel);
+}
+
+// The rows topk_wave left (n_sel = -1), by the streaming kernel: each
+// workgroup checks 64 consecutive rows and runs those in turn.
+__global__ void __launch_bounds__(256) topk_redo(TopkArgs a, int64_t rows) {
+    __shared__ StreamSmem<256> sm;
+    __shared__ uint64_t flagged;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kWave;
+    if (threadIdx.x < kWave) {
+        const int64_t r = r0 + threadIdx.x;
+        const uint64_t b = __ballot(r < rows && a.n_sel[r] == -1);
+        if (threadIdx.x == 0) flagged = b;
+    }
+    block_sync();
+    uint64_t m = flagged;
+    while (m) {
+        const int i = static_cast<int>(__builtin_ctzll(m));
+        m &= m - 1;
+        stream_row<256>(a, r0 + i, sm);
+        block_sync();  // the next row rewrites the histogram and lists
+    }
+}
+
 // ------------------------------------------------------------------ plan --
 TopkPlan topk_plan(int64_t rows, int64_t nmax, int K) {
     TopkPlan pl{};
@@ -1296,6 +1689,18 @@ hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64
     if (pl.stream) {
         a.gmax = seq_len ? nullptr : gmax;
         a.gld = gld;
+        if (a.gmax && K <= kWvMaxK) {
+            // prefill chunks with the group maxima: one wave per row, then
+            // the rows it leaves (too few groups, crowded lists) by the
+            // streaming kernel
+            hipLaunchKernelGGL(topk_wave, dim3(static_cast<uint32_t>((rows + 3) / 4)), dim3(256),
+                               0, s, a, rows);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(topk_redo, dim3(static_cast<uint32_t>((rows + kWave - 1) / kWave)),
+                               dim3(256), 0, s, a, rows);
+            return hipGetLastError();
+        }
         // with the group maxima a row's passes are short: 256 threads, so
         // that more rows are in flight per CU
         if (pl.stream_nt == 1024 && !a.gmax)

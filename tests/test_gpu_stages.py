@@ -299,17 +299,22 @@ def test_selection_tie_band(qsa, mode):
                                             (1, 400, 12000, 1024), (0, 1300, 60000, 512),
                                             (1, 700, 140000, 512), (0, 300, 1048000, 512),
                                             (1, 260, 1048000, 2048), (0, 600, 100000, 512),
-                                            (0, 2000, 64000, 512)])
+                                            (0, 2000, 64000, 512), (0, 2000, 64000, 100),
+                                            (0, 60000, 0, 512), (1, 20000, 32000, 512)])
 def test_select_matches_scores_plus_topk(qsa, mode, Tq, pos0, K):
     """qsa_select_blocks returns exactly what qsa_index_scores followed by
     qsa_topk_blocks returns (same scores bit for bit, same tie order);
     RELUSUM rows near nc = K put the K-th score on a run of exact zeros.
-    Chunks of >= 256 rows longer than 12,288 blocks take the streaming top-K;
-    rows with at least 4 groups of 16 blocks per thread take its floor from
-    the indexer's 16-block group maxima and never read the groups below it
-    (1M rows, 25K-block rows, and a chunk whose rows straddle that bound);
-    qsa_topk_blocks alone reads the scores only, so the paths must agree
-    exactly, RELUSUM zero runs included."""
+    Chunks of >= 256 rows longer than 12,288 blocks take the one-wave top-K
+    when K <= 512: rows of at least 3K/2 groups of 16 blocks take the floor
+    from the indexer's group maxima and read only the groups that reach it,
+    rows of K .. 3K/2 groups from a histogram of their keys, and rows of
+    fewer groups (or crowded lists) go to the streaming kernel (the 60,000
+    and 20,000-row cases hold all of these, and rows of nc <= K); larger
+    budgets take the streaming kernel, with its floor from the group maxima
+    for rows of at least 4 groups per thread; qsa_topk_blocks alone reads
+    the scores only, so the paths must agree exactly, RELUSUM zero runs
+    included."""
     torch = _torch()
     Tk = pos0 + Tq
     qi = synth.normal_bf16(4, (Tq, 4, 128), seed=13)
@@ -329,6 +334,53 @@ def test_select_matches_scores_plus_topk(qsa, mode, Tq, pos0, K):
     torch.cuda.synchronize()
     assert np.array_equal(n1, n2.cpu().numpy())
     assert np.array_equal(b1, b2.cpu().numpy())
+
+
+@pytest.mark.parametrize("case", ["tie_classes", "all_equal"])
+def test_select_planted_ties(qsa, case):
+    """Tie handling of the one-wave top-K (300 rows at 140,000, K = 512).
+    tie_classes: only indexer head 0 sees dim 0 of the pooled keys; 300
+    blocks score 2/sqrt(128), 400 score 1/sqrt(128), the rest 0 (the other
+    heads' zero dot products win the max): the list holds the 700 and the
+    K-th key falls inside the 400-way tie, taken lowest index first.
+    all_equal: zero queries, every score 0, so every group survives, the list
+    overflows and the streaming kernel finishes every row: the K lowest
+    blocks.  Both against qsa_topk_blocks on the scores and against the
+    selection written out from the planted classes."""
+    torch = _torch()
+    Tq, pos0, K = 300, 140000, 512
+    nb = (pos0 + Tq) // 4
+    rng = np.random.default_rng(5)
+    kb = np.zeros((nb, 128), dtype=np.uint16)
+    qi = np.zeros((Tq, 4, 128), dtype=np.uint16)
+    two = one = np.zeros(0, dtype=np.int64)
+    if case == "tie_classes":
+        perm = rng.permutation(pos0 // 4)  # blocks every row sees
+        two, one = np.sort(perm[:300]), np.sort(perm[300:700])
+        kb[:, 0] = 0xBF80  # -1: negative dot products for head 0
+        kb[two, 0] = 0x4000  # 2.0
+        kb[one, 0] = 0x3F80  # 1.0
+        qi[:, 0, 0] = 0x3F80
+    ld = (nb + 3) // 4 * 4
+    qd, kd = dev(qi), dev(kb)
+    sc = torch.empty((Tq, ld), dtype=torch.float32, device="cuda")
+    qsa.qsa_index_scores(qd, kd, 1, Tq, pos0, None, nb, 4, 128, 4, 0, sc, ld)
+    b1, n1 = run_topk(qsa, sc, 1, Tq, ld, pos0, None, nb, K)
+    wsb = qsa.qsa_select_workspace_bytes(1, Tq, nb, K)
+    ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device="cuda")
+    b2 = torch.full((Tq, K), 7, dtype=torch.int32, device="cuda")
+    n2 = torch.full((Tq,), 7, dtype=torch.int32, device="cuda")
+    qsa.qsa_select_blocks(qd, kd, 1, Tq, pos0, None, nb, 4, 128, 4, 0, K, b2, n2, ws, wsb)
+    torch.cuda.synchronize()
+    b2, n2 = b2.cpu().numpy(), n2.cpu().numpy()
+    if case == "tie_classes":
+        want = np.sort(np.concatenate([two, one[:K - two.size]]))
+    else:
+        want = np.arange(K)
+    assert np.all(n2 == K)
+    for t in range(Tq):
+        assert np.array_equal(b2[t], want), t
+    assert np.array_equal(n1, n2) and np.array_equal(b1, b2)
 
 
 def _decode_select(qsa, qi, kb, lens, K, mode=0):
