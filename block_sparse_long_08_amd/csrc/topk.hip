@@ -155,10 +155,12 @@ __device__ __forceinline__ void block_find(const uint32_t *h, uint32_t krem, Top
 }
 
 // The same search by one wave over 64 * PER bins (PER a multiple of 4);
-// returns the digit, the count above it and its own count (wave-uniform).
+// returns the digit, the count above it, its own count and the total count
+// (wave-uniform; with total < krem the digit is 0 and the rest undefined).
 template <int PER>
 __device__ __forceinline__ void wave_find(const uint32_t *h, uint32_t krem, int lane,
-                                          uint32_t &digit, uint32_t &above, uint32_t &cnt) {
+                                          uint32_t &digit, uint32_t &above, uint32_t &cnt,
+                                          uint32_t &total) {
     static_assert(PER % 4 == 0, "vector reads");
     constexpr int NB = 64 * PER;
     const int base = NB - PER * (lane + 1);
@@ -188,15 +190,17 @@ __device__ __forceinline__ void wave_find(const uint32_t *h, uint32_t krem, int 
         acc += c[i];
     }
     const uint64_t m = __ballot(mine);
-    const int src = static_cast<int>(__builtin_ctzll(m));
+    const int src = m ? static_cast<int>(__builtin_ctzll(m)) : 0;
     digit = __shfl(d, src, kWave);
     above = __shfl(ab, src, kWave);
     cnt = __shfl(cn, src, kWave);
+    total = static_cast<uint32_t>(__shfl(static_cast<int>(incl), kWave - 1, kWave));
 }
 
 __device__ __forceinline__ void wave_find1024(const uint32_t *h, uint32_t krem, int lane,
                                               uint32_t &digit, uint32_t &above, uint32_t &cnt) {
-    wave_find<16>(h, krem, lane, digit, above, cnt);
+    uint32_t total;
+    wave_find<16>(h, krem, lane, digit, above, cnt, total);
 }
 
 // Writes one selected element (block index idx) to output slot pos.
@@ -1307,36 +1311,40 @@ __device__ __forceinline__ void visit_keys(const float *s, int n, int lane, F f)
     }
 }
 
-// The floor: at least K of the keys the visitor yields (those >= lo; their
-// largest is hi) are >= the returned key, and it is at or below the K-th
-// largest of them.
+// The floor: at least K of the keys the visitor yields are >= the returned
+// key, and it is at or below the K-th largest of them.  The histogram spans
+// [lo, hi]: keys below lo are not counted, keys above hi count in the top
+// bin (hi need not be the largest key).  ok = false when fewer than K keys
+// are >= lo (the floor is then undefined).
 template <class V>
 __device__ __forceinline__ uint32_t wave_floor(V visit, uint32_t lo, uint32_t hi, uint32_t K,
-                                               uint32_t *hist, int lane) {
+                                               uint32_t *hist, int lane, bool &ok) {
+    constexpr uint32_t kTop = kWvBins - 1;
     const int L = bit_len(hi - lo);
     const int s1 = L > 8 ? L - 8 : 0;
     *reinterpret_cast<uint4 *>(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
     wave_lds_sync();
     visit([&](uint32_t k) {
-        // (keys above hi only from NaN scores, which the group maxima skip)
-        if (k >= lo) atomicAdd(&hist[min((k - lo) >> s1, static_cast<uint32_t>(kWvBins - 1))], 1u);
+        if (k >= lo) atomicAdd(&hist[min((k - lo) >> s1, kTop)], 1u);
     });
     wave_lds_sync();
-    uint32_t d, above, cnt;
-    wave_find<4>(hist, K, lane, d, above, cnt);
+    uint32_t d, above, cnt, total;
+    wave_find<4>(hist, K, lane, d, above, cnt, total);
+    ok = total >= K;
     uint32_t floor_key = lo + (d << s1);
-    if (s1 > 0 && cnt > kWvRefine) {
+    if (ok && s1 > 0 && cnt > kWvRefine) {
         // the keys of bin d, by the next 8 bits below its edge
         const int s2 = s1 > 8 ? s1 - 8 : 0;
         wave_lds_sync();  // every lane has read the histogram
         *reinterpret_cast<uint4 *>(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
         wave_lds_sync();
         visit([&](uint32_t k) {
-            if (k >= floor_key && ((k - lo) >> s1) == d) atomicAdd(&hist[(k - floor_key) >> s2], 1u);
+            if (k >= floor_key && min((k - lo) >> s1, kTop) == d)
+                atomicAdd(&hist[min((k - floor_key) >> s2, kTop)], 1u);
         });
         wave_lds_sync();
-        uint32_t d2, a2, c2;
-        wave_find<4>(hist, K - above, lane, d2, a2, c2);
+        uint32_t d2, a2, c2, t2;
+        wave_find<4>(hist, K - above, lane, d2, a2, c2, t2);
         floor_key += d2 << s2;
     }
     wave_lds_sync();
@@ -1406,18 +1414,31 @@ __device__ __forceinline__ uint32_t wave_candidates(const TopkArgs &a, const flo
     const uint32_t K = static_cast<uint32_t>(a.K);
     const int ng = G.ng;
     G.load(lane);
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    G.visit(lane, [&](uint32_t k) {
-        lo = min(lo, k);
-        hi = max(hi, k);
-    });
-    wave_minmax(lo, hi);
+    auto minmax_of = [&](auto visit, uint32_t &lo, uint32_t &hi) {
+        lo = 0xFFFFFFFFu;
+        hi = 0u;
+        visit([&](uint32_t k) {
+            lo = min(lo, k);
+            hi = max(hi, k);
+        });
+        wave_minmax(lo, hi);
+    };
+    auto gvisit = [&](auto f) { G.visit(lane, f); };
+    auto kvisit = [&](auto f) { visit_keys(s, n, lane, f); };
     wc = 0;
+    bool ok;
     if (2 * ng < 3 * a.K) {
         // ---- row form: floor from the keys themselves, then the keys that
-        // reach it
-        const uint32_t floor_key = wave_floor(
-            [&](auto f) { visit_keys(s, n, lane, f); }, lo, hi, K, sm.hist, lane);
+        // reach it.  The histogram spans the group maxima's range; with
+        // fewer than K of the keys at or above the smallest maximum (rows of
+        // few groups) it spans all the keys instead.
+        uint32_t lo, hi;
+        minmax_of(gvisit, lo, hi);
+        uint32_t floor_key = wave_floor(kvisit, lo, hi, K, sm.hist, lane, ok);
+        if (!ok) {
+            minmax_of(kvisit, lo, hi);
+            floor_key = wave_floor(kvisit, lo, hi, K, sm.hist, lane, ok);
+        }
         for (int base = 0; base < n; base += 1024) {
             uint32_t kk[4][4];
 #pragma unroll
@@ -1432,8 +1453,44 @@ __device__ __forceinline__ uint32_t wave_candidates(const TopkArgs &a, const flo
     }
     // ---- group form: floor from the group maxima, then the groups that
     // reach it
-    const uint32_t floor_key =
-        wave_floor([&](auto f) { G.visit(lane, f); }, lo, hi, K, sm.hist, lane);
+    uint32_t floor_key;
+    if constexpr (REG) {
+        uint32_t lo, hi;
+        minmax_of(gvisit, lo, hi);
+        floor_key = wave_floor(gvisit, lo, hi, K, sm.hist, lane, ok);
+    } else {
+        // Long rows: the histogram's range comes from a sample, 256 groups
+        // at each quarter of the row (one read instead of a pass over the
+        // maxima), from about the 2K ng'/ng-th largest sampled maximum
+        // (ng' = 1,024 sampled; the row's K-th largest maximum lies above it
+        // unless the sample misleads) to the largest sampled one.  When
+        // fewer than K maxima reach the low end, the exact range is taken.
+        uint32_t smp[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = ((ng >> 2) * q & ~3) + 4 * lane;  // < ng: ng > 2,048
+            const uint4 v = *reinterpret_cast<const uint4 *>(G.gm + i);
+            smp[4 * q + 0] = v.x;
+            smp[4 * q + 1] = v.y;
+            smp[4 * q + 2] = v.z;
+            smp[4 * q + 3] = v.w;
+        }
+        auto svisit = [&](auto f) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) f(smp[q]);
+        };
+        uint32_t lo, hi;
+        minmax_of(svisit, lo, hi);
+        const uint32_t ks = static_cast<uint32_t>(
+            min(static_cast<int64_t>(1024), max(static_cast<int64_t>(1),
+                                                2 * static_cast<int64_t>(K) * 1024 / ng)));
+        lo = wave_floor(svisit, lo, hi, ks, sm.hist, lane, ok);
+        floor_key = wave_floor(gvisit, lo, hi, K, sm.hist, lane, ok);
+        if (!ok) {
+            minmax_of(gvisit, lo, hi);
+            floor_key = wave_floor(gvisit, lo, hi, K, sm.hist, lane, ok);
+        }
+    }
     uint32_t carry = 0;  // surviving groups listed, not yet loaded
     const int npieces = (ng + 1023) >> 10;
     for (int p = 0; p < npieces; ++p) {
@@ -1520,10 +1577,6 @@ __global__ void __launch_bounds__(256) topk_wave(TopkArgs a, int64_t rows) {
     }
     const int n = static_cast<int>(n_row);
     const int ng = (n + 15) >> 4;
-    if (ng < a.K) {  // too few groups for the group-maximum bound
-        if (lane == 0) a.n_sel[row] = -1;
-        return;
-    }
     const float *s = a.scores + row * a.ld;
     const uint32_t *gm = a.gmax + row * a.gld;
     uint32_t wc, lo;
@@ -1560,8 +1613,8 @@ __global__ void __launch_bounds__(256) topk_wave(TopkArgs a, int64_t rows) {
                 if (sh_prev == 32 || (v >> sh_prev) == hp) atomicAdd(&sm.hist[(v >> sh) & dmask], 1u);
             }
             wave_lds_sync();
-            uint32_t dg, ab, cn;
-            wave_find<4>(sm.hist, krem, lane, dg, ab, cn);
+            uint32_t dg, ab, cn, tt;
+            wave_find<4>(sm.hist, krem, lane, dg, ab, cn, tt);
             krem -= ab;
             eqcnt = cn;
             hp = sh_prev == 32 ? dg : (hp << (sh_prev - sh)) | dg;
@@ -1674,6 +1727,9 @@ hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64
     int64_t nmax = nb_max;
     if (!seq_len && rows >= 256) nmax = min(num_complete_blocks(pos0 + Tq - 1, r), nb_max);
     const TopkPlan pl = topk_plan(rows, nmax, K);
+    // prefill chunks with the group maxima: one wave per row, then the rows
+    // it leaves (crowded lists) by the streaming kernel
+    const bool wave_rows = gmax && !seq_len && rows >= 256 && K <= kWvMaxK;
     TopkArgs a{};
     a.scores = scores;
     a.ld = ld;
@@ -1686,21 +1742,20 @@ hipError_t launch_topk(const float *scores, int B, int64_t Tq, int64_t ld, int64
     a.seq_len = seq_len;
     a.r = r;
     a.K = K;
+    if (wave_rows) {
+        a.gmax = gmax;
+        a.gld = gld;
+        hipLaunchKernelGGL(topk_wave, dim3(static_cast<uint32_t>((rows + 3) / 4)), dim3(256), 0, s,
+                           a, rows);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(topk_redo, dim3(static_cast<uint32_t>((rows + kWave - 1) / kWave)),
+                           dim3(256), 0, s, a, rows);
+        return hipGetLastError();
+    }
     if (pl.stream) {
         a.gmax = seq_len ? nullptr : gmax;
         a.gld = gld;
-        if (a.gmax && K <= kWvMaxK) {
-            // prefill chunks with the group maxima: one wave per row, then
-            // the rows it leaves (too few groups, crowded lists) by the
-            // streaming kernel
-            hipLaunchKernelGGL(topk_wave, dim3(static_cast<uint32_t>((rows + 3) / 4)), dim3(256),
-                               0, s, a, rows);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(topk_redo, dim3(static_cast<uint32_t>((rows + kWave - 1) / kWave)),
-                               dim3(256), 0, s, a, rows);
-            return hipGetLastError();
-        }
         // with the group maxima a row's passes are short: 256 threads, so
         // that more rows are in flight per CU
         if (pl.stream_nt == 1024 && !a.gmax)
