@@ -719,7 +719,7 @@ def main():
     if args.million == "on":
         # the same metric at 1M context: prefill chunk and decode (own inputs)
         del x
-        m_pre, _ = bench_prefill("prefill_1m_chunk", min(args.steps, 3), 1,
+        m_pre, _ = bench_prefill("prefill_1m_chunk", args.steps, args.warmup,
                                  with_dense=args.dense == "all", pipeline_rows=args.pipeline_rows,
                                  attn_rows=args.attn_rows)
         m = dict(workload="prefill_1m_chunk", ms_per_step=m_pre["ms_per_step"],
@@ -736,7 +736,7 @@ def main():
         out["prefill_1m_chunk"] = m
         log(f"prefill prefill_1m_chunk: {m_pre['ms_per_step']:.2f} ms/step")
         # the report's prefill condition: a 16K-token chunk over a paged cache
-        c_pre, _ = bench_prefill("prefill_1m_chunk16k", min(args.steps, 3), 1,
+        c_pre, _ = bench_prefill("prefill_1m_chunk16k", args.steps, args.warmup,
                                  with_dense=args.dense == "all", page_tokens=64,
                                  pipeline_rows=args.pipeline_rows, attn_rows=args.attn_rows)
         c = dict(workload="prefill_1m_chunk16k", page_tokens=64, ms_per_step=c_pre["ms_per_step"],

@@ -26,16 +26,18 @@ inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s);
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// Rows of one prefill score chunk (the scores of a chunk, at most 4 GiB, live
+// Rows of one prefill score chunk (the scores of a chunk, at most 8 GiB, live
 // in the workspace; top-K reads them back before the next chunk is scored).
 // Fewer, larger chunks leave fewer kernel tails idle: 4 GiB against 1 GiB
-// measured 9% faster at a 1M-token context, and is small beside 288 GB.
-constexpr int64_t kScoreChunkBytes = int64_t(1) << 32;
+// measured 9% faster at a 1M-token context, 8 GiB against 4 GiB 0.2 ms less
+// selection per 128K prefill; 8 GiB is small beside 288 GB.  Chunks are whole
+// 128-query tiles of the indexer.
+constexpr int64_t kScoreChunkBytes = int64_t(1) << 33;
 
 int64_t select_chunk_rows(int64_t Tq, int64_t ld) {
     int64_t rows = kScoreChunkBytes / (ld * 4);
-    rows = rows / 64 * 64;
-    if (rows < 64) rows = 64;
+    rows = rows / 128 * 128;
+    if (rows < 128) rows = 128;
     return rows < Tq ? rows : Tq;
 }
 
@@ -452,7 +454,7 @@ int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, i
 }
 
 // Distillation: the indexer scores of one chunk of query rows live in the
-// workspace (at most 4 GiB); the fused kernel reads them back.
+// workspace (at most 8 GiB); the fused kernel reads them back.
 static void distill_layout(int64_t Tq, int64_t nb_max, int64_t *ld, int64_t *chunk) {
     *ld = round_up(nb_max > 0 ? nb_max : 1, 4);
     *chunk = select_chunk_rows(Tq, *ld);

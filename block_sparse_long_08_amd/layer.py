@@ -35,7 +35,7 @@ class QSAPrefill:
     the RMSNorm gain of the pooled keys (kbar_mode RMSNORM), bf16 [DI].
 
     The selection of all rows runs first (one call; the library scores the
-    rows in chunks of at most 4 GiB of scores), then the sparse attention in
+    rows in chunks of at most 8 GiB of scores), then the sparse attention in
     launches of attn_rows rows (default 4,096: the 128K prefill's launches
     take 48.7 ms in all against 62.5 ms as one launch of 131,072 rows).
     pipeline_rows > 0 (and < Tq) instead selects the queries in chunks of

@@ -158,12 +158,12 @@ def test_topk_validation(lib):
 
 def test_select_validation(lib):
     lib.qsa_select_workspace_bytes.restype = ctypes.c_size_t
-    # prefill form: scores of one chunk of rows (at most 4 GiB) and their
+    # prefill form: scores of one chunk of rows (at most 8 GiB) and their
     # 16-block group maxima (1/16 of that) in the workspace
     need = lib.qsa_select_workspace_bytes(1, I64(131072), I64(32768), 512)
-    assert (1 << 31) <= need <= (1 << 32) * 17 // 16 + (1 << 20)
+    assert (1 << 32) <= need <= (1 << 33) * 17 // 16 + (1 << 20)
     assert lib.qsa_select_workspace_bytes(1, I64(1 << 20), I64(1 << 18), 512) <= \
-        (1 << 32) * 17 // 16 + (1 << 20)
+        (1 << 33) * 17 // 16 + (1 << 20)
     st = lib.qsa_select_blocks(vp(P), vp(P), 1, I64(131072), I64(0), None, I64(32768), 4, 128, 4,
                                0, 512, vp(P), vp(P), vp(P), ctypes.c_size_t(need - 1), None,
                                None)
@@ -284,8 +284,8 @@ def test_distill_validation(lib):
     assert need >= 8 * 16 * 4                          # the chunk's indexer scores
     assert lib.qsa_distill_workspace_bytes(I64(0), I64(64)) == 0
     assert lib.qsa_distill_workspace_bytes(I64(8), I64(3)) == 0   # no complete block
-    # one chunk of rows stays within 4 GiB however long the context
-    assert lib.qsa_distill_workspace_bytes(I64(1 << 20), I64(1 << 20)) <= (1 << 32)
+    # one chunk of rows stays within 8 GiB however long the context
+    assert lib.qsa_distill_workspace_bytes(I64(1 << 20), I64(1 << 20)) <= (1 << 33)
     assert distill(lib, lse=0) == NULL
     assert distill(lib, kb=0) == NULL
     assert distill(lib, kl=0) == NULL

@@ -99,8 +99,9 @@ def test_distill_tiny_contexts(qsa):
 
 def test_distill_million_token_context_several_chunks(qsa):
     """8,500 queries ending a 1,048,576-token context: the row chunks of the
-    workspace (4,096 rows at this length) split them 4096 + 4096 + 308; rows
-    at and next to each chunk edge against the oracle."""
+    workspace (8,192 rows at this length) split them 8192 + 308; rows at and
+    next to the chunk edge and to an indexer workgroup edge (4,096) against
+    the oracle."""
     Tk, Tq = 1 << 20, 8500
     pos0 = Tk - Tq
     K = synth.normal_bf16(synth.STREAM_K, (Tk, 2, 256), seed=86)
