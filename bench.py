@@ -175,7 +175,8 @@ def gather_ceiling(layer, Kr, V, reps):
 
 
 def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, page_tokens=0,
-                  with_distill=False, pipeline_rows=0, with_probe=False, attn_rows=None):
+                  with_distill=False, pipeline_rows=0, with_probe=False, attn_rows=None,
+                  kl_rows=None):
     import torch
     import block_sparse_long_08_amd as qsa
     Tq, pos0, budget, nd = WORKLOADS[name]
@@ -201,6 +202,8 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
         qsa.qsa_compress_keys(ki, 1, pos0, pos0 * 128, 128, 4, 0, kbar, (pos0 // 4) * 128,
                               rope_dim=idx_rope_dim)
     extra = {} if attn_rows is None else dict(attn_rows=attn_rows)
+    if kl_rows is not None:
+        extra["kl_rows"] = kl_rows
     layer = qsa.QSAPrefill(Tq, pos0=pos0, budget=budget, fresh=fresh, idx_rope_dim=idx_rope_dim,
                            pages=pages, pipeline_rows=pipeline_rows, **extra)
     torch.cuda.synchronize()
@@ -322,7 +325,7 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
             del ws
             # second stage: the sparse attention fused with the KL under the
             # sparse pattern, over the selection of the timed steps, in the
-            # attention's row chunks
+            # layer's launches of kl_rows rows
             fused = lambda: layer.attend_with_kl(Kr, V, qs, kb, kl)  # noqa: E731
             fused()
             torch.cuda.synchronize()
@@ -332,7 +335,8 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
             e1.record()
             torch.cuda.synchronize()
             fms = e0.elapsed_time(e1) / dsteps
-            res["sparse_kl"] = dict(ms=fms, launches=nlaunch,
+            res["sparse_kl"] = dict(ms=fms, launches=len(layer._chunks(layer.kl_rows)),
+                                    rows_per_launch=layer.kl_rows,
                                     attend_standalone_ms=stage["attend_standalone"],
                                     vs_attend=fms / stage["attend_standalone"],
                                     hbm_gbps_algorithmic=attn_bytes / (fms * 1e-3) / 1e9,
@@ -598,6 +602,8 @@ def main():
                          "rows, then the attention")
     ap.add_argument("--attn-rows", type=int, default=None,
                     help="rows per sparse-attention launch (default: the layer's)")
+    ap.add_argument("--kl-rows", type=int, default=None,
+                    help="rows per launch of the attention fused with the KL (default: the layer's)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (scale of the HBM byte counters)")
     args = ap.parse_args()
@@ -614,7 +620,7 @@ def main():
         calibration_copy()
     pre, x = bench_prefill(args.workload, args.steps, args.warmup, with_dense=args.dense == "all",
                            with_distill=args.distill == "on", pipeline_rows=args.pipeline_rows,
-                           with_probe=True, attn_rows=args.attn_rows)
+                           with_probe=True, attn_rows=args.attn_rows, kl_rows=args.kl_rows)
     log(f"prefill {args.workload}: {pre['ms_per_step']:.2f} ms/step, stages {pre['stages_ms']}")
     st = pre["stages_ms"]
     # the dominant kernel of the step is the sparse attention (attn_launches

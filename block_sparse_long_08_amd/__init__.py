@@ -67,6 +67,7 @@ _sig("qsa_distill_kl", _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i
      _i32, _i32, _i32, _vp, _vp, _sz, _vp)
 _sig("qsa_sparse_attn_prefill_kl", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
      _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp)
+_sig("qsa_sparse_attn_prefill_concurrency", _i32, _i32, _i32, _i32, _i32)
 
 EXPORTED = ["qsa_status_string", "qsa_version", "qsa_check_device", "qsa_rope_bf16",
             "qsa_compress_keys", "qsa_index_scores", "qsa_topk_workspace_bytes",
@@ -74,7 +75,7 @@ EXPORTED = ["qsa_status_string", "qsa_version", "qsa_check_device", "qsa_rope_bf
             "qsa_sparse_attn_prefill", "qsa_decode_workspace_bytes", "qsa_sparse_attn_decode",
             "qsa_decode_noalloc_max_bytes", "qsa_sparse_attn_decode_noalloc",
             "dense_attn_workspace_bytes", "dense_attn", "qsa_distill_workspace_bytes",
-            "qsa_distill_kl", "qsa_sparse_attn_prefill_kl"]
+            "qsa_distill_kl", "qsa_sparse_attn_prefill_kl", "qsa_sparse_attn_prefill_concurrency"]
 
 SCORE_MAXHEAD, SCORE_RELUSUM = 0, 1
 KBAR_MEAN, KBAR_RMSNORM = 0, 1
@@ -348,6 +349,13 @@ def qsa_sparse_attn_prefill_kl(Q, K, V, q_idx, kbar, blk_idx, n_sel, Tq: int, Tk
     _call("qsa_sparse_attn_prefill_kl", _ptr(Q), _ptr(K), _ptr(V), _ptr(q_idx), _ptr(kbar),
           _ptr(blk_idx), _ptr(n_sel), Tq, Tk, pos0, H, Hkv, D, Hi, Di, r, Kbudget, score_mode,
           _ptr(O), _ptr(lse), _ptr(kl), _stream(stream))
+
+
+def qsa_sparse_attn_prefill_concurrency(Hkv: int, Kbudget: int, with_kl: bool = False,
+                                        paged: bool = False) -> int:
+    """Queries whose sparse-prefill workgroups the current device holds at
+    once (0: unsupported arguments, or the runtime cannot say)."""
+    return int(_lib.qsa_sparse_attn_prefill_concurrency(Hkv, Kbudget, int(with_kl), int(paged)))
 
 
 from .layer import QSAPrefill, QSADecode  # noqa: E402  (chains of the calls above)

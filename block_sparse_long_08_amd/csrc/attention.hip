@@ -730,6 +730,23 @@ hipError_t launch_sparse_prefill(const AttnArgs &a, hipStream_t s) {
 
 size_t sparse_prefill_kl_lds(int Kbudget) { return PrefillLds(2, Kbudget, true).total; }
 
+int sparse_prefill_concurrency(int Hkv, int Kbudget, bool kl, bool paged) {
+    const size_t lds = PrefillLds(Hkv, Kbudget, kl).total;
+    const void *fn = kl      ? reinterpret_cast<const void *>(&attn_prefill_kernel<false, true>)
+                     : paged ? reinterpret_cast<const void *>(&attn_prefill_kernel<true, false>)
+                             : reinterpret_cast<const void *>(&attn_prefill_kernel<false, false>);
+    if (kl && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  static_cast<int>(lds)) != hipSuccess)
+        return 0;
+    int per_cu = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * Hkv, lds) != hipSuccess)
+        return 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return per_cu * cus;
+}
+
 hipError_t launch_sparse_prefill_kl(const AttnArgs &a, hipStream_t s) {
     if (a.Tq == 0 || a.B == 0) return hipSuccess;
     const dim3 grid(static_cast<uint32_t>(a.Tq), static_cast<uint32_t>(a.B));

@@ -501,6 +501,12 @@ int qsa_distill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const float *lse, const
     return QSA_OK;
 }
 
+int qsa_sparse_attn_prefill_concurrency(int Hkv, int Kbudget, int with_kl, int paged) {
+    if ((Hkv != 1 && Hkv != 2 && Hkv != 4) || Kbudget <= 0 || Kbudget > kMaxBudget) return 0;
+    if (with_kl && (paged || Hkv != 2 || Kbudget > kMaxKlBudget)) return 0;
+    return sparse_prefill_concurrency(Hkv, Kbudget, with_kl != 0, paged != 0);
+}
+
 int qsa_sparse_attn_prefill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
                                const qsa_bf16 *q_idx, const qsa_bf16 *kbar,
                                const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq,

@@ -193,6 +193,10 @@ hipError_t launch_sparse_prefill(const AttnArgs &a, hipStream_t s);
 // dynamic LDS bytes it takes at a budget.
 hipError_t launch_sparse_prefill_kl(const AttnArgs &a, hipStream_t s);
 size_t sparse_prefill_kl_lds(int Kbudget);
+// Workgroups (one per query) of the sparse prefill (kl: fused with the KL;
+// paged: over page pools) resident at once on the current device: its
+// resident workgroups per CU times the CUs; 0 when the runtime cannot say.
+int sparse_prefill_concurrency(int Hkv, int Kbudget, bool kl, bool paged);
 // Decode: split-K workgroups per (split, KV head, column tile, sequence); a
 // column tile holds 16 (query, head) pairs of one KV head.
 int decode_col_tiles(int Tq, int group);

@@ -15,10 +15,12 @@ import torch
 
 from . import (DI, HI, R, SCORE_MAXHEAD, KBAR_MEAN, qsa_compress_keys, qsa_decode_workspace_bytes,
                qsa_rope_bf16, qsa_select_blocks, qsa_select_workspace_bytes,
-               qsa_sparse_attn_decode, qsa_sparse_attn_prefill, qsa_sparse_attn_prefill_kl)
+               qsa_sparse_attn_decode, qsa_sparse_attn_prefill, qsa_sparse_attn_prefill_concurrency,
+               qsa_sparse_attn_prefill_kl)
 
 
-# rows per sparse-attention launch of the prefill
+# rows per sparse-attention launch of the prefill when the device does not
+# report how many of its workgroups it holds at once
 ATTN_ROWS = 4096
 
 
@@ -36,8 +38,20 @@ class QSAPrefill:
 
     The selection of all rows runs first (one call; the library scores the
     rows in chunks of at most 8 GiB of scores), then the sparse attention in
-    launches of attn_rows rows (default 4,096: the 128K prefill's launches
-    take 48.7 ms in all against 62.5 ms as one launch of 131,072 rows).
+    launches of attn_rows rows.  By default a launch holds as many queries
+    as the device runs workgroups of the kernel at once (1,536 on MI355X at
+    Hkv = 2, budget 512): every query costs about the same, so workgroups run
+    in rounds of that size, and each query walks its block list in
+    ascending block order: within one round the concurrent gathers sweep the
+    cache as a narrow band, which L2 and the Infinity Cache hold.  Launches
+    that span several rounds let the workgroups drift apart and the band
+    widen.  The 128K prefill's attention takes 45.1 ms in 1,536-row
+    launches (caches serve 52% of the gathered bytes), 47.7 ms in 3,072-row
+    launches, 48.5 ms in 4,096-row launches (43%), 59.3 ms in 1,792-row
+    launches and 62.5 ms as one launch of 131,072 rows; attn_rows <= 0 asks
+    for that one launch.  The fused KL form (attend_with_kl) launches kl_rows
+    rows, by default the same count (its time is the same at 1,536 and
+    4,096 rows, 1% longer at its own 512).
     pipeline_rows > 0 (and < Tq) instead selects the queries in chunks of
     that many rows and runs each chunk's attention on a second stream while
     the next chunk is selected; the results are those of the stages run one
@@ -51,7 +65,7 @@ class QSAPrefill:
                  budget: int = 512, score_mode: int = SCORE_MAXHEAD, kbar_mode: int = KBAR_MEAN,
                  theta: float = 1e7, rope_dim: int = 64, fresh: bool = True,
                  idx_rope_dim: int = 0, kbar_gain=None, pages=None, pipeline_rows: int = 0,
-                 attn_rows: int = ATTN_ROWS, device="cuda"):
+                 attn_rows: int | None = None, kl_rows: int | None = None, device="cuda"):
         self.Tq, self.pos0, self.H, self.Hkv, self.D = Tq, pos0, H, Hkv, D
         self.pages = pages  # paged caches (fresh=False): K, V and kbar are page pools
         self.Tk = pos0 + Tq
@@ -71,7 +85,13 @@ class QSAPrefill:
         self.O = torch.empty((Tq, H, D), dtype=torch.float32, device=dev)
         self.lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
         self.pipeline_rows = pipeline_rows if 0 < pipeline_rows < Tq else 0
+        if attn_rows is None:
+            attn_rows = (qsa_sparse_attn_prefill_concurrency(Hkv, budget, paged=pages is not None)
+                         or ATTN_ROWS)
         self.attn_rows = self.pipeline_rows or (attn_rows if attn_rows > 0 else Tq)
+        if kl_rows is None:
+            kl_rows = qsa_sparse_attn_prefill_concurrency(Hkv, budget) or ATTN_ROWS
+        self.kl_rows = kl_rows if kl_rows > 0 else Tq
         self.ws_bytes = qsa_select_workspace_bytes(1, self.pipeline_rows or Tq, self.nb, budget)
         self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=dev)
         # the attention stream of the pipeline (default priority)
@@ -126,11 +146,10 @@ class QSAPrefill:
         """Training form of attend(), after select(): the sparse attention of
         every row fused with the distillation KL under the sparse pattern
         (kl: fp32 [Tq]); qi and kbar as given to the selection (qi after
-        rope_indexer).  Contiguous caches; the same row chunks as the
-        pipelined attention."""
+        rope_indexer).  Contiguous caches; launches of kl_rows rows."""
         if self.pages is not None:
             raise ValueError("attend_with_kl: the fused KL runs on contiguous caches only")
-        for r0, n in self.attn_chunks():
+        for r0, n in self._chunks(self.kl_rows):
             p0 = self.pos0 + r0
             qsa_sparse_attn_prefill_kl(self.Qr[r0:r0 + n], Kr, V, qi[r0:r0 + n], kbar,
                                        self.blk_idx[r0:r0 + n], self.n_sel[r0:r0 + n], n, p0 + n,

@@ -326,6 +326,19 @@ int qsa_sparse_attn_prefill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_b
                                int r, int Kbudget, int score_mode, float *O, float *lse,
                                float *kl, void *stream);
 
+/* ---- Launch sizing of the sparse prefill (A6; the same kernels as
+ * qsa_sparse_attn_prefill and, with with_kl, qsa_sparse_attn_prefill_kl;
+ * paged: over page pools).  Returns the number of queries whose workgroups
+ * (one per query) the current device holds at once: the kernel's resident
+ * workgroups per CU times the CUs (1,536 on MI355X for Hkv = 2 and budget
+ * 512).  Every query costs about the same at a full budget, so workgroups
+ * run in rounds of this size; a caller that splits a long prefill into
+ * launches of this many queries leaves no round partly empty.  Returns 0
+ * for unsupported arguments (Hkv not 1, 2 or 4; Kbudget outside 1..2048;
+ * with_kl with paged, Hkv != 2 or Kbudget > 1024) or when the runtime
+ * cannot say.  Enqueues nothing. */
+int qsa_sparse_attn_prefill_concurrency(int Hkv, int Kbudget, int with_kl, int paged);
+
 #ifdef __cplusplus
 }
 #endif

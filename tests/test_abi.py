@@ -278,6 +278,17 @@ def distill(lib, Q=P, K=P, lse=P, qi=P, kb=P, Tq=8, Tk=64, pos0=0, H=24, Hkv=2, 
                               None)
 
 
+def test_prefill_concurrency_validation(lib):
+    """Unsupported arguments return 0 before any runtime call."""
+    f = lib.qsa_sparse_attn_prefill_concurrency
+    assert f(3, 512, 0, 0) == 0          # Hkv not 1, 2 or 4
+    assert f(2, 0, 0, 0) == 0            # empty budget
+    assert f(2, 2049, 0, 0) == 0         # budget above 2,048
+    assert f(2, 512, 1, 1) == 0          # the fused KL runs on contiguous caches
+    assert f(1, 512, 1, 0) == 0          # ... over 2 KV heads
+    assert f(2, 1025, 1, 0) == 0         # ... at budgets up to 1,024
+
+
 def test_distill_validation(lib):
     lib.qsa_distill_workspace_bytes.restype = ctypes.c_size_t
     need = lib.qsa_distill_workspace_bytes(I64(8), I64(64))

@@ -113,6 +113,32 @@ def test_deterministic(qsa):
     assert np.array_equal(O1, O2) and np.array_equal(l1, l2)
 
 
+def test_launch_sizes_give_the_same_bits(qsa):
+    """The layer's default attention launch (the device's resident
+    workgroups: CUs times the kernel's workgroups per CU) and other launch
+    sizes, including one launch of all rows, give the same O and lse bits."""
+    torch = _torch()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    c = qsa.qsa_sparse_attn_prefill_concurrency(2, 64)
+    assert c > 0 and c % cus == 0
+    ckl = qsa.qsa_sparse_attn_prefill_concurrency(2, 64, with_kl=True)
+    assert 0 < ckl <= c and ckl % cus == 0
+    assert qsa.qsa_sparse_attn_prefill_concurrency(2, 64, paged=True) % cus == 0
+    log(f"  resident workgroups: {c} plain, {ckl} with the KL ({cus} CUs)")
+    T = 5000
+    x = synth.prefill_inputs(T, seed=8)
+    outs = []
+    for rows in (None, 0, 1000, 3333):
+        layer = qsa.QSAPrefill(T, budget=64, attn_rows=rows)
+        if rows is None:
+            assert layer.attn_rows == c
+        O, lse = layer(dev(x.Q), dev(x.K), dev(x.V), dev(x.qi), dev(x.ki))
+        torch.cuda.synchronize()
+        outs.append((O.cpu().numpy().copy(), lse.cpu().numpy().copy()))
+    for O, lse in outs[1:]:
+        assert np.array_equal(O, outs[0][0]) and np.array_equal(lse, outs[0][1])
+
+
 def test_chunked_prefill_matches_one_shot(qsa):
     """Two chunks against a post-RoPE cache reproduce the one-shot prefill."""
     torch = _torch()

@@ -196,7 +196,7 @@ def test_layer_attend_with_kl_in_row_chunks(qsa):
     import torch
     T = 3000
     x = synth.prefill_inputs(T, seed=99)
-    layer = qsa.QSAPrefill(T, pos0=0, budget=256, fresh=True, pipeline_rows=1024)
+    layer = qsa.QSAPrefill(T, pos0=0, budget=256, fresh=True, pipeline_rows=1024, kl_rows=1024)
     Q, K, V, qi, ki = (dev(a) for a in (x.Q, x.K, x.V, x.qi, x.ki))
     Kr, kb = layer.rope_and_pool(Q, K, ki, None)
     qs = layer.rope_indexer(qi)
@@ -231,7 +231,8 @@ def test_layer_attend_with_kl_chunk_over_a_cache(qsa):
     kc, vc = dev(x.K), dev(x.V)
     kbar = torch.full((Tk // 4, 128), -1, dtype=torch.int16, device="cuda")
     qsa.qsa_compress_keys(dev(x.ki), 1, pos0, pos0 * 128, 128, 4, 0, kbar, (pos0 // 4) * 128)
-    layer = qsa.QSAPrefill(Tq, pos0=pos0, budget=512, fresh=False, pipeline_rows=512)
+    layer = qsa.QSAPrefill(Tq, pos0=pos0, budget=512, fresh=False, pipeline_rows=512,
+                           kl_rows=512)
     qi = dev(x.qi)
     O, lse = layer(dev(x.Q), kc, vc, qi, dev(x.ki), kbar)
     O0, lse0 = O.clone(), lse.clone()
