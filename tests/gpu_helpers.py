@@ -168,17 +168,25 @@ def check_prefill_rows(O, lse, blk, nsel, Q, Kr, V, qi, kb, rows, pos0: int, bud
     return exempt
 
 
+def score_chunk_rows(Tq: int, nb: int) -> int:
+    """Rows per score chunk of the library's selection (at most 8 GiB of fp32
+    scores, whole 128-row indexer tiles)."""
+    ld = (max(nb, 1) + 3) // 4 * 4
+    return min(Tq, max(128, (1 << 33) // (ld * 4) // 128 * 128))
+
+
 def sample_prefill_rows(Tq: int, pos0: int, budget: int, n: int, seed: int,
-                        chunk_rows: int = 4096, r: int = 4):
+                        chunk_rows=(4096,), r: int = 4):
     """Rows of a prefill to check against the oracle: the first row whose
     context exceeds the budget, the first and last row of every chunk of
-    chunk_rows rows (the layer selects and attends in such chunks), at least
-    8 rows of each trailing-block length (p + 1) mod r, and seeded random
-    rows up to n in all."""
+    each size in chunk_rows (the layer's attention launches, the library's
+    score chunks), at least 8 rows of each trailing-block length
+    (p + 1) mod r, and seeded random rows up to n in all."""
     first = max(0, r * (budget + 1) - 1 - pos0)
     want = {first, Tq - 1}
-    for c0 in range(0, Tq, chunk_rows):
-        want.update((c0, min(c0 + chunk_rows, Tq) - 1))
+    for c in chunk_rows:
+        for c0 in range(0, Tq, c):
+            want.update((c0, min(c0 + c, Tq) - 1))
     rng = np.random.default_rng(seed)
     cand = np.arange(first, Tq)
     for res in range(r):

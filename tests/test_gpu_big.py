@@ -19,7 +19,7 @@ import pytest
 import oracle
 import synth
 from gpu_helpers import (assert_close, check_prefill_rows, check_selection, dev, log,
-                         sample_prefill_rows)
+                         sample_prefill_rows, score_chunk_rows)
 
 # the oracle's side of these checks runs on the host cores for up to a few
 # minutes per test (it prints a progress line per chunk of rows)
@@ -74,7 +74,7 @@ def _run_prefill(qsa, x, budget, pages=None):
     O, lse = layer(Q, K, V, qi, ki, kbar)
     torch.cuda.synchronize()
     out = (O.cpu().numpy(), lse.cpu().numpy(), layer.blk_idx.cpu().numpy(),
-           layer.n_sel.cpu().numpy())
+           layer.n_sel.cpu().numpy(), layer.attn_rows)
     del layer, Q, K, V, qi, ki, kbar, pg
     torch.cuda.empty_cache()
     return out
@@ -84,13 +84,16 @@ def _check_full_size(qsa, Tq, pos0, needles, nrows, pages=None):
     log(f"prefill Tq={Tq} pos0={pos0} needles={needles} pages={pages}: generating inputs")
     x = synth.prefill_inputs(Tq, pos0=pos0, seed=0, needles_per_head=needles)
     log("  running the HIP path")
-    O, lse, blk, nsel = _run_prefill(qsa, x, 512, pages=pages)
+    O, lse, blk, nsel, attn_rows = _run_prefill(qsa, x, 512, pages=pages)
     # every row: a full ascending selection of min(512, nc) blocks
     nc = np.minimum((pos0 + np.arange(Tq) + 1) // 4, (pos0 + Tq) // 4)
     assert np.array_equal(nsel, np.minimum(nc, 512))
     assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse))
+    # edges of the attention launches the layer made and of the score chunks
+    edges = (attn_rows, score_chunk_rows(Tq, (pos0 + Tq) // 4))
     rows = (np.arange(Tq, dtype=np.int64) if nrows is None
-            else sample_prefill_rows(Tq, pos0, 512, nrows, seed=Tq))
+            else sample_prefill_rows(Tq, pos0, 512, nrows, seed=Tq, chunk_rows=edges))
+    log(f"  attention launches of {attn_rows} rows, score chunks of {edges[1]} rows")
     log(f"  oracle check of {rows.size} rows")
     Kr = x.K if x.k_is_rotated else oracle.rope(x.K)
     kb = oracle.compress(x.ki)
