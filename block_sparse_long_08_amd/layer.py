@@ -20,8 +20,10 @@ from . import (DI, HI, R, SCORE_MAXHEAD, KBAR_MEAN, qsa_compress_keys, qsa_decod
 
 
 # rows per sparse-attention launch of the prefill when the device does not
-# report how many of its workgroups it holds at once
+# report how many of its workgroups it holds at once, or when one round of
+# them would select each cached block fewer than SWEEP_REUSE times
 ATTN_ROWS = 4096
+SWEEP_REUSE = 8
 
 
 class QSAPrefill:
@@ -49,7 +51,11 @@ class QSAPrefill:
     launches (caches serve 52% of the gathered bytes), 47.7 ms in 3,072-row
     launches, 48.5 ms in 4,096-row launches (43%), 59.3 ms in 1,792-row
     launches and 62.5 ms as one launch of 131,072 rows; attn_rows <= 0 asks
-    for that one launch.  The fused KL form (attend_with_kl) launches kl_rows
+    for that one launch.  The sweep pays only when a round's selections
+    repeat each cached block: 1,536 x 512 selections over 32,768 blocks
+    come to 24 per block at 128K, but 3 at a 1M-token context, where 4,096-
+    row launches are faster (3.91 against 4.03 ms per 8,192 queries); the
+    default takes one-round launches at 8 or more per block.  The fused KL form (attend_with_kl) launches kl_rows
     rows, by default the same count (its time is the same at 1,536 and
     4,096 rows, 1% longer at its own 512).
     pipeline_rows > 0 (and < Tq) instead selects the queries in chunks of
@@ -86,8 +92,12 @@ class QSAPrefill:
         self.lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
         self.pipeline_rows = pipeline_rows if 0 < pipeline_rows < Tq else 0
         if attn_rows is None:
-            attn_rows = (qsa_sparse_attn_prefill_concurrency(Hkv, budget, paged=pages is not None)
-                         or ATTN_ROWS)
+            conc = qsa_sparse_attn_prefill_concurrency(Hkv, budget, paged=pages is not None)
+            # one round per launch when a round's selections hit each cached
+            # block several times over (the in-step sweep pays), else
+            # larger launches (fewer launch tails)
+            attn_rows = (conc if conc > 0 and conc * budget >= SWEEP_REUSE * max(self.nb, 1)
+                         else max(conc, ATTN_ROWS))
         self.attn_rows = self.pipeline_rows or (attn_rows if attn_rows > 0 else Tq)
         if kl_rows is None:
             kl_rows = qsa_sparse_attn_prefill_concurrency(Hkv, budget) or ATTN_ROWS
