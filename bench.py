@@ -263,7 +263,7 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
     probe_ms = gather_ceiling(layer, Kr0, V, reps) if with_probe else None
     res = dict(ms_per_step=wall * 1e3, stages_ms=stage, Tq=Tq, Tk=Tk, budget=budget,
                attn_launches=nlaunch, pipeline_rows=layer.pipeline_rows,
-               attn_rows=layer.attn_rows)
+               attn_rows=layer.attn_rows, q_rope_on_load=layer.rope_on_load)
     res["attend_launch_ms"] = (att_ms if pipe else stage["attend"]) / nlaunch
     if probe_ms is not None:
         res["gather_probe_ms"] = probe_ms

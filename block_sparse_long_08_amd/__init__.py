@@ -53,6 +53,8 @@ _sig("qsa_select_blocks", _i32, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _i32, _i3
      _i32, _vp, _vp, _vp, _sz, _vp, _vp)
 _sig("qsa_sparse_attn_prefill", _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
      _i32, _i32, _vp, _vp, _vp, _vp)
+_sig("qsa_sparse_attn_prefill_rope", _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
+     _i32, _i32, _i32, _i32, _dbl, _vp, _vp, _vp, _vp)
 _sig("qsa_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32, _i32)
 _sig("qsa_sparse_attn_decode", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32,
      _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp, _vp)
@@ -72,7 +74,8 @@ _sig("qsa_sparse_attn_prefill_concurrency", _i32, _i32, _i32, _i32, _i32)
 EXPORTED = ["qsa_status_string", "qsa_version", "qsa_check_device", "qsa_rope_bf16",
             "qsa_compress_keys", "qsa_index_scores", "qsa_topk_workspace_bytes",
             "qsa_topk_blocks", "qsa_select_workspace_bytes", "qsa_select_blocks",
-            "qsa_sparse_attn_prefill", "qsa_decode_workspace_bytes", "qsa_sparse_attn_decode",
+            "qsa_sparse_attn_prefill", "qsa_sparse_attn_prefill_rope",
+            "qsa_decode_workspace_bytes", "qsa_sparse_attn_decode",
             "qsa_decode_noalloc_max_bytes", "qsa_sparse_attn_decode_noalloc",
             "dense_attn_workspace_bytes", "dense_attn", "qsa_distill_workspace_bytes",
             "qsa_distill_kl", "qsa_sparse_attn_prefill_kl", "qsa_sparse_attn_prefill_concurrency"]
@@ -250,6 +253,22 @@ def qsa_sparse_attn_prefill(Q, K, V, blk_idx, n_sel, Tq: int, Tk: int, pos0: int
     _req(f, "lse", lse, 4, Tq * H * 4)
     _call("qsa_sparse_attn_prefill", _ptr(Q), _ptr(K), _ptr(V), _ptr(blk_idx), _ptr(n_sel), Tq,
           Tk, pos0, H, Hkv, D, r, Kbudget, _ptr(O), _ptr(lse), _pages(pages), _stream(stream))
+
+
+def qsa_sparse_attn_prefill_rope(Q, K, V, blk_idx, n_sel, Tq: int, Tk: int, pos0: int, H: int,
+                                 Hkv: int, D: int, r: int, Kbudget: int, rope_dim: int,
+                                 theta: float, O, lse=None, stream=None, pages=None) -> None:
+    """qsa_sparse_attn_prefill with Q before RoPE: the kernel rotates it on load."""
+    f = "qsa_sparse_attn_prefill_rope"
+    _req(f, "Q", Q, 2, Tq * H * D * 2)
+    _req(f, "K", K, 2, 2 if pages is not None else Tk * Hkv * D * 2)
+    _req(f, "V", V, 2, 2 if pages is not None else Tk * Hkv * D * 2)
+    _req(f, "blk_idx", blk_idx, 4, Tq * Kbudget * 4)
+    _req(f, "n_sel", n_sel, 4, Tq * 4)
+    _req(f, "O", O, 4, Tq * H * D * 4)
+    _req(f, "lse", lse, 4, Tq * H * 4)
+    _call(f, _ptr(Q), _ptr(K), _ptr(V), _ptr(blk_idx), _ptr(n_sel), Tq, Tk, pos0, H, Hkv, D, r,
+          Kbudget, rope_dim, float(theta), _ptr(O), _ptr(lse), _pages(pages), _stream(stream))
 
 
 def qsa_decode_workspace_bytes(B: int, Tq: int, H: int, Hkv: int, D: int, Kbudget: int) -> int:

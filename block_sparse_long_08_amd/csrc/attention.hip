@@ -268,23 +268,57 @@ __device__ __forceinline__ float attn_stage(const EntryList<MULTI, PMODE> &L, in
     return stage_compute<true>(L, e0, pq, kb, qT, st, vlds, lane);
 }
 
+// Two bf16 of a 32-bit word each: the pairs (dims j, j+1 of word a) and their
+// partners (the same elements of word b).
+__device__ __forceinline__ void rope_word(uint32_t &a, uint32_t &b, const double *ang, int j) {
+    uint16_t a0, a1, b0, b1;
+    rope_pair(static_cast<uint16_t>(a & 0xFFFFu), static_cast<uint16_t>(b & 0xFFFFu), ang[j],
+              ang[64 + j], a0, b0);
+    rope_pair(static_cast<uint16_t>(a >> 16), static_cast<uint16_t>(b >> 16), ang[j + 1],
+              ang[65 + j], a1, b1);
+    a = static_cast<uint32_t>(a0) | (static_cast<uint32_t>(a1) << 16);
+    b = static_cast<uint32_t>(b0) | (static_cast<uint32_t>(b1) << 16);
+}
+
+// Dims j .. j+7 (fragment a) rotated with their partners (fragment b).
+__device__ __forceinline__ void rope_quad(uint4 &a, uint4 &b, const double *ang, int j) {
+    rope_word(a.x, b.x, ang, j);
+    rope_word(a.y, b.y, ang, j + 2);
+    rope_word(a.z, b.z, ang, j + 4);
+    rope_word(a.w, b.w, ang, j + 6);
+}
+
 // Q^T fragments of column tile ct of KV head g: column n is the pair
 // 16*ct + n = (query qi, head h of the group), query rows H * kHeadDim apart;
-// columns past ncols pairs are zero.
+// columns past ncols pairs are zero.  Lane (n, g4) holds dims 32 s + 8 g4 + k
+// (k < 8) in qT[s].  With ang (cosines [0, 64), sines [64, 128) of the
+// single query's angles) the first 64 * hs dims are rotated on load: the
+// NeoX partner of dim j < 32 hs is j + 32 hs, element k of qT[s + hs], so
+// every pair sits in one lane (hs = 1 or 2: rope_dim 64 or 128).
 __device__ __forceinline__ void load_qT(const uint16_t *__restrict__ qrow, int g, int group,
-                                        int H, int ct, int ncols, int lane, bf16x8 (&qT)[8]) {
+                                        int H, int ct, int ncols, int lane, bf16x8 (&qT)[8],
+                                        const double *ang = nullptr, int hs = 0) {
     const int n = lane & 15, g4 = lane >> 4;
     const int pair = 16 * ct + n;
     const bool ok = pair < ncols;
     const int qi = ok ? pair / group : 0, h = ok ? pair - qi * group : 0;
     const uint16_t *src =
         qrow + (static_cast<int64_t>(qi) * H + g * group + h) * kHeadDim;
+    uint4 v[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        uint4 v = ok ? *reinterpret_cast<const uint4 *>(src + 32 * s + 8 * g4)
-                     : make_uint4(0, 0, 0, 0);
-        qT[s] = as_bf16x8(v);
+    for (int s = 0; s < 8; ++s)
+        v[s] = ok ? *reinterpret_cast<const uint4 *>(src + 32 * s + 8 * g4)
+                  : make_uint4(0, 0, 0, 0);
+    if (ang && ok) {
+        if (hs == 1) {
+            rope_quad(v[0], v[1], ang, 8 * g4);
+        } else {
+            rope_quad(v[0], v[2], ang, 8 * g4);
+            rope_quad(v[1], v[3], ang, 32 + 8 * g4);
+        }
     }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qT[s] = as_bf16x8(v[s]);
 }
 
 __device__ __forceinline__ void state_store(const WaveState &st, float *buf, int lane) {
@@ -356,14 +390,18 @@ constexpr int kKlGroup = 12;  // query heads per KV head (24 / 2)
 // maxima [Hkv][Kbudget][12], the per-wave head sums [Hkv][Kbudget], the
 // selected blocks' indexer scores [Kbudget] and 16 floats of reduction space.
 struct PrefillLds {
-    size_t list, mx, part, score, red, total;
+    size_t list, mx, ang, part, score, red, total;
     __host__ __device__ PrefillLds(int Hkv, int Kbudget, bool kl) {
-        list = static_cast<size_t>(Hkv) * kVStageBytes;
+        // the plain forms run one wave per workgroup, the KL form one per KV head
+        list = static_cast<size_t>(kl ? Hkv : 1) * kVStageBytes;
         mx = list + ((4 * (static_cast<size_t>(Kbudget) + 1) + 15) & ~size_t(15));
         if (!kl) {
-            part = score = red = total = mx;
+            // the plain forms: the query's RoPE angles (64 cosines, 64 sines)
+            ang = mx;
+            part = score = red = total = ang + 128 * sizeof(double);
             return;
         }
+        ang = mx;
         part = mx + 4 * static_cast<size_t>(Hkv) * kKlGroup * Kbudget;
         score = part + 4 * static_cast<size_t>(Hkv) * Kbudget;
         red = score + 4 * static_cast<size_t>(Kbudget);
@@ -411,8 +449,15 @@ __device__ __forceinline__ void tile_scores(const uint16_t *__restrict__ qi_row,
 }
 
 // ------------------------------------------------------------------------
-// Prefill: one workgroup per query, one wave per KV head; each wave walks all
-// stages of its head.  Grid: (Tq, B); block: 64 * Hkv threads.
+// Prefill: one wave per (query, KV head), walking all stages of its head.
+// Plain forms: one wave per workgroup, workgroup w = Hkv * query + head, grid
+// (Tq * Hkv, B), block 64.  Workgroups are dealt to the 8 XCDs in turn, so
+// with Hkv | 8 each XCD serves one KV head only and its L2 holds that head's
+// rows alone: the gathers of one head by the queries running together hit
+// in L2 about twice as often as when every XCD fetches both heads (a
+// loads-only probe of the 128K workload: 41 against 49 ms per step).
+// KL form: one workgroup per query, one wave per KV head (the waves share the
+// query's block masses), grid (Tq, B), block 64 * Hkv.
 // Dynamic LDS: PrefillLds.
 // PAGED: K and V are page pools; the list is translated to pool blocks once
 // (the tail block as entry ns).
@@ -423,12 +468,12 @@ __device__ __forceinline__ void tile_scores(const uint16_t *__restrict__ qi_row,
 // keep 1.5x the stages in flight: 13% faster than 2 waves per SIMD); the KL
 // form is held to 2 workgroups per CU by its LDS anyway.
 template <bool PAGED, bool KL>
-__global__ void __launch_bounds__(256, KL ? 1 : 3) attn_prefill_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256, KL ? 1 : 3) attn_prefill_kernel(AttnArgs a, RopeArgs ra) {
     static_assert(!(PAGED && KL), "the fused KL runs on contiguous caches");
     extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
     const PrefillLds lay(a.Hkv, a.Kbudget, KL);
     int32_t *lst = reinterpret_cast<int32_t *>(dyn_lds + lay.list);
-    const int64_t t = blockIdx.x, b = blockIdx.y;
+    const int64_t t = KL ? blockIdx.x : blockIdx.x / a.Hkv, b = blockIdx.y;
     const int64_t row = b * a.Tq + t;
     int64_t p = a.pos0 + t;
     const int64_t nc = num_complete_blocks(p, kBlock);
@@ -445,16 +490,21 @@ __global__ void __launch_bounds__(256, KL ? 1 : 3) attn_prefill_kernel(AttnArgs 
     const int tail = static_cast<int>((p + 1) % kBlock);
     if (PAGED && threadIdx.x == 0 && tail > 0)
         lst[ns] = static_cast<int32_t>(page_row(ptab, a.pshift, 4 * nc) >> 2);
+    double *ang = KL ? nullptr : reinterpret_cast<double *>(dyn_lds + lay.ang);
+    if (!KL && static_cast<int>(threadIdx.x) < ra.half)
+        rope_angle(p < 0 ? 0 : p, ra.inv_freq[threadIdx.x], ang[threadIdx.x], ang[64 + threadIdx.x]);
     block_sync();
     EntryList<false, PAGED ? 1 : 0> L{lst, 0, ns, tail, nc};
     if (PAGED) p = page_row(ptab, a.pshift, p);  // the safe row for masked tokens
     const int E = ns + (L.tail > 0 ? 1 : 0);
     const int nstages = (E + kStageEntries - 1) / kStageEntries;
 
-    const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int g = KL ? static_cast<int>(threadIdx.x >> 6) : static_cast<int>(blockIdx.x - t * a.Hkv);
     const int group = a.H / a.Hkv;
     bf16x8 qT[8];
-    load_qT(a.Q + row * a.H * kHeadDim, g, group, a.H, 0, group, lane, qT);
+    load_qT(a.Q + row * a.H * kHeadDim, g, group, a.H, 0, group, lane, qT,
+            ra.half > 0 ? ang : nullptr, ra.half / 32);
     const int64_t rs = static_cast<int64_t>(a.Hkv) * kHeadDim;
     const int64_t seq_off = PAGED ? 0 : b * a.Lmax * rs;
     const uint16_t *Kg = a.K + seq_off + g * kHeadDim;
@@ -465,7 +515,7 @@ __global__ void __launch_bounds__(256, KL ? 1 : 3) attn_prefill_kernel(AttnArgs 
     const int n = lane & 15, g4 = lane >> 4;
     float *mxw = reinterpret_cast<float *>(dyn_lds + lay.mx) +
                  static_cast<int64_t>(g) * a.Kbudget * kKlGroup;
-    unsigned char *vl = dyn_lds + g * kVStageBytes;
+    unsigned char *vl = dyn_lds + (KL ? g : 0) * kVStageBytes;
     if constexpr (!KL) {
         for (int sidx = 0; sidx < nstages; ++sidx)
             attn_stage(L, sidx * kStageEntries, p, pq, Kg, Vg, rs, qT, st, vl, lane);
@@ -716,15 +766,16 @@ __global__ void __launch_bounds__(256) attn_decode_merge(AttnArgs a, int nsplit,
     if (a.lse && d == 0) a.lse[bq * a.H + hq] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
 }
 
-hipError_t launch_sparse_prefill(const AttnArgs &a, hipStream_t s) {
+hipError_t launch_sparse_prefill(const AttnArgs &a, const RopeArgs &ra, hipStream_t s) {
     if (a.Tq == 0 || a.B == 0) return hipSuccess;
-    const dim3 grid(static_cast<uint32_t>(a.Tq), static_cast<uint32_t>(a.B));
+    if (ra.half != 0 && ra.half != 32 && ra.half != 64) return hipErrorInvalidValue;
+    if (a.Tq * a.Hkv > kMaxPrefillWaves) return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<uint32_t>(a.Tq * a.Hkv), static_cast<uint32_t>(a.B));
     const size_t lds = PrefillLds(a.Hkv, a.Kbudget, false).total;
     if (a.ptable)
-        hipLaunchKernelGGL((attn_prefill_kernel<true, false>), grid, dim3(64 * a.Hkv), lds, s, a);
+        hipLaunchKernelGGL((attn_prefill_kernel<true, false>), grid, dim3(kWave), lds, s, a, ra);
     else
-        hipLaunchKernelGGL((attn_prefill_kernel<false, false>), grid, dim3(64 * a.Hkv), lds, s,
-                           a);
+        hipLaunchKernelGGL((attn_prefill_kernel<false, false>), grid, dim3(kWave), lds, s, a, ra);
     return hipGetLastError();
 }
 
@@ -739,12 +790,14 @@ int sparse_prefill_concurrency(int Hkv, int Kbudget, bool kl, bool paged) {
                                   static_cast<int>(lds)) != hipSuccess)
         return 0;
     int per_cu = 0, dev = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * Hkv, lds) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kl ? 64 * Hkv : kWave, lds) !=
+        hipSuccess)
         return 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    return per_cu * cus;
+    // queries: the plain forms run Hkv workgroups per query
+    return kl ? per_cu * cus : per_cu * cus / Hkv;
 }
 
 hipError_t launch_sparse_prefill_kl(const AttnArgs &a, hipStream_t s) {
@@ -755,7 +808,9 @@ hipError_t launch_sparse_prefill_kl(const AttnArgs &a, hipStream_t s) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_prefill_kernel<false, true>), grid, dim3(64 * a.Hkv), lds, s, a);
+    RopeArgs none{};
+    hipLaunchKernelGGL((attn_prefill_kernel<false, true>), grid, dim3(64 * a.Hkv), lds, s, a,
+                       none);
     return hipGetLastError();
 }
 

@@ -5,26 +5,6 @@
 
 namespace qsa {
 
-// Round a finite double to bf16 (nearest, ties to even) by integer
-// manipulation of its bits.
-__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
-    uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
-    uint32_t sign = static_cast<uint32_t>(u >> 63) << 15;
-    int e = static_cast<int>((u >> 52) & 0x7FF) - 1023;
-    if (x == 0.0) return static_cast<uint16_t>(sign);
-    if (e < -126) {
-        // bf16 subnormal range: quantum 2^-133
-        double n = rint(fabs(x) * 0x1p133);
-        return static_cast<uint16_t>(sign | static_cast<uint32_t>(n));
-    }
-    uint64_t mant = u & ((1ull << 52) - 1);
-    uint32_t top = (static_cast<uint32_t>(e + 127) << 7) | static_cast<uint32_t>(mant >> 45);
-    uint64_t rem = mant & ((1ull << 45) - 1);
-    const uint64_t half = 1ull << 44;
-    if (rem > half || (rem == half && (top & 1u))) top += 1;
-    return static_cast<uint16_t>(sign | top);
-}
-
 struct InvFreq {
     double v[64];
 };
@@ -74,13 +54,7 @@ __global__ void __launch_bounds__(256) rope_kernel(const uint16_t *__restrict__ 
     // positions of that sequence
     int64_t p = seq_len ? seq_len[t / nq] - nq + t % nq : pos0 + t;
     if (p < 0) p = 0;
-    for (int j = threadIdx.x; j < half; j += blockDim.x) {
-        double ang = static_cast<double>(p) * inv_freq.v[j];
-        double s, c;
-        sincos(ang, &s, &c);
-        cs[j] = c;
-        sn[j] = s;
-    }
+    for (int j = threadIdx.x; j < half; j += blockDim.x) rope_angle(p, inv_freq.v[j], cs[j], sn[j]);
     block_sync();
     for (int idx = threadIdx.x, u = 0; idx < npairs; idx += blockDim.x, ++u) {
         int h = idx / half, j = idx - h * half;
@@ -88,12 +62,8 @@ __global__ void __launch_bounds__(256) rope_kernel(const uint16_t *__restrict__ 
         const uint16_t ra = u < kRopePairsPerThread ? pa[u & (kRopePairsPerThread - 1)] : xh[j];
         const uint16_t rb =
             u < kRopePairsPerThread ? pb[u & (kRopePairsPerThread - 1)] : xh[j + half];
-        double a = static_cast<double>(bf16_bits_to_f32(ra));
-        double b = static_cast<double>(bf16_bits_to_f32(rb));
-        double c = cs[j], s = sn[j];
-        double ac = a * c, bs = b * s, bc = b * c, as = a * s;
-        uint16_t o0 = f64_to_bf16_rne(ac - bs);
-        uint16_t o1 = f64_to_bf16_rne(bc + as);
+        uint16_t o0, o1;
+        rope_pair(ra, rb, cs[j], sn[j], o0, o1);
         yr[h * head_dim + j] = o0;
         yr[h * head_dim + j + half] = o1;
     }

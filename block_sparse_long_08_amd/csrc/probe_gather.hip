@@ -5,12 +5,13 @@
 // 4-token blocks and the query's incomplete block; per stage the value rows
 // by LDS DMA into an 8 KB tile (16-byte chunks at the same XOR-swizzled
 // slots) and the key rows into registers with the same lane map -- with the
-// same grid (one workgroup per query, one wave per KV head) and one stage
-// in flight per wave, and does no arithmetic but folding the key words into
-// one word per (query, head).  It needs few registers, so up to five waves
-// per SIMD run; a caller can hold it to fewer (the attention's three) with
-// padding LDS.  Its time per launch is what the memory system needs for the
-// attention's loads without their arithmetic.
+// same grid (one one-wave workgroup per query and KV head, workgroup
+// Hkv * query + head) and one stage in flight per wave, and does no
+// arithmetic but folding the key words into one word per (query, head).  It
+// needs few registers, so up to five waves per SIMD run; a caller can hold it
+// to fewer (the attention's three) with padding LDS.  Its time per launch is
+// what the memory system needs for the attention's loads without their
+// arithmetic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -67,12 +68,13 @@ __device__ __forceinline__ uint32_t stage(const Entries &L, int e0, int64_t p,
     return x;
 }
 
-__global__ void __launch_bounds__(128) gather_probe_kernel(
+__global__ void __launch_bounds__(64) gather_probe_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const int32_t *__restrict__ blk_idx, const int32_t *__restrict__ n_sel, int64_t pos0,
     int Kbudget, int Hkv, uint32_t *__restrict__ out) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char tiles[];  // 2 x 8 KB (+ padding)
-    const int64_t t = blockIdx.x;
+    extern __shared__ __attribute__((aligned(16))) unsigned char tile[];  // 8 KB (+ padding)
+    const int64_t t = blockIdx.x / Hkv;
+    const int g = static_cast<int>(blockIdx.x - t * Hkv);
     const int64_t p = pos0 + t;
     const int64_t nc = (p + 1) / kBlock;
     const int v = n_sel[t];
@@ -81,11 +83,10 @@ __global__ void __launch_bounds__(128) gather_probe_kernel(
     const Entries L{blk_idx + t * Kbudget, ns, static_cast<int>((p + 1) % kBlock), nc};
     const int E = ns + (L.tail > 0 ? 1 : 0);
     const int nstages = (E + 3) / 4;
-    const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int64_t rs = static_cast<int64_t>(Hkv) * kHeadDim;
     const uint16_t *Kg = K + g * kHeadDim;
     const uint16_t *Vg = V + g * kHeadDim;
-    unsigned char *tile = tiles + 8192 * g;
     uint32_t acc = 0;
     for (int s = 0; s < nstages; ++s) acc ^= stage(L, 4 * s, p, Kg, Vg, rs, tile, lane);
 #pragma unroll
@@ -100,21 +101,22 @@ extern "C" {
 // Gathers of the sparse prefill attention of Tq queries at pos0 .. pos0+Tq-1
 // over contiguous K, V [Tk][Hkv][256] (bf16 bits) for the selection blk_idx
 // [Tq][Kbudget] / n_sel [Tq]; out: [Tq][Hkv] words.  waves_per_simd 1..5
-// holds the kernel to that many waves per SIMD (by the LDS of a workgroup of
-// Hkv waves: 160 KB per CU); 0 leaves it free.  Device pointers; the call
+// holds the kernel to that many waves per SIMD (by the LDS of its one-wave
+// workgroups: 160 KB per CU); 0 leaves it free.  Device pointers; the call
 // enqueues one launch on stream and returns 0, or 1 when the launch was
 // rejected or an argument is out of range.
 int qsa_probe_gather(const uint16_t *K, const uint16_t *V, const int32_t *blk_idx,
                      const int32_t *n_sel, int64_t Tq, int64_t pos0, int Kbudget, int Hkv,
                      int waves_per_simd, uint32_t *out, void *stream) {
     if (!K || !V || !blk_idx || !n_sel || !out || Tq < 0 || pos0 < 0 || Kbudget <= 0 ||
-        Hkv < 1 || Hkv > 2 || Tq > 2147483647 || waves_per_simd < 0 || waves_per_simd > 5)
+        Hkv < 1 || Hkv > 2 || Tq >= (int64_t(1) << 25) || waves_per_simd < 0 ||
+        waves_per_simd > 5)
         return 1;
     if (Tq == 0) return 0;
-    size_t lds = static_cast<size_t>(Hkv) * 8192;
+    size_t lds = 8192;
     if (waves_per_simd > 0) {
-        // workgroups per CU = 4 SIMDs x waves per SIMD / waves per workgroup
-        const size_t wgs = static_cast<size_t>(4 * waves_per_simd / Hkv);
+        // workgroups per CU = 4 SIMDs x waves per SIMD
+        const size_t wgs = static_cast<size_t>(4 * waves_per_simd);
         // wgs fit in 160 KB, wgs + 1 do not
         const size_t need = (160 * 1024) / (wgs + 1) + 16;
         lds = need > lds ? need : lds;
@@ -123,7 +125,7 @@ int qsa_probe_gather(const uint16_t *K, const uint16_t *V, const int32_t *blk_id
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return 1;
-    hipLaunchKernelGGL(gather_probe_kernel, dim3(static_cast<uint32_t>(Tq)), dim3(64 * Hkv), lds,
+    hipLaunchKernelGGL(gather_probe_kernel, dim3(static_cast<uint32_t>(Tq * Hkv)), dim3(64), lds,
                        reinterpret_cast<hipStream_t>(stream), K, V, blk_idx, n_sel, pos0, Kbudget,
                        Hkv, out);
     return hipGetLastError() == hipSuccess ? 0 : 1;

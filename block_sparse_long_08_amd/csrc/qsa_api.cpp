@@ -316,10 +316,11 @@ int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_
     return QSA_OK;
 }
 
-int qsa_sparse_attn_prefill(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
-                            const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq, int64_t Tk,
-                            int64_t pos0, int H, int Hkv, int D, int r, int Kbudget, float *O,
-                            float *lse, const qsa_pages *pages, void *stream) {
+static int sparse_prefill(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
+                          const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq, int64_t Tk,
+                          int64_t pos0, int H, int Hkv, int D, int r, int Kbudget,
+                          const RopeArgs &ra, float *O, float *lse, const qsa_pages *pages,
+                          void *stream) {
     if (!Q || !K || !V || !blk_idx || !n_sel || !O) return QSA_ERR_NULL;
     if (Tq < 0 || Tk < 0 || pos0 < 0 || Kbudget <= 0) return QSA_ERR_SHAPE;
     int st = check_attn_shape(H, Hkv, D, r);
@@ -327,6 +328,7 @@ int qsa_sparse_attn_prefill(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16
     if (Tk < pos0 + Tq) return QSA_ERR_SHAPE;
     if (Kbudget > kMaxBudget) return QSA_ERR_UNSUPPORTED;
     if (Tq > kI32Max || Tk / kBlock > kI32Max) return QSA_ERR_OVERFLOW;
+    if (Tq * Hkv > kMaxPrefillWaves) return QSA_ERR_OVERFLOW;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return QSA_ERR_ALIGN;
     AttnArgs a{};
     a.Q = Q; a.K = K; a.V = V; a.blk_idx = blk_idx; a.n_sel = n_sel; a.seq_len = nullptr;
@@ -336,7 +338,32 @@ int qsa_sparse_attn_prefill(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16
     if (st != QSA_OK) return st;
     const PageTable pt = token_pages(pages);
     a.ptable = pt.table; a.pstride = pt.stride; a.pshift = pt.shift;
-    return launch_status(launch_sparse_prefill(a, as_stream(stream)));
+    return launch_status(launch_sparse_prefill(a, ra, as_stream(stream)));
+}
+
+int qsa_sparse_attn_prefill(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
+                            const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq, int64_t Tk,
+                            int64_t pos0, int H, int Hkv, int D, int r, int Kbudget, float *O,
+                            float *lse, const qsa_pages *pages, void *stream) {
+    RopeArgs none{};
+    return sparse_prefill(Q, K, V, blk_idx, n_sel, Tq, Tk, pos0, H, Hkv, D, r, Kbudget, none, O,
+                          lse, pages, stream);
+}
+
+int qsa_sparse_attn_prefill_rope(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
+                                 const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq,
+                                 int64_t Tk, int64_t pos0, int H, int Hkv, int D, int r,
+                                 int Kbudget, int rope_dim, double theta, float *O, float *lse,
+                                 const qsa_pages *pages, void *stream) {
+    if (rope_dim <= 0 || !(theta > 0.0)) return QSA_ERR_SHAPE;
+    if (rope_dim != 64 && rope_dim != 128) return QSA_ERR_UNSUPPORTED;
+    RopeArgs ra{};
+    ra.half = rope_dim / 2;
+    // the angles' frequencies exactly as qsa_rope_bf16 forms them
+    for (int j = 0; j < ra.half; ++j)
+        ra.inv_freq[j] = pow(theta, -2.0 * static_cast<double>(j) / static_cast<double>(rope_dim));
+    return sparse_prefill(Q, K, V, blk_idx, n_sel, Tq, Tk, pos0, H, Hkv, D, r, Kbudget, ra, O, lse,
+                          pages, stream);
 }
 
 // Split count and workspace bytes of the decode attention: one record per
@@ -524,6 +551,7 @@ int qsa_sparse_attn_prefill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_b
                           score_mode);
     if (st != QSA_OK) return st;
     if (Tq > kI32Max || nb_max > kI32Max) return QSA_ERR_OVERFLOW;
+    if (Tq * Hkv > kMaxPrefillWaves) return QSA_ERR_OVERFLOW;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return QSA_ERR_ALIGN;
     AttnArgs a{};
     a.Q = Q; a.K = K; a.V = V; a.blk_idx = blk_idx; a.n_sel = n_sel; a.seq_len = nullptr;

@@ -14,6 +14,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
+// waves of one prefill attention launch (Tq * Hkv): a dispatch holds fewer
+// than 2^32 threads
+constexpr int64_t kMaxPrefillWaves = (int64_t(1) << 26) - 1;
 
 // Tuned shapes.
 constexpr int kHeadDim = 256;   // attention head dim
@@ -25,6 +28,56 @@ constexpr int kBlock = 4;       // micro-block size r
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
+
+// Round a finite double to bf16 (nearest, ties to even) by integer
+// manipulation of its bits.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+    uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+    uint32_t sign = static_cast<uint32_t>(u >> 63) << 15;
+    int e = static_cast<int>((u >> 52) & 0x7FF) - 1023;
+    if (x == 0.0) return static_cast<uint16_t>(sign);
+    if (e < -126) {
+        // bf16 subnormal range: quantum 2^-133
+        double n = rint(fabs(x) * 0x1p133);
+        return static_cast<uint16_t>(sign | static_cast<uint32_t>(n));
+    }
+    uint64_t mant = u & ((1ull << 52) - 1);
+    uint32_t top = (static_cast<uint32_t>(e + 127) << 7) | static_cast<uint32_t>(mant >> 45);
+    uint64_t rem = mant & ((1ull << 45) - 1);
+    const uint64_t half = 1ull << 44;
+    if (rem > half || (rem == half && (top & 1u))) top += 1;
+    return static_cast<uint16_t>(sign | top);
+}
+
+// Partial RoPE of one NeoX pair (a at dim j, b at dim j + rope_dim / 2)
+// with the angle's cosine c and sine s: fp64 products, no contraction, one
+// RNE rounding per output.  Every kernel that rotates uses this, so their
+// results agree bit for bit.
+__device__ __forceinline__ void rope_pair(uint16_t a_bits, uint16_t b_bits, double c, double s,
+                                          uint16_t &o0, uint16_t &o1) {
+#pragma clang fp contract(off)
+    const double a = static_cast<double>(bf16_bits_to_f32(a_bits));
+    const double b = static_cast<double>(bf16_bits_to_f32(b_bits));
+    const double ac = a * c, bs = b * s, bc = b * c, as = a * s;
+    o0 = f64_to_bf16_rne(ac - bs);
+    o1 = f64_to_bf16_rne(bc + as);
+}
+
+// Angle of dim pair j at position p: the cosine and sine of p * inv_freq[j]
+// in fp64.
+__device__ __forceinline__ void rope_angle(int64_t p, double inv_freq, double &c, double &s) {
+#pragma clang fp contract(off)
+    const double ang = static_cast<double>(p) * inv_freq;
+    sincos(ang, &s, &c);
+}
+
+// Partial RoPE applied to the queries on load (sparse prefill): half = the
+// rotated pairs per head (0: none), inv_freq[j] = theta^(-2j / rope_dim)
+// formed on the host as for the RoPE kernel.
+struct RopeArgs {
+    int half;
+    double inv_freq[64];
+};
 
 // Complete blocks visible to a query at position p: floor((p+1)/r).
 __host__ __device__ __forceinline__ int64_t num_complete_blocks(int64_t p, int r) {
@@ -188,7 +241,9 @@ __device__ __forceinline__ int64_t page_row(const int32_t *tab, int sh, int64_t 
     return (static_cast<int64_t>(tab[t >> sh]) << sh) | (t & ((int64_t(1) << sh) - 1));
 }
 
-hipError_t launch_sparse_prefill(const AttnArgs &a, hipStream_t s);
+// ra.half = 0: Q as given; 32 or 64: Q rotated on load (partial RoPE over
+// 2 * ra.half dims at positions pos0 + t).
+hipError_t launch_sparse_prefill(const AttnArgs &a, const RopeArgs &ra, hipStream_t s);
 // Sparse prefill plus the distillation KL of every query (H = 24, Hkv = 2);
 // dynamic LDS bytes it takes at a budget.
 hipError_t launch_sparse_prefill_kl(const AttnArgs &a, hipStream_t s);

@@ -3,7 +3,8 @@
 Each class owns its outputs and workspaces (torch device memory, allocated
 once) and enqueues the steps of the method on the current stream:
 
-prefill (chlience section 6): A1 RoPE on Q (and on K for a fresh context),
+prefill (chlience section 6): A1 RoPE on Q (by default inside the attention
+kernel, as it loads the queries) and on K for a fresh context,
 A2 pooling of the indexer keys, A3+A4 block scores and top-K selection,
 A5+A6 sparse attention over the selected blocks plus the trailing block;
 decode: A1 on the new query, optional A2 of a block the new token completes,
@@ -16,7 +17,7 @@ import torch
 from . import (DI, HI, R, SCORE_MAXHEAD, KBAR_MEAN, qsa_compress_keys, qsa_decode_workspace_bytes,
                qsa_rope_bf16, qsa_select_blocks, qsa_select_workspace_bytes,
                qsa_sparse_attn_decode, qsa_sparse_attn_prefill, qsa_sparse_attn_prefill_concurrency,
-               qsa_sparse_attn_prefill_kl)
+               qsa_sparse_attn_prefill_kl, qsa_sparse_attn_prefill_rope)
 
 
 # rows per sparse-attention launch of the prefill when the device does not
@@ -33,6 +34,13 @@ class QSAPrefill:
     is pooled.  fresh=False: K is a post-RoPE cache and only the chunk's own
     indexer keys (positions pos0 ..) are pooled into the caller's kbar cache
     (pos0 must then be a multiple of r).
+
+    rope_on_load (rope_dim 64 or 128): the sparse attention rotates the
+    queries as it loads them (bit for bit the rotated queries), so the
+    rotated copy is neither written nor read back; Q must then stay unchanged
+    until attend() has run.  The Qr attribute still gives the rotated
+    queries: it is computed on first use after rope_and_pool (the fused KL,
+    dense references).  Otherwise Q is rotated into Qr by rope_and_pool.
 
     idx_rope_dim > 0: partial RoPE on the indexer (pooled keys rotated at their
     block's first token, indexer queries at their own positions); kbar_gain:
@@ -71,7 +79,8 @@ class QSAPrefill:
                  budget: int = 512, score_mode: int = SCORE_MAXHEAD, kbar_mode: int = KBAR_MEAN,
                  theta: float = 1e7, rope_dim: int = 64, fresh: bool = True,
                  idx_rope_dim: int = 0, kbar_gain=None, pages=None, pipeline_rows: int = 0,
-                 attn_rows: int | None = None, kl_rows: int | None = None, device="cuda"):
+                 attn_rows: int | None = None, kl_rows: int | None = None,
+                 rope_on_load: bool = True, device="cuda"):
         self.Tq, self.pos0, self.H, self.Hkv, self.D = Tq, pos0, H, Hkv, D
         self.pages = pages  # paged caches (fresh=False): K, V and kbar are page pools
         self.Tk = pos0 + Tq
@@ -80,7 +89,11 @@ class QSAPrefill:
         self.idx_rope_dim, self.kbar_gain = idx_rope_dim, kbar_gain
         self.nb = self.Tk // R
         dev = torch.device(device)
-        self.Qr = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=dev)
+        self.dev = dev
+        self.rope_on_load = bool(rope_on_load) and rope_dim in (64, 128)
+        self._Qr = None          # rotated queries, allocated on first use
+        self._q = None           # the queries of the last rope_and_pool
+        self._qr_current = False  # _Qr holds the rotation of _q
         self.Kr = torch.empty((self.Tk, Hkv, D), dtype=torch.bfloat16, device=dev) if fresh else None
         self.kbar = (torch.empty((max(self.nb, 1), DI), dtype=torch.bfloat16, device=dev)
                      if fresh else None)
@@ -109,8 +122,24 @@ class QSAPrefill:
         self.qir = (torch.empty((Tq, HI, DI), dtype=torch.bfloat16, device=dev)
                     if idx_rope_dim else None)
 
+    @property
+    def Qr(self):
+        """The rotated queries [Tq, H, D] of the last rope_and_pool."""
+        if self._Qr is None:
+            self._Qr = torch.empty((self.Tq, self.H, self.D), dtype=torch.bfloat16,
+                                   device=self.dev)
+        if not self._qr_current:
+            if self._q is None:
+                raise RuntimeError("QSAPrefill.Qr: rope_and_pool has not run")
+            qsa_rope_bf16(self._q, self._Qr, self.Tq, self.H, self.D, self.rope_dim, self.theta,
+                          self.pos0)
+            self._qr_current = True
+        return self._Qr
+
     def rope_and_pool(self, Q, K, ki, kbar=None):
-        qsa_rope_bf16(Q, self.Qr, self.Tq, self.H, self.D, self.rope_dim, self.theta, self.pos0)
+        self._q, self._qr_current = Q, False
+        if not self.rope_on_load:
+            _ = self.Qr  # rotates Q now
         pool = dict(gain=self.kbar_gain, rope_dim=self.idx_rope_dim, theta=self.theta)
         if self.fresh:
             qsa_rope_bf16(K, self.Kr, self.Tk, self.Hkv, self.D, self.rope_dim, self.theta, 0)
@@ -147,10 +176,17 @@ class QSAPrefill:
 
     def _attend_rows(self, Kr, V, r0, n):
         p0 = self.pos0 + r0
-        qsa_sparse_attn_prefill(self.Qr[r0:r0 + n], Kr, V, self.blk_idx[r0:r0 + n],
-                                self.n_sel[r0:r0 + n], n, p0 + n, p0, self.H, self.Hkv, self.D, R,
-                                self.budget, self.O[r0:r0 + n], self.lse[r0:r0 + n],
-                                pages=self.pages)
+        rows = (self.blk_idx[r0:r0 + n], self.n_sel[r0:r0 + n], n, p0 + n, p0, self.H, self.Hkv,
+                self.D, R, self.budget)
+        if self.rope_on_load:
+            if self._q is None:
+                raise RuntimeError("QSAPrefill.attend: rope_and_pool has not run")
+            qsa_sparse_attn_prefill_rope(self._q[r0:r0 + n], Kr, V, *rows, self.rope_dim,
+                                         self.theta, self.O[r0:r0 + n], self.lse[r0:r0 + n],
+                                         pages=self.pages)
+        else:
+            qsa_sparse_attn_prefill(self.Qr[r0:r0 + n], Kr, V, *rows, self.O[r0:r0 + n],
+                                    self.lse[r0:r0 + n], pages=self.pages)
 
     def attend_with_kl(self, Kr, V, qi, kbar, kl):
         """Training form of attend(), after select(): the sparse attention of

@@ -205,11 +205,27 @@ int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_
  * blk_idx/n_sel as from qsa_topk_blocks (entries must be < nc of the row);
  * O: fp32 [Tq][H][D];  lse: fp32 [Tq][H] natural-log sum of exp of the
  * scaled logits, or NULL.  Query head h reads KV head h / (H / Hkv); logits
- * are q.k / sqrt(D).  Supported: D = 256, H % Hkv == 0, H / Hkv <= 16, r = 4. */
+ * are q.k / sqrt(D).  Supported: D = 256, H % Hkv == 0, H / Hkv <= 16, r = 4,
+ * Tq * Hkv < 2^26 (one 64-thread workgroup per query and KV head; larger
+ * Tq: QSA_ERR_OVERFLOW, split the rows into several calls). */
 int qsa_sparse_attn_prefill(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
                             const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq, int64_t Tk,
                             int64_t pos0, int H, int Hkv, int D, int r, int Kbudget, float *O,
                             float *lse, const qsa_pages *pages, void *stream);
+
+/* ---- A1 + A5 + A6: the same sparse prefill attention with the queries'
+ * partial RoPE (Model Summary table: RoPE dimension 64) applied as they are
+ * loaded.  Q: [Tq][H][D] BEFORE RoPE; the result equals, bit for bit,
+ * qsa_rope_bf16(Q -> Qr, Tq, H, D, rope_dim, theta, pos0) followed by
+ * qsa_sparse_attn_prefill(Qr, ...), without writing or reading Qr (the
+ * rotated queries are never stored).  Arguments otherwise as
+ * qsa_sparse_attn_prefill.  Supported: rope_dim 64 or 128 (the NeoX pair
+ * partners then sit in one lane's fragment), theta > 0. */
+int qsa_sparse_attn_prefill_rope(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
+                                 const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq,
+                                 int64_t Tk, int64_t pos0, int H, int Hkv, int D, int r,
+                                 int Kbudget, int rope_dim, double theta, float *O, float *lse,
+                                 const qsa_pages *pages, void *stream);
 
 /* ---- A7: sparse attention, decode: the Tq newest queries of each sequence
  * (Tq = 1, or next_n speculative queries sharing one selection; see the
@@ -318,7 +334,7 @@ int qsa_distill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const float *lse, const
  * and scores stay on chip (LDS: 112 bytes per budget entry plus 16.5 KB per
  * query's workgroup).  No workspace.
  * Supported: H = 24, Hkv = 2, D = 256, Hi = 4, Di = 128, r = 4,
- * Kbudget <= 1024. */
+ * Kbudget <= 1024, Tq < 2^25. */
 int qsa_sparse_attn_prefill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
                                const qsa_bf16 *q_idx, const qsa_bf16 *kbar,
                                const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq,
@@ -329,9 +345,10 @@ int qsa_sparse_attn_prefill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_b
 /* ---- Launch sizing of the sparse prefill (A6; the same kernels as
  * qsa_sparse_attn_prefill and, with with_kl, qsa_sparse_attn_prefill_kl;
  * paged: over page pools).  Returns the number of queries whose workgroups
- * (one per query) the current device holds at once: the kernel's resident
- * workgroups per CU times the CUs (1,536 on MI355X for Hkv = 2 and budget
- * 512).  Every query costs about the same at a full budget, so workgroups
+ * (Hkv one-wave workgroups per query; with_kl: one workgroup per query) the
+ * current device holds at once: the kernel's resident workgroups per CU
+ * times the CUs, over Hkv for the plain forms (1,536 on MI355X for Hkv = 2
+ * and budget 512).  Every query costs about the same at a full budget, so workgroups
  * run in rounds of this size; a caller that splits a long prefill into
  * launches of this many queries leaves no round partly empty.  Returns 0
  * for unsupported arguments (Hkv not 1, 2 or 4; Kbudget outside 1..2048;

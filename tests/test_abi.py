@@ -203,6 +203,34 @@ def test_sparse_prefill_validation(lib):
     assert sparse_prefill(lib, V=MIS) == ALIGN
 
 
+def sparse_prefill_rope(lib, Q=P, Kt=P, V=P, blk=P, ns=P, Tq=8, Tk=8, pos0=0, H=24, Hkv=2,
+                        D=256, r=4, Kb=4, rope_dim=64, theta=1e7, O=P, pages=None):
+    f = lib.qsa_sparse_attn_prefill_rope
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 3 + [ctypes.c_int] * 6 + [
+        ctypes.c_double] + [ctypes.c_void_p] * 4
+    return f(vp(Q), vp(Kt), vp(V), vp(blk), vp(ns), Tq, Tk, pos0, H, Hkv, D, r, Kb, rope_dim,
+             theta, vp(O), None, pages, None)
+
+
+def test_sparse_prefill_rope_validation(lib):
+    """The RoPE-on-load form: its own arguments, then every check of the
+    plain form (each call fails on the host)."""
+    assert sparse_prefill_rope(lib, rope_dim=0) == SHAPE
+    assert sparse_prefill_rope(lib, theta=0.0) == SHAPE
+    assert sparse_prefill_rope(lib, theta=float("nan")) == SHAPE
+    assert sparse_prefill_rope(lib, rope_dim=32) == UNSUP   # pairs across lanes
+    assert sparse_prefill_rope(lib, rope_dim=96) == UNSUP
+    assert sparse_prefill_rope(lib, rope_dim=256) == UNSUP
+    assert sparse_prefill_rope(lib, rope_dim=128, O=0) == NULL
+    assert sparse_prefill_rope(lib, Q=0) == NULL
+    assert sparse_prefill_rope(lib, Tk=7) == SHAPE
+    assert sparse_prefill_rope(lib, H=25) == SHAPE
+    assert sparse_prefill_rope(lib, D=128) == UNSUP
+    assert sparse_prefill_rope(lib, Kb=4096) == UNSUP
+    assert sparse_prefill_rope(lib, Q=MIS) == ALIGN
+    assert sparse_prefill_rope(lib, pages=pages(page_tokens=48)) == UNSUP
+
+
 def test_decode_validation(lib):
     lib.qsa_decode_workspace_bytes.restype = ctypes.c_size_t
     need = lib.qsa_decode_workspace_bytes(32, 1, 24, 2, 256, 512)

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_helpers import assert_close, check_selection, dev, log
+from gpu_helpers import assert_close, check_selection, dev, host_u16, log
 
 pytestmark = pytest.mark.gpu
 
@@ -116,7 +116,10 @@ def test_deterministic(qsa):
 def test_launch_sizes_give_the_same_bits(qsa):
     """The layer's default attention launch (the device's resident
     workgroups: CUs times the kernel's workgroups per CU) and other launch
-    sizes, including one launch of all rows, give the same O and lse bits."""
+    sizes, including one launch of all rows, give the same O and lse bits;
+    so does the layer that rotates Q in a kernel of its own (rope_on_load
+    off), whose stored Qr equals the one the default layer computes on
+    demand."""
     torch = _torch()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     c = qsa.qsa_sparse_attn_prefill_concurrency(2, 64)
@@ -127,16 +130,20 @@ def test_launch_sizes_give_the_same_bits(qsa):
     log(f"  resident workgroups: {c} plain, {ckl} with the KL ({cus} CUs)")
     T = 5000
     x = synth.prefill_inputs(T, seed=8)
-    outs = []
-    for rows in (None, 0, 1000, 3333):
-        layer = qsa.QSAPrefill(T, budget=64, attn_rows=rows)
+    outs, qrs = [], []
+    for rows, on_load in ((None, True), (0, True), (1000, True), (3333, True), (None, False)):
+        layer = qsa.QSAPrefill(T, budget=64, attn_rows=rows, rope_on_load=on_load)
+        assert layer.rope_on_load == on_load
         if rows is None:
             assert layer.attn_rows == c
         O, lse = layer(dev(x.Q), dev(x.K), dev(x.V), dev(x.qi), dev(x.ki))
         torch.cuda.synchronize()
         outs.append((O.cpu().numpy().copy(), lse.cpu().numpy().copy()))
+        if rows is None:
+            qrs.append(host_u16(layer.Qr))
     for O, lse in outs[1:]:
         assert np.array_equal(O, outs[0][0]) and np.array_equal(lse, outs[0][1])
+    assert np.array_equal(qrs[0], qrs[1])
 
 
 def test_chunked_prefill_matches_one_shot(qsa):

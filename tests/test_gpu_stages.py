@@ -473,6 +473,61 @@ def test_sparse_prefill_attention_parity(qsa):
     assert_close(lse.cpu().numpy(), lref, "sparse prefill lse")
 
 
+def _random_selection(T, pos0, K, seed):
+    """Valid selections: row t takes min(K, nc) distinct complete blocks
+    (nc = (pos0 + t + 1) // 4) in ascending order, padded with -1."""
+    rng = np.random.default_rng(seed)
+    blk = np.full((T, K), -1, dtype=np.int32)
+    nsel = np.empty(T, dtype=np.int32)
+    for t in range(T):
+        nc = (pos0 + t + 1) // 4
+        n = min(K, nc)
+        if n:
+            blk[t, :n] = np.sort(rng.choice(nc, size=n, replace=False))
+        nsel[t] = n
+    return blk, nsel
+
+
+@pytest.mark.parametrize("T,pos0,H,Hkv,rope_dim,theta,K", [
+    (1029, 0, 24, 2, 64, 1e7, 64),          # the model's heads, ragged tail
+    (333, 70001, 24, 2, 64, 1e7, 512),      # full budget, positions past 2^16
+    (517, 4093, 16, 1, 128, 1e4, 128),      # rope over 128 dims, one KV head
+    (260, 1000, 32, 4, 64, 5e5, 256),       # four KV heads
+])
+def test_sparse_prefill_rope_on_load(qsa, T, pos0, H, Hkv, rope_dim, theta, K):
+    """The queries rotated as the attention loads them: O and lse equal, bit
+    for bit, the RoPE kernel followed by the plain sparse attention, and
+    sampled rows match the oracle (its RoPE, then its attention)."""
+    torch = _torch()
+    log(f"rope on load T={T} pos0={pos0} H={H} Hkv={Hkv} rope_dim={rope_dim} theta={theta} K={K}")
+    Tk = pos0 + T
+    Q = synth.normal_bf16(1, (T, H, 256), seed=70 + T)
+    Kc = synth.normal_bf16(2, (Tk, Hkv, 256), seed=70 + T)
+    V = synth.normal_bf16(3, (Tk, Hkv, 256), seed=70 + T)
+    blk, nsel = _random_selection(T, pos0, K, seed=T)
+    Qd, Kd, Vd, bd, nd = dev(Q), dev(Kc), dev(V), dev(blk), dev(nsel)
+    Qr = torch.empty_like(Qd)
+    qsa.qsa_rope_bf16(Qd, Qr, T, H, 256, rope_dim, theta, pos0)
+    outs = []
+    for fused in (False, True):
+        O = torch.full((T, H, 256), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+        if fused:
+            qsa.qsa_sparse_attn_prefill_rope(Qd, Kd, Vd, bd, nd, T, Tk, pos0, H, Hkv, 256, 4, K,
+                                             rope_dim, theta, O, lse)
+        else:
+            qsa.qsa_sparse_attn_prefill(Qr, Kd, Vd, bd, nd, T, Tk, pos0, H, Hkv, 256, 4, K, O, lse)
+        torch.cuda.synchronize()
+        outs.append((O.cpu().numpy(), lse.cpu().numpy()))
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32)), "O"
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32)), "lse"
+    rows = np.unique(np.array([0, 1, 2, 3, 4, T // 2, T - 2, T - 1]))
+    Qo = oracle.rope(Q, rope_dim=rope_dim, theta=theta, pos0=pos0)
+    Oref, lref = oracle.sparse_attn_rows(Qo, Kc, V, rows, blk[rows], nsel[rows], pos0=pos0)
+    assert_close(outs[1][0][rows], Oref, "rope-on-load O vs oracle")
+    assert_close(outs[1][1][rows], lref, "rope-on-load lse vs oracle")
+
+
 def test_decode_attention_parity(qsa):
     torch = _torch()
     B, Lmax, K = 5, 5000, 64
