@@ -337,6 +337,7 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
             fms = e0.elapsed_time(e1) / dsteps
             res["sparse_kl"] = dict(ms=fms, launches=len(layer._chunks(layer.kl_rows)),
                                     rows_per_launch=layer.kl_rows,
+                                    form="staged" if layer.kl_staged else "one kernel",
                                     attend_standalone_ms=stage["attend_standalone"],
                                     vs_attend=fms / stage["attend_standalone"],
                                     hbm_gbps_algorithmic=attn_bytes / (fms * 1e-3) / 1e9,

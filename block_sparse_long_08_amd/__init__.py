@@ -70,6 +70,10 @@ _sig("qsa_distill_kl", _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i
 _sig("qsa_sparse_attn_prefill_kl", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
      _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp)
 _sig("qsa_sparse_attn_prefill_concurrency", _i32, _i32, _i32, _i32, _i32)
+_sig("qsa_sparse_attn_prefill_kl_staged_workspace_bytes", _sz, _i64, _i32)
+_sig("qsa_sparse_attn_prefill_kl_staged", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+     _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _dbl, _vp, _vp, _vp, _vp, _sz,
+     _vp)
 
 EXPORTED = ["qsa_status_string", "qsa_version", "qsa_check_device", "qsa_rope_bf16",
             "qsa_compress_keys", "qsa_index_scores", "qsa_topk_workspace_bytes",
@@ -78,7 +82,9 @@ EXPORTED = ["qsa_status_string", "qsa_version", "qsa_check_device", "qsa_rope_bf
             "qsa_decode_workspace_bytes", "qsa_sparse_attn_decode",
             "qsa_decode_noalloc_max_bytes", "qsa_sparse_attn_decode_noalloc",
             "dense_attn_workspace_bytes", "dense_attn", "qsa_distill_workspace_bytes",
-            "qsa_distill_kl", "qsa_sparse_attn_prefill_kl", "qsa_sparse_attn_prefill_concurrency"]
+            "qsa_distill_kl", "qsa_sparse_attn_prefill_kl", "qsa_sparse_attn_prefill_concurrency",
+            "qsa_sparse_attn_prefill_kl_staged_workspace_bytes",
+            "qsa_sparse_attn_prefill_kl_staged"]
 
 SCORE_MAXHEAD, SCORE_RELUSUM = 0, 1
 KBAR_MEAN, KBAR_RMSNORM = 0, 1
@@ -368,6 +374,34 @@ def qsa_sparse_attn_prefill_kl(Q, K, V, q_idx, kbar, blk_idx, n_sel, Tq: int, Tk
     _call("qsa_sparse_attn_prefill_kl", _ptr(Q), _ptr(K), _ptr(V), _ptr(q_idx), _ptr(kbar),
           _ptr(blk_idx), _ptr(n_sel), Tq, Tk, pos0, H, Hkv, D, Hi, Di, r, Kbudget, score_mode,
           _ptr(O), _ptr(lse), _ptr(kl), _stream(stream))
+
+
+def qsa_sparse_attn_prefill_kl_staged_workspace_bytes(Tq: int, Kbudget: int) -> int:
+    return int(_lib.qsa_sparse_attn_prefill_kl_staged_workspace_bytes(Tq, Kbudget))
+
+
+def qsa_sparse_attn_prefill_kl_staged(Q, K, V, q_idx, kbar, blk_idx, n_sel, Tq: int, Tk: int,
+                                      pos0: int, H: int, Hkv: int, D: int, Hi: int, Di: int,
+                                      r: int, Kbudget: int, score_mode: int, O, lse, kl, ws=None,
+                                      ws_bytes: int = 0, rope_dim: int = 0, theta: float = 1e7,
+                                      stream=None) -> None:
+    """The fused KL form in two launches (plain attention writing block
+    maxima, then the KL); rope_dim > 0: Q before RoPE, rotated on load."""
+    f = "qsa_sparse_attn_prefill_kl_staged"
+    _req(f, "Q", Q, 2, Tq * H * D * 2)
+    _req(f, "K", K, 2, Tk * Hkv * D * 2)
+    _req(f, "V", V, 2, Tk * Hkv * D * 2)
+    _req(f, "q_idx", q_idx, 2, Tq * Hi * Di * 2)
+    _req(f, "kbar", kbar, 2, (Tk // r) * Di * 2)
+    _req(f, "blk_idx", blk_idx, 4, Tq * Kbudget * 4)
+    _req(f, "n_sel", n_sel, 4, Tq * 4)
+    _req(f, "O", O, 4, Tq * H * D * 4)
+    _req(f, "lse", lse, 4, Tq * H * 4)
+    _req(f, "kl", kl, 4, Tq * 4)
+    _req(f, "ws", ws, 1, ws_bytes)
+    _call(f, _ptr(Q), _ptr(K), _ptr(V), _ptr(q_idx), _ptr(kbar), _ptr(blk_idx), _ptr(n_sel), Tq,
+          Tk, pos0, H, Hkv, D, Hi, Di, r, Kbudget, score_mode, rope_dim, float(theta), _ptr(O),
+          _ptr(lse), _ptr(kl), _ptr(ws), ws_bytes, _stream(stream))
 
 
 def qsa_sparse_attn_prefill_concurrency(Hkv: int, Kbudget: int, with_kl: bool = False,

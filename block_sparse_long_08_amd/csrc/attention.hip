@@ -192,12 +192,15 @@ __device__ __forceinline__ void stage_k(const EntryList<MULTI, PMODE> &L, int e0
 // the V tile is still arriving by LDS DMA (wait for it before the PV reads);
 // otherwise the caller has written it and fenced.  Returns the largest scaled
 // logit (log2 units) among the lane's own tokens: entry e0 + g4 for column n
-// (-inf where none is visible).
+// (-inf where none is visible).  With lmx, lanes with lmo >= 0 also store
+// lmv (the previous stage's max) at lmx[lmo].
 template <bool DMA_V, bool MULTI, int PMODE>
 __device__ __forceinline__ float stage_compute(const EntryList<MULTI, PMODE> &L, int e0,
                                                int64_t pq, const bf16x8 (&kf)[8],
                                                const bf16x8 (&qT)[8], WaveState &st,
-                                               const unsigned char *vlds, int lane) {
+                                               const unsigned char *vlds, int lane,
+                                               float *lmx = nullptr, int lmo = -1,
+                                               float lmv = 0.f) {
     const int n = lane & 15, g4 = lane >> 4;
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -233,6 +236,9 @@ __device__ __forceinline__ float stage_compute(const EntryList<MULTI, PMODE> &L,
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __builtin_amdgcn_wave_barrier();
     }
+    // after the wait: stores count in vmcnt too, so the store of a stage's
+    // max waits a stage and leaves with the next one's loads in flight
+    if (lmx && lmo >= 0) lmx[lmo] = lmv;
     // O^T += V^T P^T: A = V^T rows d = 16*dt + n, k-slots = tokens 4*g4 .. +3
     const int swz = 2 * g4;  // row_swizzle(4*g4 + jj)
 #pragma unroll
@@ -257,7 +263,8 @@ __device__ __forceinline__ float attn_stage(const EntryList<MULTI, PMODE> &L, in
                                            const uint16_t *__restrict__ Kg,
                                            const uint16_t *__restrict__ Vg, int64_t rs,
                                            const bf16x8 (&qT)[8], WaveState &st,
-                                           unsigned char *vlds, int lane) {
+                                           unsigned char *vlds, int lane,
+                                           float *lmx = nullptr, int lmo = -1, float lmv = 0.f) {
     lds_fence();  // the previous stage's reads of this tile are done
     stage_v_dma(L, e0, p, Vg, rs, vlds, lane);
     uint4 kf[8];
@@ -265,7 +272,7 @@ __device__ __forceinline__ float attn_stage(const EntryList<MULTI, PMODE> &L, in
     bf16x8 kb[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) kb[s] = as_bf16x8(kf[s]);
-    return stage_compute<true>(L, e0, pq, kb, qT, st, vlds, lane);
+    return stage_compute<true>(L, e0, pq, kb, qT, st, vlds, lane, lmx, lmo, lmv);
 }
 
 // Two bf16 of a 32-bit word each: the pairs (dims j, j+1 of word a) and their
@@ -448,6 +455,75 @@ __device__ __forceinline__ void tile_scores(const uint16_t *__restrict__ qi_row,
     }
 }
 
+// KL of one query (row of the launch) from the block-max logits of its
+// selected blocks, in a workgroup of two waves, wave g holding KV head g:
+// mxg = wave g's maxima [ns][12] (LDS or device memory), lse2 = this lane's
+// head's log2-unit log-sum-exp (lanes 0..11 hold heads g*12 .. g*12+11).
+// part [2][Kbudget], sc [Kbudget] and red [16] are the workgroup's LDS.
+__device__ __forceinline__ void kl_epilogue(const AttnArgs &a, int64_t row, int ns,
+                                            const int32_t *lst, const float *mxg, float lse2,
+                                            float *part, float *sc, float *red, int g, int lane) {
+    // teacher mass of each selected block from this wave's 12 heads: the
+    // head's probability of the block's best token, exp2(max - lse2)
+    float l2[kKlGroup];
+#pragma unroll
+    for (int h = 0; h < kKlGroup; ++h) l2[h] = __shfl(lse2, h);
+    lds_fence();  // the wave's block maxima are in place
+    for (int e = lane; e < ns; e += kWave) {
+        const float *mr = mxg + e * kKlGroup;
+        float tb = 0.f;
+#pragma unroll
+        for (int h = 0; h < kKlGroup; ++h) tb += exp2f(mr[h] - l2[h]);
+        part[g * a.Kbudget + e] = tb;
+    }
+    // student logits: wave g scores tiles g, g + 2, ...
+    tile_scores(a.q_idx + row * (kIdxHeads * kIdxDim), a.kbar, lst, ns, g, 2, a.score_mode, sc,
+                lane);
+    block_sync();
+    // thread i takes blocks i, i + 128, ...: t = both waves' sums; the row's
+    // Z = sum t, A = sum t ln t, C = sum t s and the log-sum-exp of s
+    float z = 0.f, aa = 0.f, c = 0.f, m = -INFINITY, zs = 0.f;
+    for (int e = threadIdx.x; e < ns; e += 2 * kWave) {
+        const float tb = part[e] + part[a.Kbudget + e];
+        const float se = sc[e];
+        z += tb;
+        aa += tb > 0.f ? tb * logf(tb) : 0.f;
+        c += tb * se;
+        if (se > m) {
+            zs = zs * expf(m - se) + 1.f;
+            m = se;
+        } else {
+            zs += expf(se - m);
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        z += __shfl_xor(z, off);
+        aa += __shfl_xor(aa, off);
+        c += __shfl_xor(c, off);
+        const float m2 = __shfl_xor(m, off), zs2 = __shfl_xor(zs, off);
+        const float mn = fmaxf(m, m2);
+        zs = (m == -INFINITY ? 0.f : zs * expf(m - mn)) +
+             (m2 == -INFINITY ? 0.f : zs2 * expf(m2 - mn));
+        m = mn;
+    }
+    if (lane == 0) {
+        red[5 * g + 0] = z;
+        red[5 * g + 1] = aa;
+        red[5 * g + 2] = c;
+        red[5 * g + 3] = m;
+        red[5 * g + 4] = zs;
+    }
+    block_sync();
+    if (threadIdx.x != 0) return;
+    // wave 1 after wave 0
+    const float m1 = red[8], mn = fmaxf(red[3], m1);
+    const float zsum = (red[3] == -INFINITY ? 0.f : red[4] * expf(red[3] - mn)) +
+                       (m1 == -INFINITY ? 0.f : red[9] * expf(m1 - mn));
+    const float zt = red[0] + red[5], at = red[1] + red[6], ct = red[2] + red[7];
+    a.kl[row] = ns > 0 ? at / zt - logf(zt) - ct / zt + (mn + logf(zsum)) : 0.f;
+}
+
 // ------------------------------------------------------------------------
 // Prefill: one wave per (query, KV head), walking all stages of its head.
 // Plain forms: one wave per workgroup, workgroup w = Hkv * query + head, grid
@@ -467,9 +543,10 @@ __device__ __forceinline__ void tile_scores(const uint16_t *__restrict__ qi_row,
 // O accumulators then live in VGPRs instead of AGPRs, and 12 waves per CU
 // keep 1.5x the stages in flight: 13% faster than 2 waves per SIMD); the KL
 // form is held to 2 workgroups per CU by its LDS anyway.
-template <bool PAGED, bool KL>
+template <bool PAGED, bool KL, bool BMAX>
 __global__ void __launch_bounds__(256, KL ? 1 : 3) attn_prefill_kernel(AttnArgs a, RopeArgs ra) {
-    static_assert(!(PAGED && KL), "the fused KL runs on contiguous caches");
+    static_assert(!(PAGED && KL) && !(BMAX && (PAGED || KL)),
+                  "the KL forms run on contiguous caches");
     extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
     const PrefillLds lay(a.Hkv, a.Kbudget, KL);
     int32_t *lst = reinterpret_cast<int32_t *>(dyn_lds + lay.list);
@@ -517,8 +594,21 @@ __global__ void __launch_bounds__(256, KL ? 1 : 3) attn_prefill_kernel(AttnArgs 
                  static_cast<int64_t>(g) * a.Kbudget * kKlGroup;
     unsigned char *vl = dyn_lds + (KL ? g : 0) * kVStageBytes;
     if constexpr (!KL) {
-        for (int sidx = 0; sidx < nstages; ++sidx)
-            attn_stage(L, sidx * kStageEntries, p, pq, Kg, Vg, rs, qT, st, vl, lane);
+        // staged KL form: each selected block's max logit per head of the wave
+        float *bmx =
+            BMAX ? a.bmax + (row * a.Hkv + g) * static_cast<int64_t>(a.Kbudget) * kKlGroup
+                 : nullptr;
+        // each stage stores the previous stage's maxima
+        float lmv = 0.f;
+        int lmo = -1;
+        for (int sidx = 0; sidx < nstages; ++sidx) {
+            const int e0 = sidx * kStageEntries;
+            const float lm = attn_stage(L, e0, p, pq, Kg, Vg, rs, qT, st, vl, lane, bmx, lmo, lmv);
+            // this stage's slot: entry e0 + g4, head n (none past the list)
+            lmo = BMAX && n < kKlGroup && e0 + g4 < ns ? (e0 + g4) * kKlGroup + n : -1;
+            lmv = lm;
+        }
+        if (BMAX && lmo >= 0) bmx[lmo] = lmv;
     } else {
         // Two stages per step: the first stage's V by LDS DMA as above, its
         // K and the second stage's K and V into registers, all issued before
@@ -547,71 +637,16 @@ __global__ void __launch_bounds__(256, KL ? 1 : 3) attn_prefill_kernel(AttnArgs 
     const float ltot = head_total(st.l);
     state_write(st, ltot, a.O + row * a.H * kHeadDim, a.lse ? a.lse + row * a.H : nullptr, g,
                 group, lane);
-    if (!KL) return;
+    if (!KL) {
+        if (BMAX && g4 == 0 && n < group)
+            a.lse2[row * a.H + g * group + n] = ltot > 0.f ? st.m + log2f(ltot) : INFINITY;
+        return;
+    }
 
-    // teacher mass of each selected block from this wave's 12 heads: the
-    // head's probability of the block's best token, exp2(max - lse2)
     const float lse2 = ltot > 0.f ? st.m + log2f(ltot) : INFINITY;
-    float l2[kKlGroup];
-#pragma unroll
-    for (int h = 0; h < kKlGroup; ++h) l2[h] = __shfl(lse2, h);
-    float *part = reinterpret_cast<float *>(dyn_lds + lay.part);
-    lds_fence();  // the wave's block maxima are in LDS
-    for (int e = lane; e < ns; e += kWave) {
-        const float *mr = mxw + e * kKlGroup;
-        float tb = 0.f;
-#pragma unroll
-        for (int h = 0; h < kKlGroup; ++h) tb += exp2f(mr[h] - l2[h]);
-        part[g * a.Kbudget + e] = tb;
-    }
-    // student logits: wave g scores tiles g, g + 2, ...
-    float *sc = reinterpret_cast<float *>(dyn_lds + lay.score);
-    tile_scores(a.q_idx + row * (kIdxHeads * kIdxDim), a.kbar, lst, ns, g, a.Hkv, a.score_mode,
-                sc, lane);
-    block_sync();
-    // thread i takes blocks i, i + 128, ...: t = both waves' sums; the row's
-    // Z = sum t, A = sum t ln t, C = sum t s and the log-sum-exp of s
-    float z = 0.f, aa = 0.f, c = 0.f, m = -INFINITY, zs = 0.f;
-    for (int e = threadIdx.x; e < ns; e += blockDim.x) {
-        const float tb = part[e] + part[a.Kbudget + e];
-        const float se = sc[e];
-        z += tb;
-        aa += tb > 0.f ? tb * logf(tb) : 0.f;
-        c += tb * se;
-        if (se > m) {
-            zs = zs * expf(m - se) + 1.f;
-            m = se;
-        } else {
-            zs += expf(se - m);
-        }
-    }
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        z += __shfl_xor(z, off);
-        aa += __shfl_xor(aa, off);
-        c += __shfl_xor(c, off);
-        const float m2 = __shfl_xor(m, off), zs2 = __shfl_xor(zs, off);
-        const float mn = fmaxf(m, m2);
-        zs = (m == -INFINITY ? 0.f : zs * expf(m - mn)) +
-             (m2 == -INFINITY ? 0.f : zs2 * expf(m2 - mn));
-        m = mn;
-    }
-    float *red = reinterpret_cast<float *>(dyn_lds + lay.red);
-    if (lane == 0) {
-        red[5 * g + 0] = z;
-        red[5 * g + 1] = aa;
-        red[5 * g + 2] = c;
-        red[5 * g + 3] = m;
-        red[5 * g + 4] = zs;
-    }
-    block_sync();
-    if (threadIdx.x != 0) return;
-    // wave 1 after wave 0
-    const float m1 = red[8], mn = fmaxf(red[3], m1);
-    const float zsum = (red[3] == -INFINITY ? 0.f : red[4] * expf(red[3] - mn)) +
-                       (m1 == -INFINITY ? 0.f : red[9] * expf(m1 - mn));
-    const float zt = red[0] + red[5], at = red[1] + red[6], ct = red[2] + red[7];
-    a.kl[row] = ns > 0 ? at / zt - logf(zt) - ct / zt + (mn + logf(zsum)) : 0.f;
+    kl_epilogue(a, row, ns, lst, mxw, lse2, reinterpret_cast<float *>(dyn_lds + lay.part),
+                reinterpret_cast<float *>(dyn_lds + lay.score),
+                reinterpret_cast<float *>(dyn_lds + lay.red), g, lane);
 }
 
 // Split record in HBM: unnormalised O of head n (column n of O^T) at
@@ -773,9 +808,11 @@ hipError_t launch_sparse_prefill(const AttnArgs &a, const RopeArgs &ra, hipStrea
     const dim3 grid(static_cast<uint32_t>(a.Tq * a.Hkv), static_cast<uint32_t>(a.B));
     const size_t lds = PrefillLds(a.Hkv, a.Kbudget, false).total;
     if (a.ptable)
-        hipLaunchKernelGGL((attn_prefill_kernel<true, false>), grid, dim3(kWave), lds, s, a, ra);
+        hipLaunchKernelGGL((attn_prefill_kernel<true, false, false>), grid, dim3(kWave), lds, s,
+                           a, ra);
     else
-        hipLaunchKernelGGL((attn_prefill_kernel<false, false>), grid, dim3(kWave), lds, s, a, ra);
+        hipLaunchKernelGGL((attn_prefill_kernel<false, false, false>), grid, dim3(kWave), lds, s,
+                           a, ra);
     return hipGetLastError();
 }
 
@@ -783,9 +820,10 @@ size_t sparse_prefill_kl_lds(int Kbudget) { return PrefillLds(2, Kbudget, true).
 
 int sparse_prefill_concurrency(int Hkv, int Kbudget, bool kl, bool paged) {
     const size_t lds = PrefillLds(Hkv, Kbudget, kl).total;
-    const void *fn = kl      ? reinterpret_cast<const void *>(&attn_prefill_kernel<false, true>)
-                     : paged ? reinterpret_cast<const void *>(&attn_prefill_kernel<true, false>)
-                             : reinterpret_cast<const void *>(&attn_prefill_kernel<false, false>);
+    const void *fn =
+        kl      ? reinterpret_cast<const void *>(&attn_prefill_kernel<false, true, false>)
+        : paged ? reinterpret_cast<const void *>(&attn_prefill_kernel<true, false, false>)
+                : reinterpret_cast<const void *>(&attn_prefill_kernel<false, false, false>);
     if (kl && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   static_cast<int>(lds)) != hipSuccess)
         return 0;
@@ -804,13 +842,67 @@ hipError_t launch_sparse_prefill_kl(const AttnArgs &a, hipStream_t s) {
     if (a.Tq == 0 || a.B == 0) return hipSuccess;
     const dim3 grid(static_cast<uint32_t>(a.Tq), static_cast<uint32_t>(a.B));
     const size_t lds = PrefillLds(a.Hkv, a.Kbudget, true).total;
-    const void *fn = reinterpret_cast<const void *>(&attn_prefill_kernel<false, true>);
+    const void *fn = reinterpret_cast<const void *>(&attn_prefill_kernel<false, true, false>);
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
     RopeArgs none{};
-    hipLaunchKernelGGL((attn_prefill_kernel<false, true>), grid, dim3(64 * a.Hkv), lds, s, a,
-                       none);
+    hipLaunchKernelGGL((attn_prefill_kernel<false, true, false>), grid, dim3(64 * a.Hkv), lds, s,
+                       a, none);
+    return hipGetLastError();
+}
+
+// Second kernel of the staged KL form: one workgroup of two waves per query
+// (wave g: KV head g), the block list and the KL epilogue over the block
+// maxima and log-sum-exps the attention wrote to device memory.  Dynamic
+// LDS: the list (Kbudget + 1 entries), part [2][Kbudget], the scores
+// [Kbudget] and 16 floats.
+__global__ void __launch_bounds__(128) kl_from_bmax_kernel(AttnArgs a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
+    const size_t list_bytes = (4 * (static_cast<size_t>(a.Kbudget) + 1) + 15) & ~size_t(15);
+    int32_t *lst = reinterpret_cast<int32_t *>(dyn_lds);
+    float *part = reinterpret_cast<float *>(dyn_lds + list_bytes);
+    float *sc = part + 2 * a.Kbudget;
+    float *red = sc + a.Kbudget;
+    const int64_t row = blockIdx.x;
+    const int64_t p = a.pos0 + row;
+    const int64_t nc = num_complete_blocks(p, kBlock);
+    const int v = a.n_sel[row];
+    const int64_t cap = min(static_cast<int64_t>(a.Kbudget), nc);
+    const int ns = v < 0 ? 0 : (v > cap ? static_cast<int>(cap) : v);
+    const int32_t *src = a.blk_idx + row * a.Kbudget;
+    for (int i = threadIdx.x; i < ns; i += blockDim.x) {
+        int32_t bi = src[i];
+        lst[i] = bi < 0 ? 0 : (bi >= nc ? static_cast<int32_t>(nc - 1) : bi);
+    }
+    block_sync();
+    const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
+    const float lse2 = (lane & 15) < kKlGroup ? a.lse2[row * a.H + g * kKlGroup + (lane & 15)] : 0.f;
+    const float *mxg = a.bmax + (row * 2 + g) * static_cast<int64_t>(a.Kbudget) * kKlGroup;
+    kl_epilogue(a, row, ns, lst, mxg, lse2, part, sc, red, g, lane);
+}
+
+size_t sparse_prefill_kl_staged_floats(int64_t Tq, int Kbudget) {
+    // block maxima [Tq][2][Kbudget][12], then lse2 [Tq][24]
+    return static_cast<size_t>(Tq) * (2 * static_cast<size_t>(Kbudget) * kKlGroup + 2 * kKlGroup);
+}
+
+hipError_t launch_sparse_prefill_kl_staged(const AttnArgs &a, const RopeArgs &ra,
+                                           hipStream_t s) {
+    if (a.Tq == 0 || a.B == 0) return hipSuccess;
+    if (ra.half != 0 && ra.half != 32 && ra.half != 64) return hipErrorInvalidValue;
+    if (a.B != 1 || a.Hkv != 2 || a.H != 2 * kKlGroup || a.ptable || !a.bmax || !a.lse2)
+        return hipErrorInvalidValue;
+    if (a.Tq * a.Hkv > kMaxPrefillWaves) return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<uint32_t>(a.Tq * a.Hkv));
+    hipLaunchKernelGGL((attn_prefill_kernel<false, false, true>), grid, dim3(kWave),
+                       PrefillLds(a.Hkv, a.Kbudget, false).total, s, a, ra);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t lds = ((4 * (static_cast<size_t>(a.Kbudget) + 1) + 15) & ~size_t(15)) +
+                       4 * 3 * static_cast<size_t>(a.Kbudget) + 4 * 16;
+    hipLaunchKernelGGL(kl_from_bmax_kernel, dim3(static_cast<uint32_t>(a.Tq)), dim3(2 * kWave),
+                       lds, s, a);
     return hipGetLastError();
 }
 

@@ -534,18 +534,18 @@ int qsa_sparse_attn_prefill_concurrency(int Hkv, int Kbudget, int with_kl, int p
     return sparse_prefill_concurrency(Hkv, Kbudget, with_kl != 0, paged != 0);
 }
 
-int qsa_sparse_attn_prefill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
-                               const qsa_bf16 *q_idx, const qsa_bf16 *kbar,
-                               const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq,
-                               int64_t Tk, int64_t pos0, int H, int Hkv, int D, int Hi, int Di,
-                               int r, int Kbudget, int score_mode, float *O, float *lse,
-                               float *kl, void *stream) {
+// Checks shared by the two KL forms; fills a on success.
+static int kl_prefill_args(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
+                           const qsa_bf16 *q_idx, const qsa_bf16 *kbar, const int32_t *blk_idx,
+                           const int32_t *n_sel, int64_t Tq, int64_t Tk, int64_t pos0, int H,
+                           int Hkv, int D, int Hi, int Di, int r, int Kbudget, int max_budget,
+                           int score_mode, float *O, float *lse, float *kl, AttnArgs &a) {
     if (!Q || !K || !V || !blk_idx || !n_sel || !O || !kl) return QSA_ERR_NULL;
     if (Tq < 0 || Tk < 0 || pos0 < 0 || Kbudget <= 0) return QSA_ERR_SHAPE;
     int st = check_attn_shape(H, Hkv, D, r);
     if (st != QSA_OK) return st;
     if (Tk < pos0 + Tq) return QSA_ERR_SHAPE;
-    if (H != 24 || Hkv != 2 || Kbudget > kMaxKlBudget) return QSA_ERR_UNSUPPORTED;
+    if (H != 24 || Hkv != 2 || Kbudget > max_budget) return QSA_ERR_UNSUPPORTED;
     const int64_t nb_max = Tk / kBlock;
     st = check_index_args(q_idx, kbar, 1, Tq, pos0, nullptr, nb_max > 0 ? nb_max : 1, Hi, Di, r,
                           score_mode);
@@ -553,12 +553,58 @@ int qsa_sparse_attn_prefill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_b
     if (Tq > kI32Max || nb_max > kI32Max) return QSA_ERR_OVERFLOW;
     if (Tq * Hkv > kMaxPrefillWaves) return QSA_ERR_OVERFLOW;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return QSA_ERR_ALIGN;
-    AttnArgs a{};
+    a = AttnArgs{};
     a.Q = Q; a.K = K; a.V = V; a.blk_idx = blk_idx; a.n_sel = n_sel; a.seq_len = nullptr;
     a.O = O; a.lse = lse; a.part = nullptr;
     a.Tq = Tq; a.Lmax = Tk; a.pos0 = pos0; a.B = 1; a.H = H; a.Hkv = Hkv; a.Kbudget = Kbudget;
     a.q_idx = q_idx; a.kbar = kbar; a.kl = kl; a.score_mode = score_mode;
+    return QSA_OK;
+}
+
+int qsa_sparse_attn_prefill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
+                               const qsa_bf16 *q_idx, const qsa_bf16 *kbar,
+                               const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq,
+                               int64_t Tk, int64_t pos0, int H, int Hkv, int D, int Hi, int Di,
+                               int r, int Kbudget, int score_mode, float *O, float *lse,
+                               float *kl, void *stream) {
+    AttnArgs a;
+    const int st = kl_prefill_args(Q, K, V, q_idx, kbar, blk_idx, n_sel, Tq, Tk, pos0, H, Hkv, D,
+                                   Hi, Di, r, Kbudget, kMaxKlBudget, score_mode, O, lse, kl, a);
+    if (st != QSA_OK) return st;
     return launch_status(launch_sparse_prefill_kl(a, as_stream(stream)));
+}
+
+size_t qsa_sparse_attn_prefill_kl_staged_workspace_bytes(int64_t Tq, int Kbudget) {
+    if (Tq < 0 || Tq > kI32Max || Kbudget <= 0 || Kbudget > kMaxBudget) return 0;
+    return sparse_prefill_kl_staged_floats(Tq, Kbudget) * sizeof(float);
+}
+
+int qsa_sparse_attn_prefill_kl_staged(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
+                                      const qsa_bf16 *q_idx, const qsa_bf16 *kbar,
+                                      const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq,
+                                      int64_t Tk, int64_t pos0, int H, int Hkv, int D, int Hi,
+                                      int Di, int r, int Kbudget, int score_mode, int rope_dim,
+                                      double theta, float *O, float *lse, float *kl, void *ws,
+                                      size_t ws_bytes, void *stream) {
+    AttnArgs a;
+    int st = kl_prefill_args(Q, K, V, q_idx, kbar, blk_idx, n_sel, Tq, Tk, pos0, H, Hkv, D, Hi,
+                             Di, r, Kbudget, kMaxBudget, score_mode, O, lse, kl, a);
+    if (st != QSA_OK) return st;
+    RopeArgs ra{};
+    if (rope_dim != 0) {
+        if (rope_dim < 0 || !(theta > 0.0)) return QSA_ERR_SHAPE;
+        if (rope_dim != 64 && rope_dim != 128) return QSA_ERR_UNSUPPORTED;
+        ra.half = rope_dim / 2;
+        for (int j = 0; j < ra.half; ++j)
+            ra.inv_freq[j] =
+                pow(theta, -2.0 * static_cast<double>(j) / static_cast<double>(rope_dim));
+    }
+    const size_t need = sparse_prefill_kl_staged_floats(Tq, Kbudget) * sizeof(float);
+    if (need > 0 && (!ws || ws_bytes < need)) return QSA_ERR_WORKSPACE;
+    if (ws && !aligned16(ws)) return QSA_ERR_ALIGN;
+    a.bmax = static_cast<float *>(ws);
+    a.lse2 = a.bmax + static_cast<size_t>(Tq) * 2 * Kbudget * 12;
+    return launch_status(launch_sparse_prefill_kl_staged(a, ra, as_stream(stream)));
 }
 
 }  // extern "C"

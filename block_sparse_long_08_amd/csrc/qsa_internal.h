@@ -234,6 +234,12 @@ struct AttnArgs {
     const uint16_t *kbar;
     float *kl;
     int score_mode;
+    // Staged KL form: the plain prefill kernel also writes each selected
+    // block's max logit per head, bmax [Tq][Hkv][Kbudget][H / Hkv] (log2
+    // units), and each head's log2-unit log-sum-exp, lse2 [Tq][H]; a second
+    // kernel turns them into the KL.  nullptr otherwise.
+    float *bmax;
+    float *lse2;
 };
 
 // Row of token t in a page pool (tab: the sequence's page-table row).
@@ -247,6 +253,11 @@ hipError_t launch_sparse_prefill(const AttnArgs &a, const RopeArgs &ra, hipStrea
 // Sparse prefill plus the distillation KL of every query (H = 24, Hkv = 2);
 // dynamic LDS bytes it takes at a budget.
 hipError_t launch_sparse_prefill_kl(const AttnArgs &a, hipStream_t s);
+// Staged KL form: the plain prefill kernel writing a.bmax and a.lse2, then
+// the KL epilogue kernel (contiguous caches, Hkv = 2, H = 24).
+hipError_t launch_sparse_prefill_kl_staged(const AttnArgs &a, const RopeArgs &ra, hipStream_t s);
+// floats of its workspace: bmax [Tq][2][Kbudget][12], then lse2 [Tq][24]
+size_t sparse_prefill_kl_staged_floats(int64_t Tq, int Kbudget);
 size_t sparse_prefill_kl_lds(int Kbudget);
 // Workgroups (one per query) of the sparse prefill (kl: fused with the KL;
 // paged: over page pools) resident at once on the current device: its

@@ -17,7 +17,8 @@ import torch
 from . import (DI, HI, R, SCORE_MAXHEAD, KBAR_MEAN, qsa_compress_keys, qsa_decode_workspace_bytes,
                qsa_rope_bf16, qsa_select_blocks, qsa_select_workspace_bytes,
                qsa_sparse_attn_decode, qsa_sparse_attn_prefill, qsa_sparse_attn_prefill_concurrency,
-               qsa_sparse_attn_prefill_kl, qsa_sparse_attn_prefill_rope)
+               qsa_sparse_attn_prefill_kl, qsa_sparse_attn_prefill_kl_staged,
+               qsa_sparse_attn_prefill_kl_staged_workspace_bytes, qsa_sparse_attn_prefill_rope)
 
 
 # rows per sparse-attention launch of the prefill when the device does not
@@ -48,24 +49,26 @@ class QSAPrefill:
 
     The selection of all rows runs first (one call; the library scores the
     rows in chunks of at most 8 GiB of scores), then the sparse attention in
-    launches of attn_rows rows.  By default a launch holds as many queries
-    as the device runs workgroups of the kernel at once (1,536 on MI355X at
-    Hkv = 2, budget 512): every query costs about the same, so workgroups run
-    in rounds of that size, and each query walks its block list in
-    ascending block order: within one round the concurrent gathers sweep the
-    cache as a narrow band, which L2 and the Infinity Cache hold.  Launches
-    that span several rounds let the workgroups drift apart and the band
-    widen.  The 128K prefill's attention takes 45.1 ms in 1,536-row
-    launches (caches serve 52% of the gathered bytes), 47.7 ms in 3,072-row
-    launches, 48.5 ms in 4,096-row launches (43%), 59.3 ms in 1,792-row
-    launches and 62.5 ms as one launch of 131,072 rows; attn_rows <= 0 asks
-    for that one launch.  The sweep pays only when a round's selections
-    repeat each cached block: 1,536 x 512 selections over 32,768 blocks
-    come to 24 per block at 128K, but 3 at a 1M-token context, where 4,096-
-    row launches are faster (3.91 against 4.03 ms per 8,192 queries); the
-    default takes one-round launches at 8 or more per block.  The fused KL form (attend_with_kl) launches kl_rows
-    rows, by default the same count (its time is the same at 1,536 and
-    4,096 rows, 1% longer at its own 512).
+    launches of attn_rows rows.  The attention runs one one-wave workgroup
+    per query and KV head, and the device deals workgroups to its XCDs in
+    turn, so each XCD gathers the rows of one KV head.  By default a launch
+    holds as many queries as the device runs workgroups of the kernel at
+    once (1,536 on MI355X at Hkv = 2, budget 512): every query costs about
+    the same, so workgroups run in rounds of that size, and each query walks
+    its block list in ascending block order: within one round the
+    concurrent gathers sweep the cache as a narrow band, which L2 and the
+    Infinity Cache hold.  Launches that span several rounds let the
+    workgroups drift apart and the band widen.  The 128K prefill's attention
+    takes 41.0 ms in 1,536-row launches, 42.1 ms in 3,072-row launches,
+    42.6 ms in 4,096-row launches and 58.4 ms as one launch of 131,072 rows
+    (attn_rows <= 0 asks for that one launch); half-round launches leave CUs
+    idle (768 rows: 60.8 ms).  The sweep pays only when a round's
+    selections repeat each cached block: 1,536 x 512 selections over 32,768
+    blocks come to 24 per block at 128K, but 3 at a 1M-token context, where
+    4,096-row launches are faster (3.98 against 4.11-4.24 ms per 8,192
+    queries); the default takes one-round launches at 8 or more per block.
+    The KL form (attend_with_kl) launches kl_rows rows, by default the
+    plain kernel's round.
     pipeline_rows > 0 (and < Tq) instead selects the queries in chunks of
     that many rows and runs each chunk's attention on a second stream while
     the next chunk is selected; the results are those of the stages run one
@@ -80,7 +83,7 @@ class QSAPrefill:
                  theta: float = 1e7, rope_dim: int = 64, fresh: bool = True,
                  idx_rope_dim: int = 0, kbar_gain=None, pages=None, pipeline_rows: int = 0,
                  attn_rows: int | None = None, kl_rows: int | None = None,
-                 rope_on_load: bool = True, device="cuda"):
+                 rope_on_load: bool = True, kl_staged: bool = True, device="cuda"):
         self.Tq, self.pos0, self.H, self.Hkv, self.D = Tq, pos0, H, Hkv, D
         self.pages = pages  # paged caches (fresh=False): K, V and kbar are page pools
         self.Tk = pos0 + Tq
@@ -115,6 +118,8 @@ class QSAPrefill:
         if kl_rows is None:
             kl_rows = qsa_sparse_attn_prefill_concurrency(Hkv, budget) or ATTN_ROWS
         self.kl_rows = kl_rows if kl_rows > 0 else Tq
+        self.kl_staged = kl_staged
+        self._kl_ws = None  # workspace of the staged KL form, allocated on first use
         self.ws_bytes = qsa_select_workspace_bytes(1, self.pipeline_rows or Tq, self.nb, budget)
         self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=dev)
         # the attention stream of the pipeline (default priority)
@@ -192,16 +197,32 @@ class QSAPrefill:
         """Training form of attend(), after select(): the sparse attention of
         every row fused with the distillation KL under the sparse pattern
         (kl: fp32 [Tq]); qi and kbar as given to the selection (qi after
-        rope_indexer).  Contiguous caches; launches of kl_rows rows."""
+        rope_indexer).  Contiguous caches; launches of kl_rows rows.  By
+        default the staged form (the plain attention writing each selected
+        block's max logits, then the KL: the attention's head placement and
+        occupancy; a workspace of about 48 KB per row of a launch); with
+        kl_staged=False the one-kernel form (everything on chip).  Both give
+        the same bits."""
         if self.pages is not None:
             raise ValueError("attend_with_kl: the fused KL runs on contiguous caches only")
-        for r0, n in self._chunks(self.kl_rows):
+        rows = min(self.kl_rows, self.Tq)
+        if self.kl_staged and self._kl_ws is None:
+            wsb = qsa_sparse_attn_prefill_kl_staged_workspace_bytes(rows, self.budget)
+            self._kl_ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device=self.dev)
+        for r0, n in self._chunks(rows):
             p0 = self.pos0 + r0
-            qsa_sparse_attn_prefill_kl(self.Qr[r0:r0 + n], Kr, V, qi[r0:r0 + n], kbar,
-                                       self.blk_idx[r0:r0 + n], self.n_sel[r0:r0 + n], n, p0 + n,
-                                       p0, self.H, self.Hkv, self.D, HI, DI, R, self.budget,
-                                       self.score_mode, self.O[r0:r0 + n], self.lse[r0:r0 + n],
-                                       kl[r0:r0 + n])
+            sel = (self.blk_idx[r0:r0 + n], self.n_sel[r0:r0 + n], n, p0 + n, p0, self.H,
+                   self.Hkv, self.D, HI, DI, R, self.budget, self.score_mode,
+                   self.O[r0:r0 + n], self.lse[r0:r0 + n], kl[r0:r0 + n])
+            if not self.kl_staged:
+                qsa_sparse_attn_prefill_kl(self.Qr[r0:r0 + n], Kr, V, qi[r0:r0 + n], kbar, *sel)
+                continue
+            on_load = self.rope_on_load and self._q is not None
+            q = self._q if on_load else self.Qr
+            qsa_sparse_attn_prefill_kl_staged(q[r0:r0 + n], Kr, V, qi[r0:r0 + n], kbar, *sel,
+                                              self._kl_ws, self._kl_ws.numel(),
+                                              rope_dim=self.rope_dim if on_load else 0,
+                                              theta=self.theta)
 
     def select(self, qi, kbar):
         for r0, n in self._chunks():

@@ -342,6 +342,31 @@ int qsa_sparse_attn_prefill_kl(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_b
                                int r, int Kbudget, int score_mode, float *O, float *lse,
                                float *kl, void *stream);
 
+/* ---- The same distillation KL and sparse attention in two launches, for
+ * throughput (ai.info "Industry relevance" and chlience section 6 as above).
+ * The first launch is the plain sparse prefill (one wave per query and KV
+ * head, the KV heads on separate XCDs, all its waves resident at once),
+ * which also writes, per query, the max logit of every (selected block,
+ * head) and each head's log-sum-exp to the workspace; the second turns them
+ * into the teacher's block masses and the KL, with the student scores
+ * recomputed as in the one-kernel form.  O, lse and kl equal the one-kernel
+ * form's bit for bit (same arithmetic in the same order).  rope_dim 0: Q is
+ * post-RoPE; rope_dim 64 or 128: Q is before RoPE and is rotated on load
+ * with base theta, as qsa_sparse_attn_prefill_rope.  Workspace:
+ * qsa_sparse_attn_prefill_kl_staged_workspace_bytes(Tq, Kbudget) bytes,
+ * 16-byte aligned, scratch (about 48 KB per query at Kbudget 512; callers
+ * bound it by calling per chunk of rows); the bytes function returns 0 for
+ * invalid arguments.  Other arguments and support as
+ * qsa_sparse_attn_prefill_kl, except Kbudget <= 2048. */
+size_t qsa_sparse_attn_prefill_kl_staged_workspace_bytes(int64_t Tq, int Kbudget);
+int qsa_sparse_attn_prefill_kl_staged(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
+                                      const qsa_bf16 *q_idx, const qsa_bf16 *kbar,
+                                      const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq,
+                                      int64_t Tk, int64_t pos0, int H, int Hkv, int D, int Hi,
+                                      int Di, int r, int Kbudget, int score_mode, int rope_dim,
+                                      double theta, float *O, float *lse, float *kl, void *ws,
+                                      size_t ws_bytes, void *stream);
+
 /* ---- Launch sizing of the sparse prefill (A6; the same kernels as
  * qsa_sparse_attn_prefill and, with with_kl, qsa_sparse_attn_prefill_kl;
  * paged: over page pools).  Returns the number of queries whose workgroups

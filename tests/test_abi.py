@@ -371,6 +371,47 @@ def test_sparse_attn_prefill_kl_validation(lib):
     assert attn_kl(lib, Tq=0, lse=0) == OK               # lse is optional
 
 
+def attn_kl_staged(lib, Q=P, K=P, V=P, qi=P, kb=P, blk=P, ns=P, Tq=8, Tk=64, pos0=0, H=24,
+                   Hkv=2, D=256, Hi=4, Di=128, r=4, Kb=512, mode=0, rope_dim=0, theta=1e7, O=P,
+                   lse=P, kl=P, ws=P, wsb=None):
+    f = lib.qsa_sparse_attn_prefill_kl_staged
+    f.argtypes = ([ctypes.c_void_p] * 7 + [ctypes.c_int64] * 3 + [ctypes.c_int] * 9 +
+                  [ctypes.c_double] + [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p])
+    if wsb is None:
+        wsb = Tq * (2 * Kb * 12 + 24) * 4
+    return f(vp(Q), vp(K), vp(V), vp(qi), vp(kb), vp(blk), vp(ns), Tq, Tk, pos0, H, Hkv, D, Hi,
+             Di, r, Kb, mode, rope_dim, theta, vp(O), vp(lse), vp(kl), vp(ws), wsb, None)
+
+
+def test_sparse_attn_prefill_kl_staged_validation(lib):
+    """The two-launch KL form: its workspace, RoPE and budget arguments,
+    then the checks it shares with the one-kernel form (each call fails on
+    the host, or has nothing to do)."""
+    wsb = lib.qsa_sparse_attn_prefill_kl_staged_workspace_bytes
+    wsb.restype, wsb.argtypes = ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int]
+    assert wsb(8, 512) == 8 * (2 * 512 * 12 + 24) * 4    # block maxima, then lse2
+    assert wsb(1536, 2048) == 1536 * (2 * 2048 * 12 + 24) * 4
+    assert wsb(8, 0) == 0 and wsb(8, 2049) == 0 and wsb(-1, 512) == 0
+    assert wsb(0, 512) == 0
+    assert attn_kl_staged(lib, ws=0) == WORKSPACE
+    assert attn_kl_staged(lib, wsb=8 * (2 * 512 * 12 + 24) * 4 - 1) == WORKSPACE
+    assert attn_kl_staged(lib, ws=MIS) == ALIGN
+    assert attn_kl_staged(lib, rope_dim=32) == UNSUP
+    assert attn_kl_staged(lib, rope_dim=96) == UNSUP
+    assert attn_kl_staged(lib, rope_dim=-64) == SHAPE
+    assert attn_kl_staged(lib, rope_dim=64, theta=0.0) == SHAPE
+    assert attn_kl_staged(lib, Kb=2049) == UNSUP           # above every form's budget
+    assert attn_kl_staged(lib, Kb=0) == SHAPE
+    assert attn_kl_staged(lib, kl=0) == NULL
+    assert attn_kl_staged(lib, qi=0) == NULL
+    assert attn_kl_staged(lib, Tq=8, Tk=7) == SHAPE
+    assert attn_kl_staged(lib, H=16) == UNSUP
+    assert attn_kl_staged(lib, D=128) == UNSUP
+    assert attn_kl_staged(lib, mode=2) == SHAPE
+    assert attn_kl_staged(lib, Q=MIS) == ALIGN
+    assert attn_kl_staged(lib, Tq=0, ws=0, wsb=0) == OK    # nothing to do, nothing enqueued
+
+
 def noalloc(lib, q=P, Kc=P, Vc=P, sl=P, blk=P, ns=P, B=2, Tq=1, Lmax=64, H=24, Hkv=2, D=256,
             r=4, K=8, O=P, lse=P, pages=None):
     return lib.qsa_sparse_attn_decode_noalloc(vp(q), vp(Kc), vp(Vc), vp(sl), vp(blk), vp(ns), B,

@@ -51,6 +51,24 @@ def run_fused(qsa, dQ, dK, dV, dqi, dkb, blk, ns, Tq, Tk, pos0, K, mode):
     return O, lse, kl
 
 
+def run_staged(qsa, dQ, dK, dV, dqi, dkb, blk, ns, Tq, Tk, pos0, K, mode, rope_dim=0):
+    """The two-launch form (plain attention writing block maxima, then the
+    KL) through the C ABI; rope_dim > 0: dQ is before RoPE."""
+    import torch
+    O = torch.full((Tq, 24, 256), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((Tq, 24), float("nan"), dtype=torch.float32, device="cuda")
+    kl = torch.full((Tq,), float("nan"), dtype=torch.float32, device="cuda")
+    wsb = qsa.qsa_sparse_attn_prefill_kl_staged_workspace_bytes(Tq, K)
+    assert wsb == Tq * (2 * K * 12 + 24) * 4
+    # 0xFF bytes: every float of the workspace starts as a NaN
+    ws = torch.full((max(wsb, 16),), 255, dtype=torch.uint8, device="cuda")
+    qsa.qsa_sparse_attn_prefill_kl_staged(dQ, dK, dV, dqi, dkb, blk, ns, Tq, Tk, pos0, 24, 2, 256,
+                                          4, 128, 4, K, mode, O, lse, kl, ws, wsb,
+                                          rope_dim=rope_dim, theta=1e7)
+    torch.cuda.synchronize()
+    return O, lse, kl
+
+
 def run_plain(qsa, dQ, dK, dV, blk, ns, Tq, Tk, pos0, K):
     import torch
     O = torch.empty((Tq, 24, 256), dtype=torch.float32, device="cuda")
@@ -83,6 +101,9 @@ def fused_case(qsa, x, Tq, pos0, K, mode, rows):
     assert torch.equal(O, O2) and torch.equal(lse, lse2), "outputs differ from the plain kernel"
     _, _, kl2 = run_fused(qsa, dQ, dK, dV, dqi, dkb, blk, ns, Tq, Tk, pos0, K, mode)
     assert torch.equal(kl, kl2), "two runs differ"
+    O3, lse3, kl3 = run_staged(qsa, dQ, dK, dV, dqi, dkb, blk, ns, Tq, Tk, pos0, K, mode)
+    assert torch.equal(O, O3) and torch.equal(lse, lse3), "staged form: O or lse differ"
+    assert torch.equal(kl, kl3), "staged form: kl differs"
     got = kl.cpu().numpy().astype(np.float64)
     sel, nsel = blk.cpu().numpy(), ns.cpu().numpy()
     ref = oracle.sparse_kl_rows(x.Q, x.K, x.qi, kb, rows, sel[rows], nsel[rows], pos0=pos0,
@@ -162,6 +183,8 @@ def test_fused_kl_empty_and_clamped_selections(qsa):
     O, lse, kl = run_fused(qsa, dQ, dK, dV, dqi, dkb, blk, ns, T, T, 0, K, 0)
     O2, lse2 = run_plain(qsa, dQ, dK, dV, blk, ns, T, T, 0, K)
     assert torch.equal(O, O2) and torch.equal(lse, lse2)
+    O3, lse3, kl3 = run_staged(qsa, dQ, dK, dV, dqi, dkb, blk, ns, T, T, 0, K, 0)
+    assert torch.equal(O, O3) and torch.equal(lse, lse3) and torch.equal(kl, kl3)
     got = kl.cpu().numpy().astype(np.float64)
     assert np.all(got[100:140] == 0.0)
     rows = np.r_[np.arange(96, 100), np.arange(900, 910)]
@@ -187,6 +210,33 @@ def test_fused_kl_128k_context_chunk(qsa, mode):
     got, ref, _, nsel = fused_case(qsa, x, Tq, pos0, 512, mode, rows)
     assert np.all(nsel == 512)
     check_kl(got[rows], ref, f"128K context, mode {mode}, sampled rows")
+
+
+def test_staged_kl_rotates_on_load_and_takes_larger_budgets(qsa):
+    """The staged form on queries before RoPE (rotated on load) equals the
+    one-kernel form on the rotated queries bit for bit; at a budget of 2,048
+    blocks (beyond the one-kernel form) its kl matches the oracle."""
+    import torch
+    T = 2100
+    x = synth.prefill_inputs(T, seed=93, needles_per_head=4)
+    kb = oracle.compress(x.ki)
+    dQ, dK, dV, dqi, dkb = dev(x.Q), dev(x.K), dev(x.V), dev(x.qi), dev(kb)
+    Qr = torch.empty_like(dQ)
+    qsa.qsa_rope_bf16(dQ, Qr, T, 24, 256, 64, 1e7, 0)
+    dKr = torch.empty_like(dK)
+    qsa.qsa_rope_bf16(dK, dKr, T, 2, 256, 64, 1e7, 0)
+    blk, ns = gpu_select(qsa, x.qi, kb, T, 0, 256, 0)
+    O, lse, kl = run_fused(qsa, Qr, dKr, dV, dqi, dkb, blk, ns, T, T, 0, 256, 0)
+    O3, lse3, kl3 = run_staged(qsa, dQ, dKr, dV, dqi, dkb, blk, ns, T, T, 0, 256, 0, rope_dim=64)
+    assert torch.equal(O, O3) and torch.equal(lse, lse3) and torch.equal(kl, kl3)
+    # budget 2,048 over T = 2,100 (rows past 8,191 would select a subset;
+    # here every row takes all its complete blocks)
+    blk2, ns2 = gpu_select(qsa, x.qi, kb, T, 0, 2048, 1)
+    _, _, kl4 = run_staged(qsa, dQ, dK, dV, dqi, dkb, blk2, ns2, T, T, 0, 2048, 1)
+    rows = np.unique(np.r_[0, 3, 4, np.arange(9, T, 97), T - 1])
+    ref = oracle.sparse_kl_rows(x.Q, x.K, x.qi, kb, rows, blk2.cpu().numpy()[rows],
+                                ns2.cpu().numpy()[rows], mode=1)
+    check_kl(kl4.cpu().numpy().astype(np.float64)[rows], ref, "staged form, budget 2048")
 
 
 def test_layer_attend_with_kl_in_row_chunks(qsa):
