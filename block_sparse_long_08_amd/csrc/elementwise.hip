@@ -69,14 +69,72 @@ __global__ void __launch_bounds__(256) rope_kernel(const uint16_t *__restrict__ 
     }
 }
 
+// Rows with few pairs (the keys' 2 heads, the indexer's 4): rpw rows per
+// workgroup, so that one round of fp64 angles (one per thread) and one
+// barrier serve several rows; the same arithmetic as rope_kernel.  Threads
+// take the rows' angles, then their untouched dims, then their pairs.
+constexpr int kRopeMaxRows = 8;
+
+__global__ void __launch_bounds__(256) rope_rows_kernel(const uint16_t *__restrict__ x,
+                                                        uint16_t *__restrict__ y, int64_t T,
+                                                        int nheads, int head_dim, int rope_dim,
+                                                        InvFreq inv_freq, int64_t pos0,
+                                                        const int64_t *__restrict__ seq_len,
+                                                        int nq, int rpw) {
+#pragma clang fp contract(off)
+    __shared__ double cs[kRopeMaxRows][64], sn[kRopeMaxRows][64];
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * rpw;
+    const int rows = static_cast<int>(min(static_cast<int64_t>(rpw), T - t0));
+    const int half = rope_dim / 2;
+    const int64_t row_elems = static_cast<int64_t>(nheads) * head_dim;
+    for (int idx = threadIdx.x; idx < rows * half; idx += blockDim.x) {
+        const int r = idx / half, j = idx - r * half;
+        const int64_t t = t0 + r;
+        // decode form: row t is query t % nq of sequence t / nq
+        int64_t p = seq_len ? seq_len[t / nq] - nq + t % nq : pos0 + t;
+        if (p < 0) p = 0;
+        rope_angle(p, inv_freq.v[j], cs[r][j], sn[r][j]);
+    }
+    if (y != x) {
+        // the untouched dims, 16 bytes at a time
+        const int per_head = (head_dim - rope_dim) / 8;
+        const int per_row = nheads * per_head;
+        for (int idx = threadIdx.x; idx < rows * per_row; idx += blockDim.x) {
+            const int r = idx / per_row, rest = idx - r * per_row;
+            const int h = rest / per_head, c = rest - h * per_head;
+            const int64_t off = (t0 + r) * row_elems + h * head_dim + rope_dim;
+            reinterpret_cast<uint4 *>(y + off)[c] = reinterpret_cast<const uint4 *>(x + off)[c];
+        }
+    }
+    block_sync();
+    const int npairs = nheads * half;
+    for (int idx = threadIdx.x; idx < rows * npairs; idx += blockDim.x) {
+        const int r = idx / npairs, rest = idx - r * npairs;
+        const int h = rest / half, j = rest - h * half;
+        const int64_t off = (t0 + r) * row_elems + h * head_dim;
+        uint16_t o0, o1;
+        rope_pair(x[off + j], x[off + j + half], cs[r][j], sn[r][j], o0, o1);
+        y[off + j] = o0;
+        y[off + j + half] = o1;
+    }
+}
+
 hipError_t launch_rope(const uint16_t *x, uint16_t *y, int64_t T, int nheads, int head_dim,
                        int rope_dim, const double *inv_freq, int64_t pos0,
                        const int64_t *seq_len, int nq, hipStream_t s) {
     if (T == 0) return hipSuccess;
     InvFreq f;
     for (int j = 0; j < 64; ++j) f.v[j] = j < rope_dim / 2 ? inv_freq[j] : 0.0;
-    hipLaunchKernelGGL(rope_kernel, dim3(static_cast<uint32_t>(T)), dim3(256), 0, s, x, y, T,
-                       nheads, head_dim, rope_dim, f, pos0, seq_len, nq);
+    const int npairs = nheads * (rope_dim / 2);
+    const int rpw = npairs > 0 ? min(kRopeMaxRows, 256 / npairs) : 1;
+    if (rpw >= 2) {
+        const int64_t nwg = (T + rpw - 1) / rpw;
+        hipLaunchKernelGGL(rope_rows_kernel, dim3(static_cast<uint32_t>(nwg)), dim3(256), 0, s,
+                           x, y, T, nheads, head_dim, rope_dim, f, pos0, seq_len, nq, rpw);
+    } else {
+        hipLaunchKernelGGL(rope_kernel, dim3(static_cast<uint32_t>(T)), dim3(256), 0, s, x, y,
+                           T, nheads, head_dim, rope_dim, f, pos0, seq_len, nq);
+    }
     return hipGetLastError();
 }
 
