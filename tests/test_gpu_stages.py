@@ -300,7 +300,9 @@ def test_selection_tie_band(qsa, mode):
                                             (1, 700, 140000, 512), (0, 300, 1048000, 512),
                                             (1, 260, 1048000, 2048), (0, 600, 100000, 512),
                                             (0, 2000, 64000, 512), (0, 2000, 64000, 100),
-                                            (0, 60000, 0, 512), (1, 20000, 32000, 512)])
+                                            (0, 60000, 0, 512), (1, 20000, 32000, 512),
+                                            (1, 300, 300000, 512), (0, 512, 262144, 64),
+                                            (1, 260, 600000, 300)])
 def test_select_matches_scores_plus_topk(qsa, mode, Tq, pos0, K):
     """qsa_select_blocks returns exactly what qsa_index_scores followed by
     qsa_topk_blocks returns (same scores bit for bit, same tie order);
@@ -312,9 +314,10 @@ def test_select_matches_scores_plus_topk(qsa, mode, Tq, pos0, K):
     fewer groups (or crowded lists) go to the streaming kernel (the 60,000
     and 20,000-row cases hold all of these, and rows of nc <= K); larger
     budgets take the streaming kernel, with its floor from the group maxima
-    for rows of at least 4 groups per thread; qsa_topk_blocks alone reads
-    the scores only, so the paths must agree exactly, RELUSUM zero runs
-    included."""
+    for rows of at least 4 groups per thread (the 300,000, 262,144 and
+    600,000 cases add long rows in both modes and budgets of 64 and 300);
+    qsa_topk_blocks alone reads the scores only, so the paths must agree
+    exactly, RELUSUM zero runs included."""
     torch = _torch()
     Tk = pos0 + Tq
     qi = synth.normal_bf16(4, (Tq, 4, 128), seed=13)
