@@ -425,8 +425,9 @@ def bench_decode(name, steps, warmup, with_dense=True):
             torch.cuda.synchronize()
             dms = _time_steps(run, steps)
             del Od, ws
+        on_load = dec.rope_on_load
         del dec
-        return _decode_rates(B, L, budget, n, ms, dms)
+        return dict(_decode_rates(B, L, budget, n, ms, dms), q_rope_on_load=on_load)
 
     res = one(1, q, qi)
     n = DECODE_NEXT_N.get(name)

@@ -58,6 +58,8 @@ _sig("qsa_sparse_attn_prefill_rope", _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, 
 _sig("qsa_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32, _i32)
 _sig("qsa_sparse_attn_decode", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32,
      _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp, _vp)
+_sig("qsa_sparse_attn_decode_rope", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32,
+     _i32, _i32, _i32, _i32, _i32, _dbl, _vp, _vp, _vp, _sz, _vp, _vp)
 _sig("qsa_decode_noalloc_max_bytes", _sz)
 _sig("qsa_sparse_attn_decode_noalloc", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32,
      _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp)
@@ -79,7 +81,7 @@ EXPORTED = ["qsa_status_string", "qsa_version", "qsa_check_device", "qsa_rope_bf
             "qsa_compress_keys", "qsa_index_scores", "qsa_topk_workspace_bytes",
             "qsa_topk_blocks", "qsa_select_workspace_bytes", "qsa_select_blocks",
             "qsa_sparse_attn_prefill", "qsa_sparse_attn_prefill_rope",
-            "qsa_decode_workspace_bytes", "qsa_sparse_attn_decode",
+            "qsa_decode_workspace_bytes", "qsa_sparse_attn_decode", "qsa_sparse_attn_decode_rope",
             "qsa_decode_noalloc_max_bytes", "qsa_sparse_attn_decode_noalloc",
             "dense_attn_workspace_bytes", "dense_attn", "qsa_distill_workspace_bytes",
             "qsa_distill_kl", "qsa_sparse_attn_prefill_kl", "qsa_sparse_attn_prefill_concurrency",
@@ -297,6 +299,26 @@ def qsa_sparse_attn_decode(q, Kc, Vc, seq_len, blk_idx, n_sel, B: int, Tq: int, 
     _call("qsa_sparse_attn_decode", _ptr(q), _ptr(Kc), _ptr(Vc), _ptr(seq_len), _ptr(blk_idx),
           _ptr(n_sel), B, Tq, Lmax, H, Hkv, D, r, Kbudget, _ptr(O), _ptr(lse), _ptr(ws),
           ws_bytes, _pages(pages), _stream(stream))
+
+
+def qsa_sparse_attn_decode_rope(q, Kc, Vc, seq_len, blk_idx, n_sel, B: int, Tq: int, Lmax: int,
+                                H: int, Hkv: int, D: int, r: int, Kbudget: int, rope_dim: int,
+                                theta: float, O, lse, ws, ws_bytes: int, stream=None,
+                                pages=None) -> None:
+    """qsa_sparse_attn_decode with q before RoPE: the kernel rotates it on load."""
+    f = "qsa_sparse_attn_decode_rope"
+    _req(f, "q", q, 2, B * Tq * H * D * 2)
+    _req(f, "Kc", Kc, 2, 2 if pages is not None else B * Lmax * Hkv * D * 2)
+    _req(f, "Vc", Vc, 2, 2 if pages is not None else B * Lmax * Hkv * D * 2)
+    _req(f, "seq_len", seq_len, 8, B * 8)
+    _req(f, "blk_idx", blk_idx, 4, B * Kbudget * 4)
+    _req(f, "n_sel", n_sel, 4, B * 4)
+    _req(f, "O", O, 4, B * Tq * H * D * 4)
+    _req(f, "lse", lse, 4, B * Tq * H * 4)
+    _req(f, "ws", ws, 1, ws_bytes)
+    _call(f, _ptr(q), _ptr(Kc), _ptr(Vc), _ptr(seq_len), _ptr(blk_idx), _ptr(n_sel), B, Tq, Lmax,
+          H, Hkv, D, r, Kbudget, rope_dim, float(theta), _ptr(O), _ptr(lse), _ptr(ws), ws_bytes,
+          _pages(pages), _stream(stream))
 
 
 def qsa_decode_noalloc_max_bytes() -> int:

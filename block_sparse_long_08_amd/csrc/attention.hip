@@ -302,28 +302,39 @@ __device__ __forceinline__ void rope_quad(uint4 &a, uint4 &b, const double *ang,
 // single query's angles) the first 64 * hs dims are rotated on load: the
 // NeoX partner of dim j < 32 hs is j + 32 hs, element k of qT[s + hs], so
 // every pair sits in one lane (hs = 1 or 2: rope_dim 64 or 128).
-__device__ __forceinline__ void load_qT(const uint16_t *__restrict__ qrow, int g, int group,
-                                        int H, int ct, int ncols, int lane, bf16x8 (&qT)[8],
-                                        const double *ang = nullptr, int hs = 0) {
+__device__ __forceinline__ bool load_q_raw(const uint16_t *__restrict__ qrow, int g, int group,
+                                           int H, int ct, int ncols, int lane, uint4 (&v)[8]) {
     const int n = lane & 15, g4 = lane >> 4;
     const int pair = 16 * ct + n;
     const bool ok = pair < ncols;
     const int qi = ok ? pair / group : 0, h = ok ? pair - qi * group : 0;
     const uint16_t *src =
         qrow + (static_cast<int64_t>(qi) * H + g * group + h) * kHeadDim;
-    uint4 v[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
         v[s] = ok ? *reinterpret_cast<const uint4 *>(src + 32 * s + 8 * g4)
                   : make_uint4(0, 0, 0, 0);
-    if (ang && ok) {
-        if (hs == 1) {
-            rope_quad(v[0], v[1], ang, 8 * g4);
-        } else {
-            rope_quad(v[0], v[2], ang, 8 * g4);
-            rope_quad(v[1], v[3], ang, 32 + 8 * g4);
-        }
+    return ok;
+}
+
+// Rotates the lane's loaded query dims by the angles ang (cosines [0, 64),
+// sines [64, 128) of the lane's query position).
+__device__ __forceinline__ void rope_q(uint4 (&v)[8], const double *ang, int hs, int lane) {
+    const int g4 = lane >> 4;
+    if (hs == 1) {
+        rope_quad(v[0], v[1], ang, 8 * g4);
+    } else {
+        rope_quad(v[0], v[2], ang, 8 * g4);
+        rope_quad(v[1], v[3], ang, 32 + 8 * g4);
     }
+}
+
+__device__ __forceinline__ void load_qT(const uint16_t *__restrict__ qrow, int g, int group,
+                                        int H, int ct, int ncols, int lane, bf16x8 (&qT)[8],
+                                        const double *ang = nullptr, int hs = 0) {
+    uint4 v[8];
+    const bool ok = load_q_raw(qrow, g, group, H, ct, ncols, lane, v);
+    if (ang && ok) rope_q(v, ang, hs, lane);
 #pragma unroll
     for (int s = 0; s < 8; ++s) qT[s] = as_bf16x8(v[s]);
 }
@@ -677,10 +688,13 @@ __device__ __forceinline__ void record_store(const WaveState &st, float *rec, in
 // reads of the split's keys and values (one HBM read per split, not one
 // per column tile).
 template <bool DENSE, bool MULTI, bool PAGED>
-__global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit, int sps,
-                                                          int nct) {
+__global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, RopeArgs ra, int nsplit,
+                                                          int sps, int nct) {
     constexpr int PMODE = PAGED ? (DENSE ? 2 : 1) : 0;
     __shared__ __attribute__((aligned(16))) unsigned char lds[3 * kRecFloats * 4];
+    // the value tiles of the 4 waves, then (rotation on load) the angles of
+    // up to 16 query positions, 128 doubles each
+    static_assert(4 * kVStageBytes + 16 * 128 * 8 <= 3 * kRecFloats * 4, "decode LDS");
     __shared__ int32_t lst[DENSE ? 1 : kMaxListLds];
     const int bx = blockIdx.x, grp = bx / (8 * nct), rem = bx - grp * 8 * nct;
     const int ct = rem >> 3, split = 8 * grp + (rem & 7);
@@ -713,9 +727,11 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit
     const int s0 = split * sps, s1 = min(s0 + sps, nstages);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int group = a.H / a.Hkv;
-    // the query rows are read while the block list arrives
-    bf16x8 qT[8];
-    load_qT(a.Q + b * nq * a.H * kHeadDim, g, group, a.H, ct, nq * group, lane, qT);
+    // the query rows are read while the block list arrives (and, with
+    // ra.half > 0, rotated once the angles of their positions are formed)
+    uint4 qv[8];
+    const bool qok = load_q_raw(a.Q + b * nq * a.H * kHeadDim, g, group, a.H, ct, nq * group,
+                                lane, qv);
     const int32_t *ptab = PAGED ? a.ptable + b * a.pstride : nullptr;
     if (!DENSE) {
         // paged: pool blocks of the split's entries, tail entries included
@@ -728,11 +744,29 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, int nsplit
                 static_cast<int32_t>(PAGED ? page_row(ptab, a.pshift, 4 * bi) >> 2 : bi);
         }
     }
+    // angles of the tile's query positions q_lo .. q_hi (the positions the
+    // RoPE kernel gives decode rows: seq_len - Tq + query, at least 0)
+    double *ang = reinterpret_cast<double *>(lds + 4 * kVStageBytes);
+    const int q_lo = 16 * ct / group;
+    if (ra.half > 0) {
+        const int q_hi = min(nq - 1, (16 * ct + 15) / group);
+        const int cnt = (q_hi - q_lo + 1) * ra.half;
+        for (int i = static_cast<int>(threadIdx.x); i < cnt; i += 256) {
+            const int qq = i / ra.half, j = i - qq * ra.half;
+            const int64_t pp = a.seq_len[b] - nq + q_lo + qq;
+            rope_angle(pp < 0 ? 0 : pp, ra.inv_freq[j], ang[qq * 128 + j],
+                       ang[qq * 128 + 64 + j]);
+        }
+    }
     EntryList<MULTI, PMODE> L{DENSE ? nullptr : lst, e_lo, ns, tail, nc, ptab, a.pshift};
     block_sync();
 
     // position of this lane's column query (-1: no query, every token masked)
     const int pair = 16 * ct + (lane & 15);
+    if (ra.half > 0 && qok) rope_q(qv, ang + (pair / group - q_lo) * 128, ra.half / 32, lane);
+    bf16x8 qT[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qT[s] = as_bf16x8(qv[s]);
     const int64_t pq = pair < nq * group ? p0 + pair / group : -1;
     const int64_t rs = static_cast<int64_t>(a.Hkv) * kHeadDim;
     const int64_t seq_off = PAGED ? 0 : b * a.Lmax * rs;
@@ -929,28 +963,29 @@ size_t decode_partial_floats(int B, int Hkv, int nsplit) {
 }
 
 template <bool DENSE, bool MULTI>
-static void launch_decode_paging(const AttnArgs &a, dim3 grid, int nsplit, int sps, int nct,
-                                 bool paged, hipStream_t s) {
+static void launch_decode_paging(const AttnArgs &a, const RopeArgs &ra, dim3 grid, int nsplit,
+                                 int sps, int nct, bool paged, hipStream_t s) {
     if (paged)
         hipLaunchKernelGGL((attn_decode_kernel<DENSE, MULTI, true>), grid, dim3(256), 0, s, a,
-                           nsplit, sps, nct);
+                           ra, nsplit, sps, nct);
     else
         hipLaunchKernelGGL((attn_decode_kernel<DENSE, MULTI, false>), grid, dim3(256), 0, s, a,
-                           nsplit, sps, nct);
+                           ra, nsplit, sps, nct);
 }
 
-static void launch_decode_variant(const AttnArgs &a, dim3 grid, int nsplit, int sps, int nct,
-                                  bool dense, bool multi, bool paged, hipStream_t s) {
+static void launch_decode_variant(const AttnArgs &a, const RopeArgs &ra, dim3 grid, int nsplit,
+                                  int sps, int nct, bool dense, bool multi, bool paged,
+                                  hipStream_t s) {
     if (dense) {
         if (multi)
-            launch_decode_paging<true, true>(a, grid, nsplit, sps, nct, paged, s);
+            launch_decode_paging<true, true>(a, ra, grid, nsplit, sps, nct, paged, s);
         else
-            launch_decode_paging<true, false>(a, grid, nsplit, sps, nct, paged, s);
+            launch_decode_paging<true, false>(a, ra, grid, nsplit, sps, nct, paged, s);
     } else {
         if (multi)
-            launch_decode_paging<false, true>(a, grid, nsplit, sps, nct, paged, s);
+            launch_decode_paging<false, true>(a, ra, grid, nsplit, sps, nct, paged, s);
         else
-            launch_decode_paging<false, false>(a, grid, nsplit, sps, nct, paged, s);
+            launch_decode_paging<false, false>(a, ra, grid, nsplit, sps, nct, paged, s);
     }
 }
 
@@ -985,7 +1020,7 @@ hipError_t decode_scratch(size_t need, float **ptr) {
     return hipSuccess;
 }
 
-hipError_t launch_attn_decode(const AttnArgs &a, int nsplit, hipStream_t s) {
+hipError_t launch_attn_decode(const AttnArgs &a, const RopeArgs &ra, int nsplit, hipStream_t s) {
     if (a.B == 0) return hipSuccess;
     const int nq = static_cast<int>(a.Tq);
     const int nct = decode_col_tiles(nq, a.H / a.Hkv);
@@ -995,7 +1030,7 @@ hipError_t launch_attn_decode(const AttnArgs &a, int nsplit, hipStream_t s) {
     const int sps = static_cast<int>((nstages + nsplit - 1) / nsplit);
     const dim3 grid(static_cast<uint32_t>((nsplit + 7) / 8 * 8 * nct),
                     static_cast<uint32_t>(a.Hkv), static_cast<uint32_t>(a.B));
-    launch_decode_variant(a, grid, nsplit, sps, nct, a.blk_idx == nullptr, nq > 1,
+    launch_decode_variant(a, ra, grid, nsplit, sps, nct, a.blk_idx == nullptr, nq > 1,
                           a.ptable != nullptr, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

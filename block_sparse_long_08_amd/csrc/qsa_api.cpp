@@ -316,6 +316,19 @@ int qsa_select_blocks(const qsa_bf16 *q_idx, const qsa_bf16 *kbar, int B, int64_
     return QSA_OK;
 }
 
+// RoPE arguments of the rotate-on-load entry points: rope_dim 64 or 128
+// (the NeoX partners then sit in one lane's query fragment), theta > 0; the
+// frequencies exactly as qsa_rope_bf16 forms them.
+static int rope_args(int rope_dim, double theta, RopeArgs &ra) {
+    ra = RopeArgs{};
+    if (rope_dim <= 0 || !(theta > 0.0)) return QSA_ERR_SHAPE;
+    if (rope_dim != 64 && rope_dim != 128) return QSA_ERR_UNSUPPORTED;
+    ra.half = rope_dim / 2;
+    for (int j = 0; j < ra.half; ++j)
+        ra.inv_freq[j] = pow(theta, -2.0 * static_cast<double>(j) / static_cast<double>(rope_dim));
+    return QSA_OK;
+}
+
 static int sparse_prefill(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V,
                           const int32_t *blk_idx, const int32_t *n_sel, int64_t Tq, int64_t Tk,
                           int64_t pos0, int H, int Hkv, int D, int r, int Kbudget,
@@ -355,13 +368,9 @@ int qsa_sparse_attn_prefill_rope(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa
                                  int64_t Tk, int64_t pos0, int H, int Hkv, int D, int r,
                                  int Kbudget, int rope_dim, double theta, float *O, float *lse,
                                  const qsa_pages *pages, void *stream) {
-    if (rope_dim <= 0 || !(theta > 0.0)) return QSA_ERR_SHAPE;
-    if (rope_dim != 64 && rope_dim != 128) return QSA_ERR_UNSUPPORTED;
-    RopeArgs ra{};
-    ra.half = rope_dim / 2;
-    // the angles' frequencies exactly as qsa_rope_bf16 forms them
-    for (int j = 0; j < ra.half; ++j)
-        ra.inv_freq[j] = pow(theta, -2.0 * static_cast<double>(j) / static_cast<double>(rope_dim));
+    RopeArgs ra;
+    const int st = rope_args(rope_dim, theta, ra);
+    if (st != QSA_OK) return st;
     return sparse_prefill(Q, K, V, blk_idx, n_sel, Tq, Tk, pos0, H, Hkv, D, r, Kbudget, ra, O, lse,
                           pages, stream);
 }
@@ -382,11 +391,11 @@ size_t qsa_decode_workspace_bytes(int B, int Tq, int H, int Hkv, int D, int Kbud
     return decode_ws(B, Tq, H, Hkv, Kbudget, nullptr);
 }
 
-int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16 *Vc,
-                           const int64_t *seq_len, const int32_t *blk_idx, const int32_t *n_sel,
-                           int B, int Tq, int64_t Lmax, int H, int Hkv, int D, int r, int Kbudget,
-                           float *O, float *lse, void *ws, size_t ws_bytes,
-                           const qsa_pages *pages, void *stream) {
+static int sparse_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16 *Vc,
+                         const int64_t *seq_len, const int32_t *blk_idx, const int32_t *n_sel,
+                         int B, int Tq, int64_t Lmax, int H, int Hkv, int D, int r, int Kbudget,
+                         const RopeArgs &ra, float *O, float *lse, void *ws, size_t ws_bytes,
+                         const qsa_pages *pages, void *stream) {
     if (!q || !Kc || !Vc || !seq_len || !blk_idx || !n_sel || !O) return QSA_ERR_NULL;
     if (B <= 0 || Lmax < 0 || Kbudget <= 0) return QSA_ERR_SHAPE;
     if (Tq < 1 || Tq > kMaxNextN) return QSA_ERR_SHAPE;
@@ -407,7 +416,30 @@ int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16
     if (st != QSA_OK) return st;
     const PageTable pt = token_pages(pages);
     a.ptable = pt.table; a.pstride = pt.stride; a.pshift = pt.shift;
-    return launch_status(launch_attn_decode(a, nsplit, as_stream(stream)));
+    return launch_status(launch_attn_decode(a, ra, nsplit, as_stream(stream)));
+}
+
+int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16 *Vc,
+                           const int64_t *seq_len, const int32_t *blk_idx, const int32_t *n_sel,
+                           int B, int Tq, int64_t Lmax, int H, int Hkv, int D, int r, int Kbudget,
+                           float *O, float *lse, void *ws, size_t ws_bytes,
+                           const qsa_pages *pages, void *stream) {
+    RopeArgs none{};
+    return sparse_decode(q, Kc, Vc, seq_len, blk_idx, n_sel, B, Tq, Lmax, H, Hkv, D, r, Kbudget,
+                         none, O, lse, ws, ws_bytes, pages, stream);
+}
+
+int qsa_sparse_attn_decode_rope(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16 *Vc,
+                                const int64_t *seq_len, const int32_t *blk_idx,
+                                const int32_t *n_sel, int B, int Tq, int64_t Lmax, int H, int Hkv,
+                                int D, int r, int Kbudget, int rope_dim, double theta, float *O,
+                                float *lse, void *ws, size_t ws_bytes, const qsa_pages *pages,
+                                void *stream) {
+    RopeArgs ra;
+    const int st = rope_args(rope_dim, theta, ra);
+    if (st != QSA_OK) return st;
+    return sparse_decode(q, Kc, Vc, seq_len, blk_idx, n_sel, B, Tq, Lmax, H, Hkv, D, r, Kbudget,
+                         ra, O, lse, ws, ws_bytes, pages, stream);
 }
 
 size_t qsa_decode_noalloc_max_bytes(void) { return kDecodeScratchBytes; }
@@ -438,7 +470,8 @@ int qsa_sparse_attn_decode_noalloc(const qsa_bf16 *q, const qsa_bf16 *Kc, const 
     a.Tq = Tq; a.Lmax = Lmax; a.pos0 = 0; a.B = B; a.H = H; a.Hkv = Hkv; a.Kbudget = Kbudget;
     const PageTable pt = token_pages(pages);
     a.ptable = pt.table; a.pstride = pt.stride; a.pshift = pt.shift;
-    return launch_status(launch_attn_decode(a, nsplit, as_stream(stream)));
+    RopeArgs none{};
+    return launch_status(launch_attn_decode(a, none, nsplit, as_stream(stream)));
 }
 
 size_t dense_attn_workspace_bytes(int B, int64_t Tq, int64_t Lmax, int H, int Hkv, int D) {
@@ -475,7 +508,8 @@ int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, i
         const size_t need = decode_ws(B, static_cast<int>(Tq), H, Hkv, Lmax / kBlock, &nsplit);
         if (!ws || ws_bytes < need) return QSA_ERR_WORKSPACE;
         if (!aligned16(ws)) return QSA_ERR_ALIGN;
-        return launch_status(launch_attn_decode(a, nsplit, s));
+        RopeArgs none{};
+        return launch_status(launch_attn_decode(a, none, nsplit, s));
     }
     return launch_status(launch_dense_prefill(a, s));
 }
@@ -592,12 +626,8 @@ int qsa_sparse_attn_prefill_kl_staged(const qsa_bf16 *Q, const qsa_bf16 *K, cons
     if (st != QSA_OK) return st;
     RopeArgs ra{};
     if (rope_dim != 0) {
-        if (rope_dim < 0 || !(theta > 0.0)) return QSA_ERR_SHAPE;
-        if (rope_dim != 64 && rope_dim != 128) return QSA_ERR_UNSUPPORTED;
-        ra.half = rope_dim / 2;
-        for (int j = 0; j < ra.half; ++j)
-            ra.inv_freq[j] =
-                pow(theta, -2.0 * static_cast<double>(j) / static_cast<double>(rope_dim));
+        st = rope_args(rope_dim, theta, ra);
+        if (st != QSA_OK) return st;
     }
     const size_t need = sparse_prefill_kl_staged_floats(Tq, Kbudget) * sizeof(float);
     if (need > 0 && (!ws || ws_bytes < need)) return QSA_ERR_WORKSPACE;

@@ -71,9 +71,9 @@ __device__ __forceinline__ void rope_angle(int64_t p, double inv_freq, double &c
     sincos(ang, &s, &c);
 }
 
-// Partial RoPE applied to the queries on load (sparse prefill): half = the
-// rotated pairs per head (0: none), inv_freq[j] = theta^(-2j / rope_dim)
-// formed on the host as for the RoPE kernel.
+// Partial RoPE applied to the queries on load (sparse prefill and decode):
+// half = the rotated pairs per head (0: none), inv_freq[j] =
+// theta^(-2j / rope_dim) formed on the host as for the RoPE kernel.
 struct RopeArgs {
     int half;
     double inv_freq[64];
@@ -269,7 +269,9 @@ int decode_col_tiles(int Tq, int group);
 int64_t decode_max_entries(int Tq, int64_t Kbudget_or_blocks);
 size_t decode_partial_floats(int B, int Hkv, int nsplit);
 int decode_num_splits(int B, int Hkv, int64_t max_entries);
-hipError_t launch_attn_decode(const AttnArgs &a, int nsplit, hipStream_t s);
+// ra.half > 0: the queries are rotated as they are loaded (angles at the
+// decode positions seq_len - Tq + query).
+hipError_t launch_attn_decode(const AttnArgs &a, const RopeArgs &ra, int nsplit, hipStream_t s);
 // The no-allocation decode: its split records live in a static device array
 // of kDecodeScratchBytes per GPU.  decode_scratch gives the array's address
 // on the current device (looked up once per device), or an error when need

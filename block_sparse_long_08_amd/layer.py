@@ -16,9 +16,10 @@ import torch
 
 from . import (DI, HI, R, SCORE_MAXHEAD, KBAR_MEAN, qsa_compress_keys, qsa_decode_workspace_bytes,
                qsa_rope_bf16, qsa_select_blocks, qsa_select_workspace_bytes,
-               qsa_sparse_attn_decode, qsa_sparse_attn_prefill, qsa_sparse_attn_prefill_concurrency,
-               qsa_sparse_attn_prefill_kl, qsa_sparse_attn_prefill_kl_staged,
-               qsa_sparse_attn_prefill_kl_staged_workspace_bytes, qsa_sparse_attn_prefill_rope)
+               qsa_sparse_attn_decode, qsa_sparse_attn_decode_rope, qsa_sparse_attn_prefill,
+               qsa_sparse_attn_prefill_concurrency, qsa_sparse_attn_prefill_kl,
+               qsa_sparse_attn_prefill_kl_staged, qsa_sparse_attn_prefill_kl_staged_workspace_bytes,
+               qsa_sparse_attn_prefill_rope)
 
 
 # rows per sparse-attention launch of the prefill when the device does not
@@ -285,8 +286,13 @@ class QSADecode:
     def __init__(self, B: int, Lmax: int, H: int = 24, Hkv: int = 2, D: int = 256,
                  budget: int = 512, score_mode: int = SCORE_MAXHEAD, kbar_mode: int = KBAR_MEAN,
                  theta: float = 1e7, rope_dim: int = 64, next_n: int = 1,
-                 idx_rope_dim: int = 0, kbar_gain=None, pages=None, device="cuda"):
+                 idx_rope_dim: int = 0, kbar_gain=None, pages=None, rope_on_load: bool = True,
+                 device="cuda"):
         self.B, self.Lmax, self.H, self.Hkv, self.D = B, Lmax, H, Hkv, D
+        # rope_on_load (rope_dim 64 or 128): the attention rotates the queries
+        # as it loads them (no RoPE launch, the rotated rows are not stored);
+        # the qr property still gives them, computed on first use
+        self.rope_on_load = bool(rope_on_load) and rope_dim in (64, 128)
         self.pages = pages  # paged caches: Kc, Vc and kbar are page pools
         self.budget, self.score_mode, self.kbar_mode = budget, score_mode, kbar_mode
         self.theta, self.rope_dim, self.next_n = theta, rope_dim, next_n
@@ -294,7 +300,10 @@ class QSADecode:
         self.nb_max = Lmax // R
         dev = torch.device(device)
         n = next_n
-        self.qr = torch.empty((B, n, H, D), dtype=torch.bfloat16, device=dev)
+        self.dev = dev
+        self._qr = None
+        self._q = self._seq_len = None
+        self._qr_current = False
         self.blk_idx = torch.empty((B, budget), dtype=torch.int32, device=dev)
         self.n_sel = torch.empty((B,), dtype=torch.int32, device=dev)
         self.O = torch.empty((B, n, H, D), dtype=torch.float32, device=dev)
@@ -305,6 +314,20 @@ class QSADecode:
         self.dec_ws = torch.empty((max(self.dec_ws_bytes, 16),), dtype=torch.uint8, device=dev)
         self.qir = (torch.empty((B, n, HI, DI), dtype=torch.bfloat16, device=dev)
                     if idx_rope_dim else None)
+
+    @property
+    def qr(self):
+        """The rotated queries [B, next_n, H, D] of the last step."""
+        if self._qr is None:
+            self._qr = torch.empty((self.B, self.next_n, self.H, self.D), dtype=torch.bfloat16,
+                                   device=self.dev)
+        if not self._qr_current:
+            if self._q is None:
+                raise RuntimeError("QSADecode.qr: no step has run")
+            qsa_rope_bf16(self._q, self._qr, self.B * self.next_n, self.H, self.D, self.rope_dim,
+                          self.theta, 0, self._seq_len, self.next_n)
+            self._qr_current = True
+        return self._qr
 
     def pool_keys(self, ki, kbar, block0: int = 0):
         """Pool indexer keys ki [B, T, DI] (T a multiple of r) into kbar[:, block0 ..]."""
@@ -323,8 +346,9 @@ class QSADecode:
         [B, HI, DI] when next_n == 1); returns O [B, next_n, H, D] and lse
         [B, next_n, H] (O [B, H, D] and lse [B, H] when next_n == 1)."""
         n = self.next_n
-        qsa_rope_bf16(q, self.qr, self.B * n, self.H, self.D, self.rope_dim, self.theta, 0,
-                      seq_len, n)
+        self._q, self._seq_len, self._qr_current = q, seq_len, False
+        if not self.rope_on_load:
+            q = self.qr
         if self.idx_rope_dim:  # indexer queries at their own positions
             qsa_rope_bf16(qi, self.qir, self.B * n, HI, DI, self.idx_rope_dim, self.theta, 0,
                           seq_len, n)
@@ -332,9 +356,15 @@ class QSADecode:
         qsa_select_blocks(qi, kbar, self.B, n, 0, seq_len, self.nb_max, HI, DI, R,
                           self.score_mode, self.budget, self.blk_idx, self.n_sel, self.sel_ws,
                           self.sel_ws_bytes, pages=self.pages)
-        qsa_sparse_attn_decode(self.qr, Kc, Vc, seq_len, self.blk_idx, self.n_sel, self.B, n,
-                               self.Lmax, self.H, self.Hkv, self.D, R, self.budget, self.O,
-                               self.lse, self.dec_ws, self.dec_ws_bytes, pages=self.pages)
+        if self.rope_on_load:
+            qsa_sparse_attn_decode_rope(q, Kc, Vc, seq_len, self.blk_idx, self.n_sel, self.B, n,
+                                        self.Lmax, self.H, self.Hkv, self.D, R, self.budget,
+                                        self.rope_dim, self.theta, self.O, self.lse, self.dec_ws,
+                                        self.dec_ws_bytes, pages=self.pages)
+        else:
+            qsa_sparse_attn_decode(q, Kc, Vc, seq_len, self.blk_idx, self.n_sel, self.B, n,
+                                   self.Lmax, self.H, self.Hkv, self.D, R, self.budget, self.O,
+                                   self.lse, self.dec_ws, self.dec_ws_bytes, pages=self.pages)
         if n == 1:
             return self.O[:, 0], self.lse[:, 0]
         return self.O, self.lse

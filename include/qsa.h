@@ -244,6 +244,21 @@ int qsa_sparse_attn_decode(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16
                            int Kbudget, float *O, float *lse, void *ws, size_t ws_bytes,
                            const qsa_pages *pages, void *stream);
 
+/* ---- A1 + A7: the same decode attention with the queries' partial RoPE
+ * (Model Summary table: RoPE dimension 64) applied as they are loaded.
+ * q: [B][Tq][H][D] BEFORE RoPE; the result equals, bit for bit,
+ * qsa_rope_bf16 of q in its decode form (row b * Tq + i at position
+ * seq_len[b] - Tq + i, at least 0) followed by qsa_sparse_attn_decode on the
+ * rotated rows, without writing or reading them.  Arguments otherwise,
+ * workspace and support as qsa_sparse_attn_decode; rope_dim 64 or 128,
+ * theta > 0 (else QSA_ERR_SHAPE / QSA_ERR_UNSUPPORTED before any launch). */
+int qsa_sparse_attn_decode_rope(const qsa_bf16 *q, const qsa_bf16 *Kc, const qsa_bf16 *Vc,
+                                const int64_t *seq_len, const int32_t *blk_idx,
+                                const int32_t *n_sel, int B, int Tq, int64_t Lmax, int H, int Hkv,
+                                int D, int r, int Kbudget, int rope_dim, double theta, float *O,
+                                float *lse, void *ws, size_t ws_bytes, const qsa_pages *pages,
+                                void *stream);
+
 /* ---- A7 without allocation: qsa_sparse_attn_decode for callers that cannot
  * allocate device memory or hand over a workspace (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation).  The

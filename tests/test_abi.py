@@ -252,6 +252,33 @@ def test_decode_validation(lib):
         assert st == SHAPE
 
 
+def decode_rope(lib, q=P, seq=P, Tq=1, H=24, Hkv=2, Kb=512, rope_dim=64, theta=1e7, O=P,
+                ws_bytes=1 << 30, pages=None):
+    f = lib.qsa_sparse_attn_decode_rope
+    f.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 2 + [ctypes.c_int64] + [
+        ctypes.c_int] * 6 + [ctypes.c_double] + [ctypes.c_void_p] * 3 + [ctypes.c_size_t] + [
+        ctypes.c_void_p] * 2
+    return f(vp(q), vp(P), vp(P), vp(seq), vp(P), vp(P), 32, Tq, 1024, H, Hkv, 256, 4, Kb,
+             rope_dim, theta, vp(O), None, vp(P), ws_bytes, pages, None)
+
+
+def test_decode_rope_validation(lib):
+    """The decode form that rotates on load: its own arguments, then the
+    plain decode's checks (each call fails on the host)."""
+    assert decode_rope(lib, rope_dim=0) == SHAPE
+    assert decode_rope(lib, theta=-1.0) == SHAPE
+    assert decode_rope(lib, rope_dim=32) == UNSUP
+    assert decode_rope(lib, rope_dim=256) == UNSUP
+    assert decode_rope(lib, seq=0) == NULL
+    assert decode_rope(lib, rope_dim=128, O=0) == NULL
+    assert decode_rope(lib, Tq=17) == SHAPE
+    assert decode_rope(lib, H=48) == UNSUP
+    assert decode_rope(lib, Kb=4096) == UNSUP
+    assert decode_rope(lib, q=MIS) == ALIGN
+    assert decode_rope(lib, ws_bytes=16) == WORKSPACE
+    assert decode_rope(lib, pages=pages(page_tokens=48)) == UNSUP
+
+
 def test_dense_validation(lib):
     st = lib.dense_attn(vp(P), vp(P), vp(P), 1, I64(16), I64(15), I64(0), None, 24, 2, 256,
                         vp(P), None, None, ctypes.c_size_t(0), None, None)

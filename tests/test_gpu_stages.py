@@ -562,6 +562,88 @@ def test_decode_attention_parity(qsa):
         assert_close(lg[b], lref[0], f"decode seq {b} lse")
 
 
+@pytest.mark.parametrize("lens,n,H,Hkv,rope_dim,theta,K,P", [
+    ((1, 2, 7, 4096, 4999), 1, 24, 2, 64, 1e7, 64, 0),   # the model's heads, short lengths
+    ((3001, 2, 20003), 4, 24, 2, 64, 1e7, 512, 0),       # speculative queries: tiles of 2 positions
+    ((5000, 3), 16, 4, 4, 128, 1e4, 128, 0),             # one head per KV head: 16 positions a tile
+    ((4097, 1030, 70001), 5, 32, 4, 64, 5e5, 256, 64),   # paged caches, 8 heads per KV head
+])
+def test_decode_rope_on_load(qsa, lens, n, H, Hkv, rope_dim, theta, K, P):
+    """The decode attention rotating its queries as it loads them: O and lse
+    equal, bit for bit, the RoPE kernel's decode form followed by the plain
+    decode attention (contiguous or paged), and every query matches the
+    oracle (its RoPE at the query's position, then its attention over the
+    shared selection and the query's own tail)."""
+    torch = _torch()
+    from test_gpu_paged import page_layout, to_pool
+    lens = np.array(lens, dtype=np.int64)
+    B, Lmax = lens.size, int(lens.max())
+    log(f"decode rope on load lens={lens.tolist()} next_n={n} H={H} Hkv={Hkv} "
+        f"rope_dim={rope_dim} K={K} pages={P}")
+    Kc = synth.normal_bf16(2, (B, Lmax, Hkv, 256), seed=80 + n)
+    Vc = synth.normal_bf16(3, (B, Lmax, Hkv, 256), seed=80 + n)
+    q = synth.normal_bf16(1, (B, n, H, 256), seed=80 + n)
+    rng = np.random.default_rng(n)
+    sel = np.full((B, K), -1, dtype=np.int32)
+    nsel = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        p0 = int(lens[b]) - n
+        nc = oracle.num_complete(p0) if p0 >= 0 else 0
+        m = min(K, nc)
+        if m:
+            sel[b, :m] = np.sort(rng.choice(nc, size=m, replace=False))
+        nsel[b] = m
+    pg = None
+    if P:
+        table, total = page_layout(lens, Lmax, P, seed=P)
+        pg = qsa.Pages(dev(table), P)
+        kc = dev(to_pool(Kc, table, total, P, valid=lens))
+        vc = dev(to_pool(Vc, table, total, P, valid=lens))
+    else:
+        kc, vc = dev(Kc), dev(Vc)
+    qd, ln, sd, nd = dev(q), dev(lens), dev(sel), dev(nsel)
+    qr = torch.empty_like(qd)
+    qsa.qsa_rope_bf16(qd, qr, B * n, H, 256, rope_dim, theta, 0, ln, n)
+    wsb = qsa.qsa_decode_workspace_bytes(B, n, H, Hkv, 256, K)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+    outs = []
+    for fused in (False, True):
+        O = torch.full((B, n, H, 256), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((B, n, H), float("nan"), dtype=torch.float32, device="cuda")
+        if fused:
+            qsa.qsa_sparse_attn_decode_rope(qd, kc, vc, ln, sd, nd, B, n, Lmax, H, Hkv, 256, 4, K,
+                                            rope_dim, theta, O, lse, ws, wsb, pages=pg)
+        else:
+            qsa.qsa_sparse_attn_decode(qr, kc, vc, ln, sd, nd, B, n, Lmax, H, Hkv, 256, 4, K, O,
+                                       lse, ws, wsb, pages=pg)
+        torch.cuda.synchronize()
+        outs.append((O.cpu().numpy(), lse.cpu().numpy()))
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32)), "O"
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32)), "lse"
+    Og, lg = outs[1]
+    got, ref, gl, rl = [], [], [], []
+    for b in range(B):
+        L = int(lens[b])
+        p0 = L - n
+        for i in range(n):
+            p = p0 + i
+            if p < 0:
+                assert np.all(Og[b, i] == 0) and np.all(np.isneginf(lg[b, i])), f"seq {b} q {i}"
+                continue
+            if p0 < 0:
+                tok = np.arange(p + 1)   # no complete block before the first query: every token
+            else:
+                tok = oracle.token_set_reuse(sel[b, :nsel[b]], p0, p)
+            qo = oracle.rope(q[b, i:i + 1], rope_dim=rope_dim, theta=theta, pos=np.array([p]))
+            o, l, _ = oracle.attend_row(qo[0], Kc[b], Vc[b], tok)
+            got.append(Og[b, i])
+            gl.append(lg[b, i])
+            ref.append(o)
+            rl.append(l)
+    assert_close(np.stack(got), np.stack(ref), "decode rope-on-load O vs oracle")
+    assert_close(np.stack(gl), np.stack(rl), "decode rope-on-load lse vs oracle")
+
+
 # ------------------------------------------------------------- A8 dense
 @pytest.mark.parametrize("B,Tq,pos0", [(1, 517, 0), (1, 200, 777), (1, 1, 1000), (1, 129, 64),
                                        (2, 100, 50)])
