@@ -195,16 +195,33 @@ __device__ __forceinline__ void stage_k(const EntryList<MULTI, PMODE> &L, int e0
 // (-inf where none is visible).  With lmx, lanes with lmo >= 0 also store
 // lmv (the previous stage's max) at lmx[lmo].
 template <bool DMA_V, bool MULTI, int PMODE>
+__device__ __forceinline__ float stage_finish(const EntryList<MULTI, PMODE> &L, int e0,
+                                              int64_t pq, f32x4 sacc, WaveState &st,
+                                              const unsigned char *vlds, int lane,
+                                              float *lmx = nullptr, int lmo = -1,
+                                              float lmv = 0.f);
+
+template <bool DMA_V, bool MULTI, int PMODE>
 __device__ __forceinline__ float stage_compute(const EntryList<MULTI, PMODE> &L, int e0,
                                                int64_t pq, const bf16x8 (&kf)[8],
                                                const bf16x8 (&qT)[8], WaveState &st,
                                                const unsigned char *vlds, int lane,
                                                float *lmx = nullptr, int lmo = -1,
                                                float lmv = 0.f) {
-    const int n = lane & 15, g4 = lane >> 4;
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 8; ++s) sacc = mfma_bf16_16x16x32(kf[s], qT[s], sacc);
+    return stage_finish<DMA_V>(L, e0, pq, sacc, st, vlds, lane, lmx, lmo, lmv);
+}
+
+// The logits S^T (16 tokens x 16 columns) in sacc: masking, online softmax
+// and the PV product of the stage.
+template <bool DMA_V, bool MULTI, int PMODE>
+__device__ __forceinline__ float stage_finish(const EntryList<MULTI, PMODE> &L, int e0,
+                                              int64_t pq, f32x4 sacc, WaveState &st,
+                                              const unsigned char *vlds, int lane,
+                                              float *lmx, int lmo, float lmv) {
+    const int n = lane & 15, g4 = lane >> 4;
     // lane (column n, group g4) holds entry e0 + g4, tokens 0..3
     const int cnt = L.visible(e0 + g4, pq);
     float sv[4];
@@ -792,6 +809,135 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, RopeArgs r
     }
 }
 
+// ------------------------------------------------------------------------
+// Dense decode of several column tiles (the baseline's speculative queries:
+// next_n query rows of 12 heads each make 3 tiles at next_n = 4): one
+// workgroup per (split, group of up to 4 column tiles, KV head, sequence)
+// whose waves are the tiles of the group.  The waves walk the split's
+// stages together: a stage's 16 key rows and 16 value rows are read from
+// memory once for all tiles (by LDS DMA, the instructions shared among the
+// waves, into one of two buffers, so the next stage arrives while this one
+// is computed), and every wave multiplies them with its own tile's queries.
+// Each wave writes its tile's split record as the one-tile kernel does, so
+// the same merge follows.  LDS: the key tile (row tt, chunk c at slot c ^ tt:
+// the 16 rows of one fragment read fall in distinct banks) and the value
+// tile (slot c ^ row_swizzle(tt), the layout stage_finish reads); before the
+// stage loop the first buffer holds the queries' RoPE angles.  (For the
+// sparse decode, whose splits hold a few stages each, the one-tile kernel
+// with its stages spread over 4 waves was faster: 89.5-90.0 against 91.0 us
+// per 4 x 1M step at next_n = 4.)
+constexpr int kTileMaxWaves = 4;
+
+template <bool PAGED, int W>
+__global__ void __launch_bounds__(64 * W) attn_decode_tiles_kernel(AttnArgs a, RopeArgs ra,
+                                                                   int nsplit, int sps, int nct) {
+    constexpr int PMODE = PAGED ? 2 : 0;
+    constexpr int nthr = 64 * W;  // the waves of the group
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kVStageBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char lds2[2 * kVStageBytes];
+    static_assert(16 * 128 * 8 <= 2 * kVStageBytes, "angles of 16 query positions");
+    const int bx = blockIdx.x, cg = bx / nsplit, split = bx - cg * nsplit;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ct = kTileMaxWaves * cg + wave;
+    const int g = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int nq = static_cast<int>(a.Tq);
+    int64_t Lb = a.seq_len[b];
+    Lb = Lb < 0 ? 0 : (Lb > a.Lmax ? a.Lmax : Lb);
+    const int64_t p_last = Lb - 1;
+    const int64_t p0 = Lb - nq;  // the first query
+    const int64_t nc = num_complete_blocks(p0, kBlock);
+    const int ns = static_cast<int>(nc);
+    const int tail = p_last >= 4 * nc ? static_cast<int>(p_last - 4 * nc + 1) : 0;
+    const int E = ns + (tail + 3) / 4;
+    const int nstages = (E + kStageEntries - 1) / kStageEntries;
+    const int s0 = split * sps, s1 = min(s0 + sps, nstages);
+    const int group = a.H / a.Hkv;
+    uint4 qv[8];
+    const bool qok = load_q_raw(a.Q + b * nq * a.H * kHeadDim, g, group, a.H, ct, nq * group,
+                                lane, qv);
+    const int32_t *ptab = PAGED ? a.ptable + b * a.pstride : nullptr;
+    // angles of the group's query positions q_lo .. q_hi (at most 16)
+    double *ang = reinterpret_cast<double *>(lds);
+    const int q_lo = 16 * kTileMaxWaves * cg / group;
+    if (ra.half > 0) {
+        const int q_hi = min(nq - 1, (16 * (kTileMaxWaves * cg + W) - 1) / group);
+        const int cnt = (q_hi - q_lo + 1) * ra.half;
+        for (int i = static_cast<int>(threadIdx.x); i < cnt; i += nthr) {
+            const int qq = i / ra.half, j = i - qq * ra.half;
+            const int64_t pp = a.seq_len[b] - nq + q_lo + qq;
+            rope_angle(pp < 0 ? 0 : pp, ra.inv_freq[j], ang[qq * 128 + j],
+                       ang[qq * 128 + 64 + j]);
+        }
+    }
+    EntryList<true, PMODE> L{nullptr, 0, ns, tail, nc, ptab, a.pshift};
+    block_sync();
+    const int pair = 16 * ct + (lane & 15);
+    if (ra.half > 0 && qok) rope_q(qv, ang + (pair / group - q_lo) * 128, ra.half / 32, lane);
+    bf16x8 qT[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qT[s] = as_bf16x8(qv[s]);
+    const int64_t pq = pair < nq * group ? p0 + pair / group : -1;
+    const int64_t rs = static_cast<int64_t>(a.Hkv) * kHeadDim;
+    const int64_t seq_off = PAGED ? 0 : b * a.Lmax * rs;
+    const uint16_t *Kg = a.K + seq_off + g * kHeadDim;
+    const uint16_t *Vg = a.V + seq_off + g * kHeadDim;
+    int64_t psafe = p_last < 0 ? 0 : p_last;
+    if (PAGED && E > 0) psafe = page_row(ptab, a.pshift, psafe);
+    WaveState st;
+    state_init(st);
+    // A stage's tiles by LDS DMA: 16 instructions of 1 KB, wave w issuing
+    // w, w + W, ...; instruction d fills bytes 1024 d .. (keys for d < 8,
+    // values after), lane l row tt = 2 (d % 8) + l / 32 at slot l % 32, which
+    // holds chunk (l % 32) ^ tt (keys) or (l % 32) ^ row_swizzle(tt) (values).
+    // Two buffers: the next stage's rows arrive while this one is computed.
+    auto issue = [&](int sidx, unsigned char *buf) {
+        const int e0 = sidx * kStageEntries;
+        for (int d = wave; d < 16; d += W) {
+            const int tt = 2 * (d & 7) + (lane >> 5);
+            const int e = e0 + (tt >> 2), i = tt & 3;
+            const int64_t tok = i < L.count(e) ? L.base(e) + i : psafe;
+            const bool val = d >= 8;
+            const int c = (lane & 31) ^ (val ? row_swizzle(tt) : tt);
+            const uint16_t *src = (val ? Vg : Kg) + tok * rs + 8 * c;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)src,
+                (__attribute__((address_space(3))) void *)(buf + 1024 * d), 16, 0, 0);
+        }
+    };
+    auto compute = [&](int sidx, const unsigned char *buf) {
+        if (ct >= nct) return;
+        // S^T = K Q^T with the key fragments read from the tile step by step
+        const int n = lane & 15, g4 = lane >> 4;
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            sacc = mfma_bf16_16x16x32(
+                *reinterpret_cast<const bf16x8 *>(buf + n * 512 + 16 * ((4 * s + g4) ^ n)), qT[s],
+                sacc);
+        stage_finish<false>(L, sidx * kStageEntries, pq, sacc, st, buf + kVStageBytes, lane);
+    };
+    const int nst = s1 > s0 ? s1 - s0 : 0;
+    block_sync();  // the angles are read
+    if (nst > 0) issue(s0, lds);
+    for (int k = 0; k < nst; k += 2) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows of stage k have landed
+        block_sync();  // every wave's, and every wave is done with the other buffer
+        if (k + 1 < nst) issue(s0 + k + 1, lds2);
+        compute(s0 + k, lds);
+        if (k + 1 >= nst) break;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        block_sync();
+        if (k + 2 < nst) issue(s0 + k + 2, lds);
+        compute(s0 + k + 1, lds2);
+    }
+    if (ct < nct) {
+        st.l = head_total(st.l);
+        const int64_t rec_id = ((b * a.Hkv + g) * nct + ct) * nsplit + split;
+        record_store(st, a.part + rec_id * static_cast<int64_t>(kRecFloats), lane);
+    }
+}
+
 // Merge the split records: 4 neighbouring threads per output element
 // (b, query, head, d), each folding every 4th split with an online rescale,
 // then combined by shuffles; neighbouring elements read neighbouring words.
@@ -946,12 +1092,31 @@ int decode_col_tiles(int Tq, int group) { return (Tq * group + 15) / 16; }
 // the tail (at most 3 + Tq tokens).
 int64_t decode_max_entries(int Tq, int64_t sel_entries) { return sel_entries + (Tq + 6) / 4; }
 
-int decode_num_splits(int B, int Hkv, int64_t max_entries) {
+bool decode_uses_tiles(int nct, bool dense) { return dense && nct >= 2; }
+
+int decode_num_splits(int B, int Hkv, int nct, int64_t max_entries, bool dense) {
     const int64_t nstages = (max_entries + kStageEntries - 1) / kStageEntries;
+    if (decode_uses_tiles(nct, dense)) {
+        // the tiles kernel: workgroups of min(nct, 4) waves, every wave
+        // through all stages of its split; as many workgroups as fit at
+        // once (2 waves per SIMD: 8 waves per CU, 256 CUs), no empty split
+        const int w = nct < kTileMaxWaves ? nct : kTileMaxWaves;
+        const int64_t ncg = (nct + kTileMaxWaves - 1) / kTileMaxWaves;
+        int64_t want = (256 * (8 / w)) / (static_cast<int64_t>(B) * Hkv * ncg);
+        if (want < 1) want = 1;
+        if (nstages <= 0) return 1;
+        const int64_t per = (nstages + want - 1) / want;
+        return static_cast<int>((nstages + per - 1) / per);
+    }
+    Hkv *= nct;
     // at most 512 workgroups (the two per CU that fit at once: one more and a
     // second round of workgroups doubles the time), at least one stage per
-    // wave
+    // wave.  The grid rounds the splits up to a multiple of 8 (the XCD
+    // mapping), so from 8 on the count is a multiple of 8 itself: 21 splits
+    // of 24 column tiles would launch 576 workgroups, 16 launch 384 (next_n
+    // = 4 at 4 x 1M: 38.9 against 28.5 us for attention and merge).
     int64_t want = 512 / (static_cast<int64_t>(B) * Hkv);
+    if (want >= 8) want -= want % 8;
     const int64_t cap = (nstages + 3) / 4;  // at least one stage per wave
     if (want > cap) want = cap;
     if (want < 1) want = 1;
@@ -1020,6 +1185,18 @@ hipError_t decode_scratch(size_t need, float **ptr) {
     return hipSuccess;
 }
 
+template <int W>
+static void launch_tiles(const AttnArgs &a, const RopeArgs &ra, dim3 grid, int nsplit, int sps,
+                         int nct, bool paged, hipStream_t s) {
+    const dim3 block(kWave * W);
+    if (paged)
+        hipLaunchKernelGGL((attn_decode_tiles_kernel<true, W>), grid, block, 0, s, a, ra, nsplit,
+                           sps, nct);
+    else
+        hipLaunchKernelGGL((attn_decode_tiles_kernel<false, W>), grid, block, 0, s, a, ra, nsplit,
+                           sps, nct);
+}
+
 hipError_t launch_attn_decode(const AttnArgs &a, const RopeArgs &ra, int nsplit, hipStream_t s) {
     if (a.B == 0) return hipSuccess;
     const int nq = static_cast<int>(a.Tq);
@@ -1028,10 +1205,23 @@ hipError_t launch_attn_decode(const AttnArgs &a, const RopeArgs &ra, int nsplit,
         decode_max_entries(nq, a.blk_idx ? static_cast<int64_t>(a.Kbudget) : a.Lmax / kBlock);
     const int64_t nstages = (max_entries + kStageEntries - 1) / kStageEntries;
     const int sps = static_cast<int>((nstages + nsplit - 1) / nsplit);
-    const dim3 grid(static_cast<uint32_t>((nsplit + 7) / 8 * 8 * nct),
-                    static_cast<uint32_t>(a.Hkv), static_cast<uint32_t>(a.B));
-    launch_decode_variant(a, ra, grid, nsplit, sps, nct, a.blk_idx == nullptr, nq > 1,
-                          a.ptable != nullptr, s);
+    const bool dense = a.blk_idx == nullptr, paged = a.ptable != nullptr;
+    if (decode_uses_tiles(nct, dense)) {
+        const int w = nct < kTileMaxWaves ? nct : kTileMaxWaves;
+        const int ncg = (nct + kTileMaxWaves - 1) / kTileMaxWaves;
+        const dim3 grid(static_cast<uint32_t>(nsplit * ncg), static_cast<uint32_t>(a.Hkv),
+                        static_cast<uint32_t>(a.B));
+        if (w == 2)
+            launch_tiles<2>(a, ra, grid, nsplit, sps, nct, paged, s);
+        else if (w == 3)
+            launch_tiles<3>(a, ra, grid, nsplit, sps, nct, paged, s);
+        else
+            launch_tiles<4>(a, ra, grid, nsplit, sps, nct, paged, s);
+    } else {
+        const dim3 grid(static_cast<uint32_t>((nsplit + 7) / 8 * 8 * nct),
+                        static_cast<uint32_t>(a.Hkv), static_cast<uint32_t>(a.B));
+        launch_decode_variant(a, ra, grid, nsplit, sps, nct, dense, nq > 1, paged, s);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t threads = 4 * static_cast<int64_t>(a.B) * nq * a.H * kHeadDim;

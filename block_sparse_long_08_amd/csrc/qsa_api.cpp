@@ -376,10 +376,12 @@ int qsa_sparse_attn_prefill_rope(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa
 }
 
 // Split count and workspace bytes of the decode attention: one record per
-// (sequence, KV head, column tile of 16 query-head pairs, split).
-static size_t decode_ws(int B, int Tq, int H, int Hkv, int64_t sel_entries, int *nsplit) {
+// (sequence, KV head, column tile of 16 query-head pairs, split).  dense:
+// the dense baseline's decode form (sel_entries = every block).
+static size_t decode_ws(int B, int Tq, int H, int Hkv, int64_t sel_entries, int *nsplit,
+                        bool dense = false) {
     const int nct = decode_col_tiles(Tq, H / Hkv);
-    const int ns = decode_num_splits(B, Hkv * nct, decode_max_entries(Tq, sel_entries));
+    const int ns = decode_num_splits(B, Hkv, nct, decode_max_entries(Tq, sel_entries), dense);
     if (nsplit) *nsplit = ns;
     return decode_partial_floats(B, Hkv * nct, ns) * sizeof(float);
 }
@@ -479,7 +481,7 @@ size_t dense_attn_workspace_bytes(int B, int64_t Tq, int64_t Lmax, int H, int Hk
     if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv || Lmax <= 0) return 0;
     // what the decode form needs (Tq <= 16); the prefill form needs none
     if (Tq < 1 || Tq > kMaxNextN) return 0;
-    return decode_ws(B, static_cast<int>(Tq), H, Hkv, Lmax / kBlock, nullptr);
+    return decode_ws(B, static_cast<int>(Tq), H, Hkv, Lmax / kBlock, nullptr, true);
 }
 
 int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, int64_t Tq,
@@ -505,7 +507,8 @@ int dense_attn(const qsa_bf16 *Q, const qsa_bf16 *K, const qsa_bf16 *V, int B, i
     hipStream_t s = as_stream(stream);
     if (seq_len) {
         int nsplit = 0;
-        const size_t need = decode_ws(B, static_cast<int>(Tq), H, Hkv, Lmax / kBlock, &nsplit);
+        const size_t need =
+            decode_ws(B, static_cast<int>(Tq), H, Hkv, Lmax / kBlock, &nsplit, true);
         if (!ws || ws_bytes < need) return QSA_ERR_WORKSPACE;
         if (!aligned16(ws)) return QSA_ERR_ALIGN;
         RopeArgs none{};

@@ -268,7 +268,10 @@ int sparse_prefill_concurrency(int Hkv, int Kbudget, bool kl, bool paged);
 int decode_col_tiles(int Tq, int group);
 int64_t decode_max_entries(int Tq, int64_t Kbudget_or_blocks);
 size_t decode_partial_floats(int B, int Hkv, int nsplit);
-int decode_num_splits(int B, int Hkv, int64_t max_entries);
+// dense: the dense baseline (every block), which with several column tiles
+// runs the tiles kernel (each stage read once for all tiles)
+bool decode_uses_tiles(int nct, bool dense);
+int decode_num_splits(int B, int Hkv, int nct, int64_t max_entries, bool dense);
 // ra.half > 0: the queries are rotated as they are loaded (angles at the
 // decode positions seq_len - Tq + query).
 hipError_t launch_attn_decode(const AttnArgs &a, const RopeArgs &ra, int nsplit, hipStream_t s);

@@ -567,6 +567,7 @@ def test_decode_attention_parity(qsa):
     ((3001, 2, 20003), 4, 24, 2, 64, 1e7, 512, 0),       # speculative queries: tiles of 2 positions
     ((5000, 3), 16, 4, 4, 128, 1e4, 128, 0),             # one head per KV head: 16 positions a tile
     ((4097, 1030, 70001), 5, 32, 4, 64, 5e5, 256, 64),   # paged caches, 8 heads per KV head
+    ((3000, 65), 16, 32, 2, 64, 1e7, 256, 0),            # 16 column tiles in 4 workgroup groups
 ])
 def test_decode_rope_on_load(qsa, lens, n, H, Hkv, rope_dim, theta, K, P):
     """The decode attention rotating its queries as it loads them: O and lse
