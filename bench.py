@@ -261,10 +261,24 @@ def bench_prefill(name, steps, warmup, with_dense=True, idx_rope_dim=0, x=None, 
     stage["select_standalone"] = _time_steps(lambda: layer.select(qs0, kb0), reps)
     stage["attend_standalone"] = _time_steps(lambda: layer.attend_chunks(Kr0, V), reps)
     probe_ms = gather_ceiling(layer, Kr0, V, reps) if with_probe else None
+    torch.cuda.synchronize()
+    # the outputs of the step's rows for the CPU leg's parity check: the first
+    # and last row of every attention launch, rows 0-3 (every (p+1) mod 4
+    # trailing-block length) and 64 seeded random rows
+    edges = {0, 1, 2, 3, Tq - 1}
+    for r0, n in layer.attn_chunks():
+        edges |= {r0, r0 + n - 1}
+    rs = np.random.default_rng(5).choice(Tq, size=min(64, Tq), replace=False)
+    prow = np.array(sorted(edges | set(int(r) for r in rs)), dtype=np.int64)
+    pidx = torch.from_numpy(prow).to("cuda")
+    res_parity = dict(rows=prow, O=layer.O[pidx].cpu().numpy(), lse=layer.lse[pidx].cpu().numpy(),
+                      sel=layer.blk_idx[pidx].cpu().numpy(),
+                      nsel=layer.n_sel[pidx].cpu().numpy())
     res = dict(ms_per_step=wall * 1e3, stages_ms=stage, Tq=Tq, Tk=Tk, budget=budget,
                attn_launches=nlaunch, pipeline_rows=layer.pipeline_rows,
                attn_rows=layer.attn_rows, q_rope_on_load=layer.rope_on_load)
     res["attend_launch_ms"] = (att_ms if pipe else stage["attend"]) / nlaunch
+    res["_parity"] = res_parity
     if probe_ms is not None:
         res["gather_probe_ms"] = probe_ms
     # algorithmic work of the step
@@ -516,8 +530,55 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(name, x, budget, seconds=15.0, kl_sample=None):
-    """The oracle (fp64, OpenMP over rows) on sampled query rows of the workload."""
+# The output bar of the parity tests (bf16 inputs, fp32 accumulation).
+PARITY_MAX_ABS = 2e-2
+PARITY_REL_L2 = 1e-3
+
+
+def _errors(got, ref):
+    d = np.asarray(got, dtype=np.float64) - np.asarray(ref, dtype=np.float64)
+    den = float(np.linalg.norm(ref))
+    return float(np.abs(d).max()) if d.size else 0.0, float(np.linalg.norm(d) / den) if den else 0.0
+
+
+def parity_record(oracle, name, x, Kr, kb, budget, gpu):
+    """The timed step's outputs on the sampled rows (gpu: rows, O, lse, sel,
+    nsel) against the oracle: the attention over the GPU's own selection
+    (every row), the selection itself (rows whose set equals the oracle's),
+    and end to end on those rows.  Errors are max-abs and rel-L2 over the
+    checked rows, beside the tests' bar."""
+    _, pos0, _, _ = WORKLOADS[name]
+    rows = gpu["rows"]
+    pos = pos0 + rows
+    Qr = oracle.rope(x.Q[rows], pos=pos)
+    t = time.time()
+    ref = oracle.qsa_rows_at(Qr, Kr, x.V, x.qi[rows], kb, pos, Kbudget=budget)
+    Oa, la = oracle.sparse_attn_rows_at(Qr, Kr, x.V, pos, gpu["sel"], gpu["nsel"])
+    secs = time.time() - t
+    same = np.array([gpu["nsel"][i] == ref["nsel"][i] and
+                     np.array_equal(gpu["sel"][i, :gpu["nsel"][i]], ref["sel"][i, :ref["nsel"][i]])
+                     for i in range(rows.size)])
+    att_o, att_l = _errors(gpu["O"], Oa), _errors(gpu["lse"], la)
+    rec = dict(rows=int(rows.size),
+               sample="first and last row of every attention launch, rows 0-3, 64 seeded "
+                      "random rows",
+               bar=dict(max_abs=PARITY_MAX_ABS, rel_l2=PARITY_REL_L2),
+               attention_on_gpu_selection=dict(O_max_abs=att_o[0], O_rel_l2=att_o[1],
+                                               lse_max_abs=att_l[0], lse_rel_l2=att_l[1]),
+               selection_equal_rows=int(same.sum()),
+               selection_differing_rows=int((~same).sum()), oracle_seconds=secs)
+    if same.any():
+        e_o, e_l = _errors(gpu["O"][same], ref["O"][same]), _errors(gpu["lse"][same], ref["lse"][same])
+        rec["end_to_end_equal_selection"] = dict(O_max_abs=e_o[0], O_rel_l2=e_o[1],
+                                                 lse_max_abs=e_l[0], lse_rel_l2=e_l[1])
+    rec["within_bar"] = bool(att_o[0] <= PARITY_MAX_ABS and att_o[1] <= PARITY_REL_L2)
+    return rec
+
+
+def cpu_baseline(name, x, budget, seconds=15.0, kl_sample=None, parity=None):
+    """The oracle (fp64, OpenMP over rows) on sampled query rows of the
+    workload; with parity (the GPU's outputs on a row sample), also the
+    parity of those rows against the oracle."""
     import oracle
     Tq, pos0, _, _ = WORKLOADS[name]
     t = time.time()
@@ -576,6 +637,8 @@ def cpu_baseline(name, x, budget, seconds=15.0, kl_sample=None):
         out["distill"] = dict(rows=8, seconds=tdd, rows_per_s=8 / tdd,
                               sample=f"rows {k0}..{k0 + 7} of {name} (stage-1 KL, dense teacher)",
                               extrapolated_s=tdd * all_vis / v8)
+    if parity is not None:
+        out["parity"] = parity_record(oracle, name, x, Kr, kb, budget, parity)
     return out
 
 
@@ -790,7 +853,13 @@ def main():
         if x is None:
             x = gen_prefill(args.workload)
         out["cpu_baseline"] = cpu_baseline(args.workload, x, pre["budget"], args.cpu_seconds,
-                                           kl_sample=pre.get("_kl_sample"))
+                                           kl_sample=pre.get("_kl_sample"),
+                                           parity=pre.get("_parity"))
+        par = out["cpu_baseline"].get("parity")
+        if par:
+            a = par["attention_on_gpu_selection"]
+            log(f"parity on {par['rows']} rows: O max-abs {a['O_max_abs']:.2e} rel-L2 "
+                f"{a['O_rel_l2']:.2e}; selection equal on {par['selection_equal_rows']}")
     print(json.dumps(out), flush=True)
 
 
