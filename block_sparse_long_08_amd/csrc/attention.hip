@@ -56,8 +56,10 @@ __device__ __forceinline__ void lds_fence() {
 // column masks it at its own position); otherwise the tail is one entry of
 // (p+1) mod 4 tokens, all visible.
 // PMODE: 0 contiguous cache; 1 paged, lst holds the page-pool block of every
-// entry (selected blocks and tail); 2 paged without a list (dense), rows
-// looked up in the page table ptab (shift psh).
+// entry (selected blocks and tail); 2 paged without a list (dense): a
+// stage's 16 tokens lie in one page (pages hold a power of two of at least
+// 16 tokens), whose pool page pg (read from the page table ptab, shift psh)
+// the caller sets before the stage.
 template <bool MULTI, int PMODE = 0>
 struct EntryList {
     const int32_t *lst;  // LDS copy of the selected blocks (sparse), or nullptr (dense)
@@ -67,6 +69,7 @@ struct EntryList {
     int64_t nc;          // complete blocks visible to the selecting query
     const int32_t *ptab = nullptr;
     int psh = 0;
+    int64_t pg = 0;  // PMODE 2: the pool page of the current stage
     __device__ __forceinline__ int count(int e) const {
         if (!MULTI) return e < ns ? 4 : (e == ns ? tail : 0);
         return e < ns ? 4 : max(0, min(4, tail - 4 * (e - ns)));
@@ -78,7 +81,7 @@ struct EntryList {
             t = 4 * static_cast<int64_t>(lst ? lst[e - lst_off] : e);
         else
             t = MULTI ? 4 * (nc + e - ns) : 4 * nc;
-        return PMODE == 2 ? page_row(ptab, psh, t) : t;
+        return PMODE == 2 ? (pg << psh) | (t & ((int64_t(1) << psh) - 1)) : t;
     }
     // token i of entry e, or the safe row p past the entry's count, with no
     // control flow: the list is read at a clamped index (contiguous
@@ -795,8 +798,21 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a, RopeArgs r
     if (PAGED && E > 0) psafe = page_row(ptab, a.pshift, psafe);
     WaveState st;
     state_init(st);
-    for (int sidx = s0 + wave; sidx < s1; sidx += 4)
-        attn_stage(L, sidx * kStageEntries, psafe, pq, Kg, Vg, rs, qT, st, vlds, lane);
+    if constexpr (PMODE == 2) {
+        // the pool page of the wave's next stage is read a stage ahead
+        auto page_of = [&](int sidx) {
+            return static_cast<int64_t>(ptab[(16 * static_cast<int64_t>(sidx)) >> a.pshift]);
+        };
+        int64_t pg_next = s0 + wave < s1 ? page_of(s0 + wave) : 0;
+        for (int sidx = s0 + wave; sidx < s1; sidx += 4) {
+            L.pg = pg_next;
+            if (sidx + 4 < s1) pg_next = page_of(sidx + 4);
+            attn_stage(L, sidx * kStageEntries, psafe, pq, Kg, Vg, rs, qT, st, vlds, lane);
+        }
+    } else {
+        for (int sidx = s0 + wave; sidx < s1; sidx += 4)
+            attn_stage(L, sidx * kStageEntries, psafe, pq, Kg, Vg, rs, qT, st, vlds, lane);
+    }
     block_sync();
     float *mbuf = reinterpret_cast<float *>(lds);
     if (wave != 0) state_store(st, mbuf + (wave - 1) * kRecFloats, lane);
@@ -891,12 +907,19 @@ __global__ void __launch_bounds__(64 * W) attn_decode_tiles_kernel(AttnArgs a, R
     // values after), lane l row tt = 2 (d % 8) + l / 32 at slot l % 32, which
     // holds chunk (l % 32) ^ tt (keys) or (l % 32) ^ row_swizzle(tt) (values).
     // Two buffers: the next stage's rows arrive while this one is computed.
-    auto issue = [&](int sidx, unsigned char *buf) {
-        const int e0 = sidx * kStageEntries;
+    // Token 16 sidx + tt is visible up to p_last; paged, a stage's 16 tokens
+    // lie in one page (pages hold a power of two of at least 16 tokens), and
+    // its pool page is read a stage ahead.
+    const int64_t pmask = PAGED ? (int64_t(1) << a.pshift) - 1 : 0;
+    auto page_of = [&](int sidx) -> int64_t {
+        return PAGED ? static_cast<int64_t>(ptab[(16 * static_cast<int64_t>(sidx)) >> a.pshift])
+                     : 0;
+    };
+    auto issue = [&](int sidx, int64_t pg, unsigned char *buf) {
         for (int d = wave; d < 16; d += W) {
             const int tt = 2 * (d & 7) + (lane >> 5);
-            const int e = e0 + (tt >> 2), i = tt & 3;
-            const int64_t tok = i < L.count(e) ? L.base(e) + i : psafe;
+            const int64_t t = 16 * static_cast<int64_t>(sidx) + tt;
+            const int64_t tok = t > p_last ? psafe : (PAGED ? (pg << a.pshift) | (t & pmask) : t);
             const bool val = d >= 8;
             const int c = (lane & 31) ^ (val ? row_swizzle(tt) : tt);
             const uint16_t *src = (val ? Vg : Kg) + tok * rs + 8 * c;
@@ -919,16 +942,26 @@ __global__ void __launch_bounds__(64 * W) attn_decode_tiles_kernel(AttnArgs a, R
     };
     const int nst = s1 > s0 ? s1 - s0 : 0;
     block_sync();  // the angles are read
-    if (nst > 0) issue(s0, lds);
+    int64_t pg = nst > 0 ? page_of(s0) : 0;
+    int64_t pg_next = nst > 1 ? page_of(s0 + 1) : 0;
+    if (nst > 0) issue(s0, pg, lds);
     for (int k = 0; k < nst; k += 2) {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows of stage k have landed
         block_sync();  // every wave's, and every wave is done with the other buffer
-        if (k + 1 < nst) issue(s0 + k + 1, lds2);
+        if (k + 1 < nst) {
+            pg = pg_next;
+            issue(s0 + k + 1, pg, lds2);
+            if (k + 2 < nst) pg_next = page_of(s0 + k + 2);
+        }
         compute(s0 + k, lds);
         if (k + 1 >= nst) break;
         __builtin_amdgcn_s_waitcnt(0x0F70);
         block_sync();
-        if (k + 2 < nst) issue(s0 + k + 2, lds);
+        if (k + 2 < nst) {
+            pg = pg_next;
+            issue(s0 + k + 2, pg, lds);
+            if (k + 3 < nst) pg_next = page_of(s0 + k + 3);
+        }
         compute(s0 + k + 1, lds2);
     }
     if (ct < nct) {
