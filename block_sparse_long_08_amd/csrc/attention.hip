@@ -971,47 +971,68 @@ __global__ void __launch_bounds__(64 * W) attn_decode_tiles_kernel(AttnArgs a, R
     }
 }
 
-// Merge the split records: 4 neighbouring threads per output element
-// (b, query, head, d), each folding every 4th split with an online rescale,
-// then combined by shuffles; neighbouring elements read neighbouring words.
-__device__ __forceinline__ void merge_step(float &M, float &acc, float &l, float m2, float acc2,
-                                           float l2) {
+// Merge the split records: one thread per 4 consecutive dimensions of an
+// output row (b, query, head), folding the splits in their order with an
+// online rescale; the loads of 4 splits are issued before their folds.
+// Neighbouring threads read neighbouring 16-byte words of a record.
+__device__ __forceinline__ void merge_step(float &M, float4 &acc, float &l, float m2,
+                                           const float4 &acc2, float l2) {
     const float mn = fmaxf(M, m2);
     const float mu = mn == -INFINITY ? 0.f : mn;
     const float a1 = exp2f(M - mu), a2 = exp2f(m2 - mu);
-    acc = acc * a1 + acc2 * a2;
+    acc.x = acc.x * a1 + acc2.x * a2;
+    acc.y = acc.y * a1 + acc2.y * a2;
+    acc.z = acc.z * a1 + acc2.z * a2;
+    acc.w = acc.w * a1 + acc2.w * a2;
     l = l * a1 + l2 * a2;
     M = mn;
 }
 
+constexpr int kMergeLanes = kHeadDim / 4;  // threads per output row
+
 __global__ void __launch_bounds__(256) attn_decode_merge(AttnArgs a, int nsplit, int nct) {
     const int group = a.H / a.Hkv;
-    const int sub = threadIdx.x & 3;
-    const int64_t total = static_cast<int64_t>(a.B) * a.Tq * a.H * kHeadDim;
-    int64_t idx = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 2;
-    const bool valid = idx < total;
-    idx = valid ? idx : total - 1;
-    const int d = static_cast<int>(idx % kHeadDim);
-    const int hq = static_cast<int>((idx / kHeadDim) % a.H);
-    const int64_t bq = idx / (static_cast<int64_t>(kHeadDim) * a.H);  // b * Tq + qi
+    const int64_t total = static_cast<int64_t>(a.B) * a.Tq * a.H * kMergeLanes;
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int d4 = static_cast<int>(idx % kMergeLanes);
+    const int64_t row = idx / kMergeLanes;  // (b * Tq + qi) * H + hq
+    const int hq = static_cast<int>(row % a.H);
+    const int64_t bq = row / a.H;
     const int64_t b = bq / a.Tq;
     const int qi = static_cast<int>(bq - b * a.Tq);
     const int g = hq / group, pair = qi * group + (hq - g * group);
     const int ct = pair >> 4, n = pair & 15;
     const float *rec =
         a.part + ((b * a.Hkv + g) * nct + ct) * nsplit * static_cast<int64_t>(kRecFloats);
-    float M = -INFINITY, acc = 0.f, l = 0.f;
-#pragma unroll 4
-    for (int s = sub; s < nsplit; s += 4) {
-        const float *r = rec + s * static_cast<int64_t>(kRecFloats);
-        merge_step(M, acc, l, r[4096 + n], r[n * kHeadDim + d], r[4096 + 64 + n]);
-    }
+    float M = -INFINITY, l = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int s = 0;
+    for (; s + 4 <= nsplit; s += 4) {
+        float m2[4], l2[4];
+        float4 a2[4];
 #pragma unroll
-    for (int off = 1; off < 4; off <<= 1)
-        merge_step(M, acc, l, __shfl_xor(M, off), __shfl_xor(acc, off), __shfl_xor(l, off));
-    if (sub != 0 || !valid) return;
-    a.O[(bq * a.H + hq) * kHeadDim + d] = l > 0.f ? acc / l : 0.f;
-    if (a.lse && d == 0) a.lse[bq * a.H + hq] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
+        for (int k = 0; k < 4; ++k) {
+            const float *r = rec + (s + k) * static_cast<int64_t>(kRecFloats);
+            m2[k] = r[4096 + n];
+            l2[k] = r[4096 + 64 + n];
+            a2[k] = *reinterpret_cast<const float4 *>(r + n * kHeadDim + 4 * d4);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) merge_step(M, acc, l, m2[k], a2[k], l2[k]);
+    }
+    for (; s < nsplit; ++s) {
+        const float *r = rec + s * static_cast<int64_t>(kRecFloats);
+        const float4 a2 = *reinterpret_cast<const float4 *>(r + n * kHeadDim + 4 * d4);
+        merge_step(M, acc, l, r[4096 + n], a2, r[4096 + 64 + n]);
+    }
+    float4 o;
+    o.x = l > 0.f ? acc.x / l : 0.f;
+    o.y = l > 0.f ? acc.y / l : 0.f;
+    o.z = l > 0.f ? acc.z / l : 0.f;
+    o.w = l > 0.f ? acc.w / l : 0.f;
+    *reinterpret_cast<float4 *>(a.O + row * kHeadDim + 4 * d4) = o;
+    if (a.lse && d4 == 0) a.lse[row] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
 }
 
 hipError_t launch_sparse_prefill(const AttnArgs &a, const RopeArgs &ra, hipStream_t s) {
@@ -1257,7 +1278,7 @@ hipError_t launch_attn_decode(const AttnArgs &a, const RopeArgs &ra, int nsplit,
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t threads = 4 * static_cast<int64_t>(a.B) * nq * a.H * kHeadDim;
+    const int64_t threads = static_cast<int64_t>(a.B) * nq * a.H * kMergeLanes;
     hipLaunchKernelGGL(attn_decode_merge, dim3(static_cast<uint32_t>((threads + 255) / 256)),
                        dim3(256), 0, s, a, nsplit, nct);
     return hipGetLastError();
