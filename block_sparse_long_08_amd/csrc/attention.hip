@@ -971,10 +971,13 @@ __global__ void __launch_bounds__(64 * W) attn_decode_tiles_kernel(AttnArgs a, R
     }
 }
 
-// Merge the split records: one thread per 4 consecutive dimensions of an
-// output row (b, query, head), folding the splits in their order with an
-// online rescale; the loads of 4 splits are issued before their folds.
-// Neighbouring threads read neighbouring 16-byte words of a record.
+// Merge the split records: SUB neighbouring threads per 4 consecutive
+// dimensions of an output row (b, query, head), thread k folding splits k,
+// k + SUB, ... in order with an online rescale (the loads of 4 splits issued
+// before their folds), then the SUB partial states combined by shuffles in a
+// fixed order.  SUB = 4 when the splits are many (few output rows, e.g.
+// 4 sequences over 33 splits), else 1.  Neighbouring threads read
+// neighbouring 16-byte words of a record.
 __device__ __forceinline__ void merge_step(float &M, float4 &acc, float &l, float m2,
                                            const float4 &acc2, float l2) {
     const float mn = fmaxf(M, m2);
@@ -988,13 +991,18 @@ __device__ __forceinline__ void merge_step(float &M, float4 &acc, float &l, floa
     M = mn;
 }
 
-constexpr int kMergeLanes = kHeadDim / 4;  // threads per output row
+constexpr int kMergeLanes = kHeadDim / 4;  // 4-dimension groups per output row
+constexpr int kMergeSubMin = 16;           // splits from which SUB = 4
 
+template <int SUB>
 __global__ void __launch_bounds__(256) attn_decode_merge(AttnArgs a, int nsplit, int nct) {
     const int group = a.H / a.Hkv;
     const int64_t total = static_cast<int64_t>(a.B) * a.Tq * a.H * kMergeLanes;
-    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (idx >= total) return;
+    const int64_t tid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int sub = static_cast<int>(tid % SUB);
+    int64_t idx = tid / SUB;
+    const bool valid = idx < total;  // the SUB threads of an element agree
+    idx = valid ? idx : total - 1;
     const int d4 = static_cast<int>(idx % kMergeLanes);
     const int64_t row = idx / kMergeLanes;  // (b * Tq + qi) * H + hq
     const int hq = static_cast<int>(row % a.H);
@@ -1007,13 +1015,13 @@ __global__ void __launch_bounds__(256) attn_decode_merge(AttnArgs a, int nsplit,
         a.part + ((b * a.Hkv + g) * nct + ct) * nsplit * static_cast<int64_t>(kRecFloats);
     float M = -INFINITY, l = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int s = 0;
-    for (; s + 4 <= nsplit; s += 4) {
+    int s = sub;
+    for (; s + 3 * SUB < nsplit; s += 4 * SUB) {
         float m2[4], l2[4];
         float4 a2[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const float *r = rec + (s + k) * static_cast<int64_t>(kRecFloats);
+            const float *r = rec + (s + k * SUB) * static_cast<int64_t>(kRecFloats);
             m2[k] = r[4096 + n];
             l2[k] = r[4096 + 64 + n];
             a2[k] = *reinterpret_cast<const float4 *>(r + n * kHeadDim + 4 * d4);
@@ -1021,11 +1029,21 @@ __global__ void __launch_bounds__(256) attn_decode_merge(AttnArgs a, int nsplit,
 #pragma unroll
         for (int k = 0; k < 4; ++k) merge_step(M, acc, l, m2[k], a2[k], l2[k]);
     }
-    for (; s < nsplit; ++s) {
+    for (; s < nsplit; s += SUB) {
         const float *r = rec + s * static_cast<int64_t>(kRecFloats);
         const float4 a2 = *reinterpret_cast<const float4 *>(r + n * kHeadDim + 4 * d4);
         merge_step(M, acc, l, r[4096 + n], a2, r[4096 + 64 + n]);
     }
+#pragma unroll
+    for (int off = 1; off < SUB; off <<= 1) {
+        float4 o2;
+        o2.x = __shfl_xor(acc.x, off);
+        o2.y = __shfl_xor(acc.y, off);
+        o2.z = __shfl_xor(acc.z, off);
+        o2.w = __shfl_xor(acc.w, off);
+        merge_step(M, acc, l, __shfl_xor(M, off), o2, __shfl_xor(l, off));
+    }
+    if (sub != 0 || !valid) return;
     float4 o;
     o.x = l > 0.f ? acc.x / l : 0.f;
     o.y = l > 0.f ? acc.y / l : 0.f;
@@ -1278,9 +1296,14 @@ hipError_t launch_attn_decode(const AttnArgs &a, const RopeArgs &ra, int nsplit,
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t threads = static_cast<int64_t>(a.B) * nq * a.H * kMergeLanes;
-    hipLaunchKernelGGL(attn_decode_merge, dim3(static_cast<uint32_t>((threads + 255) / 256)),
-                       dim3(256), 0, s, a, nsplit, nct);
+    const int64_t rows4 = static_cast<int64_t>(a.B) * nq * a.H * kMergeLanes;
+    if (nsplit >= kMergeSubMin)
+        hipLaunchKernelGGL(attn_decode_merge<4>,
+                           dim3(static_cast<uint32_t>((4 * rows4 + 255) / 256)), dim3(256), 0, s,
+                           a, nsplit, nct);
+    else
+        hipLaunchKernelGGL(attn_decode_merge<1>, dim3(static_cast<uint32_t>((rows4 + 255) / 256)),
+                           dim3(256), 0, s, a, nsplit, nct);
     return hipGetLastError();
 }
 
