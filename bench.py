@@ -707,6 +707,9 @@ def main():
     else:
         achieved = algo_gbps
         basis = "algorithmic bytes, no cache reuse (no counter summary for these kernel sources)"
+        log("roofline: the counter summary in profiles/ does not match these attention sources "
+            "(take the counter passes again); frac falls back to the no-reuse gather rate, "
+            "which is not a bound")
     roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=achieved / HBM_PEAK_GBS, traffic=traffic, basis=basis,
                 kernel="attn_prefill_kernel", launch_ms=launch_s * 1e3, launches_per_step=nl,
