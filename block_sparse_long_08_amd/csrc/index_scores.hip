@@ -6,6 +6,8 @@
 // are 4 queries x 4 heads, so the 16x16 accumulator layout (lane l holds rows
 // 4*(l/16) .. +3 of column l%16) puts one query's four heads in one lane and
 // the head combination (max or sum of ReLU) is register-local.
+#include <type_traits>
+
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -102,6 +104,12 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
         ncq[rt] = tout < Tq ? static_cast<int>(min(num_complete_blocks(pos0 + tout, kBlock), nb_max))
                             : -1;
     }
+    // the wave's rows are consecutive queries, so the first one's complete
+    // blocks bound every row's from below (-1: some row past Tq): a tile
+    // below that bound needs no causal mask
+    const int64_t tw0 = t0 + kQW * wave;
+    const int64_t nc_wave =
+        tw0 + kQW - 1 < Tq ? min(num_complete_blocks(pos0 + tw0, kBlock), nb_max) : -1;
     // write-back mapping: lane -> staged query row 4*i + lane/16, 16-byte chunk lane%16
     const int wr_q = lane >> 4, wr_c = lane & 15;
 
@@ -124,30 +132,43 @@ index_scores_prefill(const uint16_t *__restrict__ q_idx, const uint16_t *__restr
         load_tile<PAGED>(kbar, nb_rows, tile + 1, ld_bl, ld_part, kv0, kv1, kv2, kv3, ptab,
                          pg.shift);
         const int64_t b0 = tile * kBT;
+        // the scores of the tile's 64 blocks into the stage (MASKED: blocks
+        // a row does not see score -inf)
+        auto score_tile = [&](auto masked) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            bf16x8 kf[4];
+            for (int j = 0; j < 4; ++j) {
+                bf16x8 kf[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                kf[s] = as_bf16x8(*reinterpret_cast<const uint4 *>(
-                    buf + (16 * j + n) * kRowBytes + 64 * s + 16 * g4));
-            const int blk = static_cast<int>(b0) + 16 * j + n;  // blocks < 2^27
-            // the row tiles' accumulators interleaved: no MFMA waits on the
-            // one before it
-            f32x4 acc[kRT];
+                for (int s = 0; s < 4; ++s)
+                    kf[s] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+                        buf + (16 * j + n) * kRowBytes + 64 * s + 16 * g4));
+                const int blk = static_cast<int>(b0) + 16 * j + n;  // blocks < 2^27
+                // the row tiles' accumulators interleaved: no MFMA waits on
+                // the one before it
+                f32x4 acc[kRT];
 #pragma unroll
-            for (int rt = 0; rt < kRT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int rt = 0; rt < kRT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+                for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int rt = 0; rt < kRT; ++rt)
-                    acc[rt] = mfma_bf16_16x16x32(qf[rt][s], kf[s], acc[rt]);
+                    for (int rt = 0; rt < kRT; ++rt)
+                        acc[rt] = mfma_bf16_16x16x32(qf[rt][s], kf[s], acc[rt]);
 #pragma unroll
-            for (int rt = 0; rt < kRT; ++rt) {
-                const float v = blk < ncq[rt] ? combine_heads<MODE>(acc[rt]) : -INFINITY;
-                *reinterpret_cast<float *>(stage + (4 * rt + g4) * kStageRow + 4 * (16 * j + n)) = v;
+                for (int rt = 0; rt < kRT; ++rt) {
+                    float v;
+                    if constexpr (decltype(masked)::value)
+                        v = blk < ncq[rt] ? combine_heads<MODE>(acc[rt]) : -INFINITY;
+                    else
+                        v = combine_heads<MODE>(acc[rt]);
+                    *reinterpret_cast<float *>(stage + (4 * rt + g4) * kStageRow +
+                                               4 * (16 * j + n)) = v;
+                }
             }
-        }
+        };
+        if (b0 + kBT <= nc_wave)
+            score_tile(std::false_type{});
+        else
+            score_tile(std::true_type{});
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
