@@ -1182,14 +1182,16 @@ int decode_num_splits(int B, int Hkv, int nct, int64_t max_entries, bool dense) 
     }
     Hkv *= nct;
     // at most 512 workgroups (the two per CU that fit at once: one more and a
-    // second round of workgroups doubles the time), at least one stage per
-    // wave.  The grid rounds the splits up to a multiple of 8 (the XCD
-    // mapping), so from 8 on the count is a multiple of 8 itself: 21 splits
-    // of 24 column tiles would launch 576 workgroups, 16 launch 384 (next_n
-    // = 4 at 4 x 1M: 38.9 against 28.5 us for attention and merge).
+    // second round of workgroups doubles the time).  The grid rounds the
+    // splits up to a multiple of 8 (the XCD mapping), so from 8 on the count
+    // is a multiple of 8 itself: 21 splits of 24 column tiles would launch
+    // 576 workgroups, 16 launch 384 (next_n = 4 at 4 x 1M: 38.9 against
+    // 28.5 us for attention and merge).  At least two stages per wave, which
+    // caps short lists (4 x 1M: 17 splits, 0.081 ms per step; at one stage
+    // per wave 33 splits, 0.081-0.083 ms; at four 9 splits, 0.0875 ms).
     int64_t want = 512 / (static_cast<int64_t>(B) * Hkv);
     if (want >= 8) want -= want % 8;
-    const int64_t cap = (nstages + 3) / 4;  // at least one stage per wave
+    const int64_t cap = (nstages + 7) / 8;
     if (want > cap) want = cap;
     if (want < 1) want = 1;
     return static_cast<int>(want);
